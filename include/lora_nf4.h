@@ -1,0 +1,134 @@
+/*
+ * lora_nf4.h — C ABI of the fused NF4-LoRA linear for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the LoRA linear over a frozen base weight held in 4-bit
+ * NormalFloat (NF4) form, as the Unsloth pages describe it:
+ *   - "Unsloth acceleration principles: CUDA kernel fusion and memory optimization"
+ *     (kernel-fusion section): the base linear, the LoRA down- and up-projections
+ *     and the add run as one fused pass; the model is loaded with
+ *     load_in_4bit=True and get_peft_model(r, lora_alpha, lora_dropout=0,
+ *     bias="none"). Its compact-layout section fixes A in R^{d_in x r} and
+ *     B in R^{r x d_out}.
+ *   - "Unlocking AI potential: Unsloth's algorithms and implementation"
+ *     (core algorithms): a hand-written backward instead of autograd.
+ *   - "Reading the Unsloth changelog" (section 1.1): base weights resident in NF4.
+ *
+ * With T tokens, K = d_in, N = d_out, s = lora_alpha / r and D = deq(Wt), where
+ * Wt = W^T is the nn.Linear-oriented [N, K] base weight:
+ *     forward : y  = x D^T + s (x A) B
+ *     backward: dX = dY D + s (dY B^T) A^T,  dA = x^T (s dY B^T),  dB = s (x A)^T dY
+ * There is no dropout, no bias and no base-weight gradient (the base is frozen).
+ *
+ * NF4 format (the pages name NF4 but do not define it; the QLoRA NormalFloat
+ * construction is used): 16 levels q[0..15] (normal quantiles, exact zero at
+ * code 7, q[0] = -1, q[15] = 1, stored as float32); blocks of 64 consecutive
+ * elements along a row; one float32 absmax per block; code = nearest level to
+ * w / absmax, ties to the higher code; an all-zero block has absmax +0 and codes
+ * 7; two codes per byte, the even element in the low nibble.
+ *
+ * Conventions for every entry point:
+ *   - Matrices are row-major and dense. bf16 values are passed as uint16_t bit
+ *     patterns.
+ *   - Every data pointer is a DEVICE pointer owned by the caller; the library
+ *     never allocates, frees or synchronizes. Work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream) and the call returns at once.
+ *   - Arguments are validated on the host before any HIP call; on error nothing
+ *     is enqueued and a negative ln_status is returned. Faults inside kernels
+ *     cannot be detected without a synchronization and are not reported.
+ *   - Data pointers must be 16-byte aligned. Outputs must not overlap inputs.
+ *   - Calls are stateless and thread-safe; concurrent calls on different streams
+ *     are safe when their outputs do not overlap.
+ *   - Floating-point inputs must be finite (not checked: a check needs a sync).
+ */
+#ifndef LORA_NF4_H
+#define LORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LN_OK = 0,
+    LN_EINVAL = -1,      /* null pointer, size < 1, non-finite alpha, unknown dtype   */
+    LN_ESHAPE = -2,      /* d_in or cols not a multiple of 64, d_out not a multiple
+                            of 8, or a size beyond the 2^31 element-index range     */
+    LN_EALIGN = -3,      /* a data pointer is not 16-byte aligned                    */
+    LN_ERANK = -4,       /* r < 1 or r > LN_MAX_RANK                                 */
+    LN_EWORKSPACE = -5,  /* workspace null or smaller than lora_nf4_bwd_workspace_bytes */
+    LN_EALIAS = -6,      /* an output overlaps an input or another output            */
+    LN_EHIP = -7         /* a HIP launch reported an error                           */
+} ln_status;
+
+typedef enum { LN_F32 = 0, LN_BF16 = 1 } ln_dtype;
+
+#define LN_MAX_RANK 128
+
+/*
+ * nf4_quantize — blockwise NF4 quantization of w [rows, cols] (float32 or bf16
+ * per w_dtype) into codes uint8 [rows, cols/2] and absmax float32
+ * [rows, cols/64]. cols % 64 == 0. Codes and absmax are bit-exact with the
+ * definition above: the level comparisons are made exactly (float64).
+ * The frozen weight is quantized once at load time ("load_in_4bit").
+ */
+int nf4_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols,
+                 uint8_t* codes, float* absmax, void* stream);
+
+/*
+ * nf4_dequantize — out [rows, cols] = q[code] * absmax, rounded once to float32
+ * (nearest-even); for LN_BF16 output that float32 is rounded to nearest-even
+ * bf16. cols % 64 == 0.
+ */
+int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows, int64_t cols,
+                   int out_dtype, void* out, void* stream);
+
+/*
+ * lora_nf4_fwd — y = x D^T + s (x A) B, one fused pass.
+ *   x        bf16 [T, d_in]
+ *   w_codes  uint8 [d_out, d_in/2], w_absmax float32 [d_out, d_in/64] (from nf4_quantize
+ *            of the [d_out, d_in] base weight)
+ *   A        bf16 [d_in, r],  B bf16 [r, d_out]
+ *   y        bf16 [T, d_out]  (output)
+ *   u_save   bf16 [T, r] = x A, rounded to bf16 (output; may be NULL). Passing it
+ *            to lora_nf4_bwd saves that pass recomputing it.
+ * T >= 1, d_in % 64 == 0, d_out % 8 == 0, 1 <= r <= LN_MAX_RANK. s = lora_alpha / r
+ * is formed in float32 on the host.
+ */
+int lora_nf4_fwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha,
+                 const uint16_t* x, const uint8_t* w_codes, const float* w_absmax,
+                 const uint16_t* A, const uint16_t* B, uint16_t* y, uint16_t* u_save,
+                 void* stream);
+
+/*
+ * lora_nf4_bwd — dX, dA, dB of the forward above for upstream gradient dY.
+ *   dy       bf16 [T, d_out]
+ *   u_saved  bf16 [T, r] from lora_nf4_fwd, or NULL (then recomputed from x and A)
+ *   dx       bf16 [T, d_in] (output; may be NULL to skip the input gradient —
+ *            the pass over the base weight still runs, since it also forms dY B^T)
+ *   dA       bf16 [d_in, r], dB bf16 [r, d_out] (outputs)
+ *   workspace  device scratch of at least lora_nf4_bwd_workspace_bytes(T, d_in,
+ *            d_out, r) bytes, 256-byte aligned, owned by the caller; its contents
+ *            on entry do not matter and on return are unspecified. Two calls that
+ *            may run concurrently need separate workspaces.
+ * Shape rules as for lora_nf4_fwd.
+ */
+int lora_nf4_bwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha,
+                 const uint16_t* x, const uint16_t* dy,
+                 const uint8_t* w_codes, const float* w_absmax,
+                 const uint16_t* A, const uint16_t* B, const uint16_t* u_saved,
+                 uint16_t* dx, uint16_t* dA, uint16_t* dB,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes lora_nf4_bwd needs for these sizes (0 if the sizes are invalid). */
+size_t lora_nf4_bwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t r);
+
+/* A static, human-readable description of a status code. */
+const char* lora_nf4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_NF4_H */

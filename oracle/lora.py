@@ -68,3 +68,11 @@ def rel_err(got, ref) -> float:
     if den == 0.0:
         return 0.0 if num == 0.0 else float("inf")
     return num / den
+
+
+def lora_factor_grads(x, dY, A, B, alpha: float, r: int):
+    """dA = x^T (s dY B^T) and dB = s (x A)^T dY alone (they do not involve the base weight)."""
+    x, dY, A, B = (np.asarray(v, dtype=np.float64) for v in (x, dY, A, B))
+    s = float(alpha) / float(r)
+    G = s * (dY @ B.T)
+    return x.T @ G, s * ((x @ A).T @ dY)

@@ -1,0 +1,185 @@
+"""Fused NF4-LoRA linear for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding of ``liblora_nf4.so`` (C ABI in include/lora_nf4.h). Each
+function only marshals arguments: it checks tensor placement and dtypes,
+allocates outputs with PyTorch (device memory is PyTorch's job here) and calls
+the C entry point of the same name on the current HIP stream. Every step of the
+computation runs in the library's HIP kernels; there is no fallback. If the
+library has not been built, the first call raises.
+
+    codes, absmax = nf4_quantize(w)                    # w [d_out, d_in] fp32/bf16
+    y, u = lora_nf4_fwd(x, codes, absmax, A, B, lora_alpha)
+    dx, dA, dB = lora_nf4_bwd(x, dy, codes, absmax, A, B, lora_alpha, u_saved=u)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LoraNF4Error", "library", "library_path", "nf4_quantize", "nf4_dequantize",
+    "lora_nf4_fwd", "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "status_string",
+    "EXPORTED_SYMBOLS", "LN_MAX_RANK",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "liblora_nf4.so")
+
+LN_OK, LN_F32, LN_BF16 = 0, 0, 1
+LN_MAX_RANK = 128
+EXPORTED_SYMBOLS = ("nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_bwd",
+                    "lora_nf4_bwd_workspace_bytes", "lora_nf4_status_string")
+
+_lib = None
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_SIGS = {
+    "nf4_quantize": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _p, _p, _p]),
+    "nf4_dequantize": (ctypes.c_int, [_p, _p, _i64, _i64, ctypes.c_int, _p, _p]),
+    "lora_nf4_fwd": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_float,
+                                    _p, _p, _p, _p, _p, _p, _p, _p]),
+    "lora_nf4_bwd": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_float,
+                                    _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
+    "lora_nf4_bwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, ctypes.c_int32]),
+    "lora_nf4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+
+class LoraNF4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed with status {status}: {status_string(status)}")
+
+
+def library():
+    """The loaded liblora_nf4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                f"{library_path} is missing: build it with `python -m qlora_linear_amd.build` "
+                "(there is no non-HIP fallback)")
+        lib = ctypes.CDLL(library_path)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return library().lora_nf4_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != LN_OK:
+        raise LoraNF4Error(fn, status)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D")
+    return t
+
+
+def nf4_quantize(w: torch.Tensor):
+    """NF4-quantize a [rows, cols] float32 or bf16 matrix (cols % 64 == 0).
+
+    Returns (codes uint8 [rows, cols/2], absmax float32 [rows, cols/64]).
+    """
+    _dev(w, "w", ndim=2)
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("w must be float32 or bfloat16")
+    rows, cols = w.shape
+    codes = torch.empty((rows, max(cols // 2, 1)), dtype=torch.uint8, device=w.device)
+    absmax = torch.empty((rows, max(cols // 64, 1)), dtype=torch.float32, device=w.device)
+    dt = LN_BF16 if w.dtype == torch.bfloat16 else LN_F32
+    _check("nf4_quantize", library().nf4_quantize(w.data_ptr(), dt, rows, cols, codes.data_ptr(),
+                                                  absmax.data_ptr(), _stream(w)))
+    return codes, absmax
+
+
+def nf4_dequantize(codes: torch.Tensor, absmax: torch.Tensor, dtype=torch.float32):
+    """Dequantize NF4 codes/absmax back to a [rows, cols] float32 or bf16 matrix."""
+    _dev(codes, "codes", torch.uint8, 2)
+    _dev(absmax, "absmax", torch.float32, 2)
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("dtype must be float32 or bfloat16")
+    rows, cols = codes.shape[0], codes.shape[1] * 2
+    out = torch.empty((rows, cols), dtype=dtype, device=codes.device)
+    dt = LN_BF16 if dtype == torch.bfloat16 else LN_F32
+    _check("nf4_dequantize", library().nf4_dequantize(codes.data_ptr(), absmax.data_ptr(), rows,
+                                                      cols, dt, out.data_ptr(), _stream(codes)))
+    return out
+
+
+def _lora_shapes(x, codes, A, B):
+    T, K = x.shape
+    N = codes.shape[0]
+    r = A.shape[1]
+    if codes.shape[1] * 2 != K or A.shape[0] != K or B.shape != (r, N):
+        raise ValueError(f"inconsistent shapes: x {tuple(x.shape)}, codes {tuple(codes.shape)}, "
+                         f"A {tuple(A.shape)}, B {tuple(B.shape)}")
+    return T, K, N, r
+
+
+def lora_nf4_fwd(x, codes, absmax, A, B, lora_alpha: float, save_u: bool = True, out=None):
+    """y = x deq(W)^T + (lora_alpha / r) (x A) B; returns (y, u) with u = bf16(x A) or None."""
+    bf = torch.bfloat16
+    _dev(x, "x", bf, 2), _dev(codes, "codes", torch.uint8, 2), _dev(absmax, "absmax", torch.float32, 2)
+    _dev(A, "A", bf, 2), _dev(B, "B", bf, 2)
+    T, K, N, r = _lora_shapes(x, codes, A, B)
+    y = torch.empty((T, N), dtype=bf, device=x.device) if out is None else _dev(out, "out", bf, 2)
+    u = torch.empty((T, r), dtype=bf, device=x.device) if save_u else None
+    _check("lora_nf4_fwd", library().lora_nf4_fwd(T, K, N, r, float(lora_alpha), x.data_ptr(),
+                                                  codes.data_ptr(), absmax.data_ptr(), A.data_ptr(),
+                                                  B.data_ptr(), y.data_ptr(), _ptr(u), _stream(x)))
+    return y, u
+
+
+def lora_nf4_bwd_workspace_bytes(T: int, K: int, N: int, r: int) -> int:
+    return int(library().lora_nf4_bwd_workspace_bytes(T, K, N, r))
+
+
+def lora_nf4_bwd(x, dy, codes, absmax, A, B, lora_alpha: float, u_saved=None, need_dx: bool = True,
+                 workspace: torch.Tensor | None = None):
+    """Gradients (dx or None, dA, dB) of the forward for upstream gradient dy."""
+    bf = torch.bfloat16
+    _dev(x, "x", bf, 2), _dev(dy, "dy", bf, 2), _dev(codes, "codes", torch.uint8, 2)
+    _dev(absmax, "absmax", torch.float32, 2), _dev(A, "A", bf, 2), _dev(B, "B", bf, 2)
+    T, K, N, r = _lora_shapes(x, codes, A, B)
+    if dy.shape != (T, N):
+        raise ValueError("dy must be [T, d_out]")
+    if u_saved is not None:
+        _dev(u_saved, "u_saved", bf, 2)
+    dev = x.device
+    dx = torch.empty((T, K), dtype=bf, device=dev) if need_dx else None
+    dA = torch.empty((K, r), dtype=bf, device=dev)
+    dB = torch.empty((r, N), dtype=bf, device=dev)
+    nbytes = lora_nf4_bwd_workspace_bytes(T, K, N, r)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8)
+    _check("lora_nf4_bwd", library().lora_nf4_bwd(
+        T, K, N, r, float(lora_alpha), x.data_ptr(), dy.data_ptr(), codes.data_ptr(),
+        absmax.data_ptr(), A.data_ptr(), B.data_ptr(), _ptr(u_saved), _ptr(dx), dA.data_ptr(),
+        dB.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x)))
+    return dx, dA, dB

@@ -1,0 +1,159 @@
+// C ABI of the fused NF4-LoRA linear (declared in include/lora_nf4.h).
+//
+// Every entry point validates its arguments on the host before touching HIP, so
+// argument errors are reported without a GPU and nothing is enqueued on error.
+#include <cmath>
+#include <cstdint>
+
+#include "launch.h"
+#include "lora_nf4.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlap(const Span& a, const Span& b) {
+  if (a.p == nullptr || b.p == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Every output span must be disjoint from every input span and from the other outputs.
+bool any_alias(const Span* outs, int n_out, const Span* ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+// Shared shape rules of the forward and backward.
+int check_linear_shape(int64_t T, int64_t K, int64_t N, int32_t r, float alpha) {
+  if (T < 1 || K < 1 || N < 1) return LN_EINVAL;
+  if (!std::isfinite(alpha)) return LN_EINVAL;
+  if (r < 1 || r > LN_MAX_RANK) return LN_ERANK;
+  if (K % 64 != 0 || N % 8 != 0) return LN_ESHAPE;
+  if (T > kMaxDim || K > kMaxDim || N > kMaxDim) return LN_ESHAPE;
+  return LN_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LN_OK : LN_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* lora_nf4_status_string(int status) {
+  switch (status) {
+    case LN_OK: return "ok";
+    case LN_EINVAL: return "invalid argument (null pointer, size < 1, non-finite alpha or unknown dtype)";
+    case LN_ESHAPE: return "unsupported shape (d_in/cols must be a multiple of 64, d_out a multiple of 8, sizes below 2^31)";
+    case LN_EALIGN: return "data pointer not 16-byte aligned (workspace: 256-byte)";
+    case LN_ERANK: return "LoRA rank r outside [1, LN_MAX_RANK]";
+    case LN_EWORKSPACE: return "workspace missing or smaller than lora_nf4_bwd_workspace_bytes()";
+    case LN_EALIAS: return "an output overlaps an input or another output";
+    case LN_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int nf4_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols, uint8_t* codes,
+                 float* absmax, void* stream) {
+  if (w == nullptr || codes == nullptr || absmax == nullptr) return LN_EINVAL;
+  if (w_dtype != LN_F32 && w_dtype != LN_BF16) return LN_EINVAL;
+  if (rows < 1 || cols < 1) return LN_EINVAL;
+  if (cols % 64 != 0 || rows > kMaxDim || cols > kMaxDim || rows * cols > (int64_t(1) << 38))
+    return LN_ESHAPE;
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(absmax)) return LN_EALIGN;
+  const size_t n = static_cast<size_t>(rows * cols);
+  const Span outs[2] = {{codes, n / 2}, {absmax, n / 64 * 4}};
+  const Span ins[1] = {{w, n * (w_dtype == LN_BF16 ? 2 : 4)}};
+  if (any_alias(outs, 2, ins, 1)) return LN_EALIAS;
+  return hip_status(lnf4::launch_nf4_quantize(w, w_dtype == LN_BF16, rows, cols, codes, absmax,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows, int64_t cols,
+                   int out_dtype, void* out, void* stream) {
+  if (codes == nullptr || absmax == nullptr || out == nullptr) return LN_EINVAL;
+  if (out_dtype != LN_F32 && out_dtype != LN_BF16) return LN_EINVAL;
+  if (rows < 1 || cols < 1) return LN_EINVAL;
+  if (cols % 64 != 0 || rows > kMaxDim || cols > kMaxDim || rows * cols > (int64_t(1) << 38))
+    return LN_ESHAPE;
+  if (!aligned16(codes) || !aligned16(absmax) || !aligned16(out)) return LN_EALIGN;
+  const size_t n = static_cast<size_t>(rows * cols);
+  const Span outs[1] = {{out, n * (out_dtype == LN_BF16 ? 2 : 4)}};
+  const Span ins[2] = {{codes, n / 2}, {absmax, n / 64 * 4}};
+  if (any_alias(outs, 1, ins, 2)) return LN_EALIAS;
+  return hip_status(lnf4::launch_nf4_dequantize(codes, absmax, rows, cols, out_dtype == LN_BF16, out,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int lora_nf4_fwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha,
+                 const uint16_t* x, const uint8_t* w_codes, const float* w_absmax,
+                 const uint16_t* A, const uint16_t* B, uint16_t* y, uint16_t* u_save,
+                 void* stream) {
+  if (x == nullptr || w_codes == nullptr || w_absmax == nullptr || A == nullptr || B == nullptr ||
+      y == nullptr)
+    return LN_EINVAL;
+  int st = check_linear_shape(T, d_in, d_out, r, lora_alpha);
+  if (st != LN_OK) return st;
+  if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_absmax) || !aligned16(A) ||
+      !aligned16(B) || !aligned16(y) || (u_save != nullptr && !aligned16(u_save)))
+    return LN_EALIGN;
+  const size_t t = T, k = d_in, n = d_out, rr = r;
+  const Span outs[2] = {{y, t * n * 2}, {u_save, t * rr * 2}};
+  const Span ins[5] = {{x, t * k * 2}, {w_codes, n * k / 2}, {w_absmax, n * k / 64 * 4},
+                       {A, k * rr * 2}, {B, rr * n * 2}};
+  if (any_alias(outs, 2, ins, 5)) return LN_EALIAS;
+  const float s = lora_alpha / static_cast<float>(r);
+  return hip_status(lnf4::launch_lora_fwd(static_cast<int>(T), static_cast<int>(d_in),
+                                          static_cast<int>(d_out), r, s, x, w_codes, w_absmax, A, B,
+                                          y, u_save, static_cast<hipStream_t>(stream)));
+}
+
+size_t lora_nf4_bwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t r) {
+  if (check_linear_shape(T, d_in, d_out, r, 1.0f) != LN_OK) return 0;
+  return lnf4::plan_bwd(T, d_in, d_out, r).bytes;
+}
+
+int lora_nf4_bwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha,
+                 const uint16_t* x, const uint16_t* dy, const uint8_t* w_codes,
+                 const float* w_absmax, const uint16_t* A, const uint16_t* B,
+                 const uint16_t* u_saved, uint16_t* dx, uint16_t* dA, uint16_t* dB,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (x == nullptr || dy == nullptr || w_codes == nullptr || w_absmax == nullptr || A == nullptr ||
+      B == nullptr || dA == nullptr || dB == nullptr)
+    return LN_EINVAL;
+  int st = check_linear_shape(T, d_in, d_out, r, lora_alpha);
+  if (st != LN_OK) return st;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(w_codes) || !aligned16(w_absmax) ||
+      !aligned16(A) || !aligned16(B) || !aligned16(dA) || !aligned16(dB) ||
+      (u_saved != nullptr && !aligned16(u_saved)) || (dx != nullptr && !aligned16(dx)))
+    return LN_EALIGN;
+  const lnf4::BwdPlan plan = lnf4::plan_bwd(T, d_in, d_out, r);
+  if (workspace == nullptr || workspace_bytes < plan.bytes) return LN_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LN_EALIGN;
+  const size_t t = T, k = d_in, n = d_out, rr = r;
+  const Span outs[4] = {{dx, t * k * 2}, {dA, k * rr * 2}, {dB, rr * n * 2}, {workspace, plan.bytes}};
+  const Span ins[7] = {{x, t * k * 2},        {dy, t * n * 2},   {w_codes, n * k / 2},
+                       {w_absmax, n * k / 64 * 4}, {A, k * rr * 2}, {B, rr * n * 2},
+                       {u_saved, t * rr * 2}};
+  if (any_alias(outs, 4, ins, 7)) return LN_EALIAS;
+  const float s = lora_alpha / static_cast<float>(r);
+  return hip_status(lnf4::launch_lora_bwd(static_cast<int>(T), static_cast<int>(d_in),
+                                          static_cast<int>(d_out), r, s, x, dy, w_codes, w_absmax,
+                                          A, B, u_saved, dx, dA, dB, workspace, plan,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

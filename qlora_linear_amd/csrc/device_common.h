@@ -1,0 +1,76 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 packing, the bf16 MFMA
+// wrapper and its fragment layout, the NF4 level table, and the XCD-aware
+// workgroup remap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lnf4 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// NF4 levels as float32 bit patterns, code 0..15. The QLoRA NormalFloat
+// construction: quantiles of N(0,1) at 8 evenly spaced probabilities from
+// delta = 1 - (1/30 + 1/32)/2 towards 1/2 (positive side) and 7 (negative side),
+// plus an exact zero, divided by the quantile at delta, rounded to float32.
+__host__ __device__ constexpr uint32_t kNf4LevelBits[16] = {
+    0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu, 0xbe3d353du,
+    0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
+    0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
+
+__device__ __forceinline__ float nf4_level(int c) { return __uint_as_float(kNf4LevelBits[c]); }
+
+// Two float32 -> packed nearest-even bf16 (v_cvt_pk_bf16_f32); `lo` lands in the
+// low half, i.e. at the lower address.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t p = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float v) {
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// v_mfma_f32_16x16x32_bf16: D[16x16] = A[16x32] * B[32x16] + C, fp32 accumulate.
+// Operand fragments (one 16-byte register quad per lane):
+//   A: lane l holds row (l & 15), reduction elements 8*(l >> 4) .. +7
+//   B: lane l holds column (l & 15), reduction elements 8*(l >> 4) .. +7
+//   C/D: lane l holds column (l & 15), rows 4*(l >> 4) .. +3
+// Any permutation of the reduction index applied to both A and B leaves the
+// product unchanged; kernels rely only on the row/column mapping.
+__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Workgroup ids are dispatched round-robin over the 8 XCDs of MI355X (each with
+// its own L2). Map them so that each XCD receives one contiguous range of
+// logical tile ids; neighbouring logical tiles (which share input rows) then
+// share an L2. A bijection on [0, n).
+__device__ __forceinline__ int xcd_remap(int pid, int n) {
+  constexpr int kXcd = 8;
+  const int per = n / kXcd, rem = n % kXcd;
+  const int xcd = pid % kXcd, local = pid / kXcd;
+  return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+// Grouped (m, n) ordering of a logical tile id: `group_m` row-tiles are swept
+// together so that their column tiles reuse the same weight strip.
+__device__ __forceinline__ void tile_coords(int lid, int mt, int nt, int group_m, int& m, int& n) {
+  const int per_group = group_m * nt;
+  const int g = lid / per_group;
+  const int first_m = g * group_m;
+  const int gsize = min(mt - first_m, group_m);
+  const int in = lid - g * per_group;
+  m = first_m + in % gsize;
+  n = in / gsize;
+}
+
+}  // namespace lnf4

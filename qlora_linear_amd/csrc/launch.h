@@ -1,0 +1,39 @@
+// Internal launchers, one per kernel family. Arguments are already validated by
+// the C-ABI layer (api.cpp); each launcher only enqueues work on `stream` and
+// returns the hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lnf4 {
+
+hipError_t launch_nf4_quantize(const void* w, bool w_is_bf16, int64_t rows, int64_t cols,
+                               uint8_t* codes, float* absmax, hipStream_t stream);
+
+hipError_t launch_nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows,
+                                 int64_t cols, bool out_bf16, void* out, hipStream_t stream);
+
+hipError_t launch_lora_fwd(int T, int K, int N, int r, float s, const uint16_t* x,
+                           const uint8_t* codes, const float* absmax, const uint16_t* A,
+                           const uint16_t* B, uint16_t* y, uint16_t* u_save, hipStream_t stream);
+
+// Backward plan: how the workspace is carved. Shared by the launcher and the
+// workspace-size query so the two always agree.
+struct BwdPlan {
+  int rp;             // r rounded up to the MFMA reduction granularity (32)
+  int splits_a;       // token splits of the dA reduction
+  int splits_b;       // token splits of the dB reduction
+  size_t off_g, off_u, off_pa, off_pb;  // byte offsets into the workspace
+  size_t bytes;       // total workspace bytes
+};
+BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r);
+
+hipError_t launch_lora_bwd(int T, int K, int N, int r, float s, const uint16_t* x,
+                           const uint16_t* dy, const uint8_t* codes, const float* absmax,
+                           const uint16_t* A, const uint16_t* B, const uint16_t* u_saved,
+                           uint16_t* dx, uint16_t* dA, uint16_t* dB, void* workspace,
+                           const BwdPlan& plan, hipStream_t stream);
+
+}  // namespace lnf4

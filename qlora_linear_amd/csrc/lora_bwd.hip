@@ -1,0 +1,441 @@
+// Fused NF4-LoRA linear, backward (gfx950).
+//
+// The pages replace autograd with hand-written backward kernels ("Unlocking AI
+// potential: Unsloth's algorithms and implementation", core-algorithms section;
+// "Unsloth performance measured: is it really 2x faster?", section 3). For the
+// LoRA linear with frozen NF4 base, s = alpha / r and D = deq(Wt):
+//     G  = s dY B^T        dX = dY D + G A^T        dA = x^T G        dB = s U^T dY
+// Kernels, all on the caller's stream with no host synchronization:
+//   1. lora_dx_kernel   — K-loop over d_out in NF4-block steps: dequantizes the
+//      weight tile into LDS transposed (reduction index contiguous), bf16 MFMA
+//      for dY D; G = s dY B^T accumulated from the same dY fragments; epilogue
+//      adds G A^T and stores dX; the first column tile also writes bf16 G.
+//   2. lora_u_kernel    — U = x A when the forward's copy is not supplied.
+//   3. skinny_tn_kernel — split-T partial sums of M^T V for the two rank-r
+//      gradients (dA: M = x, V = G; dB: M = dY, V = U), bf16 MFMA on tiles
+//      staged transposed in LDS.
+//   4. skinny_reduce_kernel — fixed-order sum of the partials (deterministic),
+//      scale, bf16 store in the gradient's layout.
+#include "device_common.h"
+#include "launch.h"
+
+namespace lnf4 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBK = 64;
+constexpr int kLds = kBK + 8;
+
+template <int BM, int BN, int RT>
+struct DxCfg {
+  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int TM = WM / 16, TN = WN / 16;
+  static constexpr int RP = ((RT * 16 + 31) / 32) * 32;
+  static constexpr int UT = (RT + 1) / 2;
+  static constexpr int ES = RP + 8;
+  static constexpr int SX = (BM * (ES > kLds ? ES : kLds));
+  static constexpr int SW = (BN * (ES > kLds ? ES : kLds));
+  static constexpr int KPW = BN / 4;  // weight columns (k) dequantized per wave per step
+};
+
+template <int BM, int BN, int RT>
+__global__ __launch_bounds__(kThreads) void lora_dx_kernel(
+    int T, int K, int N, int r, float s, const uint16_t* __restrict__ dy,
+    const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ dx,
+    uint16_t* __restrict__ g_out) {
+  using C = DxCfg<BM, BN, RT>;
+  __shared__ __align__(16) uint16_t dys[C::SX];   // dY tile [BM][64 of n]
+  __shared__ __align__(16) uint16_t ds[C::SW];    // deq weight, transposed: [BN of k][64 of n]
+  __shared__ __align__(16) uint16_t bs[RT * 16 * kLds];  // B slice [r][64 of n]
+  __shared__ float lut[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int mt = (T + BM - 1) / BM, kt_tiles = (K + BN - 1) / BN;
+  int tm, tk;
+  tile_coords(xcd_remap(blockIdx.x, mt * kt_tiles), mt, kt_tiles, 8, tm, tk);
+  const int m0 = tm * BM, k0 = tk * BN;
+  const int K2 = K / 2, KB = K / kBK;
+
+  if (tid < 16) lut[tid] = nf4_level(tid);
+
+  f32x4_t acc[C::TM][C::TN];
+  f32x4_t gacc[C::TM][C::UT];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < C::UT; ++u) gacc[i][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int NS = (N + kBK - 1) / kBK;
+  for (int ns = 0; ns < NS; ++ns) {
+    const int n0 = ns * kBK;
+    __syncthreads();
+    // dY tile [BM x 64]
+    for (int c = tid; c < BM * 8; c += kThreads) {
+      const int row = c >> 3, ch = c & 7;
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (m0 + row < T && n0 + ch * 8 < N)
+        v = *reinterpret_cast<const uint4*>(dy + static_cast<size_t>(m0 + row) * N + n0 + ch * 8);
+      *reinterpret_cast<uint4*>(dys + row * kLds + ch * 8) = v;
+    }
+    // B slice [r x 64] (rows of B are contiguous in n)
+    for (int c = tid; c < RT * 16 * 8; c += kThreads) {
+      const int j = c >> 3, ch = c & 7;
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (j < r && n0 + ch * 8 < N)
+        v = *reinterpret_cast<const uint4*>(B + static_cast<size_t>(j) * N + n0 + ch * 8);
+      *reinterpret_cast<uint4*>(bs + j * kLds + ch * 8) = v;
+    }
+    // weight tile: lane = row n (64 rows), wave = a run of KPW columns k;
+    // dequantized values are written transposed, ds[k][n].
+    {
+      const int n = n0 + lane;
+#pragma unroll
+      for (int part = 0; part < C::KPW / 32; ++part) {
+        const int kl = wave * C::KPW + part * 32;  // local k of this 32-run
+        const int kg = k0 + kl;
+        uint4 cw = {0u, 0u, 0u, 0u};
+        float a = 0.f;
+        if (n < N && kg < K) {
+          cw = *reinterpret_cast<const uint4*>(codes + static_cast<size_t>(n) * K2 + kg / 2);
+          a = absmax[static_cast<size_t>(n) * KB + kg / kBK];
+        }
+        const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+          for (int h = 0; h < 8; ++h) {
+            const float v = lut[(cws[q] >> (4 * h)) & 15u] * a;
+            ds[(kl + q * 8 + h) * kLds + lane] = to_bf16(v);
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int kc = kk * 32 + lq * 8;
+      uint4 af[C::TM], bfr[C::TN];
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+        af[i] = *reinterpret_cast<const uint4*>(dys + (wm * C::WM + i * 16 + l16) * kLds + kc);
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        bfr[j] = *reinterpret_cast<const uint4*>(ds + (wn * C::WN + j * 16 + l16) * kLds + kc);
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+#pragma unroll
+      for (int u = 0; u < C::UT; ++u) {
+        const int jt = 2 * u + wn;
+        if (jt < RT) {
+          const uint4 bu = *reinterpret_cast<const uint4*>(bs + (jt * 16 + l16) * kLds + kc);
+#pragma unroll
+          for (int i = 0; i < C::TM; ++i) gacc[i][u] = mfma16(af[i], bu, gacc[i][u]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: acc += bf16(G) A^T, G = s dY B^T ----------------------------------
+  __syncthreads();
+  uint16_t* gs = dys;  // [BM][ES]
+  uint16_t* at = ds;   // [BN][ES]: rows k, rank contiguous (A is [K, r] row-major)
+#pragma unroll
+  for (int u = 0; u < C::UT; ++u) {
+    const int jt = 2 * u + wn;
+    if (jt < RT) {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = wm * C::WM + i * 16 + lq * 4 + e, col = jt * 16 + l16;
+          const uint16_t gv = to_bf16(s * gacc[i][u][e]);
+          gs[row * C::ES + col] = gv;
+          if (tk == 0 && col < r && m0 + row < T) g_out[static_cast<size_t>(m0 + row) * r + col] = gv;
+        }
+    }
+  }
+  constexpr int PADC = C::RP - RT * 16;
+  if (PADC > 0)
+    for (int e = tid; e < BM * PADC; e += kThreads) {
+      const int row = e / PADC, col = RT * 16 + (e - row * PADC);
+      gs[row * C::ES + col] = 0;
+    }
+  for (int e = tid; e < BN * C::RP; e += kThreads) {
+    const int c = e / C::RP, j = e - c * C::RP;
+    at[c * C::ES + j] = (j < r && k0 + c < K) ? A[static_cast<size_t>(k0 + c) * r + j] : uint16_t(0);
+  }
+  __syncthreads();
+  if (dx == nullptr) return;
+#pragma unroll
+  for (int ks = 0; ks < C::RP / 32; ++ks) {
+    const int kc = ks * 32 + lq * 8;
+    uint4 af[C::TM], bfr[C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+      af[i] = *reinterpret_cast<const uint4*>(gs + (wm * C::WM + i * 16 + l16) * C::ES + kc);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+      bfr[j] = *reinterpret_cast<const uint4*>(at + (wn * C::WN + j * 16 + l16) * C::ES + kc);
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+  }
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + wm * C::WM + i * 16 + lq * 4 + e;
+        const int col = k0 + wn * C::WN + j * 16 + l16;
+        if (row < T && col < K) dx[static_cast<size_t>(row) * K + col] = to_bf16(acc[i][j][e]);
+      }
+}
+
+// U = x A, bf16 [T, r]: 64 token rows per workgroup, one 16-row strip per wave.
+template <int RT>
+__global__ __launch_bounds__(kThreads) void lora_u_kernel(int T, int K, int r,
+                                                          const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ A,
+                                                          uint16_t* __restrict__ u) {
+  __shared__ __align__(16) uint16_t xs[64 * kLds];
+  __shared__ __align__(16) uint16_t as_[RT * 16 * kLds];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int m0 = blockIdx.x * 64;
+  f32x4_t uacc[RT];
+#pragma unroll
+  for (int jt = 0; jt < RT; ++jt) uacc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < K; k0 += kBK) {
+    __syncthreads();
+    for (int c = tid; c < 64 * 8; c += kThreads) {
+      const int row = c >> 3, ch = c & 7;
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (m0 + row < T)
+        v = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(m0 + row) * K + k0 + ch * 8);
+      *reinterpret_cast<uint4*>(xs + row * kLds + ch * 8) = v;
+    }
+    for (int e = tid; e < kBK * RT * 16; e += kThreads) {
+      const int kk = e / (RT * 16), j = e - kk * (RT * 16);
+      as_[j * kLds + kk] = (j < r) ? A[static_cast<size_t>(k0 + kk) * r + j] : uint16_t(0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int kc = kk * 32 + lq * 8;
+      const uint4 af = *reinterpret_cast<const uint4*>(xs + (wave * 16 + l16) * kLds + kc);
+#pragma unroll
+      for (int jt = 0; jt < RT; ++jt) {
+        const uint4 bu = *reinterpret_cast<const uint4*>(as_ + (jt * 16 + l16) * kLds + kc);
+        uacc[jt] = mfma16(af, bu, uacc[jt]);
+      }
+    }
+  }
+#pragma unroll
+  for (int jt = 0; jt < RT; ++jt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = m0 + wave * 16 + lq * 4 + e, col = jt * 16 + l16;
+      if (row < T && col < r) u[static_cast<size_t>(row) * r + col] = to_bf16(uacc[jt][e]);
+    }
+}
+
+// partial[split][c][j] = sum over the split's token range of M[t][c] * V[t][j].
+// M is [T, C] (C % 8 == 0), V is [T, r]. 128 columns per workgroup; each wave
+// owns 32 columns x all rank tiles. Both operands are staged transposed in LDS
+// so the token (reduction) index is contiguous for the MFMA fragments.
+template <int RT>
+__global__ __launch_bounds__(kThreads) void skinny_tn_kernel(int T, int Ccols, int r, int t_chunk,
+                                                             const uint16_t* __restrict__ M,
+                                                             const uint16_t* __restrict__ V,
+                                                             float* __restrict__ partial) {
+  constexpr int BC = 128;
+  __shared__ __align__(16) uint16_t mts[BC * kLds];
+  __shared__ __align__(16) uint16_t vts[RT * 16 * kLds];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int c0 = blockIdx.x * BC;
+  const int split = blockIdx.y;
+  const int t_begin = split * t_chunk;
+  const int t_end = min(T, t_begin + t_chunk);
+  f32x4_t acc[2][RT];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jt = 0; jt < RT; ++jt) acc[i][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int t0 = t_begin; t0 < t_end; t0 += kBK) {
+    __syncthreads();
+    for (int c = tid; c < kBK * (BC / 8); c += kThreads) {
+      const int tl = c / (BC / 8), ch = c - tl * (BC / 8);
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (t0 + tl < t_end && c0 + ch * 8 < Ccols)
+        v = *reinterpret_cast<const uint4*>(M + static_cast<size_t>(t0 + tl) * Ccols + c0 + ch * 8);
+      const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        mts[(ch * 8 + 2 * h) * kLds + tl] = static_cast<uint16_t>(vv[h] & 0xFFFFu);
+        mts[(ch * 8 + 2 * h + 1) * kLds + tl] = static_cast<uint16_t>(vv[h] >> 16);
+      }
+    }
+    for (int e = tid; e < kBK * RT * 16; e += kThreads) {
+      const int tl = e / (RT * 16), j = e - tl * (RT * 16);
+      vts[j * kLds + tl] = (j < r && t0 + tl < t_end) ? V[static_cast<size_t>(t0 + tl) * r + j] : uint16_t(0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int kc = kk * 32 + lq * 8;
+      uint4 af[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const uint4*>(mts + (wave * 32 + i * 16 + l16) * kLds + kc);
+#pragma unroll
+      for (int jt = 0; jt < RT; ++jt) {
+        const uint4 bv = *reinterpret_cast<const uint4*>(vts + (jt * 16 + l16) * kLds + kc);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[i][jt] = mfma16(af[i], bv, acc[i][jt]);
+      }
+    }
+  }
+  constexpr int RS = RT * 16;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jt = 0; jt < RT; ++jt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = c0 + wave * 32 + i * 16 + lq * 4 + e, j = jt * 16 + l16;
+        if (c < Ccols) partial[(static_cast<size_t>(split) * Ccols + c) * RS + j] = acc[i][jt][e];
+      }
+}
+
+// out = scale * sum_split partial, in split order; bf16 [C, r] or, transposed, [r, C].
+__global__ __launch_bounds__(kThreads) void skinny_reduce_kernel(const float* __restrict__ partial,
+                                                                 int splits, int Ccols, int r, int rs,
+                                                                 float scale, int transposed,
+                                                                 uint16_t* __restrict__ out) {
+  const int idx = blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= Ccols * r) return;
+  int c, j;
+  if (transposed) {
+    j = idx / Ccols;
+    c = idx - j * Ccols;
+  } else {
+    c = idx / r;
+    j = idx - c * r;
+  }
+  float sum = 0.f;
+  for (int sp = 0; sp < splits; ++sp) sum += partial[(static_cast<size_t>(sp) * Ccols + c) * rs + j];
+  out[idx] = to_bf16(scale * sum);
+}
+
+template <int RT>
+hipError_t launch_bwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
+                         const uint16_t* dy, const uint8_t* codes, const float* absmax,
+                         const uint16_t* A, const uint16_t* B, const uint16_t* u_saved,
+                         uint16_t* dx, uint16_t* dA, uint16_t* dB, void* workspace,
+                         const BwdPlan& p, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* g = reinterpret_cast<uint16_t*>(ws + p.off_g);
+  uint16_t* u = reinterpret_cast<uint16_t*>(ws + p.off_u);
+  float* pa = reinterpret_cast<float*>(ws + p.off_pa);
+  float* pb = reinterpret_cast<float*>(ws + p.off_pb);
+  constexpr int BM = 128, BN = 128;
+  const int tiles = ((T + BM - 1) / BM) * ((K + BN - 1) / BN);
+  lora_dx_kernel<BM, BN, RT><<<tiles, kThreads, 0, stream>>>(T, K, N, r, s, dy, codes, absmax, A, B,
+                                                             dx, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint16_t* uu = u_saved;
+  if (uu == nullptr) {
+    lora_u_kernel<RT><<<(T + 63) / 64, kThreads, 0, stream>>>(T, K, r, x, A, u);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    uu = u;
+  }
+  const int tca = (T + p.splits_a - 1) / p.splits_a;
+  const int tcb = (T + p.splits_b - 1) / p.splits_b;
+  skinny_tn_kernel<RT><<<dim3((K + 127) / 128, p.splits_a), kThreads, 0, stream>>>(T, K, r, tca, x, g,
+                                                                                   pa);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  skinny_tn_kernel<RT><<<dim3((N + 127) / 128, p.splits_b), kThreads, 0, stream>>>(T, N, r, tcb, dy,
+                                                                                   uu, pb);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  skinny_reduce_kernel<<<(K * r + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
+      pa, p.splits_a, K, r, RT * 16, 1.0f, 0, dA);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  skinny_reduce_kernel<<<(N * r + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
+      pb, p.splits_b, N, r, RT * 16, s, 1, dB);
+  return hipGetLastError();
+}
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+// Token splits for a skinny reduction over `cols` columns: enough workgroups
+// to fill the chip a few times over, each split a multiple of 64 tokens.
+int choose_splits(int64_t T, int64_t cols) {
+  const int64_t col_blocks = (cols + 127) / 128;
+  int64_t want = (1024 + col_blocks - 1) / col_blocks;
+  const int64_t max_splits = (T + 63) / 64;
+  if (want > max_splits) want = max_splits;
+  if (want < 1) want = 1;
+  // make every split a whole number of 64-token steps
+  int64_t chunk = (T + want - 1) / want;
+  chunk = ((chunk + 63) / 64) * 64;
+  return static_cast<int>((T + chunk - 1) / chunk);
+}
+
+}  // namespace
+
+BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r) {
+  BwdPlan p{};
+  const int64_t rs = ((r + 15) / 16) * 16;
+  p.rp = static_cast<int>(((r + 31) / 32) * 32);
+  p.splits_a = choose_splits(T, K);
+  p.splits_b = choose_splits(T, N);
+  size_t off = 0;
+  p.off_g = off;
+  off = align256(off + static_cast<size_t>(T) * r * 2);
+  p.off_u = off;
+  off = align256(off + static_cast<size_t>(T) * r * 2);
+  p.off_pa = off;
+  off = align256(off + static_cast<size_t>(p.splits_a) * K * rs * 4);
+  p.off_pb = off;
+  off = align256(off + static_cast<size_t>(p.splits_b) * N * rs * 4);
+  p.bytes = off;
+  return p;
+}
+
+hipError_t launch_lora_bwd(int T, int K, int N, int r, float s, const uint16_t* x,
+                           const uint16_t* dy, const uint8_t* codes, const float* absmax,
+                           const uint16_t* A, const uint16_t* B, const uint16_t* u_saved,
+                           uint16_t* dx, uint16_t* dA, uint16_t* dB, void* workspace,
+                           const BwdPlan& plan, hipStream_t stream) {
+#define LNF4_BWD(RT_)                                                                              \
+  return launch_bwd_rt<RT_>(T, K, N, r, s, x, dy, codes, absmax, A, B, u_saved, dx, dA, dB,        \
+                            workspace, plan, stream)
+  switch ((r + 15) / 16) {
+    case 1: LNF4_BWD(1);
+    case 2: LNF4_BWD(2);
+    case 3: LNF4_BWD(3);
+    case 4: LNF4_BWD(4);
+    case 5: LNF4_BWD(5);
+    case 6: LNF4_BWD(6);
+    case 7: LNF4_BWD(7);
+    case 8: LNF4_BWD(8);
+    default: return hipErrorInvalidValue;
+  }
+#undef LNF4_BWD
+}
+
+}  // namespace lnf4

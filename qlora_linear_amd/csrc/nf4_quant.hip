@@ -1,0 +1,101 @@
+// NF4 blockwise quantization and dequantization kernels (gfx950).
+//
+// The pages keep the frozen base weight in 4-bit NF4 form ("Unsloth
+// acceleration principles: CUDA kernel fusion and memory optimization",
+// kernel-fusion section, load_in_4bit=True; "Reading the Unsloth changelog",
+// section 1.1). Both kernels are HBM-bound elementwise passes run once per
+// weight (quantize) or only for export / tests (dequantize).
+#include "device_common.h"
+#include "launch.h"
+
+namespace lnf4 {
+namespace {
+
+// Decision thresholds between neighbouring levels, exact in float64.
+__device__ __forceinline__ double nf4_midpoint(int i) {
+  return 0.5 * (static_cast<double>(nf4_level(i)) + static_cast<double>(nf4_level(i + 1)));
+}
+
+// Code of w in a block of absmax a > 0: the number of thresholds w reaches,
+// i.e. the nearest level to w / a with ties going up. m_i * a is exact in
+// float64 (at most 27 + 24 significant bits), so each comparison is exact.
+__device__ __forceinline__ uint32_t nf4_code(float w, float a) {
+  if (a == 0.0f) return 7u;
+  const double wd = w, ad = a;
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 15; ++i) c += (wd >= nf4_midpoint(i) * ad) ? 1u : 0u;
+  return c;
+}
+
+__device__ __forceinline__ float load_elem(const float* w, int64_t i) { return w[i]; }
+__device__ __forceinline__ float load_elem(const uint16_t* w, int64_t i) { return bf16_to_f32(w[i]); }
+
+// One thread per output byte (two elements). A 64-element block is 32
+// consecutive threads — half a wavefront — so the absmax is a 32-lane
+// butterfly max. The byte count is a multiple of 32, so every half-wave is
+// either fully in range or fully out of it.
+template <typename In>
+__global__ __launch_bounds__(256) void nf4_quantize_kernel(const In* __restrict__ w, int64_t nbytes,
+                                                           uint8_t* __restrict__ codes,
+                                                           float* __restrict__ absmax) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= nbytes) return;
+  const float w0 = load_elem(w, 2 * i), w1 = load_elem(w, 2 * i + 1);
+  float m = fmaxf(fabsf(w0), fabsf(w1));
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 32));
+  const uint32_t c0 = nf4_code(w0, m), c1 = nf4_code(w1, m);
+  codes[i] = static_cast<uint8_t>(c0 | (c1 << 4));
+  if ((i & 31) == 0) absmax[i >> 5] = m;
+}
+
+// One thread per dword of codes (8 elements of one block). Output: the product
+// level * absmax, one float32 rounding; bf16 output rounds that float32 again.
+__global__ __launch_bounds__(256) void nf4_dequantize_kernel(const uint32_t* __restrict__ codes,
+                                                             const float* __restrict__ absmax,
+                                                             int64_t ndw, int out_bf16,
+                                                             void* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= ndw) return;
+  const uint32_t c = codes[i];
+  const float a = absmax[i >> 3];
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = nf4_level((c >> (4 * j)) & 15u) * a;
+  if (out_bf16) {
+    uint4 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+               pack_bf16x2(v[6], v[7])};
+    reinterpret_cast<uint4*>(out)[i] = o;
+  } else {
+    float4* o = reinterpret_cast<float4*>(out) + 2 * i;
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_nf4_quantize(const void* w, bool w_is_bf16, int64_t rows, int64_t cols,
+                               uint8_t* codes, float* absmax, hipStream_t stream) {
+  const int64_t nbytes = rows * cols / 2;
+  const dim3 grid(static_cast<unsigned>((nbytes + 255) / 256));
+  if (w_is_bf16)
+    nf4_quantize_kernel<uint16_t><<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(w), nbytes,
+                                                            codes, absmax);
+  else
+    nf4_quantize_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(w), nbytes, codes,
+                                                         absmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows,
+                                 int64_t cols, bool out_bf16, void* out, hipStream_t stream) {
+  const int64_t ndw = rows * cols / 8;
+  const dim3 grid(static_cast<unsigned>((ndw + 255) / 256));
+  nf4_dequantize_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<const uint32_t*>(codes), absmax,
+                                                  ndw, out_bf16 ? 1 : 0, out);
+  return hipGetLastError();
+}
+
+}  // namespace lnf4

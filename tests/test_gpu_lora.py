@@ -1,0 +1,168 @@
+"""Fused NF4-LoRA forward and backward on the GPU against the fp64 oracle.
+
+Bar: max|gpu - ref| / max|ref| <= 1e-2 for y, dX, dA, dB (bf16 outputs, fp32
+accumulation); U saved by the forward to the same bar. Small shapes compare
+every element; full workload sizes compare sampled rows of y and dX and the
+full dA and dB.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import lora as olora
+from oracle import nf4 as onf4
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def q():
+    import qlora_linear_amd as q
+    q.library()
+    return q
+
+
+def _f64(bits):
+    return olora.bf16_to_f64(bits)
+
+
+def _run_gpu(q, inp, alpha, u_saved=True, need_dx=True):
+    from tests.gpu_util import dev_bf16
+    x, W, A, B, dY = (dev_bf16(inp[k]) for k in ("x", "W", "A", "B", "dY"))
+    codes, absmax = q.nf4_quantize(W)
+    y, u = q.lora_nf4_fwd(x, codes, absmax, A, B, alpha, save_u=True)
+    dx, dA, dB = q.lora_nf4_bwd(x, dY, codes, absmax, A, B, alpha,
+                                u_saved=u if u_saved else None, need_dx=need_dx)
+    torch.cuda.synchronize()
+    return y, u, dx, dA, dB
+
+
+def _oracle_D(inp):
+    codes, absmax = onf4.quantize(synth.bf16_bits_to_f32(inp["W"]))
+    return onf4.dequantize_exact(codes, absmax)
+
+
+def _check_full(q, inp, alpha, r, label):
+    from tests.gpu_util import host_f64
+    y, u, dx, dA, dB = _run_gpu(q, inp, alpha)
+    x, A, B, dY = (_f64(inp[k]) for k in ("x", "A", "B", "dY"))
+    D = _oracle_D(inp)
+    y_ref, U_ref = olora.forward(x, D, A, B, alpha, r)
+    dX_ref, dA_ref, dB_ref = olora.backward(x, dY, D, A, B, alpha, r)
+    errs = {
+        "y": olora.rel_err(host_f64(y), y_ref),
+        "u": olora.rel_err(host_f64(u), U_ref),
+        "dx": olora.rel_err(host_f64(dx), dX_ref),
+        "dA": olora.rel_err(host_f64(dA), dA_ref),
+        "dB": olora.rel_err(host_f64(dB), dB_ref),
+    }
+    print(label, {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= TOL, (label, k, v)
+    return errs
+
+
+def test_tiny_workload(q):
+    w = synth.WORKLOADS[0]
+    inp = synth.projection_inputs(w, 0)
+    _check_full(q, inp, w.alpha, w.r, "tiny")
+
+
+# (T, d_in, d_out, r): ragged token counts, partial tiles in every dimension,
+# ranks from 1 to the maximum.
+ODD = [(1, 64, 64, 1), (63, 128, 192, 8), (65, 192, 64, 16), (200, 320, 136, 64),
+       (130, 256, 8, 128), (257, 64, 520, 24), (129, 384, 264, 17), (17, 640, 1000, 40)]
+
+
+@pytest.mark.parametrize("T,K,N,r", ODD)
+def test_odd_shapes(q, T, K, N, r):
+    inp = synth.custom_inputs(1, T, K, N, r)
+    _check_full(q, inp, 16.0, r, f"odd T={T} K={K} N={N} r={r}")
+
+
+def test_recompute_u_and_skip_dx_paths(q):
+    from tests.gpu_util import host_f64
+    inp = synth.custom_inputs(2, 300, 256, 192, 16)
+    y, u, dx, dA, dB = _run_gpu(q, inp, 32.0, u_saved=True)
+    _, _, dx2, dA2, dB2 = _run_gpu(q, inp, 32.0, u_saved=False)
+    _, _, dx3, dA3, dB3 = _run_gpu(q, inp, 32.0, u_saved=True, need_dx=False)
+    assert dx3 is None
+    for a, b in ((dA, dA2), (dB, dB2), (dx, dx2)):
+        assert olora.rel_err(host_f64(b), host_f64(a)) <= TOL
+    assert torch.equal(dA3, dA) and torch.equal(dB3, dB)
+
+
+def test_bitwise_deterministic(q):
+    inp = synth.custom_inputs(3, 1000, 512, 384, 16)
+    r1 = _run_gpu(q, inp, 16.0)
+    r2 = _run_gpu(q, inp, 16.0)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
+def test_guard_bands_untouched(q):
+    """Outputs written through the C ABI stay inside their buffers."""
+    from tests.gpu_util import Guarded, dev_bf16
+    T, K, N, r = 131, 192, 200, 12
+    inp = synth.custom_inputs(4, T, K, N, r)
+    x, W, A, B, dY = (dev_bf16(inp[k]) for k in ("x", "W", "A", "B", "dY"))
+    codes, absmax = q.nf4_quantize(W)
+    gy, gu, gdx, gda, gdb = Guarded(T * N * 2), Guarded(T * r * 2), Guarded(T * K * 2), \
+        Guarded(K * r * 2), Guarded(r * N * 2)
+    lib = q.library()
+    stream = torch.cuda.current_stream().cuda_stream
+    st = lib.lora_nf4_fwd(T, K, N, r, 16.0, x.data_ptr(), codes.data_ptr(), absmax.data_ptr(),
+                          A.data_ptr(), B.data_ptr(), gy.ptr, gu.ptr, stream)
+    assert st == 0
+    nbytes = lib.lora_nf4_bwd_workspace_bytes(T, K, N, r)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    st = lib.lora_nf4_bwd(T, K, N, r, 16.0, x.data_ptr(), dY.data_ptr(), codes.data_ptr(),
+                          absmax.data_ptr(), A.data_ptr(), B.data_ptr(), gu.ptr, gdx.ptr, gda.ptr,
+                          gdb.ptr, ws.data_ptr(), ctypes.c_size_t(nbytes), stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    for g in (gy, gu, gdx, gda, gdb):
+        assert g.canaries_intact()
+    y_ref, _ = olora.forward(_f64(inp["x"]), _oracle_D(inp), _f64(inp["A"]), _f64(inp["B"]), 16.0, r)
+    from tests.gpu_util import host_f64
+    assert olora.rel_err(host_f64(gy.view(torch.bfloat16, (T, N))), y_ref) <= TOL
+
+
+def _sample_rows(T, n=48, seed=0):
+    g = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, T - 1], g.choice(T, size=n, replace=False)]))
+    return rows
+
+
+FULL = [(1, 0), (2, 1), (2, 3), (3, 0), (4, 1), (4, 4)]
+
+
+@pytest.mark.parametrize("wi,pi", FULL)
+def test_full_size_sampled(q, wi, pi):
+    """Full workload sizes, in the launch configuration the benchmark times."""
+    from tests.gpu_util import host_f64
+    w = synth.WORKLOADS[wi]
+    p = w.projections[pi]
+    inp = synth.projection_inputs(w, pi)
+    y, u, dx, dA, dB = _run_gpu(q, inp, w.alpha)
+    rows = _sample_rows(w.tokens)
+    x, A, B, dY = (_f64(inp[k]) for k in ("x", "A", "B", "dY"))
+    D = _oracle_D(inp)
+    y_ref, U_ref = olora.forward(x[rows], D, A, B, w.alpha, w.r)
+    dX_ref, _, _ = olora.backward(x[rows], dY[rows], D, A, B, w.alpha, w.r)
+    dA_ref, dB_ref = olora.lora_factor_grads(x, dY, A, B, w.alpha, w.r)
+    rows_t = torch.from_numpy(rows).cuda()
+    errs = {
+        "y": olora.rel_err(host_f64(y[rows_t]), y_ref),
+        "u": olora.rel_err(host_f64(u[rows_t]), U_ref),
+        "dx": olora.rel_err(host_f64(dx[rows_t]), dX_ref),
+        "dA": olora.rel_err(host_f64(dA), dA_ref),
+        "dB": olora.rel_err(host_f64(dB), dB_ref),
+    }
+    print(w.name, p.name, {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= TOL, (w.name, p.name, k, v)

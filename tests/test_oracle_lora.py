@@ -126,3 +126,10 @@ def test_rel_err_helper():
 def test_bf16_decode():
     bits = np.array([0x3F80, 0xBF80, 0x0000, 0x4049], dtype=np.uint16)
     assert list(lora.bf16_to_f64(bits)) == [1.0, -1.0, 0.0, 3.140625]
+
+
+def test_factor_grads_agree_with_full_backward():
+    x, D, A, B, dY, alpha, r = _case(8, T=9, K=128, N=7, r=5)
+    _, dA, dB = lora.backward(x, dY, D, A, B, alpha, r)
+    dA2, dB2 = lora.lora_factor_grads(x, dY, A, B, alpha, r)
+    assert np.allclose(dA, dA2, rtol=0, atol=1e-13) and np.allclose(dB, dB2, rtol=0, atol=1e-13)
