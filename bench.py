@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused NF4-LoRA linear, forward + backward, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = lora_nf4_fwd + lora_nf4_bwd (dX, dA, dB; U reused from the forward)
+over every projection of the workload, on seeded synthetic bf16 inputs already
+resident in HBM (the NF4 weights are quantized once, before timing, as at model
+load). Default workload: the Llama-3-8B q_proj projection, T = 8192 tokens
+(batch 4 x seq 2048), d_in = d_out = 4096, r = 16, alpha = 16.
+
+Prints ONE JSON line. `value` is algorithmic TFLOP/s of the whole step:
+4 T d_in d_out + 6 T r (d_in + d_out) per projection (no dequantization, no
+padding, no redundant in-tile work counted). `roofline` describes the forward
+kernel (one launch per lora_nf4_fwd call, timed with HIP events on the stream it
+runs on); `cpu_baseline` times the CPU fp64 oracle on a bounded token sample of
+the same projection.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+METRIC = "fused NF4-LoRA linear fwd+bwd TFLOP/s & tokens/s, % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 bf16 FLOP/clk x 2.4 GHz (published: 2.5 PFLOP/s dense)
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_lora_fwd_kernel_llama3-8b-q_proj.json")
+FWD_SOURCES = ("qlora_linear_amd/csrc/lora_fwd.hip", "qlora_linear_amd/csrc/device_common.h")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3-8b-q_proj",
+                    help="one of: " + ", ".join(w.name for w in synth.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def fwd_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in FWD_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per forward launch from the committed rocprofv3 counter runs, or
+    None when they were taken on a different version of the forward kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != fwd_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w: synth.Workload, target_s: float):
+    """The oracle as it stands, fwd + bwd of the workload's first projection on a
+    token sample sized to take about target_s seconds on this host."""
+    from oracle import lora as olora
+    from oracle import nf4 as onf4
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    p = w.projections[0]
+    inp = synth.projection_inputs(w, 0)
+    codes, absmax = onf4.quantize(synth.bf16_bits_to_f32(inp["W"]))   # one-time, not timed
+    x_all, dy_all = olora.bf16_to_f64(inp["x"]), olora.bf16_to_f64(inp["dY"])
+    A, B = olora.bf16_to_f64(inp["A"]), olora.bf16_to_f64(inp["B"])
+
+    def step(tok):
+        D = onf4.dequantize_exact(codes, absmax)
+        olora.forward(x_all[:tok], D, A, B, w.alpha, w.r)
+        olora.backward(x_all[:tok], dy_all[:tok], D, A, B, w.alpha, w.r)
+
+    tok = min(256, w.tokens)
+    t0 = time.perf_counter()
+    step(tok)
+    dt = time.perf_counter() - t0
+    tok = int(min(w.tokens, max(64, tok * target_s / max(dt, 1e-3))))
+    tok = max(64, (tok // 64) * 64)
+    t0 = time.perf_counter()
+    step(tok)
+    dt = time.perf_counter() - t0
+    fl = synth.flops(tok, p.d_in, p.d_out, w.r)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "seconds": round(dt, 3), "tokens_per_s": round(tok / dt, 1),
+            "sample": f"{p.name} {p.d_in}->{p.d_out} r={w.r}, {tok} of {w.tokens} tokens, "
+                      f"fp64 NumPy fwd+bwd incl. dequantization"}
+
+
+def to_dev_bf16(bits):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.to("cuda").view(torch.bfloat16)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus N with N > 1 is not supported "
+              "(the path shards over tokens with one all-reduce of dA/dB, which is not built here).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import qlora_linear_amd as q
+
+    w = next((x for x in synth.WORKLOADS if x.name == args.workload), None)
+    if w is None:
+        sys.exit(f"unknown workload {args.workload}")
+    q.library()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    # resident inputs, NF4 weights quantized once (model load), workspaces preallocated
+    projs = []
+    for pi, p in enumerate(w.projections):
+        inp = synth.projection_inputs(w, pi)
+        x, W, A, B, dY = (to_dev_bf16(inp[k]) for k in ("x", "W", "A", "B", "dY"))
+        codes, absmax = q.nf4_quantize(W)
+        del W
+        T, K, N, r = w.tokens, p.d_in, p.d_out, w.r
+        ws = torch.empty(q.lora_nf4_bwd_workspace_bytes(T, K, N, r), dtype=torch.uint8, device="cuda")
+        projs.append(dict(p=p, x=x, A=A, B=B, dY=dY, codes=codes, absmax=absmax, ws=ws,
+                          y=torch.empty((T, N), dtype=torch.bfloat16, device="cuda"),
+                          u=torch.empty((T, r), dtype=torch.bfloat16, device="cuda"),
+                          dx=torch.empty((T, K), dtype=torch.bfloat16, device="cuda"),
+                          dA=torch.empty((K, r), dtype=torch.bfloat16, device="cuda"),
+                          dB=torch.empty((r, N), dtype=torch.bfloat16, device="cuda")))
+    lib = q.library()
+    sp = stream.cuda_stream
+
+    def fwd(d):
+        p = d["p"]
+        st = lib.lora_nf4_fwd(w.tokens, p.d_in, p.d_out, w.r, w.alpha, d["x"].data_ptr(),
+                              d["codes"].data_ptr(), d["absmax"].data_ptr(), d["A"].data_ptr(),
+                              d["B"].data_ptr(), d["y"].data_ptr(), d["u"].data_ptr(), sp)
+        if st != 0:
+            raise q.LoraNF4Error("lora_nf4_fwd", st)
+
+    def bwd(d):
+        p = d["p"]
+        st = lib.lora_nf4_bwd(w.tokens, p.d_in, p.d_out, w.r, w.alpha, d["x"].data_ptr(),
+                              d["dY"].data_ptr(), d["codes"].data_ptr(), d["absmax"].data_ptr(),
+                              d["A"].data_ptr(), d["B"].data_ptr(), d["u"].data_ptr(),
+                              d["dx"].data_ptr(), d["dA"].data_ptr(), d["dB"].data_ptr(),
+                              d["ws"].data_ptr(), d["ws"].numel(), sp)
+        if st != 0:
+            raise q.LoraNF4Error("lora_nf4_bwd", st)
+
+    for _ in range(args.warmup):
+        for d in projs:
+            fwd(d)
+            bwd(d)
+    torch.cuda.synchronize()
+
+    # events around every forward launch (one kernel each) and every backward call
+    nev = args.steps * len(projs)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nev)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    i = 0
+    for _ in range(args.steps):
+        for d in projs:
+            ev[i][0].record(stream)
+            fwd(d)
+            ev[i][1].record(stream)
+            bwd(d)
+            ev[i][2].record(stream)
+            i += 1
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+
+    flops_step = sum(synth.flops(w.tokens, d["p"].d_in, d["p"].d_out, w.r) for d in projs)
+    tflops = flops_step / (ms_step * 1e-3) / 1e12
+    tokens_s = w.tokens / (ms_step * 1e-3)
+
+    # forward kernel of the largest projection: average launch duration
+    big = max(range(len(projs)), key=lambda j: projs[j]["p"].d_in * projs[j]["p"].d_out)
+    fwd_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(nev) if k % len(projs) == big]
+    bwd_ms = [ev[k][1].elapsed_time(ev[k][2]) for k in range(nev) if k % len(projs) == big]
+    pb = projs[big]["p"]
+    T, K, N, r = w.tokens, pb.d_in, pb.d_out, w.r
+    fwd_flops = 2 * T * K * N + 2 * T * K * r + 2 * T * r * N
+    fwd_avg = float(np.mean(fwd_ms))
+    achieved = fwd_flops / (fwd_avg * 1e-3) / 1e12
+    traffic = measured_traffic()
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.tokens, "batch": w.batch, "seq": w.seq,
+                   "r": w.r, "alpha": w.alpha,
+                   "projections": [f"{d['p'].name} {d['p'].d_in}->{d['p'].d_out}" for d in projs],
+                   "weights": "NF4 blocksize 64, fp32 absmax", "parallelism": "single GPU"},
+        "tokens_per_s": round(tokens_s, 1),
+        "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "fwd_ms": round(fwd_avg, 4),
+        "bwd_ms": round(float(np.mean(bwd_ms)), 4),
+        "host_wall_s": round(wall, 4),
+        "roofline": {"kernel": "lora_fwd_kernel", "projection": f"{pb.name} {K}->{N}",
+                     "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -11,6 +11,7 @@ namespace lnf4 {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // NF4 levels as float32 bit patterns, code 0..15. The QLoRA NormalFloat
 // construction: quantiles of N(0,1) at 8 evenly spaced probabilities from
@@ -48,6 +49,26 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// v_mfma_f32_32x32x16_bf16: D[32x32] = A[32x16] * B[16x32] + C, fp32 accumulate.
+//   A: lane l holds row (l & 31), reduction elements 8*(l >> 5) .. +7
+//   B: lane l holds column (l & 31), reduction elements 8*(l >> 5) .. +7
+//   C/D element e of lane l: column (l & 31), row 8*(e >> 2) + 4*(l >> 5) + (e & 3)
+__device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int mfma32_row(int e, int lane) {
+  return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+}
+
+// Element offset of (row, 16-byte chunk) in a [rows][64] bf16 LDS tile whose
+// chunks are XOR-swizzled by (row / 2) % 8. Fragment reads (16 consecutive rows
+// at one chunk) and whole-row writes are then free of bank conflicts.
+__device__ __forceinline__ int swz64(int row, int chunk) {
+  return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
 // Workgroup ids are dispatched round-robin over the 8 XCDs of MI355X (each with
