@@ -71,6 +71,44 @@ __device__ __forceinline__ int swz64(int row, int chunk) {
   return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
+// ---- buffer resources (raw buffers: byte offsets, out-of-range loads return 0) ----
+// Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format).
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           kBufferFlags);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(voff),
+                                                                         static_cast<int>(soff), 0));
+}
+
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<int>(voff),
+                                                                           static_cast<int>(soff), 0));
+}
+
+// 16 bytes per lane from global straight into LDS: lane i writes lds_base + 16 i
+// (lds_base must be uniform across the wave; it is passed through M0).
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t rs, void* lds_base, uint32_t voff,
+                                               uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds_base),
+                                           16, static_cast<int>(voff), static_cast<int>(soff), 0, 0);
+}
+
+// Wait until every vector-memory load this wave issued has landed (vmcnt = 0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Wait until at most N (< 16) vector-memory loads are outstanding. Loads retire
+// in issue order, so this waits for everything but the N most recent loads.
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 // Workgroup ids are dispatched round-robin over the 8 XCDs of MI355X (each with
 // its own L2). Map them so that each XCD receives one contiguous range of
 // logical tile ids; neighbouring logical tiles (which share input rows) then

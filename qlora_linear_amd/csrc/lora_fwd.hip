@@ -21,6 +21,8 @@
 //     wave owns 32 token rows of U.
 //   * Epilogue: bf16(s U) and B go through LDS, one more MFMA pass over the rank
 //     dimension adds (s U) B into the accumulators, and bf16 y is stored.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -30,26 +32,27 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kTileElems = 256 * 64;  // one bf16 [256][64] tile
-
-template <int RU>
-struct FwdLds {
-  static constexpr int kStageElems = 2 * kTileElems + RU * 64;  // x, W, A^T slice
-  static constexpr int kLutByte = 2 * kStageElems * 2;
-  static constexpr int kBytes = kLutByte + 64;
-};
+constexpr int kAStride = 72;          // A^T slice rows: 64 bf16 + 16 B pad (conflict-free b128 reads)
 
 // RU: U columns accumulated in the K-loop (r rounded up to 32); RE: rank
 // padded to the 16-wide reduction step of the epilogue MFMA.
+//
+// LDS (static, so the compiler can prove the direct-to-LDS loads into one stage
+// never alias reads of the other): level table, two stages of x [256][64],
+// dequantized weight [256][64] and A^T slice [RU][64], all bf16 and swizzled.
 template <int RU, int RE>
 __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
     int T, int K, int N, int r, float s, const uint16_t* __restrict__ x,
     const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ y,
     uint16_t* __restrict__ u_save) {
-  using L = FwdLds<RU>;
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* const lds = reinterpret_cast<uint16_t*>(smem);
-  float* const lut = reinterpret_cast<float*>(smem + L::kLutByte);
+  __shared__ float lut[16];
+  __shared__ __align__(16) uint16_t xs0[kTileElems];
+  __shared__ __align__(16) uint16_t xs1[kTileElems];
+  __shared__ __align__(16) uint16_t ws0[kTileElems];
+  __shared__ __align__(16) uint16_t ws1[kTileElems];
+  __shared__ __align__(16) uint16_t as0[RU * kAStride];
+  __shared__ __align__(16) uint16_t as1[RU * kAStride];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 128 x 64 each
@@ -62,79 +65,118 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
 
   if (tid < 16) lut[tid] = nf4_level(tid);
   // A^T slice rows r .. RU-1 stay zero in both stages
-  for (int e = tid; e < 2 * (RU - r) * 64; e += kThreads) {
-    const int st = e / ((RU - r) * 64), rem = e - st * (RU - r) * 64;
-    lds[st * L::kStageElems + 2 * kTileElems + r * 64 + rem] = 0;
+  for (int e = r * kAStride + tid; e < RU * kAStride; e += kThreads) {
+    as0[e] = 0;
+    as1[e] = 0;
   }
 
-  // ---- per-thread global->register staging of one K-step ------------------------
-  // x: 4 chunks of 16 B (rows c>>3, chunk c&7 for c = tid + 512 i)
-  // codes: row tid>>1, 16 bytes (32 codes) at half tid&1 of the 64-element block
+  // ---- global -> LDS / register staging of one K-step (buffer loads) ------------
+  // Buffer resources cover this tile's rows only: loads of rows past T (x) or N
+  // (weights) return zeros, and the per-step advance is a uniform scalar offset.
+  const int rows_x = min(T - m0, BM), rows_w = min(N - n0, BN);
+  const auto rs_x = make_rsrc(x + static_cast<size_t>(m0) * K, static_cast<uint32_t>(rows_x) * K * 2);
+  const auto rs_c = make_rsrc(codes + static_cast<size_t>(n0) * K2, static_cast<uint32_t>(rows_w) * K2);
+  const auto rs_s = make_rsrc(absmax + static_cast<size_t>(n0) * KB, static_cast<uint32_t>(rows_w) * KB * 4);
+  const auto rs_a = make_rsrc(A, static_cast<uint32_t>(K) * r * 2);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  // x: wave w fills rows 32 w .. 32 w + 31 with four 1 KB direct-to-LDS loads
+  // (8 rows each). Lane i lands on physical chunk i & 7 of its row, so it loads
+  // the logical chunk that the swizzle maps there.
+  uint32_t xvoff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = (wave * 4 + q) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    xvoff[q] = static_cast<uint32_t>(row) * K * 2 + chunk * 16;
+  }
+  auto load_x_lds = [&](int kt, uint16_t* stage) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      buf_load16_lds(rs_x, stage + (wave_u * 4 + q) * 512, xvoff[q], kt * BK * 2);
+  };
+  // codes: row tid>>1, 16 bytes (32 codes) at half tid&1 of the block; one absmax
+  const int crow = tid >> 1, chalf = tid & 1;
+  const uint32_t cvoff = static_cast<uint32_t>(crow) * K2 + chalf * 16;
+  const uint32_t svoff = static_cast<uint32_t>(crow) * KB * 4;
   // A slice: the 64 x r block of A is contiguous; 8-element chunks tid + 512 i
   // (r % 8 == 0 on this path)
   constexpr int kAPer = (64 * RU / 8 + kThreads - 1) / kThreads;
-  uint4 xr[4];
-  uint4 cr;
-  float ar;
-  uint4 arr[kAPer];
-  const int crow = tid >> 1, chalf = tid & 1;
-  const bool crow_ok = n0 + crow < N;
-  const uint8_t* cptr = codes + static_cast<size_t>(n0 + crow) * K2 + chalf * 16;
-  const float* aptr = absmax + static_cast<size_t>(n0 + crow) * KB;
-
-  auto load_stage = [&](int kt) {
-    const int k0 = kt * BK;
+  // Register sets for step s live in slot s & 1, so the prefetch of step kt + 2
+  // and the dequantization of step kt + 1 use different registers with no copies.
+  uint4 creg[2], areg[2][kAPer];
+  float sreg[2];
+  auto load_codes = [&](int kt, int slot) {
+    creg[slot] = buf_load16(rs_c, cvoff, kt * 32);
+    sreg[slot] = __uint_as_float(buf_load4(rs_s, svoff, kt * 4));
+  };
+  auto load_a = [&](int kt, int slot) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i, row = c >> 3, ch = c & 7;
-      xr[i] = (m0 + row < T)
-                  ? *reinterpret_cast<const uint4*>(x + static_cast<size_t>(m0 + row) * K + k0 + ch * 8)
-                  : uint4{0u, 0u, 0u, 0u};
-    }
-    if (crow_ok) {
-      cr = *reinterpret_cast<const uint4*>(cptr + kt * 32);
-      ar = aptr[kt];
-    } else {
-      cr = uint4{0u, 0u, 0u, 0u};
-      ar = 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < kAPer; ++i) {
-      const int c = tid + kThreads * i;
-      arr[i] = (c < 8 * r) ? *reinterpret_cast<const uint4*>(A + static_cast<size_t>(k0) * r + c * 8)
-                           : uint4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < kAPer; ++i)
+      areg[slot][i] = buf_load16(rs_a, (tid + kThreads * i) * 16, kt * BK * r * 2);
   };
 
-  auto store_stage = [&](int st) {
-    uint16_t* xs = lds + st * L::kStageElems;
-    uint16_t* ws = xs + kTileElems;
-    uint16_t* as = ws + kTileElems;
+  // Loop-invariant LDS element offsets. Every fragment row this lane reads has
+  // the same swizzle key ((row >> 1) & 7 depends only on lane & 31), so one chunk
+  // offset per k-slice serves all of its A and B fragments.
+  const int fkey = (l32 >> 1) & 7;
+  int choff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i, row = c >> 3, ch = c & 7;
-      *reinterpret_cast<uint4*>(xs + swz64(row, ch)) = xr[i];
-    }
-    const uint32_t cw[4] = {cr.x, cr.y, cr.z, cr.w};
+  for (int ks = 0; ks < 4; ++ks) choff[ks] = ((2 * ks + lh) ^ fkey) << 3;
+  const int a_off = (wm * 128 + l32) * 64;  // + i * 2048
+  const int b_off = (wn * 64 + l32) * 64;   // + j * 2048
+  const int ua_off = a_off + wn * 2048;
+  const int ub_off = l32 * kAStride;        // + u * 32 * kAStride
+  const int wkey = (crow >> 1) & 7;
+  int ws_off[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t w = cw[q];
-      uint4 o;
-      o.x = pack_bf16x2(lut[w & 15u] * ar, lut[(w >> 4) & 15u] * ar);
-      o.y = pack_bf16x2(lut[(w >> 8) & 15u] * ar, lut[(w >> 12) & 15u] * ar);
-      o.z = pack_bf16x2(lut[(w >> 16) & 15u] * ar, lut[(w >> 20) & 15u] * ar);
-      o.w = pack_bf16x2(lut[(w >> 24) & 15u] * ar, lut[w >> 28] * ar);
-      *reinterpret_cast<uint4*>(ws + swz64(crow, chalf * 4 + q)) = o;
+  for (int q = 0; q < 4; ++q) ws_off[q] = crow * 64 + (((chalf * 4 + q) ^ wkey) << 3);
+
+  // Dequantize the 8 codes of one dword (one NF4 block, scale a) to 8 bf16 and
+  // store them as one 16-byte chunk. Level addresses (4 * code) come from two
+  // byte planes: even codes (w << 2) & 0x3C.., odd codes (w >> 2) & 0x3C...
+  const unsigned char* lutb = reinterpret_cast<const unsigned char*>(lut);
+  auto lookup = [&](uint32_t w, float* v) {
+    const uint32_t ev = (w << 2) & 0x3C3C3C3Cu, od = (w >> 2) & 0x3C3C3C3Cu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = *reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(ev, 8 * j, 8));
+      v[2 * j + 1] = *reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(od, 8 * j, 8));
     }
+  };
+  auto finish_store = [&](const float* lv, float a, uint16_t* dst) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = lv[j] * a;
+    uint4 o;
+    o.x = pack_bf16x2(v[0], v[1]);
+    o.y = pack_bf16x2(v[2], v[3]);
+    o.z = pack_bf16x2(v[4], v[5]);
+    o.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(dst) = o;
+  };
+  auto dequant_store = [&](uint32_t w, float a, uint16_t* dst) {
+    float lv[8];
+    lookup(w, lv);
+    finish_store(lv, a, dst);
+  };
+  // Thread c < 8 r owns 8 consecutive j of one k of the A slice (r % 8 == 0) and
+  // writes them transposed: rows j0 .. j0 + 7 of the padded A^T tile, one address
+  // register plus immediate row offsets.
+  int a_dst[kAPer];
+#pragma unroll
+  for (int i = 0; i < kAPer; ++i) {
+    const int c = tid + kThreads * i, e = c * 8, kk = e / r, j0 = e - kk * r;
+    a_dst[i] = j0 * kAStride + kk;
+  }
+  auto store_a = [&](uint16_t* as, const uint4* arr) {
 #pragma unroll
     for (int i = 0; i < kAPer; ++i) {
-      const int c = tid + kThreads * i;
-      if (c < 8 * r) {
-        const int e = c * 8, kk = e / r, j0 = e - kk * r;  // 8 consecutive j of one k (r % 8 == 0)
+      if (tid + kThreads * i < 8 * r) {
         const uint32_t v[4] = {arr[i].x, arr[i].y, arr[i].z, arr[i].w};
 #pragma unroll
         for (int h = 0; h < 8; ++h)
-          as[swz64(j0 + h, kk >> 3) + (kk & 7)] = static_cast<uint16_t>(v[h >> 1] >> (16 * (h & 1)));
+          as[a_dst[i] + h * kAStride] = static_cast<uint16_t>(v[h >> 1] >> (16 * (h & 1)));
       }
     }
   };
@@ -152,60 +194,114 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) uacc[u][e] = 0.f;
 
-  load_stage(0);
-  __syncthreads();  // lut and zeroed A^T rows visible
-  store_stage(0);
-  if (KB > 1) load_stage(1);
+  // prologue: step 0 into stage 0, step 1 into registers
+  load_x_lds(0, xs0);
+  load_codes(0, 0);
+  load_a(0, 0);
+  wait_vmem();
+  __syncthreads();  // lut, zeroed A^T rows and x of step 0 visible
+  {
+    const uint32_t cw[4] = {creg[0].x, creg[0].y, creg[0].z, creg[0].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dequant_store(cw[q], sreg[0], ws0 + ws_off[q]);
+    store_a(as0, areg[0]);
+  }
+  load_codes(1, 1);  // past the last step these loads return unused data (or zeros)
+  load_a(1, 1);
   __syncthreads();
 
-  for (int kt = 0; kt < KB; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KB) store_stage(cur ^ 1);
-    if (kt + 2 < KB) load_stage(kt + 2);
-    const uint16_t* xs = lds + cur * L::kStageElems;
-    const uint16_t* ws = xs + kTileElems;
-    const uint16_t* as = ws + kTileElems;
+  // One K-step. `cur` is a compile-time stage index (the loop is unrolled by two)
+  // so every LDS address below is a loop-invariant register plus an immediate.
+  // The step is branch-free: on the last step the next-stage work lands in the
+  // unused stage (loads past the end read zeros or unused bytes), which keeps
+  // the whole step one basic block for the scheduler. Fragments of k-slice
+  // ks + 1 and the level lookups of code dword ks + 1 are issued one slice ahead
+  // of their use.
+  struct Frag {
+    uint4 a[4], b[2], au, bu[RU / 32 > 0 ? RU / 32 : 1];
+  };
+  auto kstep = [&](int kt, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value;
+    const uint16_t* xc = cur ? xs1 : xs0;
+    const uint16_t* wc = cur ? ws1 : ws0;
+    const uint16_t* ac = cur ? as1 : as0;
+    uint16_t* xn = cur ? xs0 : xs1;
+    uint16_t* wnx = cur ? ws0 : ws1;
+    uint16_t* an = cur ? as0 : as1;
+    load_x_lds(kt + 1, xn);
+    constexpr int nslot = cur ^ 1;  // registers of step kt + 1
+    load_codes(kt + 2, cur);
+    load_a(kt + 2, cur);
+    const uint32_t cw[4] = {creg[nslot].x, creg[nslot].y, creg[nslot].z, creg[nslot].w};
+    const float ar = sreg[nslot];
+    auto read_frag = [&](Frag& f, int ks) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const uint4*>(xc + a_off + i * 2048 + choff[ks]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) f.b[j] = *reinterpret_cast<const uint4*>(wc + b_off + j * 2048 + choff[ks]);
+      if constexpr (RU > 0) {
+        f.au = *reinterpret_cast<const uint4*>(xc + ua_off + choff[ks]);
+#pragma unroll
+        for (int u = 0; u < RU / 32; ++u)
+          f.bu[u] = *reinterpret_cast<const uint4*>(ac + ub_off + u * 32 * kAStride + (2 * ks + lh) * 8);
+      }
+    };
+    Frag fr[2];
+    float lv[2][8];
+    read_frag(fr[0], 0);
+    lookup(cw[0], lv[0]);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int ch = 2 * ks + lh;
-      uint4 a[4], b[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const uint4*>(xs + swz64(wm * 128 + i * 32 + l32, ch));
-#pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const uint4*>(ws + swz64(wn * 64 + j * 32 + l32, ch));
+      Frag& f = fr[ks & 1];
+      if (ks < 3) {
+        read_frag(fr[(ks + 1) & 1], ks + 1);
+        lookup(cw[ks + 1], lv[(ks + 1) & 1]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
       if constexpr (RU > 0) {
-        const uint4 au = *reinterpret_cast<const uint4*>(xs + swz64(wm * 128 + wn * 32 + l32, ch));
 #pragma unroll
-        for (int u = 0; u < RU / 32; ++u) {
-          const uint4 bu = *reinterpret_cast<const uint4*>(as + swz64(u * 32 + l32, ch));
-          uacc[u] = mfma32(au, bu, uacc[u]);
-        }
+        for (int u = 0; u < RU / 32; ++u) uacc[u] = mfma32(f.au, f.bu[u], uacc[u]);
       }
+      finish_store(lv[ks & 1], ar, wnx + ws_off[ks]);
+      if (ks == 3) store_a(an, areg[nslot]);
     }
+    // x of the next stage has landed in LDS (the codes, absmax and A loads of step
+    // kt + 2, issued after it, may still be in flight)
+    wait_vmem_upto<2 + kAPer>();
     __syncthreads();
+  };
+  for (int kt = 0; kt < KB; kt += 2) {
+    kstep(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < KB) kstep(kt + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: acc += bf16(s U) B ---------------------------------------------
-  constexpr int ES = RE + 8;  // LDS row stride (bf16) of the rank-wide tiles
-  uint16_t* us = lds;             // [256][ES]
-  uint16_t* bt = lds + 256 * ES;  // [256][ES]: B^T tile
+  // Rank-wide tiles: rows of RE bf16, padded to RE + 8 (conflict-free 16-byte
+  // reads) when that fits a [256][64] buffer, else swizzled like the main tiles.
+  constexpr int ES = RE + 8;
+  constexpr bool kPad = 256 * ES <= kTileElems;
+  auto ep = [](int row, int col) {  // element offset of (row, col)
+    if constexpr (kPad) return row * ES + col;
+    else return swz64(row, col >> 3) + (col & 7);
+  };
+  uint16_t* us = xs0;  // [256][RE] bf16(s U)
+  uint16_t* bt = ws0;  // [256][RE] B^T tile
 #pragma unroll
   for (int u = 0; u < RU / 32; ++u)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int row = wm * 128 + wn * 32 + mfma32_row(e, lane), col = u * 32 + l32;
       const float uv = uacc[u][e];
-      if (col < RE) us[row * ES + col] = to_bf16(s * uv);
+      if (col < RE) us[ep(row, col)] = to_bf16(s * uv);
       if (u_save != nullptr && tn == 0 && col < r && m0 + row < T)
         u_save[static_cast<size_t>(m0 + row) * r + col] = to_bf16(uv);
     }
   for (int e = tid; e < 256 * RE; e += kThreads) {
     const int j = e >> 8, c = e & 255;
-    bt[c * ES + j] = (j < r && n0 + c < N) ? B[static_cast<size_t>(j) * N + n0 + c] : uint16_t(0);
+    bt[ep(c, j)] = (j < r && n0 + c < N) ? B[static_cast<size_t>(j) * N + n0 + c] : uint16_t(0);
   }
   __syncthreads();
 #pragma unroll
@@ -213,10 +309,10 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
     uint4 a[4], b[2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const uint4*>(us + (wm * 128 + i * 32 + l32) * ES + ks * 16 + lh * 8);
+      a[i] = *reinterpret_cast<const uint4*>(us + ep(wm * 128 + i * 32 + l32, ks * 16 + lh * 8));
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      b[j] = *reinterpret_cast<const uint4*>(bt + (wn * 64 + j * 32 + l32) * ES + ks * 16 + lh * 8);
+      b[j] = *reinterpret_cast<const uint4*>(bt + ep(wn * 64 + j * 32 + l32, ks * 16 + lh * 8));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -239,16 +335,8 @@ template <int RU, int RE>
 hipError_t launch_fwd_t(int T, int K, int N, int r, float s, const uint16_t* x, const uint8_t* codes,
                         const float* absmax, const uint16_t* A, const uint16_t* B, uint16_t* y,
                         uint16_t* u_save, hipStream_t stream) {
-  constexpr int bytes = FwdLds<RU>::kBytes;
-  static bool attr_set = false;  // benign race: every thread sets the same value
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lora_fwd_kernel<RU, RE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   const int tiles = ((T + BM - 1) / BM) * ((N + BN - 1) / BN);
-  lora_fwd_kernel<RU, RE><<<tiles, kThreads, bytes, stream>>>(T, K, N, r, s, x, codes, absmax, A, B, y,
+  lora_fwd_kernel<RU, RE><<<tiles, kThreads, 0, stream>>>(T, K, N, r, s, x, codes, absmax, A, B, y,
                                                               u_save);
   return hipGetLastError();
 }
