@@ -71,6 +71,18 @@ __device__ __forceinline__ int swz64(int row, int chunk) {
   return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
+// ds_read_b64_tr_b16 (transposing LDS read). Within each group of 16 lanes, lane
+// m supplies the address of 4 consecutive b16 values; lane j receives value
+// (j & 3) of the chunks supplied by lanes 4 i + (j >> 2), i = 0..3. Pointing lane
+// m at row n0 + (m >> 2), columns c0 + 4 (m & 3) .. +3 of a row-major [n][c] tile
+// hands lane j the column c0 + j, rows n0 .. n0 + 3: a transposed fragment.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 // ---- buffer resources (raw buffers: byte offsets, out-of-range loads return 0) ----
 // Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format).
 constexpr int kBufferFlags = 0x00020000;

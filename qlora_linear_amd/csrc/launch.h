@@ -24,6 +24,21 @@ hipError_t launch_lora_fwd(int T, int K, int N, int r, float s, const uint16_t* 
                            const uint8_t* codes, const float* absmax, const uint16_t* A,
                            const uint16_t* B, uint16_t* y, uint16_t* u_save, hipStream_t stream);
 
+// dX kernel for ranks r % 8 == 0, r <= 64 (256 x 256 tiles); also writes bf16
+// G = s dY B^T [T, r] to g_out.
+bool lora_dx_supported(int r);
+hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* dy,
+                          const uint8_t* codes, const float* absmax, const uint16_t* A,
+                          const uint16_t* B, uint16_t* dx, uint16_t* g_out, hipStream_t stream);
+
+// Buffer resources address at most 2^31 - 1 bytes; the 256 x 256 kernels are
+// used only when every operand they cover fits.
+inline bool fits_buffer(int64_t T, int64_t K, int64_t N) {
+  const int64_t lim = (int64_t(1) << 31) - 1;
+  return T * K * 2 < lim && T * N * 2 < lim && N * K / 2 < lim && N * (K / 64) * 4 < lim &&
+         K * 128 * 2 < lim && N * 64 * 2 < lim;
+}
+
 // Backward plan: how the workspace is carved. Shared by the launcher and the
 // workspace-size query so the two always agree.
 struct BwdPlan {

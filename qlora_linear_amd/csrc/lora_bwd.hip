@@ -351,11 +351,16 @@ hipError_t launch_bwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
   uint16_t* u = reinterpret_cast<uint16_t*>(ws + p.off_u);
   float* pa = reinterpret_cast<float*>(ws + p.off_pa);
   float* pb = reinterpret_cast<float*>(ws + p.off_pb);
-  constexpr int BM = 128, BN = 128;
-  const int tiles = ((T + BM - 1) / BM) * ((K + BN - 1) / BN);
-  lora_dx_kernel<BM, BN, RT><<<tiles, kThreads, 0, stream>>>(T, K, N, r, s, dy, codes, absmax, A, B,
-                                                             dx, g);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (lora_dx_supported(r) && fits_buffer(T, K, N)) {
+    e = launch_lora_dx(T, K, N, r, s, dy, codes, absmax, A, B, dx, g, stream);
+  } else {
+    constexpr int BM = 128, BN = 128;
+    const int tiles = ((T + BM - 1) / BM) * ((K + BN - 1) / BN);
+    lora_dx_kernel<BM, BN, RT><<<tiles, kThreads, 0, stream>>>(T, K, N, r, s, dy, codes, absmax, A,
+                                                               B, dx, g);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   const uint16_t* uu = u_saved;
   if (uu == nullptr) {

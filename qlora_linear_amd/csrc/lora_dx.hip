@@ -1,0 +1,303 @@
+// Fused NF4-LoRA linear, backward input gradient (gfx950):
+//     G  = s dY B^T                      (bf16, also written out for dA)
+//     dX = dY deq(Wt) + G A^T
+// The pages replace autograd with hand-written backward kernels ("Unlocking AI
+// potential: Unsloth's algorithms and implementation", core-algorithms section).
+//
+// Work decomposition mirrors the forward kernel: 256 x 256 dX tile (tokens x
+// d_in) per 512-thread workgroup, 8 waves of 128 x 64, v_mfma_f32_32x32x16_bf16,
+// reduction over d_out in steps of 64. The base weight is used transposed here
+// (the reduction runs along its rows), so its 64 x 256 tile is dequantized into
+// LDS in its natural row-major orientation with 16-byte stores and read back with
+// ds_read_b64_tr_b16, which hands each lane a column of four consecutive rows:
+// exactly the MFMA B fragment. The same dY fragments accumulate G = s dY B^T for
+// the epilogue, which adds G A^T with one more MFMA pass over the rank.
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace lnf4 {
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kTileElems = 256 * 64;  // dY tile [256][64]
+constexpr int kDStride = 256 + 32;    // deq weight tile rows: 256 bf16 + 64 B pad
+constexpr int kDElems = 64 * kDStride;
+constexpr int kBStride = 72;          // B slice rows: 64 bf16 + 16 B pad
+
+template <int RU, int RE>
+__global__ __launch_bounds__(kThreads) void lora_dx_kernel(
+    int T, int K, int N, int r, float s, const uint16_t* __restrict__ dy,
+    const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ dx,
+    uint16_t* __restrict__ g_out) {
+  __shared__ float lut[16];
+  __shared__ __align__(16) uint16_t ys0[kTileElems];
+  __shared__ __align__(16) uint16_t ys1[kTileElems];
+  __shared__ __align__(16) uint16_t ds0[kDElems];
+  __shared__ __align__(16) uint16_t ds1[kDElems];
+  __shared__ __align__(16) uint16_t bs0[RU * kBStride];
+  __shared__ __align__(16) uint16_t bs1[RU * kBStride];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 128 x 64 each
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int mt = (T + BM - 1) / BM, kt_tiles = (K + BN - 1) / BN;
+  int tm, tk;
+  tile_coords(xcd_remap(blockIdx.x, mt * kt_tiles), mt, kt_tiles, 4, tm, tk);
+  const int m0 = tm * BM, k0 = tk * BN;
+  const int K2 = K / 2, KB = K / 64;
+  const int NS = (N + BK - 1) / BK;  // reduction steps over d_out
+
+  if (tid < 16) lut[tid] = nf4_level(tid);
+
+  // ---- buffer resources: out-of-range loads return zeros ------------------------
+  const int rows_t = min(T - m0, BM);
+  const auto rs_y = make_rsrc(dy + static_cast<size_t>(m0) * N, static_cast<uint32_t>(rows_t) * N * 2);
+  const auto rs_c = make_rsrc(codes + k0 / 2, static_cast<uint32_t>(static_cast<size_t>(N) * K2 - k0 / 2));
+  const auto rs_s = make_rsrc(absmax + k0 / 64, static_cast<uint32_t>((static_cast<size_t>(N) * KB - k0 / 64) * 4));
+  const auto rs_b = make_rsrc(B, static_cast<uint32_t>(r) * N * 2);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  // dY: wave w fills rows 32 w .. 32 w + 31 of the [256][64] tile, swizzled
+  uint32_t yvoff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = (wave * 4 + q) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    yvoff[q] = static_cast<uint32_t>(row) * N * 2 + chunk * 16;
+  }
+  auto load_y_lds = [&](int st, uint16_t* stage) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) buf_load16_lds(rs_y, stage + (wave_u * 4 + q) * 512, yvoff[q], st * BK * 2);
+  };
+  // weight codes: row nl = tid >> 3 of the 64-row step, 32 columns (one half of
+  // an NF4 block) at run tid & 7 of the 256-column tile
+  const int nl = tid >> 3, run = tid & 7;
+  const uint32_t cvoff = static_cast<uint32_t>(nl) * K2 + run * 16;
+  const uint32_t svoff = (static_cast<uint32_t>(nl) * KB + (run >> 1)) * 4;
+  // B slice: row j = tid >> 3 (< RU), 8 columns at chunk tid & 7; columns past
+  // d_out are zeroed here (the buffer range would only stop them at the end of B)
+  const int bj = tid >> 3, bch = tid & 7;
+  const uint32_t bvoff = static_cast<uint32_t>(bj) * N * 2 + bch * 16;
+  uint4 creg[2], breg[2];
+  float sreg[2];
+  // Three loads per thread and step (rows j >= r fall outside rs_b and read
+  // zeros), so every wave can wait on the same vmcnt.
+  auto load_regs = [&](int st, int slot) {
+    creg[slot] = buf_load16(rs_c, cvoff, st * 64 * K2);
+    sreg[slot] = __uint_as_float(buf_load4(rs_s, svoff, st * 64 * KB * 4));
+    const uint4 v = buf_load16(rs_b, bvoff, st * BK * 2);
+    breg[slot] = (st * BK + bch * 8 < N) ? v : uint4{0u, 0u, 0u, 0u};
+  };
+
+  const int fkey = (l32 >> 1) & 7;
+  int choff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) choff[ks] = ((2 * ks + lh) ^ fkey) << 3;
+  const int a_off = (wm * 128 + l32) * 64;  // + i * 2048
+  const int ga_off = a_off + wn * 2048;     // this wave's 32 rows of G
+  // transposed weight fragment: 16-lane group g, lane m within it
+  const int g16 = lane >> 4, m16 = lane & 15;
+  const int d_off = ((g16 >> 1) * 8 + (m16 >> 2)) * kDStride + wn * 64 + (g16 & 1) * 16 + 4 * (m16 & 3);
+  const int gb_off = l32 * kBStride + lh * 8;  // + u * 32 * kBStride + ks * 16
+
+  const unsigned char* lutb = reinterpret_cast<const unsigned char*>(lut);
+  auto lookup = [&](uint32_t w, float* v) {
+    const uint32_t ev = (w << 2) & 0x3C3C3C3Cu, od = (w >> 2) & 0x3C3C3C3Cu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = *reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(ev, 8 * j, 8));
+      v[2 * j + 1] = *reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(od, 8 * j, 8));
+    }
+  };
+  auto finish_store = [&](const float* lv, float a, uint16_t* dst) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = lv[j] * a;
+    uint4 o;
+    o.x = pack_bf16x2(v[0], v[1]);
+    o.y = pack_bf16x2(v[2], v[3]);
+    o.z = pack_bf16x2(v[4], v[5]);
+    o.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(dst) = o;
+  };
+  const int dw_off = nl * kDStride + run * 32;  // + q * 8
+  auto store_b = [&](uint16_t* bs, const uint4& v) {
+    if (bj < RU) *reinterpret_cast<uint4*>(bs + bj * kBStride + bch * 8) = v;
+  };
+
+  f32x16_t acc[4][2];
+  f32x16_t gacc[RU / 32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+#pragma unroll
+  for (int u = 0; u < RU / 32; ++u)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) gacc[u][e] = 0.f;
+
+  // prologue: step 0 into stage 0, step 1 into registers
+  load_y_lds(0, ys0);
+  load_regs(0, 0);
+  wait_vmem();
+  __syncthreads();  // lut and dY of step 0 visible
+  {
+    const uint32_t cw[4] = {creg[0].x, creg[0].y, creg[0].z, creg[0].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float lv[8];
+      lookup(cw[q], lv);
+      finish_store(lv, sreg[0], ds0 + dw_off + q * 8);
+    }
+    store_b(bs0, breg[0]);
+  }
+  load_regs(1, 1);
+  __syncthreads();
+
+  struct Frag {
+    uint4 a[4], b[2], ga, gb[RU / 32];
+  };
+  auto kstep = [&](int st, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value;
+    constexpr int nslot = cur ^ 1;
+    const uint16_t* yc = cur ? ys1 : ys0;
+    const uint16_t* dc = cur ? ds1 : ds0;
+    const uint16_t* bc = cur ? bs1 : bs0;
+    uint16_t* yn = cur ? ys0 : ys1;
+    uint16_t* dn = cur ? ds0 : ds1;
+    uint16_t* bn = cur ? bs0 : bs1;
+    load_y_lds(st + 1, yn);
+    load_regs(st + 2, cur);
+    const uint32_t cw[4] = {creg[nslot].x, creg[nslot].y, creg[nslot].z, creg[nslot].w};
+    const float ar = sreg[nslot];
+    auto read_frag = [&](Frag& f, int ks) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const uint4*>(yc + a_off + i * 2048 + choff[ks]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint16_t* p = dc + d_off + ks * 16 * kDStride + j * 32;
+        const uint2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * kDStride);
+        f.b[j] = uint4{lo.x, lo.y, hi.x, hi.y};
+      }
+      f.ga = *reinterpret_cast<const uint4*>(yc + ga_off + choff[ks]);
+#pragma unroll
+      for (int u = 0; u < RU / 32; ++u)
+        f.gb[u] = *reinterpret_cast<const uint4*>(bc + gb_off + u * 32 * kBStride + ks * 16);
+    };
+    Frag fr[2];
+    float lv[2][8];
+    read_frag(fr[0], 0);
+    lookup(cw[0], lv[0]);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      Frag& f = fr[ks & 1];
+      if (ks < 3) {
+        read_frag(fr[(ks + 1) & 1], ks + 1);
+        lookup(cw[ks + 1], lv[(ks + 1) & 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
+#pragma unroll
+      for (int u = 0; u < RU / 32; ++u) gacc[u] = mfma32(f.ga, f.gb[u], gacc[u]);
+      finish_store(lv[ks & 1], ar, dn + dw_off + ks * 8);
+      if (ks == 3) store_b(bn, breg[nslot]);
+    }
+    // dY of the next stage has landed (the step st + 2 register loads issued after
+    // it may still be in flight)
+    wait_vmem_upto<3>();
+    __syncthreads();
+  };
+  for (int st = 0; st < NS; st += 2) {
+    kstep(st, std::integral_constant<int, 0>{});
+    if (st + 1 < NS) kstep(st + 1, std::integral_constant<int, 1>{});
+  }
+
+  // ---- epilogue: acc += bf16(G) A^T ----------------------------------------------
+  constexpr int ES = RE + 8;
+  constexpr bool kPad = 256 * ES <= kTileElems;
+  auto ep = [](int row, int col) {
+    if constexpr (kPad) return row * ES + col;
+    else return swz64(row, col >> 3) + (col & 7);
+  };
+  uint16_t* gs = ys0;  // [256][RE] bf16(G), G = s dY B^T
+  uint16_t* at = ys1;  // [256][RE] rows k of A (A is [d_in, r] row-major)
+#pragma unroll
+  for (int u = 0; u < RU / 32; ++u)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = wm * 128 + wn * 32 + mfma32_row(e, lane), col = u * 32 + l32;
+      const uint16_t gv = to_bf16(s * gacc[u][e]);
+      if (col < RE) gs[ep(row, col)] = gv;
+      if (tk == 0 && col < r && m0 + row < T) g_out[static_cast<size_t>(m0 + row) * r + col] = gv;
+    }
+  for (int e = tid; e < 256 * (RE / 8); e += kThreads) {
+    const int c = e / (RE / 8), jc = e - c * (RE / 8);
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (k0 + c < K && jc * 8 < r)
+      v = *reinterpret_cast<const uint4*>(A + static_cast<size_t>(k0 + c) * r + jc * 8);
+    *reinterpret_cast<uint4*>(at + ep(c, jc * 8)) = v;
+  }
+  __syncthreads();
+  if (dx == nullptr) return;
+#pragma unroll
+  for (int ks = 0; ks < RE / 16; ++ks) {
+    uint4 a[4], b[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a[i] = *reinterpret_cast<const uint4*>(gs + ep(wm * 128 + i * 32 + l32, ks * 16 + lh * 8));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      b[j] = *reinterpret_cast<const uint4*>(at + ep(wn * 64 + j * 32 + l32, ks * 16 + lh * 8));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = k0 + wn * 64 + j * 32 + l32;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm * 128 + i * 32 + mfma32_row(e, lane);
+        if (row < T && col < K) dx[static_cast<size_t>(row) * K + col] = to_bf16(acc[i][j][e]);
+      }
+    }
+}
+
+template <int RU, int RE>
+hipError_t launch_dx_t(int T, int K, int N, int r, float s, const uint16_t* dy, const uint8_t* codes,
+                       const float* absmax, const uint16_t* A, const uint16_t* B, uint16_t* dx,
+                       uint16_t* g_out, hipStream_t stream) {
+  const int tiles = ((T + BM - 1) / BM) * ((K + BN - 1) / BN);
+  lora_dx_kernel<RU, RE><<<tiles, kThreads, 0, stream>>>(T, K, N, r, s, dy, codes, absmax, A, B, dx,
+                                                          g_out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool lora_dx_supported(int r) { return r % 8 == 0 && r <= 64; }
+
+hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* dy,
+                          const uint8_t* codes, const float* absmax, const uint16_t* A,
+                          const uint16_t* B, uint16_t* dx, uint16_t* g_out, hipStream_t stream) {
+  switch ((r + 15) / 16) {
+    case 1: return launch_dx_t<32, 16>(T, K, N, r, s, dy, codes, absmax, A, B, dx, g_out, stream);
+    case 2: return launch_dx_t<32, 32>(T, K, N, r, s, dy, codes, absmax, A, B, dx, g_out, stream);
+    case 3: return launch_dx_t<64, 48>(T, K, N, r, s, dy, codes, absmax, A, B, dx, g_out, stream);
+    case 4: return launch_dx_t<64, 64>(T, K, N, r, s, dy, codes, absmax, A, B, dx, g_out, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace lnf4

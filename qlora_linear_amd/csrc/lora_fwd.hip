@@ -346,7 +346,7 @@ hipError_t launch_fwd_t(int T, int K, int N, int r, float s, const uint16_t* x, 
 hipError_t launch_lora_fwd(int T, int K, int N, int r, float s, const uint16_t* x,
                            const uint8_t* codes, const float* absmax, const uint16_t* A,
                            const uint16_t* B, uint16_t* y, uint16_t* u_save, hipStream_t stream) {
-  if (r % 8 != 0)
+  if (r % 8 != 0 || !fits_buffer(T, K, N))
     return launch_lora_fwd_generic(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
   switch ((r + 15) / 16) {
     case 1: return launch_fwd_t<32, 16>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
