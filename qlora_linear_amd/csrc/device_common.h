@@ -117,8 +117,9 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // in issue order, so this waits for everything but the N most recent loads.
 template <int N>
 __device__ __forceinline__ void wait_vmem_upto() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  // gfx9 s_waitcnt: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Workgroup ids are dispatched round-robin over the 8 XCDs of MI355X (each with

@@ -39,9 +39,19 @@ inline bool fits_buffer(int64_t T, int64_t K, int64_t N) {
          K * 128 * 2 < lim && N * 64 * 2 < lim;
 }
 
+// Rank-r gradients dA, dB in one launch plus one reduce (r % 8 == 0, r <= 64).
+// part_a: [splits][r][K] fp32, part_b: [splits][r][N] fp32.
+bool lora_skinny_supported(int r);
+int skinny_splits(int64_t T, int64_t K, int64_t N);
+hipError_t launch_lora_skinny(int T, int K, int N, int r, float s, const uint16_t* x,
+                              const uint16_t* g, const uint16_t* dy, const uint16_t* u,
+                              float* part_a, float* part_b, int splits, uint16_t* dA,
+                              uint16_t* dB, hipStream_t stream);
+
 // Backward plan: how the workspace is carved. Shared by the launcher and the
 // workspace-size query so the two always agree.
 struct BwdPlan {
+  bool fast;          // 256 x 256 dX kernel and the one-launch rank-r gradients
   int rp;             // r rounded up to the MFMA reduction granularity (32)
   int splits_a;       // token splits of the dA reduction
   int splits_b;       // token splits of the dB reduction

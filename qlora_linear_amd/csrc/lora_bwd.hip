@@ -352,7 +352,7 @@ hipError_t launch_bwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
   float* pa = reinterpret_cast<float*>(ws + p.off_pa);
   float* pb = reinterpret_cast<float*>(ws + p.off_pb);
   hipError_t e;
-  if (lora_dx_supported(r) && fits_buffer(T, K, N)) {
+  if (p.fast) {
     e = launch_lora_dx(T, K, N, r, s, dy, codes, absmax, A, B, dx, g, stream);
   } else {
     constexpr int BM = 128, BN = 128;
@@ -368,6 +368,8 @@ hipError_t launch_bwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
     if ((e = hipGetLastError()) != hipSuccess) return e;
     uu = u;
   }
+  if (p.fast)
+    return launch_lora_skinny(T, K, N, r, s, x, g, dy, uu, pa, pb, p.splits_a, dA, dB, stream);
   const int tca = (T + p.splits_a - 1) / p.splits_a;
   const int tcb = (T + p.splits_b - 1) / p.splits_b;
   skinny_tn_kernel<RT><<<dim3((K + 127) / 128, p.splits_a), kThreads, 0, stream>>>(T, K, r, tca, x, g,
@@ -404,10 +406,15 @@ int choose_splits(int64_t T, int64_t cols) {
 
 BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r) {
   BwdPlan p{};
-  const int64_t rs = ((r + 15) / 16) * 16;
+  p.fast = lora_dx_supported(r) && lora_skinny_supported(r) && fits_buffer(T, K, N);
+  const int64_t rs = p.fast ? r : ((r + 15) / 16) * 16;
   p.rp = static_cast<int>(((r + 31) / 32) * 32);
-  p.splits_a = choose_splits(T, K);
-  p.splits_b = choose_splits(T, N);
+  if (p.fast) {
+    p.splits_a = p.splits_b = skinny_splits(T, K, N);
+  } else {
+    p.splits_a = choose_splits(T, K);
+    p.splits_b = choose_splits(T, N);
+  }
   size_t off = 0;
   p.off_g = off;
   off = align256(off + static_cast<size_t>(T) * r * 2);
