@@ -50,7 +50,16 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="run under rocprofv3 --pmc: one plain copy of COPY_BYTES (calibration), "
+                         "then --steps fwd+bwd steps; prints nothing else")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc output dirs (FETCH_SIZE, WRITE_SIZE runs of "
+                         "--counter-pass) into the traffic record used by the roofline")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20  # calibration copy: reads and writes exactly this many bytes
 
 
 def fwd_source_sha() -> str:
@@ -72,6 +81,55 @@ def measured_traffic():
     if t.get("source_sha") != fwd_source_sha():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def counter_means(d: str, counter: str) -> dict:
+    """Mean per-dispatch value of `counter` per kernel name from a rocprofv3 csv run."""
+    import csv
+    import glob
+    import collections
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                per[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def ingest_counters(fetch_dir: str, write_dir: str):
+    fetch = counter_means(fetch_dir, "FETCH_SIZE")
+    write = counter_means(write_dir, "WRITE_SIZE")
+
+    def pick(tbl, key):
+        hits = [v for k, v in tbl.items() if key in k]
+        if not hits:
+            raise SystemExit(f"no dispatch of {key} in the counter data")
+        return hits[0]
+
+    copy_key = "MulFunctor"  # the calibration copy: torch.mul(src, 1.0, out=dst)
+    cal_f = (COPY_BYTES / 1024) / pick(fetch, copy_key)
+    cal_w = (COPY_BYTES / 1024) / pick(write, copy_key)
+    rec = {"kernel": "lora_fwd_kernel", "workload": "llama3-8b-q_proj",
+           "commands": ["rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o run --output-format csv -- "
+                        "python3 bench.py --counter-pass --steps 2",
+                        "rocprofv3 --pmc WRITE_SIZE -d WRITE_DIR -o run --output-format csv -- "
+                        "python3 bench.py --counter-pass --steps 2",
+                        "python3 bench.py --ingest-counters FETCH_DIR WRITE_DIR"],
+           "source_sha": fwd_source_sha(),
+           "fetch_kib_raw": pick(fetch, "lora_fwd_kernel"), "write_kib_raw": pick(write, "lora_fwd_kernel"),
+           "calibration": {"copy_bytes": COPY_BYTES, "fetch_factor": cal_f, "write_factor": cal_w}}
+    rec["hbm_bytes_per_launch"] = round(1024 * (rec["fetch_kib_raw"] * cal_f + rec["write_kib_raw"] * cal_w))
+    others = {}
+    for key in ("lora_dx_kernel", "skinny_partial_kernel", "skinny_reduce2_kernel"):
+        try:
+            others[key] = round(1024 * (pick(fetch, key) * cal_f + pick(write, key) * cal_w))
+        except SystemExit:
+            pass
+    rec["other_kernels_hbm_bytes_per_launch"] = others
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def cpu_baseline(w: synth.Workload, target_s: float):
@@ -119,6 +177,9 @@ def to_dev_bf16(bits):
 
 def main():
     args = parse()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus N with N > 1 is not supported "
               "(the path shards over tokens with one all-reduce of dA/dB, which is not built here).",
@@ -169,6 +230,18 @@ def main():
                               d["ws"].data_ptr(), d["ws"].numel(), sp)
         if st != 0:
             raise q.LoraNF4Error("lora_nf4_bwd", st)
+
+    if args.counter_pass:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)  # plain copy of known size: calibrates the counters
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            for d in projs:
+                fwd(d)
+                bwd(d)
+        torch.cuda.synchronize()
+        return
 
     for _ in range(args.warmup):
         for d in projs:

@@ -1,0 +1,110 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora_nf4.h")
+
+LN_OK, LN_EINVAL, LN_ESHAPE, LN_EALIGN, LN_ERANK, LN_EWORKSPACE, LN_EALIAS = 0, -1, -2, -3, -4, -5, -6
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import qlora_linear_amd as q
+    if not os.path.exists(q.library_path):
+        from qlora_linear_amd import build
+        build.build()
+    return q.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_bwd",
+                            "lora_nf4_bwd_workspace_bytes", "lora_nf4_status_string"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    import qlora_linear_amd as q
+    assert sorted(q.EXPORTED_SYMBOLS) == declared_functions()
+
+
+def test_status_strings(lib):
+    for st in range(0, -8, -1):
+        s = lib.lora_nf4_status_string(st).decode()
+        assert s and s != "unknown status"
+    assert lib.lora_nf4_status_string(-99).decode() == "unknown status"
+
+
+# Plausible device-like addresses (never dereferenced: every call below fails validation).
+P = 1 << 40
+
+
+def _fwd(lib, T=8, K=64, N=64, r=8, alpha=16.0, x=P, c=P + (1 << 30), a=P + (2 << 30), A=P + (3 << 30),
+         B=P + (4 << 30), y=P + (5 << 30), u=None):
+    return lib.lora_nf4_fwd(T, K, N, r, alpha, x, c, a, A, B, y, u, None)
+
+
+def test_fwd_validation(lib):
+    assert _fwd(lib, x=None) == LN_EINVAL
+    assert _fwd(lib, T=0) == LN_EINVAL
+    assert _fwd(lib, alpha=float("nan")) == LN_EINVAL
+    assert _fwd(lib, r=0) == LN_ERANK
+    assert _fwd(lib, r=129) == LN_ERANK
+    assert _fwd(lib, K=100) == LN_ESHAPE
+    assert _fwd(lib, N=12) == LN_ESHAPE
+    assert _fwd(lib, x=P + 8) == LN_EALIGN
+    assert _fwd(lib, y=P) == LN_EALIAS                      # output on top of x
+    assert _fwd(lib, u=P + (5 << 30) + 64) == LN_EALIAS     # u_save inside y
+
+
+def test_bwd_validation_and_workspace(lib):
+    T, K, N, r = 8, 64, 64, 8
+    need = lib.lora_nf4_bwd_workspace_bytes(T, K, N, r)
+    assert need > 0
+    assert lib.lora_nf4_bwd_workspace_bytes(T, 65, N, r) == 0
+    assert lib.lora_nf4_bwd_workspace_bytes(T, K, N, 0) == 0
+    ptrs = [P + (i << 30) for i in range(12)]
+    x, dy, c, a, A, B, u, dx, dA, dB, ws = ptrs[:11]
+
+    def call(ws_ptr=ws, ws_bytes=need, **kw):
+        args = dict(x=x, dy=dy, c=c, a=a, A=A, B=B, u=u, dx=dx, dA=dA, dB=dB)
+        args.update(kw)
+        return lib.lora_nf4_bwd(T, K, N, r, 16.0, args["x"], args["dy"], args["c"], args["a"], args["A"],
+                                args["B"], args["u"], args["dx"], args["dA"], args["dB"], ws_ptr,
+                                ctypes.c_size_t(ws_bytes), None)
+
+    assert call(dA=None) == LN_EINVAL
+    assert call(ws_ptr=None) == LN_EWORKSPACE
+    assert call(ws_bytes=need - 1) == LN_EWORKSPACE
+    assert call(ws_ptr=ws + 16) == LN_EALIGN                # workspace must be 256-byte aligned
+    assert call(dx=x) == LN_EALIAS
+    assert call(dB=dA) == LN_EALIAS
+
+
+def test_quantize_validation(lib):
+    assert lib.nf4_quantize(None, 0, 4, 64, P, P + (1 << 30), None) == LN_EINVAL
+    assert lib.nf4_quantize(P, 2, 4, 64, P + (1 << 30), P + (2 << 30), None) == LN_EINVAL
+    assert lib.nf4_quantize(P, 0, 4, 96, P + (1 << 30), P + (2 << 30), None) == LN_ESHAPE
+    assert lib.nf4_quantize(P + 4, 0, 4, 64, P + (1 << 30), P + (2 << 30), None) == LN_EALIGN
+    assert lib.nf4_quantize(P, 0, 4, 64, P + 64, P + (2 << 30), None) == LN_EALIAS
+    assert lib.nf4_dequantize(P, P + (1 << 30), 4, 64, 3, P + (2 << 30), None) == LN_EINVAL
+    assert lib.nf4_dequantize(P, P + (1 << 30), 4, 64, 0, P + 16, None) == LN_EALIAS
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import qlora_linear_amd as q
+    with pytest.raises(ValueError):
+        q.nf4_quantize(torch.zeros(4, 64))
