@@ -10,8 +10,9 @@
 // (the reduction runs along its rows), so its 64 x 256 tile is dequantized into
 // LDS in its natural row-major orientation with 16-byte stores and read back with
 // ds_read_b64_tr_b16, which hands each lane a column of four consecutive rows:
-// exactly the MFMA B fragment. The same dY fragments accumulate G = s dY B^T for
-// the epilogue, which adds G A^T with one more MFMA pass over the rank.
+// exactly the MFMA B fragment. The same dY tile accumulates G = s dY B^T for the
+// epilogue (16 x 16 x 32 MFMAs for r <= 16, else 32 x 32 x 16), which adds G A^T
+// with one more MFMA pass over the rank.
 #include <type_traits>
 
 #include "device_common.h"
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ dx,
     uint16_t* __restrict__ g_out) {
-  __shared__ float lut[16];
+  __shared__ __align__(1024) float lut[16];  // first in LDS: level addresses need no base
   __shared__ __align__(16) uint16_t ys0[kTileElems];
   __shared__ __align__(16) uint16_t ys1[kTileElems];
   __shared__ __align__(16) uint16_t ds0[kDElems];
@@ -103,10 +104,20 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
   const int g16 = lane >> 4, m16 = lane & 15;
   const int d_off = ((g16 >> 1) * 8 + (m16 >> 2)) * kDStride + wn * 64 + (g16 & 1) * 16 + 4 * (m16 & 3);
   const int gb_off = l32 * kBStride + lh * 8;  // + u * 32 * kBStride + ks * 16
+  // r <= 16: 16 x 16 x 32 fragments of G rows wm * 128 + wn * 32 + 16 rb + (lane & 15)
+  constexpr bool kG16 = RU == 16;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int ga16_off = (wm * 128 + wn * 32 + l16) * 64;  // + rb * 1024
+  int choff16[2];
+#pragma unroll
+  for (int kq = 0; kq < 2; ++kq) choff16[kq] = ((4 * kq + lq) ^ (l16 >> 1)) << 3;
+  const int gb16_off = l16 * kBStride + 8 * lq;         // + kq * 32
 
   const unsigned char* lutb = reinterpret_cast<const unsigned char*>(lut);
   auto lookup = [&](uint32_t w, float* v) {
-    const uint32_t ev = (w << 2) & 0x3C3C3C3Cu, od = (w >> 2) & 0x3C3C3C3Cu;
+    uint32_t ev = (w << 2) & 0x3C3C3C3Cu, od = (w >> 2) & 0x3C3C3C3Cu;
+    // keep the two planes: otherwise each address is rebuilt as shift + mask
+    asm volatile("" : "+v"(ev), "+v"(od));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       v[2 * j] = *reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(ev, 8 * j, 8));
@@ -130,7 +141,8 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
   };
 
   f32x16_t acc[4][2];
-  f32x16_t gacc[RU / 32];
+  f32x16_t gacc[RU / 32 > 0 ? RU / 32 : 1];
+  f32x4_t gacc16[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -161,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
   __syncthreads();
 
   struct Frag {
-    uint4 a[4], b[2], ga, gb[RU / 32];
+    uint4 a[4], b[2], ga, gb[RU / 32 > 0 ? RU / 32 : 1], ga16[2], gb16;
   };
   auto kstep = [&](int st, auto cur_c) {
     constexpr int cur = decltype(cur_c)::value;
@@ -185,10 +197,18 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
         const uint2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * kDStride);
         f.b[j] = uint4{lo.x, lo.y, hi.x, hi.y};
       }
-      f.ga = *reinterpret_cast<const uint4*>(yc + ga_off + choff[ks]);
+      if constexpr (kG16) {
+        if (ks & 1) {  // one 32-wide k-slice of G per two 16-wide MFMA slices
+          f.ga16[0] = *reinterpret_cast<const uint4*>(yc + ga16_off + choff16[ks >> 1]);
+          f.ga16[1] = *reinterpret_cast<const uint4*>(yc + ga16_off + 1024 + choff16[ks >> 1]);
+          f.gb16 = *reinterpret_cast<const uint4*>(bc + gb16_off + (ks >> 1) * 32);
+        }
+      } else {
+        f.ga = *reinterpret_cast<const uint4*>(yc + ga_off + choff[ks]);
 #pragma unroll
-      for (int u = 0; u < RU / 32; ++u)
-        f.gb[u] = *reinterpret_cast<const uint4*>(bc + gb_off + u * 32 * kBStride + ks * 16);
+        for (int u = 0; u < RU / 32; ++u)
+          f.gb[u] = *reinterpret_cast<const uint4*>(bc + gb_off + u * 32 * kBStride + ks * 16);
+      }
     };
     Frag fr[2];
     float lv[2][8];
@@ -205,8 +225,15 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
+      if constexpr (kG16) {
+        if (ks & 1) {
+          gacc16[0] = mfma16(f.ga16[0], f.gb16, gacc16[0]);
+          gacc16[1] = mfma16(f.ga16[1], f.gb16, gacc16[1]);
+        }
+      } else {
 #pragma unroll
-      for (int u = 0; u < RU / 32; ++u) gacc[u] = mfma32(f.ga, f.gb[u], gacc[u]);
+        for (int u = 0; u < RU / 32; ++u) gacc[u] = mfma32(f.ga, f.gb[u], gacc[u]);
+      }
       finish_store(lv[ks & 1], ar, dn + dw_off + ks * 8);
       if (ks == 3) store_b(bn, breg[nslot]);
     }
@@ -238,6 +265,17 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
       if (col < RE) gs[ep(row, col)] = gv;
       if (tk == 0 && col < r && m0 + row < T) g_out[static_cast<size_t>(m0 + row) * r + col] = gv;
     }
+  if constexpr (kG16) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = wm * 128 + wn * 32 + rb * 16 + 4 * lq + e;
+        const uint16_t gv = to_bf16(s * gacc16[rb][e]);
+        gs[ep(row, l16)] = gv;
+        if (tk == 0 && l16 < r && m0 + row < T) g_out[static_cast<size_t>(m0 + row) * r + l16] = gv;
+      }
+  }
   for (int e = tid; e < 256 * (RE / 8); e += kThreads) {
     const int c = e / (RE / 8), jc = e - c * (RE / 8);
     uint4 v = {0u, 0u, 0u, 0u};
@@ -292,7 +330,7 @@ hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* d
                           const uint8_t* codes, const float* absmax, const uint16_t* A,
                           const uint16_t* B, uint16_t* dx, uint16_t* g_out, hipStream_t stream) {
   switch ((r + 15) / 16) {
-    case 1: return launch_dx_t<32, 16>(T, K, N, r, s, dy, codes, absmax, A, B, dx, g_out, stream);
+    case 1: return launch_dx_t<16, 16>(T, K, N, r, s, dy, codes, absmax, A, B, dx, g_out, stream);
     case 2: return launch_dx_t<32, 32>(T, K, N, r, s, dy, codes, absmax, A, B, dx, g_out, stream);
     case 3: return launch_dx_t<64, 48>(T, K, N, r, s, dy, codes, absmax, A, B, dx, g_out, stream);
     case 4: return launch_dx_t<64, 64>(T, K, N, r, s, dy, codes, absmax, A, B, dx, g_out, stream);

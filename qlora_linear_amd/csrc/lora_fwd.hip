@@ -17,8 +17,8 @@
 //     MFMAs consume one stage, the next stage's x is stored and its packed codes
 //     (already in registers) are dequantized into the other: level lookup in an
 //     LDS table, multiply by the row's absmax, round to bf16.
-//   * U = x A is accumulated in the same loop from the same x fragments: each
-//     wave owns 32 token rows of U.
+//   * U = x A is accumulated in the same loop from the same x tile: each wave
+//     owns 32 token rows of U (16 x 16 x 32 MFMAs for r <= 16, else 32 x 32 x 16).
 //   * Epilogue: bf16(s U) and B go through LDS, one more MFMA pass over the rank
 //     dimension adds (s U) B into the accumulators, and bf16 y is stored.
 #include <type_traits>
@@ -34,8 +34,8 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kTileElems = 256 * 64;  // one bf16 [256][64] tile
 constexpr int kAStride = 72;          // A^T slice rows: 64 bf16 + 16 B pad (conflict-free b128 reads)
 
-// RU: U columns accumulated in the K-loop (r rounded up to 32); RE: rank
-// padded to the 16-wide reduction step of the epilogue MFMA.
+// RU: U columns accumulated in the K-loop (16 for r <= 16, else r rounded up to
+// 32); RE: rank padded to the 16-wide reduction step of the epilogue MFMA.
 //
 // LDS (static, so the compiler can prove the direct-to-LDS loads into one stage
 // never alias reads of the other): level table, two stages of x [256][64],
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ y,
     uint16_t* __restrict__ u_save) {
-  __shared__ float lut[16];
+  __shared__ __align__(1024) float lut[16];  // first in LDS: level addresses need no base
   __shared__ __align__(16) uint16_t xs0[kTileElems];
   __shared__ __align__(16) uint16_t xs1[kTileElems];
   __shared__ __align__(16) uint16_t ws0[kTileElems];
@@ -127,6 +127,14 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
   const int b_off = (wn * 64 + l32) * 64;   // + j * 2048
   const int ua_off = a_off + wn * 2048;
   const int ub_off = l32 * kAStride;        // + u * 32 * kAStride
+  // r <= 16: 16 x 16 x 32 fragments of U rows wm * 128 + wn * 32 + 16 rb + (lane & 15)
+  constexpr bool kU16 = RU == 16;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int ua16_off = (wm * 128 + wn * 32 + l16) * 64;  // + rb * 1024
+  int choff16[2];
+#pragma unroll
+  for (int kq = 0; kq < 2; ++kq) choff16[kq] = ((4 * kq + lq) ^ (l16 >> 1)) << 3;
+  const int ub16_off = l16 * kAStride + 8 * lq;         // + kq * 32
   const int wkey = (crow >> 1) & 7;
   int ws_off[4];
 #pragma unroll
@@ -137,7 +145,9 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
   // byte planes: even codes (w << 2) & 0x3C.., odd codes (w >> 2) & 0x3C...
   const unsigned char* lutb = reinterpret_cast<const unsigned char*>(lut);
   auto lookup = [&](uint32_t w, float* v) {
-    const uint32_t ev = (w << 2) & 0x3C3C3C3Cu, od = (w >> 2) & 0x3C3C3C3Cu;
+    uint32_t ev = (w << 2) & 0x3C3C3C3Cu, od = (w >> 2) & 0x3C3C3C3Cu;
+    // keep the two planes: otherwise each address is rebuilt as shift + mask
+    asm volatile("" : "+v"(ev), "+v"(od));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       v[2 * j] = *reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(ev, 8 * j, 8));
@@ -183,6 +193,7 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
 
   f32x16_t acc[4][2];
   f32x16_t uacc[RU / 32 > 0 ? RU / 32 : 1];
+  f32x4_t uacc16[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -218,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
   // ks + 1 and the level lookups of code dword ks + 1 are issued one slice ahead
   // of their use.
   struct Frag {
-    uint4 a[4], b[2], au, bu[RU / 32 > 0 ? RU / 32 : 1];
+    uint4 a[4], b[2], au, bu[RU / 32 > 0 ? RU / 32 : 1], au16[2], bu16;
   };
   auto kstep = [&](int kt, auto cur_c) {
     constexpr int cur = decltype(cur_c)::value;
@@ -239,7 +250,13 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
       for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const uint4*>(xc + a_off + i * 2048 + choff[ks]);
 #pragma unroll
       for (int j = 0; j < 2; ++j) f.b[j] = *reinterpret_cast<const uint4*>(wc + b_off + j * 2048 + choff[ks]);
-      if constexpr (RU > 0) {
+      if constexpr (kU16) {
+        if (ks & 1) {  // one 32-wide k-slice of U per two 16-wide MFMA slices
+          f.au16[0] = *reinterpret_cast<const uint4*>(xc + ua16_off + choff16[ks >> 1]);
+          f.au16[1] = *reinterpret_cast<const uint4*>(xc + ua16_off + 1024 + choff16[ks >> 1]);
+          f.bu16 = *reinterpret_cast<const uint4*>(ac + ub16_off + (ks >> 1) * 32);
+        }
+      } else if constexpr (RU > 0) {
         f.au = *reinterpret_cast<const uint4*>(xc + ua_off + choff[ks]);
 #pragma unroll
         for (int u = 0; u < RU / 32; ++u)
@@ -261,7 +278,12 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
-      if constexpr (RU > 0) {
+      if constexpr (kU16) {
+        if (ks & 1) {
+          uacc16[0] = mfma16(f.au16[0], f.bu16, uacc16[0]);
+          uacc16[1] = mfma16(f.au16[1], f.bu16, uacc16[1]);
+        }
+      } else if constexpr (RU > 0) {
 #pragma unroll
         for (int u = 0; u < RU / 32; ++u) uacc[u] = mfma32(f.au, f.bu[u], uacc[u]);
       }
@@ -299,6 +321,18 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
       if (u_save != nullptr && tn == 0 && col < r && m0 + row < T)
         u_save[static_cast<size_t>(m0 + row) * r + col] = to_bf16(uv);
     }
+  if constexpr (kU16) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = wm * 128 + wn * 32 + rb * 16 + 4 * lq + e;
+        const float uv = uacc16[rb][e];
+        us[ep(row, l16)] = to_bf16(s * uv);
+        if (u_save != nullptr && tn == 0 && l16 < r && m0 + row < T)
+          u_save[static_cast<size_t>(m0 + row) * r + l16] = to_bf16(uv);
+      }
+  }
   for (int e = tid; e < 256 * RE; e += kThreads) {
     const int j = e >> 8, c = e & 255;
     bt[ep(c, j)] = (j < r && n0 + c < N) ? B[static_cast<size_t>(j) * N + n0 + c] : uint16_t(0);
@@ -349,7 +383,7 @@ hipError_t launch_lora_fwd(int T, int K, int N, int r, float s, const uint16_t* 
   if (r % 8 != 0 || !fits_buffer(T, K, N))
     return launch_lora_fwd_generic(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
   switch ((r + 15) / 16) {
-    case 1: return launch_fwd_t<32, 16>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
+    case 1: return launch_fwd_t<16, 16>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
     case 2: return launch_fwd_t<32, 32>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
     case 3: return launch_fwd_t<64, 48>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
     case 4: return launch_fwd_t<64, 64>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
