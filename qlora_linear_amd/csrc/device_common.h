@@ -84,6 +84,9 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 }
 
 // ---- buffer resources (raw buffers: byte offsets, out-of-range loads return 0) ----
+// The range check compares voffset + soffset (+ the instruction offset) against
+// the descriptor's byte count, so a run-ahead load that a uniform soffset pushes
+// past the end reads zeros, never the memory that follows (checked on gfx950).
 // Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format).
 constexpr int kBufferFlags = 0x00020000;
 

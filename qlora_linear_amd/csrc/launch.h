@@ -24,6 +24,13 @@ hipError_t launch_lora_fwd(int T, int K, int N, int r, float s, const uint16_t* 
                            const uint8_t* codes, const float* absmax, const uint16_t* A,
                            const uint16_t* B, uint16_t* y, uint16_t* u_save, hipStream_t stream);
 
+// Weight-streaming forward for a few tokens (1 <= T <= 32, r % 8 == 0, r <= 64):
+// one workgroup per 16 weight rows, no workspace.
+bool lora_fwd_stream_supported(int64_t T, int r);
+hipError_t launch_lora_fwd_stream(int T, int K, int N, int r, float s, const uint16_t* x,
+                                  const uint8_t* codes, const float* absmax, const uint16_t* A,
+                                  const uint16_t* B, uint16_t* y, uint16_t* u_save, hipStream_t stream);
+
 // dX kernel for ranks r % 8 == 0, r <= 64 (256 x 256 tiles); also writes bf16
 // G = s dY B^T [T, r] to g_out.
 bool lora_dx_supported(int r);

@@ -382,6 +382,8 @@ hipError_t launch_lora_fwd(int T, int K, int N, int r, float s, const uint16_t* 
                            const uint16_t* B, uint16_t* y, uint16_t* u_save, hipStream_t stream) {
   if (r % 8 != 0 || !fits_buffer(T, K, N))
     return launch_lora_fwd_generic(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
+  if (lora_fwd_stream_supported(T, r))
+    return launch_lora_fwd_stream(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
   switch ((r + 15) / 16) {
     case 1: return launch_fwd_t<16, 16>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
     case 2: return launch_fwd_t<32, 32>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);

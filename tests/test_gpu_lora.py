@@ -84,6 +84,21 @@ def test_odd_shapes(q, T, K, N, r):
     _check_full(q, inp, 16.0, r, f"odd T={T} K={K} N={N} r={r}")
 
 
+# Few tokens (T <= 32, r % 8 == 0, r <= 64): the weight-streaming forward. Cases
+# cover a single half-filled reduction chunk (d_in = 64), a half-filled last
+# chunk (d_in % 128 == 64), d_out not a multiple of the 16-row block, one and two
+# 16-token blocks, and every rank block count.
+FEW = [(1, 64, 16, 8), (1, 4096, 64, 16), (5, 192, 40, 16), (9, 64, 8, 56), (16, 256, 48, 24),
+       (17, 320, 136, 64), (32, 448, 1000, 32), (32, 128, 8, 8), (16, 4096, 4096, 16),
+       (32, 4096, 1024, 64)]
+
+
+@pytest.mark.parametrize("T,K,N,r", FEW)
+def test_few_token_shapes(q, T, K, N, r):
+    inp = synth.custom_inputs(5, T, K, N, r)
+    _check_full(q, inp, 16.0, r, f"few T={T} K={K} N={N} r={r}")
+
+
 def test_recompute_u_and_skip_dx_paths(q):
     from tests.gpu_util import host_f64
     inp = synth.custom_inputs(2, 300, 256, 192, 16)
@@ -104,10 +119,10 @@ def test_bitwise_deterministic(q):
         assert torch.equal(a, b)
 
 
-def test_guard_bands_untouched(q):
+@pytest.mark.parametrize("T,K,N,r", [(131, 192, 200, 12), (7, 320, 72, 24)])
+def test_guard_bands_untouched(q, T, K, N, r):
     """Outputs written through the C ABI stay inside their buffers."""
     from tests.gpu_util import Guarded, dev_bf16
-    T, K, N, r = 131, 192, 200, 12
     inp = synth.custom_inputs(4, T, K, N, r)
     x, W, A, B, dY = (dev_bf16(inp[k]) for k in ("x", "W", "A", "B", "dY"))
     codes, absmax = q.nf4_quantize(W)
