@@ -38,6 +38,16 @@ hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* d
                           const uint8_t* codes, const float* absmax, const uint16_t* A,
                           const uint16_t* B, uint16_t* dx, uint16_t* g_out, hipStream_t stream);
 
+// Weight-streaming dX for a few tokens (1 <= T <= 32, r % 8 == 0, r <= 64): split
+// over d_in column blocks and d_out slices, fp32 partials in part_x [S][T][K] and
+// part_g [S][T][r], then one reduce that stores dX and bf16 G.
+bool lora_dx_stream_supported(int64_t T, int r);
+void dx_stream_split(int64_t K, int64_t N, int* splits, int* rows_per_split);
+hipError_t launch_lora_dx_stream(int T, int K, int N, int r, float s, const uint16_t* dy,
+                                 const uint8_t* codes, const float* absmax, const uint16_t* A,
+                                 const uint16_t* B, uint16_t* dx, uint16_t* g_out, float* part_x,
+                                 float* part_g, hipStream_t stream);
+
 // Buffer resources address at most 2^31 - 1 bytes; the 256 x 256 kernels are
 // used only when every operand they cover fits.
 inline bool fits_buffer(int64_t T, int64_t K, int64_t N) {
@@ -59,10 +69,13 @@ hipError_t launch_lora_skinny(int T, int K, int N, int r, float s, const uint16_
 // workspace-size query so the two always agree.
 struct BwdPlan {
   bool fast;          // 256 x 256 dX kernel and the one-launch rank-r gradients
+  bool stream;        // few tokens: weight-streaming dX (with the fast rank-r gradients)
+  int splits_x;       // d_out slices of the weight-streaming dX
   int rp;             // r rounded up to the MFMA reduction granularity (32)
   int splits_a;       // token splits of the dA reduction
   int splits_b;       // token splits of the dB reduction
   size_t off_g, off_u, off_pa, off_pb;  // byte offsets into the workspace
+  size_t off_px, off_pg;                // weight-streaming dX partials
   size_t bytes;       // total workspace bytes
 };
 BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r);

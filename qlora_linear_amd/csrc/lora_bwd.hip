@@ -352,7 +352,11 @@ hipError_t launch_bwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
   float* pa = reinterpret_cast<float*>(ws + p.off_pa);
   float* pb = reinterpret_cast<float*>(ws + p.off_pb);
   hipError_t e;
-  if (p.fast) {
+  if (p.stream) {
+    e = launch_lora_dx_stream(T, K, N, r, s, dy, codes, absmax, A, B, dx, g,
+                              reinterpret_cast<float*>(ws + p.off_px),
+                              reinterpret_cast<float*>(ws + p.off_pg), stream);
+  } else if (p.fast) {
     e = launch_lora_dx(T, K, N, r, s, dy, codes, absmax, A, B, dx, g, stream);
   } else {
     constexpr int BM = 128, BN = 128;
@@ -424,6 +428,16 @@ BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r) {
   off = align256(off + static_cast<size_t>(p.splits_a) * K * rs * 4);
   p.off_pb = off;
   off = align256(off + static_cast<size_t>(p.splits_b) * N * rs * 4);
+  p.stream = p.fast && lora_dx_stream_supported(T, r);
+  p.splits_x = 0;
+  p.off_px = p.off_pg = off;
+  if (p.stream) {
+    int per = 0;
+    dx_stream_split(K, N, &p.splits_x, &per);
+    off = align256(off + static_cast<size_t>(p.splits_x) * T * K * 4);
+    p.off_pg = off;
+    off = align256(off + static_cast<size_t>(p.splits_x) * T * r * 4);
+  }
   p.bytes = off;
   return p;
 }

@@ -99,9 +99,10 @@ def test_few_token_shapes(q, T, K, N, r):
     _check_full(q, inp, 16.0, r, f"few T={T} K={K} N={N} r={r}")
 
 
-def test_recompute_u_and_skip_dx_paths(q):
+@pytest.mark.parametrize("T,K,N,r", [(300, 256, 192, 16), (7, 320, 200, 24)])
+def test_recompute_u_and_skip_dx_paths(q, T, K, N, r):
     from tests.gpu_util import host_f64
-    inp = synth.custom_inputs(2, 300, 256, 192, 16)
+    inp = synth.custom_inputs(2, T, K, N, r)
     y, u, dx, dA, dB = _run_gpu(q, inp, 32.0, u_saved=True)
     _, _, dx2, dA2, dB2 = _run_gpu(q, inp, 32.0, u_saved=False)
     _, _, dx3, dA3, dB3 = _run_gpu(q, inp, 32.0, u_saved=True, need_dx=False)
