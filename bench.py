@@ -14,7 +14,9 @@ Prints ONE JSON line. `value` is algorithmic TFLOP/s of the whole step:
 padding, no redundant in-tile work counted). `roofline` describes the forward
 kernel (one launch per lora_nf4_fwd call, timed with HIP events on the stream it
 runs on); `cpu_baseline` times the CPU fp64 oracle on a bounded token sample of
-the same projection.
+the same projection; `small_tokens` times forward and backward of the largest
+projection at a few tokens (the weight-streaming kernels), where the bound is
+reading the packed weight from HBM.
 """
 from __future__ import annotations
 
@@ -50,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--small-tokens", type=int, default=16,
+                    help="token count of the weight-bound measurement (0: skip)")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run under rocprofv3 --pmc: one plain copy of COPY_BYTES (calibration), "
                          "then --steps fwd+bwd steps; prints nothing else")
@@ -159,14 +163,69 @@ def cpu_baseline(w: synth.Workload, target_s: float):
     dt = time.perf_counter() - t0
     tok = int(min(w.tokens, max(64, tok * target_s / max(dt, 1e-3))))
     tok = max(64, (tok // 64) * 64)
+    # the whole workload may take well under target_s on a fast host: repeat it
+    reps = max(1, min(20, int(target_s / max(dt * tok / min(256, w.tokens), 1e-3))))
     t0 = time.perf_counter()
-    step(tok)
-    dt = time.perf_counter() - t0
+    for _ in range(reps):
+        step(tok)
+    dt = (time.perf_counter() - t0) / reps
     fl = synth.flops(tok, p.d_in, p.d_out, w.r)
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle", "seconds": round(dt, 3), "tokens_per_s": round(tok / dt, 1),
-            "sample": f"{p.name} {p.d_in}->{p.d_out} r={w.r}, {tok} of {w.tokens} tokens, "
+            "kind": "oracle", "seconds_per_pass": round(dt, 3), "passes": reps,
+            "tokens_per_s": round(tok / dt, 1),
+            "sample": f"{p.name} {p.d_in}->{p.d_out} r={w.r}, {tok} of {w.tokens} tokens"
+                      f"{f' x {reps} passes' if reps > 1 else ''}, "
                       f"fp64 NumPy fwd+bwd incl. dequantization"}
+
+
+def small_token_run(lib, q, torch, d, w, tokens, sp, reps=50):
+    """Forward and backward of one projection at a few tokens (first rows of the
+    resident x and dY), back to back through the C ABI with preallocated buffers;
+    HIP events on the stream bracket `reps` calls of each."""
+    p = d["p"]
+    T, K, N, r = min(tokens, w.tokens), p.d_in, p.d_out, w.r
+    x, dy = d["x"][:T], d["dY"][:T]
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    u = torch.empty((T, r), dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty((K, r), dtype=torch.bfloat16, device="cuda")
+    dB = torch.empty((r, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(q.lora_nf4_bwd_workspace_bytes(T, K, N, r), dtype=torch.uint8, device="cuda")
+
+    def fwd():
+        st = lib.lora_nf4_fwd(T, K, N, r, w.alpha, x.data_ptr(), d["codes"].data_ptr(),
+                              d["absmax"].data_ptr(), d["A"].data_ptr(), d["B"].data_ptr(),
+                              y.data_ptr(), u.data_ptr(), sp)
+        if st != 0:
+            raise q.LoraNF4Error("lora_nf4_fwd", st)
+
+    def bwd():
+        st = lib.lora_nf4_bwd(T, K, N, r, w.alpha, x.data_ptr(), dy.data_ptr(), d["codes"].data_ptr(),
+                              d["absmax"].data_ptr(), d["A"].data_ptr(), d["B"].data_ptr(), u.data_ptr(),
+                              dx.data_ptr(), dA.data_ptr(), dB.data_ptr(), ws.data_ptr(), ws.numel(), sp)
+        if st != 0:
+            raise q.LoraNF4Error("lora_nf4_bwd", st)
+
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn in (("fwd", fwd), ("bwd", bwd)):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1000.0 / reps
+    wbytes = N * K // 2 + N * (K // 64) * 4  # packed codes + fp32 absmax, read once per call
+    return {"tokens": T, "projection": f"{p.name} {K}->{N}", "r": r,
+            "fwd_us": round(res["fwd"], 2), "bwd_us": round(res["bwd"], 2),
+            "weight_bytes": wbytes, "bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "fwd_weight_GBps": round(wbytes / res["fwd"] / 1e3, 1),
+            "fwd_frac": round(wbytes / res["fwd"] / 1e3 / PEAK_HBM_GBS, 4),
+            "bwd_weight_GBps": round(wbytes / res["bwd"] / 1e3, 1)}
 
 
 def to_dev_bf16(bits):
@@ -314,6 +373,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
+    if args.small_tokens > 0:
+        out["small_tokens"] = small_token_run(lib, q, torch, projs[big], w, args.small_tokens, sp)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
