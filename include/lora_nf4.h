@@ -65,6 +65,7 @@ typedef enum {
 typedef enum { LN_F32 = 0, LN_BF16 = 1 } ln_dtype;
 
 #define LN_MAX_RANK 128
+#define LN_MAX_PROJ 8   /* projections per lora_nf4_fwd_multi call */
 
 /*
  * nf4_quantize — blockwise NF4 quantization of w [rows, cols] (float32 or bf16
@@ -100,6 +101,34 @@ int lora_nf4_fwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_a
                  const uint16_t* x, const uint8_t* w_codes, const float* w_absmax,
                  const uint16_t* A, const uint16_t* B, uint16_t* y, uint16_t* u_save,
                  void* stream);
+
+/*
+ * lora_nf4_fwd_multi — the forward of n_proj LoRA projections that read the same
+ * x, e.g. q/k/v or gate/up (the target modules q_proj, k_proj, v_proj, o_proj of
+ * "Unsloth acceleration principles: CUDA kernel fusion and memory optimization",
+ * kernel-fusion section; the q/k/v projection products issued as one group on the
+ * "Unsloth in three lines of code" page, section 2). For every g < n_proj:
+ *     y[g] = x D_g^T + s (x A[g]) B[g],   u_save[g] = bf16(x A[g])
+ * exactly as n_proj calls of lora_nf4_fwd would compute them, but in one launch
+ * over the column tiles of all projections when they take the tiled path (x is
+ * then read once per token tile for all of them; narrow projections such as
+ * k/v at d_out = 1024 no longer leave most of the GPU idle).
+ *   n_proj               1 .. LN_MAX_PROJ
+ *   d_out                HOST array [n_proj]: d_out of each projection (% 8 == 0)
+ *   w_codes, w_absmax,
+ *   A, B, y              HOST arrays [n_proj] of DEVICE pointers, each laid out as
+ *                        for lora_nf4_fwd with that projection's d_out
+ *   u_save               NULL, or a HOST array [n_proj] whose entries may be NULL
+ * All projections share T, d_in, r and lora_alpha. The host arrays are read
+ * during the call only. Every output (each y[g], each u_save[g]) must be
+ * disjoint from every input and from the other outputs (LN_EALIAS). Errors as
+ * for lora_nf4_fwd, plus LN_EINVAL for n_proj out of range or a NULL array.
+ */
+int lora_nf4_fwd_multi(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d_out, int32_t r,
+                       float lora_alpha, const uint16_t* x, const uint8_t* const* w_codes,
+                       const float* const* w_absmax, const uint16_t* const* A,
+                       const uint16_t* const* B, uint16_t* const* y, uint16_t* const* u_save,
+                       void* stream);
 
 /*
  * lora_nf4_bwd — dX, dA, dB of the forward above for upstream gradient dY.

@@ -10,6 +10,7 @@ library has not been built, the first call raises.
     codes, absmax = nf4_quantize(w)                    # w [d_out, d_in] fp32/bf16
     y, u = lora_nf4_fwd(x, codes, absmax, A, B, lora_alpha)
     dx, dA, dB = lora_nf4_bwd(x, dy, codes, absmax, A, B, lora_alpha, u_saved=u)
+    ys, us = lora_nf4_fwd_multi(x, [cq, ck, cv], [aq, ak, av], [Aq, Ak, Av], [Bq, Bk, Bv], alpha)
 """
 from __future__ import annotations
 
@@ -20,8 +21,8 @@ import torch
 
 __all__ = [
     "LoraNF4Error", "library", "library_path", "nf4_quantize", "nf4_dequantize",
-    "lora_nf4_fwd", "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "status_string",
-    "EXPORTED_SYMBOLS", "LN_MAX_RANK",
+    "lora_nf4_fwd", "lora_nf4_fwd_multi", "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes",
+    "status_string", "EXPORTED_SYMBOLS", "LN_MAX_RANK", "LN_MAX_PROJ",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -29,8 +30,9 @@ library_path = os.path.join(_PKG, "liblora_nf4.so")
 
 LN_OK, LN_F32, LN_BF16 = 0, 0, 1
 LN_MAX_RANK = 128
-EXPORTED_SYMBOLS = ("nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_bwd",
-                    "lora_nf4_bwd_workspace_bytes", "lora_nf4_status_string")
+LN_MAX_PROJ = 8
+EXPORTED_SYMBOLS = ("nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_fwd_multi",
+                    "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_status_string")
 
 _lib = None
 
@@ -41,6 +43,8 @@ _SIGS = {
     "nf4_dequantize": (ctypes.c_int, [_p, _p, _i64, _i64, ctypes.c_int, _p, _p]),
     "lora_nf4_fwd": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_float,
                                     _p, _p, _p, _p, _p, _p, _p, _p]),
+    "lora_nf4_fwd_multi": (ctypes.c_int, [_i64, _i64, ctypes.c_int32, _p, ctypes.c_int32,
+                                          ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _p]),
     "lora_nf4_bwd": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_float,
                                     _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
     "lora_nf4_bwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, ctypes.c_int32]),
@@ -153,6 +157,38 @@ def lora_nf4_fwd(x, codes, absmax, A, B, lora_alpha: float, save_u: bool = True,
                                                   codes.data_ptr(), absmax.data_ptr(), A.data_ptr(),
                                                   B.data_ptr(), y.data_ptr(), _ptr(u), _stream(x)))
     return y, u
+
+
+def _ptr_array(ptrs):
+    arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def lora_nf4_fwd_multi(x, codes, absmax, A, B, lora_alpha: float, save_u: bool = True):
+    """Forward of several projections that share x (lists, one entry per projection):
+    returns ([y_g], [u_g] or None), the same values as one lora_nf4_fwd per projection."""
+    bf = torch.bfloat16
+    _dev(x, "x", bf, 2)
+    n = len(codes)
+    if not (len(absmax) == len(A) == len(B) == n) or n < 1:
+        raise ValueError("codes, absmax, A and B must be lists of the same non-zero length")
+    shapes = []
+    for g in range(n):
+        _dev(codes[g], f"codes[{g}]", torch.uint8, 2), _dev(absmax[g], f"absmax[{g}]", torch.float32, 2)
+        _dev(A[g], f"A[{g}]", bf, 2), _dev(B[g], f"B[{g}]", bf, 2)
+        shapes.append(_lora_shapes(x, codes[g], A[g], B[g]))
+    T, K, _, r = shapes[0]
+    if any(sh[3] != r for sh in shapes):
+        raise ValueError("all projections must share the rank r")
+    ys = [torch.empty((T, sh[2]), dtype=bf, device=x.device) for sh in shapes]
+    us = [torch.empty((T, r), dtype=bf, device=x.device) for _ in shapes] if save_u else None
+    d_out = (ctypes.c_int64 * n)(*[sh[2] for sh in shapes])
+    keep = [_ptr_array([t.data_ptr() for t in lst]) for lst in (codes, absmax, A, B, ys)]
+    u_arr = _ptr_array([t.data_ptr() for t in us]) if save_u else (None, None)
+    _check("lora_nf4_fwd_multi", library().lora_nf4_fwd_multi(
+        T, K, n, ctypes.cast(d_out, ctypes.c_void_p), r, float(lora_alpha), x.data_ptr(),
+        keep[0][1], keep[1][1], keep[2][1], keep[3][1], keep[4][1], u_arr[1], _stream(x)))
+    return ys, us
 
 
 def lora_nf4_bwd_workspace_bytes(T: int, K: int, N: int, r: int) -> int:

@@ -121,6 +121,48 @@ int lora_nf4_fwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_a
                                           y, u_save, static_cast<hipStream_t>(stream)));
 }
 
+int lora_nf4_fwd_multi(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d_out, int32_t r,
+                       float lora_alpha, const uint16_t* x, const uint8_t* const* w_codes,
+                       const float* const* w_absmax, const uint16_t* const* A,
+                       const uint16_t* const* B, uint16_t* const* y, uint16_t* const* u_save,
+                       void* stream) {
+  if (n_proj < 1 || n_proj > LN_MAX_PROJ) return LN_EINVAL;
+  if (x == nullptr || d_out == nullptr || w_codes == nullptr || w_absmax == nullptr ||
+      A == nullptr || B == nullptr || y == nullptr)
+    return LN_EINVAL;
+  if (!aligned16(x)) return LN_EALIGN;
+  const size_t t = T, k = d_in, rr = r;
+  Span outs[2 * LN_MAX_PROJ];
+  Span ins[1 + 4 * LN_MAX_PROJ];
+  int n_out = 0, n_in = 0;
+  int N[LN_MAX_PROJ];
+  ins[n_in++] = {x, t * k * 2};
+  for (int g = 0; g < n_proj; ++g) {
+    if (w_codes[g] == nullptr || w_absmax[g] == nullptr || A[g] == nullptr || B[g] == nullptr ||
+        y[g] == nullptr)
+      return LN_EINVAL;
+    const int st = check_linear_shape(T, d_in, d_out[g], r, lora_alpha);
+    if (st != LN_OK) return st;
+    uint16_t* u = u_save == nullptr ? nullptr : u_save[g];
+    if (!aligned16(w_codes[g]) || !aligned16(w_absmax[g]) || !aligned16(A[g]) || !aligned16(B[g]) ||
+        !aligned16(y[g]) || (u != nullptr && !aligned16(u)))
+      return LN_EALIGN;
+    const size_t n = d_out[g];
+    N[g] = static_cast<int>(d_out[g]);
+    outs[n_out++] = {y[g], t * n * 2};
+    outs[n_out++] = {u, t * rr * 2};
+    ins[n_in++] = {w_codes[g], n * k / 2};
+    ins[n_in++] = {w_absmax[g], n * k / 64 * 4};
+    ins[n_in++] = {A[g], k * rr * 2};
+    ins[n_in++] = {B[g], rr * n * 2};
+  }
+  if (any_alias(outs, n_out, ins, n_in)) return LN_EALIAS;
+  const float s = lora_alpha / static_cast<float>(r);
+  return hip_status(lnf4::launch_lora_fwd_multi(static_cast<int>(T), static_cast<int>(d_in), n_proj, N,
+                                                r, s, x, w_codes, w_absmax, A, B, y, u_save,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 size_t lora_nf4_bwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t r) {
   if (check_linear_shape(T, d_in, d_out, r, 1.0f) != LN_OK) return 0;
   return lnf4::plan_bwd(T, d_in, d_out, r).bytes;

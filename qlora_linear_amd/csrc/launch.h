@@ -24,6 +24,15 @@ hipError_t launch_lora_fwd(int T, int K, int N, int r, float s, const uint16_t* 
                            const uint8_t* codes, const float* absmax, const uint16_t* A,
                            const uint16_t* B, uint16_t* y, uint16_t* u_save, hipStream_t stream);
 
+// Several projections of the same x (q/k/v, gate/up) in one forward launch when
+// every projection takes the 256 x 256 tiles; otherwise one launch per projection.
+constexpr int kMaxProj = 8;
+hipError_t launch_lora_fwd_multi(int T, int K, int n_proj, const int* N, int r, float s,
+                                 const uint16_t* x, const uint8_t* const* codes,
+                                 const float* const* absmax, const uint16_t* const* A,
+                                 const uint16_t* const* B, uint16_t* const* y,
+                                 uint16_t* const* u_save, hipStream_t stream);
+
 // Weight-streaming forward for a few tokens (1 <= T <= 32, r % 8 == 0, r <= 64):
 // one workgroup per 16 weight rows, no workspace.
 bool lora_fwd_stream_supported(int64_t T, int r);

@@ -21,6 +21,11 @@
 //     owns 32 token rows of U (16 x 16 x 32 MFMAs for r <= 16, else 32 x 32 x 16).
 //   * Epilogue: bf16(s U) and B go through LDS, one more MFMA pass over the rank
 //     dimension adds (s U) B into the accumulators, and bf16 y is stored.
+//   * Several projections of the same x (q/k/v or gate/up: the multi-projection
+//     fusion) share one launch: the column tiles of all projections form one
+//     grid, each tile reads its projection's weight, A, B and output from a small
+//     table passed by value, and the tile order keeps a token tile's x hot in L2
+//     across projections. A single projection is a one-entry table.
 #include <type_traits>
 
 #include "device_common.h"
@@ -34,6 +39,19 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kTileElems = 256 * 64;  // one bf16 [256][64] tile
 constexpr int kAStride = 72;          // A^T slice rows: 64 bf16 + 16 B pad (conflict-free b128 reads)
 
+// Projections of one launch; tile_end[g] = column tiles of projections 0..g.
+struct ProjTable {
+  int n;
+  int tile_end[kMaxProj];
+  int N[kMaxProj];
+  const uint8_t* codes[kMaxProj];
+  const float* absmax[kMaxProj];
+  const uint16_t* A[kMaxProj];
+  const uint16_t* B[kMaxProj];
+  uint16_t* y[kMaxProj];
+  uint16_t* u[kMaxProj];
+};
+
 // RU: U columns accumulated in the K-loop (16 for r <= 16, else r rounded up to
 // 32); RE: rank padded to the 16-wide reduction step of the epilogue MFMA.
 //
@@ -41,11 +59,9 @@ constexpr int kAStride = 72;          // A^T slice rows: 64 bf16 + 16 B pad (con
 // never alias reads of the other): level table, two stages of x [256][64],
 // dequantized weight [256][64] and A^T slice [RU][64], all bf16 and swizzled.
 template <int RU, int RE>
-__global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
-    int T, int K, int N, int r, float s, const uint16_t* __restrict__ x,
-    const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ y,
-    uint16_t* __restrict__ u_save) {
+__global__ __launch_bounds__(kThreads) void lora_fwd_kernel(int T, int K, int r, float s,
+                                                            const uint16_t* __restrict__ x,
+                                                            const ProjTable tab) {
   __shared__ __align__(1024) float lut[16];  // first in LDS: level addresses need no base
   __shared__ __align__(16) uint16_t xs0[kTileElems];
   __shared__ __align__(16) uint16_t xs1[kTileElems];
@@ -57,9 +73,19 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 128 x 64 each
   const int l32 = lane & 31, lh = lane >> 5;
-  const int mt = (T + BM - 1) / BM, nt = (N + BN - 1) / BN;
+  const int mt = (T + BM - 1) / BM, nt_all = tab.tile_end[tab.n - 1];
   int tm, tn;
-  tile_coords(xcd_remap(blockIdx.x, mt * nt), mt, nt, 4, tm, tn);
+  tile_coords(xcd_remap(blockIdx.x, mt * nt_all), mt, nt_all, 4, tm, tn);
+  int gp = 0;  // this tile's projection (wave-uniform)
+  while (gp + 1 < tab.n && tn >= tab.tile_end[gp]) ++gp;
+  if (gp > 0) tn -= tab.tile_end[gp - 1];
+  const int N = tab.N[gp];
+  const uint8_t* __restrict__ codes = tab.codes[gp];
+  const float* __restrict__ absmax = tab.absmax[gp];
+  const uint16_t* __restrict__ A = tab.A[gp];
+  const uint16_t* __restrict__ B = tab.B[gp];
+  uint16_t* __restrict__ y = tab.y[gp];
+  uint16_t* __restrict__ u_save = tab.u[gp];
   const int m0 = tm * BM, n0 = tn * BN;
   const int K2 = K / 2, KB = K / BK;
 
@@ -366,13 +392,21 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
 }
 
 template <int RU, int RE>
-hipError_t launch_fwd_t(int T, int K, int N, int r, float s, const uint16_t* x, const uint8_t* codes,
-                        const float* absmax, const uint16_t* A, const uint16_t* B, uint16_t* y,
-                        uint16_t* u_save, hipStream_t stream) {
-  const int tiles = ((T + BM - 1) / BM) * ((N + BN - 1) / BN);
-  lora_fwd_kernel<RU, RE><<<tiles, kThreads, 0, stream>>>(T, K, N, r, s, x, codes, absmax, A, B, y,
-                                                              u_save);
+hipError_t launch_fwd_t(int T, int K, int r, float s, const uint16_t* x, const ProjTable& tab,
+                        hipStream_t stream) {
+  const int tiles = ((T + BM - 1) / BM) * tab.tile_end[tab.n - 1];
+  lora_fwd_kernel<RU, RE><<<tiles, kThreads, 0, stream>>>(T, K, r, s, x, tab);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_table(int T, int K, int r, float s, const uint16_t* x, const ProjTable& tab,
+                            hipStream_t stream) {
+  switch ((r + 15) / 16) {
+    case 1: return launch_fwd_t<16, 16>(T, K, r, s, x, tab, stream);
+    case 2: return launch_fwd_t<32, 32>(T, K, r, s, x, tab, stream);
+    case 3: return launch_fwd_t<64, 48>(T, K, r, s, x, tab, stream);
+    default: return launch_fwd_t<64, 64>(T, K, r, s, x, tab, stream);
+  }
 }
 
 }  // namespace
@@ -380,18 +414,53 @@ hipError_t launch_fwd_t(int T, int K, int N, int r, float s, const uint16_t* x, 
 hipError_t launch_lora_fwd(int T, int K, int N, int r, float s, const uint16_t* x,
                            const uint8_t* codes, const float* absmax, const uint16_t* A,
                            const uint16_t* B, uint16_t* y, uint16_t* u_save, hipStream_t stream) {
-  if (r % 8 != 0 || !fits_buffer(T, K, N))
+  if (r % 8 != 0 || r > 64 || !fits_buffer(T, K, N))
     return launch_lora_fwd_generic(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
   if (lora_fwd_stream_supported(T, r))
     return launch_lora_fwd_stream(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
-  switch ((r + 15) / 16) {
-    case 1: return launch_fwd_t<16, 16>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
-    case 2: return launch_fwd_t<32, 32>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
-    case 3: return launch_fwd_t<64, 48>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
-    case 4: return launch_fwd_t<64, 64>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
-    default:
-      return launch_lora_fwd_generic(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
+  ProjTable tab{};
+  tab.n = 1;
+  tab.tile_end[0] = (N + BN - 1) / BN;
+  tab.N[0] = N;
+  tab.codes[0] = codes;
+  tab.absmax[0] = absmax;
+  tab.A[0] = A;
+  tab.B[0] = B;
+  tab.y[0] = y;
+  tab.u[0] = u_save;
+  return launch_fwd_table(T, K, r, s, x, tab, stream);
+}
+
+hipError_t launch_lora_fwd_multi(int T, int K, int n_proj, const int* N, int r, float s,
+                                 const uint16_t* x, const uint8_t* const* codes,
+                                 const float* const* absmax, const uint16_t* const* A,
+                                 const uint16_t* const* B, uint16_t* const* y,
+                                 uint16_t* const* u_save, hipStream_t stream) {
+  bool tiled = r % 8 == 0 && r <= 64 && !lora_fwd_stream_supported(T, r) && n_proj <= kMaxProj;
+  for (int g = 0; g < n_proj; ++g) tiled = tiled && fits_buffer(T, K, N[g]);
+  if (!tiled) {  // each projection on its own path
+    for (int g = 0; g < n_proj; ++g) {
+      const hipError_t e = launch_lora_fwd(T, K, N[g], r, s, x, codes[g], absmax[g], A[g], B[g], y[g],
+                                           u_save == nullptr ? nullptr : u_save[g], stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
+  ProjTable tab{};
+  tab.n = n_proj;
+  int tiles = 0;
+  for (int g = 0; g < n_proj; ++g) {
+    tiles += (N[g] + BN - 1) / BN;
+    tab.tile_end[g] = tiles;
+    tab.N[g] = N[g];
+    tab.codes[g] = codes[g];
+    tab.absmax[g] = absmax[g];
+    tab.A[g] = A[g];
+    tab.B[g] = B[g];
+    tab.y[g] = y[g];
+    tab.u[g] = u_save == nullptr ? nullptr : u_save[g];
+  }
+  return launch_fwd_table(T, K, r, s, x, tab, stream);
 }
 
 }  // namespace lnf4

@@ -29,8 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert names == sorted(["nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_bwd",
-                            "lora_nf4_bwd_workspace_bytes", "lora_nf4_status_string"])
+    assert names == sorted(["nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_fwd_multi",
+                            "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -67,6 +67,43 @@ def test_fwd_validation(lib):
     assert _fwd(lib, x=P + 8) == LN_EALIGN
     assert _fwd(lib, y=P) == LN_EALIAS                      # output on top of x
     assert _fwd(lib, u=P + (5 << 30) + 64) == LN_EALIAS     # u_save inside y
+
+
+def _fwd_multi(lib, n=3, T=8, K=64, N=(64, 16, 16), r=8, alpha=16.0, x=P, ptrs=None, u=None, null=None):
+    # projection g's tensors sit at P + ((8 g + i) << 30), i = codes, absmax, A, B, y
+    vp = ctypes.c_void_p
+    base = {name: [P + ((8 * (g + 1) + i) << 30) for g in range(n)]
+            for i, name in enumerate(("codes", "absmax", "A", "B", "y"))}
+    if ptrs:
+        for name, (g, v) in ptrs.items():
+            base[name][g] = v
+    arrs = {name: (vp * n)(*vals) for name, vals in base.items()}
+    if null:
+        arrs[null] = None
+    d_out = (ctypes.c_int64 * n)(*list(N)[:n])
+    u_arr = None if u is None else (vp * n)(*u)
+    return lib.lora_nf4_fwd_multi(T, K, n, ctypes.cast(d_out, vp), r, alpha, x,
+                                  *(ctypes.cast(arrs[k], vp) if arrs[k] is not None else None
+                                    for k in ("codes", "absmax", "A", "B", "y")),
+                                  ctypes.cast(u_arr, vp) if u_arr is not None else None, None)
+
+
+def test_fwd_multi_validation(lib):
+    assert _fwd_multi(lib, n=0) == LN_EINVAL
+    assert _fwd_multi(lib, n=9, N=(64,) * 9) == LN_EINVAL
+    assert _fwd_multi(lib, null="A") == LN_EINVAL
+    assert _fwd_multi(lib, x=None) == LN_EINVAL
+    assert _fwd_multi(lib, ptrs={"B": (1, None)}) == LN_EINVAL
+    assert _fwd_multi(lib, N=(64, 12, 16)) == LN_ESHAPE
+    assert _fwd_multi(lib, K=100) == LN_ESHAPE
+    assert _fwd_multi(lib, r=0) == LN_ERANK
+    assert _fwd_multi(lib, alpha=float("inf")) == LN_EINVAL
+    assert _fwd_multi(lib, x=P + 8) == LN_EALIGN
+    assert _fwd_multi(lib, ptrs={"codes": (2, P + (3 << 30) + 4)}) == LN_EALIGN
+    y0 = P + ((8 * 1 + 4) << 30)
+    assert _fwd_multi(lib, ptrs={"y": (2, y0 + 256)}) == LN_EALIAS     # y[2] inside y[0]
+    assert _fwd_multi(lib, ptrs={"y": (1, P)}) == LN_EALIAS            # y[1] on top of x
+    assert _fwd_multi(lib, u=[None, y0, None]) == LN_EALIAS           # u[1] on top of y[0]
 
 
 def test_bwd_validation_and_workspace(lib):

@@ -182,3 +182,48 @@ def test_full_size_sampled(q, wi, pi):
     print(w.name, p.name, {k: f"{v:.2e}" for k, v in errs.items()})
     for k, v in errs.items():
         assert v <= TOL, (w.name, p.name, k, v)
+
+
+# Multi-projection forward: the same values as one lora_nf4_fwd per projection
+# (bitwise: each output tile runs the same kernel code on the same data), on the
+# tiled path (one launch), the few-token path and the generic path.
+MULTI = [(300, 256, (256, 64, 64), 16), (200, 320, (200, 40, 8), 24), (8, 192, (64, 16, 16), 16),
+         (150, 128, (72, 136), 12)]
+
+
+@pytest.mark.parametrize("T,K,Ns,r", MULTI)
+def test_fwd_multi_matches_single(q, T, K, Ns, r):
+    from tests.gpu_util import dev_bf16, host_f64
+    ins = [synth.custom_inputs(6 + g, T, K, N, r) for g, N in enumerate(Ns)]
+    x = dev_bf16(ins[0]["x"])
+    codes, absmax, A, B = [], [], [], []
+    for inp in ins:
+        c, a = q.nf4_quantize(dev_bf16(inp["W"]))
+        codes.append(c), absmax.append(a), A.append(dev_bf16(inp["A"])), B.append(dev_bf16(inp["B"]))
+    ys, us = q.lora_nf4_fwd_multi(x, codes, absmax, A, B, 16.0)
+    for g in range(len(Ns)):
+        y1, u1 = q.lora_nf4_fwd(x, codes[g], absmax[g], A[g], B[g], 16.0)
+        torch.cuda.synchronize()
+        assert torch.equal(ys[g], y1) and torch.equal(us[g], u1), (T, K, Ns, r, g)
+    # and against the oracle for the first projection
+    D = _oracle_D(ins[0])
+    y_ref, u_ref = olora.forward(_f64(ins[0]["x"]), D, _f64(ins[0]["A"]), _f64(ins[0]["B"]), 16.0, r)
+    assert olora.rel_err(host_f64(ys[0]), y_ref) <= TOL
+    assert olora.rel_err(host_f64(us[0]), u_ref) <= TOL
+
+
+def test_fwd_multi_full_size_qkv(q):
+    """Llama-3-8B q, k, v (4096 -> 4096, 1024, 1024) at 8192 tokens, r = 64, one shared x."""
+    from tests.gpu_util import dev_bf16
+    w = next(x for x in synth.WORKLOADS if x.name == "llama3-8b-attn-r64")
+    ins = [synth.projection_inputs(w, pi) for pi in range(3)]
+    x = dev_bf16(ins[0]["x"])
+    codes, absmax, A, B = [], [], [], []
+    for inp in ins:
+        c, a = q.nf4_quantize(dev_bf16(inp["W"]))
+        codes.append(c), absmax.append(a), A.append(dev_bf16(inp["A"])), B.append(dev_bf16(inp["B"]))
+    ys, us = q.lora_nf4_fwd_multi(x, codes, absmax, A, B, w.alpha)
+    for g in range(3):
+        y1, u1 = q.lora_nf4_fwd(x, codes[g], absmax[g], A[g], B[g], w.alpha)
+        torch.cuda.synchronize()
+        assert torch.equal(ys[g], y1) and torch.equal(us[g], u1), g
