@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the fused NF4-LoRA linear, forward + backward, on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--fuse] [--no-cpu-baseline]
 
 One step = lora_nf4_fwd + lora_nf4_bwd (dX, dA, dB; U reused from the forward)
 over every projection of the workload, on seeded synthetic bf16 inputs already
@@ -16,7 +16,9 @@ kernel (one launch per lora_nf4_fwd call, timed with HIP events on the stream it
 runs on); `cpu_baseline` times the CPU fp64 oracle on a bounded token sample of
 the same projection; `small_tokens` times forward and backward of the largest
 projection at a few tokens (the weight-streaming kernels), where the bound is
-reading the packed weight from HBM.
+reading the packed weight from HBM. With --fuse, projections that read the same
+activations in a transformer layer (q/k/v, gate/up) share one x and run their
+forward as one lora_nf4_fwd_multi launch; the FLOPs counted are unchanged.
 """
 from __future__ import annotations
 
@@ -49,6 +51,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3-8b-q_proj",
                     help="one of: " + ", ".join(w.name for w in synth.WORKLOADS))
+    ap.add_argument("--fuse", action="store_true",
+                    help="q/k/v and gate/up share x and run one multi-projection forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -272,6 +276,28 @@ def main():
     lib = q.library()
     sp = stream.cuda_stream
 
+    # forward units: one projection each, or (--fuse) the groups that share x
+    units, seen = [], {}
+    for j, d in enumerate(projs):
+        key = {"q_proj": "qkv", "k_proj": "qkv", "v_proj": "qkv", "gate_proj": "gu",
+               "up_proj": "gu"}.get(d["p"].name) if args.fuse else None
+        if key is not None and key in seen:
+            units[seen[key]].append(j)
+            d["x"] = projs[units[seen[key]][0]]["x"]  # the group reads one x
+        else:
+            if key is not None:
+                seen[key] = len(units)
+            units.append([j])
+    import ctypes
+    multi_args = {}
+    for ui, un in enumerate(units):
+        if len(un) > 1:
+            arr = lambda key: (ctypes.c_void_p * len(un))(*[projs[j][key].data_ptr() for j in un])
+            multi_args[ui] = dict(d_out=(ctypes.c_int64 * len(un))(*[projs[j]["p"].d_out for j in un]),
+                                  codes=arr("codes"), absmax=arr("absmax"), A=arr("A"), B=arr("B"),
+                                  y=arr("y"), u=arr("u"))
+    torch.cuda.empty_cache()
+
     def fwd(d):
         p = d["p"]
         st = lib.lora_nf4_fwd(w.tokens, p.d_in, p.d_out, w.r, w.alpha, d["x"].data_ptr(),
@@ -290,26 +316,41 @@ def main():
         if st != 0:
             raise q.LoraNF4Error("lora_nf4_bwd", st)
 
+    def fwd_unit(ui):
+        un = units[ui]
+        if len(un) == 1:
+            return fwd(projs[un[0]])
+        m, d0 = multi_args[ui], projs[un[0]]
+        cv = lambda a: ctypes.cast(a, ctypes.c_void_p)
+        st = lib.lora_nf4_fwd_multi(w.tokens, d0["p"].d_in, len(un), cv(m["d_out"]), w.r, w.alpha,
+                                    d0["x"].data_ptr(), cv(m["codes"]), cv(m["absmax"]), cv(m["A"]),
+                                    cv(m["B"]), cv(m["y"]), cv(m["u"]), sp)
+        if st != 0:
+            raise q.LoraNF4Error("lora_nf4_fwd_multi", st)
+
+    def step_all():
+        for ui, un in enumerate(units):
+            fwd_unit(ui)
+            for j in un:
+                bwd(projs[j])
+
     if args.counter_pass:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         torch.mul(src, 1.0, out=dst)  # plain copy of known size: calibrates the counters
         torch.cuda.synchronize()
         for _ in range(args.steps):
-            for d in projs:
-                fwd(d)
-                bwd(d)
+            step_all()
         torch.cuda.synchronize()
         return
 
     for _ in range(args.warmup):
-        for d in projs:
-            fwd(d)
-            bwd(d)
+        step_all()
     torch.cuda.synchronize()
 
-    # events around every forward launch (one kernel each) and every backward call
-    nev = args.steps * len(projs)
+    # events around every forward launch (one kernel each; one per unit) and the
+    # backward calls of the unit's projections
+    nev = args.steps * len(units)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nev)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -318,11 +359,12 @@ def main():
     t_start.record(stream)
     i = 0
     for _ in range(args.steps):
-        for d in projs:
+        for ui, un in enumerate(units):
             ev[i][0].record(stream)
-            fwd(d)
+            fwd_unit(ui)
             ev[i][1].record(stream)
-            bwd(d)
+            for j in un:
+                bwd(projs[j])
             ev[i][2].record(stream)
             i += 1
     t_end.record(stream)
@@ -335,13 +377,17 @@ def main():
     tflops = flops_step / (ms_step * 1e-3) / 1e12
     tokens_s = w.tokens / (ms_step * 1e-3)
 
-    # forward kernel of the largest projection: average launch duration
+    # forward launch of the unit holding the largest projection: average duration
     big = max(range(len(projs)), key=lambda j: projs[j]["p"].d_in * projs[j]["p"].d_out)
-    fwd_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(nev) if k % len(projs) == big]
-    bwd_ms = [ev[k][1].elapsed_time(ev[k][2]) for k in range(nev) if k % len(projs) == big]
+    bu = next(ui for ui, un in enumerate(units) if big in un)
+    fwd_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(nev) if k % len(units) == bu]
+    bwd_ms = [ev[k][1].elapsed_time(ev[k][2]) for k in range(nev) if k % len(units) == bu]
     pb = projs[big]["p"]
     T, K, N, r = w.tokens, pb.d_in, pb.d_out, w.r
-    fwd_flops = 2 * T * K * N + 2 * T * K * r + 2 * T * r * N
+    fwd_flops = sum(2 * T * projs[j]["p"].d_in * projs[j]["p"].d_out
+                    + 2 * T * r * (projs[j]["p"].d_in + projs[j]["p"].d_out) for j in units[bu])
+    unit_label = " + ".join(f"{projs[j]['p'].name} {projs[j]['p'].d_in}->{projs[j]['p'].d_out}"
+                            for j in units[bu])
     fwd_avg = float(np.mean(fwd_ms))
     achieved = fwd_flops / (fwd_avg * 1e-3) / 1e12
     traffic = measured_traffic()
@@ -362,13 +408,14 @@ def main():
         "config": {"workload": w.name, "tokens": w.tokens, "batch": w.batch, "seq": w.seq,
                    "r": w.r, "alpha": w.alpha,
                    "projections": [f"{d['p'].name} {d['p'].d_in}->{d['p'].d_out}" for d in projs],
-                   "weights": "NF4 blocksize 64, fp32 absmax", "parallelism": "single GPU"},
+                   "weights": "NF4 blocksize 64, fp32 absmax", "parallelism": "single GPU",
+                   "fused_forward": [[projs[j]["p"].name for j in un] for un in units if len(un) > 1]},
         "tokens_per_s": round(tokens_s, 1),
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(fwd_avg, 4),
         "bwd_ms": round(float(np.mean(bwd_ms)), 4),
         "host_wall_s": round(wall, 4),
-        "roofline": {"kernel": "lora_fwd_kernel", "projection": f"{pb.name} {K}->{N}",
+        "roofline": {"kernel": "lora_fwd_kernel", "projection": unit_label,
                      "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
