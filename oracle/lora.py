@@ -26,6 +26,13 @@ Layout: the base weight is the nn.Linear-oriented matrix Wt = W^T of shape
     dX = dY D + G A^T             [T, d_in]
     dA = x^T G                    [d_in, r]
     dB = s U^T dY                 [r, d_out]
+
+After training, the adapters are merged into the base weight and saved at 16 bits
+(the "Unsloth in three lines of code" page, section 4; "Reading the Unsloth
+changelog", command-line part of section 2, where saving turns the 4-bit model
+into a 16-bit one). In the same orientation:
+
+    W' = D + s (A B)^T            [d_out, d_in],   so that x W'^T = y
 """
 from __future__ import annotations
 
@@ -76,3 +83,10 @@ def lora_factor_grads(x, dY, A, B, alpha: float, r: int):
     s = float(alpha) / float(r)
     G = s * (dY @ B.T)
     return x.T @ G, s * ((x @ A).T @ dY)
+
+
+def merge(D, A, B, alpha: float, r: int):
+    """Merged base weight W' = D + (alpha/r) (A B)^T, [d_out, d_in], in float64."""
+    D, A, B = (np.asarray(v, dtype=np.float64) for v in (D, A, B))
+    s = float(alpha) / float(r)
+    return D + s * (A @ B).T

@@ -133,3 +133,36 @@ def test_factor_grads_agree_with_full_backward():
     _, dA, dB = lora.backward(x, dY, D, A, B, alpha, r)
     dA2, dB2 = lora.lora_factor_grads(x, dY, A, B, alpha, r)
     assert np.allclose(dA, dA2, rtol=0, atol=1e-13) and np.allclose(dB, dB2, rtol=0, atol=1e-13)
+
+
+# ---- merge: W' = D + s (A B)^T ------------------------------------------------------
+
+def test_merge_reproduces_the_forward():
+    """x W'^T equals the forward's y: pins orientation and scale of the merge
+    against the forward (itself pinned by the triple loop above)."""
+    g = np.random.default_rng(31)
+    T, K, N, r, alpha = 5, 12, 7, 3, 6.0
+    x, D = g.standard_normal((T, K)), g.standard_normal((N, K))
+    A, B = g.standard_normal((K, r)), g.standard_normal((r, N))
+    y, _ = lora.forward(x, D, A, B, alpha, r)
+    Wm = lora.merge(D, A, B, alpha, r)
+    assert Wm.shape == (N, K)
+    np.testing.assert_allclose(x @ Wm.T, y, rtol=1e-12, atol=1e-12)
+
+
+def test_merge_rank_one_elementwise():
+    """r = 1: W'[n, k] = D[n, k] + alpha a[k] b[n], written out element by element."""
+    g = np.random.default_rng(32)
+    K, N, alpha = 6, 4, 2.5
+    D = g.standard_normal((N, K))
+    a, b = g.standard_normal(K), g.standard_normal(N)
+    Wm = lora.merge(D, a.reshape(K, 1), b.reshape(1, N), alpha, 1)
+    for n in range(N):
+        for k in range(K):
+            assert abs(Wm[n, k] - (D[n, k] + alpha * a[k] * b[n])) <= 1e-12
+
+
+def test_merge_with_zero_b_is_the_dequantized_base():
+    g = np.random.default_rng(33)
+    D = g.standard_normal((8, 16))
+    assert np.array_equal(lora.merge(D, g.standard_normal((16, 4)), np.zeros((4, 8)), 16.0, 4), D)
