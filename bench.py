@@ -16,7 +16,8 @@ kernel (one launch per lora_nf4_fwd call, timed with HIP events on the stream it
 runs on); `cpu_baseline` times the CPU fp64 oracle on a bounded token sample of
 the same projection; `small_tokens` times forward and backward of the largest
 projection at a few tokens (the weight-streaming kernels), where the bound is
-reading the packed weight from HBM. With --fuse, projections that read the same
+reading the packed weight from HBM; `merge` times lora_nf4_merge of that
+projection (the 16-bit export, also HBM-bound). With --fuse, projections that read the same
 activations in a transformer layer (q/k/v, gate/up) share one x and run their
 forward as one lora_nf4_fwd_multi launch; the FLOPs counted are unchanged.
 """
@@ -232,6 +233,37 @@ def small_token_run(lib, q, torch, d, w, tokens, sp, reps=50):
             "bwd_weight_GBps": round(wbytes / res["bwd"] / 1e3, 1)}
 
 
+def merge_run(lib, q, torch, d, w, sp, reps=20):
+    """lora_nf4_merge of one projection into a preallocated bf16 [d_out, d_in], HIP
+    events around `reps` back-to-back C-ABI calls; bytes = packed weight in + bf16 out."""
+    p = d["p"]
+    K, N, r = p.d_in, p.d_out, w.r
+    out = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        st = lib.lora_nf4_merge(K, N, r, w.alpha, d["codes"].data_ptr(), d["absmax"].data_ptr(),
+                                d["A"].data_ptr(), d["B"].data_ptr(), 1, out.data_ptr(), sp)
+        if st != 0:
+            raise q.LoraNF4Error("lora_nf4_merge", st)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
+    nbytes = N * K // 2 + N * (K // 64) * 4 + N * K * 2
+    del out
+    return {"projection": f"{p.name} {K}->{N}", "r": r, "us": round(us, 2), "bytes": nbytes,
+            "bound": "hbm", "achieved": round(nbytes / us / 1e3, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
+
+
 def to_dev_bf16(bits):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
@@ -422,6 +454,7 @@ def main():
     }
     if args.small_tokens > 0:
         out["small_tokens"] = small_token_run(lib, q, torch, projs[big], w, args.small_tokens, sp)
+    out["merge"] = merge_run(lib, q, torch, projs[big], w, sp)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)

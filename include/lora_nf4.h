@@ -150,6 +150,24 @@ int lora_nf4_bwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_a
                  uint16_t* dx, uint16_t* dA, uint16_t* dB,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * lora_nf4_merge — the merged base weight for export after training,
+ *     W' = D + s (A B)^T,   [d_out, d_in],  s = lora_alpha / r
+ * (the adapters folded into the base and saved at 16 bits: "Unsloth in three
+ * lines of code", section 4; "Reading the Unsloth changelog", command-line part
+ * of section 2). Element (n, k) is the float32 sum of q[code] * absmax (rounded
+ * once to float32, as nf4_dequantize) and s * sum_j A[k][j] B[j][n] (float32
+ * accumulation), rounded once to out_dtype (LN_BF16: nearest-even). Then
+ * x W'^T reproduces lora_nf4_fwd's y up to rounding.
+ *   w_codes, w_absmax   as for lora_nf4_fwd ([d_out, d_in] base weight)
+ *   A bf16 [d_in, r],  B bf16 [r, d_out]
+ *   out  [d_out, d_in] of out_dtype (LN_BF16 or LN_F32), output
+ * d_in % 64 == 0, d_out >= 1, 1 <= r <= LN_MAX_RANK; out disjoint from the inputs.
+ */
+int lora_nf4_merge(int64_t d_in, int64_t d_out, int32_t r, float lora_alpha, const uint8_t* w_codes,
+                   const float* w_absmax, const uint16_t* A, const uint16_t* B, int out_dtype,
+                   void* out, void* stream);
+
 /* Workspace bytes lora_nf4_bwd needs for these sizes (0 if the sizes are invalid). */
 size_t lora_nf4_bwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t r);
 

@@ -11,6 +11,7 @@ library has not been built, the first call raises.
     y, u = lora_nf4_fwd(x, codes, absmax, A, B, lora_alpha)
     dx, dA, dB = lora_nf4_bwd(x, dy, codes, absmax, A, B, lora_alpha, u_saved=u)
     ys, us = lora_nf4_fwd_multi(x, [cq, ck, cv], [aq, ak, av], [Aq, Ak, Av], [Bq, Bk, Bv], alpha)
+    w_merged = lora_nf4_merge(codes, absmax, A, B, lora_alpha)   # bf16 [d_out, d_in]
 """
 from __future__ import annotations
 
@@ -21,7 +22,7 @@ import torch
 
 __all__ = [
     "LoraNF4Error", "library", "library_path", "nf4_quantize", "nf4_dequantize",
-    "lora_nf4_fwd", "lora_nf4_fwd_multi", "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes",
+    "lora_nf4_fwd", "lora_nf4_fwd_multi", "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_merge",
     "status_string", "EXPORTED_SYMBOLS", "LN_MAX_RANK", "LN_MAX_PROJ",
 ]
 
@@ -32,7 +33,8 @@ LN_OK, LN_F32, LN_BF16 = 0, 0, 1
 LN_MAX_RANK = 128
 LN_MAX_PROJ = 8
 EXPORTED_SYMBOLS = ("nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_fwd_multi",
-                    "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_status_string")
+                    "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_merge",
+                    "lora_nf4_status_string")
 
 _lib = None
 
@@ -48,6 +50,8 @@ _SIGS = {
     "lora_nf4_bwd": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_float,
                                     _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
     "lora_nf4_bwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, ctypes.c_int32]),
+    "lora_nf4_merge": (ctypes.c_int, [_i64, _i64, ctypes.c_int32, ctypes.c_float, _p, _p, _p, _p,
+                                      ctypes.c_int, _p, _p]),
     "lora_nf4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -219,3 +223,21 @@ def lora_nf4_bwd(x, dy, codes, absmax, A, B, lora_alpha: float, u_saved=None, ne
         absmax.data_ptr(), A.data_ptr(), B.data_ptr(), _ptr(u_saved), _ptr(dx), dA.data_ptr(),
         dB.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x)))
     return dx, dA, dB
+
+
+def lora_nf4_merge(codes, absmax, A, B, lora_alpha: float, dtype=torch.bfloat16):
+    """Merged base weight W' = deq(W) + (lora_alpha / r) (A B)^T, [d_out, d_in], bf16 or float32."""
+    _dev(codes, "codes", torch.uint8, 2), _dev(absmax, "absmax", torch.float32, 2)
+    _dev(A, "A", torch.bfloat16, 2), _dev(B, "B", torch.bfloat16, 2)
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("dtype must be float32 or bfloat16")
+    N, K, r = codes.shape[0], codes.shape[1] * 2, A.shape[1]
+    if A.shape[0] != K or B.shape != (r, N):
+        raise ValueError(f"inconsistent shapes: codes {tuple(codes.shape)}, A {tuple(A.shape)}, "
+                         f"B {tuple(B.shape)}")
+    out = torch.empty((N, K), dtype=dtype, device=codes.device)
+    dt = LN_BF16 if dtype == torch.bfloat16 else LN_F32
+    _check("lora_nf4_merge", library().lora_nf4_merge(K, N, r, float(lora_alpha), codes.data_ptr(),
+                                                      absmax.data_ptr(), A.data_ptr(), B.data_ptr(), dt,
+                                                      out.data_ptr(), _stream(codes)))
+    return out

@@ -163,6 +163,28 @@ int lora_nf4_fwd_multi(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int lora_nf4_merge(int64_t d_in, int64_t d_out, int32_t r, float lora_alpha, const uint8_t* w_codes,
+                   const float* w_absmax, const uint16_t* A, const uint16_t* B, int out_dtype,
+                   void* out, void* stream) {
+  if (w_codes == nullptr || w_absmax == nullptr || A == nullptr || B == nullptr || out == nullptr)
+    return LN_EINVAL;
+  if (out_dtype != LN_F32 && out_dtype != LN_BF16) return LN_EINVAL;
+  if (d_in < 1 || d_out < 1 || !std::isfinite(lora_alpha)) return LN_EINVAL;
+  if (r < 1 || r > LN_MAX_RANK) return LN_ERANK;
+  if (d_in % 64 != 0 || d_in > kMaxDim || d_out > kMaxDim || d_in * d_out > (int64_t(1) << 38))
+    return LN_ESHAPE;
+  if (!aligned16(w_codes) || !aligned16(w_absmax) || !aligned16(A) || !aligned16(B) || !aligned16(out))
+    return LN_EALIGN;
+  const size_t k = d_in, n = d_out, rr = r;
+  const Span outs[1] = {{out, n * k * (out_dtype == LN_BF16 ? 2 : 4)}};
+  const Span ins[4] = {{w_codes, n * k / 2}, {w_absmax, n * k / 64 * 4}, {A, k * rr * 2}, {B, rr * n * 2}};
+  if (any_alias(outs, 1, ins, 4)) return LN_EALIAS;
+  const float s = lora_alpha / static_cast<float>(r);
+  return hip_status(lnf4::launch_lora_merge(static_cast<int>(d_in), static_cast<int>(d_out), r, s, w_codes,
+                                            w_absmax, A, B, out_dtype == LN_BF16, out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 size_t lora_nf4_bwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t r) {
   if (check_linear_shape(T, d_in, d_out, r, 1.0f) != LN_OK) return 0;
   return lnf4::plan_bwd(T, d_in, d_out, r).bytes;

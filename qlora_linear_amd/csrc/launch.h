@@ -40,6 +40,11 @@ hipError_t launch_lora_fwd_stream(int T, int K, int N, int r, float s, const uin
                                   const uint8_t* codes, const float* absmax, const uint16_t* A,
                                   const uint16_t* B, uint16_t* y, uint16_t* u_save, hipStream_t stream);
 
+// Merged base weight W' = D + s (A B)^T, [N, K], bf16 or float32 (any r <= 128).
+hipError_t launch_lora_merge(int K, int N, int r, float s, const uint8_t* codes, const float* absmax,
+                             const uint16_t* A, const uint16_t* B, bool out_bf16, void* out,
+                             hipStream_t stream);
+
 // dX kernel for ranks r % 8 == 0, r <= 64 (256 x 256 tiles); also writes bf16
 // G = s dY B^T [T, r] to g_out.
 bool lora_dx_supported(int r);

@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_fwd_multi",
-                            "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_status_string"])
+                            "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_merge",
+                            "lora_nf4_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -128,6 +129,25 @@ def test_bwd_validation_and_workspace(lib):
     assert call(ws_ptr=ws + 16) == LN_EALIGN                # workspace must be 256-byte aligned
     assert call(dx=x) == LN_EALIAS
     assert call(dB=dA) == LN_EALIAS
+
+
+def test_merge_validation(lib):
+    c, a, A, B, o = (P + (i << 30) for i in range(5))
+
+    def call(K=64, N=16, r=8, alpha=16.0, dt=1, **kw):
+        p = dict(c=c, a=a, A=A, B=B, o=o)
+        p.update(kw)
+        return lib.lora_nf4_merge(K, N, r, alpha, p["c"], p["a"], p["A"], p["B"], dt, p["o"], None)
+
+    assert call(o=None) == LN_EINVAL
+    assert call(dt=5) == LN_EINVAL
+    assert call(N=0) == LN_EINVAL
+    assert call(alpha=float("nan")) == LN_EINVAL
+    assert call(r=0) == LN_ERANK
+    assert call(r=200) == LN_ERANK
+    assert call(K=96) == LN_ESHAPE
+    assert call(A=A + 2) == LN_EALIGN
+    assert call(o=c + 64) == LN_EALIAS
 
 
 def test_quantize_validation(lib):
