@@ -52,7 +52,8 @@ extern "C" {
 
 typedef enum {
     LN_OK = 0,
-    LN_EINVAL = -1,      /* null pointer, size < 1, non-finite alpha, unknown dtype   */
+    LN_EINVAL = -1,      /* null pointer, negative T or other size < 1, non-finite
+                            alpha, unknown dtype                                    */
     LN_ESHAPE = -2,      /* d_in or cols not a multiple of 64, d_out not a multiple
                             of 8, or a size beyond the 2^31 element-index range     */
     LN_EALIGN = -3,      /* a data pointer is not 16-byte aligned                    */
@@ -94,8 +95,9 @@ int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows, int6
  *   y        bf16 [T, d_out]  (output)
  *   u_save   bf16 [T, r] = x A, rounded to bf16 (output; may be NULL). Passing it
  *            to lora_nf4_bwd saves that pass recomputing it.
- * T >= 1, d_in % 64 == 0, d_out % 8 == 0, 1 <= r <= LN_MAX_RANK. s = lora_alpha / r
- * is formed in float32 on the host.
+ * T >= 0, d_in % 64 == 0, d_out % 8 == 0, 1 <= r <= LN_MAX_RANK. s = lora_alpha / r
+ * is formed in float32 on the host. T = 0 is an empty batch: nothing is computed
+ * and x, y, u_save may be NULL.
  */
 int lora_nf4_fwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha,
                  const uint16_t* x, const uint8_t* w_codes, const float* w_absmax,
@@ -141,7 +143,9 @@ int lora_nf4_fwd_multi(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d
  *            d_out, r) bytes, 256-byte aligned, owned by the caller; its contents
  *            on entry do not matter and on return are unspecified. Two calls that
  *            may run concurrently need separate workspaces.
- * Shape rules as for lora_nf4_fwd.
+ * Shape rules as for lora_nf4_fwd. With T = 0 (empty batch) dA and dB are set to
+ * zero (empty sums), x, dy, u_saved, dx and the workspace may be NULL, and
+ * lora_nf4_bwd_workspace_bytes is 0.
  */
 int lora_nf4_bwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha,
                  const uint16_t* x, const uint16_t* dy,

@@ -216,7 +216,7 @@ def lora_nf4_bwd(x, dy, codes, absmax, A, B, lora_alpha: float, u_saved=None, ne
     dB = torch.empty((r, N), dtype=bf, device=dev)
     nbytes = lora_nf4_bwd_workspace_bytes(T, K, N, r)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     _dev(workspace, "workspace", torch.uint8)
     _check("lora_nf4_bwd", library().lora_nf4_bwd(
         T, K, N, r, float(lora_alpha), x.data_ptr(), dy.data_ptr(), codes.data_ptr(),

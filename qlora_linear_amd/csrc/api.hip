@@ -36,9 +36,9 @@ bool any_alias(const Span* outs, int n_out, const Span* ins, int n_in) {
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 
-// Shared shape rules of the forward and backward.
+// Shared shape rules of the forward and backward (T = 0 is an empty batch).
 int check_linear_shape(int64_t T, int64_t K, int64_t N, int32_t r, float alpha) {
-  if (T < 1 || K < 1 || N < 1) return LN_EINVAL;
+  if (T < 0 || K < 1 || N < 1) return LN_EINVAL;
   if (!std::isfinite(alpha)) return LN_EINVAL;
   if (r < 1 || r > LN_MAX_RANK) return LN_ERANK;
   if (K % 64 != 0 || N % 8 != 0) return LN_ESHAPE;
@@ -55,7 +55,7 @@ extern "C" {
 const char* lora_nf4_status_string(int status) {
   switch (status) {
     case LN_OK: return "ok";
-    case LN_EINVAL: return "invalid argument (null pointer, size < 1, non-finite alpha or unknown dtype)";
+    case LN_EINVAL: return "invalid argument (null pointer, negative T or other size < 1, non-finite alpha or unknown dtype)";
     case LN_ESHAPE: return "unsupported shape (d_in/cols must be a multiple of 64, d_out a multiple of 8, sizes below 2^31)";
     case LN_EALIGN: return "data pointer not 16-byte aligned (workspace: 256-byte)";
     case LN_ERANK: return "LoRA rank r outside [1, LN_MAX_RANK]";
@@ -102,11 +102,11 @@ int lora_nf4_fwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_a
                  const uint16_t* x, const uint8_t* w_codes, const float* w_absmax,
                  const uint16_t* A, const uint16_t* B, uint16_t* y, uint16_t* u_save,
                  void* stream) {
-  if (x == nullptr || w_codes == nullptr || w_absmax == nullptr || A == nullptr || B == nullptr ||
-      y == nullptr)
-    return LN_EINVAL;
+  if (w_codes == nullptr || w_absmax == nullptr || A == nullptr || B == nullptr) return LN_EINVAL;
+  if (T != 0 && (x == nullptr || y == nullptr)) return LN_EINVAL;
   int st = check_linear_shape(T, d_in, d_out, r, lora_alpha);
   if (st != LN_OK) return st;
+  if (T == 0) return LN_OK;  // empty batch: nothing to compute
   if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_absmax) || !aligned16(A) ||
       !aligned16(B) || !aligned16(y) || (u_save != nullptr && !aligned16(u_save)))
     return LN_EALIGN;
@@ -127,7 +127,7 @@ int lora_nf4_fwd_multi(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d
                        const uint16_t* const* B, uint16_t* const* y, uint16_t* const* u_save,
                        void* stream) {
   if (n_proj < 1 || n_proj > LN_MAX_PROJ) return LN_EINVAL;
-  if (x == nullptr || d_out == nullptr || w_codes == nullptr || w_absmax == nullptr ||
+  if ((T != 0 && x == nullptr) || d_out == nullptr || w_codes == nullptr || w_absmax == nullptr ||
       A == nullptr || B == nullptr || y == nullptr)
     return LN_EINVAL;
   if (!aligned16(x)) return LN_EALIGN;
@@ -139,7 +139,7 @@ int lora_nf4_fwd_multi(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d
   ins[n_in++] = {x, t * k * 2};
   for (int g = 0; g < n_proj; ++g) {
     if (w_codes[g] == nullptr || w_absmax[g] == nullptr || A[g] == nullptr || B[g] == nullptr ||
-        y[g] == nullptr)
+        (T != 0 && y[g] == nullptr))
       return LN_EINVAL;
     const int st = check_linear_shape(T, d_in, d_out[g], r, lora_alpha);
     if (st != LN_OK) return st;
@@ -157,6 +157,7 @@ int lora_nf4_fwd_multi(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d
     ins[n_in++] = {B[g], rr * n * 2};
   }
   if (any_alias(outs, n_out, ins, n_in)) return LN_EALIAS;
+  if (T == 0) return LN_OK;  // empty batch
   const float s = lora_alpha / static_cast<float>(r);
   return hip_status(lnf4::launch_lora_fwd_multi(static_cast<int>(T), static_cast<int>(d_in), n_proj, N,
                                                 r, s, x, w_codes, w_absmax, A, B, y, u_save,
@@ -186,7 +187,7 @@ int lora_nf4_merge(int64_t d_in, int64_t d_out, int32_t r, float lora_alpha, con
 }
 
 size_t lora_nf4_bwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t r) {
-  if (check_linear_shape(T, d_in, d_out, r, 1.0f) != LN_OK) return 0;
+  if (T == 0 || check_linear_shape(T, d_in, d_out, r, 1.0f) != LN_OK) return 0;
   return lnf4::plan_bwd(T, d_in, d_out, r).bytes;
 }
 
@@ -195,11 +196,24 @@ int lora_nf4_bwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_a
                  const float* w_absmax, const uint16_t* A, const uint16_t* B,
                  const uint16_t* u_saved, uint16_t* dx, uint16_t* dA, uint16_t* dB,
                  void* workspace, size_t workspace_bytes, void* stream) {
-  if (x == nullptr || dy == nullptr || w_codes == nullptr || w_absmax == nullptr || A == nullptr ||
-      B == nullptr || dA == nullptr || dB == nullptr)
+  if (w_codes == nullptr || w_absmax == nullptr || A == nullptr || B == nullptr || dA == nullptr ||
+      dB == nullptr)
     return LN_EINVAL;
+  if (T != 0 && (x == nullptr || dy == nullptr)) return LN_EINVAL;
   int st = check_linear_shape(T, d_in, d_out, r, lora_alpha);
   if (st != LN_OK) return st;
+  if (T == 0) {  // empty batch: the gradients of A and B are empty sums
+    if (!aligned16(dA) || !aligned16(dB)) return LN_EALIGN;
+    const Span outs[2] = {{dA, static_cast<size_t>(d_in) * r * 2}, {dB, static_cast<size_t>(r) * d_out * 2}};
+    const Span ins[4] = {{w_codes, static_cast<size_t>(d_out) * d_in / 2},
+                         {w_absmax, static_cast<size_t>(d_out) * d_in / 64 * 4},
+                         {A, static_cast<size_t>(d_in) * r * 2}, {B, static_cast<size_t>(r) * d_out * 2}};
+    if (any_alias(outs, 2, ins, 4)) return LN_EALIAS;
+    hipError_t e = lnf4::launch_zero_u16(dA, static_cast<int64_t>(d_in) * r, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess)
+      e = lnf4::launch_zero_u16(dB, static_cast<int64_t>(r) * d_out, static_cast<hipStream_t>(stream));
+    return hip_status(e);
+  }
   if (!aligned16(x) || !aligned16(dy) || !aligned16(w_codes) || !aligned16(w_absmax) ||
       !aligned16(A) || !aligned16(B) || !aligned16(dA) || !aligned16(dB) ||
       (u_saved != nullptr && !aligned16(u_saved)) || (dx != nullptr && !aligned16(dx)))

@@ -15,6 +15,9 @@ hipError_t launch_nf4_quantize(const void* w, bool w_is_bf16, int64_t rows, int6
 hipError_t launch_nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows,
                                  int64_t cols, bool out_bf16, void* out, hipStream_t stream);
 
+// Zero n 16-bit elements (a fill kernel, so the call can sit in a captured graph).
+hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t stream);
+
 hipError_t launch_lora_fwd_generic(int T, int K, int N, int r, float s, const uint16_t* x,
                                    const uint8_t* codes, const float* absmax, const uint16_t* A,
                                    const uint16_t* B, uint16_t* y, uint16_t* u_save,

@@ -98,4 +98,19 @@ hipError_t launch_nf4_dequantize(const uint8_t* codes, const float* absmax, int6
   return hipGetLastError();
 }
 
+namespace {
+__global__ void zero_u16_kernel(uint16_t* __restrict__ p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = 0;
+}
+}  // namespace
+
+hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  zero_u16_kernel<<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), 256, 0, stream>>>(p, n);
+  return hipGetLastError();
+}
+
 }  // namespace lnf4

@@ -59,7 +59,11 @@ def _fwd(lib, T=8, K=64, N=64, r=8, alpha=16.0, x=P, c=P + (1 << 30), a=P + (2 <
 
 def test_fwd_validation(lib):
     assert _fwd(lib, x=None) == LN_EINVAL
-    assert _fwd(lib, T=0) == LN_EINVAL
+    assert _fwd(lib, T=-1) == LN_EINVAL
+    # T = 0 is an empty batch: accepted, nothing enqueued, token operands may be NULL
+    assert _fwd(lib, T=0) == LN_OK
+    assert _fwd(lib, T=0, x=None, y=None) == LN_OK
+    assert _fwd(lib, T=0, A=None) == LN_EINVAL
     assert _fwd(lib, alpha=float("nan")) == LN_EINVAL
     assert _fwd(lib, r=0) == LN_ERANK
     assert _fwd(lib, r=129) == LN_ERANK
@@ -91,6 +95,7 @@ def _fwd_multi(lib, n=3, T=8, K=64, N=(64, 16, 16), r=8, alpha=16.0, x=P, ptrs=N
 
 def test_fwd_multi_validation(lib):
     assert _fwd_multi(lib, n=0) == LN_EINVAL
+    assert _fwd_multi(lib, T=0, x=None) == LN_OK
     assert _fwd_multi(lib, n=9, N=(64,) * 9) == LN_EINVAL
     assert _fwd_multi(lib, null="A") == LN_EINVAL
     assert _fwd_multi(lib, x=None) == LN_EINVAL
@@ -111,6 +116,7 @@ def test_bwd_validation_and_workspace(lib):
     T, K, N, r = 8, 64, 64, 8
     need = lib.lora_nf4_bwd_workspace_bytes(T, K, N, r)
     assert need > 0
+    assert lib.lora_nf4_bwd_workspace_bytes(0, K, N, r) == 0
     assert lib.lora_nf4_bwd_workspace_bytes(T, 65, N, r) == 0
     assert lib.lora_nf4_bwd_workspace_bytes(T, K, N, 0) == 0
     ptrs = [P + (i << 30) for i in range(12)]

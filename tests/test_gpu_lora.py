@@ -112,12 +112,65 @@ def test_recompute_u_and_skip_dx_paths(q, T, K, N, r):
     assert torch.equal(dA3, dA) and torch.equal(dB3, dB)
 
 
-def test_bitwise_deterministic(q):
-    inp = synth.custom_inputs(3, 1000, 512, 384, 16)
+@pytest.mark.parametrize("T", [1000, 16])
+def test_bitwise_deterministic(q, T):
+    inp = synth.custom_inputs(3, T, 512, 384, 16)
     r1 = _run_gpu(q, inp, 16.0)
     r2 = _run_gpu(q, inp, 16.0)
     for a, b in zip(r1, r2):
         assert torch.equal(a, b)
+
+
+def test_empty_batch(q):
+    """T = 0: the forward is a no-op and the backward's dA, dB are zero (empty sums)."""
+    from tests.gpu_util import dev_bf16
+    inp = synth.custom_inputs(9, 4, 256, 64, 16)
+    codes, absmax = q.nf4_quantize(dev_bf16(inp["W"]))
+    A, B = dev_bf16(inp["A"]), dev_bf16(inp["B"])
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    dy = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    y, u = q.lora_nf4_fwd(x, codes, absmax, A, B, 16.0)
+    assert y.shape == (0, 64) and u.shape == (0, 16)
+    dx, dA, dB = q.lora_nf4_bwd(x, dy, codes, absmax, A, B, 16.0)
+    torch.cuda.synchronize()
+    assert dx.shape == (0, 256)
+    assert not dA.any() and not dB.any()
+
+
+def test_operand_beyond_two_gib(q):
+    """x and dX of 2 GiB each (past the buffer-descriptor range: the generic
+    kernels) on sampled rows and sampled dA / dB entries against the oracle."""
+    from tests.gpu_util import dev_bf16, host_f64
+    T, K, N, r, alpha = 262144, 4096, 64, 8, 16.0
+    g = torch.Generator(device="cuda").manual_seed(123)
+    x = torch.randn((T, K), generator=g, device="cuda").to(torch.bfloat16)
+    dy = (torch.randn((T, N), generator=g, device="cuda") * 0.01).to(torch.bfloat16)
+    small = synth.custom_inputs(12, 1, K, N, r)
+    codes, absmax = q.nf4_quantize(dev_bf16(small["W"]))
+    A, B = dev_bf16(small["A"]), dev_bf16(small["B"])
+    assert x.numel() * 2 >= 2 ** 31
+    y, u = q.lora_nf4_fwd(x, codes, absmax, A, B, alpha)
+    dx, dA, dB = q.lora_nf4_bwd(x, dy, codes, absmax, A, B, alpha, u_saved=u)
+    torch.cuda.synchronize()
+    D = _oracle_D(small)
+    Af, Bf = _f64(small["A"]), _f64(small["B"])
+    s = alpha / r
+    rows = torch.tensor([0, 1, 777, 65536, 131071, 200000, T - 2, T - 1], device="cuda")
+    xr, dyr = host_f64(x[rows]), host_f64(dy[rows])
+    y_ref, u_ref = olora.forward(xr, D, Af, Bf, alpha, r)
+    dx_ref, _, _ = olora.backward(xr, dyr, D, Af, Bf, alpha, r)
+    assert olora.rel_err(host_f64(y[rows]), y_ref) <= TOL
+    assert olora.rel_err(host_f64(u[rows]), u_ref) <= TOL
+    assert olora.rel_err(host_f64(dx[rows]), dx_ref) <= TOL
+    # dA[k, j] = sum_t x[t, k] G[t, j] and dB[j, n] = s sum_t U[t, j] dY[t, n] over
+    # all T: exact G from dY; U from the forward's saved U (checked on rows above)
+    G = s * (host_f64(dy) @ Bf.T)
+    ks = [0, 1, 1234, K - 1]
+    xk = host_f64(x[:, ks])
+    dA_ref = xk.T @ G
+    assert olora.rel_err(host_f64(dA[ks]), dA_ref) <= TOL
+    dB_ref = s * (host_f64(u).T @ host_f64(dy))
+    assert olora.rel_err(host_f64(dB), dB_ref) <= TOL
 
 
 @pytest.mark.parametrize("T,K,N,r", [(131, 192, 200, 12), (7, 320, 72, 24)])
