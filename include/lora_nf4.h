@@ -175,6 +175,60 @@ int lora_nf4_merge(int64_t d_in, int64_t d_out, int32_t r, float lora_alpha, con
 /* Workspace bytes lora_nf4_bwd needs for these sizes (0 if the sizes are invalid). */
 size_t lora_nf4_bwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t r);
 
+/*
+ * lora_adamw_step — one AdamW update of a LoRA factor (A or B), the optimizer
+ * phase of a training step ("Unsloth performance measured: is it really 2x
+ * faster?", section 2.2 time table, optimizer.step row; section 3: 16-bit
+ * gradient states). Decoupled weight decay; for every element i < n, in float32:
+ *     g = grad[i];  m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g^2
+ *     p = p (1 - lr weight_decay) - (lr / (1 - beta1^step)) m / (sqrt(v) / sqrt(1 - beta2^step) + eps)
+ * then m and v are stored as bf16 (nearest-even), p stays float32 and p_bf16 =
+ * bf16(p) is the copy lora_nf4_fwd / lora_nf4_bwd read.
+ *   p       float32 [n] master copy (in/out)      p_bf16  bf16 [n] (out)
+ *   grad    bf16 [n] (e.g. dA or dB of lora_nf4_bwd)
+ *   m, v    bf16 [n] first and second moments (in/out; zero before step 1)
+ *   step    1-based step number (bias correction)
+ * n >= 0 (0: nothing to do); eps > 0; 0 <= beta1, beta2 < 1; finite lr and
+ * weight_decay. All arrays disjoint (LN_EALIAS), 16-byte aligned (LN_EALIGN).
+ */
+int lora_adamw_step(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* grad, uint16_t* m,
+                    uint16_t* v, int32_t step, float lr, float beta1, float beta2, float eps,
+                    float weight_decay, void* stream);
+
+/*
+ * lora_nf4_rslora_alpha — the lora_alpha to pass to the entry points above so
+ * that their scale lora_alpha / r (formed in float32) equals the rank-stabilized
+ * scale alpha / sqrt(r) rounded to float32 (the --use_rslora option of "Reading
+ * the Unsloth changelog", section 2.1). Exact whenever such a float32 exists
+ * (always for power-of-two r); otherwise the one whose scale is nearest. Host
+ * function, no GPU work. NaN for r outside [1, LN_MAX_RANK] or non-finite alpha.
+ */
+float lora_nf4_rslora_alpha(float lora_alpha, int32_t r);
+
+/*
+ * nf4_absmax_quantize / nf4_absmax_dequantize — double quantization of the
+ * float32 block scales of an NF4 weight (the absmax array of nf4_quantize, n =
+ * rows * cols / 64 entries in row-major order). The pages keep the base weight
+ * resident in 4-bit form ("Reading the Unsloth changelog", section 1.1); the
+ * scales are stored once more at 8 bits (QLoRA-style double quantization):
+ * blocks of 256 consecutive scales (the last may be shorter); per block with
+ * minimum lo and maximum hi, in float32 with nearest-even rounding per step:
+ *     offset = lo/2 + hi/2,   d = max(hi - offset, offset - lo),   scale = d / 448
+ *     code   = E4M3((a - offset) / scale)   (0 when scale == 0)
+ * E4M3 = OCP FP8 E4M3FN, nearest value with ties to the even code, saturating
+ * at +-448, sign from the input's sign bit. Dequantization gives
+ *     a' = value(code) * scale + offset   (two roundings, no fused multiply-add),
+ * which the NF4 entry points take in place of absmax. Storage: 8 bits per 64
+ * weights plus 64 bits per 16384 weights, against 32 bits per 64 weights.
+ *   absmax  float32 [n];  q  uint8 [n];  scale, offset  float32 [ceil(n / 256)]
+ * n >= 0 (0: nothing to do); all pointers 16-byte aligned; outputs disjoint from
+ * inputs. Scales must be finite.
+ */
+int nf4_absmax_quantize(const float* absmax, int64_t n, uint8_t* q, float* scale, float* offset,
+                        void* stream);
+int nf4_absmax_dequantize(const uint8_t* q, const float* scale, const float* offset, int64_t n,
+                          float* absmax, void* stream);
+
 /* A static, human-readable description of a status code. */
 const char* lora_nf4_status_string(int status);
 

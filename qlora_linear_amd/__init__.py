@@ -12,6 +12,10 @@ library has not been built, the first call raises.
     dx, dA, dB = lora_nf4_bwd(x, dy, codes, absmax, A, B, lora_alpha, u_saved=u)
     ys, us = lora_nf4_fwd_multi(x, [cq, ck, cv], [aq, ak, av], [Aq, Ak, Av], [Bq, Bk, Bv], alpha)
     w_merged = lora_nf4_merge(codes, absmax, A, B, lora_alpha)   # bf16 [d_out, d_in]
+    lora_adamw_step(A_master, A, dA, mA, vA, step, lr)           # in place, A = bf16(A_master)
+    q, sc, off = nf4_absmax_quantize(absmax)                     # 8-bit block scales
+    absmax2 = nf4_absmax_dequantize(q, sc, off).view_as(absmax)
+    alpha_rs = rslora_alpha(lora_alpha, r)                       # scale alpha / sqrt(r)
 """
 from __future__ import annotations
 
@@ -24,6 +28,7 @@ __all__ = [
     "LoraNF4Error", "library", "library_path", "nf4_quantize", "nf4_dequantize",
     "lora_nf4_fwd", "lora_nf4_fwd_multi", "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_merge",
     "status_string", "EXPORTED_SYMBOLS", "LN_MAX_RANK", "LN_MAX_PROJ",
+    "lora_adamw_step", "rslora_alpha", "nf4_absmax_quantize", "nf4_absmax_dequantize",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +39,8 @@ LN_MAX_RANK = 128
 LN_MAX_PROJ = 8
 EXPORTED_SYMBOLS = ("nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_fwd_multi",
                     "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_merge",
-                    "lora_nf4_status_string")
+                    "lora_nf4_status_string", "lora_adamw_step", "lora_nf4_rslora_alpha",
+                    "nf4_absmax_quantize", "nf4_absmax_dequantize")
 
 _lib = None
 
@@ -53,6 +59,11 @@ _SIGS = {
     "lora_nf4_merge": (ctypes.c_int, [_i64, _i64, ctypes.c_int32, ctypes.c_float, _p, _p, _p, _p,
                                       ctypes.c_int, _p, _p]),
     "lora_nf4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "lora_adamw_step": (ctypes.c_int, [_i64, _p, _p, _p, _p, _p, ctypes.c_int32, ctypes.c_float,
+                                       ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, _p]),
+    "lora_nf4_rslora_alpha": (ctypes.c_float, [ctypes.c_float, ctypes.c_int32]),
+    "nf4_absmax_quantize": (ctypes.c_int, [_p, _i64, _p, _p, _p, _p]),
+    "nf4_absmax_dequantize": (ctypes.c_int, [_p, _p, _p, _i64, _p, _p]),
 }
 
 
@@ -240,4 +251,54 @@ def lora_nf4_merge(codes, absmax, A, B, lora_alpha: float, dtype=torch.bfloat16)
     _check("lora_nf4_merge", library().lora_nf4_merge(K, N, r, float(lora_alpha), codes.data_ptr(),
                                                       absmax.data_ptr(), A.data_ptr(), B.data_ptr(), dt,
                                                       out.data_ptr(), _stream(codes)))
+    return out
+
+
+def lora_adamw_step(p_master, p_bf16, grad, m, v, step: int, lr: float, betas=(0.9, 0.999),
+                    eps: float = 1e-8, weight_decay: float = 0.0):
+    """One AdamW step in place: p_master (float32), p_bf16 = bf16(p_master), moments m, v (bf16)."""
+    bf = torch.bfloat16
+    _dev(p_master, "p_master", torch.float32), _dev(p_bf16, "p_bf16", bf), _dev(grad, "grad", bf)
+    _dev(m, "m", bf), _dev(v, "v", bf)
+    n = p_master.numel()
+    for t, name in ((p_bf16, "p_bf16"), (grad, "grad"), (m, "m"), (v, "v")):
+        if t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements, p_master {n}")
+    _check("lora_adamw_step", library().lora_adamw_step(
+        n, p_master.data_ptr(), p_bf16.data_ptr(), grad.data_ptr(), m.data_ptr(), v.data_ptr(), int(step),
+        float(lr), float(betas[0]), float(betas[1]), float(eps), float(weight_decay), _stream(p_master)))
+
+
+def rslora_alpha(lora_alpha: float, r: int) -> float:
+    """The lora_alpha whose library scale lora_alpha / r equals f32(lora_alpha / sqrt(r))."""
+    a = library().lora_nf4_rslora_alpha(float(lora_alpha), int(r))
+    if a != a:
+        raise ValueError(f"no rank-stabilized alpha for lora_alpha={lora_alpha}, r={r}")
+    return a
+
+
+def nf4_absmax_quantize(absmax):
+    """Double quantization of NF4 block scales: (codes uint8 [n], scale, offset float32 [ceil(n/256)])."""
+    _dev(absmax, "absmax", torch.float32)
+    n = absmax.numel()
+    nb = (n + 255) // 256
+    dev = absmax.device
+    q = torch.empty(n, dtype=torch.uint8, device=dev)
+    sc = torch.empty(nb, dtype=torch.float32, device=dev)
+    off = torch.empty(nb, dtype=torch.float32, device=dev)
+    _check("nf4_absmax_quantize", library().nf4_absmax_quantize(absmax.data_ptr(), n, q.data_ptr(),
+                                                                sc.data_ptr(), off.data_ptr(), _stream(absmax)))
+    return q, sc, off
+
+
+def nf4_absmax_dequantize(q, scale, offset):
+    """float32 [n] block scales from their double-quantized form (use .view_as(absmax))."""
+    _dev(q, "q", torch.uint8), _dev(scale, "scale", torch.float32), _dev(offset, "offset", torch.float32)
+    n = q.numel()
+    nb = (n + 255) // 256
+    if scale.numel() != nb or offset.numel() != nb:
+        raise ValueError(f"scale and offset need {nb} entries for {n} codes")
+    out = torch.empty(n, dtype=torch.float32, device=q.device)
+    _check("nf4_absmax_dequantize", library().nf4_absmax_dequantize(
+        q.data_ptr(), scale.data_ptr(), offset.data_ptr(), n, out.data_ptr(), _stream(q)))
     return out

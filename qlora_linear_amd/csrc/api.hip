@@ -234,4 +234,67 @@ int lora_nf4_bwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_a
                                           static_cast<hipStream_t>(stream)));
 }
 
+int lora_adamw_step(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* grad, uint16_t* m,
+                    uint16_t* v, int32_t step, float lr, float beta1, float beta2, float eps,
+                    float weight_decay, void* stream) {
+  if (n < 0 || step < 1) return LN_EINVAL;
+  if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(eps) || !(eps > 0.0f) ||
+      !(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+    return LN_EINVAL;
+  if (n == 0) return LN_OK;
+  if (p == nullptr || p_bf16 == nullptr || grad == nullptr || m == nullptr || v == nullptr)
+    return LN_EINVAL;
+  if (n > (int64_t(1) << 40)) return LN_ESHAPE;
+  if (!aligned16(p) || !aligned16(p_bf16) || !aligned16(grad) || !aligned16(m) || !aligned16(v))
+    return LN_EALIGN;
+  const size_t nn = static_cast<size_t>(n);
+  const Span outs[4] = {{p, nn * 4}, {p_bf16, nn * 2}, {m, nn * 2}, {v, nn * 2}};
+  const Span ins[1] = {{grad, nn * 2}};
+  if (any_alias(outs, 4, ins, 1)) return LN_EALIAS;
+  return hip_status(lnf4::launch_adamw(n, p, p_bf16, grad, m, v, step, lr, beta1, beta2, eps,
+                                       weight_decay, static_cast<hipStream_t>(stream)));
+}
+
+float lora_nf4_rslora_alpha(float lora_alpha, int32_t r) {
+  if (r < 1 || r > LN_MAX_RANK || !std::isfinite(lora_alpha)) return std::nanf("");
+  const float rf = static_cast<float>(r);
+  const float target = static_cast<float>(static_cast<double>(lora_alpha) / std::sqrt(static_cast<double>(r)));
+  // x -> f32(x / r) is monotone: walk from target * r to the first x whose
+  // quotient reaches target, then keep whichever neighbour lands nearer.
+  float a = target * rf;
+  if (!std::isfinite(a)) return std::nanf("");
+  for (int it = 0; it < 64 && a / rf > target; ++it) a = std::nextafter(a, -HUGE_VALF);
+  for (int it = 0; it < 64 && a / rf < target; ++it) a = std::nextafter(a, HUGE_VALF);
+  const float below = std::nextafter(a, -HUGE_VALF);
+  return (a / rf - target <= target - below / rf) ? a : below;
+}
+
+int nf4_absmax_quantize(const float* absmax, int64_t n, uint8_t* q, float* scale, float* offset,
+                        void* stream) {
+  if (n < 0) return LN_EINVAL;
+  if (n == 0) return LN_OK;
+  if (absmax == nullptr || q == nullptr || scale == nullptr || offset == nullptr) return LN_EINVAL;
+  if (n > (int64_t(1) << 38)) return LN_ESHAPE;
+  if (!aligned16(absmax) || !aligned16(q) || !aligned16(scale) || !aligned16(offset)) return LN_EALIGN;
+  const size_t nn = static_cast<size_t>(n), nb = (nn + 255) / 256;
+  const Span outs[3] = {{q, nn}, {scale, nb * 4}, {offset, nb * 4}};
+  const Span ins[1] = {{absmax, nn * 4}};
+  if (any_alias(outs, 3, ins, 1)) return LN_EALIAS;
+  return hip_status(lnf4::launch_absmax_dq(n, absmax, q, scale, offset, static_cast<hipStream_t>(stream)));
+}
+
+int nf4_absmax_dequantize(const uint8_t* q, const float* scale, const float* offset, int64_t n,
+                          float* absmax, void* stream) {
+  if (n < 0) return LN_EINVAL;
+  if (n == 0) return LN_OK;
+  if (absmax == nullptr || q == nullptr || scale == nullptr || offset == nullptr) return LN_EINVAL;
+  if (n > (int64_t(1) << 38)) return LN_ESHAPE;
+  if (!aligned16(absmax) || !aligned16(q) || !aligned16(scale) || !aligned16(offset)) return LN_EALIGN;
+  const size_t nn = static_cast<size_t>(n), nb = (nn + 255) / 256;
+  const Span outs[1] = {{absmax, nn * 4}};
+  const Span ins[3] = {{q, nn}, {scale, nb * 4}, {offset, nb * 4}};
+  if (any_alias(outs, 1, ins, 3)) return LN_EALIAS;
+  return hip_status(lnf4::launch_absmax_undq(n, q, scale, offset, absmax, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

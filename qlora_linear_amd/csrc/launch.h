@@ -103,4 +103,17 @@ hipError_t launch_lora_bwd(int T, int K, int N, int r, float s, const uint16_t* 
                            uint16_t* dx, uint16_t* dA, uint16_t* dB, void* workspace,
                            const BwdPlan& plan, hipStream_t stream);
 
+// AdamW step of one parameter array (float32 master p, bf16 copy, bf16 gradient
+// and moments), elementwise over n elements.
+hipError_t launch_adamw(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* g, uint16_t* m,
+                        uint16_t* v, int step, float lr, float beta1, float beta2, float eps,
+                        float weight_decay, hipStream_t stream);
+
+// Double quantization of n float32 block scales: E4M3 codes, one float32 scale
+// and offset per 256 scales; and its inverse.
+hipError_t launch_absmax_dq(int64_t n, const float* absmax, uint8_t* q, float* scale, float* offset,
+                            hipStream_t stream);
+hipError_t launch_absmax_undq(int64_t n, const uint8_t* q, const float* scale, const float* offset,
+                              float* out, hipStream_t stream);
+
 }  // namespace lnf4

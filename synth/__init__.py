@@ -147,3 +147,17 @@ def custom_inputs(seed: int, T: int, K: int, N: int, r: int, x_std=1.0, w_std=0.
 def flops(T: int, K: int, N: int, r: int) -> int:
     """Algorithmic FLOPs of one fused LoRA linear forward + backward (no dW: base frozen)."""
     return 4 * T * K * N + 6 * T * r * (K + N)
+
+
+def optimizer_inputs(seed: int, n: int, step_scale: float = 1e-3) -> dict:
+    """Seeded state of one LoRA factor for an optimizer step: float32 master
+    weights ~ U(-1/64, 1/64), bf16 gradient ~ N(0, step_scale) with a spread of
+    magnitudes (some near the eps scale), bf16 first moment ~ N(0, step_scale / 3)
+    and bf16 second moment ~ |N(0, step_scale^2)|."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2000, seed, n])))
+    p = ((g.random(n, dtype=np.float32) * np.float32(2) - np.float32(1)) * np.float32(1 / 64)).astype(np.float32)
+    mag = (np.float32(10.0) ** g.uniform(-6, 0, n).astype(np.float32)).astype(np.float32)
+    grad = f32_to_bf16_bits(g.standard_normal(n, dtype=np.float32) * np.float32(step_scale) * mag)
+    m = f32_to_bf16_bits(g.standard_normal(n, dtype=np.float32) * np.float32(step_scale / 3))
+    v = f32_to_bf16_bits(np.abs(g.standard_normal(n, dtype=np.float32)) * np.float32(step_scale ** 2))
+    return {"p": p, "grad": grad, "m": m, "v": v}

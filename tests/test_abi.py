@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_fwd_multi",
                             "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_merge",
-                            "lora_nf4_status_string"])
+                            "lora_nf4_status_string", "lora_adamw_step", "lora_nf4_rslora_alpha",
+                            "nf4_absmax_quantize", "nf4_absmax_dequantize"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -164,6 +165,56 @@ def test_quantize_validation(lib):
     assert lib.nf4_quantize(P, 0, 4, 64, P + 64, P + (2 << 30), None) == LN_EALIAS
     assert lib.nf4_dequantize(P, P + (1 << 30), 4, 64, 3, P + (2 << 30), None) == LN_EINVAL
     assert lib.nf4_dequantize(P, P + (1 << 30), 4, 64, 0, P + 16, None) == LN_EALIAS
+
+
+def test_adamw_validation(lib):
+    p, pb, g, m, v = (P + (i << 30) for i in range(5))
+
+    def call(n=64, step=1, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0, **kw):
+        a = dict(p=p, pb=pb, g=g, m=m, v=v)
+        a.update(kw)
+        return lib.lora_adamw_step(n, a["p"], a["pb"], a["g"], a["m"], a["v"], step, lr, b1, b2, eps, wd, None)
+
+    assert call(n=0, p=None) == LN_OK  # empty: nothing to do
+    assert call(n=-1) == LN_EINVAL
+    assert call(step=0) == LN_EINVAL
+    assert call(eps=0.0) == LN_EINVAL
+    assert call(b1=1.0) == LN_EINVAL
+    assert call(b2=-0.1) == LN_EINVAL
+    assert call(lr=float("inf")) == LN_EINVAL
+    assert call(m=None) == LN_EINVAL
+    assert call(v=v + 8) == LN_EALIGN
+    assert call(m=g + 64) == LN_EALIAS  # a moment overlapping the gradient
+    assert call(pb=p + 128) == LN_EALIAS
+
+
+def test_absmax_dq_validation(lib):
+    a, q, s, o = (P + (i << 30) for i in range(4))
+    assert lib.nf4_absmax_quantize(a, 0, None, None, None, None) == LN_OK
+    assert lib.nf4_absmax_quantize(a, -5, q, s, o, None) == LN_EINVAL
+    assert lib.nf4_absmax_quantize(None, 300, q, s, o, None) == LN_EINVAL
+    assert lib.nf4_absmax_quantize(a, 300, q + 1, s, o, None) == LN_EALIGN
+    assert lib.nf4_absmax_quantize(a, 300, q, s, a + 16, None) == LN_EALIAS
+    assert lib.nf4_absmax_quantize(a, 300, q, s, s, None) == LN_EALIAS  # scale and offset the same array
+    assert lib.nf4_absmax_dequantize(q, s, o, 300, None, None) == LN_EINVAL
+    assert lib.nf4_absmax_dequantize(q, s, o, 300, q + 64, None) == LN_EALIAS
+
+
+def test_rslora_alpha_gives_the_rank_stabilized_scale_exactly(lib):
+    import numpy as np
+    from oracle import optim
+    for alpha in (1.0, 16.0, 32.0, 7.5, 0.3):
+        for r in (1, 2, 3, 5, 8, 12, 16, 24, 32, 48, 64, 100, 128):
+            a = lib.lora_nf4_rslora_alpha(alpha, r)
+            got = np.float32(a) / np.float32(r)  # the library's own s = lora_alpha / r in float32
+            want = np.float32(optim.rslora_scale(float(np.float32(alpha)), r))  # alpha crosses as float32
+            if r & (r - 1) == 0:
+                assert got == want, (alpha, r)
+            else:
+                assert abs(float(got) - float(want)) <= float(np.spacing(want)), (alpha, r)
+    assert lib.lora_nf4_rslora_alpha(32.0, 16) == 128.0  # s = 32 / sqrt(16) = 8
+    assert lib.lora_nf4_rslora_alpha(16.0, 0) != lib.lora_nf4_rslora_alpha(16.0, 0)  # NaN
+    assert lib.lora_nf4_rslora_alpha(float("inf"), 4) != lib.lora_nf4_rslora_alpha(float("inf"), 4)
 
 
 def test_binding_rejects_cpu_tensors():
