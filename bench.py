@@ -264,6 +264,61 @@ def merge_run(lib, q, torch, d, w, sp, reps=20):
             "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
 
 
+def train_step_run(lib, q, torch, d, w, sp, reps=50):
+    """The training-step companions on one projection, HIP events around `reps`
+    back-to-back C-ABI calls each:
+      adamw      lora_adamw_step over A and B (float32 master, bf16 copy, bf16
+                 gradient and moments); bytes = 4 + 2 + 2 + 2*2 + 2*2 read/written
+                 per element = 16 (master in and out, copy out, gradient in, m, v in
+                 and out);
+      absmax_dq  nf4_absmax_quantize of the projection's block scales; bytes = 4 in
+                 + 1 out per scale (+ 8 per 256)."""
+    p = d["p"]
+    K, N, r = p.d_in, p.d_out, w.r
+    n = K * r + r * N
+    master = torch.zeros(n, dtype=torch.float32, device="cuda")
+    copy = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    grad = torch.full((n,), 1e-3, dtype=torch.bfloat16, device="cuda")
+    m = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    na = d["absmax"].numel()
+    dq_q = torch.empty(na, dtype=torch.uint8, device="cuda")
+    dq_s = torch.empty((na + 255) // 256, dtype=torch.float32, device="cuda")
+    dq_o = torch.empty_like(dq_s)
+
+    def adamw(step):
+        st = lib.lora_adamw_step(n, master.data_ptr(), copy.data_ptr(), grad.data_ptr(), m.data_ptr(),
+                                 v.data_ptr(), step, 1e-4, 0.9, 0.999, 1e-8, 0.01, sp)
+        if st != 0:
+            raise q.LoraNF4Error("lora_adamw_step", st)
+
+    def dq(step):
+        st = lib.nf4_absmax_quantize(d["absmax"].data_ptr(), na, dq_q.data_ptr(), dq_s.data_ptr(),
+                                     dq_o.data_ptr(), sp)
+        if st != 0:
+            raise q.LoraNF4Error("nf4_absmax_quantize", st)
+
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name, fn, nbytes in (("adamw", adamw, 16 * n), ("absmax_dq", dq, 5 * na + 8 * dq_s.numel())):
+        for i in range(3):
+            fn(i + 1)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i + 4)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / reps
+        out[name] = {"elements": n if name == "adamw" else na, "us": round(us, 2), "bytes": nbytes,
+                     "bound": "hbm", "achieved": round(nbytes / us / 1e3, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
+    out["projection"] = f"{p.name} {K}->{N}"
+    del master, copy, grad, m, v, dq_q, dq_s, dq_o
+    return out
+
+
 def to_dev_bf16(bits):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
@@ -455,6 +510,7 @@ def main():
     if args.small_tokens > 0:
         out["small_tokens"] = small_token_run(lib, q, torch, projs[big], w, args.small_tokens, sp)
     out["merge"] = merge_run(lib, q, torch, projs[big], w, sp)
+    out["train_step"] = train_step_run(lib, q, torch, projs[big], w, sp)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
