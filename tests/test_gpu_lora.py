@@ -75,7 +75,8 @@ def test_tiny_workload(q):
 # (T, d_in, d_out, r): ragged token counts, partial tiles in every dimension,
 # ranks from 1 to the maximum.
 ODD = [(1, 64, 64, 1), (63, 128, 192, 8), (65, 192, 64, 16), (200, 320, 136, 64),
-       (130, 256, 8, 128), (257, 64, 520, 24), (129, 384, 264, 17), (17, 640, 1000, 40)]
+       (130, 256, 8, 128), (257, 64, 520, 24), (129, 384, 264, 17), (17, 640, 1000, 40),
+       (260, 192, 296, 48)]
 
 
 @pytest.mark.parametrize("T,K,N,r", ODD)
