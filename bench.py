@@ -18,8 +18,9 @@ the same projection; `small_tokens` times forward and backward of the largest
 projection at a few tokens (the weight-streaming kernels), where the bound is
 reading the packed weight from HBM; `merge` times lora_nf4_merge of that
 projection (the 16-bit export, also HBM-bound). With --fuse, projections that read the same
-activations in a transformer layer (q/k/v, gate/up) share one x and run their
-forward as one lora_nf4_fwd_multi launch; the FLOPs counted are unchanged.
+activations in a transformer layer (q/k/v, gate/up) share one x, run their
+forward as one lora_nf4_fwd_multi launch and their backward as one
+lora_nf4_bwd_multi call (dX summed over the group); the FLOPs counted are unchanged.
 """
 from __future__ import annotations
 
@@ -380,9 +381,14 @@ def main():
     for ui, un in enumerate(units):
         if len(un) > 1:
             arr = lambda key: (ctypes.c_void_p * len(un))(*[projs[j][key].data_ptr() for j in un])
-            multi_args[ui] = dict(d_out=(ctypes.c_int64 * len(un))(*[projs[j]["p"].d_out for j in un]),
+            d_out = [projs[j]["p"].d_out for j in un]
+            nb = q.lora_nf4_bwd_multi_workspace_bytes(w.tokens, projs[un[0]]["p"].d_in, d_out, w.r)
+            multi_args[ui] = dict(d_out=(ctypes.c_int64 * len(un))(*d_out),
                                   codes=arr("codes"), absmax=arr("absmax"), A=arr("A"), B=arr("B"),
-                                  y=arr("y"), u=arr("u"))
+                                  y=arr("y"), u=arr("u"), dy=arr("dY"), dA=arr("dA"), dB=arr("dB"),
+                                  ws=torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda"))
+            for j in un:  # the group's per-projection backward workspaces are not used
+                projs[j]["ws"] = torch.empty(0, dtype=torch.uint8, device="cuda")
     torch.cuda.empty_cache()
 
     def fwd(d):
@@ -415,11 +421,23 @@ def main():
         if st != 0:
             raise q.LoraNF4Error("lora_nf4_fwd_multi", st)
 
+    def bwd_unit(ui):
+        un = units[ui]
+        if len(un) == 1:
+            return bwd(projs[un[0]])
+        m, d0 = multi_args[ui], projs[un[0]]
+        cv = lambda a: ctypes.cast(a, ctypes.c_void_p)
+        st = lib.lora_nf4_bwd_multi(w.tokens, d0["p"].d_in, len(un), cv(m["d_out"]), w.r, w.alpha,
+                                    d0["x"].data_ptr(), cv(m["dy"]), cv(m["codes"]), cv(m["absmax"]),
+                                    cv(m["A"]), cv(m["B"]), cv(m["u"]), d0["dx"].data_ptr(), cv(m["dA"]),
+                                    cv(m["dB"]), m["ws"].data_ptr(), m["ws"].numel(), sp)
+        if st != 0:
+            raise q.LoraNF4Error("lora_nf4_bwd_multi", st)
+
     def step_all():
         for ui, un in enumerate(units):
             fwd_unit(ui)
-            for j in un:
-                bwd(projs[j])
+            bwd_unit(ui)
 
     if args.counter_pass:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -450,8 +468,7 @@ def main():
             ev[i][0].record(stream)
             fwd_unit(ui)
             ev[i][1].record(stream)
-            for j in un:
-                bwd(projs[j])
+            bwd_unit(ui)
             ev[i][2].record(stream)
             i += 1
     t_end.record(stream)
@@ -496,7 +513,8 @@ def main():
                    "r": w.r, "alpha": w.alpha,
                    "projections": [f"{d['p'].name} {d['p'].d_in}->{d['p'].d_out}" for d in projs],
                    "weights": "NF4 blocksize 64, fp32 absmax", "parallelism": "single GPU",
-                   "fused_forward": [[projs[j]["p"].name for j in un] for un in units if len(un) > 1]},
+                   "fused_forward": [[projs[j]["p"].name for j in un] for un in units if len(un) > 1],
+                   "fused_backward": [[projs[j]["p"].name for j in un] for un in units if len(un) > 1]},
         "tokens_per_s": round(tokens_s, 1),
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(fwd_avg, 4),

@@ -66,7 +66,7 @@ typedef enum {
 typedef enum { LN_F32 = 0, LN_BF16 = 1 } ln_dtype;
 
 #define LN_MAX_RANK 128
-#define LN_MAX_PROJ 8   /* projections per lora_nf4_fwd_multi call */
+#define LN_MAX_PROJ 8   /* projections per lora_nf4_fwd_multi / lora_nf4_bwd_multi call */
 
 /*
  * nf4_quantize — blockwise NF4 quantization of w [rows, cols] (float32 or bf16
@@ -153,6 +153,41 @@ int lora_nf4_bwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_a
                  const uint16_t* A, const uint16_t* B, const uint16_t* u_saved,
                  uint16_t* dx, uint16_t* dA, uint16_t* dB,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lora_nf4_bwd_multi — the backward of n_proj projections that read the same x
+ * (q/k/v or gate/up, as for lora_nf4_fwd_multi): their input gradients add up,
+ *     dX = sum_g ( dY[g] D_g + s (dY[g] B[g]^T) A[g]^T )
+ *     dA[g] = x^T (s dY[g] B[g]^T),   dB[g] = s (x A[g])^T dY[g]
+ * the same sums n_proj calls of lora_nf4_bwd compute, with dX summed. When every
+ * d_out is a multiple of 64, r % 8 == 0, n_proj r <= 64 and T > 32, one dX pass
+ * runs over the projections' concatenated d_out (no per-projection dX in HBM)
+ * and one pass over x yields every dA; otherwise the projections run one after
+ * another and dX accumulates (float32 add of bf16 partial results).
+ *   n_proj             1 .. LN_MAX_PROJ;  d_out  HOST array [n_proj] (% 8 == 0)
+ *   dy, w_codes, w_absmax, A, B, dA, dB
+ *                      HOST arrays [n_proj] of DEVICE pointers, laid out as for
+ *                      lora_nf4_bwd with that projection's d_out
+ *   u_saved            NULL, or a HOST array [n_proj] whose entries may be NULL
+ *                      (bf16 x A[g] from lora_nf4_fwd_multi; recomputed if NULL)
+ *   dx                 bf16 [T, d_in] (output; may be NULL to skip it)
+ *   workspace          at least lora_nf4_bwd_multi_workspace_bytes(...) bytes,
+ *                      256-byte aligned, as for lora_nf4_bwd
+ * All projections share T, d_in, r and lora_alpha. Every output (dx, each dA[g],
+ * dB[g], the workspace) must be disjoint from every input and the other outputs
+ * (LN_EALIAS). T = 0 zeroes every dA[g] and dB[g]. Other errors as for
+ * lora_nf4_bwd, plus LN_EINVAL for n_proj out of range or a NULL array.
+ */
+int lora_nf4_bwd_multi(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d_out, int32_t r,
+                       float lora_alpha, const uint16_t* x, const uint16_t* const* dy,
+                       const uint8_t* const* w_codes, const float* const* w_absmax,
+                       const uint16_t* const* A, const uint16_t* const* B,
+                       const uint16_t* const* u_saved, uint16_t* dx, uint16_t* const* dA,
+                       uint16_t* const* dB, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes lora_nf4_bwd_multi needs (0 if the sizes are invalid or T = 0). */
+size_t lora_nf4_bwd_multi_workspace_bytes(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d_out,
+                                          int32_t r);
 
 /*
  * lora_nf4_merge — the merged base weight for export after training,

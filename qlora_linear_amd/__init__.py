@@ -11,6 +11,8 @@ library has not been built, the first call raises.
     y, u = lora_nf4_fwd(x, codes, absmax, A, B, lora_alpha)
     dx, dA, dB = lora_nf4_bwd(x, dy, codes, absmax, A, B, lora_alpha, u_saved=u)
     ys, us = lora_nf4_fwd_multi(x, [cq, ck, cv], [aq, ak, av], [Aq, Ak, Av], [Bq, Bk, Bv], alpha)
+    dx, dAs, dBs = lora_nf4_bwd_multi(x, dys, [cq, ck, cv], [aq, ak, av], [Aq, Ak, Av], [Bq, Bk, Bv],
+                                      alpha, u_saved=us)              # dx summed over q/k/v
     w_merged = lora_nf4_merge(codes, absmax, A, B, lora_alpha)   # bf16 [d_out, d_in]
     lora_adamw_step(A_master, A, dA, mA, vA, step, lr)           # in place, A = bf16(A_master)
     q, sc, off = nf4_absmax_quantize(absmax)                     # 8-bit block scales
@@ -29,6 +31,7 @@ __all__ = [
     "lora_nf4_fwd", "lora_nf4_fwd_multi", "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_merge",
     "status_string", "EXPORTED_SYMBOLS", "LN_MAX_RANK", "LN_MAX_PROJ",
     "lora_adamw_step", "rslora_alpha", "nf4_absmax_quantize", "nf4_absmax_dequantize",
+    "lora_nf4_bwd_multi", "lora_nf4_bwd_multi_workspace_bytes",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -40,7 +43,8 @@ LN_MAX_PROJ = 8
 EXPORTED_SYMBOLS = ("nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_fwd_multi",
                     "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_merge",
                     "lora_nf4_status_string", "lora_adamw_step", "lora_nf4_rslora_alpha",
-                    "nf4_absmax_quantize", "nf4_absmax_dequantize")
+                    "nf4_absmax_quantize", "nf4_absmax_dequantize", "lora_nf4_bwd_multi",
+                    "lora_nf4_bwd_multi_workspace_bytes")
 
 _lib = None
 
@@ -62,6 +66,9 @@ _SIGS = {
     "lora_adamw_step": (ctypes.c_int, [_i64, _p, _p, _p, _p, _p, ctypes.c_int32, ctypes.c_float,
                                        ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, _p]),
     "lora_nf4_rslora_alpha": (ctypes.c_float, [ctypes.c_float, ctypes.c_int32]),
+    "lora_nf4_bwd_multi": (ctypes.c_int, [_i64, _i64, ctypes.c_int32, _p, ctypes.c_int32, ctypes.c_float,
+                                          _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
+    "lora_nf4_bwd_multi_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, ctypes.c_int32, _p, ctypes.c_int32]),
     "nf4_absmax_quantize": (ctypes.c_int, [_p, _i64, _p, _p, _p, _p]),
     "nf4_absmax_dequantize": (ctypes.c_int, [_p, _p, _p, _i64, _p, _p]),
 }
@@ -234,6 +241,52 @@ def lora_nf4_bwd(x, dy, codes, absmax, A, B, lora_alpha: float, u_saved=None, ne
         absmax.data_ptr(), A.data_ptr(), B.data_ptr(), _ptr(u_saved), _ptr(dx), dA.data_ptr(),
         dB.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x)))
     return dx, dA, dB
+
+
+def lora_nf4_bwd_multi_workspace_bytes(T: int, K: int, d_outs, r: int) -> int:
+    n = len(d_outs)
+    arr = (ctypes.c_int64 * n)(*d_outs)
+    return int(library().lora_nf4_bwd_multi_workspace_bytes(T, K, n, ctypes.cast(arr, ctypes.c_void_p), r))
+
+
+def lora_nf4_bwd_multi(x, dy, codes, absmax, A, B, lora_alpha: float, u_saved=None, need_dx: bool = True,
+                       workspace: torch.Tensor | None = None):
+    """Backward of projections sharing x: (dx summed over them or None, [dA_g], [dB_g])."""
+    bf = torch.bfloat16
+    _dev(x, "x", bf, 2)
+    n = len(codes)
+    if not (len(dy) == len(absmax) == len(A) == len(B) == n) or (u_saved is not None and len(u_saved) != n):
+        raise ValueError("dy, codes, absmax, A, B (and u_saved) need one entry per projection")
+    shapes = []
+    for g in range(n):
+        _dev(dy[g], f"dy[{g}]", bf, 2), _dev(codes[g], f"codes[{g}]", torch.uint8, 2)
+        _dev(absmax[g], f"absmax[{g}]", torch.float32, 2), _dev(A[g], f"A[{g}]", bf, 2), _dev(B[g], f"B[{g}]", bf, 2)
+        if u_saved is not None and u_saved[g] is not None:
+            _dev(u_saved[g], f"u_saved[{g}]", bf, 2)
+        sh = _lora_shapes(x, codes[g], A[g], B[g])
+        if dy[g].shape != (sh[0], sh[2]):
+            raise ValueError(f"dy[{g}] must be [T, d_out]")
+        shapes.append(sh)
+    T, K, _, r = shapes[0]
+    if any(sh[3] != r for sh in shapes):
+        raise ValueError("all projections must share the rank r")
+    dev = x.device
+    dx = torch.empty((T, K), dtype=bf, device=dev) if need_dx else None
+    dAs = [torch.empty((K, r), dtype=bf, device=dev) for _ in range(n)]
+    dBs = [torch.empty((r, sh[2]), dtype=bf, device=dev) for sh in shapes]
+    d_out = [sh[2] for sh in shapes]
+    nbytes = lora_nf4_bwd_multi_workspace_bytes(T, K, d_out, r)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8)
+    d_arr = (ctypes.c_int64 * n)(*d_out)
+    keep = [_ptr_array([t.data_ptr() for t in lst]) for lst in (dy, codes, absmax, A, B, dAs, dBs)]
+    u_arr = _ptr_array([0 if t is None else t.data_ptr() for t in u_saved]) if u_saved is not None else (None, None)
+    _check("lora_nf4_bwd_multi", library().lora_nf4_bwd_multi(
+        T, K, n, ctypes.cast(d_arr, ctypes.c_void_p), r, float(lora_alpha), x.data_ptr(), keep[0][1], keep[1][1],
+        keep[2][1], keep[3][1], keep[4][1], u_arr[1], _ptr(dx), keep[5][1], keep[6][1], workspace.data_ptr(),
+        workspace.numel(), _stream(x)))
+    return dx, dAs, dBs
 
 
 def lora_nf4_merge(codes, absmax, A, B, lora_alpha: float, dtype=torch.bfloat16):

@@ -234,6 +234,78 @@ int lora_nf4_bwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_a
                                           static_cast<hipStream_t>(stream)));
 }
 
+size_t lora_nf4_bwd_multi_workspace_bytes(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d_out,
+                                          int32_t r) {
+  if (T == 0 || n_proj < 1 || n_proj > LN_MAX_PROJ || d_out == nullptr) return 0;
+  int N[LN_MAX_PROJ];
+  for (int g = 0; g < n_proj; ++g) {
+    if (check_linear_shape(T, d_in, d_out[g], r, 1.0f) != LN_OK) return 0;
+    N[g] = static_cast<int>(d_out[g]);
+  }
+  return lnf4::plan_bwd_multi(T, d_in, n_proj, N, r).bytes;
+}
+
+int lora_nf4_bwd_multi(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d_out, int32_t r,
+                       float lora_alpha, const uint16_t* x, const uint16_t* const* dy,
+                       const uint8_t* const* w_codes, const float* const* w_absmax,
+                       const uint16_t* const* A, const uint16_t* const* B,
+                       const uint16_t* const* u_saved, uint16_t* dx, uint16_t* const* dA,
+                       uint16_t* const* dB, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_proj < 1 || n_proj > LN_MAX_PROJ) return LN_EINVAL;
+  if (d_out == nullptr || dy == nullptr || w_codes == nullptr || w_absmax == nullptr || A == nullptr ||
+      B == nullptr || dA == nullptr || dB == nullptr)
+    return LN_EINVAL;
+  if (T != 0 && x == nullptr) return LN_EINVAL;
+  const size_t t = T, k = d_in, rr = r;
+  Span outs[2 + 2 * LN_MAX_PROJ];
+  Span ins[1 + 6 * LN_MAX_PROJ];
+  int n_out = 0, n_in = 0;
+  int N[LN_MAX_PROJ];
+  ins[n_in++] = {x, t * k * 2};
+  outs[n_out++] = {dx, t * k * 2};
+  for (int g = 0; g < n_proj; ++g) {
+    if (w_codes[g] == nullptr || w_absmax[g] == nullptr || A[g] == nullptr || B[g] == nullptr ||
+        dA[g] == nullptr || dB[g] == nullptr || (T != 0 && dy[g] == nullptr))
+      return LN_EINVAL;
+    const int st = check_linear_shape(T, d_in, d_out[g], r, lora_alpha);
+    if (st != LN_OK) return st;
+    const uint16_t* u = u_saved == nullptr ? nullptr : u_saved[g];
+    if (!aligned16(w_codes[g]) || !aligned16(w_absmax[g]) || !aligned16(A[g]) || !aligned16(B[g]) ||
+        !aligned16(dA[g]) || !aligned16(dB[g]) || !aligned16(dy[g]) || (u != nullptr && !aligned16(u)))
+      return LN_EALIGN;
+    const size_t n = d_out[g];
+    N[g] = static_cast<int>(d_out[g]);
+    outs[n_out++] = {dA[g], k * rr * 2};
+    outs[n_out++] = {dB[g], rr * n * 2};
+    ins[n_in++] = {dy[g], t * n * 2};
+    ins[n_in++] = {w_codes[g], n * k / 2};
+    ins[n_in++] = {w_absmax[g], n * k / 64 * 4};
+    ins[n_in++] = {A[g], k * rr * 2};
+    ins[n_in++] = {B[g], rr * n * 2};
+    ins[n_in++] = {u, t * rr * 2};
+  }
+  if (!aligned16(x) || (dx != nullptr && !aligned16(dx))) return LN_EALIGN;
+  if (T == 0) {  // empty batch: every dA and dB is an empty sum
+    if (any_alias(outs, n_out, ins, n_in)) return LN_EALIAS;
+    hipError_t e = hipSuccess;
+    for (int g = 0; g < n_proj && e == hipSuccess; ++g) {
+      e = lnf4::launch_zero_u16(dA[g], static_cast<int64_t>(d_in) * r, static_cast<hipStream_t>(stream));
+      if (e == hipSuccess)
+        e = lnf4::launch_zero_u16(dB[g], static_cast<int64_t>(r) * d_out[g], static_cast<hipStream_t>(stream));
+    }
+    return hip_status(e);
+  }
+  const lnf4::BwdMultiPlan plan = lnf4::plan_bwd_multi(T, d_in, n_proj, N, r);
+  if (workspace == nullptr || workspace_bytes < plan.bytes) return LN_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LN_EALIGN;
+  outs[n_out++] = {workspace, plan.bytes};
+  if (any_alias(outs, n_out, ins, n_in)) return LN_EALIAS;
+  const float s = lora_alpha / static_cast<float>(r);
+  return hip_status(lnf4::launch_lora_bwd_multi(static_cast<int>(T), static_cast<int>(d_in), n_proj, N, r, s,
+                                                x, dy, w_codes, w_absmax, A, B, u_saved, dx, dA, dB,
+                                                workspace, plan, static_cast<hipStream_t>(stream)));
+}
+
 int lora_adamw_step(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* grad, uint16_t* m,
                     uint16_t* v, int32_t step, float lr, float beta1, float beta2, float eps,
                     float weight_decay, void* stream) {

@@ -55,6 +55,26 @@ hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* d
                           const uint8_t* codes, const float* absmax, const uint16_t* A,
                           const uint16_t* B, uint16_t* dx, uint16_t* g_out, hipStream_t stream);
 
+// The dX kernel over a table of projections that share x: the reduction runs over
+// their concatenated d_out (step_end[g] = 64-wide steps of projections 0..g) and
+// dX = sum_g dY_g D_g + G_g A_g^T; g_out [T][n r] receives every G_g side by side.
+// A one-entry table is the single-projection kernel.
+struct DxTable {
+  int n;
+  int step_end[kMaxProj];
+  int N[kMaxProj];
+  const uint16_t* dy[kMaxProj];
+  const uint8_t* codes[kMaxProj];
+  const float* absmax[kMaxProj];
+  const uint16_t* A[kMaxProj];
+  const uint16_t* B[kMaxProj];
+};
+// Several projections take this kernel when every d_out is a multiple of 64 and
+// n r <= 64 (r % 8 == 0).
+bool lora_dx_multi_supported(int n_proj, const int* N, int r);
+hipError_t launch_lora_dx_table(int T, int K, int r, float s, const DxTable& tab, uint16_t* dx,
+                                uint16_t* g_out, hipStream_t stream);
+
 // Weight-streaming dX for a few tokens (1 <= T <= 32, r % 8 == 0, r <= 64): split
 // over d_in column blocks and d_out slices, fp32 partials in part_x [S][T][K] and
 // part_g [S][T][r], then one reduce that stores dX and bf16 G.
@@ -73,13 +93,20 @@ inline bool fits_buffer(int64_t T, int64_t K, int64_t N) {
          K * 128 * 2 < lim && N * 64 * 2 < lim;
 }
 
-// Rank-r gradients dA, dB in one launch plus one reduce (r % 8 == 0, r <= 64).
-// part_a: [splits][r][K] fp32, part_b: [splits][r][N] fp32.
+// Rank-r gradients dA, dB in one launch plus one reduce (ranks % 8 == 0, <= 64):
+// dA = x^T G over K columns with G [T][ra], dB = s U^T dY over N columns with
+// U [T][rb]; K = 0 or N = 0 leaves that job out. dA's ra columns are split into
+// projections of da.gw columns each, projection g stored at da.p[g] as [K][gw].
+// part_a: [splits][ra][K] fp32, part_b: [splits][rb][N] fp32.
+struct DaOut {
+  uint16_t* p[kMaxProj];
+  int gw;
+};
 bool lora_skinny_supported(int r);
 int skinny_splits(int64_t T, int64_t K, int64_t N);
-hipError_t launch_lora_skinny(int T, int K, int N, int r, float s, const uint16_t* x,
+hipError_t launch_lora_skinny(int T, int K, int N, int ra, int rb, float s, const uint16_t* x,
                               const uint16_t* g, const uint16_t* dy, const uint16_t* u,
-                              float* part_a, float* part_b, int splits, uint16_t* dA,
+                              float* part_a, float* part_b, int splits, const DaOut& da,
                               uint16_t* dB, hipStream_t stream);
 
 // Backward plan: how the workspace is carved. Shared by the launcher and the
@@ -102,6 +129,27 @@ hipError_t launch_lora_bwd(int T, int K, int N, int r, float s, const uint16_t* 
                            const uint16_t* A, const uint16_t* B, const uint16_t* u_saved,
                            uint16_t* dx, uint16_t* dA, uint16_t* dB, void* workspace,
                            const BwdPlan& plan, hipStream_t stream);
+
+// Backward of several projections that share x (dX summed over them). Fused: one
+// dX launch over all projections (G side by side in [T][n r]), one pass over x
+// for every dA with the first projection's dB, one pass per further dB.
+// Otherwise one backward per projection, dX accumulated from a scratch copy.
+struct BwdMultiPlan {
+  bool fused;
+  int n, R;                   // projections, n r
+  int splits_a;               // fused: token splits of the dA pass (and the first dB)
+  int splits_b[kMaxProj];     // fused: token splits of the dB passes of projections 1 ..
+  size_t off_g, off_u, off_pa, off_pb;  // fused
+  size_t off_single, off_dxt;           // per-projection fallback
+  size_t bytes;
+};
+BwdMultiPlan plan_bwd_multi(int64_t T, int64_t K, int n, const int* N, int r);
+hipError_t launch_lora_bwd_multi(int T, int K, int n, const int* N, int r, float s, const uint16_t* x,
+                                 const uint16_t* const* dy, const uint8_t* const* codes,
+                                 const float* const* absmax, const uint16_t* const* A,
+                                 const uint16_t* const* B, const uint16_t* const* u_saved, uint16_t* dx,
+                                 uint16_t* const* dA, uint16_t* const* dB, void* workspace,
+                                 const BwdMultiPlan& p, hipStream_t stream);
 
 // AdamW step of one parameter array (float32 master p, bf16 copy, bf16 gradient
 // and moments), elementwise over n elements.

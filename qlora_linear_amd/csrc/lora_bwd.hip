@@ -16,6 +16,8 @@
 //      staged transposed in LDS.
 //   4. skinny_reduce_kernel — fixed-order sum of the partials (deterministic),
 //      scale, bf16 store in the gradient's layout.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -372,8 +374,12 @@ hipError_t launch_bwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
     if ((e = hipGetLastError()) != hipSuccess) return e;
     uu = u;
   }
-  if (p.fast)
-    return launch_lora_skinny(T, K, N, r, s, x, g, dy, uu, pa, pb, p.splits_a, dA, dB, stream);
+  if (p.fast) {
+    DaOut da{};
+    da.p[0] = dA;
+    da.gw = r;
+    return launch_lora_skinny(T, K, N, r, r, s, x, g, dy, uu, pa, pb, p.splits_a, da, dB, stream);
+  }
   const int tca = (T + p.splits_a - 1) / p.splits_a;
   const int tcb = (T + p.splits_b - 1) / p.splits_b;
   skinny_tn_kernel<RT><<<dim3((K + 127) / 128, p.splits_a), kThreads, 0, stream>>>(T, K, r, tca, x, g,
@@ -388,6 +394,44 @@ hipError_t launch_bwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
   skinny_reduce_kernel<<<(N * r + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
       pb, p.splits_b, N, r, RT * 16, s, 1, dB);
   return hipGetLastError();
+}
+
+// dst += src over n bf16 elements (float32 add, one nearest-even rounding).
+__global__ __launch_bounds__(256) void add_bf16_kernel(int64_t n, uint16_t* __restrict__ dst,
+                                                       const uint16_t* __restrict__ src) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (i + 8 <= n) {
+    const uint4 a = *reinterpret_cast<const uint4*>(dst + i);
+    const uint4 b = *reinterpret_cast<const uint4*>(src + i);
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = pack_bf16x2(__uint_as_float(aw[q] << 16) + __uint_as_float(bw[q] << 16),
+                         __uint_as_float(aw[q] & 0xFFFF0000u) + __uint_as_float(bw[q] & 0xFFFF0000u));
+    *reinterpret_cast<uint4*>(dst + i) = uint4{o[0], o[1], o[2], o[3]};
+  } else {
+    for (int64_t k = i; k < n; ++k) dst[k] = to_bf16(bf16_to_f32(dst[k]) + bf16_to_f32(src[k]));
+  }
+}
+
+hipError_t launch_u(int T, int K, int r, const uint16_t* x, const uint16_t* A, uint16_t* u,
+                    hipStream_t stream) {
+#define LNF4_U(RT_) \
+  lora_u_kernel<RT_><<<(T + 63) / 64, kThreads, 0, stream>>>(T, K, r, x, A, u); \
+  return hipGetLastError()
+  switch ((r + 15) / 16) {
+    case 1: LNF4_U(1);
+    case 2: LNF4_U(2);
+    case 3: LNF4_U(3);
+    case 4: LNF4_U(4);
+    case 5: LNF4_U(5);
+    case 6: LNF4_U(6);
+    case 7: LNF4_U(7);
+    case 8: LNF4_U(8);
+    default: return hipErrorInvalidValue;
+  }
+#undef LNF4_U
 }
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -462,6 +506,102 @@ hipError_t launch_lora_bwd(int T, int K, int N, int r, float s, const uint16_t* 
     default: return hipErrorInvalidValue;
   }
 #undef LNF4_BWD
+}
+
+BwdMultiPlan plan_bwd_multi(int64_t T, int64_t K, int n, const int* N, int r) {
+  BwdMultiPlan p{};
+  p.n = n;
+  p.R = n * r;
+  bool fused = n > 1 && lora_dx_multi_supported(n, N, r) && lora_skinny_supported(p.R) &&
+               !lora_dx_stream_supported(T, r);
+  for (int g = 0; g < n && fused; ++g) fused = fits_buffer(T, K, N[g]);
+  p.fused = fused;
+  size_t off = 0;
+  if (fused) {
+    p.off_g = off;
+    off = align256(off + static_cast<size_t>(T) * p.R * 2);
+    p.off_u = off;
+    off = align256(off + static_cast<size_t>(n) * T * r * 2);
+    p.splits_a = skinny_splits(T, K, N[0]);
+    size_t pb = static_cast<size_t>(p.splits_a) * N[0] * r * 4;
+    for (int g = 1; g < n; ++g) {
+      p.splits_b[g] = skinny_splits(T, 0, N[g]);
+      pb = std::max(pb, static_cast<size_t>(p.splits_b[g]) * N[g] * r * 4);
+    }
+    p.off_pa = off;
+    off = align256(off + static_cast<size_t>(p.splits_a) * K * p.R * 4);
+    p.off_pb = off;
+    off = align256(off + pb);
+  } else {
+    size_t single = 0;
+    for (int g = 0; g < n; ++g) single = std::max(single, plan_bwd(T, K, N[g], r).bytes);
+    p.off_single = off;
+    off = align256(off + single);
+    p.off_dxt = off;
+    if (n > 1) off = align256(off + static_cast<size_t>(T) * K * 2);
+  }
+  p.bytes = off;
+  return p;
+}
+
+hipError_t launch_lora_bwd_multi(int T, int K, int n, const int* N, int r, float s, const uint16_t* x,
+                                 const uint16_t* const* dy, const uint8_t* const* codes,
+                                 const float* const* absmax, const uint16_t* const* A,
+                                 const uint16_t* const* B, const uint16_t* const* u_saved, uint16_t* dx,
+                                 uint16_t* const* dA, uint16_t* const* dB, void* workspace,
+                                 const BwdMultiPlan& p, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e = hipSuccess;
+  if (!p.fused) {  // one backward per projection; dX accumulated
+    uint16_t* dxt = reinterpret_cast<uint16_t*>(ws + p.off_dxt);
+    for (int g = 0; g < n; ++g) {
+      const uint16_t* u = u_saved == nullptr ? nullptr : u_saved[g];
+      uint16_t* dxg = (dx != nullptr && g > 0) ? dxt : dx;
+      e = launch_lora_bwd(T, K, N[g], r, s, x, dy[g], codes[g], absmax[g], A[g], B[g], u, dxg, dA[g], dB[g],
+                          ws + p.off_single, plan_bwd(T, K, N[g], r), stream);
+      if (e != hipSuccess) return e;
+      if (dxg == dxt) {
+        const int64_t total = static_cast<int64_t>(T) * K;
+        add_bf16_kernel<<<static_cast<unsigned>((total / 8 + 255) / 256 + 1), 256, 0, stream>>>(total, dx, dxt);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+    }
+    return hipSuccess;
+  }
+  DxTable tab{};
+  tab.n = n;
+  int steps = 0;
+  for (int g = 0; g < n; ++g) {
+    steps += N[g] / 64;
+    tab.step_end[g] = steps;
+    tab.N[g] = N[g];
+    tab.dy[g] = dy[g];
+    tab.codes[g] = codes[g];
+    tab.absmax[g] = absmax[g];
+    tab.A[g] = A[g];
+    tab.B[g] = B[g];
+  }
+  uint16_t* G = reinterpret_cast<uint16_t*>(ws + p.off_g);
+  if ((e = launch_lora_dx_table(T, K, r, s, tab, dx, G, stream)) != hipSuccess) return e;
+  const uint16_t* uu[kMaxProj];
+  for (int g = 0; g < n; ++g) {
+    uu[g] = u_saved == nullptr ? nullptr : u_saved[g];
+    if (uu[g] == nullptr) {
+      uint16_t* u = reinterpret_cast<uint16_t*>(ws + p.off_u) + static_cast<size_t>(g) * T * r;
+      if ((e = launch_u(T, K, r, x, A[g], u, stream)) != hipSuccess) return e;
+      uu[g] = u;
+    }
+  }
+  float* pa = reinterpret_cast<float*>(ws + p.off_pa);
+  float* pb = reinterpret_cast<float*>(ws + p.off_pb);
+  DaOut da{};
+  da.gw = r;
+  for (int g = 0; g < n; ++g) da.p[g] = dA[g];
+  // dA of every projection from one pass over x (G side by side), with dB of the first
+  e = launch_lora_skinny(T, K, N[0], p.R, r, s, x, G, dy[0], uu[0], pa, pb, p.splits_a, da, dB[0], stream);
+  for (int g = 1; g < n && e == hipSuccess; ++g)
+    e = launch_lora_skinny(T, 0, N[g], p.R, r, s, x, G, dy[g], uu[g], pa, pb, p.splits_b[g], da, dB[g], stream);
+  return e;
 }
 
 }  // namespace lnf4

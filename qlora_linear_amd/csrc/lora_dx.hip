@@ -13,6 +13,15 @@
 // exactly the MFMA B fragment. The same dY tile accumulates G = s dY B^T for the
 // epilogue (16 x 16 x 32 MFMAs for r <= 16, else 32 x 32 x 16), which adds G A^T
 // with one more MFMA pass over the rank.
+//
+// Several projections of one input (q/k/v, gate/up) sum their input gradients:
+//     dX = sum_g (dY_g D_g + G_g A_g^T),   G_g = s dY_g B_g^T.
+// The reduction then runs over the concatenated d_out of all projections (the
+// table switches the dY, weight and B operands at each projection's first step).
+// At the end of a projection's steps its G_g is flushed, bf16, into columns
+// g r .. g r + r - 1 of g_out [T][n r] and the accumulator restarts; every
+// column tile writes the same bits there. The epilogue reads the tile's rows back
+// and adds [G_0 .. G_n-1] [A_0 .. A_n-1]^T in one MFMA pass over n r.
 #include <type_traits>
 
 #include "device_common.h"
@@ -28,12 +37,10 @@ constexpr int kDStride = 256 + 32;    // deq weight tile rows: 256 bf16 + 64 B p
 constexpr int kDElems = 64 * kDStride;
 constexpr int kBStride = 72;          // B slice rows: 64 bf16 + 16 B pad
 
-template <int RU, int RE>
-__global__ __launch_bounds__(kThreads) void lora_dx_kernel(
-    int T, int K, int N, int r, float s, const uint16_t* __restrict__ dy,
-    const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ dx,
-    uint16_t* __restrict__ g_out) {
+template <int RU, int RE, bool MULTI>
+__global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, float s, const DxTable tab,
+                                                           uint16_t* __restrict__ dx,
+                                                           uint16_t* __restrict__ g_out) {
   __shared__ __align__(1024) float lut[16];  // first in LDS: level addresses need no base
   __shared__ __align__(16) uint16_t ys0[kTileElems];
   __shared__ __align__(16) uint16_t ys1[kTileElems];
@@ -50,29 +57,49 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
   tile_coords(xcd_remap(blockIdx.x, mt * kt_tiles), mt, kt_tiles, 4, tm, tk);
   const int m0 = tm * BM, k0 = tk * BN;
   const int K2 = K / 2, KB = K / 64;
-  const int NS = (N + BK - 1) / BK;  // reduction steps over d_out
+  const int NS = tab.step_end[tab.n - 1];  // reduction steps over all d_out
+  constexpr bool multi = MULTI;
+  const int R = tab.n * r;  // g_out row length
 
   if (tid < 16) lut[tid] = nf4_level(tid);
 
   // ---- buffer resources: out-of-range loads return zeros ------------------------
+  // Several projections: each load stream (dY one step ahead; codes, absmax and
+  // B two steps ahead) keeps its projection's descriptors and offsets in
+  // registers and moves to the next projection when its step crosses a boundary
+  // (steps advance by one, every projection has at least one), so the loop reads
+  // the table only at those crossings. Steps past the end stay in the last
+  // projection beyond its range: their loads read zeros or unused bytes.
   const int rows_t = min(T - m0, BM);
-  const auto rs_y = make_rsrc(dy + static_cast<size_t>(m0) * N, static_cast<uint32_t>(rows_t) * N * 2);
-  const auto rs_c = make_rsrc(codes + k0 / 2, static_cast<uint32_t>(static_cast<size_t>(N) * K2 - k0 / 2));
-  const auto rs_s = make_rsrc(absmax + k0 / 64, static_cast<uint32_t>((static_cast<size_t>(N) * KB - k0 / 64) * 4));
-  const auto rs_b = make_rsrc(B, static_cast<uint32_t>(r) * N * 2);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   // dY: wave w fills rows 32 w .. 32 w + 31 of the [256][64] tile, swizzled
+  const int N0 = tab.N[0];
   uint32_t yvoff[4];
+  auto set_yvoff = [&](int Ng) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = (wave * 4 + q) * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-    yvoff[q] = static_cast<uint32_t>(row) * N * 2 + chunk * 16;
-  }
+    for (int q = 0; q < 4; ++q) {
+      const int row = (wave * 4 + q) * 8 + (lane >> 3);
+      yvoff[q] = static_cast<uint32_t>(row) * Ng * 2 + ((lane & 7) ^ ((row >> 1) & 7)) * 16;
+    }
+  };
+  set_yvoff(N0);
+  auto rs_y = make_rsrc(tab.dy[0] + static_cast<size_t>(m0) * N0, static_cast<uint32_t>(rows_t) * N0 * 2);
+  int y_g = 0, y_beg = 0, y_end = tab.step_end[0];
   auto load_y_lds = [&](int st, uint16_t* stage) {
+    if constexpr (MULTI) {
+      if (st >= y_end && y_g + 1 < tab.n) {
+        ++y_g;
+        y_beg = y_end;
+        y_end = tab.step_end[y_g];
+        const int Ng = tab.N[y_g];
+        rs_y = make_rsrc(tab.dy[y_g] + static_cast<size_t>(m0) * Ng, static_cast<uint32_t>(rows_t) * Ng * 2);
+        set_yvoff(Ng);
+      }
+    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) buf_load16_lds(rs_y, stage + (wave_u * 4 + q) * 512, yvoff[q], st * BK * 2);
+    for (int q = 0; q < 4; ++q)
+      buf_load16_lds(rs_y, stage + (wave_u * 4 + q) * 512, yvoff[q], (st - y_beg) * BK * 2);
   };
   // weight codes: row nl = tid >> 3 of the 64-row step, 32 columns (one half of
   // an NF4 block) at run tid & 7 of the 256-column tile
@@ -82,16 +109,34 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
   // B slice: row j = tid >> 3 (< RU), 8 columns at chunk tid & 7; columns past
   // d_out are zeroed here (the buffer range would only stop them at the end of B)
   const int bj = tid >> 3, bch = tid & 7;
-  const uint32_t bvoff = static_cast<uint32_t>(bj) * N * 2 + bch * 16;
   uint4 creg[2], breg[2];
   float sreg[2];
   // Three loads per thread and step (rows j >= r fall outside rs_b and read
   // zeros), so every wave can wait on the same vmcnt.
+  auto rs_c = make_rsrc(tab.codes[0] + k0 / 2, static_cast<uint32_t>(static_cast<size_t>(N0) * K2 - k0 / 2));
+  auto rs_s = make_rsrc(tab.absmax[0] + k0 / 64, static_cast<uint32_t>((static_cast<size_t>(N0) * KB - k0 / 64) * 4));
+  auto rs_b = make_rsrc(tab.B[0], static_cast<uint32_t>(r) * N0 * 2);
+  uint32_t bvoff = static_cast<uint32_t>(bj) * N0 * 2 + bch * 16;
+  int w_g = 0, w_beg = 0, w_end = tab.step_end[0], w_N = N0;
   auto load_regs = [&](int st, int slot) {
-    creg[slot] = buf_load16(rs_c, cvoff, st * 64 * K2);
-    sreg[slot] = __uint_as_float(buf_load4(rs_s, svoff, st * 64 * KB * 4));
-    const uint4 v = buf_load16(rs_b, bvoff, st * BK * 2);
-    breg[slot] = (st * BK + bch * 8 < N) ? v : uint4{0u, 0u, 0u, 0u};
+    if constexpr (MULTI) {
+      if (st >= w_end && w_g + 1 < tab.n) {
+        ++w_g;
+        w_beg = w_end;
+        w_end = tab.step_end[w_g];
+        w_N = tab.N[w_g];
+        rs_c = make_rsrc(tab.codes[w_g] + k0 / 2, static_cast<uint32_t>(static_cast<size_t>(w_N) * K2 - k0 / 2));
+        rs_s = make_rsrc(tab.absmax[w_g] + k0 / 64,
+                         static_cast<uint32_t>((static_cast<size_t>(w_N) * KB - k0 / 64) * 4));
+        rs_b = make_rsrc(tab.B[w_g], static_cast<uint32_t>(r) * w_N * 2);
+        bvoff = static_cast<uint32_t>(bj) * w_N * 2 + bch * 16;
+      }
+    }
+    const int ls = st - w_beg;
+    creg[slot] = buf_load16(rs_c, cvoff, ls * 64 * K2);
+    sreg[slot] = __uint_as_float(buf_load4(rs_s, svoff, ls * 64 * KB * 4));
+    const uint4 v = buf_load16(rs_b, bvoff, ls * BK * 2);
+    breg[slot] = (ls * BK + bch * 8 < w_N) ? v : uint4{0u, 0u, 0u, 0u};
   };
 
   const int fkey = (l32 >> 1) & 7;
@@ -242,9 +287,43 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
     wait_vmem_upto<3>();
     __syncthreads();
   };
+  // Several projections: at the end of projection g's steps, store bf16(s G_g)
+  // for this wave's rows into g_out columns g r .. and restart the accumulator.
+  int gseg = 0, gend = tab.step_end[0];
+  auto flush = [&](int st) {
+    if constexpr (!MULTI) return;
+    if (st + 1 != gend) return;
+    const size_t col0 = static_cast<size_t>(gseg) * r;
+#pragma unroll
+    for (int u = 0; u < RU / 32; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = wm * 128 + wn * 32 + mfma32_row(e, lane), col = u * 32 + l32;
+        if (col < r && m0 + row < T)
+          g_out[static_cast<size_t>(m0 + row) * R + col0 + col] = to_bf16(s * gacc[u][e]);
+        gacc[u][e] = 0.f;
+      }
+    if constexpr (kG16) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = wm * 128 + wn * 32 + rb * 16 + 4 * lq + e;
+          if (l16 < r && m0 + row < T)
+            g_out[static_cast<size_t>(m0 + row) * R + col0 + l16] = to_bf16(s * gacc16[rb][e]);
+          gacc16[rb][e] = 0.f;
+        }
+    }
+    ++gseg;
+    if (gseg < tab.n) gend = tab.step_end[gseg];
+  };
   for (int st = 0; st < NS; st += 2) {
     kstep(st, std::integral_constant<int, 0>{});
-    if (st + 1 < NS) kstep(st + 1, std::integral_constant<int, 1>{});
+    flush(st);
+    if (st + 1 < NS) {
+      kstep(st + 1, std::integral_constant<int, 1>{});
+      flush(st + 1);
+    }
   }
 
   // ---- epilogue: acc += bf16(G) A^T ----------------------------------------------
@@ -254,33 +333,47 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
     if constexpr (kPad) return row * ES + col;
     else return swz64(row, col >> 3) + (col & 7);
   };
-  uint16_t* gs = ys0;  // [256][RE] bf16(G), G = s dY B^T
-  uint16_t* at = ys1;  // [256][RE] rows k of A (A is [d_in, r] row-major)
-#pragma unroll
-  for (int u = 0; u < RU / 32; ++u)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = wm * 128 + wn * 32 + mfma32_row(e, lane), col = u * 32 + l32;
-      const uint16_t gv = to_bf16(s * gacc[u][e]);
-      if (col < RE) gs[ep(row, col)] = gv;
-      if (tk == 0 && col < r && m0 + row < T) g_out[static_cast<size_t>(m0 + row) * r + col] = gv;
+  uint16_t* gs = ys0;  // [256][RE] bf16(G), G = s dY B^T (all projections side by side)
+  uint16_t* at = ys1;  // [256][RE] rows k of A (A is [d_in, r] row-major), projections side by side
+  if constexpr (MULTI) {
+    if (dx == nullptr) return;
+    __threadfence_block();  // this tile's G stores, before other waves read them back
+    __syncthreads();
+    for (int e = tid; e < 256 * (RE / 8); e += kThreads) {
+      const int row = e / (RE / 8), jc = e - row * (RE / 8);
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (jc * 8 < R && m0 + row < T)
+        v = *reinterpret_cast<const uint4*>(g_out + static_cast<size_t>(m0 + row) * R + jc * 8);
+      *reinterpret_cast<uint4*>(gs + ep(row, jc * 8)) = v;
     }
-  if constexpr (kG16) {
+  } else {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int u = 0; u < RU / 32; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = wm * 128 + wn * 32 + rb * 16 + 4 * lq + e;
-        const uint16_t gv = to_bf16(s * gacc16[rb][e]);
-        gs[ep(row, l16)] = gv;
-        if (tk == 0 && l16 < r && m0 + row < T) g_out[static_cast<size_t>(m0 + row) * r + l16] = gv;
+      for (int e = 0; e < 16; ++e) {
+        const int row = wm * 128 + wn * 32 + mfma32_row(e, lane), col = u * 32 + l32;
+        const uint16_t gv = to_bf16(s * gacc[u][e]);
+        if (col < RE) gs[ep(row, col)] = gv;
+        if (tk == 0 && col < r && m0 + row < T) g_out[static_cast<size_t>(m0 + row) * r + col] = gv;
       }
+    if constexpr (kG16) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = wm * 128 + wn * 32 + rb * 16 + 4 * lq + e;
+          const uint16_t gv = to_bf16(s * gacc16[rb][e]);
+          gs[ep(row, l16)] = gv;
+          if (tk == 0 && l16 < r && m0 + row < T) g_out[static_cast<size_t>(m0 + row) * r + l16] = gv;
+        }
+    }
   }
   for (int e = tid; e < 256 * (RE / 8); e += kThreads) {
     const int c = e / (RE / 8), jc = e - c * (RE / 8);
+    const int g = jc * 8 / r, j0 = jc * 8 - g * r;  // r % 8 == 0: a chunk never straddles projections
     uint4 v = {0u, 0u, 0u, 0u};
-    if (k0 + c < K && jc * 8 < r)
-      v = *reinterpret_cast<const uint4*>(A + static_cast<size_t>(k0 + c) * r + jc * 8);
+    if (k0 + c < K && jc * 8 < R)
+      v = *reinterpret_cast<const uint4*>(tab.A[g] + static_cast<size_t>(k0 + c) * r + j0);
     *reinterpret_cast<uint4*>(at + ep(c, jc * 8)) = v;
   }
   __syncthreads();
@@ -312,13 +405,11 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
     }
 }
 
-template <int RU, int RE>
-hipError_t launch_dx_t(int T, int K, int N, int r, float s, const uint16_t* dy, const uint8_t* codes,
-                       const float* absmax, const uint16_t* A, const uint16_t* B, uint16_t* dx,
-                       uint16_t* g_out, hipStream_t stream) {
+template <int RU, int RE, bool MULTI>
+hipError_t launch_dx_t(int T, int K, int r, float s, const DxTable& tab, uint16_t* dx, uint16_t* g_out,
+                       hipStream_t stream) {
   const int tiles = ((T + BM - 1) / BM) * ((K + BN - 1) / BN);
-  lora_dx_kernel<RU, RE><<<tiles, kThreads, 0, stream>>>(T, K, N, r, s, dy, codes, absmax, A, B, dx,
-                                                          g_out);
+  lora_dx_kernel<RU, RE, MULTI><<<tiles, kThreads, 0, stream>>>(T, K, r, s, tab, dx, g_out);
   return hipGetLastError();
 }
 
@@ -326,16 +417,52 @@ hipError_t launch_dx_t(int T, int K, int N, int r, float s, const uint16_t* dy, 
 
 bool lora_dx_supported(int r) { return r % 8 == 0 && r <= 64; }
 
+bool lora_dx_multi_supported(int n_proj, const int* N, int r) {
+  if (n_proj < 1 || n_proj > kMaxProj || r % 8 != 0 || n_proj * r > 64) return false;
+  for (int g = 0; g < n_proj; ++g)
+    if (N[g] % BK != 0) return false;
+  return true;
+}
+
+hipError_t launch_lora_dx_table(int T, int K, int r, float s, const DxTable& tab, uint16_t* dx,
+                                uint16_t* g_out, hipStream_t stream) {
+  const int R = tab.n * r;
+  if (tab.n == 1) {
+    switch ((r + 15) / 16) {
+      case 1: return launch_dx_t<16, 16, false>(T, K, r, s, tab, dx, g_out, stream);
+      case 2: return launch_dx_t<32, 32, false>(T, K, r, s, tab, dx, g_out, stream);
+      case 3: return launch_dx_t<64, 48, false>(T, K, r, s, tab, dx, g_out, stream);
+      case 4: return launch_dx_t<64, 64, false>(T, K, r, s, tab, dx, g_out, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  // several projections: RU from r, RE from n r (<= 64)
+  if (r <= 16) {
+    switch ((R + 15) / 16) {
+      case 1: return launch_dx_t<16, 16, true>(T, K, r, s, tab, dx, g_out, stream);
+      case 2: return launch_dx_t<16, 32, true>(T, K, r, s, tab, dx, g_out, stream);
+      case 3: return launch_dx_t<16, 48, true>(T, K, r, s, tab, dx, g_out, stream);
+      case 4: return launch_dx_t<16, 64, true>(T, K, r, s, tab, dx, g_out, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (r <= 32 && R <= 64) return launch_dx_t<32, 64, true>(T, K, r, s, tab, dx, g_out, stream);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* dy,
                           const uint8_t* codes, const float* absmax, const uint16_t* A,
                           const uint16_t* B, uint16_t* dx, uint16_t* g_out, hipStream_t stream) {
-  switch ((r + 15) / 16) {
-    case 1: return launch_dx_t<16, 16>(T, K, N, r, s, dy, codes, absmax, A, B, dx, g_out, stream);
-    case 2: return launch_dx_t<32, 32>(T, K, N, r, s, dy, codes, absmax, A, B, dx, g_out, stream);
-    case 3: return launch_dx_t<64, 48>(T, K, N, r, s, dy, codes, absmax, A, B, dx, g_out, stream);
-    case 4: return launch_dx_t<64, 64>(T, K, N, r, s, dy, codes, absmax, A, B, dx, g_out, stream);
-    default: return hipErrorInvalidValue;
-  }
+  DxTable tab{};
+  tab.n = 1;
+  tab.step_end[0] = (N + BK - 1) / BK;
+  tab.N[0] = N;
+  tab.dy[0] = dy;
+  tab.codes[0] = codes;
+  tab.absmax[0] = absmax;
+  tab.A[0] = A;
+  tab.B[0] = B;
+  return launch_lora_dx_table(T, K, r, s, tab, dx, g_out, stream);
 }
 
 }  // namespace lnf4

@@ -34,7 +34,7 @@ __device__ __forceinline__ int m_off(int t, int c) {
 
 template <int RU>
 __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(
-    int T, int K, int N, int r, int cb_a, int t_per_split, const uint16_t* __restrict__ x,
+    int T, int K, int N, int ra, int rb, int cb_a, int t_per_split, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ dy, const uint16_t* __restrict__ u,
     float* __restrict__ part_a, float* __restrict__ part_b) {
   // V stages hold [64][r] bf16 contiguous (64 r * 2 bytes); fragment reads of the
@@ -47,6 +47,7 @@ __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool job_a = static_cast<int>(blockIdx.x) < cb_a;
   const int cb = job_a ? blockIdx.x : blockIdx.x - cb_a;
+  const int r = job_a ? ra : rb;  // rank of this job's V (its row length)
   const int C = job_a ? K : N;
   const uint16_t* M = job_a ? x : dy;
   const uint16_t* V = job_a ? g : u;
@@ -165,24 +166,26 @@ __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(
     }
 }
 
-// dA[c][j] = sum_split part_a[split][j][c];  dB[j][c] = s sum_split part_b[split][j][c]
+// dA[c][j] = sum_split part_a[split][j][c], columns j split into projections of
+// da.gw ranks (dA_g[c][j - g gw]);  dB[j][c] = s sum_split part_b[split][j][c]
 __global__ __launch_bounds__(256) void skinny_reduce2_kernel(const float* __restrict__ part_a,
                                                              const float* __restrict__ part_b,
-                                                             int splits, int K, int N, int r, float s,
-                                                             uint16_t* __restrict__ dA,
+                                                             int splits, int K, int N, int ra, int rb,
+                                                             float s, const DaOut da,
                                                              uint16_t* __restrict__ dB) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t na = static_cast<int64_t>(K) * r;
+  const int64_t na = static_cast<int64_t>(K) * ra;
   if (idx < na) {
     const int j = static_cast<int>(idx / K), c = static_cast<int>(idx - static_cast<int64_t>(j) * K);
     float sum = 0.f;
-    for (int sp = 0; sp < splits; ++sp) sum += part_a[(static_cast<size_t>(sp) * r + j) * K + c];
-    dA[static_cast<size_t>(c) * r + j] = to_bf16(sum);
-  } else if (idx < na + static_cast<int64_t>(N) * r) {
+    for (int sp = 0; sp < splits; ++sp) sum += part_a[(static_cast<size_t>(sp) * ra + j) * K + c];
+    const int g = j / da.gw, jj = j - g * da.gw;
+    da.p[g][static_cast<size_t>(c) * da.gw + jj] = to_bf16(sum);
+  } else if (idx < na + static_cast<int64_t>(N) * rb) {
     const int64_t i2 = idx - na;
     const int j = static_cast<int>(i2 / N), c = static_cast<int>(i2 - static_cast<int64_t>(j) * N);
     float sum = 0.f;
-    for (int sp = 0; sp < splits; ++sp) sum += part_b[(static_cast<size_t>(sp) * r + j) * N + c];
+    for (int sp = 0; sp < splits; ++sp) sum += part_b[(static_cast<size_t>(sp) * rb + j) * N + c];
     dB[static_cast<size_t>(j) * N + c] = to_bf16(s * sum);
   }
 }
@@ -204,25 +207,25 @@ int skinny_splits(int64_t T, int64_t K, int64_t N) {
   return static_cast<int>((T + per - 1) / per);
 }
 
-hipError_t launch_lora_skinny(int T, int K, int N, int r, float s, const uint16_t* x,
+hipError_t launch_lora_skinny(int T, int K, int N, int ra, int rb, float s, const uint16_t* x,
                               const uint16_t* g, const uint16_t* dy, const uint16_t* u,
-                              float* part_a, float* part_b, int splits, uint16_t* dA,
+                              float* part_a, float* part_b, int splits, const DaOut& da,
                               uint16_t* dB, hipStream_t stream) {
   int per = (T + splits - 1) / splits;
   per = ((per + TT - 1) / TT) * TT;
   const int cb_a = (K + BC - 1) / BC, cb_b = (N + BC - 1) / BC;
   const dim3 grid(cb_a + cb_b, splits);
-  if (r <= 32)
-    skinny_partial_kernel<32><<<grid, kThreads, 0, stream>>>(T, K, N, r, cb_a, per, x, g, dy, u, part_a,
-                                                             part_b);
+  if ((K > 0 ? ra : 0) <= 32 && (N > 0 ? rb : 0) <= 32)
+    skinny_partial_kernel<32><<<grid, kThreads, 0, stream>>>(T, K, N, ra, rb, cb_a, per, x, g, dy, u,
+                                                             part_a, part_b);
   else
-    skinny_partial_kernel<64><<<grid, kThreads, 0, stream>>>(T, K, N, r, cb_a, per, x, g, dy, u, part_a,
-                                                             part_b);
+    skinny_partial_kernel<64><<<grid, kThreads, 0, stream>>>(T, K, N, ra, rb, cb_a, per, x, g, dy, u,
+                                                             part_a, part_b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t total = static_cast<int64_t>(K + N) * r;
+  const int64_t total = static_cast<int64_t>(K) * ra + static_cast<int64_t>(N) * rb;
   skinny_reduce2_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(
-      part_a, part_b, splits, K, N, r, s, dA, dB);
+      part_a, part_b, splits, K, N, ra, rb, s, da, dB);
   return hipGetLastError();
 }
 

@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     assert names == sorted(["nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_fwd_multi",
                             "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_merge",
                             "lora_nf4_status_string", "lora_adamw_step", "lora_nf4_rslora_alpha",
-                            "nf4_absmax_quantize", "nf4_absmax_dequantize"])
+                            "nf4_absmax_quantize", "nf4_absmax_dequantize", "lora_nf4_bwd_multi",
+                            "lora_nf4_bwd_multi_workspace_bytes"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -165,6 +166,40 @@ def test_quantize_validation(lib):
     assert lib.nf4_quantize(P, 0, 4, 64, P + 64, P + (2 << 30), None) == LN_EALIAS
     assert lib.nf4_dequantize(P, P + (1 << 30), 4, 64, 3, P + (2 << 30), None) == LN_EINVAL
     assert lib.nf4_dequantize(P, P + (1 << 30), 4, 64, 0, P + 16, None) == LN_EALIAS
+
+
+def test_bwd_multi_validation(lib):
+    import ctypes
+    n = 3
+    base = [P + (i << 30) for i in range(40)]
+    arr = lambda vals: (ctypes.c_void_p * len(vals))(*vals)
+    d_out = (ctypes.c_int64 * n)(64, 64, 128)
+
+    def call(T=64, K=128, r=16, alpha=16.0, nproj=n, ws_bytes=1 << 30, **kw):
+        a = dict(x=base[0], dy=arr(base[1:4]), c=arr(base[4:7]), s=arr(base[7:10]), A=arr(base[10:13]),
+                 B=arr(base[13:16]), u=None, dx=base[16], dA=arr(base[17:20]), dB=arr(base[20:23]), ws=base[23],
+                 d=d_out)
+        a.update(kw)
+        return lib.lora_nf4_bwd_multi(T, K, nproj, a["d"], r, alpha, a["x"], a["dy"], a["c"], a["s"], a["A"],
+                                      a["B"], a["u"], a["dx"], a["dA"], a["dB"], a["ws"], ws_bytes, None)
+
+    assert call(nproj=0) == LN_EINVAL
+    assert call(nproj=9) == LN_EINVAL
+    assert call(dy=None) == LN_EINVAL
+    assert call(dA=arr([base[17], None, base[19]])) == LN_EINVAL
+    assert call(r=0) == LN_ERANK
+    assert call(K=96) == LN_ESHAPE
+    assert call(d=(ctypes.c_int64 * n)(64, 60, 128)) == LN_ESHAPE
+    assert call(dx=base[16] + 8) == LN_EALIGN
+    assert call(ws=None) == LN_EWORKSPACE
+    assert call(ws_bytes=16) == LN_EWORKSPACE
+    assert call(ws=base[23] + 16) == LN_EALIGN
+    assert call(dB=arr([base[20], base[1], base[22]])) == LN_EALIAS  # a dB on top of a dy
+    assert call(dx=base[10]) == LN_EALIAS  # dx on top of A[0]
+    need = lib.lora_nf4_bwd_multi_workspace_bytes(64, 128, n, d_out, 16)
+    assert need > 0
+    assert lib.lora_nf4_bwd_multi_workspace_bytes(0, 128, n, d_out, 16) == 0
+    assert lib.lora_nf4_bwd_multi_workspace_bytes(64, 96, n, d_out, 16) == 0
 
 
 def test_adamw_validation(lib):
