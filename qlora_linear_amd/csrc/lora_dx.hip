@@ -34,6 +34,11 @@ constexpr int kThreads = 512;
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kTileElems = 256 * 64;  // dY tile [256][64]
 constexpr int kDStride = 256 + 32;    // deq weight tile rows: 256 bf16 + 64 B pad
+// Row n of the dequantized weight tile starts at n kDStride + dshift(n): rows
+// four apart (one transposing read covers four consecutive rows) are shifted by
+// 16 bytes per group of four, which spreads the 16-byte dequantization stores
+// of a 16-lane group over all 64 banks.
+__device__ __forceinline__ int dshift(int n) { return 8 * ((n >> 2) & 3); }
 constexpr int kDElems = 64 * kDStride;
 constexpr int kBStride = 72;          // B slice rows: 64 bf16 + 16 B pad
 
@@ -103,7 +108,11 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
   };
   // weight codes: row nl = tid >> 3 of the 64-row step, 32 columns (one half of
   // an NF4 block) at run tid & 7 of the 256-column tile
-  const int nl = tid >> 3, run = tid & 7;
+  // (thread bits: [1:0] low run, [3:2] low row group, [4] high run, [6:5] high row
+  // group, [8:7] row within the group of four; each 16 lanes then store to
+  // distinct banks)
+  const int run = (tid & 3) | (((tid >> 4) & 1) << 2);
+  const int nl = 4 * (((tid >> 2) & 3) | (((tid >> 5) & 3) << 2)) + ((tid >> 7) & 3);
   const uint32_t cvoff = static_cast<uint32_t>(nl) * K2 + run * 16;
   const uint32_t svoff = (static_cast<uint32_t>(nl) * KB + (run >> 1)) * 4;
   // B slice: row j = tid >> 3 (< RU), 8 columns at chunk tid & 7; columns past
@@ -147,7 +156,10 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
   const int ga_off = a_off + wn * 2048;     // this wave's 32 rows of G
   // transposed weight fragment: 16-lane group g, lane m within it
   const int g16 = lane >> 4, m16 = lane & 15;
-  const int d_off = ((g16 >> 1) * 8 + (m16 >> 2)) * kDStride + wn * 64 + (g16 & 1) * 16 + 4 * (m16 & 3);
+  // rows 8 (g16 >> 1) + (m16 >> 2) (+ 4 for the second read): row groups 2 (g16 >> 1)
+  // and 2 (g16 >> 1) + 1, so the second read sits one group shift further
+  const int d_off = ((g16 >> 1) * 8 + (m16 >> 2)) * kDStride + dshift((g16 >> 1) * 8) + wn * 64 +
+                    (g16 & 1) * 16 + 4 * (m16 & 3);
   const int gb_off = l32 * kBStride + lh * 8;  // + u * 32 * kBStride + ks * 16
   // r <= 16: 16 x 16 x 32 fragments of G rows wm * 128 + wn * 32 + 16 rb + (lane & 15)
   constexpr bool kG16 = RU == 16;
@@ -180,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
     o.w = pack_bf16x2(v[6], v[7]);
     *reinterpret_cast<uint4*>(dst) = o;
   };
-  const int dw_off = nl * kDStride + run * 32;  // + q * 8
+  const int dw_off = nl * kDStride + dshift(nl) + run * 32;  // + q * 8
   auto store_b = [&](uint16_t* bs, const uint4& v) {
     if (bj < RU) *reinterpret_cast<uint4*>(bs + bj * kBStride + bch * 8) = v;
   };
@@ -239,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const uint16_t* p = dc + d_off + ks * 16 * kDStride + j * 32;
-        const uint2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * kDStride);
+        const uint2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * kDStride + 8);
         f.b[j] = uint4{lo.x, lo.y, hi.x, hi.y};
       }
       if constexpr (kG16) {
