@@ -94,8 +94,9 @@ inline bool fits_buffer(int64_t T, int64_t K, int64_t N) {
 }
 
 // Rank-r gradients dA, dB in one launch plus one reduce (ranks % 8 == 0, <= 64):
-// dA = x^T G over K columns with G [T][ra], dB = s U^T dY over N columns with
-// U [T][rb]; K = 0 or N = 0 leaves that job out. dA's ra columns are split into
+// dA = x^T G over K columns with G [T][ra] at row stride vsa (>= ra: a column
+// slice of a wider array), dB = s U^T dY over N columns with U [T][rb]; K = 0 or
+// N = 0 leaves that job out. dA's ra columns are split into
 // projections of da.gw columns each, projection g stored at da.p[g] as [K][gw].
 // part_a: [splits][ra][K] fp32, part_b: [splits][rb][N] fp32.
 struct DaOut {
@@ -104,7 +105,7 @@ struct DaOut {
 };
 bool lora_skinny_supported(int r);
 int skinny_splits(int64_t T, int64_t K, int64_t N);
-hipError_t launch_lora_skinny(int T, int K, int N, int ra, int rb, float s, const uint16_t* x,
+hipError_t launch_lora_skinny(int T, int K, int N, int ra, int rb, int vsa, float s, const uint16_t* x,
                               const uint16_t* g, const uint16_t* dy, const uint16_t* u,
                               float* part_a, float* part_b, int splits, const DaOut& da,
                               uint16_t* dB, hipStream_t stream);
@@ -131,14 +132,15 @@ hipError_t launch_lora_bwd(int T, int K, int N, int r, float s, const uint16_t* 
                            const BwdPlan& plan, hipStream_t stream);
 
 // Backward of several projections that share x (dX summed over them). Fused: one
-// dX launch over all projections (G side by side in [T][n r]), one pass over x
-// for every dA with the first projection's dB, one pass per further dB.
-// Otherwise one backward per projection, dX accumulated from a scratch copy.
+// dX launch over all projections (G side by side in [T][n r]); for n r <= 64 one
+// pass over x for every dA with the first projection's dB and one pass per further
+// dB, else one pass per projection for its dA and dB. Otherwise (ragged d_out, few
+// tokens) one backward per projection, dX accumulated from a scratch copy.
 struct BwdMultiPlan {
   bool fused;
   int n, R;                   // projections, n r
-  int splits_a;               // fused: token splits of the dA pass (and the first dB)
-  int splits_b[kMaxProj];     // fused: token splits of the dB passes of projections 1 ..
+  int splits_a;               // fused: token splits of the first rank-r pass
+  int splits_b[kMaxProj];     // fused: token splits of the passes of projections 1 ..
   size_t off_g, off_u, off_pa, off_pb;  // fused
   size_t off_single, off_dxt;           // per-projection fallback
   size_t bytes;

@@ -378,7 +378,7 @@ hipError_t launch_bwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
     DaOut da{};
     da.p[0] = dA;
     da.gw = r;
-    return launch_lora_skinny(T, K, N, r, r, s, x, g, dy, uu, pa, pb, p.splits_a, da, dB, stream);
+    return launch_lora_skinny(T, K, N, r, r, r, s, x, g, dy, uu, pa, pb, p.splits_a, da, dB, stream);
   }
   const int tca = (T + p.splits_a - 1) / p.splits_a;
   const int tcb = (T + p.splits_b - 1) / p.splits_b;
@@ -512,8 +512,8 @@ BwdMultiPlan plan_bwd_multi(int64_t T, int64_t K, int n, const int* N, int r) {
   BwdMultiPlan p{};
   p.n = n;
   p.R = n * r;
-  bool fused = n > 1 && lora_dx_multi_supported(n, N, r) && lora_skinny_supported(p.R) &&
-               !lora_dx_stream_supported(T, r);
+  bool fused = n > 1 && lora_dx_multi_supported(n, N, r) && lora_skinny_supported(r) &&
+               !lora_dx_stream_supported(T, r) && static_cast<int64_t>(T) * p.R * 2 < (int64_t(1) << 31);
   for (int g = 0; g < n && fused; ++g) fused = fits_buffer(T, K, N[g]);
   p.fused = fused;
   size_t off = 0;
@@ -522,14 +522,20 @@ BwdMultiPlan plan_bwd_multi(int64_t T, int64_t K, int n, const int* N, int r) {
     off = align256(off + static_cast<size_t>(T) * p.R * 2);
     p.off_u = off;
     off = align256(off + static_cast<size_t>(n) * T * r * 2);
+    // n r <= 64: one pass over x for every dA (rank n r) with the first dB, then
+    // one pass per further dB; wider: one pass per projection for its dA and dB
+    // (G read as a column slice of the side-by-side array)
+    const bool one_pass = lora_skinny_supported(p.R);
     p.splits_a = skinny_splits(T, K, N[0]);
+    size_t pa = static_cast<size_t>(p.splits_a) * K * (one_pass ? p.R : r) * 4;
     size_t pb = static_cast<size_t>(p.splits_a) * N[0] * r * 4;
     for (int g = 1; g < n; ++g) {
-      p.splits_b[g] = skinny_splits(T, 0, N[g]);
+      p.splits_b[g] = skinny_splits(T, one_pass ? 0 : K, N[g]);
+      if (!one_pass) pa = std::max(pa, static_cast<size_t>(p.splits_b[g]) * K * r * 4);
       pb = std::max(pb, static_cast<size_t>(p.splits_b[g]) * N[g] * r * 4);
     }
     p.off_pa = off;
-    off = align256(off + static_cast<size_t>(p.splits_a) * K * p.R * 4);
+    off = align256(off + pa);
     p.off_pb = off;
     off = align256(off + pb);
   } else {
@@ -596,11 +602,21 @@ hipError_t launch_lora_bwd_multi(int T, int K, int n, const int* N, int r, float
   float* pb = reinterpret_cast<float*>(ws + p.off_pb);
   DaOut da{};
   da.gw = r;
-  for (int g = 0; g < n; ++g) da.p[g] = dA[g];
-  // dA of every projection from one pass over x (G side by side), with dB of the first
-  e = launch_lora_skinny(T, K, N[0], p.R, r, s, x, G, dy[0], uu[0], pa, pb, p.splits_a, da, dB[0], stream);
-  for (int g = 1; g < n && e == hipSuccess; ++g)
-    e = launch_lora_skinny(T, 0, N[g], p.R, r, s, x, G, dy[g], uu[g], pa, pb, p.splits_b[g], da, dB[g], stream);
+  if (lora_skinny_supported(p.R)) {
+    for (int g = 0; g < n; ++g) da.p[g] = dA[g];
+    // dA of every projection from one pass over x (G side by side), with dB of the first
+    e = launch_lora_skinny(T, K, N[0], p.R, r, p.R, s, x, G, dy[0], uu[0], pa, pb, p.splits_a, da, dB[0],
+                           stream);
+    for (int g = 1; g < n && e == hipSuccess; ++g)
+      e = launch_lora_skinny(T, 0, N[g], p.R, r, p.R, s, x, G, dy[g], uu[g], pa, pb, p.splits_b[g], da, dB[g],
+                             stream);
+    return e;
+  }
+  for (int g = 0; g < n && e == hipSuccess; ++g) {  // one pass per projection, G column slice g
+    da.p[0] = dA[g];
+    e = launch_lora_skinny(T, K, N[g], r, r, p.R, s, x, G + static_cast<size_t>(g) * r, dy[g], uu[g], pa, pb,
+                           g == 0 ? p.splits_a : p.splits_b[g], da, dB[g], stream);
+  }
   return e;
 }
 

@@ -345,18 +345,52 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
     if constexpr (kPad) return row * ES + col;
     else return swz64(row, col >> 3) + (col & 7);
   };
-  uint16_t* gs = ys0;  // [256][RE] bf16(G), G = s dY B^T (all projections side by side)
+  uint16_t* gs = ys0;  // [256][RE] bf16(G), G = s dY B^T (projections side by side)
   uint16_t* at = ys1;  // [256][RE] rows k of A (A is [d_in, r] row-major), projections side by side
+  // one MFMA pass over RE rank columns: acc += gs at^T
+  auto lora_pass = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < RE / 16; ++ks) {
+      uint4 a[4], b[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const uint4*>(gs + ep(wm * 128 + i * 32 + l32, ks * 16 + lh * 8));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const uint4*>(at + ep(wn * 64 + j * 32 + l32, ks * 16 + lh * 8));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+    }
+  };
+  // A^T columns c0 .. c0 + RE - 1 of the side-by-side projections
+  auto stage_at = [&](int c0) {
+    for (int e = tid; e < 256 * (RE / 8); e += kThreads) {
+      const int c = e / (RE / 8), jc = c0 + 8 * (e - c * (RE / 8));
+      const int g = jc / r, j0 = jc - g * r;  // r % 8 == 0: a chunk never straddles projections
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (k0 + c < K && jc < R)
+        v = *reinterpret_cast<const uint4*>(tab.A[g] + static_cast<size_t>(k0 + c) * r + j0);
+      *reinterpret_cast<uint4*>(at + ep(c, jc - c0)) = v;
+    }
+  };
   if constexpr (MULTI) {
     if (dx == nullptr) return;
     __threadfence_block();  // this tile's G stores, before other waves read them back
-    __syncthreads();
-    for (int e = tid; e < 256 * (RE / 8); e += kThreads) {
-      const int row = e / (RE / 8), jc = e - row * (RE / 8);
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (jc * 8 < R && m0 + row < T)
-        v = *reinterpret_cast<const uint4*>(g_out + static_cast<size_t>(m0 + row) * R + jc * 8);
-      *reinterpret_cast<uint4*>(gs + ep(row, jc * 8)) = v;
+    // n r may exceed RE: the rank columns are added RE at a time
+    for (int c0 = 0; c0 < R; c0 += RE) {
+      __syncthreads();  // previous pass (or the K-loop) done with gs and at
+      for (int e = tid; e < 256 * (RE / 8); e += kThreads) {
+        const int row = e / (RE / 8), jc = c0 + 8 * (e - row * (RE / 8));
+        uint4 v = {0u, 0u, 0u, 0u};
+        if (jc < R && m0 + row < T)
+          v = *reinterpret_cast<const uint4*>(g_out + static_cast<size_t>(m0 + row) * R + jc);
+        *reinterpret_cast<uint4*>(gs + ep(row, jc - c0)) = v;
+      }
+      stage_at(c0);
+      __syncthreads();
+      lora_pass();
     }
   } else {
 #pragma unroll
@@ -379,30 +413,10 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
           if (tk == 0 && l16 < r && m0 + row < T) g_out[static_cast<size_t>(m0 + row) * r + l16] = gv;
         }
     }
-  }
-  for (int e = tid; e < 256 * (RE / 8); e += kThreads) {
-    const int c = e / (RE / 8), jc = e - c * (RE / 8);
-    const int g = jc * 8 / r, j0 = jc * 8 - g * r;  // r % 8 == 0: a chunk never straddles projections
-    uint4 v = {0u, 0u, 0u, 0u};
-    if (k0 + c < K && jc * 8 < R)
-      v = *reinterpret_cast<const uint4*>(tab.A[g] + static_cast<size_t>(k0 + c) * r + j0);
-    *reinterpret_cast<uint4*>(at + ep(c, jc * 8)) = v;
-  }
-  __syncthreads();
-  if (dx == nullptr) return;
-#pragma unroll
-  for (int ks = 0; ks < RE / 16; ++ks) {
-    uint4 a[4], b[2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const uint4*>(gs + ep(wm * 128 + i * 32 + l32, ks * 16 + lh * 8));
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      b[j] = *reinterpret_cast<const uint4*>(at + ep(wn * 64 + j * 32 + l32, ks * 16 + lh * 8));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+    stage_at(0);
+    __syncthreads();
+    if (dx == nullptr) return;
+    lora_pass();
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -430,7 +444,7 @@ hipError_t launch_dx_t(int T, int K, int r, float s, const DxTable& tab, uint16_
 bool lora_dx_supported(int r) { return r % 8 == 0 && r <= 64; }
 
 bool lora_dx_multi_supported(int n_proj, const int* N, int r) {
-  if (n_proj < 1 || n_proj > kMaxProj || r % 8 != 0 || n_proj * r > 64) return false;
+  if (n_proj < 1 || n_proj > kMaxProj || r % 8 != 0 || r > 64) return false;
   for (int g = 0; g < n_proj; ++g)
     if (N[g] % BK != 0) return false;
   return true;
@@ -448,18 +462,21 @@ hipError_t launch_lora_dx_table(int T, int K, int r, float s, const DxTable& tab
       default: return hipErrorInvalidValue;
     }
   }
-  // several projections: RU from r, RE from n r (<= 64)
+  // several projections: RU from r, RE from n r (64 at most: wider sums take several passes)
+  const int RE = R >= 64 ? 64 : ((R + 15) / 16) * 16;
   if (r <= 16) {
-    switch ((R + 15) / 16) {
-      case 1: return launch_dx_t<16, 16, true>(T, K, r, s, tab, dx, g_out, stream);
-      case 2: return launch_dx_t<16, 32, true>(T, K, r, s, tab, dx, g_out, stream);
-      case 3: return launch_dx_t<16, 48, true>(T, K, r, s, tab, dx, g_out, stream);
-      case 4: return launch_dx_t<16, 64, true>(T, K, r, s, tab, dx, g_out, stream);
-      default: return hipErrorInvalidValue;
+    switch (RE) {
+      case 16: return launch_dx_t<16, 16, true>(T, K, r, s, tab, dx, g_out, stream);
+      case 32: return launch_dx_t<16, 32, true>(T, K, r, s, tab, dx, g_out, stream);
+      case 48: return launch_dx_t<16, 48, true>(T, K, r, s, tab, dx, g_out, stream);
+      default: return launch_dx_t<16, 64, true>(T, K, r, s, tab, dx, g_out, stream);
     }
   }
-  if (r <= 32 && R <= 64) return launch_dx_t<32, 64, true>(T, K, r, s, tab, dx, g_out, stream);
-  return hipErrorInvalidValue;
+  if (r <= 32) {
+    if (RE == 48) return launch_dx_t<32, 48, true>(T, K, r, s, tab, dx, g_out, stream);
+    return launch_dx_t<32, 64, true>(T, K, r, s, tab, dx, g_out, stream);
+  }
+  return launch_dx_t<64, 64, true>(T, K, r, s, tab, dx, g_out, stream);
 }
 
 hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* dy,

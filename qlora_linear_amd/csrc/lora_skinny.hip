@@ -34,7 +34,7 @@ __device__ __forceinline__ int m_off(int t, int c) {
 
 template <int RU>
 __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(
-    int T, int K, int N, int ra, int rb, int cb_a, int t_per_split, const uint16_t* __restrict__ x,
+    int T, int K, int N, int ra, int rb, int vsa, int cb_a, int t_per_split, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ dy, const uint16_t* __restrict__ u,
     float* __restrict__ part_a, float* __restrict__ part_b) {
   // V stages hold [64][r] bf16 contiguous (64 r * 2 bytes); fragment reads of the
@@ -47,7 +47,8 @@ __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool job_a = static_cast<int>(blockIdx.x) < cb_a;
   const int cb = job_a ? blockIdx.x : blockIdx.x - cb_a;
-  const int r = job_a ? ra : rb;  // rank of this job's V (its row length)
+  const int r = job_a ? ra : rb;      // rank of this job's V (the columns used)
+  const int vstr = job_a ? vsa : rb;  // V row stride (elements): G may be a column slice
   const int C = job_a ? K : N;
   const uint16_t* M = job_a ? x : dy;
   const uint16_t* V = job_a ? g : u;
@@ -62,8 +63,8 @@ __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(
   // read as zeros.
   const auto rs_m = make_rsrc(M + static_cast<size_t>(t_begin) * C,
                               static_cast<uint32_t>(t_end - t_begin) * C * 2);
-  const auto rs_v = make_rsrc(V + static_cast<size_t>(t_begin) * r,
-                              static_cast<uint32_t>(t_end - t_begin) * r * 2);
+  const auto rs_v = make_rsrc(V + static_cast<size_t>(t_begin) * vstr,
+                              static_cast<uint32_t>(t_end - t_begin - 1) * vstr * 2 + r * 2);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   // M stage: each wave fills 16 rows with eight 1 KB loads (2 rows each); lane i
@@ -77,11 +78,19 @@ __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(
     const int lunit = unit ^ (2 * (t & 3));
     mvoff[q] = static_cast<uint32_t>(t) * C * 2 + (c0 + lunit * 16 + half * 8) * 2;
   }
-  // V stage: 64 r bf16 contiguous = r / 8 KB pieces (r % 8 == 0). Every wave
-  // issues kVPW piece loads per step so all waves wait on the same vmcnt; pieces
-  // past r / 8 use an out-of-range offset and only write zeros into the stage.
+  // V stage: [64][r] bf16 contiguous in LDS = r / 8 KB pieces (r % 8 == 0); lane
+  // L of piece p brings elements 512 p + 8 L .. +7 of that block, i.e. token row
+  // (512 p + 8 L) / r, columns (512 p + 8 L) % r of V (row stride vstr). Every
+  // wave issues kVPW piece loads per step so all waves wait on the same vmcnt;
+  // pieces past r / 8 use an out-of-range offset and only write zeros.
   constexpr int kVPW = RU / 32;
   const int v_pieces = r / 8;
+  uint32_t vvoff[kVPW];
+#pragma unroll
+  for (int p = 0; p < kVPW; ++p) {
+    const int piece = wave * kVPW + p, e = piece * 512 + lane * 8;
+    vvoff[p] = piece < v_pieces ? static_cast<uint32_t>((e / r) * vstr + e % r) * 2 : 0x7FFFFFF0u;
+  }
   auto issue = [&](int st) {
     const int stage = st % kStages;
 #pragma unroll
@@ -90,8 +99,7 @@ __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(
 #pragma unroll
     for (int p = 0; p < kVPW; ++p) {
       const int piece = wave_u * kVPW + p;
-      buf_load16_lds(rs_v, &vs[stage][piece * 512], piece < v_pieces ? lane * 16 : 0x7FFFFFF0u,
-                     st * TT * r * 2 + piece * 1024);
+      buf_load16_lds(rs_v, &vs[stage][piece * 512], vvoff[p], st * TT * vstr * 2);
     }
   };
 
@@ -207,7 +215,7 @@ int skinny_splits(int64_t T, int64_t K, int64_t N) {
   return static_cast<int>((T + per - 1) / per);
 }
 
-hipError_t launch_lora_skinny(int T, int K, int N, int ra, int rb, float s, const uint16_t* x,
+hipError_t launch_lora_skinny(int T, int K, int N, int ra, int rb, int vsa, float s, const uint16_t* x,
                               const uint16_t* g, const uint16_t* dy, const uint16_t* u,
                               float* part_a, float* part_b, int splits, const DaOut& da,
                               uint16_t* dB, hipStream_t stream) {
@@ -216,10 +224,10 @@ hipError_t launch_lora_skinny(int T, int K, int N, int ra, int rb, float s, cons
   const int cb_a = (K + BC - 1) / BC, cb_b = (N + BC - 1) / BC;
   const dim3 grid(cb_a + cb_b, splits);
   if ((K > 0 ? ra : 0) <= 32 && (N > 0 ? rb : 0) <= 32)
-    skinny_partial_kernel<32><<<grid, kThreads, 0, stream>>>(T, K, N, ra, rb, cb_a, per, x, g, dy, u,
+    skinny_partial_kernel<32><<<grid, kThreads, 0, stream>>>(T, K, N, ra, rb, vsa, cb_a, per, x, g, dy, u,
                                                              part_a, part_b);
   else
-    skinny_partial_kernel<64><<<grid, kThreads, 0, stream>>>(T, K, N, ra, rb, cb_a, per, x, g, dy, u,
+    skinny_partial_kernel<64><<<grid, kThreads, 0, stream>>>(T, K, N, ra, rb, vsa, cb_a, per, x, g, dy, u,
                                                              part_a, part_b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -2,11 +2,12 @@
 oracle: dX summed over the projections, dA and dB of each, within the linear's
 tolerance (max|err| / max|ref| <= 1e-2).
 
-Cases cover the fused path (every d_out a multiple of 64, n r <= 64, T > 32:
-one dX launch over the concatenated d_out, one pass over x for every dA) with
-2, 3 and 4 projections and ranks 8 .. 32, ragged token counts and partial
-d_in tiles; and the per-projection path (a d_out not a multiple of 64, few
-tokens, n r > 64, no dX). One case runs the Qwen-14B-shaped q/k/v at full size
+Cases cover the fused path (every d_out a multiple of 64, T > 32: one dX
+launch over the concatenated d_out; for n r <= 64 one pass over x for every dA,
+wider sums in several epilogue passes and one dA pass per projection) with 2, 3
+and 4 projections and ranks 8 .. 64, ragged token counts and partial d_in
+tiles; and the per-projection path (a d_out not a multiple of 64, few tokens,
+no dX). One case runs the Qwen-14B-shaped q/k/v at full size
 (8192 tokens, 5120 -> 5120 each, r = 16) and checks sampled rows of dX and
 sampled columns of dA and dB against the oracle.
 """
@@ -52,7 +53,9 @@ CASES = [
     (100, 128, (64, 192), 8, True, True),           # fused, r = 8
     (150, 128, (72, 136), 16, True, True),          # d_out % 64 != 0: per projection
     (8, 192, (64, 64, 64), 16, True, True),         # few tokens: per projection (weight streaming)
-    (100, 192, (64, 128), 40, True, True),          # n r > 64: per projection
+    (100, 192, (64, 128), 40, True, True),          # fused, n r = 80 > 64: two epilogue passes, dA per projection
+    (260, 256, (128, 64, 64), 64, True, True),      # fused, rank 64 q/k/v-like: n r = 192
+    (200, 128, (64, 64, 64), 32, False, True),      # fused, n r = 96, U recomputed
     (300, 256, (256, 64, 64), 16, True, False),     # fused, dX not requested
 ]
 
