@@ -17,7 +17,9 @@ runs on); `cpu_baseline` times the CPU fp64 oracle on a bounded token sample of
 the same projection; `small_tokens` times forward and backward of the largest
 projection at a few tokens (the weight-streaming kernels), where the bound is
 reading the packed weight from HBM; `merge` times lora_nf4_merge of that
-projection (the 16-bit export, also HBM-bound). With --fuse, projections that read the same
+projection (the 16-bit export, also HBM-bound); `train_step` times the AdamW step of A and B and the
+absmax double quantization; `multi_projection` times Llama-3-8B q/k/v (r = 64, one x) as one
+lora_nf4_fwd_multi + lora_nf4_bwd_multi against separate calls. With --fuse, projections that read the same
 activations in a transformer layer (q/k/v, gate/up) share one x, run their
 forward as one lora_nf4_fwd_multi launch and their backward as one
 lora_nf4_bwd_multi call (dX summed over the group); the FLOPs counted are unchanged.
@@ -53,6 +55,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3-8b-q_proj",
                     help="one of: " + ", ".join(w.name for w in synth.WORKLOADS))
+    ap.add_argument("--no-multi", action="store_true",
+                    help="skip the q/k/v multi-projection leg (fused against separate calls)")
     ap.add_argument("--fuse", action="store_true",
                     help="q/k/v and gate/up share x and run one multi-projection forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -320,6 +324,80 @@ def train_step_run(lib, q, torch, d, w, sp, reps=50):
     return out
 
 
+def multi_projection_run(lib, q, torch, sp, reps=10):
+    """Llama-3-8B q/k/v (4096 -> 4096, 1024, 1024) at 8192 tokens, r = 64, sharing one
+    x: one fwd + bwd of the three projections as lora_nf4_fwd_multi + lora_nf4_bwd_multi
+    (dX summed over them) against three lora_nf4_fwd + three lora_nf4_bwd calls (three
+    separate dX, not summed). HIP events around `reps` back-to-back steps each."""
+    w = next(x for x in synth.WORKLOADS if x.name == "llama3-8b-attn-r64")
+    T, r = w.tokens, w.r
+    ins = [synth.projection_inputs(w, g, tensors=("W", "A", "B", "dY") if g else ("x", "W", "A", "B", "dY"))
+           for g in range(3)]
+    x = to_dev_bf16(ins[0]["x"])
+    K = w.projections[0].d_in
+    Ns = [w.projections[g].d_out for g in range(3)]
+    codes, absmax, A, B, dy = [], [], [], [], []
+    for inp in ins:
+        c, a = q.nf4_quantize(to_dev_bf16(inp["W"]))
+        codes.append(c), absmax.append(a)
+        A.append(to_dev_bf16(inp["A"])), B.append(to_dev_bf16(inp["B"])), dy.append(to_dev_bf16(inp["dY"]))
+    ys, us = q.lora_nf4_fwd_multi(x, codes, absmax, A, B, w.alpha)
+    dx = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    dxs = [torch.empty((T, K), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    dAs = [torch.empty((K, r), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    dBs = [torch.empty((r, N), dtype=torch.bfloat16, device="cuda") for N in Ns]
+    wsm = torch.empty(max(q.lora_nf4_bwd_multi_workspace_bytes(T, K, Ns, r), 256), dtype=torch.uint8, device="cuda")
+    wss = [torch.empty(max(q.lora_nf4_bwd_workspace_bytes(T, K, N, r), 256), dtype=torch.uint8, device="cuda")
+           for N in Ns]
+    import ctypes
+    arr = lambda ts: (ctypes.c_void_p * 3)(*[t.data_ptr() for t in ts])
+    cv = lambda a: ctypes.cast(a, ctypes.c_void_p)
+    d_out = (ctypes.c_int64 * 3)(*Ns)
+    keep = dict(c=arr(codes), a=arr(absmax), A=arr(A), B=arr(B), y=arr(ys), u=arr(us), dy=arr(dy), dA=arr(dAs),
+                dB=arr(dBs))
+
+    def fused():
+        st = lib.lora_nf4_fwd_multi(T, K, 3, cv(d_out), r, w.alpha, x.data_ptr(), cv(keep["c"]), cv(keep["a"]),
+                                    cv(keep["A"]), cv(keep["B"]), cv(keep["y"]), cv(keep["u"]), sp)
+        st = st or lib.lora_nf4_bwd_multi(T, K, 3, cv(d_out), r, w.alpha, x.data_ptr(), cv(keep["dy"]),
+                                          cv(keep["c"]), cv(keep["a"]), cv(keep["A"]), cv(keep["B"]),
+                                          cv(keep["u"]), dx.data_ptr(), cv(keep["dA"]), cv(keep["dB"]),
+                                          wsm.data_ptr(), wsm.numel(), sp)
+        if st != 0:
+            raise q.LoraNF4Error("lora_nf4_fwd_multi / lora_nf4_bwd_multi", st)
+
+    def separate():
+        for g in range(3):
+            st = lib.lora_nf4_fwd(T, K, Ns[g], r, w.alpha, x.data_ptr(), codes[g].data_ptr(), absmax[g].data_ptr(),
+                                  A[g].data_ptr(), B[g].data_ptr(), ys[g].data_ptr(), us[g].data_ptr(), sp)
+            st = st or lib.lora_nf4_bwd(T, K, Ns[g], r, w.alpha, x.data_ptr(), dy[g].data_ptr(),
+                                        codes[g].data_ptr(), absmax[g].data_ptr(), A[g].data_ptr(),
+                                        B[g].data_ptr(), us[g].data_ptr(), dxs[g].data_ptr(), dAs[g].data_ptr(),
+                                        dBs[g].data_ptr(), wss[g].data_ptr(), wss[g].numel(), sp)
+            if st != 0:
+                raise q.LoraNF4Error("lora_nf4_fwd / lora_nf4_bwd", st)
+
+    out = {"workload": "llama3-8b-attn-r64 q_proj + k_proj + v_proj (one x)", "tokens": T, "r": r}
+    stream = torch.cuda.current_stream()
+    flops = sum(synth.flops(T, K, N, r) for N in Ns)
+    for name, fn in (("fused", fused), ("separate", separate)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[f"{name}_ms"] = round(ms, 4)
+        out[f"{name}_tflops"] = round(flops / (ms * 1e-3) / 1e12, 2)
+    out["note"] = "separate leaves three dX arrays unsummed; fused returns their sum"
+    del x, codes, absmax, A, B, dy, ys, us, dx, dxs, dAs, dBs, wsm, wss
+    return out
+
+
 def to_dev_bf16(bits):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
@@ -529,6 +607,8 @@ def main():
         out["small_tokens"] = small_token_run(lib, q, torch, projs[big], w, args.small_tokens, sp)
     out["merge"] = merge_run(lib, q, torch, projs[big], w, sp)
     out["train_step"] = train_step_run(lib, q, torch, projs[big], w, sp)
+    if not args.no_multi:
+        out["multi_projection"] = multi_projection_run(lib, q, torch, sp)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
