@@ -16,12 +16,13 @@
 //      share a CU);
 //   2. v_mfma_f32_16x16x32_bf16 forms (A B)^T with A as the row operand (its rows
 //      are contiguous in the reduction j). The MFMA row m of block b reads A row
-//      16 (m >> 2) + 4 b + (m & 3) of the wave's 64 columns, so that across the
-//      four blocks a lane's accumulators hold 16 consecutive columns k of one row
-//      n;
-//   3. each lane dequantizes exactly those 16 elements (8 bytes of codes, one
-//      absmax), adds s times its accumulators and stores 32 (bf16) or 64
-//      (float32) contiguous bytes: no second pass through LDS.
+//      32 (b >> 1) + 8 (m >> 2) + 4 (b & 1) + (m & 3) of the wave's 64 columns, so
+//      that a lane (m = l16, g) holds columns 8 g .. 8 g + 7 (blocks 0, 1) and
+//      32 + 8 g .. 32 + 8 g + 7 (blocks 2, 3) of one row n;
+//   3. each lane dequantizes exactly those 16 elements (2 x 4 bytes of codes, one
+//      absmax), adds s times its accumulators and stores them: the four lanes of a
+//      row write 64 contiguous bytes per bf16 store instruction (128 per float32
+//      pair); no second pass through LDS.
 #include "device_common.h"
 #include "launch.h"
 
@@ -51,7 +52,8 @@ __global__ __launch_bounds__(kThreads) void lora_merge_kernel(int K, int N, int 
   if (tid < 16) lut[tid] = nf4_level(tid);
 
   // step 3's codes and absmax, loaded first so their latency overlaps steps 1-2:
-  // n-block nb, lane (l16, g): row n0 + 16 nb + l16, columns kw + 16 g .. +15
+  // n-block nb, lane (l16, g): row n0 + 16 nb + l16, columns kw + 8 g .. +7 and
+  // kw + 32 + 8 g .. +7
   const int K2 = K / 2, KB = K / 64;
   uint2 cw[4];
   float av[4];
@@ -59,49 +61,81 @@ __global__ __launch_bounds__(kThreads) void lora_merge_kernel(int K, int N, int 
   for (int nb = 0; nb < 4; ++nb) {
     const int n = n0 + 16 * nb + l16;
     const bool ok = n < N && kw < K;
-    cw[nb] = ok ? *reinterpret_cast<const uint2*>(codes + static_cast<size_t>(n) * K2 + kw / 2 + 8 * g)
-                : uint2{0u, 0u};
+    const uint32_t* crow = reinterpret_cast<const uint32_t*>(codes + static_cast<size_t>(n) * K2 + kw / 2);
+    cw[nb] = ok ? uint2{crow[g], crow[4 + g]} : uint2{0u, 0u};
     av[nb] = ok ? absmax[static_cast<size_t>(n) * KB + kw / 64] : 0.f;
   }
 
-  // ---- 1. stage A and B (batches of 8 independent loads: a plain loop waits on
-  // each). A rows k0 .. k0 + 255 are one contiguous run of 256 r elements.
+  // ---- 1. stage A and B. A rows k0 .. k0 + 255 are one contiguous run of 256 r
+  // elements; B columns n0 .. n0 + 63 are 128-byte runs of its rows. With r and
+  // d_out multiples of 8 both are read as 16-byte chunks (few loads in flight per
+  // thread, all independent); otherwise element by element in batches of 8.
   const int na = kMK * r;
-  for (int e0 = tid; e0 < na; e0 += 8 * kThreads) {
-    uint16_t v[8];
+  if (r % 8 == 0 && N % 8 == 0) {
+    for (int c0 = tid; c0 < na / 8; c0 += 4 * kThreads) {
+      uint4 v[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = e0 + u * kThreads;
-      v[u] = (e < na && k0 + e / r < K) ? A[static_cast<size_t>(k0) * r + e] : uint16_t(0);
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + u * kThreads, e = 8 * c;
+        v[u] = (c < na / 8 && k0 + e / r < K) ? *reinterpret_cast<const uint4*>(A + static_cast<size_t>(k0) * r + e)
+                                              : uint4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + u * kThreads, e = 8 * c;
+        if (c < na / 8) *reinterpret_cast<uint4*>(at + (e / r) * RS + e % r) = v[u];
+      }
     }
+    for (int c = tid; c < r * (kMN / 8); c += kThreads) {
+      const int j = c / (kMN / 8), nn = 8 * (c - j * (kMN / 8));
+      const uint4 v = n0 + nn < N ? *reinterpret_cast<const uint4*>(B + static_cast<size_t>(j) * N + n0 + nn)
+                                  : uint4{0u, 0u, 0u, 0u};
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = e0 + u * kThreads;
-      if (e < na) at[(e / r) * RS + e % r] = v[u];
+      for (int t = 0; t < 8; ++t) bt[(nn + t) * RS + j] = static_cast<uint16_t>(w[t >> 1] >> (16 * (t & 1)));
+    }
+    for (int e = tid; e < kMN * (RP - r); e += kThreads) {
+      const int nn = e / (RP - r), jj = r + e - nn * (RP - r);
+      bt[nn * RS + jj] = 0;
+    }
+  } else {
+    for (int e0 = tid; e0 < na; e0 += 8 * kThreads) {
+      uint16_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * kThreads;
+        v[u] = (e < na && k0 + e / r < K) ? A[static_cast<size_t>(k0) * r + e] : uint16_t(0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * kThreads;
+        if (e < na) at[(e / r) * RS + e % r] = v[u];
+      }
+    }
+    for (int e0 = tid; e0 < kMN * RP; e0 += 8 * kThreads) {
+      uint16_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * kThreads, j = e / kMN, nn = e % kMN;
+        v[u] = (e < kMN * RP && j < r && n0 + nn < N) ? B[static_cast<size_t>(j) * N + n0 + nn] : uint16_t(0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * kThreads;
+        if (e < kMN * RP) bt[(e % kMN) * RS + e / kMN] = v[u];
+      }
     }
   }
   for (int e = tid; e < kMK * (RP - r); e += kThreads) {
     const int kk = e / (RP - r), j = r + e - kk * (RP - r);
     at[kk * RS + j] = 0;
   }
-  for (int e0 = tid; e0 < kMN * RP; e0 += 8 * kThreads) {
-    uint16_t v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = e0 + u * kThreads, j = e / kMN, nn = e % kMN;
-      v[u] = (e < kMN * RP && j < r && n0 + nn < N) ? B[static_cast<size_t>(j) * N + n0 + nn] : uint16_t(0);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = e0 + u * kThreads;
-      if (e < kMN * RP) bt[(e % kMN) * RS + e / kMN] = v[u];
-    }
-  }
   __syncthreads();
   if (kw >= K) return;
 
   // ---- 2 + 3. per n-block: (A B)^T for 16 rows x 64 columns, then the elements
-  const int arow = 64 * wave + 16 * (l16 >> 2) + (l16 & 3);  // + 4 b: A row of MFMA row l16, block b
+  // A row of MFMA row l16 in block b: 64 wave + 32 (b >> 1) + 8 (l16 >> 2) + 4 (b & 1) + (l16 & 3)
+  const int arow = 64 * wave + 8 * (l16 >> 2) + (l16 & 3);
   const unsigned char* lutb = reinterpret_cast<const unsigned char*>(lut);
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
@@ -112,13 +146,14 @@ __global__ __launch_bounds__(kThreads) void lora_merge_kernel(int K, int N, int 
       acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int jq = 0; jq < RP / 32; ++jq) {
-        const uint4 a = *reinterpret_cast<const uint4*>(at + (arow + 4 * b) * RS + 32 * jq + 8 * g);
+        const uint4 a = *reinterpret_cast<const uint4*>(at + (arow + 32 * (b >> 1) + 4 * (b & 1)) * RS + 32 * jq + 8 * g);
         const uint4 bb = *reinterpret_cast<const uint4*>(bt + (16 * nb + l16) * RS + 32 * jq + 8 * g);
         acc[b] = mfma16(a, bb, acc[b]);
       }
     }
     if (n >= N) continue;
-    // lane (l16, g) now holds column 16 g + 4 b + e of row n in acc[b][e]
+    // lane (l16, g) now holds column 32 (b >> 1) + 8 g + 4 (b & 1) + e of row n in acc[b][e];
+    // v[i] is column 8 g + i (i < 8) or 32 + 8 g + i - 8, i.e. acc[i >> 2][i & 3]
     const float sc = av[nb];
     const uint32_t w2[2] = {cw[nb].x, cw[nb].y};
     float v[16];
@@ -135,17 +170,19 @@ __global__ __launch_bounds__(kThreads) void lora_merge_kernel(int K, int N, int 
                 s * acc[i1 >> 2][i1 & 3];
       }
     }
-    const size_t o = static_cast<size_t>(n) * K + kw + 16 * g;
+    const size_t o = static_cast<size_t>(n) * K + kw + 8 * g;
     if constexpr (OUT_BF16) {
-      uint4* op = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o);
-      op[0] = uint4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                    pack_bf16x2(v[6], v[7])};
-      op[1] = uint4{pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]), pack_bf16x2(v[12], v[13]),
-                    pack_bf16x2(v[14], v[15])};
+      uint16_t* op = static_cast<uint16_t*>(out) + o;
+      *reinterpret_cast<uint4*>(op) = uint4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+      *reinterpret_cast<uint4*>(op + 32) = uint4{pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]),
+                                                pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15])};
     } else {
-      float4* op = reinterpret_cast<float4*>(static_cast<float*>(out) + o);
+      float* op = static_cast<float*>(out) + o;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) op[q4] = float4{v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]};
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<float4*>(op + (q4 >> 1) * 32 + (q4 & 1) * 4) =
+            float4{v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]};
     }
   }
 }

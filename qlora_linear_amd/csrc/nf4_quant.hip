@@ -52,25 +52,44 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const In* __restrict_
 
 // One thread per dword of codes (8 elements of one block). Output: the product
 // level * absmax, one float32 rounding; bf16 output rounds that float32 again.
+// Dequantization: code word (8 elements, one 64-element block per 8 words) w
+// of a workgroup's 4 x 256 words is handled by thread w % 256, so each load and
+// store instruction covers consecutive words across the wave and every thread
+// has four independent loads in flight. Levels come from a 16-entry LDS table.
+constexpr int kDqWords = 4;
+template <bool BF16>
 __global__ __launch_bounds__(256) void nf4_dequantize_kernel(const uint32_t* __restrict__ codes,
                                                              const float* __restrict__ absmax,
-                                                             int64_t ndw, int out_bf16,
-                                                             void* __restrict__ out) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= ndw) return;
-  const uint32_t c = codes[i];
-  const float a = absmax[i >> 3];
-  float v[8];
+                                                             int64_t ndw, void* __restrict__ out) {
+  __shared__ float lut[16];
+  if (threadIdx.x < 16) lut[threadIdx.x] = nf4_level(threadIdx.x);
+  __syncthreads();
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * 256 * kDqWords; base < ndw;
+       base += static_cast<int64_t>(gridDim.x) * 256 * kDqWords) {
+    uint32_t c[kDqWords];
+    float a[kDqWords];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = nf4_level((c >> (4 * j)) & 15u) * a;
-  if (out_bf16) {
-    uint4 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-               pack_bf16x2(v[6], v[7])};
-    reinterpret_cast<uint4*>(out)[i] = o;
-  } else {
-    float4* o = reinterpret_cast<float4*>(out) + 2 * i;
-    o[0] = make_float4(v[0], v[1], v[2], v[3]);
-    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    for (int q = 0; q < kDqWords; ++q) {
+      const int64_t i = base + q * 256 + threadIdx.x;
+      c[q] = i < ndw ? codes[i] : 0u;
+      a[q] = i < ndw ? absmax[i >> 3] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < kDqWords; ++q) {
+      const int64_t i = base + q * 256 + threadIdx.x;
+      if (i >= ndw) continue;
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = lut[(c[q] >> (4 * j)) & 15u] * a[q];
+      if constexpr (BF16) {
+        reinterpret_cast<uint4*>(out)[i] = uint4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                 pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+      } else {
+        float4* o = reinterpret_cast<float4*>(out) + 2 * i;
+        o[0] = make_float4(v[0], v[1], v[2], v[3]);
+        o[1] = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
   }
 }
 
@@ -92,9 +111,15 @@ hipError_t launch_nf4_quantize(const void* w, bool w_is_bf16, int64_t rows, int6
 hipError_t launch_nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows,
                                  int64_t cols, bool out_bf16, void* out, hipStream_t stream) {
   const int64_t ndw = rows * cols / 8;
-  const dim3 grid(static_cast<unsigned>((ndw + 255) / 256));
-  nf4_dequantize_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<const uint32_t*>(codes), absmax,
-                                                  ndw, out_bf16 ? 1 : 0, out);
+  int64_t blocks = (ndw + 256 * kDqWords - 1) / (256 * kDqWords);
+  if (blocks > 65536) blocks = 65536;  // the kernel strides over the rest
+  const dim3 grid(static_cast<unsigned>(blocks));
+  if (out_bf16)
+    nf4_dequantize_kernel<true><<<grid, 256, 0, stream>>>(reinterpret_cast<const uint32_t*>(codes), absmax,
+                                                          ndw, out);
+  else
+    nf4_dequantize_kernel<false><<<grid, 256, 0, stream>>>(reinterpret_cast<const uint32_t*>(codes), absmax,
+                                                           ndw, out);
   return hipGetLastError();
 }
 
