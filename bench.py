@@ -16,7 +16,8 @@ kernel (one launch per lora_nf4_fwd call, timed with HIP events on the stream it
 runs on); `cpu_baseline` times the CPU fp64 oracle on a bounded token sample of
 the same projection; `small_tokens` times forward and backward of the largest
 projection at a few tokens (the weight-streaming kernels), where the bound is
-reading the packed weight from HBM; `merge` times lora_nf4_merge of that
+reading the packed weight from HBM; `medium_tokens` does the same at a few hundred
+tokens (tiled kernels on a grid of 128 x 128 tiles); `merge` times lora_nf4_merge of that
 projection (the 16-bit export, also HBM-bound); `train_step` times the AdamW step of A and B and the
 absmax double quantization; `multi_projection` times Llama-3-8B q/k/v (r = 64, one x) as one
 lora_nf4_fwd_multi + lora_nf4_bwd_multi against separate calls. With --fuse, projections that read the same
@@ -64,6 +65,8 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--small-tokens", type=int, default=16,
                     help="token count of the weight-bound measurement (0: skip)")
+    ap.add_argument("--medium-tokens", type=int, default=512,
+                    help="token count of the medium-size measurement (0: skip)")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run under rocprofv3 --pmc: one plain copy of COPY_BYTES (calibration), "
                          "then --steps fwd+bwd steps; prints nothing else")
@@ -188,10 +191,11 @@ def cpu_baseline(w: synth.Workload, target_s: float):
                       f"fp64 NumPy fwd+bwd incl. dequantization"}
 
 
-def small_token_run(lib, q, torch, d, w, tokens, sp, reps=50):
-    """Forward and backward of one projection at a few tokens (first rows of the
-    resident x and dY), back to back through the C ABI with preallocated buffers;
-    HIP events on the stream bracket `reps` calls of each."""
+def time_fwd_bwd(lib, q, torch, d, w, tokens, sp, reps):
+    """Forward and backward of one projection on the first `tokens` rows of the
+    resident x and dY, back to back through the C ABI with preallocated buffers;
+    HIP events on the stream bracket `reps` calls of each. Returns (T, K, N, r,
+    forward us, backward us)."""
     p = d["p"]
     T, K, N, r = min(tokens, w.tokens), p.d_in, p.d_out, w.r
     x, dy = d["x"][:T], d["dY"][:T]
@@ -229,13 +233,33 @@ def small_token_run(lib, q, torch, d, w, tokens, sp, reps=50):
         e1.record(stream)
         torch.cuda.synchronize()
         res[name] = e0.elapsed_time(e1) * 1000.0 / reps
+    return T, K, N, r, res["fwd"], res["bwd"]
+
+
+def small_token_run(lib, q, torch, d, w, tokens, sp, reps=50):
+    """A few tokens: the weight-streaming kernels, bound by reading the packed weight."""
+    T, K, N, r, f_us, b_us = time_fwd_bwd(lib, q, torch, d, w, tokens, sp, reps)
+    res = {"fwd": f_us, "bwd": b_us}
     wbytes = N * K // 2 + N * (K // 64) * 4  # packed codes + fp32 absmax, read once per call
-    return {"tokens": T, "projection": f"{p.name} {K}->{N}", "r": r,
+    return {"tokens": T, "projection": f"{d['p'].name} {K}->{N}", "r": r,
             "fwd_us": round(res["fwd"], 2), "bwd_us": round(res["bwd"], 2),
             "weight_bytes": wbytes, "bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "fwd_weight_GBps": round(wbytes / res["fwd"] / 1e3, 1),
             "fwd_frac": round(wbytes / res["fwd"] / 1e3 / PEAK_HBM_GBS, 4),
             "bwd_weight_GBps": round(wbytes / res["bwd"] / 1e3, 1)}
+
+
+def medium_token_run(lib, q, torch, d, w, tokens, sp, reps=50):
+    """Hundreds of tokens: the tiled kernels on a grid too small for 256 x 256 tiles
+    to fill the GPU (the launcher then takes 128 x 128 tiles). Algorithmic TFLOP/s
+    of forward and backward (same per-token FLOPs as the step)."""
+    T, K, N, r, f_us, b_us = time_fwd_bwd(lib, q, torch, d, w, tokens, sp, reps)
+    f_fl = 2 * T * K * N + 2 * T * r * (K + N)
+    b_fl = 2 * T * K * N + 4 * T * r * (K + N)
+    return {"tokens": T, "projection": f"{d['p'].name} {K}->{N}", "r": r,
+            "fwd_us": round(f_us, 2), "bwd_us": round(b_us, 2), "bound": "mfma",
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "fwd_TFLOPs": round(f_fl / f_us / 1e6, 1), "bwd_TFLOPs": round(b_fl / b_us / 1e6, 1)}
 
 
 def merge_run(lib, q, torch, d, w, sp, reps=20):
@@ -605,6 +629,8 @@ def main():
     }
     if args.small_tokens > 0:
         out["small_tokens"] = small_token_run(lib, q, torch, projs[big], w, args.small_tokens, sp)
+    if args.medium_tokens > 0:
+        out["medium_tokens"] = medium_token_run(lib, q, torch, projs[big], w, args.medium_tokens, sp)
     out["merge"] = merge_run(lib, q, torch, projs[big], w, sp)
     out["train_step"] = train_step_run(lib, q, torch, projs[big], w, sp)
     if not args.no_multi:

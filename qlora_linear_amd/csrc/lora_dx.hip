@@ -6,8 +6,10 @@
 //
 // Work decomposition mirrors the forward kernel: 256 x 256 dX tile (tokens x
 // d_in) per 512-thread workgroup, 8 waves of 128 x 64, v_mfma_f32_32x32x16_bf16,
-// reduction over d_out in steps of 64. The base weight is used transposed here
-// (the reduction runs along its rows), so its 64 x 256 tile is dequantized into
+// reduction over d_out in steps of 64; or, when those tiles would leave CUs idle,
+// 128 x 128 tiles per 256-thread workgroup (4 waves of 64 x 64), half the LDS.
+// The base weight is used transposed here (the reduction runs along its rows), so
+// its 64 x BT tile is dequantized into
 // LDS in its natural row-major orientation with 16-byte stores and read back with
 // ds_read_b64_tr_b16, which hands each lane a column of four consecutive rows:
 // exactly the MFMA B fragment. The same dY tile accumulates G = s dY B^T for the
@@ -30,22 +32,37 @@
 namespace lnf4 {
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kTileElems = 256 * 64;  // dY tile [256][64]
-constexpr int kDStride = 256 + 32;    // deq weight tile rows: 256 bf16 + 64 B pad
-// Row n of the dequantized weight tile starts at n kDStride + dshift(n): rows
-// four apart (one transposing read covers four consecutive rows) are shifted by
-// 16 bytes per group of four, which spreads the 16-byte dequantization stores
-// of a 16-lane group over all 64 banks.
+constexpr int BK = 64;
+// Row n of the dequantized weight tile starts at n kDStride + dshift(n). The row
+// stride (BT + 32 bf16) is 64 bytes past a multiple of 256, so the four rows of
+// one transposing read, and the two column halves a 32-lane group reads, fall on
+// distinct banks; rows four apart are shifted by 16 bytes per group of four,
+// which spreads the 16-byte dequantization stores of a 16-lane group over all 64
+// banks.
 __device__ __forceinline__ int dshift(int n) { return 8 * ((n >> 2) & 3); }
-constexpr int kDElems = 64 * kDStride;
-constexpr int kBStride = 72;          // B slice rows: 64 bf16 + 16 B pad
+constexpr int kBStride = 72;  // B slice rows: 64 bf16 + 16 B pad
 
-template <int RU, int RE, bool MULTI>
-__global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, float s, const DxTable tab,
-                                                           uint16_t* __restrict__ dx,
-                                                           uint16_t* __restrict__ g_out) {
+// Square dX tile of edge BT (256 or 128): 2 x (BT / 64) waves, each owning
+// BT / 2 token rows x 64 d_in columns.
+template <int BT>
+struct DxTile {
+  static constexpr int kThreads = 2 * BT;
+  static constexpr int kWN = BT / 64;         // waves along d_in
+  static constexpr int kFM = BT / 64;         // 32-row fragments per wave along tokens
+  static constexpr int kTileElems = BT * 64;  // dY tile [BT][64]
+  static constexpr int kDStride = BT + 32;    // deq weight tile rows
+  static constexpr int kDElems = 64 * kDStride;
+  static constexpr int kRuns = BT / 32;       // 32-column runs of one weight row
+  static constexpr int kMinBlocks = BT == 128 ? 2 : 1;
+};
+
+template <int BT, int RU, int RE, bool MULTI>
+__global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void lora_dx_kernel(
+    int T, int K, int r, float s, const DxTable tab, uint16_t* __restrict__ dx,
+    uint16_t* __restrict__ g_out) {
+  using Tl = DxTile<BT>;
+  constexpr int kThreads = Tl::kThreads, BM = BT, BN = BT, kFM = Tl::kFM, kHalf = BT / 2;
+  constexpr int kTileElems = Tl::kTileElems, kDStride = Tl::kDStride, kDElems = Tl::kDElems;
   __shared__ __align__(1024) float lut[16];  // first in LDS: level addresses need no base
   __shared__ __align__(16) uint16_t ys0[kTileElems];
   __shared__ __align__(16) uint16_t ys1[kTileElems];
@@ -55,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
   __shared__ __align__(16) uint16_t bs1[RU * kBStride];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 128 x 64 each
+  const int wm = wave / Tl::kWN, wn = wave % Tl::kWN;  // 2 x kWN waves, BT / 2 x 64 each
   const int l32 = lane & 31, lh = lane >> 5;
   const int mt = (T + BM - 1) / BM, kt_tiles = (K + BN - 1) / BN;
   int tm, tk;
@@ -78,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
   const int rows_t = min(T - m0, BM);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
-  // dY: wave w fills rows 32 w .. 32 w + 31 of the [256][64] tile, swizzled
+  // dY: wave w fills rows 32 w .. 32 w + 31 of the [BT][64] tile, swizzled
   const int N0 = tab.N[0];
   uint32_t yvoff[4];
   auto set_yvoff = [&](int Ng) {
@@ -106,21 +123,25 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
     for (int q = 0; q < 4; ++q)
       buf_load16_lds(rs_y, stage + (wave_u * 4 + q) * 512, yvoff[q], (st - y_beg) * BK * 2);
   };
-  // weight codes: row nl = tid >> 3 of the 64-row step, 32 columns (one half of
-  // an NF4 block) at run tid & 7 of the 256-column tile
-  // (thread bits: [1:0] low run, [3:2] low row group, [4] high run, [6:5] high row
-  // group, [8:7] row within the group of four; each 16 lanes then store to
-  // distinct banks)
-  const int run = (tid & 3) | (((tid >> 4) & 1) << 2);
-  const int nl = 4 * (((tid >> 2) & 3) | (((tid >> 5) & 3) << 2)) + ((tid >> 7) & 3);
+  // weight codes: one of the 64 rows of the step, 32 columns (one half of an NF4
+  // block) at one of the BT / 32 runs of the tile. Thread bits, 256 x 256 tiles:
+  // [1:0] low run, [3:2] low row group, [4] high run, [6:5] high row group, [8:7]
+  // row within the group of four; 128 x 128 tiles: [1:0] run, [3:2] low row
+  // group, [5:4] high row group, [7:6] row within the group. Each 16 lanes then
+  // store to distinct banks.
+  const int run = BT == 256 ? (tid & 3) | (((tid >> 4) & 1) << 2) : (tid & 3);
+  const int nl = BT == 256 ? 4 * (((tid >> 2) & 3) | (((tid >> 5) & 3) << 2)) + ((tid >> 7) & 3)
+                           : 4 * (((tid >> 2) & 3) | (((tid >> 4) & 3) << 2)) + ((tid >> 6) & 3);
   const uint32_t cvoff = static_cast<uint32_t>(nl) * K2 + run * 16;
   const uint32_t svoff = (static_cast<uint32_t>(nl) * KB + (run >> 1)) * 4;
-  // B slice: row j = tid >> 3 (< RU), 8 columns at chunk tid & 7; columns past
-  // d_out are zeroed here (the buffer range would only stop them at the end of B)
+  // B slice: row j = tid >> 3 (+ kThreads / 8 per further load, < RU), 8 columns
+  // at chunk tid & 7; columns past d_out are zeroed here (the buffer range would
+  // only stop them at the end of B)
+  constexpr int kBPer = (RU * 8 + kThreads - 1) / kThreads;
   const int bj = tid >> 3, bch = tid & 7;
-  uint4 creg[2], breg[2];
+  uint4 creg[2], breg[2][kBPer];
   float sreg[2];
-  // Three loads per thread and step (rows j >= r fall outside rs_b and read
+  // 2 + kBPer loads per thread and step (rows j >= r fall outside rs_b and read
   // zeros), so every wave can wait on the same vmcnt.
   auto rs_c = make_rsrc(tab.codes[0] + k0 / 2, static_cast<uint32_t>(static_cast<size_t>(N0) * K2 - k0 / 2));
   auto rs_s = make_rsrc(tab.absmax[0] + k0 / 64, static_cast<uint32_t>((static_cast<size_t>(N0) * KB - k0 / 64) * 4));
@@ -144,15 +165,18 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
     const int ls = st - w_beg;
     creg[slot] = buf_load16(rs_c, cvoff, ls * 64 * K2);
     sreg[slot] = __uint_as_float(buf_load4(rs_s, svoff, ls * 64 * KB * 4));
-    const uint4 v = buf_load16(rs_b, bvoff, ls * BK * 2);
-    breg[slot] = (ls * BK + bch * 8 < w_N) ? v : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) {
+      const uint4 v = buf_load16(rs_b, bvoff + i * (kThreads / 8) * w_N * 2, ls * BK * 2);
+      breg[slot][i] = (ls * BK + bch * 8 < w_N) ? v : uint4{0u, 0u, 0u, 0u};
+    }
   };
 
   const int fkey = (l32 >> 1) & 7;
   int choff[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) choff[ks] = ((2 * ks + lh) ^ fkey) << 3;
-  const int a_off = (wm * 128 + l32) * 64;  // + i * 2048
+  const int a_off = (wm * kHalf + l32) * 64;  // + i * 2048
   const int ga_off = a_off + wn * 2048;     // this wave's 32 rows of G
   // transposed weight fragment: 16-lane group g, lane m within it
   const int g16 = lane >> 4, m16 = lane & 15;
@@ -161,10 +185,10 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
   const int d_off = ((g16 >> 1) * 8 + (m16 >> 2)) * kDStride + dshift((g16 >> 1) * 8) + wn * 64 +
                     (g16 & 1) * 16 + 4 * (m16 & 3);
   const int gb_off = l32 * kBStride + lh * 8;  // + u * 32 * kBStride + ks * 16
-  // r <= 16: 16 x 16 x 32 fragments of G rows wm * 128 + wn * 32 + 16 rb + (lane & 15)
+  // r <= 16: 16 x 16 x 32 fragments of G rows wm * BT / 2 + wn * 32 + 16 rb + (lane & 15)
   constexpr bool kG16 = RU == 16;
   const int l16 = lane & 15, lq = lane >> 4;
-  const int ga16_off = (wm * 128 + wn * 32 + l16) * 64;  // + rb * 1024
+  const int ga16_off = (wm * kHalf + wn * 32 + l16) * 64;  // + rb * 1024
   int choff16[2];
 #pragma unroll
   for (int kq = 0; kq < 2; ++kq) choff16[kq] = ((4 * kq + lq) ^ (l16 >> 1)) << 3;
@@ -193,15 +217,19 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
     *reinterpret_cast<uint4*>(dst) = o;
   };
   const int dw_off = nl * kDStride + dshift(nl) + run * 32;  // + q * 8
-  auto store_b = [&](uint16_t* bs, const uint4& v) {
-    if (bj < RU) *reinterpret_cast<uint4*>(bs + bj * kBStride + bch * 8) = v;
+  auto store_b = [&](uint16_t* bs, const uint4* v) {
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) {
+      const int j = bj + i * (kThreads / 8);
+      if (j < RU) *reinterpret_cast<uint4*>(bs + j * kBStride + bch * 8) = v[i];
+    }
   };
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[kFM][2];
   f32x16_t gacc[RU / 32 > 0 ? RU / 32 : 1];
   f32x4_t gacc16[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kFM; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -230,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
   __syncthreads();
 
   struct Frag {
-    uint4 a[4], b[2], ga, gb[RU / 32 > 0 ? RU / 32 : 1], ga16[2], gb16;
+    uint4 a[kFM], b[2], ga, gb[RU / 32 > 0 ? RU / 32 : 1], ga16[2], gb16;
   };
   auto kstep = [&](int st, auto cur_c) {
     constexpr int cur = decltype(cur_c)::value;
@@ -247,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
     const float ar = sreg[nslot];
     auto read_frag = [&](Frag& f, int ks) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const uint4*>(yc + a_off + i * 2048 + choff[ks]);
+      for (int i = 0; i < kFM; ++i) f.a[i] = *reinterpret_cast<const uint4*>(yc + a_off + i * 2048 + choff[ks]);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const uint16_t* p = dc + d_off + ks * 16 * kDStride + j * 32;
@@ -279,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
         lookup(cw[ks + 1], lv[(ks + 1) & 1]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kFM; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
       if constexpr (kG16) {
@@ -296,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
     }
     // dY of the next stage has landed (the step st + 2 register loads issued after
     // it may still be in flight)
-    wait_vmem_upto<3>();
+    wait_vmem_upto<2 + kBPer>();
     __syncthreads();
   };
   // Several projections: at the end of projection g's steps, store bf16(s G_g)
@@ -310,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
     for (int u = 0; u < RU / 32; ++u)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = wm * 128 + wn * 32 + mfma32_row(e, lane), col = u * 32 + l32;
+        const int row = wm * kHalf + wn * 32 + mfma32_row(e, lane), col = u * 32 + l32;
         if (col < r && m0 + row < T)
           g_out[static_cast<size_t>(m0 + row) * R + col0 + col] = to_bf16(s * gacc[u][e]);
         gacc[u][e] = 0.f;
@@ -320,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int row = wm * 128 + wn * 32 + rb * 16 + 4 * lq + e;
+          const int row = wm * kHalf + wn * 32 + rb * 16 + 4 * lq + e;
           if (l16 < r && m0 + row < T)
             g_out[static_cast<size_t>(m0 + row) * R + col0 + l16] = to_bf16(s * gacc16[rb][e]);
           gacc16[rb][e] = 0.f;
@@ -340,33 +368,33 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
 
   // ---- epilogue: acc += bf16(G) A^T ----------------------------------------------
   constexpr int ES = RE + 8;
-  constexpr bool kPad = 256 * ES <= kTileElems;
+  constexpr bool kPad = BT * ES <= kTileElems;
   auto ep = [](int row, int col) {
     if constexpr (kPad) return row * ES + col;
     else return swz64(row, col >> 3) + (col & 7);
   };
-  uint16_t* gs = ys0;  // [256][RE] bf16(G), G = s dY B^T (projections side by side)
-  uint16_t* at = ys1;  // [256][RE] rows k of A (A is [d_in, r] row-major), projections side by side
+  uint16_t* gs = ys0;  // [BT][RE] bf16(G), G = s dY B^T (projections side by side)
+  uint16_t* at = ys1;  // [BT][RE] rows k of A (A is [d_in, r] row-major), projections side by side
   // one MFMA pass over RE rank columns: acc += gs at^T
   auto lora_pass = [&]() {
 #pragma unroll
     for (int ks = 0; ks < RE / 16; ++ks) {
-      uint4 a[4], b[2];
+      uint4 a[kFM], b[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const uint4*>(gs + ep(wm * 128 + i * 32 + l32, ks * 16 + lh * 8));
+      for (int i = 0; i < kFM; ++i)
+        a[i] = *reinterpret_cast<const uint4*>(gs + ep(wm * kHalf + i * 32 + l32, ks * 16 + lh * 8));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         b[j] = *reinterpret_cast<const uint4*>(at + ep(wn * 64 + j * 32 + l32, ks * 16 + lh * 8));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kFM; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
     }
   };
   // A^T columns c0 .. c0 + RE - 1 of the side-by-side projections
   auto stage_at = [&](int c0) {
-    for (int e = tid; e < 256 * (RE / 8); e += kThreads) {
+    for (int e = tid; e < BT * (RE / 8); e += kThreads) {
       const int c = e / (RE / 8), jc = c0 + 8 * (e - c * (RE / 8));
       const int g = jc / r, j0 = jc - g * r;  // r % 8 == 0: a chunk never straddles projections
       uint4 v = {0u, 0u, 0u, 0u};
@@ -381,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
     // n r may exceed RE: the rank columns are added RE at a time
     for (int c0 = 0; c0 < R; c0 += RE) {
       __syncthreads();  // previous pass (or the K-loop) done with gs and at
-      for (int e = tid; e < 256 * (RE / 8); e += kThreads) {
+      for (int e = tid; e < BT * (RE / 8); e += kThreads) {
         const int row = e / (RE / 8), jc = c0 + 8 * (e - row * (RE / 8));
         uint4 v = {0u, 0u, 0u, 0u};
         if (jc < R && m0 + row < T)
@@ -397,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
     for (int u = 0; u < RU / 32; ++u)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = wm * 128 + wn * 32 + mfma32_row(e, lane), col = u * 32 + l32;
+        const int row = wm * kHalf + wn * 32 + mfma32_row(e, lane), col = u * 32 + l32;
         const uint16_t gv = to_bf16(s * gacc[u][e]);
         if (col < RE) gs[ep(row, col)] = gv;
         if (tk == 0 && col < r && m0 + row < T) g_out[static_cast<size_t>(m0 + row) * r + col] = gv;
@@ -407,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int row = wm * 128 + wn * 32 + rb * 16 + 4 * lq + e;
+          const int row = wm * kHalf + wn * 32 + rb * 16 + 4 * lq + e;
           const uint16_t gv = to_bf16(s * gacc16[rb][e]);
           gs[ep(row, l16)] = gv;
           if (tk == 0 && l16 < r && m0 + row < T) g_out[static_cast<size_t>(m0 + row) * r + l16] = gv;
@@ -419,24 +447,69 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(int T, int K, int r, 
     lora_pass();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kFM; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = k0 + wn * 64 + j * 32 + l32;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * 128 + i * 32 + mfma32_row(e, lane);
+        const int row = m0 + wm * kHalf + i * 32 + mfma32_row(e, lane);
         if (row < T && col < K) dx[static_cast<size_t>(row) * K + col] = to_bf16(acc[i][j][e]);
       }
     }
 }
 
-template <int RU, int RE, bool MULTI>
+template <int BT, int RU, int RE, bool MULTI>
 hipError_t launch_dx_t(int T, int K, int r, float s, const DxTable& tab, uint16_t* dx, uint16_t* g_out,
                        hipStream_t stream) {
-  const int tiles = ((T + BM - 1) / BM) * ((K + BN - 1) / BN);
-  lora_dx_kernel<RU, RE, MULTI><<<tiles, kThreads, 0, stream>>>(T, K, r, s, tab, dx, g_out);
+  const int tiles = ((T + BT - 1) / BT) * ((K + BT - 1) / BT);
+  lora_dx_kernel<BT, RU, RE, MULTI><<<tiles, DxTile<BT>::kThreads, 0, stream>>>(T, K, r, s, tab, dx, g_out);
   return hipGetLastError();
+}
+
+template <int BT>
+hipError_t launch_dx_rank(int T, int K, int r, float s, const DxTable& tab, uint16_t* dx, uint16_t* g_out,
+                          hipStream_t stream) {
+  const int R = tab.n * r;
+  if (tab.n == 1) {
+    switch ((r + 15) / 16) {
+      case 1: return launch_dx_t<BT, 16, 16, false>(T, K, r, s, tab, dx, g_out, stream);
+      case 2: return launch_dx_t<BT, 32, 32, false>(T, K, r, s, tab, dx, g_out, stream);
+      case 3: return launch_dx_t<BT, 64, 48, false>(T, K, r, s, tab, dx, g_out, stream);
+      case 4: return launch_dx_t<BT, 64, 64, false>(T, K, r, s, tab, dx, g_out, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  // several projections: RU from r, RE from n r (64 at most: wider sums take several passes)
+  const int RE = R >= 64 ? 64 : ((R + 15) / 16) * 16;
+  if (r <= 16) {
+    switch (RE) {
+      case 16: return launch_dx_t<BT, 16, 16, true>(T, K, r, s, tab, dx, g_out, stream);
+      case 32: return launch_dx_t<BT, 16, 32, true>(T, K, r, s, tab, dx, g_out, stream);
+      case 48: return launch_dx_t<BT, 16, 48, true>(T, K, r, s, tab, dx, g_out, stream);
+      default: return launch_dx_t<BT, 16, 64, true>(T, K, r, s, tab, dx, g_out, stream);
+    }
+  }
+  if (r <= 32) {
+    if (RE == 48) return launch_dx_t<BT, 32, 48, true>(T, K, r, s, tab, dx, g_out, stream);
+    return launch_dx_t<BT, 32, 64, true>(T, K, r, s, tab, dx, g_out, stream);
+  }
+  return launch_dx_t<BT, 64, 64, true>(T, K, r, s, tab, dx, g_out, stream);
+}
+
+// Tile edge from a round count: 256 x 256 tiles run one per CU; 128 x 128 tiles
+// two per CU at rank <= 16 (one above, where the B slices push the LDS past half
+// a CU). A full round of 128 tiles costs a fraction of a round of 256 tiles
+// (measured on MI355X); the outputs are the same either way.
+constexpr int kDxCost128Num = 3, kDxCost128Den = 4;  // rank <= 16
+constexpr int kDxCost128NumR = 2, kDxCost128DenR = 3;  // rank > 16
+int dx_tile_edge(int64_t T, int64_t K, int r) {
+  const int64_t rounds256 = ((T + 255) / 256 * ((K + 255) / 256) + 255) / 256;
+  const int slots128 = r <= 16 ? 512 : 256;
+  const int64_t rounds128 = ((T + 127) / 128 * ((K + 127) / 128) + slots128 - 1) / slots128;
+  const bool small = r <= 16 ? kDxCost128Num * rounds128 < kDxCost128Den * rounds256
+                             : kDxCost128NumR * rounds128 < kDxCost128DenR * rounds256;
+  return small ? 128 : 256;
 }
 
 }  // namespace
@@ -452,31 +525,8 @@ bool lora_dx_multi_supported(int n_proj, const int* N, int r) {
 
 hipError_t launch_lora_dx_table(int T, int K, int r, float s, const DxTable& tab, uint16_t* dx,
                                 uint16_t* g_out, hipStream_t stream) {
-  const int R = tab.n * r;
-  if (tab.n == 1) {
-    switch ((r + 15) / 16) {
-      case 1: return launch_dx_t<16, 16, false>(T, K, r, s, tab, dx, g_out, stream);
-      case 2: return launch_dx_t<32, 32, false>(T, K, r, s, tab, dx, g_out, stream);
-      case 3: return launch_dx_t<64, 48, false>(T, K, r, s, tab, dx, g_out, stream);
-      case 4: return launch_dx_t<64, 64, false>(T, K, r, s, tab, dx, g_out, stream);
-      default: return hipErrorInvalidValue;
-    }
-  }
-  // several projections: RU from r, RE from n r (64 at most: wider sums take several passes)
-  const int RE = R >= 64 ? 64 : ((R + 15) / 16) * 16;
-  if (r <= 16) {
-    switch (RE) {
-      case 16: return launch_dx_t<16, 16, true>(T, K, r, s, tab, dx, g_out, stream);
-      case 32: return launch_dx_t<16, 32, true>(T, K, r, s, tab, dx, g_out, stream);
-      case 48: return launch_dx_t<16, 48, true>(T, K, r, s, tab, dx, g_out, stream);
-      default: return launch_dx_t<16, 64, true>(T, K, r, s, tab, dx, g_out, stream);
-    }
-  }
-  if (r <= 32) {
-    if (RE == 48) return launch_dx_t<32, 48, true>(T, K, r, s, tab, dx, g_out, stream);
-    return launch_dx_t<32, 64, true>(T, K, r, s, tab, dx, g_out, stream);
-  }
-  return launch_dx_t<64, 64, true>(T, K, r, s, tab, dx, g_out, stream);
+  if (dx_tile_edge(T, K, r) == 256) return launch_dx_rank<256>(T, K, r, s, tab, dx, g_out, stream);
+  return launch_dx_rank<128>(T, K, r, s, tab, dx, g_out, stream);
 }
 
 hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* dy,

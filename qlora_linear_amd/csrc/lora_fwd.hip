@@ -8,9 +8,13 @@
 //
 // Work decomposition (MI355X, 256 CUs in 8 XCDs, 160 KB LDS per CU):
 //   * 256 x 256 output tile per workgroup, 512 threads = 8 waves (2 per SIMD),
-//     each wave owning a 128 x 64 sub-tile of 2 x 4 v_mfma_f32_32x32x16_bf16
+//     each wave owning a 128 x 64 sub-tile of 4 x 2 v_mfma_f32_32x32x16_bf16
 //     accumulators. A large M-tile amortizes the in-loop dequantization: every
 //     weight element is dequantized T/256 times over the whole GEMM.
+//   * When 256 x 256 tiles would leave CUs idle (a few thousand tokens or fewer
+//     over a narrow d_out), the same kernel runs 128 x 128 tiles: 256 threads in
+//     2 x 2 waves of 64 x 64 (2 x 2 accumulators), half the LDS, so two
+//     workgroups share a CU and the grid has four times as many tiles.
 //   * K-loop in steps of 64 = one NF4 block, so every weight row has exactly one
 //     absmax per step. LDS holds two stages (x tile, dequantized weight tile,
 //     A slice), XOR-swizzled for conflict-free 16-byte fragment reads; while the
@@ -34,10 +38,20 @@
 namespace lnf4 {
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kTileElems = 256 * 64;  // one bf16 [256][64] tile
-constexpr int kAStride = 72;          // A^T slice rows: 64 bf16 + 16 B pad (conflict-free b128 reads)
+constexpr int BK = 64;
+constexpr int kAStride = 72;  // A^T slice rows: 64 bf16 + 16 B pad (conflict-free b128 reads)
+
+// Square output tile of edge BT (256 or 128): 2 x (BT / 64) waves, each owning
+// BT / 2 token rows x 64 columns.
+template <int BT>
+struct FwdTile {
+  static constexpr int kThreads = 2 * BT;
+  static constexpr int kWN = BT / 64;          // waves along d_out
+  static constexpr int kFM = BT / 64;          // 32-row fragments per wave along tokens
+  static constexpr int kTileElems = BT * 64;   // one bf16 [BT][64] tile
+  // workgroups per CU the register budget is sized for (LDS allows two at 128)
+  static constexpr int kMinBlocks = BT == 128 ? 2 : 1;
+};
 
 // Projections of one launch; tile_end[g] = column tiles of projections 0..g.
 struct ProjTable {
@@ -52,16 +66,20 @@ struct ProjTable {
   uint16_t* u[kMaxProj];
 };
 
-// RU: U columns accumulated in the K-loop (16 for r <= 16, else r rounded up to
-// 32); RE: rank padded to the 16-wide reduction step of the epilogue MFMA.
+// BT: tile edge; RU: U columns accumulated in the K-loop (16 for r <= 16, else r
+// rounded up to 32); RE: rank padded to the 16-wide reduction step of the
+// epilogue MFMA.
 //
 // LDS (static, so the compiler can prove the direct-to-LDS loads into one stage
-// never alias reads of the other): level table, two stages of x [256][64],
-// dequantized weight [256][64] and A^T slice [RU][64], all bf16 and swizzled.
-template <int RU, int RE>
-__global__ __launch_bounds__(kThreads) void lora_fwd_kernel(int T, int K, int r, float s,
-                                                            const uint16_t* __restrict__ x,
-                                                            const ProjTable tab) {
+// never alias reads of the other): level table, two stages of x [BT][64],
+// dequantized weight [BT][64] and A^T slice [RU][64], all bf16 and swizzled.
+template <int BT, int RU, int RE>
+__global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) void lora_fwd_kernel(int T, int K, int r, float s,
+                                                                        const uint16_t* __restrict__ x,
+                                                                        const ProjTable tab) {
+  using Tl = FwdTile<BT>;
+  constexpr int kThreads = Tl::kThreads, BM = BT, BN = BT, kFM = Tl::kFM, kHalf = BT / 2;
+  constexpr int kTileElems = Tl::kTileElems;
   __shared__ __align__(1024) float lut[16];  // first in LDS: level addresses need no base
   __shared__ __align__(16) uint16_t xs0[kTileElems];
   __shared__ __align__(16) uint16_t xs1[kTileElems];
@@ -71,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(int T, int K, int r,
   __shared__ __align__(16) uint16_t as1[RU * kAStride];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 128 x 64 each
+  const int wm = wave / Tl::kWN, wn = wave % Tl::kWN;  // 2 x kWN waves, BT / 2 x 64 each
   const int l32 = lane & 31, lh = lane >> 5;
   const int mt = (T + BM - 1) / BM, nt_all = tab.tile_end[tab.n - 1];
   int tm, tn;
@@ -107,6 +125,7 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(int T, int K, int r,
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   // x: wave w fills rows 32 w .. 32 w + 31 with four 1 KB direct-to-LDS loads
+  // (BT / 32 waves cover the tile)
   // (8 rows each). Lane i lands on physical chunk i & 7 of its row, so it loads
   // the logical chunk that the swizzle maps there.
   uint32_t xvoff[4];
@@ -121,11 +140,11 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(int T, int K, int r,
     for (int q = 0; q < 4; ++q)
       buf_load16_lds(rs_x, stage + (wave_u * 4 + q) * 512, xvoff[q], kt * BK * 2);
   };
-  // codes: row tid>>1, 16 bytes (32 codes) at half tid&1 of the block; one absmax
+  // codes: row tid>>1 (< BT), 16 bytes (32 codes) at half tid&1 of the block; one absmax
   const int crow = tid >> 1, chalf = tid & 1;
   const uint32_t cvoff = static_cast<uint32_t>(crow) * K2 + chalf * 16;
   const uint32_t svoff = static_cast<uint32_t>(crow) * KB * 4;
-  // A slice: the 64 x r block of A is contiguous; 8-element chunks tid + 512 i
+  // A slice: the 64 x r block of A is contiguous; 8-element chunks tid + kThreads i
   // (r % 8 == 0 on this path)
   constexpr int kAPer = (64 * RU / 8 + kThreads - 1) / kThreads;
   // Register sets for step s live in slot s & 1, so the prefetch of step kt + 2
@@ -149,25 +168,25 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(int T, int K, int r,
   int choff[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) choff[ks] = ((2 * ks + lh) ^ fkey) << 3;
-  const int a_off = (wm * 128 + l32) * 64;  // + i * 2048
+  const int a_off = (wm * kHalf + l32) * 64;  // + i * 2048
   const int b_off = (wn * 64 + l32) * 64;   // + j * 2048
   const int ua_off = a_off + wn * 2048;
-  // Rank 64: row block i of the wave's 128 x rows is block (i + wn) & 3 of its
-  // slab, so block 0 is the 32 rows whose U this wave accumulates and U takes the
+  // Rank 64: row block i of the wave's BT / 2 x rows is block (i + wn) % kFM of
+  // its slab, so block 0 is the 32 rows whose U this wave accumulates and U takes the
   // main x fragment instead of a read of its own (measured: 6 % faster at r = 64,
   // slower at r <= 32, where the extra address arithmetic costs more than the
   // read). choff[ks] = choff[0] ^ (ks << 4), so each block keeps one address
   // register (its row offset has no bits below 6).
   constexpr bool kRot = RU == 64;
-  int xb[4];
+  int xb[kFM];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) xb[i] = ((wm * 128 + ((i + wn) & 3) * 32 + l32) * 64) | choff[0];
-  auto blk = [&](int i) { return kRot ? ((i + wn) & 3) : i; };  // row block of fragment i
+  for (int i = 0; i < kFM; ++i) xb[i] = ((wm * kHalf + ((i + wn) % kFM) * 32 + l32) * 64) | choff[0];
+  auto blk = [&](int i) { return kRot ? ((i + wn) % kFM) : i; };  // row block of fragment i
   const int ub_off = l32 * kAStride;        // + u * 32 * kAStride
-  // r <= 16: 16 x 16 x 32 fragments of U rows wm * 128 + wn * 32 + 16 rb + (lane & 15)
+  // r <= 16: 16 x 16 x 32 fragments of U rows wm * BT / 2 + wn * 32 + 16 rb + (lane & 15)
   constexpr bool kU16 = RU == 16;
   const int l16 = lane & 15, lq = lane >> 4;
-  const int ua16_off = (wm * 128 + wn * 32 + l16) * 64;  // + rb * 1024
+  const int ua16_off = (wm * kHalf + wn * 32 + l16) * 64;  // + rb * 1024
   int choff16[2];
 #pragma unroll
   for (int kq = 0; kq < 2; ++kq) choff16[kq] = ((4 * kq + lq) ^ (l16 >> 1)) << 3;
@@ -228,11 +247,11 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(int T, int K, int r,
     }
   };
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[kFM][2];
   f32x16_t uacc[RU / 32 > 0 ? RU / 32 : 1];
   f32x4_t uacc16[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kFM; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -266,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(int T, int K, int r,
   // ks + 1 and the level lookups of code dword ks + 1 are issued one slice ahead
   // of their use.
   struct Frag {
-    uint4 a[4], b[2], au, bu[RU / 32 > 0 ? RU / 32 : 1], au16[2], bu16;
+    uint4 a[kFM], b[2], au, bu[RU / 32 > 0 ? RU / 32 : 1], au16[2], bu16;
   };
   auto kstep = [&](int kt, auto cur_c) {
     constexpr int cur = decltype(cur_c)::value;
@@ -284,11 +303,15 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(int T, int K, int r,
     const float ar = sreg[nslot];
     // re-declared opaque every step: one register per block, the slice bits
     // flipped per read, rather than one hoisted register per (block, slice)
-    int xbs[4] = {xb[0], xb[1], xb[2], xb[3]};
-    if constexpr (kRot) asm volatile("" : "+v"(xbs[0]), "+v"(xbs[1]), "+v"(xbs[2]), "+v"(xbs[3]));
+    int xbs[kFM];
+#pragma unroll
+    for (int i = 0; i < kFM; ++i) {
+      xbs[i] = xb[i];
+      if constexpr (kRot) asm volatile("" : "+v"(xbs[i]));
+    }
     auto read_frag = [&](Frag& f, int ks) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kFM; ++i)
         f.a[i] = kRot ? *reinterpret_cast<const uint4*>(xc + (xbs[i] ^ (ks << 4)))
                       : *reinterpret_cast<const uint4*>(xc + a_off + i * 2048 + choff[ks]);
 #pragma unroll
@@ -318,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(int T, int K, int r,
         lookup(cw[ks + 1], lv[(ks + 1) & 1]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kFM; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
       if constexpr (kU16) {
@@ -345,20 +368,20 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(int T, int K, int r,
 
   // ---- epilogue: acc += bf16(s U) B ---------------------------------------------
   // Rank-wide tiles: rows of RE bf16, padded to RE + 8 (conflict-free 16-byte
-  // reads) when that fits a [256][64] buffer, else swizzled like the main tiles.
+  // reads) when that fits a [BT][64] buffer, else swizzled like the main tiles.
   constexpr int ES = RE + 8;
-  constexpr bool kPad = 256 * ES <= kTileElems;
+  constexpr bool kPad = BT * ES <= kTileElems;
   auto ep = [](int row, int col) {  // element offset of (row, col)
     if constexpr (kPad) return row * ES + col;
     else return swz64(row, col >> 3) + (col & 7);
   };
-  uint16_t* us = xs0;  // [256][RE] bf16(s U)
-  uint16_t* bt = ws0;  // [256][RE] B^T tile
+  uint16_t* us = xs0;  // [BT][RE] bf16(s U)
+  uint16_t* bt = ws0;  // [BT][RE] B^T tile
 #pragma unroll
   for (int u = 0; u < RU / 32; ++u)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int row = wm * 128 + wn * 32 + mfma32_row(e, lane), col = u * 32 + l32;
+      const int row = wm * kHalf + wn * 32 + mfma32_row(e, lane), col = u * 32 + l32;
       const float uv = uacc[u][e];
       if (col < RE) us[ep(row, col)] = to_bf16(s * uv);
       if (u_save != nullptr && tn == 0 && col < r && m0 + row < T)
@@ -369,61 +392,94 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(int T, int K, int r,
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = wm * 128 + wn * 32 + rb * 16 + 4 * lq + e;
+        const int row = wm * kHalf + wn * 32 + rb * 16 + 4 * lq + e;
         const float uv = uacc16[rb][e];
         us[ep(row, l16)] = to_bf16(s * uv);
         if (u_save != nullptr && tn == 0 && l16 < r && m0 + row < T)
           u_save[static_cast<size_t>(m0 + row) * r + l16] = to_bf16(uv);
       }
   }
-  for (int e = tid; e < 256 * RE; e += kThreads) {
-    const int j = e >> 8, c = e & 255;
+  for (int e = tid; e < BT * RE; e += kThreads) {
+    const int j = e / BT, c = e % BT;
     bt[ep(c, j)] = (j < r && n0 + c < N) ? B[static_cast<size_t>(j) * N + n0 + c] : uint16_t(0);
   }
   __syncthreads();
 #pragma unroll
   for (int ks = 0; ks < RE / 16; ++ks) {
-    uint4 a[4], b[2];
+    uint4 a[kFM], b[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const uint4*>(us + ep(wm * 128 + blk(i) * 32 + l32, ks * 16 + lh * 8));
+    for (int i = 0; i < kFM; ++i)
+      a[i] = *reinterpret_cast<const uint4*>(us + ep(wm * kHalf + blk(i) * 32 + l32, ks * 16 + lh * 8));
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       b[j] = *reinterpret_cast<const uint4*>(bt + ep(wn * 64 + j * 32 + l32, ks * 16 + lh * 8));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kFM; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kFM; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = n0 + wn * 64 + j * 32 + l32;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * 128 + blk(i) * 32 + mfma32_row(e, lane);
+        const int row = m0 + wm * kHalf + blk(i) * 32 + mfma32_row(e, lane);
         if (row < T && col < N) y[static_cast<size_t>(row) * N + col] = to_bf16(acc[i][j][e]);
       }
     }
 }
 
-template <int RU, int RE>
+template <int BT, int RU, int RE>
 hipError_t launch_fwd_t(int T, int K, int r, float s, const uint16_t* x, const ProjTable& tab,
                         hipStream_t stream) {
-  const int tiles = ((T + BM - 1) / BM) * tab.tile_end[tab.n - 1];
-  lora_fwd_kernel<RU, RE><<<tiles, kThreads, 0, stream>>>(T, K, r, s, x, tab);
+  const int tiles = ((T + BT - 1) / BT) * tab.tile_end[tab.n - 1];
+  lora_fwd_kernel<BT, RU, RE><<<tiles, FwdTile<BT>::kThreads, 0, stream>>>(T, K, r, s, x, tab);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_table(int T, int K, int r, float s, const uint16_t* x, const ProjTable& tab,
-                            hipStream_t stream) {
+template <int BT>
+hipError_t launch_fwd_rank(int T, int K, int r, float s, const uint16_t* x, const ProjTable& tab,
+                           hipStream_t stream) {
   switch ((r + 15) / 16) {
-    case 1: return launch_fwd_t<16, 16>(T, K, r, s, x, tab, stream);
-    case 2: return launch_fwd_t<32, 32>(T, K, r, s, x, tab, stream);
-    case 3: return launch_fwd_t<64, 48>(T, K, r, s, x, tab, stream);
-    default: return launch_fwd_t<64, 64>(T, K, r, s, x, tab, stream);
+    case 1: return launch_fwd_t<BT, 16, 16>(T, K, r, s, x, tab, stream);
+    case 2: return launch_fwd_t<BT, 32, 32>(T, K, r, s, x, tab, stream);
+    case 3: return launch_fwd_t<BT, 64, 48>(T, K, r, s, x, tab, stream);
+    default: return launch_fwd_t<BT, 64, 64>(T, K, r, s, x, tab, stream);
   }
+}
+
+// Tile edge from a round count: a grid of 256 x 256 tiles runs in rounds of 256
+// (one per CU), one of 128 x 128 tiles in rounds of 512 (two per CU; 256 at rank
+// > 32, whose LDS allows one). Measured on MI355X (4096 -> 4096, 5120 -> 5120 and
+// 8192 -> 28672, 64 to 8192 tokens), a full round of 128 tiles costs about 3/4 of
+// a round of 256 tiles at rank <= 32 and 2/3 at rank 64, with the same outputs
+// either way (each output accumulates in the same order).
+int fwd_tile_edge(int64_t T, int cols256, int cols128, int r) {
+  const int64_t rounds256 = ((T + 255) / 256 * cols256 + 255) / 256;
+  const int slots128 = r <= 32 ? 512 : 256;
+  const int64_t rounds128 = ((T + 127) / 128 * cols128 + slots128 - 1) / slots128;
+  const bool small = r <= 32 ? 3 * rounds128 < 4 * rounds256 : 2 * rounds128 < 3 * rounds256;
+  return small ? 128 : 256;
+}
+
+// tab.N and the pointers are set; the column-tile prefix sums follow the tile edge.
+hipError_t launch_fwd_table(int T, int K, int r, float s, const uint16_t* x, ProjTable& tab,
+                            hipStream_t stream) {
+  int cols256 = 0, cols128 = 0;
+  for (int g = 0; g < tab.n; ++g) {
+    cols256 += (tab.N[g] + 255) / 256;
+    cols128 += (tab.N[g] + 127) / 128;
+  }
+  const int bt = fwd_tile_edge(T, cols256, cols128, r);
+  int tiles = 0;
+  for (int g = 0; g < tab.n; ++g) {
+    tiles += (tab.N[g] + bt - 1) / bt;
+    tab.tile_end[g] = tiles;
+  }
+  if (bt == 256) return launch_fwd_rank<256>(T, K, r, s, x, tab, stream);
+  return launch_fwd_rank<128>(T, K, r, s, x, tab, stream);
 }
 
 }  // namespace
@@ -437,7 +493,6 @@ hipError_t launch_lora_fwd(int T, int K, int N, int r, float s, const uint16_t* 
     return launch_lora_fwd_stream(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
   ProjTable tab{};
   tab.n = 1;
-  tab.tile_end[0] = (N + BN - 1) / BN;
   tab.N[0] = N;
   tab.codes[0] = codes;
   tab.absmax[0] = absmax;
@@ -465,10 +520,7 @@ hipError_t launch_lora_fwd_multi(int T, int K, int n_proj, const int* N, int r, 
   }
   ProjTable tab{};
   tab.n = n_proj;
-  int tiles = 0;
   for (int g = 0; g < n_proj; ++g) {
-    tiles += (N[g] + BN - 1) / BN;
-    tab.tile_end[g] = tiles;
     tab.N[g] = N[g];
     tab.codes[g] = codes[g];
     tab.absmax[g] = absmax[g];

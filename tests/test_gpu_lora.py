@@ -100,6 +100,56 @@ def test_few_token_shapes(q, T, K, N, r):
     _check_full(q, inp, 16.0, r, f"few T={T} K={K} N={N} r={r}")
 
 
+@pytest.mark.parametrize("r", [16, 64])
+def test_forward_tile_edges_agree(q, r):
+    """The forward runs 256 x 256 tiles when they fill the GPU and 128 x 128 tiles
+    otherwise; both accumulate every output in the same order. d_out = 32808 at 300
+    tokens gives 2 x 129 = 258 tiles of 256 (256 path, ragged in both dimensions);
+    the first 1000 columns alone give 8 (128 path). Same bits, and the oracle."""
+    from tests.gpu_util import dev_bf16, host_f64
+    T, K, N, Nsub = 300, 256, 32808, 1000
+    inp = synth.custom_inputs(11, T, K, N, r)
+    x, W, A, B = (dev_bf16(inp[k]) for k in ("x", "W", "A", "B"))
+    codes, absmax = q.nf4_quantize(W)
+    y, u = q.lora_nf4_fwd(x, codes, absmax, A, B, 16.0)
+    ys, us = q.lora_nf4_fwd(x, codes[:Nsub].contiguous(), absmax[:Nsub].contiguous(), A,
+                            B[:, :Nsub].contiguous(), 16.0)
+    torch.cuda.synchronize()
+    assert torch.equal(ys, y[:, :Nsub]) and torch.equal(us, u)
+    cols = np.unique(np.concatenate([np.arange(0, N, 97), [N - 1]]))
+    Wc = synth.bf16_bits_to_f32(inp["W"])[cols]
+    c, a = onf4.quantize(Wc)
+    y_ref, u_ref = olora.forward(_f64(inp["x"]), onf4.dequantize_exact(c, a), _f64(inp["A"]),
+                                 _f64(inp["B"])[:, cols], 16.0, r)
+    assert olora.rel_err(host_f64(y)[:, cols], y_ref) <= TOL
+    assert olora.rel_err(host_f64(u), u_ref) <= TOL
+
+
+@pytest.mark.parametrize("r", [16, 64])
+def test_dx_tile_edges_agree(q, r):
+    """The input gradient's tile edge follows the same round count: 500 tokens x
+    d_in 32704 is 2 x 128 tiles of 256 (one round; 256 path, ragged tokens), its
+    first 1024 columns alone 4 x 8 tiles of 128. dX columns depend only on their
+    own weight columns and rows of A: same bits, and the oracle on sampled columns."""
+    from tests.gpu_util import dev_bf16, host_f64
+    T, K, N, Ksub, alpha = 500, 32704, 64, 1024, 16.0
+    inp = synth.custom_inputs(12, T, K, N, r, dy_std=0.1)
+    x, W, A, B, dY = (dev_bf16(inp[k]) for k in ("x", "W", "A", "B", "dY"))
+    codes, absmax = q.nf4_quantize(W)
+    dx, _, _ = q.lora_nf4_bwd(x, dY, codes, absmax, A, B, alpha)
+    dxs, _, _ = q.lora_nf4_bwd(x[:, :Ksub].contiguous(), dY, codes[:, :Ksub // 2].contiguous(),
+                               absmax[:, :Ksub // 64].contiguous(), A[:Ksub].contiguous(), B, alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(dxs, dx[:, :Ksub])
+    cols = np.unique(np.concatenate([np.arange(0, K, 211), [K - 1]]))
+    c, a = onf4.quantize(synth.bf16_bits_to_f32(inp["W"]))
+    D = onf4.dequantize_exact(c, a)
+    dYr, Ar, Br = _f64(inp["dY"]), _f64(inp["A"]), _f64(inp["B"])
+    G = (alpha / r) * (dYr @ Br.T)
+    dx_ref = dYr @ D[:, cols] + G @ Ar[cols].T
+    assert olora.rel_err(host_f64(dx)[:, cols], dx_ref) <= TOL
+
+
 @pytest.mark.parametrize("T,K,N,r", [(300, 256, 192, 16), (7, 320, 200, 24)])
 def test_recompute_u_and_skip_dx_paths(q, T, K, N, r):
     from tests.gpu_util import host_f64
