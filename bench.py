@@ -205,11 +205,12 @@ def time_fwd_bwd(lib, q, torch, d, w, tokens, sp, reps):
     dA = torch.empty((K, r), dtype=torch.bfloat16, device="cuda")
     dB = torch.empty((r, N), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(q.lora_nf4_bwd_workspace_bytes(T, K, N, r), dtype=torch.uint8, device="cuda")
+    fws = torch.empty(max(q.lora_nf4_fwd_workspace_bytes(T, K, N, r), 256), dtype=torch.uint8, device="cuda")
 
     def fwd():
         st = lib.lora_nf4_fwd(T, K, N, r, w.alpha, x.data_ptr(), d["codes"].data_ptr(),
                               d["absmax"].data_ptr(), d["A"].data_ptr(), d["B"].data_ptr(),
-                              y.data_ptr(), u.data_ptr(), sp)
+                              y.data_ptr(), u.data_ptr(), fws.data_ptr(), fws.numel(), sp)
         if st != 0:
             raise q.LoraNF4Error("lora_nf4_fwd", st)
 
@@ -373,6 +374,10 @@ def multi_projection_run(lib, q, torch, sp, reps=10):
     wsm = torch.empty(max(q.lora_nf4_bwd_multi_workspace_bytes(T, K, Ns, r), 256), dtype=torch.uint8, device="cuda")
     wss = [torch.empty(max(q.lora_nf4_bwd_workspace_bytes(T, K, N, r), 256), dtype=torch.uint8, device="cuda")
            for N in Ns]
+    fwsm = torch.empty(max(q.lora_nf4_fwd_multi_workspace_bytes(T, K, Ns, r), 256), dtype=torch.uint8,
+                       device="cuda")
+    fwss = [torch.empty(max(q.lora_nf4_fwd_workspace_bytes(T, K, N, r), 256), dtype=torch.uint8, device="cuda")
+            for N in Ns]
     import ctypes
     arr = lambda ts: (ctypes.c_void_p * 3)(*[t.data_ptr() for t in ts])
     cv = lambda a: ctypes.cast(a, ctypes.c_void_p)
@@ -382,7 +387,8 @@ def multi_projection_run(lib, q, torch, sp, reps=10):
 
     def fused():
         st = lib.lora_nf4_fwd_multi(T, K, 3, cv(d_out), r, w.alpha, x.data_ptr(), cv(keep["c"]), cv(keep["a"]),
-                                    cv(keep["A"]), cv(keep["B"]), cv(keep["y"]), cv(keep["u"]), sp)
+                                    cv(keep["A"]), cv(keep["B"]), cv(keep["y"]), cv(keep["u"]), fwsm.data_ptr(),
+                                    fwsm.numel(), sp)
         st = st or lib.lora_nf4_bwd_multi(T, K, 3, cv(d_out), r, w.alpha, x.data_ptr(), cv(keep["dy"]),
                                           cv(keep["c"]), cv(keep["a"]), cv(keep["A"]), cv(keep["B"]),
                                           cv(keep["u"]), dx.data_ptr(), cv(keep["dA"]), cv(keep["dB"]),
@@ -393,7 +399,8 @@ def multi_projection_run(lib, q, torch, sp, reps=10):
     def separate():
         for g in range(3):
             st = lib.lora_nf4_fwd(T, K, Ns[g], r, w.alpha, x.data_ptr(), codes[g].data_ptr(), absmax[g].data_ptr(),
-                                  A[g].data_ptr(), B[g].data_ptr(), ys[g].data_ptr(), us[g].data_ptr(), sp)
+                                  A[g].data_ptr(), B[g].data_ptr(), ys[g].data_ptr(), us[g].data_ptr(),
+                                  fwss[g].data_ptr(), fwss[g].numel(), sp)
             st = st or lib.lora_nf4_bwd(T, K, Ns[g], r, w.alpha, x.data_ptr(), dy[g].data_ptr(),
                                         codes[g].data_ptr(), absmax[g].data_ptr(), A[g].data_ptr(),
                                         B[g].data_ptr(), us[g].data_ptr(), dxs[g].data_ptr(), dAs[g].data_ptr(),
@@ -457,7 +464,8 @@ def main():
         del W
         T, K, N, r = w.tokens, p.d_in, p.d_out, w.r
         ws = torch.empty(q.lora_nf4_bwd_workspace_bytes(T, K, N, r), dtype=torch.uint8, device="cuda")
-        projs.append(dict(p=p, x=x, A=A, B=B, dY=dY, codes=codes, absmax=absmax, ws=ws,
+        fws = torch.empty(max(q.lora_nf4_fwd_workspace_bytes(T, K, N, r), 256), dtype=torch.uint8, device="cuda")
+        projs.append(dict(p=p, x=x, A=A, B=B, dY=dY, codes=codes, absmax=absmax, ws=ws, fws=fws,
                           y=torch.empty((T, N), dtype=torch.bfloat16, device="cuda"),
                           u=torch.empty((T, r), dtype=torch.bfloat16, device="cuda"),
                           dx=torch.empty((T, K), dtype=torch.bfloat16, device="cuda"),
@@ -485,10 +493,12 @@ def main():
             arr = lambda key: (ctypes.c_void_p * len(un))(*[projs[j][key].data_ptr() for j in un])
             d_out = [projs[j]["p"].d_out for j in un]
             nb = q.lora_nf4_bwd_multi_workspace_bytes(w.tokens, projs[un[0]]["p"].d_in, d_out, w.r)
+            nf = q.lora_nf4_fwd_multi_workspace_bytes(w.tokens, projs[un[0]]["p"].d_in, d_out, w.r)
             multi_args[ui] = dict(d_out=(ctypes.c_int64 * len(un))(*d_out),
                                   codes=arr("codes"), absmax=arr("absmax"), A=arr("A"), B=arr("B"),
                                   y=arr("y"), u=arr("u"), dy=arr("dY"), dA=arr("dA"), dB=arr("dB"),
-                                  ws=torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda"))
+                                  ws=torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda"),
+                                  fws=torch.empty(max(nf, 256), dtype=torch.uint8, device="cuda"))
             for j in un:  # the group's per-projection backward workspaces are not used
                 projs[j]["ws"] = torch.empty(0, dtype=torch.uint8, device="cuda")
     torch.cuda.empty_cache()
@@ -497,7 +507,8 @@ def main():
         p = d["p"]
         st = lib.lora_nf4_fwd(w.tokens, p.d_in, p.d_out, w.r, w.alpha, d["x"].data_ptr(),
                               d["codes"].data_ptr(), d["absmax"].data_ptr(), d["A"].data_ptr(),
-                              d["B"].data_ptr(), d["y"].data_ptr(), d["u"].data_ptr(), sp)
+                              d["B"].data_ptr(), d["y"].data_ptr(), d["u"].data_ptr(), d["fws"].data_ptr(),
+                              d["fws"].numel(), sp)
         if st != 0:
             raise q.LoraNF4Error("lora_nf4_fwd", st)
 
@@ -519,7 +530,7 @@ def main():
         cv = lambda a: ctypes.cast(a, ctypes.c_void_p)
         st = lib.lora_nf4_fwd_multi(w.tokens, d0["p"].d_in, len(un), cv(m["d_out"]), w.r, w.alpha,
                                     d0["x"].data_ptr(), cv(m["codes"]), cv(m["absmax"]), cv(m["A"]),
-                                    cv(m["B"]), cv(m["y"]), cv(m["u"]), sp)
+                                    cv(m["B"]), cv(m["y"]), cv(m["u"]), m["fws"].data_ptr(), m["fws"].numel(), sp)
         if st != 0:
             raise q.LoraNF4Error("lora_nf4_fwd_multi", st)
 

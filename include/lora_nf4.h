@@ -58,7 +58,7 @@ typedef enum {
                             of 8, or a size beyond the 2^31 element-index range     */
     LN_EALIGN = -3,      /* a data pointer is not 16-byte aligned                    */
     LN_ERANK = -4,       /* r < 1 or r > LN_MAX_RANK                                 */
-    LN_EWORKSPACE = -5,  /* workspace null or smaller than lora_nf4_bwd_workspace_bytes */
+    LN_EWORKSPACE = -5,  /* workspace null or smaller than the entry point's *_workspace_bytes */
     LN_EALIAS = -6,      /* an output overlaps an input or another output            */
     LN_EHIP = -7         /* a HIP launch reported an error                           */
 } ln_status;
@@ -95,14 +95,26 @@ int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows, int6
  *   y        bf16 [T, d_out]  (output)
  *   u_save   bf16 [T, r] = x A, rounded to bf16 (output; may be NULL). Passing it
  *            to lora_nf4_bwd saves that pass recomputing it.
+ *   workspace  device scratch of at least lora_nf4_fwd_workspace_bytes(T, d_in,
+ *            d_out, r) bytes, 256-byte aligned, owned by the caller (contents on
+ *            entry do not matter, on return unspecified; concurrent calls need
+ *            separate workspaces). That size is non-zero only for few tokens
+ *            (T <= 128 at r % 8 == 0, r <= 64), where the reduction over d_in is
+ *            split across workgroups and fp32 partial sums meet in the workspace;
+ *            when it is 0 the workspace may be NULL.
  * T >= 0, d_in % 64 == 0, d_out % 8 == 0, 1 <= r <= LN_MAX_RANK. s = lora_alpha / r
  * is formed in float32 on the host. T = 0 is an empty batch: nothing is computed
- * and x, y, u_save may be NULL.
+ * and x, y, u_save and the workspace may be NULL. LN_EWORKSPACE if the workspace
+ * is needed and NULL or too small; the workspace must not overlap any operand.
  */
 int lora_nf4_fwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha,
                  const uint16_t* x, const uint8_t* w_codes, const float* w_absmax,
                  const uint16_t* A, const uint16_t* B, uint16_t* y, uint16_t* u_save,
-                 void* stream);
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes lora_nf4_fwd needs (0 if the sizes are invalid, T = 0, or the
+   shape takes a path without one). */
+size_t lora_nf4_fwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t r);
 
 /*
  * lora_nf4_fwd_multi — the forward of n_proj LoRA projections that read the same
@@ -121,16 +133,26 @@ int lora_nf4_fwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_a
  *   A, B, y              HOST arrays [n_proj] of DEVICE pointers, each laid out as
  *                        for lora_nf4_fwd with that projection's d_out
  *   u_save               NULL, or a HOST array [n_proj] whose entries may be NULL
+ *   workspace            as for lora_nf4_fwd, sized by
+ *                        lora_nf4_fwd_multi_workspace_bytes (non-zero only when
+ *                        the projections run one after the other on the
+ *                        few-token path, which then reuse it in turn)
  * All projections share T, d_in, r and lora_alpha. The host arrays are read
- * during the call only. Every output (each y[g], each u_save[g]) must be
- * disjoint from every input and from the other outputs (LN_EALIAS). Errors as
- * for lora_nf4_fwd, plus LN_EINVAL for n_proj out of range or a NULL array.
+ * during the call only. Every output (each y[g], each u_save[g], the workspace)
+ * must be disjoint from every input and from the other outputs (LN_EALIAS).
+ * Errors as for lora_nf4_fwd, plus LN_EINVAL for n_proj out of range or a NULL
+ * array.
  */
 int lora_nf4_fwd_multi(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d_out, int32_t r,
                        float lora_alpha, const uint16_t* x, const uint8_t* const* w_codes,
                        const float* const* w_absmax, const uint16_t* const* A,
                        const uint16_t* const* B, uint16_t* const* y, uint16_t* const* u_save,
-                       void* stream);
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes lora_nf4_fwd_multi needs (0 if the sizes are invalid, T = 0, or
+   no projection needs one). */
+size_t lora_nf4_fwd_multi_workspace_bytes(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d_out,
+                                          int32_t r);
 
 /*
  * lora_nf4_bwd — dX, dA, dB of the forward above for upstream gradient dY.

@@ -44,7 +44,8 @@ EXPORTED_SYMBOLS = ("nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_
                     "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_merge",
                     "lora_nf4_status_string", "lora_adamw_step", "lora_nf4_rslora_alpha",
                     "nf4_absmax_quantize", "nf4_absmax_dequantize", "lora_nf4_bwd_multi",
-                    "lora_nf4_bwd_multi_workspace_bytes")
+                    "lora_nf4_bwd_multi_workspace_bytes", "lora_nf4_fwd_workspace_bytes",
+                    "lora_nf4_fwd_multi_workspace_bytes")
 
 _lib = None
 
@@ -54,9 +55,11 @@ _SIGS = {
     "nf4_quantize": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _p, _p, _p]),
     "nf4_dequantize": (ctypes.c_int, [_p, _p, _i64, _i64, ctypes.c_int, _p, _p]),
     "lora_nf4_fwd": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_float,
-                                    _p, _p, _p, _p, _p, _p, _p, _p]),
+                                    _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
+    "lora_nf4_fwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, ctypes.c_int32]),
     "lora_nf4_fwd_multi": (ctypes.c_int, [_i64, _i64, ctypes.c_int32, _p, ctypes.c_int32,
-                                          ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _p]),
+                                          ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
+    "lora_nf4_fwd_multi_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, ctypes.c_int32, _p, ctypes.c_int32]),
     "lora_nf4_bwd": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_float,
                                     _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
     "lora_nf4_bwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, ctypes.c_int32]),
@@ -167,17 +170,33 @@ def _lora_shapes(x, codes, A, B):
     return T, K, N, r
 
 
-def lora_nf4_fwd(x, codes, absmax, A, B, lora_alpha: float, save_u: bool = True, out=None):
-    """y = x deq(W)^T + (lora_alpha / r) (x A) B; returns (y, u) with u = bf16(x A) or None."""
+def lora_nf4_fwd_workspace_bytes(T: int, K: int, N: int, r: int) -> int:
+    return int(library().lora_nf4_fwd_workspace_bytes(T, K, N, r))
+
+
+def _workspace(nbytes: int, workspace, device):
+    """The caller's workspace tensor, or a new one when the entry point needs one."""
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes > 0 else None
+    return _dev(workspace, "workspace", torch.uint8)
+
+
+def lora_nf4_fwd(x, codes, absmax, A, B, lora_alpha: float, save_u: bool = True, out=None,
+                 workspace: torch.Tensor | None = None):
+    """y = x deq(W)^T + (lora_alpha / r) (x A) B; returns (y, u) with u = bf16(x A) or None.
+    Few-token shapes need a workspace (lora_nf4_fwd_workspace_bytes); one is allocated
+    when none is given."""
     bf = torch.bfloat16
     _dev(x, "x", bf, 2), _dev(codes, "codes", torch.uint8, 2), _dev(absmax, "absmax", torch.float32, 2)
     _dev(A, "A", bf, 2), _dev(B, "B", bf, 2)
     T, K, N, r = _lora_shapes(x, codes, A, B)
     y = torch.empty((T, N), dtype=bf, device=x.device) if out is None else _dev(out, "out", bf, 2)
     u = torch.empty((T, r), dtype=bf, device=x.device) if save_u else None
+    ws = _workspace(lora_nf4_fwd_workspace_bytes(T, K, N, r), workspace, x.device)
     _check("lora_nf4_fwd", library().lora_nf4_fwd(T, K, N, r, float(lora_alpha), x.data_ptr(),
                                                   codes.data_ptr(), absmax.data_ptr(), A.data_ptr(),
-                                                  B.data_ptr(), y.data_ptr(), _ptr(u), _stream(x)))
+                                                  B.data_ptr(), y.data_ptr(), _ptr(u), _ptr(ws),
+                                                  0 if ws is None else ws.numel(), _stream(x)))
     return y, u
 
 
@@ -186,7 +205,14 @@ def _ptr_array(ptrs):
     return arr, ctypes.cast(arr, ctypes.c_void_p)
 
 
-def lora_nf4_fwd_multi(x, codes, absmax, A, B, lora_alpha: float, save_u: bool = True):
+def lora_nf4_fwd_multi_workspace_bytes(T: int, K: int, d_outs, r: int) -> int:
+    n = len(d_outs)
+    arr = (ctypes.c_int64 * n)(*d_outs)
+    return int(library().lora_nf4_fwd_multi_workspace_bytes(T, K, n, ctypes.cast(arr, ctypes.c_void_p), r))
+
+
+def lora_nf4_fwd_multi(x, codes, absmax, A, B, lora_alpha: float, save_u: bool = True,
+                       workspace: torch.Tensor | None = None):
     """Forward of several projections that share x (lists, one entry per projection):
     returns ([y_g], [u_g] or None), the same values as one lora_nf4_fwd per projection."""
     bf = torch.bfloat16
@@ -207,9 +233,12 @@ def lora_nf4_fwd_multi(x, codes, absmax, A, B, lora_alpha: float, save_u: bool =
     d_out = (ctypes.c_int64 * n)(*[sh[2] for sh in shapes])
     keep = [_ptr_array([t.data_ptr() for t in lst]) for lst in (codes, absmax, A, B, ys)]
     u_arr = _ptr_array([t.data_ptr() for t in us]) if save_u else (None, None)
+    ws = _workspace(lora_nf4_fwd_multi_workspace_bytes(T, K, [sh[2] for sh in shapes], r), workspace,
+                    x.device)
     _check("lora_nf4_fwd_multi", library().lora_nf4_fwd_multi(
         T, K, n, ctypes.cast(d_out, ctypes.c_void_p), r, float(lora_alpha), x.data_ptr(),
-        keep[0][1], keep[1][1], keep[2][1], keep[3][1], keep[4][1], u_arr[1], _stream(x)))
+        keep[0][1], keep[1][1], keep[2][1], keep[3][1], keep[4][1], u_arr[1], _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(x)))
     return ys, us
 
 

@@ -59,7 +59,7 @@ const char* lora_nf4_status_string(int status) {
     case LN_ESHAPE: return "unsupported shape (d_in/cols must be a multiple of 64, d_out a multiple of 8, sizes below 2^31)";
     case LN_EALIGN: return "data pointer not 16-byte aligned (workspace: 256-byte)";
     case LN_ERANK: return "LoRA rank r outside [1, LN_MAX_RANK]";
-    case LN_EWORKSPACE: return "workspace missing or smaller than lora_nf4_bwd_workspace_bytes()";
+    case LN_EWORKSPACE: return "workspace missing or smaller than the entry point's *_workspace_bytes()";
     case LN_EALIAS: return "an output overlaps an input or another output";
     case LN_EHIP: return "HIP launch error";
     default: return "unknown status";
@@ -98,10 +98,15 @@ int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows, int6
                                                 static_cast<hipStream_t>(stream)));
 }
 
+size_t lora_nf4_fwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t r) {
+  if (T == 0 || check_linear_shape(T, d_in, d_out, r, 1.0f) != LN_OK) return 0;
+  return lnf4::fwd_workspace_bytes(T, d_in, d_out, r);
+}
+
 int lora_nf4_fwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha,
                  const uint16_t* x, const uint8_t* w_codes, const float* w_absmax,
                  const uint16_t* A, const uint16_t* B, uint16_t* y, uint16_t* u_save,
-                 void* stream) {
+                 void* workspace, size_t workspace_bytes, void* stream) {
   if (w_codes == nullptr || w_absmax == nullptr || A == nullptr || B == nullptr) return LN_EINVAL;
   if (T != 0 && (x == nullptr || y == nullptr)) return LN_EINVAL;
   int st = check_linear_shape(T, d_in, d_out, r, lora_alpha);
@@ -110,29 +115,43 @@ int lora_nf4_fwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_a
   if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_absmax) || !aligned16(A) ||
       !aligned16(B) || !aligned16(y) || (u_save != nullptr && !aligned16(u_save)))
     return LN_EALIGN;
+  const size_t need = lnf4::fwd_workspace_bytes(T, d_in, d_out, r);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LN_EWORKSPACE;
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LN_EALIGN;
   const size_t t = T, k = d_in, n = d_out, rr = r;
-  const Span outs[2] = {{y, t * n * 2}, {u_save, t * rr * 2}};
+  const Span outs[3] = {{y, t * n * 2}, {u_save, t * rr * 2}, {need > 0 ? workspace : nullptr, need}};
   const Span ins[5] = {{x, t * k * 2}, {w_codes, n * k / 2}, {w_absmax, n * k / 64 * 4},
                        {A, k * rr * 2}, {B, rr * n * 2}};
-  if (any_alias(outs, 2, ins, 5)) return LN_EALIAS;
+  if (any_alias(outs, 3, ins, 5)) return LN_EALIAS;
   const float s = lora_alpha / static_cast<float>(r);
   return hip_status(lnf4::launch_lora_fwd(static_cast<int>(T), static_cast<int>(d_in),
                                           static_cast<int>(d_out), r, s, x, w_codes, w_absmax, A, B,
-                                          y, u_save, static_cast<hipStream_t>(stream)));
+                                          y, u_save, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t lora_nf4_fwd_multi_workspace_bytes(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d_out,
+                                          int32_t r) {
+  if (T == 0 || n_proj < 1 || n_proj > LN_MAX_PROJ || d_out == nullptr) return 0;
+  int N[LN_MAX_PROJ];
+  for (int g = 0; g < n_proj; ++g) {
+    if (check_linear_shape(T, d_in, d_out[g], r, 1.0f) != LN_OK) return 0;
+    N[g] = static_cast<int>(d_out[g]);
+  }
+  return lnf4::fwd_multi_workspace_bytes(T, d_in, n_proj, N, r);
 }
 
 int lora_nf4_fwd_multi(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d_out, int32_t r,
                        float lora_alpha, const uint16_t* x, const uint8_t* const* w_codes,
                        const float* const* w_absmax, const uint16_t* const* A,
                        const uint16_t* const* B, uint16_t* const* y, uint16_t* const* u_save,
-                       void* stream) {
+                       void* workspace, size_t workspace_bytes, void* stream) {
   if (n_proj < 1 || n_proj > LN_MAX_PROJ) return LN_EINVAL;
   if ((T != 0 && x == nullptr) || d_out == nullptr || w_codes == nullptr || w_absmax == nullptr ||
       A == nullptr || B == nullptr || y == nullptr)
     return LN_EINVAL;
   if (!aligned16(x)) return LN_EALIGN;
   const size_t t = T, k = d_in, rr = r;
-  Span outs[2 * LN_MAX_PROJ];
+  Span outs[2 * LN_MAX_PROJ + 1];
   Span ins[1 + 4 * LN_MAX_PROJ];
   int n_out = 0, n_in = 0;
   int N[LN_MAX_PROJ];
@@ -156,11 +175,15 @@ int lora_nf4_fwd_multi(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d
     ins[n_in++] = {A[g], k * rr * 2};
     ins[n_in++] = {B[g], rr * n * 2};
   }
+  const size_t need = T == 0 ? 0 : lnf4::fwd_multi_workspace_bytes(T, d_in, n_proj, N, r);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LN_EWORKSPACE;
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LN_EALIGN;
+  if (need > 0) outs[n_out++] = {workspace, need};
   if (any_alias(outs, n_out, ins, n_in)) return LN_EALIAS;
   if (T == 0) return LN_OK;  // empty batch
   const float s = lora_alpha / static_cast<float>(r);
   return hip_status(lnf4::launch_lora_fwd_multi(static_cast<int>(T), static_cast<int>(d_in), n_proj, N,
-                                                r, s, x, w_codes, w_absmax, A, B, y, u_save,
+                                                r, s, x, w_codes, w_absmax, A, B, y, u_save, workspace,
                                                 static_cast<hipStream_t>(stream)));
 }
 

@@ -23,18 +23,43 @@ hipError_t launch_lora_fwd_generic(int T, int K, int N, int r, float s, const ui
                                    const uint16_t* B, uint16_t* y, uint16_t* u_save,
                                    hipStream_t stream);
 
+// Forward dispatch: generic kernels (ranks not a multiple of 8 or above 64, operands
+// past the buffer range), split-K weight streaming (few tokens; needs a workspace of
+// fwd_workspace_bytes), tiled kernels otherwise. `workspace` may be null when
+// fwd_workspace_bytes is 0.
+size_t fwd_workspace_bytes(int64_t T, int64_t K, int64_t N, int r);
 hipError_t launch_lora_fwd(int T, int K, int N, int r, float s, const uint16_t* x,
                            const uint8_t* codes, const float* absmax, const uint16_t* A,
-                           const uint16_t* B, uint16_t* y, uint16_t* u_save, hipStream_t stream);
+                           const uint16_t* B, uint16_t* y, uint16_t* u_save, void* workspace,
+                           hipStream_t stream);
 
 // Several projections of the same x (q/k/v, gate/up) in one forward launch when
-// every projection takes the 256 x 256 tiles; otherwise one launch per projection.
+// every projection takes the tiled kernels; otherwise one forward per projection,
+// one after the other on the stream, sharing the workspace (the largest of theirs).
 constexpr int kMaxProj = 8;
+size_t fwd_multi_workspace_bytes(int64_t T, int64_t K, int n_proj, const int* N, int r);
 hipError_t launch_lora_fwd_multi(int T, int K, int n_proj, const int* N, int r, float s,
                                  const uint16_t* x, const uint8_t* const* codes,
                                  const float* const* absmax, const uint16_t* const* A,
                                  const uint16_t* const* B, uint16_t* const* y,
-                                 uint16_t* const* u_save, hipStream_t stream);
+                                 uint16_t* const* u_save, void* workspace, hipStream_t stream);
+
+// Split-K weight-streaming forward for up to 128 tokens (r % 8 == 0, r <= 64):
+// workgroups of 64 weight rows x one of `splits` d_in chunks (plus one per split
+// and 16-wide rank block for U), fp32 partials [splits][T][N] and [splits][T][r]
+// in the workspace, then one reduce that stores y and U.
+struct SplitKPlan {
+  int ncb;          // 64-row column blocks
+  int splits;       // d_in chunks (each non-empty)
+  int steps_per;    // 128-element reduction steps per chunk
+  size_t part_bytes, bytes;
+};
+bool lora_fwd_splitk_supported(int64_t T, int r);
+SplitKPlan plan_fwd_splitk(int T, int K, int N, int r);
+hipError_t launch_lora_fwd_splitk(int T, int K, int N, int r, float s, const uint16_t* x,
+                                  const uint8_t* codes, const float* absmax, const uint16_t* A,
+                                  const uint16_t* B, uint16_t* y, uint16_t* u_save, void* workspace,
+                                  hipStream_t stream);
 
 // Weight-streaming forward for a few tokens (1 <= T <= 32, r % 8 == 0, r <= 64):
 // one workgroup per 16 weight rows, no workspace.

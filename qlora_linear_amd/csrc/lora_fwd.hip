@@ -484,11 +484,46 @@ hipError_t launch_fwd_table(int T, int K, int r, float s, const uint16_t* x, Pro
 
 }  // namespace
 
+namespace {
+// Few tokens: the one-launch weight-streaming kernel when its 16-row workgroups
+// fit one round of the CUs (T <= 32, d_out <= 4096), else the split-K kernel and
+// its reduce (measured on MI355X: the reduce costs a few microseconds of latency,
+// which one round of streaming workgroups beats).
+bool fwd_uses_splitk(int64_t T, int64_t K, int64_t N, int r) {
+  if (r % 8 != 0 || r > 64 || !fits_buffer(T, K, N) || !lora_fwd_splitk_supported(T, r)) return false;
+  return !(lora_fwd_stream_supported(T, r) && (N + 15) / 16 <= 256);
+}
+bool fwd_multi_tiled(int64_t T, int64_t K, int n_proj, const int* N, int r) {
+  bool tiled = r % 8 == 0 && r <= 64 && n_proj <= kMaxProj && !lora_fwd_stream_supported(T, r);
+  for (int g = 0; g < n_proj; ++g) tiled = tiled && fits_buffer(T, K, N[g]) && !fwd_uses_splitk(T, K, N[g], r);
+  return tiled;
+}
+}  // namespace
+
+size_t fwd_workspace_bytes(int64_t T, int64_t K, int64_t N, int r) {
+  return fwd_uses_splitk(T, K, N, r) ? plan_fwd_splitk(static_cast<int>(T), static_cast<int>(K),
+                                                       static_cast<int>(N), r).bytes
+                                     : 0;
+}
+
+size_t fwd_multi_workspace_bytes(int64_t T, int64_t K, int n_proj, const int* N, int r) {
+  if (fwd_multi_tiled(T, K, n_proj, N, r)) return 0;
+  size_t b = 0;
+  for (int g = 0; g < n_proj; ++g) {
+    const size_t bg = fwd_workspace_bytes(T, K, N[g], r);
+    b = bg > b ? bg : b;
+  }
+  return b;
+}
+
 hipError_t launch_lora_fwd(int T, int K, int N, int r, float s, const uint16_t* x,
                            const uint8_t* codes, const float* absmax, const uint16_t* A,
-                           const uint16_t* B, uint16_t* y, uint16_t* u_save, hipStream_t stream) {
+                           const uint16_t* B, uint16_t* y, uint16_t* u_save, void* workspace,
+                           hipStream_t stream) {
   if (r % 8 != 0 || r > 64 || !fits_buffer(T, K, N))
     return launch_lora_fwd_generic(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
+  if (fwd_uses_splitk(T, K, N, r))
+    return launch_lora_fwd_splitk(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, workspace, stream);
   if (lora_fwd_stream_supported(T, r))
     return launch_lora_fwd_stream(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
   ProjTable tab{};
@@ -507,13 +542,11 @@ hipError_t launch_lora_fwd_multi(int T, int K, int n_proj, const int* N, int r, 
                                  const uint16_t* x, const uint8_t* const* codes,
                                  const float* const* absmax, const uint16_t* const* A,
                                  const uint16_t* const* B, uint16_t* const* y,
-                                 uint16_t* const* u_save, hipStream_t stream) {
-  bool tiled = r % 8 == 0 && r <= 64 && !lora_fwd_stream_supported(T, r) && n_proj <= kMaxProj;
-  for (int g = 0; g < n_proj; ++g) tiled = tiled && fits_buffer(T, K, N[g]);
-  if (!tiled) {  // each projection on its own path
+                                 uint16_t* const* u_save, void* workspace, hipStream_t stream) {
+  if (!fwd_multi_tiled(T, K, n_proj, N, r)) {  // each projection on its own path
     for (int g = 0; g < n_proj; ++g) {
       const hipError_t e = launch_lora_fwd(T, K, N[g], r, s, x, codes[g], absmax[g], A[g], B[g], y[g],
-                                           u_save == nullptr ? nullptr : u_save[g], stream);
+                                           u_save == nullptr ? nullptr : u_save[g], workspace, stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
                             "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_merge",
                             "lora_nf4_status_string", "lora_adamw_step", "lora_nf4_rslora_alpha",
                             "nf4_absmax_quantize", "nf4_absmax_dequantize", "lora_nf4_bwd_multi",
-                            "lora_nf4_bwd_multi_workspace_bytes"])
+                            "lora_nf4_bwd_multi_workspace_bytes", "lora_nf4_fwd_workspace_bytes",
+                            "lora_nf4_fwd_multi_workspace_bytes"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -55,8 +56,10 @@ P = 1 << 40
 
 
 def _fwd(lib, T=8, K=64, N=64, r=8, alpha=16.0, x=P, c=P + (1 << 30), a=P + (2 << 30), A=P + (3 << 30),
-         B=P + (4 << 30), y=P + (5 << 30), u=None):
-    return lib.lora_nf4_fwd(T, K, N, r, alpha, x, c, a, A, B, y, u, None)
+         B=P + (4 << 30), y=P + (5 << 30), u=None, ws=P + (6 << 30), ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.lora_nf4_fwd_workspace_bytes(max(T, 0), K, N, r)
+    return lib.lora_nf4_fwd(T, K, N, r, alpha, x, c, a, A, B, y, u, ws, ctypes.c_size_t(ws_bytes), None)
 
 
 def test_fwd_validation(lib):
@@ -76,7 +79,36 @@ def test_fwd_validation(lib):
     assert _fwd(lib, u=P + (5 << 30) + 64) == LN_EALIAS     # u_save inside y
 
 
-def _fwd_multi(lib, n=3, T=8, K=64, N=(64, 16, 16), r=8, alpha=16.0, x=P, ptrs=None, u=None, null=None):
+def test_fwd_workspace(lib):
+    """Up to 128 tokens the reduction over d_in is split across workgroups, with a
+    workspace (except a few tokens on d_out <= 4096: one streaming launch); the
+    tiled and generic paths take none (NULL accepted)."""
+    need = lib.lora_nf4_fwd_workspace_bytes(64, 64, 64, 8)
+    assert need > 0 and need % 256 == 0
+    assert lib.lora_nf4_fwd_workspace_bytes(128, 4096, 4096, 16) > 0
+    assert lib.lora_nf4_fwd_workspace_bytes(8, 4096, 8192, 16) > 0       # few tokens, wide d_out
+    assert lib.lora_nf4_fwd_workspace_bytes(8, 4096, 4096, 16) == 0      # few tokens: streaming
+    assert lib.lora_nf4_fwd_workspace_bytes(8192, 4096, 4096, 16) == 0   # tiled
+    assert lib.lora_nf4_fwd_workspace_bytes(64, 64, 64, 12) == 0         # r % 8 != 0: generic kernels
+    assert lib.lora_nf4_fwd_workspace_bytes(0, 64, 64, 8) == 0
+    assert lib.lora_nf4_fwd_workspace_bytes(64, 65, 64, 8) == 0          # invalid sizes
+    assert _fwd(lib, T=64, ws=None) == LN_EWORKSPACE
+    assert _fwd(lib, T=64, ws_bytes=need - 1) == LN_EWORKSPACE
+    assert _fwd(lib, T=64, ws=P + (6 << 30) + 16) == LN_EALIGN
+    assert _fwd(lib, T=64, ws=P + (5 << 30)) == LN_EALIAS            # workspace on top of y
+    assert _fwd(lib, T=64, ws=P + (3 << 30)) == LN_EALIAS            # workspace on top of A
+    assert _fwd(lib, T=0, ws=None, ws_bytes=0) == LN_OK
+    # multi: the largest per-projection need, none for the tiled single launch
+    vp = ctypes.c_void_p
+    d_out = (ctypes.c_int64 * 3)(64, 16, 16)
+    assert lib.lora_nf4_fwd_multi_workspace_bytes(64, 64, 3, ctypes.cast(d_out, vp), 8) == need
+    big = (ctypes.c_int64 * 3)(4096, 1024, 1024)
+    assert lib.lora_nf4_fwd_multi_workspace_bytes(8192, 4096, 3, ctypes.cast(big, vp), 16) == 0
+    assert lib.lora_nf4_fwd_multi_workspace_bytes(64, 64, 0, ctypes.cast(d_out, vp), 8) == 0
+
+
+def _fwd_multi(lib, n=3, T=8, K=64, N=(64, 16, 16), r=8, alpha=16.0, x=P, ptrs=None, u=None, null=None,
+               ws=P + (7 << 30), ws_bytes=None):
     # projection g's tensors sit at P + ((8 g + i) << 30), i = codes, absmax, A, B, y
     vp = ctypes.c_void_p
     base = {name: [P + ((8 * (g + 1) + i) << 30) for g in range(n)]
@@ -89,10 +121,13 @@ def _fwd_multi(lib, n=3, T=8, K=64, N=(64, 16, 16), r=8, alpha=16.0, x=P, ptrs=N
         arrs[null] = None
     d_out = (ctypes.c_int64 * n)(*list(N)[:n])
     u_arr = None if u is None else (vp * n)(*u)
+    if ws_bytes is None:
+        ws_bytes = lib.lora_nf4_fwd_multi_workspace_bytes(max(T, 0), K, n, ctypes.cast(d_out, vp), r)
     return lib.lora_nf4_fwd_multi(T, K, n, ctypes.cast(d_out, vp), r, alpha, x,
                                   *(ctypes.cast(arrs[k], vp) if arrs[k] is not None else None
                                     for k in ("codes", "absmax", "A", "B", "y")),
-                                  ctypes.cast(u_arr, vp) if u_arr is not None else None, None)
+                                  ctypes.cast(u_arr, vp) if u_arr is not None else None, ws,
+                                  ctypes.c_size_t(ws_bytes), None)
 
 
 def test_fwd_multi_validation(lib):
@@ -112,6 +147,8 @@ def test_fwd_multi_validation(lib):
     assert _fwd_multi(lib, ptrs={"y": (2, y0 + 256)}) == LN_EALIAS     # y[2] inside y[0]
     assert _fwd_multi(lib, ptrs={"y": (1, P)}) == LN_EALIAS            # y[1] on top of x
     assert _fwd_multi(lib, u=[None, y0, None]) == LN_EALIAS           # u[1] on top of y[0]
+    assert _fwd_multi(lib, T=64, ws=None) == LN_EWORKSPACE
+    assert _fwd_multi(lib, T=64, ws=y0) == LN_EALIAS                  # workspace on top of y[0]
 
 
 def test_bwd_validation_and_workspace(lib):

@@ -85,13 +85,17 @@ def test_odd_shapes(q, T, K, N, r):
     _check_full(q, inp, 16.0, r, f"odd T={T} K={K} N={N} r={r}")
 
 
-# Few tokens (T <= 32, r % 8 == 0, r <= 64): the weight-streaming forward. Cases
-# cover a single half-filled reduction chunk (d_in = 64), a half-filled last
-# chunk (d_in % 128 == 64), d_out not a multiple of the 16-row block, one and two
-# 16-token blocks, and every rank block count.
+# Few tokens (r % 8 == 0, r <= 64): the one-launch weight-streaming forward (T <=
+# 32, d_out <= 4096), the split-K weight-streaming forward (T <= 128 otherwise),
+# and the weight-streaming dX (T <= 32). Cases cover a single half-filled
+# reduction step (d_in = 64), a half-filled last step (d_in % 128 == 64), d_out
+# not a multiple of the 16- or 64-row block, one, two, four and eight 16-token
+# blocks, one and many d_in splits, and every rank block count.
 FEW = [(1, 64, 16, 8), (1, 4096, 64, 16), (5, 192, 40, 16), (9, 64, 8, 56), (16, 256, 48, 24),
        (17, 320, 136, 64), (32, 448, 1000, 32), (32, 128, 8, 8), (16, 4096, 4096, 16),
-       (32, 4096, 1024, 64)]
+       (32, 4096, 1024, 64), (48, 192, 72, 24), (64, 4096, 4096, 16), (100, 320, 200, 64),
+       (128, 448, 1000, 32), (127, 2048, 136, 8), (1, 320, 4104, 16), (8, 192, 5000, 64),
+       (32, 2048, 4160, 40)]
 
 
 @pytest.mark.parametrize("T,K,N,r", FEW)
@@ -163,7 +167,7 @@ def test_recompute_u_and_skip_dx_paths(q, T, K, N, r):
     assert torch.equal(dA3, dA) and torch.equal(dB3, dB)
 
 
-@pytest.mark.parametrize("T", [1000, 16])
+@pytest.mark.parametrize("T", [1000, 100, 16])
 def test_bitwise_deterministic(q, T):
     inp = synth.custom_inputs(3, T, 512, 384, 16)
     r1 = _run_gpu(q, inp, 16.0)
@@ -224,7 +228,7 @@ def test_operand_beyond_two_gib(q):
     assert olora.rel_err(host_f64(dB), dB_ref) <= TOL
 
 
-@pytest.mark.parametrize("T,K,N,r", [(131, 192, 200, 12), (7, 320, 72, 24)])
+@pytest.mark.parametrize("T,K,N,r", [(131, 192, 200, 12), (7, 320, 72, 24), (100, 448, 200, 16)])
 def test_guard_bands_untouched(q, T, K, N, r):
     """Outputs written through the C ABI stay inside their buffers."""
     from tests.gpu_util import Guarded, dev_bf16
@@ -235,8 +239,11 @@ def test_guard_bands_untouched(q, T, K, N, r):
         Guarded(K * r * 2), Guarded(r * N * 2)
     lib = q.library()
     stream = torch.cuda.current_stream().cuda_stream
+    fbytes = lib.lora_nf4_fwd_workspace_bytes(T, K, N, r)
+    gws = Guarded(fbytes) if fbytes else None
     st = lib.lora_nf4_fwd(T, K, N, r, 16.0, x.data_ptr(), codes.data_ptr(), absmax.data_ptr(),
-                          A.data_ptr(), B.data_ptr(), gy.ptr, gu.ptr, stream)
+                          A.data_ptr(), B.data_ptr(), gy.ptr, gu.ptr, gws.ptr if gws else None,
+                          ctypes.c_size_t(fbytes), stream)
     assert st == 0
     nbytes = lib.lora_nf4_bwd_workspace_bytes(T, K, N, r)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -245,7 +252,7 @@ def test_guard_bands_untouched(q, T, K, N, r):
                           gdb.ptr, ws.data_ptr(), ctypes.c_size_t(nbytes), stream)
     assert st == 0
     torch.cuda.synchronize()
-    for g in (gy, gu, gdx, gda, gdb):
+    for g in (gy, gu, gdx, gda, gdb) + ((gws,) if gws else ()):
         assert g.canaries_intact()
     y_ref, _ = olora.forward(_f64(inp["x"]), _oracle_D(inp), _f64(inp["A"]), _f64(inp["B"]), 16.0, r)
     from tests.gpu_util import host_f64
@@ -290,9 +297,10 @@ def test_full_size_sampled(q, wi, pi):
 
 # Multi-projection forward: the same values as one lora_nf4_fwd per projection
 # (bitwise: each output tile runs the same kernel code on the same data), on the
-# tiled path (one launch), the few-token path and the generic path.
+# tiled path (one launch), the few-token paths (one workspace shared by the
+# projections in turn on the split-K path) and the generic path.
 MULTI = [(300, 256, (256, 64, 64), 16), (200, 320, (200, 40, 8), 24), (8, 192, (64, 16, 16), 16),
-         (150, 128, (72, 136), 12)]
+         (150, 128, (72, 136), 12), (100, 256, (128, 64, 64), 16)]
 
 
 @pytest.mark.parametrize("T,K,Ns,r", MULTI)
