@@ -100,12 +100,19 @@ bool lora_dx_multi_supported(int n_proj, const int* N, int r);
 hipError_t launch_lora_dx_table(int T, int K, int r, float s, const DxTable& tab, uint16_t* dx,
                                 uint16_t* g_out, hipStream_t stream);
 
-// Weight-streaming dX for a few tokens (1 <= T <= 32, r % 8 == 0, r <= 64): split
-// over d_in column blocks and d_out slices, fp32 partials in part_x [S][T][K] and
-// part_g [S][T][r], then one reduce that stores dX and bf16 G.
-bool lora_dx_stream_supported(int64_t T, int r);
-void dx_stream_split(int64_t K, int64_t N, int* splits, int* rows_per_split);
-hipError_t launch_lora_dx_stream(int T, int K, int N, int r, float s, const uint16_t* dy,
+// Split-K weight-streaming dX for up to 128 tokens (r % 8 == 0, r <= 64):
+// workgroups of 128 d_in columns x one of `splits` d_out slices (plus one per slice
+// and 16-wide rank block for G), fp32 partials part_x [splits][T][K] and part_g
+// [splits][T][r], then one reduce that stores dX (if non-null) and bf16 G.
+struct DxSplitPlan {
+  int kcb;              // 128-column blocks of d_in
+  int splits;           // d_out slices (each non-empty)
+  int rows_per_split;   // multiple of 64
+  size_t part_x_bytes, part_g_bytes;
+};
+bool lora_dx_splitk_supported(int64_t T, int r);
+DxSplitPlan plan_dx_splitk(int64_t T, int64_t K, int64_t N, int r);
+hipError_t launch_lora_dx_splitk(int T, int K, int N, int r, float s, const uint16_t* dy,
                                  const uint8_t* codes, const float* absmax, const uint16_t* A,
                                  const uint16_t* B, uint16_t* dx, uint16_t* g_out, float* part_x,
                                  float* part_g, hipStream_t stream);
@@ -139,8 +146,8 @@ hipError_t launch_lora_skinny(int T, int K, int N, int ra, int rb, int vsa, floa
 // workspace-size query so the two always agree.
 struct BwdPlan {
   bool fast;          // 256 x 256 dX kernel and the one-launch rank-r gradients
-  bool stream;        // few tokens: weight-streaming dX (with the fast rank-r gradients)
-  int splits_x;       // d_out slices of the weight-streaming dX
+  bool splitk;        // up to 128 tokens: split-K weight-streaming dX (with the fast rank-r gradients)
+  int splits_x;       // d_out slices of the split-K dX
   int rp;             // r rounded up to the MFMA reduction granularity (32)
   int splits_a;       // token splits of the dA reduction
   int splits_b;       // token splits of the dB reduction
@@ -159,8 +166,8 @@ hipError_t launch_lora_bwd(int T, int K, int N, int r, float s, const uint16_t* 
 // Backward of several projections that share x (dX summed over them). Fused: one
 // dX launch over all projections (G side by side in [T][n r]); for n r <= 64 one
 // pass over x for every dA with the first projection's dB and one pass per further
-// dB, else one pass per projection for its dA and dB. Otherwise (ragged d_out, few
-// tokens) one backward per projection, dX accumulated from a scratch copy.
+// dB, else one pass per projection for its dA and dB. Otherwise (ragged d_out, up
+// to 128 tokens) one backward per projection, dX accumulated from a scratch copy.
 struct BwdMultiPlan {
   bool fused;
   int n, R;                   // projections, n r

@@ -354,8 +354,8 @@ hipError_t launch_bwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
   float* pa = reinterpret_cast<float*>(ws + p.off_pa);
   float* pb = reinterpret_cast<float*>(ws + p.off_pb);
   hipError_t e;
-  if (p.stream) {
-    e = launch_lora_dx_stream(T, K, N, r, s, dy, codes, absmax, A, B, dx, g,
+  if (p.splitk) {
+    e = launch_lora_dx_splitk(T, K, N, r, s, dy, codes, absmax, A, B, dx, g,
                               reinterpret_cast<float*>(ws + p.off_px),
                               reinterpret_cast<float*>(ws + p.off_pg), stream);
   } else if (p.fast) {
@@ -472,15 +472,15 @@ BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r) {
   off = align256(off + static_cast<size_t>(p.splits_a) * K * rs * 4);
   p.off_pb = off;
   off = align256(off + static_cast<size_t>(p.splits_b) * N * rs * 4);
-  p.stream = p.fast && lora_dx_stream_supported(T, r);
+  p.splitk = p.fast && lora_dx_splitk_supported(T, r);
   p.splits_x = 0;
   p.off_px = p.off_pg = off;
-  if (p.stream) {
-    int per = 0;
-    dx_stream_split(K, N, &p.splits_x, &per);
-    off = align256(off + static_cast<size_t>(p.splits_x) * T * K * 4);
+  if (p.splitk) {
+    const DxSplitPlan d = plan_dx_splitk(T, K, N, r);
+    p.splits_x = d.splits;
+    off = align256(off + d.part_x_bytes);
     p.off_pg = off;
-    off = align256(off + static_cast<size_t>(p.splits_x) * T * r * 4);
+    off = align256(off + d.part_g_bytes);
   }
   p.bytes = off;
   return p;
@@ -513,7 +513,8 @@ BwdMultiPlan plan_bwd_multi(int64_t T, int64_t K, int n, const int* N, int r) {
   p.n = n;
   p.R = n * r;
   bool fused = n > 1 && lora_dx_multi_supported(n, N, r) && lora_skinny_supported(r) &&
-               !lora_dx_stream_supported(T, r) && static_cast<int64_t>(T) * p.R * 2 < (int64_t(1) << 31);
+               !lora_dx_splitk_supported(T, r) &&
+               static_cast<int64_t>(T) * p.R * 2 < (int64_t(1) << 31);
   for (int g = 0; g < n && fused; ++g) fused = fits_buffer(T, K, N[g]);
   p.fused = fused;
   size_t off = 0;

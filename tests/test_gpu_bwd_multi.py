@@ -2,11 +2,11 @@
 oracle: dX summed over the projections, dA and dB of each, within the linear's
 tolerance (max|err| / max|ref| <= 1e-2).
 
-Cases cover the fused path (every d_out a multiple of 64, T > 32: one dX
+Cases cover the fused path (every d_out a multiple of 64, T > 128: one dX
 launch over the concatenated d_out; for n r <= 64 one pass over x for every dA,
 wider sums in several epilogue passes and one dA pass per projection) with 2, 3
 and 4 projections and ranks 8 .. 64, ragged token counts and partial d_in
-tiles; and the per-projection path (a d_out not a multiple of 64, few tokens,
+tiles; and the per-projection path (a d_out not a multiple of 64, up to 128 tokens,
 no dX). One case runs the Qwen-14B-shaped q/k/v at full size
 (8192 tokens, 5120 -> 5120 each, r = 16) and checks sampled rows of dX and
 sampled columns of dA and dB against the oracle.
@@ -50,10 +50,11 @@ CASES = [
     (300, 256, (256, 64, 64), 16, True, True),      # fused, q/k/v-like, RE = 48
     (260, 192, (128, 64), 24, False, True),         # fused, r = 24 (two projections), U recomputed
     (257, 320, (64, 64, 128, 64), 16, True, True),  # fused, four projections, RE = 64
-    (100, 128, (64, 192), 8, True, True),           # fused, r = 8
+    (140, 128, (64, 192), 8, True, True),           # fused, r = 8
     (150, 128, (72, 136), 16, True, True),          # d_out % 64 != 0: per projection
     (8, 192, (64, 64, 64), 16, True, True),         # few tokens: per projection (weight streaming)
-    (100, 192, (64, 128), 40, True, True),          # fused, n r = 80 > 64: two epilogue passes, dA per projection
+    (150, 192, (64, 128), 40, True, True),          # fused, n r = 80 > 64: two epilogue passes, dA per projection
+    (100, 256, (128, 64, 64), 16, True, True),      # up to 128 tokens: per projection (split-K dX)
     (260, 256, (128, 64, 64), 64, True, True),      # fused, rank 64 q/k/v-like: n r = 192
     (200, 128, (64, 64, 64), 32, False, True),      # fused, n r = 96, U recomputed
     (300, 256, (256, 64, 64), 16, True, False),     # fused, dX not requested

@@ -87,7 +87,7 @@ def test_odd_shapes(q, T, K, N, r):
 
 # Few tokens (r % 8 == 0, r <= 64): the one-launch weight-streaming forward (T <=
 # 32, d_out <= 4096), the split-K weight-streaming forward (T <= 128 otherwise),
-# and the weight-streaming dX (T <= 32). Cases cover a single half-filled
+# and the split-K weight-streaming dX (T <= 128). Cases cover a single half-filled
 # reduction step (d_in = 64), a half-filled last step (d_in % 128 == 64), d_out
 # not a multiple of the 16- or 64-row block, one, two, four and eight 16-token
 # blocks, one and many d_in splits, and every rank block count.
