@@ -55,6 +55,11 @@ struct SplitKPlan {
   size_t part_bytes, bytes;
 };
 bool lora_fwd_splitk_supported(int64_t T, int r);
+// y = bf16(sum_sp part[sp] + bf16(s sum_sp upart[sp]) B), u_save = bf16(sum_sp upart)
+// (nullable), for part [S][T][N] and upart [S][T][r] fp32, S <= 16.
+hipError_t launch_fwd_splitk_reduce(int T, int N, int r, int S, float s, const float* part,
+                                    const float* upart, const uint16_t* B, uint16_t* y, uint16_t* u_save,
+                                    hipStream_t stream);
 SplitKPlan plan_fwd_splitk(int T, int K, int N, int r);
 hipError_t launch_lora_fwd_splitk(int T, int K, int N, int r, float s, const uint16_t* x,
                                   const uint8_t* codes, const float* absmax, const uint16_t* A,

@@ -25,6 +25,10 @@
 //     owns 32 token rows of U (16 x 16 x 32 MFMAs for r <= 16, else 32 x 32 x 16).
 //   * Epilogue: bf16(s U) and B go through LDS, one more MFMA pass over the rank
 //     dimension adds (s U) B into the accumulators, and bf16 y is stored.
+//   * When even 128 x 128 tiles leave CUs idle (a few hundred tokens over a
+//     narrow d_out), a single projection's K-loop is split across workgroups:
+//     each writes fp32 partial products (and partial U) to a workspace and the
+//     split-K reduce adds bf16(s U) B and stores y.
 //   * Several projections of the same x (q/k/v or gate/up: the multi-projection
 //     fusion) share one launch: the column tiles of all projections form one
 //     grid, each tile reads its projection's weight, A, B and output from a small
@@ -73,10 +77,15 @@ struct ProjTable {
 // LDS (static, so the compiler can prove the direct-to-LDS loads into one stage
 // never alias reads of the other): level table, two stages of x [BT][64],
 // dequantized weight [BT][64] and A^T slice [RU][64], all bf16 and swizzled.
+//
+// Split mode (part != nullptr, one projection): workgroup b runs tile b % tiles
+// over K-steps [steps_per (b / tiles), ...) and writes fp32 partial products to
+// part [split][T][N] and, from the first column tile, fp32 partial U to upart
+// [split][T][r]; no epilogue.
 template <int BT, int RU, int RE>
-__global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) void lora_fwd_kernel(int T, int K, int r, float s,
-                                                                        const uint16_t* __restrict__ x,
-                                                                        const ProjTable tab) {
+__global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) void lora_fwd_kernel(
+    int T, int K, int r, float s, const uint16_t* __restrict__ x, const ProjTable tab, int steps_per,
+    float* __restrict__ part, float* __restrict__ upart) {
   using Tl = FwdTile<BT>;
   constexpr int kThreads = Tl::kThreads, BM = BT, BN = BT, kFM = Tl::kFM, kHalf = BT / 2;
   constexpr int kTileElems = Tl::kTileElems;
@@ -92,8 +101,10 @@ __global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) voi
   const int wm = wave / Tl::kWN, wn = wave % Tl::kWN;  // 2 x kWN waves, BT / 2 x 64 each
   const int l32 = lane & 31, lh = lane >> 5;
   const int mt = (T + BM - 1) / BM, nt_all = tab.tile_end[tab.n - 1];
+  const int tiles = mt * nt_all;
+  const int tile_id = blockIdx.x % tiles, sp = blockIdx.x / tiles;
   int tm, tn;
-  tile_coords(xcd_remap(blockIdx.x, mt * nt_all), mt, nt_all, 4, tm, tn);
+  tile_coords(xcd_remap(tile_id, tiles), mt, nt_all, 4, tm, tn);
   int gp = 0;  // this tile's projection (wave-uniform)
   while (gp + 1 < tab.n && tn >= tab.tile_end[gp]) ++gp;
   if (gp > 0) tn -= tab.tile_end[gp - 1];
@@ -106,6 +117,8 @@ __global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) voi
   uint16_t* __restrict__ u_save = tab.u[gp];
   const int m0 = tm * BM, n0 = tn * BN;
   const int K2 = K / 2, KB = K / BK;
+  const int kbeg = sp * steps_per;                 // first K-step of this workgroup
+  const int nsteps = min(KB - kbeg, steps_per);    // >= 1
 
   if (tid < 16) lut[tid] = nf4_level(tid);
   // A^T slice rows r .. RU-1 stay zero in both stages
@@ -117,11 +130,16 @@ __global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) voi
   // ---- global -> LDS / register staging of one K-step (buffer loads) ------------
   // Buffer resources cover this tile's rows only: loads of rows past T (x) or N
   // (weights) return zeros, and the per-step advance is a uniform scalar offset.
+  // (shifted to the workgroup's first K-step; row strides are unchanged)
   const int rows_x = min(T - m0, BM), rows_w = min(N - n0, BN);
-  const auto rs_x = make_rsrc(x + static_cast<size_t>(m0) * K, static_cast<uint32_t>(rows_x) * K * 2);
-  const auto rs_c = make_rsrc(codes + static_cast<size_t>(n0) * K2, static_cast<uint32_t>(rows_w) * K2);
-  const auto rs_s = make_rsrc(absmax + static_cast<size_t>(n0) * KB, static_cast<uint32_t>(rows_w) * KB * 4);
-  const auto rs_a = make_rsrc(A, static_cast<uint32_t>(K) * r * 2);
+  const auto rs_x = make_rsrc(x + static_cast<size_t>(m0) * K + kbeg * BK,
+                              static_cast<uint32_t>(rows_x) * K * 2 - kbeg * BK * 2);
+  const auto rs_c = make_rsrc(codes + static_cast<size_t>(n0) * K2 + kbeg * 32,
+                              static_cast<uint32_t>(rows_w) * K2 - kbeg * 32);
+  const auto rs_s = make_rsrc(absmax + static_cast<size_t>(n0) * KB + kbeg,
+                              (static_cast<uint32_t>(rows_w) * KB - kbeg) * 4);
+  const auto rs_a = make_rsrc(A + static_cast<size_t>(kbeg) * BK * r,
+                              static_cast<uint32_t>(K - kbeg * BK) * r * 2);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   // x: wave w fills rows 32 w .. 32 w + 31 with four 1 KB direct-to-LDS loads
@@ -361,9 +379,43 @@ __global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) voi
     wait_vmem_upto<2 + kAPer>();
     __syncthreads();
   };
-  for (int kt = 0; kt < KB; kt += 2) {
+  for (int kt = 0; kt < nsteps; kt += 2) {
     kstep(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < KB) kstep(kt + 1, std::integral_constant<int, 1>{});
+    if (kt + 1 < nsteps) kstep(kt + 1, std::integral_constant<int, 1>{});
+  }
+
+  if (part != nullptr) {  // split mode: fp32 partials, no epilogue
+    wait_vmem();          // run-ahead loads land before the workgroup ends
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = n0 + wn * 64 + j * 32 + l32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = m0 + wm * kHalf + blk(i) * 32 + mfma32_row(e, lane);
+          if (row < T && col < N) part[(static_cast<size_t>(sp) * T + row) * N + col] = acc[i][j][e];
+        }
+      }
+    if (tn != 0) return;
+    float* ud = upart + static_cast<size_t>(sp) * T * r;
+#pragma unroll
+    for (int u = 0; u < RU / 32; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm * kHalf + wn * 32 + mfma32_row(e, lane), col = u * 32 + l32;
+        if (col < r && row < T) ud[static_cast<size_t>(row) * r + col] = uacc[u][e];
+      }
+    if constexpr (kU16) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = m0 + wm * kHalf + wn * 32 + rb * 16 + 4 * lq + e;
+          if (l16 < r && row < T) ud[static_cast<size_t>(row) * r + l16] = uacc16[rb][e];
+        }
+    }
+    return;
   }
 
   // ---- epilogue: acc += bf16(s U) B ---------------------------------------------
@@ -432,21 +484,22 @@ __global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) voi
 }
 
 template <int BT, int RU, int RE>
-hipError_t launch_fwd_t(int T, int K, int r, float s, const uint16_t* x, const ProjTable& tab,
-                        hipStream_t stream) {
+hipError_t launch_fwd_t(int T, int K, int r, float s, const uint16_t* x, const ProjTable& tab, int splits,
+                        int steps_per, float* part, float* upart, hipStream_t stream) {
   const int tiles = ((T + BT - 1) / BT) * tab.tile_end[tab.n - 1];
-  lora_fwd_kernel<BT, RU, RE><<<tiles, FwdTile<BT>::kThreads, 0, stream>>>(T, K, r, s, x, tab);
+  lora_fwd_kernel<BT, RU, RE><<<tiles * splits, FwdTile<BT>::kThreads, 0, stream>>>(T, K, r, s, x, tab,
+                                                                                   steps_per, part, upart);
   return hipGetLastError();
 }
 
 template <int BT>
-hipError_t launch_fwd_rank(int T, int K, int r, float s, const uint16_t* x, const ProjTable& tab,
-                           hipStream_t stream) {
+hipError_t launch_fwd_rank(int T, int K, int r, float s, const uint16_t* x, const ProjTable& tab, int splits,
+                           int steps_per, float* part, float* upart, hipStream_t stream) {
   switch ((r + 15) / 16) {
-    case 1: return launch_fwd_t<BT, 16, 16>(T, K, r, s, x, tab, stream);
-    case 2: return launch_fwd_t<BT, 32, 32>(T, K, r, s, x, tab, stream);
-    case 3: return launch_fwd_t<BT, 64, 48>(T, K, r, s, x, tab, stream);
-    default: return launch_fwd_t<BT, 64, 64>(T, K, r, s, x, tab, stream);
+    case 1: return launch_fwd_t<BT, 16, 16>(T, K, r, s, x, tab, splits, steps_per, part, upart, stream);
+    case 2: return launch_fwd_t<BT, 32, 32>(T, K, r, s, x, tab, splits, steps_per, part, upart, stream);
+    case 3: return launch_fwd_t<BT, 64, 48>(T, K, r, s, x, tab, splits, steps_per, part, upart, stream);
+    default: return launch_fwd_t<BT, 64, 64>(T, K, r, s, x, tab, splits, steps_per, part, upart, stream);
   }
 }
 
@@ -464,9 +517,44 @@ int fwd_tile_edge(int64_t T, int cols256, int cols128, int r) {
   return small ? 128 : 256;
 }
 
+// K-splits of the tiled forward of one projection. The split costs a pass over
+// S T N fp32 partials plus the reduce's rereads of B, so it pays where the tile
+// grid leaves most resident slots idle (128 x 128 tiles: two per CU at rank <=
+// 32): filling at most 32 % of them, or 50 % when the main loop dominates (rank
+// > 32, or d_in >= 16384). Measured on MI355X at 160 .. 2048 tokens over q_proj,
+// Qwen-14B, the 70B gate and down and k/v shapes, the rule splits exactly where
+// splitting was faster. S fills the slots, at most four
+// ways and at least eight 64-element steps per split (1 = no split).
+struct TiledSplit {
+  int bt, splits, steps_per;
+};
+TiledSplit tiled_split(int64_t T, int64_t K, int64_t N, int r) {
+  TiledSplit p{};
+  p.bt = fwd_tile_edge(T, static_cast<int>((N + 255) / 256), static_cast<int>((N + 127) / 128), r);
+  const int64_t tiles = (T + p.bt - 1) / p.bt * ((N + p.bt - 1) / p.bt);
+  const int64_t slots = 256 * (p.bt == 128 && r <= 32 ? 2 : 1);
+  const int KB = static_cast<int>(K / BK);
+  const bool long_main = r > 32 || K >= 16384;
+  const bool idle = 100 * tiles <= 32 * slots || (long_main && 2 * tiles <= slots);
+  int S = static_cast<int>(slots / tiles);
+  S = S > 4 ? 4 : S;
+  S = S > KB / 8 ? KB / 8 : S;
+  S = idle && S >= 2 ? S : 1;
+  p.steps_per = (KB + S - 1) / S;
+  p.splits = (KB + p.steps_per - 1) / p.steps_per;  // every split non-empty
+  return p;
+}
+
+size_t tiled_split_bytes(int64_t T, int64_t N, int r, int splits) {
+  if (splits <= 1) return 0;
+  const size_t a = (static_cast<size_t>(splits) * T * N * 4 + 255) & ~static_cast<size_t>(255);
+  return a + ((static_cast<size_t>(splits) * T * r * 4 + 255) & ~static_cast<size_t>(255));
+}
+
 // tab.N and the pointers are set; the column-tile prefix sums follow the tile edge.
+// A single projection whose tile grid leaves CUs idle runs split (workspace).
 hipError_t launch_fwd_table(int T, int K, int r, float s, const uint16_t* x, ProjTable& tab,
-                            hipStream_t stream) {
+                            void* workspace, hipStream_t stream) {
   int cols256 = 0, cols128 = 0;
   for (int g = 0; g < tab.n; ++g) {
     cols256 += (tab.N[g] + 255) / 256;
@@ -478,8 +566,19 @@ hipError_t launch_fwd_table(int T, int K, int r, float s, const uint16_t* x, Pro
     tiles += (tab.N[g] + bt - 1) / bt;
     tab.tile_end[g] = tiles;
   }
-  if (bt == 256) return launch_fwd_rank<256>(T, K, r, s, x, tab, stream);
-  return launch_fwd_rank<128>(T, K, r, s, x, tab, stream);
+  TiledSplit sp{bt, 1, K / BK};
+  if (tab.n == 1 && workspace != nullptr) sp = tiled_split(T, K, tab.N[0], r);
+  float* part = nullptr;
+  float* upart = nullptr;
+  if (sp.splits > 1) {
+    part = static_cast<float*>(workspace);
+    upart = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                     ((static_cast<size_t>(sp.splits) * T * tab.N[0] * 4 + 255) & ~static_cast<size_t>(255)));
+  }
+  const hipError_t e = bt == 256 ? launch_fwd_rank<256>(T, K, r, s, x, tab, sp.splits, sp.steps_per, part, upart, stream)
+                                 : launch_fwd_rank<128>(T, K, r, s, x, tab, sp.splits, sp.steps_per, part, upart, stream);
+  if (e != hipSuccess || sp.splits <= 1) return e;
+  return launch_fwd_splitk_reduce(T, tab.N[0], r, sp.splits, s, part, upart, tab.B[0], tab.y[0], tab.u[0], stream);
 }
 
 }  // namespace
@@ -493,17 +592,23 @@ bool fwd_uses_splitk(int64_t T, int64_t K, int64_t N, int r) {
   if (r % 8 != 0 || r > 64 || !fits_buffer(T, K, N) || !lora_fwd_splitk_supported(T, r)) return false;
   return !(lora_fwd_stream_supported(T, r) && (N + 15) / 16 <= 256);
 }
+// One launch for several projections unless one of them would run a path of its
+// own (few tokens, or a K-split tiled forward): the fused launch then gives the
+// same values as separate calls, in the same summation order.
 bool fwd_multi_tiled(int64_t T, int64_t K, int n_proj, const int* N, int r) {
   bool tiled = r % 8 == 0 && r <= 64 && n_proj <= kMaxProj && !lora_fwd_stream_supported(T, r);
-  for (int g = 0; g < n_proj; ++g) tiled = tiled && fits_buffer(T, K, N[g]) && !fwd_uses_splitk(T, K, N[g], r);
+  for (int g = 0; g < n_proj; ++g)
+    tiled = tiled && fits_buffer(T, K, N[g]) && !fwd_uses_splitk(T, K, N[g], r) &&
+            tiled_split(T, K, N[g], r).splits == 1;
   return tiled;
 }
 }  // namespace
 
 size_t fwd_workspace_bytes(int64_t T, int64_t K, int64_t N, int r) {
-  return fwd_uses_splitk(T, K, N, r) ? plan_fwd_splitk(static_cast<int>(T), static_cast<int>(K),
-                                                       static_cast<int>(N), r).bytes
-                                     : 0;
+  if (fwd_uses_splitk(T, K, N, r))
+    return plan_fwd_splitk(static_cast<int>(T), static_cast<int>(K), static_cast<int>(N), r).bytes;
+  if (r % 8 != 0 || r > 64 || !fits_buffer(T, K, N) || lora_fwd_stream_supported(T, r)) return 0;
+  return tiled_split_bytes(T, N, r, tiled_split(T, K, N, r).splits);
 }
 
 size_t fwd_multi_workspace_bytes(int64_t T, int64_t K, int n_proj, const int* N, int r) {
@@ -535,7 +640,7 @@ hipError_t launch_lora_fwd(int T, int K, int N, int r, float s, const uint16_t* 
   tab.B[0] = B;
   tab.y[0] = y;
   tab.u[0] = u_save;
-  return launch_fwd_table(T, K, r, s, x, tab, stream);
+  return launch_fwd_table(T, K, r, s, x, tab, workspace, stream);
 }
 
 hipError_t launch_lora_fwd_multi(int T, int K, int n_proj, const int* N, int r, float s,
@@ -562,7 +667,7 @@ hipError_t launch_lora_fwd_multi(int T, int K, int n_proj, const int* N, int r, 
     tab.y[g] = y[g];
     tab.u[g] = u_save == nullptr ? nullptr : u_save[g];
   }
-  return launch_fwd_table(T, K, r, s, x, tab, stream);
+  return launch_fwd_table(T, K, r, s, x, tab, nullptr, stream);
 }
 
 }  // namespace lnf4

@@ -393,8 +393,14 @@ hipError_t launch_lora_fwd_splitk(int T, int K, int N, int r, float s, const uin
   else if (T <= 64) e = launch_splitk_t<4>(T, K, N, r, p, x, codes, absmax, A, part, upart, stream);
   else e = launch_splitk_t<8>(T, K, N, r, p, x, codes, absmax, A, part, upart, stream);
   if (e != hipSuccess) return e;
+  return launch_fwd_splitk_reduce(T, N, r, p.splits, s, part, upart, B, y, u_save, stream);
+}
+
+hipError_t launch_fwd_splitk_reduce(int T, int N, int r, int S, float s, const float* part,
+                                    const float* upart, const uint16_t* B, uint16_t* y, uint16_t* u_save,
+                                    hipStream_t stream) {
   const dim3 grid((N + kRCols - 1) / kRCols, (T + kRRows - 1) / kRRows);
-  lora_fwd_splitk_reduce<<<grid, kRThreads, 0, stream>>>(T, N, r, p.splits, s, part, upart, B, y, u_save);
+  lora_fwd_splitk_reduce<<<grid, kRThreads, 0, stream>>>(T, N, r, S, s, part, upart, B, y, u_save);
   return hipGetLastError();
 }
 

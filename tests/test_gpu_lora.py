@@ -73,10 +73,11 @@ def test_tiny_workload(q):
 
 
 # (T, d_in, d_out, r): ragged token counts, partial tiles in every dimension,
-# ranks from 1 to the maximum.
+# ranks from 1 to the maximum; the last two split the tiled forward's K-loop
+# (few tiles, d_in >= 1024).
 ODD = [(1, 64, 64, 1), (63, 128, 192, 8), (65, 192, 64, 16), (200, 320, 136, 64),
        (130, 256, 8, 128), (257, 64, 520, 24), (129, 384, 264, 17), (17, 640, 1000, 40),
-       (260, 192, 296, 48)]
+       (260, 192, 296, 48), (300, 2048, 200, 16), (200, 1536, 136, 64)]
 
 
 @pytest.mark.parametrize("T,K,N,r", ODD)
@@ -228,7 +229,8 @@ def test_operand_beyond_two_gib(q):
     assert olora.rel_err(host_f64(dB), dB_ref) <= TOL
 
 
-@pytest.mark.parametrize("T,K,N,r", [(131, 192, 200, 12), (7, 320, 72, 24), (100, 448, 200, 16)])
+@pytest.mark.parametrize("T,K,N,r", [(131, 192, 200, 12), (7, 320, 72, 24), (100, 448, 200, 16),
+                                     (260, 1024, 136, 16)])
 def test_guard_bands_untouched(q, T, K, N, r):
     """Outputs written through the C ABI stay inside their buffers."""
     from tests.gpu_util import Guarded, dev_bf16
@@ -297,10 +299,10 @@ def test_full_size_sampled(q, wi, pi):
 
 # Multi-projection forward: the same values as one lora_nf4_fwd per projection
 # (bitwise: each output tile runs the same kernel code on the same data), on the
-# tiled path (one launch), the few-token paths (one workspace shared by the
-# projections in turn on the split-K path) and the generic path.
+# tiled path (one launch), the few-token paths and the K-split tiled forward
+# (one workspace shared by the projections in turn) and the generic path.
 MULTI = [(300, 256, (256, 64, 64), 16), (200, 320, (200, 40, 8), 24), (8, 192, (64, 16, 16), 16),
-         (150, 128, (72, 136), 12), (100, 256, (128, 64, 64), 16)]
+         (150, 128, (72, 136), 12), (100, 256, (128, 64, 64), 16), (300, 2048, (256, 64, 64), 16)]
 
 
 @pytest.mark.parametrize("T,K,Ns,r", MULTI)
