@@ -98,9 +98,10 @@ int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows, int6
  *   workspace  device scratch of at least lora_nf4_fwd_workspace_bytes(T, d_in,
  *            d_out, r) bytes, 256-byte aligned, owned by the caller (contents on
  *            entry do not matter, on return unspecified; concurrent calls need
- *            separate workspaces). That size is non-zero only for few tokens
- *            (T <= 128 at r % 8 == 0, r <= 64), where the reduction over d_in is
- *            split across workgroups and fp32 partial sums meet in the workspace;
+ *            separate workspaces). That size is non-zero only where the
+ *            reduction over d_in is split across workgroups and fp32 partial sums
+ *            meet in the workspace: few tokens (T <= 128 at r % 8 == 0, r <= 64),
+ *            and token counts whose output tiles leave most of the GPU idle;
  *            when it is 0 the workspace may be NULL.
  * T >= 0, d_in % 64 == 0, d_out % 8 == 0, 1 <= r <= LN_MAX_RANK. s = lora_alpha / r
  * is formed in float32 on the host. T = 0 is an empty batch: nothing is computed

@@ -78,12 +78,19 @@ hipError_t launch_lora_merge(int K, int N, int r, float s, const uint8_t* codes,
                              const uint16_t* A, const uint16_t* B, bool out_bf16, void* out,
                              hipStream_t stream);
 
-// dX kernel for ranks r % 8 == 0, r <= 64 (256 x 256 tiles); also writes bf16
-// G = s dY B^T [T, r] to g_out.
+// dX kernel for ranks r % 8 == 0, r <= 64 (256 x 256 or 128 x 128 tiles); also
+// writes bf16 G = s dY B^T [T, r] to g_out. With part_x / part_g (sized by
+// dx_tiled_split: [splits][T][K] and [splits][T][r] fp32) a small tile grid splits
+// its reduction over d_out and the split-K dX reduce finishes; null: no split.
 bool lora_dx_supported(int r);
+struct DxTiledSplit {
+  int splits, steps_per;
+};
+DxTiledSplit dx_tiled_split(int64_t T, int64_t K, int64_t N, int r);
 hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* dy,
                           const uint8_t* codes, const float* absmax, const uint16_t* A,
-                          const uint16_t* B, uint16_t* dx, uint16_t* g_out, hipStream_t stream);
+                          const uint16_t* B, uint16_t* dx, uint16_t* g_out, float* part_x, float* part_g,
+                          hipStream_t stream);
 
 // The dX kernel over a table of projections that share x: the reduction runs over
 // their concatenated d_out (step_end[g] = 64-wide steps of projections 0..g) and
@@ -117,6 +124,11 @@ struct DxSplitPlan {
 };
 bool lora_dx_splitk_supported(int64_t T, int r);
 DxSplitPlan plan_dx_splitk(int64_t T, int64_t K, int64_t N, int r);
+// dX = sum_sp part_x[sp] + bf16(G) A^T, G = s sum_sp part_g[sp]; g_out = bf16(G);
+// S <= 16; dx may be null (G only).
+hipError_t launch_dx_splitk_reduce(int T, int K, int r, int S, float s, const float* part_x,
+                                   const float* part_g, const uint16_t* A, uint16_t* dx, uint16_t* g_out,
+                                   hipStream_t stream);
 hipError_t launch_lora_dx_splitk(int T, int K, int N, int r, float s, const uint16_t* dy,
                                  const uint8_t* codes, const float* absmax, const uint16_t* A,
                                  const uint16_t* B, uint16_t* dx, uint16_t* g_out, float* part_x,

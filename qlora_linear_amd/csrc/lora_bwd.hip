@@ -359,7 +359,10 @@ hipError_t launch_bwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
                               reinterpret_cast<float*>(ws + p.off_px),
                               reinterpret_cast<float*>(ws + p.off_pg), stream);
   } else if (p.fast) {
-    e = launch_lora_dx(T, K, N, r, s, dy, codes, absmax, A, B, dx, g, stream);
+    const bool split = p.splits_x > 1;
+    e = launch_lora_dx(T, K, N, r, s, dy, codes, absmax, A, B, dx, g,
+                       split ? reinterpret_cast<float*>(ws + p.off_px) : nullptr,
+                       split ? reinterpret_cast<float*>(ws + p.off_pg) : nullptr, stream);
   } else {
     constexpr int BM = 128, BN = 128;
     const int tiles = ((T + BM - 1) / BM) * ((K + BN - 1) / BN);
@@ -481,6 +484,14 @@ BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r) {
     off = align256(off + d.part_x_bytes);
     p.off_pg = off;
     off = align256(off + d.part_g_bytes);
+  } else if (p.fast) {  // tiled dX, split over d_out when its tile grid is small
+    const DxTiledSplit d = dx_tiled_split(T, K, N, r);
+    if (d.splits > 1) {
+      p.splits_x = d.splits;
+      off = align256(off + static_cast<size_t>(d.splits) * T * K * 4);
+      p.off_pg = off;
+      off = align256(off + static_cast<size_t>(d.splits) * T * r * 4);
+    }
   }
   p.bytes = off;
   return p;

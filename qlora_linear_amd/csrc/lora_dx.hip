@@ -56,10 +56,14 @@ struct DxTile {
   static constexpr int kMinBlocks = BT == 128 ? 2 : 1;
 };
 
+// Split mode (part_x != nullptr, one projection): workgroup b runs tile b % tiles
+// over d_out steps [steps_per (b / tiles), ...) and writes fp32 partial dX to
+// part_x [split][T][K] and, from the first column tile, fp32 partial dY B^T to
+// part_g [split][T][r]; no epilogue.
 template <int BT, int RU, int RE, bool MULTI>
 __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void lora_dx_kernel(
     int T, int K, int r, float s, const DxTable tab, uint16_t* __restrict__ dx,
-    uint16_t* __restrict__ g_out) {
+    uint16_t* __restrict__ g_out, int steps_per, float* __restrict__ part_x, float* __restrict__ part_g) {
   using Tl = DxTile<BT>;
   constexpr int kThreads = Tl::kThreads, BM = BT, BN = BT, kFM = Tl::kFM, kHalf = BT / 2;
   constexpr int kTileElems = Tl::kTileElems, kDStride = Tl::kDStride, kDElems = Tl::kDElems;
@@ -75,11 +79,15 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
   const int wm = wave / Tl::kWN, wn = wave % Tl::kWN;  // 2 x kWN waves, BT / 2 x 64 each
   const int l32 = lane & 31, lh = lane >> 5;
   const int mt = (T + BM - 1) / BM, kt_tiles = (K + BN - 1) / BN;
+  const int tiles = mt * kt_tiles;
+  const int tile_id = blockIdx.x % tiles, sp = blockIdx.x / tiles;
   int tm, tk;
-  tile_coords(xcd_remap(blockIdx.x, mt * kt_tiles), mt, kt_tiles, 4, tm, tk);
+  tile_coords(xcd_remap(tile_id, tiles), mt, kt_tiles, 4, tm, tk);
   const int m0 = tm * BM, k0 = tk * BN;
   const int K2 = K / 2, KB = K / 64;
-  const int NS = tab.step_end[tab.n - 1];  // reduction steps over all d_out
+  const int NS_all = tab.step_end[tab.n - 1];  // reduction steps over all d_out
+  const int sbeg = sp * steps_per;              // this workgroup's first step (0 unless split)
+  const int NS = min(NS_all, sbeg + steps_per);  // one past its last step
   constexpr bool multi = MULTI;
   const int R = tab.n * r;  // g_out row length
 
@@ -240,8 +248,8 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
     for (int e = 0; e < 16; ++e) gacc[u][e] = 0.f;
 
   // prologue: step 0 into stage 0, step 1 into registers
-  load_y_lds(0, ys0);
-  load_regs(0, 0);
+  load_y_lds(sbeg, ys0);
+  load_regs(sbeg, 0);
   wait_vmem();
   __syncthreads();  // lut and dY of step 0 visible
   {
@@ -254,7 +262,7 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
     }
     store_b(bs0, breg[0]);
   }
-  load_regs(1, 1);
+  load_regs(sbeg + 1, 1);
   __syncthreads();
 
   struct Frag {
@@ -357,13 +365,47 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
     ++gseg;
     if (gseg < tab.n) gend = tab.step_end[gseg];
   };
-  for (int st = 0; st < NS; st += 2) {
+  for (int st = sbeg; st < NS; st += 2) {
     kstep(st, std::integral_constant<int, 0>{});
     flush(st);
     if (st + 1 < NS) {
       kstep(st + 1, std::integral_constant<int, 1>{});
       flush(st + 1);
     }
+  }
+
+  if (part_x != nullptr) {  // split mode: fp32 partials, no epilogue
+    wait_vmem();            // run-ahead loads land before the workgroup ends
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = k0 + wn * 64 + j * 32 + l32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = m0 + wm * kHalf + i * 32 + mfma32_row(e, lane);
+          if (row < T && col < K) part_x[(static_cast<size_t>(sp) * T + row) * K + col] = acc[i][j][e];
+        }
+      }
+    if (tk != 0) return;
+    float* gd = part_g + static_cast<size_t>(sp) * T * r;
+#pragma unroll
+    for (int u = 0; u < RU / 32; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm * kHalf + wn * 32 + mfma32_row(e, lane), col = u * 32 + l32;
+        if (col < r && row < T) gd[static_cast<size_t>(row) * r + col] = gacc[u][e];
+      }
+    if constexpr (kG16) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = m0 + wm * kHalf + wn * 32 + rb * 16 + 4 * lq + e;
+          if (l16 < r && row < T) gd[static_cast<size_t>(row) * r + l16] = gacc16[rb][e];
+        }
+    }
+    return;
   }
 
   // ---- epilogue: acc += bf16(G) A^T ----------------------------------------------
@@ -459,24 +501,32 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
     }
 }
 
+// Dispatch arguments: split mode when part_x != nullptr (single projection).
+struct DxSplitArgs {
+  int splits, steps_per;
+  float* part_x;
+  float* part_g;
+};
+
 template <int BT, int RU, int RE, bool MULTI>
 hipError_t launch_dx_t(int T, int K, int r, float s, const DxTable& tab, uint16_t* dx, uint16_t* g_out,
-                       hipStream_t stream) {
+                       const DxSplitArgs& a, hipStream_t stream) {
   const int tiles = ((T + BT - 1) / BT) * ((K + BT - 1) / BT);
-  lora_dx_kernel<BT, RU, RE, MULTI><<<tiles, DxTile<BT>::kThreads, 0, stream>>>(T, K, r, s, tab, dx, g_out);
+  lora_dx_kernel<BT, RU, RE, MULTI><<<tiles * a.splits, DxTile<BT>::kThreads, 0, stream>>>(
+      T, K, r, s, tab, dx, g_out, a.steps_per, a.part_x, a.part_g);
   return hipGetLastError();
 }
 
 template <int BT>
 hipError_t launch_dx_rank(int T, int K, int r, float s, const DxTable& tab, uint16_t* dx, uint16_t* g_out,
-                          hipStream_t stream) {
+                          const DxSplitArgs& a, hipStream_t stream) {
   const int R = tab.n * r;
   if (tab.n == 1) {
     switch ((r + 15) / 16) {
-      case 1: return launch_dx_t<BT, 16, 16, false>(T, K, r, s, tab, dx, g_out, stream);
-      case 2: return launch_dx_t<BT, 32, 32, false>(T, K, r, s, tab, dx, g_out, stream);
-      case 3: return launch_dx_t<BT, 64, 48, false>(T, K, r, s, tab, dx, g_out, stream);
-      case 4: return launch_dx_t<BT, 64, 64, false>(T, K, r, s, tab, dx, g_out, stream);
+      case 1: return launch_dx_t<BT, 16, 16, false>(T, K, r, s, tab, dx, g_out, a, stream);
+      case 2: return launch_dx_t<BT, 32, 32, false>(T, K, r, s, tab, dx, g_out, a, stream);
+      case 3: return launch_dx_t<BT, 64, 48, false>(T, K, r, s, tab, dx, g_out, a, stream);
+      case 4: return launch_dx_t<BT, 64, 64, false>(T, K, r, s, tab, dx, g_out, a, stream);
       default: return hipErrorInvalidValue;
     }
   }
@@ -484,17 +534,17 @@ hipError_t launch_dx_rank(int T, int K, int r, float s, const DxTable& tab, uint
   const int RE = R >= 64 ? 64 : ((R + 15) / 16) * 16;
   if (r <= 16) {
     switch (RE) {
-      case 16: return launch_dx_t<BT, 16, 16, true>(T, K, r, s, tab, dx, g_out, stream);
-      case 32: return launch_dx_t<BT, 16, 32, true>(T, K, r, s, tab, dx, g_out, stream);
-      case 48: return launch_dx_t<BT, 16, 48, true>(T, K, r, s, tab, dx, g_out, stream);
-      default: return launch_dx_t<BT, 16, 64, true>(T, K, r, s, tab, dx, g_out, stream);
+      case 16: return launch_dx_t<BT, 16, 16, true>(T, K, r, s, tab, dx, g_out, a, stream);
+      case 32: return launch_dx_t<BT, 16, 32, true>(T, K, r, s, tab, dx, g_out, a, stream);
+      case 48: return launch_dx_t<BT, 16, 48, true>(T, K, r, s, tab, dx, g_out, a, stream);
+      default: return launch_dx_t<BT, 16, 64, true>(T, K, r, s, tab, dx, g_out, a, stream);
     }
   }
   if (r <= 32) {
-    if (RE == 48) return launch_dx_t<BT, 32, 48, true>(T, K, r, s, tab, dx, g_out, stream);
-    return launch_dx_t<BT, 32, 64, true>(T, K, r, s, tab, dx, g_out, stream);
+    if (RE == 48) return launch_dx_t<BT, 32, 48, true>(T, K, r, s, tab, dx, g_out, a, stream);
+    return launch_dx_t<BT, 32, 64, true>(T, K, r, s, tab, dx, g_out, a, stream);
   }
-  return launch_dx_t<BT, 64, 64, true>(T, K, r, s, tab, dx, g_out, stream);
+  return launch_dx_t<BT, 64, 64, true>(T, K, r, s, tab, dx, g_out, a, stream);
 }
 
 // Tile edge from a round count: 256 x 256 tiles run one per CU; 128 x 128 tiles
@@ -525,13 +575,38 @@ bool lora_dx_multi_supported(int n_proj, const int* N, int r) {
 
 hipError_t launch_lora_dx_table(int T, int K, int r, float s, const DxTable& tab, uint16_t* dx,
                                 uint16_t* g_out, hipStream_t stream) {
-  if (dx_tile_edge(T, K, r) == 256) return launch_dx_rank<256>(T, K, r, s, tab, dx, g_out, stream);
-  return launch_dx_rank<128>(T, K, r, s, tab, dx, g_out, stream);
+  const DxSplitArgs a{1, tab.step_end[tab.n - 1], nullptr, nullptr};
+  if (dx_tile_edge(T, K, r) == 256) return launch_dx_rank<256>(T, K, r, s, tab, dx, g_out, a, stream);
+  return launch_dx_rank<128>(T, K, r, s, tab, dx, g_out, a, stream);
+}
+
+// d_out splits of the tiled dX of one projection: the rule of the tiled forward's
+// K-split with d_out as the reduction (slots: 128 x 128 tiles two per CU at rank
+// <= 16), at most four ways and at least sixteen 64-row steps per split (a shorter
+// d_out does not pay for the fp32 partials). A half-idle grid splits only for a long
+// d_out, or at rank > 32 while strictly under half the slots (measured: 4096-wide
+// dX at rank 64 and 128 tiles is slower split).
+DxTiledSplit dx_tiled_split(int64_t T, int64_t K, int64_t N, int r) {
+  DxTiledSplit p{};
+  const int bt = dx_tile_edge(T, K, r);
+  const int64_t tiles = (T + bt - 1) / bt * ((K + bt - 1) / bt);
+  const int64_t slots = 256 * (bt == 128 && r <= 16 ? 2 : 1);
+  const int NS = static_cast<int>((N + BK - 1) / BK);
+  const bool half_idle = N >= 16384 ? 2 * tiles <= slots : r > 32 && 2 * tiles < slots;
+  const bool idle = 100 * tiles <= 32 * slots || half_idle;
+  int S = static_cast<int>(slots / tiles);
+  S = S > 4 ? 4 : S;
+  S = S > NS / 16 ? NS / 16 : S;
+  S = idle && S >= 2 ? S : 1;
+  p.steps_per = (NS + S - 1) / S;
+  p.splits = (NS + p.steps_per - 1) / p.steps_per;  // every split non-empty
+  return p;
 }
 
 hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* dy,
                           const uint8_t* codes, const float* absmax, const uint16_t* A,
-                          const uint16_t* B, uint16_t* dx, uint16_t* g_out, hipStream_t stream) {
+                          const uint16_t* B, uint16_t* dx, uint16_t* g_out, float* part_x, float* part_g,
+                          hipStream_t stream) {
   DxTable tab{};
   tab.n = 1;
   tab.step_end[0] = (N + BK - 1) / BK;
@@ -541,7 +616,13 @@ hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* d
   tab.absmax[0] = absmax;
   tab.A[0] = A;
   tab.B[0] = B;
-  return launch_lora_dx_table(T, K, r, s, tab, dx, g_out, stream);
+  const DxTiledSplit sp = part_x != nullptr ? dx_tiled_split(T, K, N, r) : DxTiledSplit{1, tab.step_end[0]};
+  if (sp.splits <= 1) return launch_lora_dx_table(T, K, r, s, tab, dx, g_out, stream);
+  const DxSplitArgs a{sp.splits, sp.steps_per, part_x, part_g};
+  const hipError_t e = dx_tile_edge(T, K, r) == 256 ? launch_dx_rank<256>(T, K, r, s, tab, dx, g_out, a, stream)
+                                                    : launch_dx_rank<128>(T, K, r, s, tab, dx, g_out, a, stream);
+  if (e != hipSuccess) return e;
+  return launch_dx_splitk_reduce(T, K, r, sp.splits, s, part_x, part_g, A, dx, g_out, stream);
 }
 
 }  // namespace lnf4

@@ -408,8 +408,14 @@ hipError_t launch_lora_dx_splitk(int T, int K, int N, int r, float s, const uint
   else if (T <= 64) e = launch_dx_splitk_t<4>(T, K, N, r, p, dy, codes, absmax, B, part_x, part_g, stream);
   else e = launch_dx_splitk_t<8>(T, K, N, r, p, dy, codes, absmax, B, part_x, part_g, stream);
   if (e != hipSuccess) return e;
+  return launch_dx_splitk_reduce(T, K, r, p.splits, s, part_x, part_g, A, dx, g_out, stream);
+}
+
+hipError_t launch_dx_splitk_reduce(int T, int K, int r, int S, float s, const float* part_x,
+                                   const float* part_g, const uint16_t* A, uint16_t* dx, uint16_t* g_out,
+                                   hipStream_t stream) {
   const dim3 grid((K + kRCols - 1) / kRCols, (T + kRRows - 1) / kRRows);
-  lora_dx_splitk_reduce<<<grid, kRThreads, 0, stream>>>(T, K, r, p.splits, s, part_x, part_g, A, dx, g_out);
+  lora_dx_splitk_reduce<<<grid, kRThreads, 0, stream>>>(T, K, r, S, s, part_x, part_g, A, dx, g_out);
   return hipGetLastError();
 }
 

@@ -73,11 +73,13 @@ def test_tiny_workload(q):
 
 
 # (T, d_in, d_out, r): ragged token counts, partial tiles in every dimension,
-# ranks from 1 to the maximum; the last two split the tiled forward's K-loop
-# (few tiles, d_in >= 1024).
+# ranks from 1 to the maximum; the last four split the reduction of the tiled
+# kernels across workgroups: the forward's over d_in (few tiles, d_in >= 1024),
+# then dX's over d_out (few tiles, d_out >= 2048).
 ODD = [(1, 64, 64, 1), (63, 128, 192, 8), (65, 192, 64, 16), (200, 320, 136, 64),
        (130, 256, 8, 128), (257, 64, 520, 24), (129, 384, 264, 17), (17, 640, 1000, 40),
-       (260, 192, 296, 48), (300, 2048, 200, 16), (200, 1536, 136, 64)]
+       (260, 192, 296, 48), (300, 2048, 200, 16), (200, 1536, 136, 64), (300, 256, 2048, 16),
+       (200, 192, 2056, 64)]
 
 
 @pytest.mark.parametrize("T,K,N,r", ODD)
