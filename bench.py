@@ -46,7 +46,8 @@ METRIC = "fused NF4-LoRA linear fwd+bwd TFLOP/s & tokens/s, % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 bf16 FLOP/clk x 2.4 GHz (published: 2.5 PFLOP/s dense)
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_lora_fwd_kernel_llama3-8b-q_proj.json")
-FWD_SOURCES = ("qlora_linear_amd/csrc/lora_fwd.hip", "qlora_linear_amd/csrc/device_common.h")
+FWD_SOURCES = ("qlora_linear_amd/csrc/lora_fwd.hip", "qlora_linear_amd/csrc/nf4_quant.hip",
+               "qlora_linear_amd/csrc/device_common.h")
 
 
 def parse():
@@ -100,49 +101,71 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def counter_means(d: str, counter: str) -> dict:
-    """Mean per-dispatch value of `counter` per kernel name from a rocprofv3 csv run."""
+def counter_dispatches(d: str, counter: str) -> list:
+    """(dispatch id, kernel name, value summed over XCDs) of `counter` from a rocprofv3 csv run,
+    in dispatch order."""
     import csv
     import glob
     import collections
-    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    per = collections.defaultdict(float)
+    names = {}
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] == counter:
-                per[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
-    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+                did = int(r["Dispatch_Id"])
+                per[did] += float(r["Counter_Value"])
+                names[did] = r["Kernel_Name"]
+    return [(did, names[did], per[did]) for did in sorted(per)]
+
+
+def forward_kib(disp: list) -> tuple:
+    """Mean counter value (KiB) per forward call and per other kernel. From 1024 tokens a
+    forward call is two launches, the weight's dequantization and the tile kernel
+    (lora_fwd_kernel); the tile kernel also runs the backward's input gradient, after
+    the transposed dequantization, and counts there as dX."""
+    import collections
+    fwd, other = [], collections.defaultdict(list)
+    prev = None
+    for _, name, v in disp:
+        if "lora_fwd_kernel" in name:
+            if prev is not None and "nf4_dequantize_t_kernel" in prev[0]:
+                other["lora_dx (nf4_dequantize_t_kernel + lora_fwd_kernel)"].append(prev[1] + v)
+            elif prev is not None and "nf4_dequantize_kernel" in prev[0]:
+                fwd.append(prev[1] + v)
+            else:
+                fwd.append(v)
+        elif "nf4_dequantize" not in name:
+            for key in ("lora_dx_kernel", "skinny_partial_kernel", "skinny_reduce2_kernel", "MulFunctor"):
+                if key in name:
+                    other[key].append(v)
+        prev = (name, v)
+    if not fwd:
+        raise SystemExit("no dispatch of lora_fwd_kernel in the counter data")
+    return sum(fwd) / len(fwd), {k: sum(v) / len(v) for k, v in other.items()}
 
 
 def ingest_counters(fetch_dir: str, write_dir: str):
-    fetch = counter_means(fetch_dir, "FETCH_SIZE")
-    write = counter_means(write_dir, "WRITE_SIZE")
-
-    def pick(tbl, key):
-        hits = [v for k, v in tbl.items() if key in k]
-        if not hits:
-            raise SystemExit(f"no dispatch of {key} in the counter data")
-        return hits[0]
-
+    fetch_fwd, fetch_other = forward_kib(counter_dispatches(fetch_dir, "FETCH_SIZE"))
+    write_fwd, write_other = forward_kib(counter_dispatches(write_dir, "WRITE_SIZE"))
     copy_key = "MulFunctor"  # the calibration copy: torch.mul(src, 1.0, out=dst)
-    cal_f = (COPY_BYTES / 1024) / pick(fetch, copy_key)
-    cal_w = (COPY_BYTES / 1024) / pick(write, copy_key)
-    rec = {"kernel": "lora_fwd_kernel", "workload": "llama3-8b-q_proj",
+    if copy_key not in fetch_other or copy_key not in write_other:
+        raise SystemExit("no dispatch of the calibration copy in the counter data")
+    cal_f = (COPY_BYTES / 1024) / fetch_other[copy_key]
+    cal_w = (COPY_BYTES / 1024) / write_other[copy_key]
+    rec = {"kernel": "lora_fwd (nf4_dequantize_kernel + lora_fwd_kernel from 1024 tokens)",
+           "workload": "llama3-8b-q_proj",
            "commands": ["rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o run --output-format csv -- "
                         "python3 bench.py --counter-pass --steps 2",
                         "rocprofv3 --pmc WRITE_SIZE -d WRITE_DIR -o run --output-format csv -- "
                         "python3 bench.py --counter-pass --steps 2",
                         "python3 bench.py --ingest-counters FETCH_DIR WRITE_DIR"],
            "source_sha": fwd_source_sha(),
-           "fetch_kib_raw": pick(fetch, "lora_fwd_kernel"), "write_kib_raw": pick(write, "lora_fwd_kernel"),
+           "fetch_kib_raw": fetch_fwd, "write_kib_raw": write_fwd,
            "calibration": {"copy_bytes": COPY_BYTES, "fetch_factor": cal_f, "write_factor": cal_w}}
     rec["hbm_bytes_per_launch"] = round(1024 * (rec["fetch_kib_raw"] * cal_f + rec["write_kib_raw"] * cal_w))
-    others = {}
-    for key in ("lora_dx_kernel", "skinny_partial_kernel", "skinny_reduce2_kernel"):
-        try:
-            others[key] = round(1024 * (pick(fetch, key) * cal_f + pick(write, key) * cal_w))
-        except SystemExit:
-            pass
-    rec["other_kernels_hbm_bytes_per_launch"] = others
+    rec["other_kernels_hbm_bytes_per_launch"] = {
+        k: round(1024 * (fetch_other[k] * cal_f + write_other.get(k, 0.0) * cal_w))
+        for k in fetch_other if k != copy_key}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
@@ -633,7 +656,8 @@ def main():
         "fwd_ms": round(fwd_avg, 4),
         "bwd_ms": round(float(np.mean(bwd_ms)), 4),
         "host_wall_s": round(wall, 4),
-        "roofline": {"kernel": "lora_fwd_kernel", "projection": unit_label,
+        "roofline": {"kernel": ("lora_fwd (nf4_dequantize_kernel + lora_fwd_kernel)" if T >= 1024
+                                else "lora_fwd_kernel"), "projection": unit_label,
                      "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},

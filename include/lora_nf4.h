@@ -98,11 +98,13 @@ int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows, int6
  *   workspace  device scratch of at least lora_nf4_fwd_workspace_bytes(T, d_in,
  *            d_out, r) bytes, 256-byte aligned, owned by the caller (contents on
  *            entry do not matter, on return unspecified; concurrent calls need
- *            separate workspaces). That size is non-zero only where the
- *            reduction over d_in is split across workgroups and fp32 partial sums
- *            meet in the workspace: few tokens (T <= 128 at r % 8 == 0, r <= 64),
- *            and token counts whose output tiles leave most of the GPU idle;
- *            when it is 0 the workspace may be NULL.
+ *            separate workspaces). That size is non-zero where the reduction
+ *            over d_in is split across workgroups and fp32 partial sums meet in
+ *            the workspace (few tokens: T <= 128 at r % 8 == 0, r <= 64; and
+ *            token counts whose output tiles leave most of the GPU idle), and
+ *            from T = 1024 on, where the weight is dequantized once into it
+ *            (bf16 [d_out, d_in]: 2 d_in d_out bytes, the same values the fused
+ *            kernels produce); when it is 0 the workspace may be NULL.
  * T >= 0, d_in % 64 == 0, d_out % 8 == 0, 1 <= r <= LN_MAX_RANK. s = lora_alpha / r
  * is formed in float32 on the host. T = 0 is an empty batch: nothing is computed
  * and x, y, u_save and the workspace may be NULL. LN_EWORKSPACE if the workspace
@@ -135,9 +137,11 @@ size_t lora_nf4_fwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int3
  *                        for lora_nf4_fwd with that projection's d_out
  *   u_save               NULL, or a HOST array [n_proj] whose entries may be NULL
  *   workspace            as for lora_nf4_fwd, sized by
- *                        lora_nf4_fwd_multi_workspace_bytes (non-zero only when
- *                        the projections run one after the other on the
- *                        few-token path, which then reuse it in turn)
+ *                        lora_nf4_fwd_multi_workspace_bytes: non-zero when the
+ *                        projections run one after the other on a path that
+ *                        needs one (they reuse it in turn), and for one shared
+ *                        launch from T = 1024 on (every projection's weight
+ *                        dequantized into it, one after another)
  * All projections share T, d_in, r and lora_alpha. The host arrays are read
  * during the call only. Every output (each y[g], each u_save[g], the workspace)
  * must be disjoint from every input and from the other outputs (LN_EALIAS).

@@ -14,6 +14,12 @@ hipError_t launch_nf4_quantize(const void* w, bool w_is_bf16, int64_t rows, int6
 
 hipError_t launch_nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows,
                                  int64_t cols, bool out_bf16, void* out, hipStream_t stream);
+// out [cols][rows] = bf16 deq(codes [rows][cols])^T (rows % 8 == 0, cols % 64 == 0),
+// and in the same launch out0 [c0][r0] = in0 [r0][c0]^T, out1 [c1][r1] = in1 [r1][c1]^T
+// (16-bit elements; the small factors that go with the weight).
+hipError_t launch_nf4_dequantize_t(const uint8_t* codes, const float* absmax, int rows, int cols,
+                                   uint16_t* out, const uint16_t* in0, int r0, int c0, uint16_t* out0,
+                                   const uint16_t* in1, int r1, int c1, uint16_t* out1, hipStream_t stream);
 
 // Zero n 16-bit elements (a fill kernel, so the call can sit in a captured graph).
 hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t stream);
@@ -170,9 +176,18 @@ struct BwdPlan {
   int splits_b;       // token splits of the dB reduction
   size_t off_g, off_u, off_pa, off_pb;  // byte offsets into the workspace
   size_t off_px, off_pg;                // weight-streaming dX partials
+  bool dq;                              // dX through the forward kernels (dx_dq_supported)
+  size_t off_wt, off_bt, off_at;        // its transposed weight and factors
   size_t bytes;       // total workspace bytes
 };
 BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r);
+
+// dX (and G = bf16(s dY B^T)) of one projection through the forward kernels, from
+// the transposed dequantized weight wt [K][N] and the transposed factors bt [N][r],
+// at [r][K] (lora_fwd.hip).
+bool dx_dq_supported(int64_t T, int64_t K, int64_t N, int r);
+hipError_t launch_dx_dq(int T, int K, int N, int r, float s, const uint16_t* dy, const uint16_t* wt,
+                        const uint16_t* bt, const uint16_t* at, uint16_t* dx, uint16_t* g, hipStream_t stream);
 
 hipError_t launch_lora_bwd(int T, int K, int N, int r, float s, const uint16_t* x,
                            const uint16_t* dy, const uint8_t* codes, const float* absmax,

@@ -358,6 +358,13 @@ hipError_t launch_bwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
     e = launch_lora_dx_splitk(T, K, N, r, s, dy, codes, absmax, A, B, dx, g,
                               reinterpret_cast<float*>(ws + p.off_px),
                               reinterpret_cast<float*>(ws + p.off_pg), stream);
+  } else if (p.dq) {
+    uint16_t* wt = reinterpret_cast<uint16_t*>(ws + p.off_wt);
+    uint16_t* bt = reinterpret_cast<uint16_t*>(ws + p.off_bt);
+    uint16_t* at = reinterpret_cast<uint16_t*>(ws + p.off_at);
+    if ((e = launch_nf4_dequantize_t(codes, absmax, N, K, wt, B, r, N, bt, A, K, r, at, stream)) != hipSuccess)
+      return e;
+    e = launch_dx_dq(T, K, N, r, s, dy, wt, bt, at, dx, g, stream);
   } else if (p.fast) {
     const bool split = p.splits_x > 1;
     e = launch_lora_dx(T, K, N, r, s, dy, codes, absmax, A, B, dx, g,
@@ -484,6 +491,14 @@ BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r) {
     off = align256(off + d.part_x_bytes);
     p.off_pg = off;
     off = align256(off + d.part_g_bytes);
+  } else if (p.fast && dx_dq_supported(T, K, N, r)) {  // dX through the forward kernels
+    p.dq = true;
+    p.off_wt = off;
+    off = align256(off + static_cast<size_t>(K) * N * 2);
+    p.off_bt = off;
+    off = align256(off + static_cast<size_t>(N) * r * 2);
+    p.off_at = off;
+    off = align256(off + static_cast<size_t>(r) * K * 2);
   } else if (p.fast) {  // tiled dX, split over d_out when its tile grid is small
     const DxTiledSplit d = dx_tiled_split(T, K, N, r);
     if (d.splits > 1) {

@@ -82,13 +82,17 @@ def test_fwd_validation(lib):
 def test_fwd_workspace(lib):
     """Up to 128 tokens the reduction over d_in is split across workgroups, with a
     workspace (except a few tokens on d_out <= 4096: one streaming launch); the
-    tiled and generic paths take none (NULL accepted)."""
+    tiled path takes none below 1024 tokens (NULL accepted) and the dequantized
+    weight from 1024 tokens on; the generic path takes none."""
     need = lib.lora_nf4_fwd_workspace_bytes(64, 64, 64, 8)
     assert need > 0 and need % 256 == 0
     assert lib.lora_nf4_fwd_workspace_bytes(128, 4096, 4096, 16) > 0
     assert lib.lora_nf4_fwd_workspace_bytes(8, 4096, 8192, 16) > 0       # few tokens, wide d_out
     assert lib.lora_nf4_fwd_workspace_bytes(8, 4096, 4096, 16) == 0      # few tokens: streaming
-    assert lib.lora_nf4_fwd_workspace_bytes(8192, 4096, 4096, 16) == 0   # tiled
+    assert lib.lora_nf4_fwd_workspace_bytes(1000, 4096, 4096, 16) == 0   # tiled
+    # from 1024 tokens the weight is dequantized once into the workspace (bf16)
+    assert lib.lora_nf4_fwd_workspace_bytes(8192, 4096, 4096, 16) == 4096 * 4096 * 2
+    assert lib.lora_nf4_fwd_workspace_bytes(1024, 320, 200, 16) == (320 * 200 * 2 + 255) // 256 * 256
     assert lib.lora_nf4_fwd_workspace_bytes(64, 64, 64, 12) == 0         # r % 8 != 0: generic kernels
     assert lib.lora_nf4_fwd_workspace_bytes(0, 64, 64, 8) == 0
     assert lib.lora_nf4_fwd_workspace_bytes(64, 65, 64, 8) == 0          # invalid sizes
@@ -103,7 +107,7 @@ def test_fwd_workspace(lib):
     d_out = (ctypes.c_int64 * 3)(64, 16, 16)
     assert lib.lora_nf4_fwd_multi_workspace_bytes(64, 64, 3, ctypes.cast(d_out, vp), 8) == need
     big = (ctypes.c_int64 * 3)(4096, 1024, 1024)
-    assert lib.lora_nf4_fwd_multi_workspace_bytes(8192, 4096, 3, ctypes.cast(big, vp), 16) == 0
+    assert lib.lora_nf4_fwd_multi_workspace_bytes(8192, 4096, 3, ctypes.cast(big, vp), 16) == 6144 * 4096 * 2
     assert lib.lora_nf4_fwd_multi_workspace_bytes(64, 64, 0, ctypes.cast(d_out, vp), 8) == 0
 
 

@@ -132,6 +132,46 @@ def test_forward_tile_edges_agree(q, r):
     assert olora.rel_err(host_f64(u), u_ref) <= TOL
 
 
+# From 1024 tokens the forward dequantizes the weight once into its workspace and
+# runs the tiles on bf16; the values are those of the in-loop dequantization.
+# Ragged T, d_in and d_out (odd step counts), every rank block.
+DQ = [(1100, 320, 200, 16), (1030, 448, 520, 64), (2080, 192, 264, 24), (1040, 256, 136, 40)]
+
+
+@pytest.mark.parametrize("T,K,N,r", DQ)
+def test_forward_dequantized_matches_in_loop(q, T, K, N, r):
+    """Rows 0 .. 1022 through the dequantize-then-GEMM path (T >= 1024) and
+    through the in-loop dequantization (T = 1023): each output row depends on its
+    own input row only, in the same order, so the bits agree; and the oracle."""
+    from tests.gpu_util import dev_bf16, host_f64
+    inp = synth.custom_inputs(12, T, K, N, r)
+    x, W, A, B = (dev_bf16(inp[k]) for k in ("x", "W", "A", "B"))
+    codes, absmax = q.nf4_quantize(W)
+    assert q.lora_nf4_fwd_workspace_bytes(T, K, N, r) >= K * N * 2
+    assert q.lora_nf4_fwd_workspace_bytes(1023, K, N, r) == 0
+    y, u = q.lora_nf4_fwd(x, codes, absmax, A, B, 16.0)
+    y1, u1 = q.lora_nf4_fwd(x[:1023].contiguous(), codes, absmax, A, B, 16.0)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:1023], y1) and torch.equal(u[:1023], u1)
+    y_ref, u_ref = olora.forward(_f64(inp["x"]), _oracle_D(inp), _f64(inp["A"]), _f64(inp["B"]), 16.0, r)
+    assert olora.rel_err(host_f64(y), y_ref) <= TOL
+    assert olora.rel_err(host_f64(u), u_ref) <= TOL
+
+
+# From 8192 tokens at rank <= 16 with d_out a multiple of 64, the backward takes dX
+# through the forward's kernels: the weight dequantized transposed into the
+# workspace, x = dY, A = B^T, B = A^T; the saved U, scaled by s, is G. Ragged T
+# and d_in, one to eight d_out steps, both rank blocks it takes; the full oracle
+# on every output.
+DQ_BWD = [(8200, 320, 192, 16), (8230, 192, 128, 8), (9000, 128, 64, 16), (8300, 448, 512, 16)]
+
+
+@pytest.mark.parametrize("T,K,N,r", DQ_BWD)
+def test_backward_dequantized(q, T, K, N, r):
+    inp = synth.custom_inputs(13, T, K, N, r)
+    _check_full(q, inp, 16.0, r, f"dq-bwd T={T} K={K} N={N} r={r}")
+
+
 @pytest.mark.parametrize("r", [16, 64])
 def test_dx_tile_edges_agree(q, r):
     """The input gradient's tile edge follows the same round count: 500 tokens x
@@ -157,7 +197,7 @@ def test_dx_tile_edges_agree(q, r):
     assert olora.rel_err(host_f64(dx)[:, cols], dx_ref) <= TOL
 
 
-@pytest.mark.parametrize("T,K,N,r", [(300, 256, 192, 16), (7, 320, 200, 24)])
+@pytest.mark.parametrize("T,K,N,r", [(300, 256, 192, 16), (7, 320, 200, 24), (8200, 256, 192, 16)])
 def test_recompute_u_and_skip_dx_paths(q, T, K, N, r):
     from tests.gpu_util import host_f64
     inp = synth.custom_inputs(2, T, K, N, r)
@@ -232,7 +272,7 @@ def test_operand_beyond_two_gib(q):
 
 
 @pytest.mark.parametrize("T,K,N,r", [(131, 192, 200, 12), (7, 320, 72, 24), (100, 448, 200, 16),
-                                     (260, 1024, 136, 16)])
+                                     (260, 1024, 136, 16), (1040, 320, 200, 16), (8200, 320, 192, 16)])
 def test_guard_bands_untouched(q, T, K, N, r):
     """Outputs written through the C ABI stay inside their buffers."""
     from tests.gpu_util import Guarded, dev_bf16
@@ -301,10 +341,12 @@ def test_full_size_sampled(q, wi, pi):
 
 # Multi-projection forward: the same values as one lora_nf4_fwd per projection
 # (bitwise: each output tile runs the same kernel code on the same data), on the
-# tiled path (one launch), the few-token paths and the K-split tiled forward
-# (one workspace shared by the projections in turn) and the generic path.
+# tiled path (one launch; from 1024 tokens with every weight dequantized into the
+# workspace), the few-token paths and the K-split tiled forward (one workspace
+# shared by the projections in turn) and the generic path.
 MULTI = [(300, 256, (256, 64, 64), 16), (200, 320, (200, 40, 8), 24), (8, 192, (64, 16, 16), 16),
-         (150, 128, (72, 136), 12), (100, 256, (128, 64, 64), 16), (300, 2048, (256, 64, 64), 16)]
+         (150, 128, (72, 136), 12), (100, 256, (128, 64, 64), 16), (300, 2048, (256, 64, 64), 16),
+         (1100, 320, (200, 72, 136), 16)]
 
 
 @pytest.mark.parametrize("T,K,Ns,r", MULTI)
