@@ -553,8 +553,11 @@ int fwd_tile_edge(int64_t T, int cols256, int cols128, int r) {
 // 32): filling at most 32 % of them, or 50 % when the main loop dominates (rank
 // > 32, or d_in >= 16384). Measured on MI355X at 160 .. 2048 tokens over q_proj,
 // Qwen-14B, the 70B gate and down and k/v shapes, the rule splits exactly where
-// splitting was faster. S fills the slots, at most four
-// ways and at least eight 64-element steps per split (1 = no split).
+// splitting was faster. From 4096 tokens nothing splits: the partials grow with T
+// while the unsplit dequantize-then-GEMM path runs at the same speed (k/v at rank
+// 64, 8192 tokens: 157 us split, 149 us unsplit), and unsplit projections can share
+// one multi-projection launch (q/k/v: 650 -> 500 us). S fills the slots, at most
+// four ways and at least eight 64-element steps per split (1 = no split).
 struct TiledSplit {
   int bt, splits, steps_per;
 };
@@ -569,7 +572,7 @@ TiledSplit tiled_split(int64_t T, int64_t K, int64_t N, int r) {
   int S = static_cast<int>(slots / tiles);
   S = S > 4 ? 4 : S;
   S = S > KB / 8 ? KB / 8 : S;
-  S = idle && S >= 2 ? S : 1;
+  S = idle && S >= 2 && T < 4096 ? S : 1;
   p.steps_per = (KB + S - 1) / S;
   p.splits = (KB + p.steps_per - 1) / p.steps_per;  // every split non-empty
   return p;
