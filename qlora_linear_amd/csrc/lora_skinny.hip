@@ -174,6 +174,23 @@ __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(
     }
 }
 
+// Sum of p[sp * stride], sp = 0 .. splits - 1, in split order. The loads go out in
+// independent batches of eight (a plain loop pays one memory latency per split:
+// 13-16 us at 64 splits); the additions keep their order, so the bits do not change.
+__device__ __forceinline__ float sum_splits(const float* __restrict__ p, int splits, size_t stride) {
+  float sum = 0.f;
+  int sp = 0;
+  for (; sp + 8 <= splits; sp += 8) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = p[static_cast<size_t>(sp + q) * stride];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) sum += v[q];
+  }
+  for (; sp < splits; ++sp) sum += p[static_cast<size_t>(sp) * stride];
+  return sum;
+}
+
 // dA[c][j] = sum_split part_a[split][j][c], columns j split into projections of
 // da.gw ranks (dA_g[c][j - g gw]);  dB[j][c] = s sum_split part_b[split][j][c]
 __global__ __launch_bounds__(256) void skinny_reduce2_kernel(const float* __restrict__ part_a,
@@ -185,15 +202,13 @@ __global__ __launch_bounds__(256) void skinny_reduce2_kernel(const float* __rest
   const int64_t na = static_cast<int64_t>(K) * ra;
   if (idx < na) {
     const int j = static_cast<int>(idx / K), c = static_cast<int>(idx - static_cast<int64_t>(j) * K);
-    float sum = 0.f;
-    for (int sp = 0; sp < splits; ++sp) sum += part_a[(static_cast<size_t>(sp) * ra + j) * K + c];
+    const float sum = sum_splits(part_a + static_cast<size_t>(j) * K + c, splits, static_cast<size_t>(ra) * K);
     const int g = j / da.gw, jj = j - g * da.gw;
     da.p[g][static_cast<size_t>(c) * da.gw + jj] = to_bf16(sum);
   } else if (idx < na + static_cast<int64_t>(N) * rb) {
     const int64_t i2 = idx - na;
     const int j = static_cast<int>(i2 / N), c = static_cast<int>(i2 - static_cast<int64_t>(j) * N);
-    float sum = 0.f;
-    for (int sp = 0; sp < splits; ++sp) sum += part_b[(static_cast<size_t>(sp) * rb + j) * N + c];
+    const float sum = sum_splits(part_b + static_cast<size_t>(j) * N + c, splits, static_cast<size_t>(rb) * N);
     dB[static_cast<size_t>(j) * N + c] = to_bf16(s * sum);
   }
 }
