@@ -337,28 +337,37 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
   };
   // Several projections: at the end of projection g's steps, store bf16(s G_g)
   // for this wave's rows into g_out columns g r .. and restart the accumulator.
+  // The lane's first row is made opaque here and every other row is that plus a
+  // constant times R (uniform): otherwise the compiler hoists the 32 loop-invariant
+  // row addresses out of the K-loop and keeps them live through it (spills).
   int gseg = 0, gend = tab.step_end[0];
   auto flush = [&](int st) {
     if constexpr (!MULTI) return;
     if (st + 1 != gend) return;
     const size_t col0 = static_cast<size_t>(gseg) * r;
+    if constexpr (RU / 32 > 0) {
+      int lrow = m0 + wm * kHalf + wn * 32 + 4 * lh;  // row of element 0 of this lane
+      asm volatile("" : "+v"(lrow));
+      uint16_t* gp = g_out + static_cast<size_t>(lrow) * R + col0 + l32;
 #pragma unroll
-    for (int u = 0; u < RU / 32; ++u)
+      for (int u = 0; u < RU / 32; ++u)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = wm * kHalf + wn * 32 + mfma32_row(e, lane), col = u * 32 + l32;
-        if (col < r && m0 + row < T)
-          g_out[static_cast<size_t>(m0 + row) * R + col0 + col] = to_bf16(s * gacc[u][e]);
-        gacc[u][e] = 0.f;
-      }
+        for (int e = 0; e < 16; ++e) {
+          const int dr = 8 * (e >> 2) + (e & 3);  // mfma32_row(e, lane) - 4 (lane >> 5)
+          if (u * 32 + l32 < r && lrow + dr < T) gp[static_cast<size_t>(dr) * R + u * 32] = to_bf16(s * gacc[u][e]);
+          gacc[u][e] = 0.f;
+        }
+    }
     if constexpr (kG16) {
+      int lrow = m0 + wm * kHalf + wn * 32 + 4 * lq;
+      asm volatile("" : "+v"(lrow));
+      uint16_t* gp = g_out + static_cast<size_t>(lrow) * R + col0 + l16;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int row = wm * kHalf + wn * 32 + rb * 16 + 4 * lq + e;
-          if (l16 < r && m0 + row < T)
-            g_out[static_cast<size_t>(m0 + row) * R + col0 + l16] = to_bf16(s * gacc16[rb][e]);
+          const int dr = rb * 16 + e;
+          if (l16 < r && lrow + dr < T) gp[static_cast<size_t>(dr) * R] = to_bf16(s * gacc16[rb][e]);
           gacc16[rb][e] = 0.f;
         }
     }
