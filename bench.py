@@ -152,7 +152,7 @@ def ingest_counters(fetch_dir: str, write_dir: str):
         raise SystemExit("no dispatch of the calibration copy in the counter data")
     cal_f = (COPY_BYTES / 1024) / fetch_other[copy_key]
     cal_w = (COPY_BYTES / 1024) / write_other[copy_key]
-    rec = {"kernel": "lora_fwd (nf4_dequantize_kernel + lora_fwd_kernel from 1024 tokens)",
+    rec = {"kernel": "lora_fwd (nf4_dequantize_kernel + lora_fwd_kernel at large token counts)",
            "workload": "llama3-8b-q_proj",
            "commands": ["rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o run --output-format csv -- "
                         "python3 bench.py --counter-pass --steps 2",
@@ -656,7 +656,8 @@ def main():
         "fwd_ms": round(fwd_avg, 4),
         "bwd_ms": round(float(np.mean(bwd_ms)), 4),
         "host_wall_s": round(wall, 4),
-        "roofline": {"kernel": ("lora_fwd (nf4_dequantize_kernel + lora_fwd_kernel)" if T >= 1024
+        "roofline": {"kernel": ("lora_fwd (nf4_dequantize_kernel + lora_fwd_kernel)"
+                                if q.lora_nf4_fwd_workspace_bytes(T, K, N, r) >= K * N * 2
                                 else "lora_fwd_kernel"), "projection": unit_label,
                      "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

@@ -102,7 +102,8 @@ int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows, int6
  *            over d_in is split across workgroups and fp32 partial sums meet in
  *            the workspace (few tokens: T <= 128 at r % 8 == 0, r <= 64; and
  *            token counts whose output tiles leave most of the GPU idle), and
- *            from T = 1024 on, where the weight is dequantized once into it
+ *            at large token counts (from T = 1024, or 4096 where the output grid
+ *            runs 256 x 256 tiles), where the weight is dequantized once into it
  *            (bf16 [d_out, d_in]: 2 d_in d_out bytes, the same values the fused
  *            kernels produce); when it is 0 the workspace may be NULL.
  * T >= 0, d_in % 64 == 0, d_out % 8 == 0, 1 <= r <= LN_MAX_RANK. s = lora_alpha / r
@@ -140,8 +141,8 @@ size_t lora_nf4_fwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int3
  *                        lora_nf4_fwd_multi_workspace_bytes: non-zero when the
  *                        projections run one after the other on a path that
  *                        needs one (they reuse it in turn), and for one shared
- *                        launch from T = 1024 on (every projection's weight
- *                        dequantized into it, one after another)
+ *                        launch at large token counts (every projection's
+ *                        weight dequantized into it, one after another)
  * All projections share T, d_in, r and lora_alpha. The host arrays are read
  * during the call only. Every output (each y[g], each u_save[g], the workspace)
  * must be disjoint from every input and from the other outputs (LN_EALIAS).

@@ -578,15 +578,17 @@ TiledSplit tiled_split(int64_t T, int64_t K, int64_t N, int r) {
   return p;
 }
 
-// Dequantize-then-GEMM: from 1024 tokens on, each weight tile is read by at least
-// four (256-row) or eight (128-row) token tiles, and dequantizing the whole weight
-// once into the workspace (bf16 [N][K], one pass at HBM speed: 2.56 bytes per
-// weight) and staging bf16 tiles like x costs less than dequantizing in every
-// tile's loop. Measured on MI355X (4096 -> 4096 at 8192 tokens: 295 -> 261 us; the
-// 70B gate and down projections -7 %; 1024-2048 tokens within a few percent
-// either way). Same values: the dequantization rounds exactly as the in-loop one.
-constexpr int64_t kDqMinTokens = 1024;
-bool fwd_dq(int64_t T) { return T >= kDqMinTokens; }
+// Dequantize-then-GEMM: the in-loop dequantization is repeated by every token tile
+// (T / tile edge times per weight element). Once there are enough of them,
+// dequantizing the whole weight once into the workspace (bf16 [N][K], one pass at
+// HBM speed: 2.56 bytes per weight) and staging bf16 tiles like x costs less: from
+// 8 token tiles of 128 rows (T >= 1024) or 16 of 256 rows (T >= 4096). Measured on
+// MI355X: 4096 -> 4096 at 8192 tokens 295 -> 261 us, at 1024 tokens (128-row
+// tiles) 71 -> 65 us; the 70B gate at 1024 tokens (4 tiles of 256 rows) runs
+// 15 % faster in-loop (586 -> 496 us), and 256-row grids at 2048 tokens are within
+// +-5 % either way. Same values: the dequantization rounds exactly as the in-loop
+// one.
+bool fwd_dq(int64_t T, int bt) { return T >= (bt == 256 ? 4096 : 1024); }
 size_t dq_bytes(int64_t K, int64_t N) {
   return (static_cast<size_t>(N) * K * 2 + 255) & ~static_cast<size_t>(255);
 }
@@ -615,7 +617,7 @@ hipError_t launch_fwd_table(int T, int K, int r, float s, const uint16_t* x, Pro
   TiledSplit sp{bt, 1, K / BK};
   if (tab.n == 1 && workspace != nullptr) sp = tiled_split(T, K, tab.N[0], r);
   // the weights of every projection dequantized one after another into the workspace
-  const bool dq = workspace != nullptr && sp.splits == 1 && fwd_dq(T);
+  const bool dq = workspace != nullptr && sp.splits == 1 && fwd_dq(T, bt);
   if (dq) {
     unsigned char* w = static_cast<unsigned char*>(workspace);
     for (int g = 0; g < tab.n; ++g) {
@@ -666,15 +668,26 @@ size_t fwd_workspace_bytes(int64_t T, int64_t K, int64_t N, int r) {
   if (fwd_uses_splitk(T, K, N, r))
     return plan_fwd_splitk(static_cast<int>(T), static_cast<int>(K), static_cast<int>(N), r).bytes;
   if (r % 8 != 0 || r > 64 || !fits_buffer(T, K, N) || lora_fwd_stream_supported(T, r)) return 0;
-  const int splits = tiled_split(T, K, N, r).splits;
-  if (splits == 1 && fwd_dq(T)) return dq_bytes(K, N);
-  return tiled_split_bytes(T, N, r, splits);
+  const TiledSplit ts = tiled_split(T, K, N, r);
+  if (ts.splits == 1 && fwd_dq(T, ts.bt)) return dq_bytes(K, N);
+  return tiled_split_bytes(T, N, r, ts.splits);
+}
+
+// Tile edge of one launch over several projections (their column tiles form one
+// grid), as launch_fwd_table chooses it.
+int table_edge(int64_t T, int n_proj, const int* N, int r) {
+  int cols256 = 0, cols128 = 0;
+  for (int g = 0; g < n_proj; ++g) {
+    cols256 += (N[g] + 255) / 256;
+    cols128 += (N[g] + 127) / 128;
+  }
+  return fwd_tile_edge(T, cols256, cols128, r);
 }
 
 size_t fwd_multi_workspace_bytes(int64_t T, int64_t K, int n_proj, const int* N, int r) {
   if (fwd_multi_tiled(T, K, n_proj, N, r)) {
     size_t b = 0;
-    for (int g = 0; fwd_dq(T) && g < n_proj; ++g) b += dq_bytes(K, N[g]);
+    for (int g = 0; fwd_dq(T, table_edge(T, n_proj, N, r)) && g < n_proj; ++g) b += dq_bytes(K, N[g]);
     return b;
   }
   size_t b = 0;
@@ -733,7 +746,8 @@ hipError_t launch_lora_fwd_multi(int T, int K, int n_proj, const int* N, int r, 
     tab.y[g] = y[g];
     tab.u[g] = u_save == nullptr ? nullptr : u_save[g];
   }
-  return launch_fwd_table(T, K, r, s, x, tab, fwd_dq(T) ? workspace : nullptr, stream);
+  return launch_fwd_table(T, K, r, s, x, tab, fwd_dq(T, table_edge(T, n_proj, N, r)) ? workspace : nullptr,
+                          stream);
 }
 
 // Input gradient through the dequantize-then-GEMM forward kernels: with Wt =
