@@ -29,6 +29,11 @@
 //     narrow d_out), a single projection's K-loop is split across workgroups:
 //     each writes fp32 partial products (and partial U) to a workspace and the
 //     split-K reduce adds bf16(s U) B and stores y.
+//   * With many token tiles (8 of 128 rows or 16 of 256) the in-loop
+//     dequantization would be repeated that many times per weight element: the
+//     call then dequantizes the weight once into the workspace (bf16, the same
+//     values) and the kernel stages bf16 weight tiles like x (DQ instances). The
+//     backward's input gradient reuses these instances on the transposed weight.
 //   * Several projections of the same x (q/k/v or gate/up: the multi-projection
 //     fusion) share one launch: the column tiles of all projections form one
 //     grid, each tile reads its projection's weight, A, B and output from a small
