@@ -121,19 +121,17 @@ def counter_dispatches(d: str, counter: str) -> list:
 def forward_kib(disp: list) -> tuple:
     """Mean counter value (KiB) per forward call and per other kernel. From 1024 tokens a
     forward call is two launches, the weight's dequantization and the tile kernel
-    (lora_fwd_kernel); the tile kernel also runs the backward's input gradient, after
-    the transposed dequantization, and counts there as dX."""
+    (lora_fwd_kernel); the backward's input gradient likewise pairs it with the dX tile
+    kernel (lora_dx_kernel)."""
     import collections
     fwd, other = [], collections.defaultdict(list)
     prev = None
     for _, name, v in disp:
+        after_dq = prev is not None and "nf4_dequantize_kernel" in prev[0]
         if "lora_fwd_kernel" in name:
-            if prev is not None and "nf4_dequantize_t_kernel" in prev[0]:
-                other["lora_dx (nf4_dequantize_t_kernel + lora_fwd_kernel)"].append(prev[1] + v)
-            elif prev is not None and "nf4_dequantize_kernel" in prev[0]:
-                fwd.append(prev[1] + v)
-            else:
-                fwd.append(v)
+            fwd.append(prev[1] + v if after_dq else v)
+        elif "lora_dx_kernel" in name and after_dq:
+            other["lora_dx (nf4_dequantize_kernel + lora_dx_kernel)"].append(prev[1] + v)
         elif "nf4_dequantize" not in name:
             for key in ("lora_dx_kernel", "skinny_partial_kernel", "skinny_reduce2_kernel", "MulFunctor"):
                 if key in name:

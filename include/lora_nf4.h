@@ -170,7 +170,9 @@ size_t lora_nf4_fwd_multi_workspace_bytes(int64_t T, int64_t d_in, int32_t n_pro
  *   workspace  device scratch of at least lora_nf4_bwd_workspace_bytes(T, d_in,
  *            d_out, r) bytes, 256-byte aligned, owned by the caller; its contents
  *            on entry do not matter and on return are unspecified. Two calls that
- *            may run concurrently need separate workspaces.
+ *            may run concurrently need separate workspaces. At large token counts
+ *            (from T = 1024, or 4096 where dX runs 256 x 256 tiles) it also holds
+ *            the bf16 dequantized weight, 2 d_in d_out bytes.
  * Shape rules as for lora_nf4_fwd. With T = 0 (empty batch) dA and dB are set to
  * zero (empty sums), x, dy, u_saved, dx and the workspace may be NULL, and
  * lora_nf4_bwd_workspace_bytes is 0.

@@ -14,12 +14,6 @@ hipError_t launch_nf4_quantize(const void* w, bool w_is_bf16, int64_t rows, int6
 
 hipError_t launch_nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows,
                                  int64_t cols, bool out_bf16, void* out, hipStream_t stream);
-// out [cols][rows] = bf16 deq(codes [rows][cols])^T (rows % 8 == 0, cols % 64 == 0),
-// and in the same launch out0 [c0][r0] = in0 [r0][c0]^T, out1 [c1][r1] = in1 [r1][c1]^T
-// (16-bit elements; the small factors that go with the weight).
-hipError_t launch_nf4_dequantize_t(const uint8_t* codes, const float* absmax, int rows, int cols,
-                                   uint16_t* out, const uint16_t* in0, int r0, int c0, uint16_t* out0,
-                                   const uint16_t* in1, int r1, int c1, uint16_t* out1, hipStream_t stream);
 
 // Zero n 16-bit elements (a fill kernel, so the call can sit in a captured graph).
 hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t stream);
@@ -93,10 +87,14 @@ struct DxTiledSplit {
   int splits, steps_per;
 };
 DxTiledSplit dx_tiled_split(int64_t T, int64_t K, int64_t N, int r);
+// wdq: bf16 [N][K] deq(W) written beforehand (then codes and absmax are not read),
+// or nullptr to dequantize in the loop.
 hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* dy,
                           const uint8_t* codes, const float* absmax, const uint16_t* A,
-                          const uint16_t* B, uint16_t* dx, uint16_t* g_out, float* part_x, float* part_g,
-                          hipStream_t stream);
+                          const uint16_t* B, const uint16_t* wdq, uint16_t* dx, uint16_t* g_out, float* part_x,
+                          float* part_g, hipStream_t stream);
+// Whether the tiled dX takes a weight dequantized beforehand (large token counts).
+bool dx_dq(int64_t T, int64_t K, int64_t N, int r);
 
 // The dX kernel over a table of projections that share x: the reduction runs over
 // their concatenated d_out (step_end[g] = 64-wide steps of projections 0..g) and
@@ -111,6 +109,9 @@ struct DxTable {
   const float* absmax[kMaxProj];
   const uint16_t* A[kMaxProj];
   const uint16_t* B[kMaxProj];
+  // bf16 [N][K] dequantized weights; when wdq[0] is non-null every entry is set and
+  // the kernel reads these instead of the codes
+  const uint16_t* wdq[kMaxProj];
 };
 // Several projections take this kernel when every d_out is a multiple of 64 and
 // n r <= 64 (r % 8 == 0).
@@ -176,18 +177,11 @@ struct BwdPlan {
   int splits_b;       // token splits of the dB reduction
   size_t off_g, off_u, off_pa, off_pb;  // byte offsets into the workspace
   size_t off_px, off_pg;                // weight-streaming dX partials
-  bool dq;                              // dX through the forward kernels (dx_dq_supported)
-  size_t off_wt, off_bt, off_at;        // its transposed weight and factors
+  bool dqx;                             // tiled dX on the dequantized weight (dx_dq)
+  size_t off_w;                         // that weight, bf16 [N][K]
   size_t bytes;       // total workspace bytes
 };
 BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r);
-
-// dX (and G = bf16(s dY B^T)) of one projection through the forward kernels, from
-// the transposed dequantized weight wt [K][N] and the transposed factors bt [N][r],
-// at [r][K] (lora_fwd.hip).
-bool dx_dq_supported(int64_t T, int64_t K, int64_t N, int r);
-hipError_t launch_dx_dq(int T, int K, int N, int r, float s, const uint16_t* dy, const uint16_t* wt,
-                        const uint16_t* bt, const uint16_t* at, uint16_t* dx, uint16_t* g, hipStream_t stream);
 
 hipError_t launch_lora_bwd(int T, int K, int N, int r, float s, const uint16_t* x,
                            const uint16_t* dy, const uint8_t* codes, const float* absmax,
@@ -206,6 +200,8 @@ struct BwdMultiPlan {
   int splits_a;               // fused: token splits of the first rank-r pass
   int splits_b[kMaxProj];     // fused: token splits of the passes of projections 1 ..
   size_t off_g, off_u, off_pa, off_pb;  // fused
+  bool dq;                              // fused: dX on the dequantized weights (dx_dq)
+  size_t off_w[kMaxProj];               // those weights, bf16 [N_g][K]
   size_t off_single, off_dxt;           // per-projection fallback
   size_t bytes;
 };

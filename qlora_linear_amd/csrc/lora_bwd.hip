@@ -358,16 +358,11 @@ hipError_t launch_bwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
     e = launch_lora_dx_splitk(T, K, N, r, s, dy, codes, absmax, A, B, dx, g,
                               reinterpret_cast<float*>(ws + p.off_px),
                               reinterpret_cast<float*>(ws + p.off_pg), stream);
-  } else if (p.dq) {
-    uint16_t* wt = reinterpret_cast<uint16_t*>(ws + p.off_wt);
-    uint16_t* bt = reinterpret_cast<uint16_t*>(ws + p.off_bt);
-    uint16_t* at = reinterpret_cast<uint16_t*>(ws + p.off_at);
-    if ((e = launch_nf4_dequantize_t(codes, absmax, N, K, wt, B, r, N, bt, A, K, r, at, stream)) != hipSuccess)
-      return e;
-    e = launch_dx_dq(T, K, N, r, s, dy, wt, bt, at, dx, g, stream);
   } else if (p.fast) {
     const bool split = p.splits_x > 1;
-    e = launch_lora_dx(T, K, N, r, s, dy, codes, absmax, A, B, dx, g,
+    uint16_t* w = p.dqx ? reinterpret_cast<uint16_t*>(ws + p.off_w) : nullptr;
+    if (p.dqx && (e = launch_nf4_dequantize(codes, absmax, N, K, true, w, stream)) != hipSuccess) return e;
+    e = launch_lora_dx(T, K, N, r, s, dy, codes, absmax, A, B, w, dx, g,
                        split ? reinterpret_cast<float*>(ws + p.off_px) : nullptr,
                        split ? reinterpret_cast<float*>(ws + p.off_pg) : nullptr, stream);
   } else {
@@ -491,14 +486,6 @@ BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r) {
     off = align256(off + d.part_x_bytes);
     p.off_pg = off;
     off = align256(off + d.part_g_bytes);
-  } else if (p.fast && dx_dq_supported(T, K, N, r)) {  // dX through the forward kernels
-    p.dq = true;
-    p.off_wt = off;
-    off = align256(off + static_cast<size_t>(K) * N * 2);
-    p.off_bt = off;
-    off = align256(off + static_cast<size_t>(N) * r * 2);
-    p.off_at = off;
-    off = align256(off + static_cast<size_t>(r) * K * 2);
   } else if (p.fast) {  // tiled dX, split over d_out when its tile grid is small
     const DxTiledSplit d = dx_tiled_split(T, K, N, r);
     if (d.splits > 1) {
@@ -506,6 +493,10 @@ BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r) {
       off = align256(off + static_cast<size_t>(d.splits) * T * K * 4);
       p.off_pg = off;
       off = align256(off + static_cast<size_t>(d.splits) * T * r * 4);
+    } else if (dx_dq(T, K, N, r)) {
+      p.dqx = true;
+      p.off_w = off;
+      off = align256(off + static_cast<size_t>(N) * K * 2);
     }
   }
   p.bytes = off;
@@ -565,6 +556,12 @@ BwdMultiPlan plan_bwd_multi(int64_t T, int64_t K, int n, const int* N, int r) {
     off = align256(off + pa);
     p.off_pb = off;
     off = align256(off + pb);
+    p.dq = true;
+    for (int g = 0; g < n; ++g) p.dq = p.dq && dx_dq(T, K, N[g], r);
+    for (int g = 0; g < n && p.dq; ++g) {
+      p.off_w[g] = off;
+      off = align256(off + static_cast<size_t>(N[g]) * K * 2);
+    }
   } else {
     size_t single = 0;
     for (int g = 0; g < n; ++g) single = std::max(single, plan_bwd(T, K, N[g], r).bytes);
@@ -613,6 +610,11 @@ hipError_t launch_lora_bwd_multi(int T, int K, int n, const int* N, int r, float
     tab.absmax[g] = absmax[g];
     tab.A[g] = A[g];
     tab.B[g] = B[g];
+    if (p.dq) {
+      uint16_t* w = reinterpret_cast<uint16_t*>(ws + p.off_w[g]);
+      if ((e = launch_nf4_dequantize(codes[g], absmax[g], N[g], K, true, w, stream)) != hipSuccess) return e;
+      tab.wdq[g] = w;
+    }
   }
   uint16_t* G = reinterpret_cast<uint16_t*>(ws + p.off_g);
   if ((e = launch_lora_dx_table(T, K, r, s, tab, dx, G, stream)) != hipSuccess) return e;

@@ -24,6 +24,13 @@
 // g r .. g r + r - 1 of g_out [T][n r] and the accumulator restarts; every
 // column tile writes the same bits there. The epilogue reads the tile's rows back
 // and adds [G_0 .. G_n-1] [A_0 .. A_n-1]^T in one MFMA pass over n r.
+//
+// DQ instances: at large token counts each weight tile is read by many token
+// tiles, so the weight is dequantized once beforehand into bf16 [N][K] (the same
+// bf16(level x absmax) values) and the kernel loads its 64 x BT tiles straight
+// into LDS like the dY tiles, unpadded: the 16-byte piece p of row n sits at
+// piece p ^ 4 (n & 3), which keeps the four rows of a transposing read on
+// distinct banks. The arithmetic, and so every output bit, is the same.
 #include <type_traits>
 
 #include "device_common.h"
@@ -60,13 +67,14 @@ struct DxTile {
 // over d_out steps [steps_per (b / tiles), ...) and writes fp32 partial dX to
 // part_x [split][T][K] and, from the first column tile, fp32 partial dY B^T to
 // part_g [split][T][r]; no epilogue.
-template <int BT, int RU, int RE, bool MULTI>
+template <int BT, int RU, int RE, bool MULTI, bool DQ>
 __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void lora_dx_kernel(
     int T, int K, int r, float s, const DxTable tab, uint16_t* __restrict__ dx,
     uint16_t* __restrict__ g_out, int steps_per, float* __restrict__ part_x, float* __restrict__ part_g) {
   using Tl = DxTile<BT>;
   constexpr int kThreads = Tl::kThreads, BM = BT, BN = BT, kFM = Tl::kFM, kHalf = BT / 2;
-  constexpr int kTileElems = Tl::kTileElems, kDStride = Tl::kDStride, kDElems = Tl::kDElems;
+  constexpr int kTileElems = Tl::kTileElems, kDStride = Tl::kDStride;
+  constexpr int kDElems = DQ ? 64 * BT : Tl::kDElems;  // DQ: unpadded [64][BT]
   __shared__ __align__(1024) float lut[16];  // first in LDS: level addresses need no base
   __shared__ __align__(16) uint16_t ys0[kTileElems];
   __shared__ __align__(16) uint16_t ys1[kTileElems];
@@ -115,6 +123,21 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
   };
   set_yvoff(N0);
   auto rs_y = make_rsrc(tab.dy[0] + static_cast<size_t>(m0) * N0, static_cast<uint32_t>(rows_t) * N0 * 2);
+  // DQ weight tile: wave w fills 1 KB pieces 4 w .. 4 w + 3 of the [64][BT] stage;
+  // lane l of piece c lands at element 512 c + 8 l (row n, 16-byte piece p') and
+  // loads piece p' ^ 4 (n & 3) of that weight row. Rows past d_out lie outside the
+  // range and read zeros; columns past d_in only reach dX columns that are not stored.
+  uint32_t wvoff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = (wave * 4 + q) * 512 + lane * 8, n = e / BT, pp = (e % BT) / 8;
+    wvoff[q] = static_cast<uint32_t>(n) * K * 2 + ((pp ^ (4 * (n & 3))) * 16);
+  }
+  auto w_rsrc = [&](int g) {
+    return make_rsrc(DQ ? tab.wdq[g] + k0 : tab.dy[g],
+                     DQ ? static_cast<uint32_t>((static_cast<size_t>(tab.N[g]) * K - k0) * 2) : 0u);
+  };
+  auto rs_w = w_rsrc(0);
   int y_g = 0, y_beg = 0, y_end = tab.step_end[0];
   auto load_y_lds = [&](int st, uint16_t* stage) {
     if constexpr (MULTI) {
@@ -125,11 +148,18 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
         const int Ng = tab.N[y_g];
         rs_y = make_rsrc(tab.dy[y_g] + static_cast<size_t>(m0) * Ng, static_cast<uint32_t>(rows_t) * Ng * 2);
         set_yvoff(Ng);
+        if constexpr (DQ) rs_w = w_rsrc(y_g);
       }
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       buf_load16_lds(rs_y, stage + (wave_u * 4 + q) * 512, yvoff[q], (st - y_beg) * BK * 2);
+  };
+  // the weight tile of the step load_y_lds was last called with
+  auto load_w_lds = [&](int st, uint16_t* stage) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      buf_load16_lds(rs_w, stage + (wave_u * 4 + q) * 512, wvoff[q], (st - y_beg) * BK * K * 2);
   };
   // weight codes: one of the 64 rows of the step, 32 columns (one half of an NF4
   // block) at one of the BT / 32 runs of the tile. Thread bits, 256 x 256 tiles:
@@ -163,16 +193,21 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
         w_beg = w_end;
         w_end = tab.step_end[w_g];
         w_N = tab.N[w_g];
-        rs_c = make_rsrc(tab.codes[w_g] + k0 / 2, static_cast<uint32_t>(static_cast<size_t>(w_N) * K2 - k0 / 2));
-        rs_s = make_rsrc(tab.absmax[w_g] + k0 / 64,
-                         static_cast<uint32_t>((static_cast<size_t>(w_N) * KB - k0 / 64) * 4));
+        if constexpr (!DQ) {
+          rs_c = make_rsrc(tab.codes[w_g] + k0 / 2,
+                           static_cast<uint32_t>(static_cast<size_t>(w_N) * K2 - k0 / 2));
+          rs_s = make_rsrc(tab.absmax[w_g] + k0 / 64,
+                           static_cast<uint32_t>((static_cast<size_t>(w_N) * KB - k0 / 64) * 4));
+        }
         rs_b = make_rsrc(tab.B[w_g], static_cast<uint32_t>(r) * w_N * 2);
         bvoff = static_cast<uint32_t>(bj) * w_N * 2 + bch * 16;
       }
     }
     const int ls = st - w_beg;
-    creg[slot] = buf_load16(rs_c, cvoff, ls * 64 * K2);
-    sreg[slot] = __uint_as_float(buf_load4(rs_s, svoff, ls * 64 * KB * 4));
+    if constexpr (!DQ) {
+      creg[slot] = buf_load16(rs_c, cvoff, ls * 64 * K2);
+      sreg[slot] = __uint_as_float(buf_load4(rs_s, svoff, ls * 64 * KB * 4));
+    }
 #pragma unroll
     for (int i = 0; i < kBPer; ++i) {
       const uint4 v = buf_load16(rs_b, bvoff + i * (kThreads / 8) * w_N * 2, ls * BK * 2);
@@ -192,6 +227,12 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
   // and 2 (g16 >> 1) + 1, so the second read sits one group shift further
   const int d_off = ((g16 >> 1) * 8 + (m16 >> 2)) * kDStride + dshift((g16 >> 1) * 8) + wn * 64 +
                     (g16 & 1) * 16 + 4 * (m16 & 3);
+  // DQ layout: the same rows and columns, column half j at its swizzled piece
+  int dq_off[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    dq_off[j] = ((g16 >> 1) * 8 + (m16 >> 2)) * BT +
+                (((wn * 8 + j * 4 + (g16 & 1) * 2 + ((m16 & 3) >> 1)) ^ (4 * (m16 >> 2))) * 8) + 4 * (m16 & 1);
   const int gb_off = l32 * kBStride + lh * 8;  // + u * 32 * kBStride + ks * 16
   // r <= 16: 16 x 16 x 32 fragments of G rows wm * BT / 2 + wn * 32 + 16 rb + (lane & 15)
   constexpr bool kG16 = RU == 16;
@@ -249,16 +290,19 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
 
   // prologue: step 0 into stage 0, step 1 into registers
   load_y_lds(sbeg, ys0);
+  if constexpr (DQ) load_w_lds(sbeg, ds0);
   load_regs(sbeg, 0);
   wait_vmem();
   __syncthreads();  // lut and dY of step 0 visible
   {
-    const uint32_t cw[4] = {creg[0].x, creg[0].y, creg[0].z, creg[0].w};
+    if constexpr (!DQ) {
+      const uint32_t cw[4] = {creg[0].x, creg[0].y, creg[0].z, creg[0].w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float lv[8];
-      lookup(cw[q], lv);
-      finish_store(lv, sreg[0], ds0 + dw_off + q * 8);
+      for (int q = 0; q < 4; ++q) {
+        float lv[8];
+        lookup(cw[q], lv);
+        finish_store(lv, sreg[0], ds0 + dw_off + q * 8);
+      }
     }
     store_b(bs0, breg[0]);
   }
@@ -278,7 +322,10 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
     uint16_t* dn = cur ? ds0 : ds1;
     uint16_t* bn = cur ? bs0 : bs1;
     load_y_lds(st + 1, yn);
+    if constexpr (DQ) load_w_lds(st + 1, dn);
     load_regs(st + 2, cur);
+    // DQ: keep the next stage's loads at the top of the step
+    if constexpr (DQ) __builtin_amdgcn_sched_barrier(0);
     const uint32_t cw[4] = {creg[nslot].x, creg[nslot].y, creg[nslot].z, creg[nslot].w};
     const float ar = sreg[nslot];
     auto read_frag = [&](Frag& f, int ks) {
@@ -286,9 +333,15 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
       for (int i = 0; i < kFM; ++i) f.a[i] = *reinterpret_cast<const uint4*>(yc + a_off + i * 2048 + choff[ks]);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint16_t* p = dc + d_off + ks * 16 * kDStride + j * 32;
-        const uint2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * kDStride + 8);
-        f.b[j] = uint4{lo.x, lo.y, hi.x, hi.y};
+        if constexpr (DQ) {
+          const uint16_t* p = dc + dq_off[j] + ks * 16 * BT;
+          const uint2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * BT);
+          f.b[j] = uint4{lo.x, lo.y, hi.x, hi.y};
+        } else {
+          const uint16_t* p = dc + d_off + ks * 16 * kDStride + j * 32;
+          const uint2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * kDStride + 8);
+          f.b[j] = uint4{lo.x, lo.y, hi.x, hi.y};
+        }
       }
       if constexpr (kG16) {
         if (ks & 1) {  // one 32-wide k-slice of G per two 16-wide MFMA slices
@@ -306,13 +359,13 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
     Frag fr[2];
     float lv[2][8];
     read_frag(fr[0], 0);
-    lookup(cw[0], lv[0]);
+    if constexpr (!DQ) lookup(cw[0], lv[0]);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       Frag& f = fr[ks & 1];
       if (ks < 3) {
         read_frag(fr[(ks + 1) & 1], ks + 1);
-        lookup(cw[ks + 1], lv[(ks + 1) & 1]);
+        if constexpr (!DQ) lookup(cw[ks + 1], lv[(ks + 1) & 1]);
       }
 #pragma unroll
       for (int i = 0; i < kFM; ++i)
@@ -327,12 +380,12 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
 #pragma unroll
         for (int u = 0; u < RU / 32; ++u) gacc[u] = mfma32(f.ga, f.gb[u], gacc[u]);
       }
-      finish_store(lv[ks & 1], ar, dn + dw_off + ks * 8);
+      if constexpr (!DQ) finish_store(lv[ks & 1], ar, dn + dw_off + ks * 8);
       if (ks == 3) store_b(bn, breg[nslot]);
     }
-    // dY of the next stage has landed (the step st + 2 register loads issued after
-    // it may still be in flight)
-    wait_vmem_upto<2 + kBPer>();
+    // dY (and the DQ weight) of the next stage has landed (the step st + 2 register
+    // loads issued after it may still be in flight)
+    wait_vmem_upto<(DQ ? 0 : 2) + kBPer>();
     __syncthreads();
   };
   // Several projections: at the end of projection g's steps, store bf16(s G_g)
@@ -521,8 +574,12 @@ template <int BT, int RU, int RE, bool MULTI>
 hipError_t launch_dx_t(int T, int K, int r, float s, const DxTable& tab, uint16_t* dx, uint16_t* g_out,
                        const DxSplitArgs& a, hipStream_t stream) {
   const int tiles = ((T + BT - 1) / BT) * ((K + BT - 1) / BT);
-  lora_dx_kernel<BT, RU, RE, MULTI><<<tiles * a.splits, DxTile<BT>::kThreads, 0, stream>>>(
-      T, K, r, s, tab, dx, g_out, a.steps_per, a.part_x, a.part_g);
+  if (tab.wdq[0] != nullptr)
+    lora_dx_kernel<BT, RU, RE, MULTI, true><<<tiles * a.splits, DxTile<BT>::kThreads, 0, stream>>>(
+        T, K, r, s, tab, dx, g_out, a.steps_per, a.part_x, a.part_g);
+  else
+    lora_dx_kernel<BT, RU, RE, MULTI, false><<<tiles * a.splits, DxTile<BT>::kThreads, 0, stream>>>(
+        T, K, r, s, tab, dx, g_out, a.steps_per, a.part_x, a.part_g);
   return hipGetLastError();
 }
 
@@ -612,10 +669,18 @@ DxTiledSplit dx_tiled_split(int64_t T, int64_t K, int64_t N, int r) {
   return p;
 }
 
+// The tiled dX on a weight dequantized beforehand: from 1024 tokens on 128 x 128
+// tiles and 4096 on 256 x 256 tiles (the forward's rule: there each weight tile
+// is read by at least eight token tiles), with the bf16 weight within one buffer
+// range.
+bool dx_dq(int64_t T, int64_t K, int64_t N, int r) {
+  return T >= (dx_tile_edge(T, K, r) == 256 ? 4096 : 1024) && N * K * 2 < (int64_t(1) << 31) - 1;
+}
+
 hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* dy,
                           const uint8_t* codes, const float* absmax, const uint16_t* A,
-                          const uint16_t* B, uint16_t* dx, uint16_t* g_out, float* part_x, float* part_g,
-                          hipStream_t stream) {
+                          const uint16_t* B, const uint16_t* wdq, uint16_t* dx, uint16_t* g_out, float* part_x,
+                          float* part_g, hipStream_t stream) {
   DxTable tab{};
   tab.n = 1;
   tab.step_end[0] = (N + BK - 1) / BK;
@@ -625,6 +690,7 @@ hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* d
   tab.absmax[0] = absmax;
   tab.A[0] = A;
   tab.B[0] = B;
+  tab.wdq[0] = wdq;
   const DxTiledSplit sp = part_x != nullptr ? dx_tiled_split(T, K, N, r) : DxTiledSplit{1, tab.step_end[0]};
   if (sp.splits <= 1) return launch_lora_dx_table(T, K, r, s, tab, dx, g_out, stream);
   const DxSplitArgs a{sp.splits, sp.steps_per, part_x, part_g};

@@ -32,8 +32,7 @@
 //   * With many token tiles (8 of 128 rows or 16 of 256) the in-loop
 //     dequantization would be repeated that many times per weight element: the
 //     call then dequantizes the weight once into the workspace (bf16, the same
-//     values) and the kernel stages bf16 weight tiles like x (DQ instances). The
-//     backward's input gradient reuses these instances on the transposed weight.
+//     values) and the kernel stages bf16 weight tiles like x (DQ instances).
 //   * Several projections of the same x (q/k/v or gate/up: the multi-projection
 //     fusion) share one launch: the column tiles of all projections form one
 //     grid, each tile reads its projection's weight, A, B and output from a small
@@ -63,11 +62,8 @@ struct FwdTile {
 };
 
 // Projections of one launch; tile_end[g] = column tiles of projections 0..g.
-// u_save receives bf16(u_scale U): 1 for the forward's U; s when the kernel runs
-// the input gradient (x = dY, A = B^T), whose G = s dY B^T the backward reuses.
 struct ProjTable {
   int n;
-  float u_scale;
   int tile_end[kMaxProj];
   int N[kMaxProj];
   const uint8_t* codes[kMaxProj];
@@ -467,7 +463,7 @@ __global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) voi
       const float uv = uacc[u][e];
       if (col < RE) us[ep(row, col)] = to_bf16(s * uv);
       if (u_save != nullptr && tn == 0 && col < r && m0 + row < T)
-        u_save[static_cast<size_t>(m0 + row) * r + col] = to_bf16(tab.u_scale * uv);
+        u_save[static_cast<size_t>(m0 + row) * r + col] = to_bf16(uv);
     }
   if constexpr (kU16) {
 #pragma unroll
@@ -478,10 +474,9 @@ __global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) voi
         const float uv = uacc16[rb][e];
         us[ep(row, l16)] = to_bf16(s * uv);
         if (u_save != nullptr && tn == 0 && l16 < r && m0 + row < T)
-          u_save[static_cast<size_t>(m0 + row) * r + l16] = to_bf16(tab.u_scale * uv);
+          u_save[static_cast<size_t>(m0 + row) * r + l16] = to_bf16(uv);
       }
   }
-  if (y == nullptr) return;  // only U wanted (the input-gradient use without dX)
   for (int e = tid; e < BT * RE; e += kThreads) {
     const int j = e / BT, c = e % BT;
     bt[ep(c, j)] = (j < r && n0 + c < N) ? B[static_cast<size_t>(j) * N + n0 + c] : uint16_t(0);
@@ -715,7 +710,6 @@ hipError_t launch_lora_fwd(int T, int K, int N, int r, float s, const uint16_t* 
     return launch_lora_fwd_stream(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
   ProjTable tab{};
   tab.n = 1;
-  tab.u_scale = 1.0f;
   tab.N[0] = N;
   tab.codes[0] = codes;
   tab.absmax[0] = absmax;
@@ -741,7 +735,6 @@ hipError_t launch_lora_fwd_multi(int T, int K, int n_proj, const int* N, int r, 
   }
   ProjTable tab{};
   tab.n = n_proj;
-  tab.u_scale = 1.0f;
   for (int g = 0; g < n_proj; ++g) {
     tab.N[g] = N[g];
     tab.codes[g] = codes[g];
@@ -753,39 +746,6 @@ hipError_t launch_lora_fwd_multi(int T, int K, int n_proj, const int* N, int r, 
   }
   return launch_fwd_table(T, K, r, s, x, tab, fwd_dq(T, table_edge(T, n_proj, N, r)) ? workspace : nullptr,
                           stream);
-}
-
-// Input gradient through the dequantize-then-GEMM forward kernels: with Wt =
-// deq(W)^T [d_in][d_out], Bt = B^T [d_out][r] and At = A^T [r][d_in], the forward
-// of x = dY over the weight Wt computes dY W and, as its U, dY B^T, and its
-// epilogue adds bf16(s dY B^T) A^T: the dX of the backward pass; the saved U,
-// scaled by s, is the G that dA needs. Same bits as the dX kernel (same MFMA
-// shapes, same reduction order). The dX kernel's loop is about as fast as this
-// GEMM, so the path pays only where the transposed dequantization (2.56 bytes per
-// weight) is small next to it: measured on MI355X, rank <= 16 from 8192 tokens
-// (4096 -> 4096: 301 -> 294 us per backward; 1024 -> 4096: 126 -> 116 us; the 70B
-// projections about 1 % faster), slower at rank 64 and at fewer tokens. d_out must
-// be whole 64-element steps.
-bool dx_dq_supported(int64_t T, int64_t K, int64_t N, int r) {
-  return T >= 8192 && r % 8 == 0 && r <= 16 && N % BK == 0 && fits_buffer(T, N, K) &&
-         tiled_split(T, N, K, r).splits == 1;
-}
-
-hipError_t launch_dx_dq(int T, int K, int N, int r, float s, const uint16_t* dy, const uint16_t* wt,
-                        const uint16_t* bt, const uint16_t* at, uint16_t* dx, uint16_t* g, hipStream_t stream) {
-  ProjTable tab{};
-  tab.n = 1;
-  tab.u_scale = s;
-  tab.N[0] = K;
-  tab.wdq[0] = wt;
-  tab.A[0] = bt;
-  tab.B[0] = at;
-  tab.y[0] = dx;
-  tab.u[0] = g;
-  const int bt_edge = fwd_tile_edge(T, (K + 255) / 256, (K + 127) / 128, r);
-  tab.tile_end[0] = (K + bt_edge - 1) / bt_edge;
-  return bt_edge == 256 ? launch_fwd_rank<256>(T, N, r, s, dy, tab, 1, N / BK, nullptr, nullptr, true, stream)
-                        : launch_fwd_rank<128>(T, N, r, s, dy, tab, 1, N / BK, nullptr, nullptr, true, stream);
 }
 
 }  // namespace lnf4

@@ -3,8 +3,9 @@
 // The pages keep the frozen base weight in 4-bit NF4 form ("Unsloth
 // acceleration principles: CUDA kernel fusion and memory optimization",
 // kernel-fusion section, load_in_4bit=True; "Reading the Unsloth changelog",
-// section 1.1). Both kernels are HBM-bound elementwise passes run once per
-// weight (quantize) or only for export / tests (dequantize).
+// section 1.1). Both kernels are HBM-bound elementwise passes: quantization runs
+// once per weight; dequantization to bf16 runs once per forward or backward call
+// at large token counts, where the tile kernels then read bf16 weight tiles.
 #include "device_common.h"
 #include "launch.h"
 
@@ -93,89 +94,7 @@ __global__ __launch_bounds__(256) void nf4_dequantize_kernel(const uint32_t* __r
   }
 }
 
-// Transposed dequantization: out [cols][rows] = deq(codes [rows][cols])^T, bf16,
-// each value rounded as in nf4_dequantize_kernel. Workgroup b < rt * ct takes the
-// 128 x 128 block (b % rt, b / rt). Thread t dequantizes rows 2p and 2p + 1 (p =
-// t % 64) over 32 columns (quarter t / 64: one 16-byte code load per row), stores
-// each (row 2p, row 2p + 1) pair as one dword of an LDS tile [128 columns][64
-// pairs] (a wave writes 256 consecutive bytes), and the tile leaves as 256-byte
-// runs of out rows. The workgroups after those transpose the two small [R][C]
-// 16-bit factors (tr_in / tr_out, R = tr_rows, C = tr_cols; 1024 elements per
-// workgroup) that travel with the weight.
-struct SmallTranspose {
-  const uint16_t* in[2];
-  uint16_t* out[2];
-  int rows[2], cols[2];
-};
-__global__ __launch_bounds__(256) void nf4_dequantize_t_kernel(const uint8_t* __restrict__ codes,
-                                                               const float* __restrict__ absmax,
-                                                               int rows, int cols, uint16_t* __restrict__ out,
-                                                               SmallTranspose tr) {
-  __shared__ float lut[16];
-  __shared__ __align__(16) uint32_t tile[128 * 64];
-  const int t = threadIdx.x, p = t & 63, kq = t >> 6;
-  const int rt = (rows + 127) / 128, nb = rt * ((cols + 127) / 128);
-  if (static_cast<int>(blockIdx.x) >= nb) {
-    int e = (static_cast<int>(blockIdx.x) - nb) * 1024 + t;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int R = tr.rows[h], C = tr.cols[h], n = R * C;
-      for (int i = 0; i < 4; ++i) {
-        const int j = e + 256 * i;  // out index (c, r) = (j / R, j % R); < 0: the other factor's
-        if (j >= 0 && j < n) {
-          const int c = j / R, r = j - c * R;
-          tr.out[h][j] = tr.in[h][r * C + c];
-        }
-      }
-      e -= (n + 1023) / 1024 * 1024;
-    }
-    return;
-  }
-  const int r0 = (static_cast<int>(blockIdx.x) % rt) * 128, c0 = (static_cast<int>(blockIdx.x) / rt) * 128;
-  if (t < 16) lut[t] = nf4_level(t);
-  const int ra = r0 + 2 * p, cbeg = c0 + kq * 32;
-  const int64_t k2 = cols / 2, kb = cols / 64;
-  uint4 cw[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-  float sc[2] = {0.f, 0.f};
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (cbeg < cols && ra + h < rows) {  // rows % 8 == 0: both rows of a pair exist or neither
-      cw[h] = *reinterpret_cast<const uint4*>(codes + (ra + h) * k2 + cbeg / 2);
-      sc[h] = absmax[(ra + h) * kb + cbeg / 64];
-    }
-  }
-  __syncthreads();  // lut
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t wa = q == 0 ? cw[0].x : q == 1 ? cw[0].y : q == 2 ? cw[0].z : cw[0].w;
-    const uint32_t wb = q == 0 ? cw[1].x : q == 1 ? cw[1].y : q == 2 ? cw[1].z : cw[1].w;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      tile[(kq * 32 + q * 8 + j) * 64 + p] =
-          pack_bf16x2(lut[(wa >> (4 * j)) & 15u] * sc[0], lut[(wb >> (4 * j)) & 15u] * sc[1]);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int lc = i * 16 + (t >> 4), ch = t & 15;
-    const int c = c0 + lc, r = r0 + ch * 8;
-    if (c < cols && r < rows)
-      *reinterpret_cast<uint4*>(out + static_cast<int64_t>(c) * rows + r) =
-          *reinterpret_cast<const uint4*>(tile + lc * 64 + ch * 4);
-  }
-}
-
 }  // namespace
-
-hipError_t launch_nf4_dequantize_t(const uint8_t* codes, const float* absmax, int rows, int cols,
-                                   uint16_t* out, const uint16_t* in0, int r0, int c0, uint16_t* out0,
-                                   const uint16_t* in1, int r1, int c1, uint16_t* out1, hipStream_t stream) {
-  SmallTranspose tr{{in0, in1}, {out0, out1}, {r0, r1}, {c0, c1}};
-  const int64_t nb = static_cast<int64_t>((rows + 127) / 128) * ((cols + 127) / 128) +
-                     (static_cast<int64_t>(r0) * c0 + 1023) / 1024 + (static_cast<int64_t>(r1) * c1 + 1023) / 1024;
-  nf4_dequantize_t_kernel<<<static_cast<unsigned>(nb), 256, 0, stream>>>(codes, absmax, rows, cols, out, tr);
-  return hipGetLastError();
-}
 
 hipError_t launch_nf4_quantize(const void* w, bool w_is_bf16, int64_t rows, int64_t cols,
                                uint8_t* codes, float* absmax, hipStream_t stream) {

@@ -1,20 +1,20 @@
 """Host logic of bench.py: turning per-dispatch counter rows into the forward's
 traffic (no GPU). From 1024 tokens a forward call is the weight's dequantization
-followed by the tile kernel; the same tile kernel also runs the backward's input
-gradient after the transposed dequantization and must not be counted as forward."""
+followed by the tile kernel; the backward's input gradient pairs the same
+dequantization with the dX tile kernel and must not be counted as forward."""
 import bench
 
 
 def _rows():
     # (dispatch id, kernel name, KiB): copy, then two steps of fwd (dequant + tile),
-    # bwd (transposed dequant + tile as dX, rank-r kernels)
+    # bwd (dequant + dX tile kernel, rank-r kernels)
     out = [(1, "void at::native::MulFunctor<float>", 512.0)]
     did = 2
     for _ in range(2):
         for name, v in (("void lnf4::nf4_dequantize_kernel<true>(unsigned int const*)", 40.0),
                         ("void lnf4::lora_fwd_kernel<256, 16, 16, true>(int)", 100.0),
-                        ("lnf4::nf4_dequantize_t_kernel(unsigned char const*)", 45.0),
-                        ("void lnf4::lora_fwd_kernel<256, 16, 16, true>(int)", 110.0),
+                        ("void lnf4::nf4_dequantize_kernel<true>(unsigned int const*)", 45.0),
+                        ("void lnf4::lora_dx_kernel<256, 16, 16, false, true>(int)", 110.0),
                         ("void lnf4::skinny_partial_kernel<32>(int)", 30.0),
                         ("lnf4::skinny_reduce2_kernel(float const*)", 2.0)):
             out.append((did, name, v))
@@ -25,7 +25,7 @@ def _rows():
 def test_forward_traffic_pairs_dequantization_with_its_tile_kernel():
     fwd, other = bench.forward_kib(_rows())
     assert fwd == 140.0                                  # 40 + 100, not the dX tile kernel
-    assert other["lora_dx (nf4_dequantize_t_kernel + lora_fwd_kernel)"] == 155.0
+    assert other["lora_dx (nf4_dequantize_kernel + lora_dx_kernel)"] == 155.0
     assert other["skinny_partial_kernel"] == 30.0 and other["skinny_reduce2_kernel"] == 2.0
     assert other["MulFunctor"] == 512.0
 

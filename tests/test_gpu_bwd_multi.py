@@ -6,7 +6,8 @@ Cases cover the fused path (every d_out a multiple of 64, T > 128: one dX
 launch over the concatenated d_out; for n r <= 64 one pass over x for every dA,
 wider sums in several epilogue passes and one dA pass per projection) with 2, 3
 and 4 projections and ranks 8 .. 64, ragged token counts and partial d_in
-tiles; and the per-projection path (a d_out not a multiple of 64, up to 128 tokens,
+tiles, from 1024 tokens on weights dequantized into the workspace; and the
+per-projection path (a d_out not a multiple of 64, up to 128 tokens,
 no dX). One case runs the Qwen-14B-shaped q/k/v at full size
 (8192 tokens, 5120 -> 5120 each, r = 16) and checks sampled rows of dX and
 sampled columns of dA and dB against the oracle.
@@ -58,6 +59,8 @@ CASES = [
     (260, 256, (128, 64, 64), 64, True, True),      # fused, rank 64 q/k/v-like: n r = 192
     (200, 128, (64, 64, 64), 32, False, True),      # fused, n r = 96, U recomputed
     (300, 256, (256, 64, 64), 16, True, False),     # fused, dX not requested
+    (1100, 320, (128, 64, 64), 16, True, True),     # fused, dX on the dequantized weights (128 tiles)
+    (4100, 256, (128, 64, 64), 64, False, True),    # the same at rank 64, U recomputed
 ]
 
 
@@ -85,6 +88,20 @@ def test_bwd_multi_matches_oracle(q, T, K, Ns, r, with_u, with_dx):
         assert olora.rel_err(host_f64(dx), dx_ref) <= TOL
     else:
         assert dx is None
+
+
+def test_bwd_multi_dx_dequantized_matches_in_loop(q):
+    """From 1024 tokens (128 x 128 tiles) the fused dX reads weights dequantized
+    into the workspace; rows 0 .. 1022 match the in-loop path at 1023 tokens bit
+    for bit (rows are independent, the summation order is the same)."""
+    T, K, Ns, r = 1100, 320, (128, 64, 64), 16
+    ins = [synth.custom_inputs(40 + g, T, K, N, r, dy_std=0.1) for g, N in enumerate(Ns)]
+    x, codes, absmax, A, B, dy = _dev_inputs(q, ins)
+    dx, _, _ = q.lora_nf4_bwd_multi(x, dy, codes, absmax, A, B, 16.0)
+    dx1, _, _ = q.lora_nf4_bwd_multi(x[:1023].contiguous(), [d[:1023].contiguous() for d in dy], codes, absmax,
+                                     A, B, 16.0)
+    torch.cuda.synchronize()
+    assert torch.equal(dx[:1023], dx1)
 
 
 def test_bwd_multi_empty_batch(q):

@@ -158,11 +158,10 @@ def test_forward_dequantized_matches_in_loop(q, T, K, N, r):
     assert olora.rel_err(host_f64(u), u_ref) <= TOL
 
 
-# From 8192 tokens at rank <= 16 with d_out a multiple of 64, the backward takes dX
-# through the forward's kernels: the weight dequantized transposed into the
-# workspace, x = dY, A = B^T, B = A^T; the saved U, scaled by s, is G. Ragged T
-# and d_in, one to eight d_out steps, both rank blocks it takes; the full oracle
-# on every output.
+# From 4096 tokens on 256 x 256 dX tiles (1024 on 128 x 128 tiles) the dX kernel
+# runs on the weight dequantized once into the workspace. Large token counts,
+# ragged T and d_in, one to eight d_out steps, ranks 8 and 16; the full oracle on
+# every output.
 DQ_BWD = [(8200, 320, 192, 16), (8230, 192, 128, 8), (9000, 128, 64, 16), (8300, 448, 512, 16)]
 
 
@@ -170,6 +169,26 @@ DQ_BWD = [(8200, 320, 192, 16), (8230, 192, 128, 8), (9000, 128, 64, 16), (8300,
 def test_backward_dequantized(q, T, K, N, r):
     inp = synth.custom_inputs(13, T, K, N, r)
     _check_full(q, inp, 16.0, r, f"dq-bwd T={T} K={K} N={N} r={r}")
+
+
+# The same path against the in-loop dequantization: rows of dX are independent,
+# so rows 0 .. T_in - 1 match, bit for bit, a call at T_in tokens, just under the
+# threshold on the same tile edge. Ragged d_in and d_out, ranks 16 .. 64; the
+# full oracle on every output.
+DQX = [(1100, 4160, 200, 24, 1023), (4100, 4096, 192, 64, 4095), (4096, 4160, 136, 16, 4095)]
+
+
+@pytest.mark.parametrize("T,K,N,r,T_in", DQX)
+def test_dx_dequantized_matches_in_loop(q, T, K, N, r, T_in):
+    from tests.gpu_util import dev_bf16
+    inp = synth.custom_inputs(14, T, K, N, r, dy_std=0.1)
+    x, W, A, B, dY = (dev_bf16(inp[k]) for k in ("x", "W", "A", "B", "dY"))
+    codes, absmax = q.nf4_quantize(W)
+    dx, _, _ = q.lora_nf4_bwd(x, dY, codes, absmax, A, B, 16.0)
+    dx1, _, _ = q.lora_nf4_bwd(x[:T_in].contiguous(), dY[:T_in].contiguous(), codes, absmax, A, B, 16.0)
+    torch.cuda.synchronize()
+    assert torch.equal(dx[:T_in], dx1)
+    _check_full(q, inp, 16.0, r, f"dqx T={T} K={K} N={N} r={r}")
 
 
 @pytest.mark.parametrize("r", [16, 64])
