@@ -155,6 +155,21 @@ def test_fwd_multi_validation(lib):
     assert _fwd_multi(lib, T=64, ws=y0) == LN_EALIAS                  # workspace on top of y[0]
 
 
+def test_bwd_workspace_holds_the_dequantized_weight_at_large_token_counts(lib):
+    """dX runs on a bf16 copy of the weight from 1024 tokens on 128 x 128 tiles and
+    from 4096 on 256 x 256 tiles (q_proj 4096 x 4096 takes 128 tiles at 1024 tokens
+    and 256 at 4095 and 4096): the workspace grows by at least 2 d_in d_out bytes
+    across each threshold."""
+    K = N = 4096
+    w = 2 * K * N
+    for r in (16, 64):
+        assert lib.lora_nf4_bwd_workspace_bytes(1023, K, N, r) < w
+        assert lib.lora_nf4_bwd_workspace_bytes(1024, K, N, r) - lib.lora_nf4_bwd_workspace_bytes(1023, K, N, r) >= w
+        assert lib.lora_nf4_bwd_workspace_bytes(4095, K, N, r) < w
+        assert lib.lora_nf4_bwd_workspace_bytes(4096, K, N, r) - lib.lora_nf4_bwd_workspace_bytes(4095, K, N, r) >= w
+        assert lib.lora_nf4_bwd_workspace_bytes(8192, K, N, r) >= w
+
+
 def test_bwd_validation_and_workspace(lib):
     T, K, N, r = 8, 64, 64, 8
     need = lib.lora_nf4_bwd_workspace_bytes(T, K, N, r)
