@@ -33,6 +33,9 @@
 //     dequantization would be repeated that many times per weight element: the
 //     call then dequantizes the weight once into the workspace (bf16, the same
 //     values) and the kernel stages bf16 weight tiles like x (DQ instances).
+//     There, from 4096 tokens at rank > 16, U = x A comes from a separate pass
+//     and the tile kernel (RU = 0) only reads bf16(s U) in its epilogue: the
+//     in-loop U is recomputed by every column tile.
 //   * Several projections of the same x (q/k/v or gate/up: the multi-projection
 //     fusion) share one launch: the column tiles of all projections form one
 //     grid, each tile reads its projection's weight, A, B and output from a small
@@ -69,6 +72,7 @@ struct ProjTable {
   const uint8_t* codes[kMaxProj];
   const float* absmax[kMaxProj];
   const uint16_t* wdq[kMaxProj];  // bf16 [N][K] dequantized weight (DQ kernels only)
+  const uint16_t* usg[kMaxProj];  // bf16(s U) [T][r] from the U pass (RU = 0 kernels only)
   const uint16_t* A[kMaxProj];
   const uint16_t* B[kMaxProj];
   uint16_t* y[kMaxProj];
@@ -103,8 +107,8 @@ __global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) voi
   __shared__ __align__(16) uint16_t xs1[kTileElems];
   __shared__ __align__(16) uint16_t ws0[kTileElems];
   __shared__ __align__(16) uint16_t ws1[kTileElems];
-  __shared__ __align__(16) uint16_t as0[RU * kAStride];
-  __shared__ __align__(16) uint16_t as1[RU * kAStride];
+  __shared__ __align__(16) uint16_t as0[RU > 0 ? RU * kAStride : 8];
+  __shared__ __align__(16) uint16_t as1[RU > 0 ? RU * kAStride : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Tl::kWN, wn = wave % Tl::kWN;  // 2 x kWN waves, BT / 2 x 64 each
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) voi
   constexpr int kAPer = (64 * RU / 8 + kThreads - 1) / kThreads;
   // Register sets for step s live in slot s & 1, so the prefetch of step kt + 2
   // and the dequantization of step kt + 1 use different registers with no copies.
-  uint4 creg[2], areg[2][kAPer];
+  uint4 creg[2], areg[2][kAPer > 0 ? kAPer : 1];
   float sreg[2];
   auto load_codes = [&](int kt, int slot) {
     creg[slot] = buf_load16(rs_c, cvoff, kt * 32);
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) voi
   // Thread c < 8 r owns 8 consecutive j of one k of the A slice (r % 8 == 0) and
   // writes them transposed: rows j0 .. j0 + 7 of the padded A^T tile, one address
   // register plus immediate row offsets.
-  int a_dst[kAPer];
+  int a_dst[kAPer > 0 ? kAPer : 1];
 #pragma unroll
   for (int i = 0; i < kAPer; ++i) {
     const int c = tid + kThreads * i, e = c * 8, kk = e / r, j0 = e - kk * r;
@@ -477,6 +481,15 @@ __global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) voi
           u_save[static_cast<size_t>(m0 + row) * r + l16] = to_bf16(uv);
       }
   }
+  if constexpr (RU == 0) {  // bf16(s U) of this tile's rows, written by the U pass
+    const uint16_t* ug = tab.usg[gp];
+    for (int e = tid; e < BT * (RE / 8); e += kThreads) {
+      const int row = e / (RE / 8), c8 = 8 * (e - row * (RE / 8));
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (c8 < r && m0 + row < T) v = *reinterpret_cast<const uint4*>(ug + static_cast<size_t>(m0 + row) * r + c8);
+      *reinterpret_cast<uint4*>(us + ep(row, c8)) = v;
+    }
+  }
   for (int e = tid; e < BT * RE; e += kThreads) {
     const int j = e / BT, c = e % BT;
     bt[ep(c, j)] = (j < r && n0 + c < N) ? B[static_cast<size_t>(j) * N + n0 + c] : uint16_t(0);
@@ -531,6 +544,101 @@ hipError_t launch_fwd_rank(int T, int K, int r, float s, const uint16_t* x, cons
     case 3: return launch_fwd_t<BT, 64, 48>(T, K, r, s, x, tab, splits, steps_per, part, upart, dq, stream);
     default: return launch_fwd_t<BT, 64, 64>(T, K, r, s, x, tab, splits, steps_per, part, upart, dq, stream);
   }
+}
+
+// U = x A on its own, for the large-token forward at rank > 16 (the tile kernel
+// then takes RU = 0 and reads bf16(s U) in its epilogue): the in-loop U is
+// recomputed by every column tile, which at rank 32 / 64 costs 15 / 24 % of the
+// loop. One workgroup per 32 token rows; wave w accumulates d_in quarter w with
+// 32 x 32 x 16 MFMAs straight from global memory (x rows and rows of A^T, 16 bytes
+// per lane), and wave 0 adds the four partials in a fixed order. Rows past T and
+// rank rows past r lie outside the buffer ranges and read zeros.
+template <int RU>
+__global__ __launch_bounds__(256) void lora_u_pass_kernel(int T, int K, int r, float s,
+                                                          const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ at,
+                                                          uint16_t* __restrict__ us_out,
+                                                          uint16_t* __restrict__ u_save) {
+  constexpr int NU = RU / 32;
+  __shared__ float red[3 * NU * 16 * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, lh = lane >> 5;
+  const int m0 = blockIdx.x * 32;
+  const int rows = min(T - m0, 32);
+  const int kq = K / 4;  // d_in % 64 == 0: whole 16-wide slices per wave
+  const auto rs_x = make_rsrc(x + static_cast<size_t>(m0) * K, static_cast<uint32_t>(rows) * K * 2);
+  const auto rs_a = make_rsrc(at, static_cast<uint32_t>(r) * K * 2);
+  const uint32_t xoff = static_cast<uint32_t>(l32) * K * 2 + (wave * kq + 8 * lh) * 2;
+  uint32_t aoff[NU];
+  f32x16_t acc[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    aoff[u] = static_cast<uint32_t>(u * 32 + l32) * K * 2 + (wave * kq + 8 * lh) * 2;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[u][e] = 0.f;
+  }
+#pragma unroll 8
+  for (int k = 0; k < kq; k += 16) {
+    const uint4 xa = buf_load16(rs_x, xoff, k * 2);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) acc[u] = mfma32(xa, buf_load16(rs_a, aoff[u], k * 2), acc[u]);
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[(((wave - 1) * NU + u) * 16 + e) * 64 + lane] = acc[u][e];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float v = acc[u][e] + red[((0 * NU + u) * 16 + e) * 64 + lane] + red[((1 * NU + u) * 16 + e) * 64 + lane] +
+                      red[((2 * NU + u) * 16 + e) * 64 + lane];
+      const int row = m0 + mfma32_row(e, lane), col = u * 32 + l32;
+      if (row < T && col < r) {
+        us_out[static_cast<size_t>(row) * r + col] = to_bf16(s * v);
+        if (u_save != nullptr) u_save[static_cast<size_t>(row) * r + col] = to_bf16(v);
+      }
+    }
+}
+
+// at [r][K] = A^T (A [K][r]), one element per thread.
+__global__ __launch_bounds__(256) void transpose_a_kernel(const uint16_t* __restrict__ a, int K, int r,
+                                                          uint16_t* __restrict__ at) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(K) * r) return;
+  const int j = static_cast<int>(i / K), k = static_cast<int>(i - static_cast<int64_t>(j) * K);
+  at[i] = a[static_cast<size_t>(k) * r + j];
+}
+
+hipError_t launch_u_pass(int T, int K, int r, float s, const uint16_t* x, const uint16_t* A, uint16_t* at,
+                         uint16_t* us_out, uint16_t* u_save, hipStream_t stream) {
+  const int64_t n = static_cast<int64_t>(K) * r;
+  transpose_a_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(A, K, r, at);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned grid = static_cast<unsigned>((T + 31) / 32);
+  if (r <= 32)
+    lora_u_pass_kernel<32><<<grid, 256, 0, stream>>>(T, K, r, s, x, at, us_out, u_save);
+  else
+    lora_u_pass_kernel<64><<<grid, 256, 0, stream>>>(T, K, r, s, x, at, us_out, u_save);
+  return hipGetLastError();
+}
+
+// The DQ tile kernel with U from the U pass (RU = 0), epilogue width by rank.
+template <int BT>
+hipError_t launch_fwd_ug(int T, int K, int r, float s, const uint16_t* x, const ProjTable& tab, hipStream_t stream) {
+  const int tiles = ((T + BT - 1) / BT) * tab.tile_end[tab.n - 1];
+  const int steps = K / BK;
+  constexpr int kT = FwdTile<BT>::kThreads;
+  switch ((r + 15) / 16) {
+    case 2: lora_fwd_kernel<BT, 0, 32, true><<<tiles, kT, 0, stream>>>(T, K, r, s, x, tab, steps, nullptr, nullptr); break;
+    case 3: lora_fwd_kernel<BT, 0, 48, true><<<tiles, kT, 0, stream>>>(T, K, r, s, x, tab, steps, nullptr, nullptr); break;
+    default: lora_fwd_kernel<BT, 0, 64, true><<<tiles, kT, 0, stream>>>(T, K, r, s, x, tab, steps, nullptr, nullptr); break;
+  }
+  return hipGetLastError();
 }
 
 // Tile edge from a round count: a grid of 256 x 256 tiles runs in rounds of 256
@@ -589,8 +697,18 @@ TiledSplit tiled_split(int64_t T, int64_t K, int64_t N, int r) {
 // +-5 % either way. Same values: the dequantization rounds exactly as the in-loop
 // one.
 bool fwd_dq(int64_t T, int bt) { return T >= (bt == 256 ? 4096 : 1024); }
-size_t dq_bytes(int64_t K, int64_t N) {
-  return (static_cast<size_t>(N) * K * 2 + 255) & ~static_cast<size_t>(255);
+// Rank > 16 on that path from 4096 tokens also takes the U pass (A^T [r][K] and
+// bf16(s U) [T][r] follow each projection's weight in the workspace). Measured on
+// MI355X, forward at 8192 tokens, in-loop U -> U pass: 4096 -> 4096 r = 32
+// 288 -> 270 us, r = 64 338 -> 290 us; 4096 -> 14336 r = 64 1172 -> 925 us;
+// 4096 -> 1024 r = 64 145 -> 134 us. At 2048 tokens it is even and at 1024 slower
+// (72 -> 84 us at r = 32): the U pass runs T / 32 workgroups.
+bool fwd_ug(int64_t T, int r) { return r > 16 && T >= 4096; }
+size_t dq_bytes(int64_t T, int64_t K, int64_t N, int r) {
+  const auto al = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
+  size_t b = al(static_cast<size_t>(N) * K * 2);
+  if (fwd_ug(T, r)) b += al(static_cast<size_t>(r) * K * 2) + al(static_cast<size_t>(T) * r * 2);
+  return b;
 }
 
 size_t tiled_split_bytes(int64_t T, int64_t N, int r, int splits) {
@@ -618,15 +736,24 @@ hipError_t launch_fwd_table(int T, int K, int r, float s, const uint16_t* x, Pro
   if (tab.n == 1 && workspace != nullptr) sp = tiled_split(T, K, tab.N[0], r);
   // the weights of every projection dequantized one after another into the workspace
   const bool dq = workspace != nullptr && sp.splits == 1 && fwd_dq(T, bt);
+  const bool ug = dq && fwd_ug(T, r);
   if (dq) {
     unsigned char* w = static_cast<unsigned char*>(workspace);
     for (int g = 0; g < tab.n; ++g) {
-      const hipError_t e = launch_nf4_dequantize(tab.codes[g], tab.absmax[g], tab.N[g], K, true, w, stream);
+      hipError_t e = launch_nf4_dequantize(tab.codes[g], tab.absmax[g], tab.N[g], K, true, w, stream);
       if (e != hipSuccess) return e;
       tab.wdq[g] = reinterpret_cast<const uint16_t*>(w);
-      w += dq_bytes(K, tab.N[g]);
+      if (ug) {
+        uint16_t* at = reinterpret_cast<uint16_t*>(w + ((static_cast<size_t>(tab.N[g]) * K * 2 + 255) & ~size_t(255)));
+        uint16_t* usg = at + (((static_cast<size_t>(r) * K * 2 + 255) & ~size_t(255)) / 2);
+        e = launch_u_pass(T, K, r, s, x, tab.A[g], at, usg, tab.u[g], stream);
+        if (e != hipSuccess) return e;
+        tab.usg[g] = usg;
+      }
+      w += dq_bytes(T, K, tab.N[g], r);
     }
   }
+  if (ug) return bt == 256 ? launch_fwd_ug<256>(T, K, r, s, x, tab, stream) : launch_fwd_ug<128>(T, K, r, s, x, tab, stream);
   float* part = nullptr;
   float* upart = nullptr;
   if (sp.splits > 1) {
@@ -669,7 +796,7 @@ size_t fwd_workspace_bytes(int64_t T, int64_t K, int64_t N, int r) {
     return plan_fwd_splitk(static_cast<int>(T), static_cast<int>(K), static_cast<int>(N), r).bytes;
   if (r % 8 != 0 || r > 64 || !fits_buffer(T, K, N) || lora_fwd_stream_supported(T, r)) return 0;
   const TiledSplit ts = tiled_split(T, K, N, r);
-  if (ts.splits == 1 && fwd_dq(T, ts.bt)) return dq_bytes(K, N);
+  if (ts.splits == 1 && fwd_dq(T, ts.bt)) return dq_bytes(T, K, N, r);
   return tiled_split_bytes(T, N, r, ts.splits);
 }
 
@@ -687,7 +814,7 @@ int table_edge(int64_t T, int n_proj, const int* N, int r) {
 size_t fwd_multi_workspace_bytes(int64_t T, int64_t K, int n_proj, const int* N, int r) {
   if (fwd_multi_tiled(T, K, n_proj, N, r)) {
     size_t b = 0;
-    for (int g = 0; fwd_dq(T, table_edge(T, n_proj, N, r)) && g < n_proj; ++g) b += dq_bytes(K, N[g]);
+    for (int g = 0; fwd_dq(T, table_edge(T, n_proj, N, r)) && g < n_proj; ++g) b += dq_bytes(T, K, N[g], r);
     return b;
   }
   size_t b = 0;

@@ -158,6 +158,20 @@ def test_forward_dequantized_matches_in_loop(q, T, K, N, r):
     assert olora.rel_err(host_f64(u), u_ref) <= TOL
 
 
+# From 4096 tokens at rank > 16 the dequantize-then-GEMM forward takes U = x A
+# from a separate pass (d_in split over four waves, fixed-order sum; the tile
+# kernel reads bf16(s U) in its epilogue): ranks 24 (half the 32-wide block), 40
+# and 64, ragged T, d_in and d_out; the full oracle on every output.
+UPASS = [(4100, 320, 200, 64), (4130, 192, 136, 24), (4096, 448, 72, 40)]
+
+
+@pytest.mark.parametrize("T,K,N,r", UPASS)
+def test_forward_u_pass(q, T, K, N, r):
+    inp = synth.custom_inputs(15, T, K, N, r)
+    assert q.lora_nf4_fwd_workspace_bytes(T, K, N, r) >= K * N * 2 + T * r * 2
+    _check_full(q, inp, 16.0, r, f"u-pass T={T} K={K} N={N} r={r}")
+
+
 # From 4096 tokens on 256 x 256 dX tiles (1024 on 128 x 128 tiles) the dX kernel
 # runs on the weight dequantized once into the workspace. Large token counts,
 # ragged T and d_in, one to eight d_out steps, ranks 8 and 16; the full oracle on
