@@ -54,8 +54,8 @@ typedef enum {
     LN_OK = 0,
     LN_EINVAL = -1,      /* null pointer, negative T or other size < 1, non-finite
                             alpha, unknown dtype                                    */
-    LN_ESHAPE = -2,      /* d_in or cols not a multiple of 64, d_out not a multiple
-                            of 8, or a size beyond the 2^31 element-index range     */
+    LN_ESHAPE = -2,      /* d_in or cols not a multiple of 64, or a size beyond the
+                            2^31 element-index range                                */
     LN_EALIGN = -3,      /* a data pointer is not 16-byte aligned                    */
     LN_ERANK = -4,       /* r < 1 or r > LN_MAX_RANK                                 */
     LN_EWORKSPACE = -5,  /* workspace null or smaller than the entry point's *_workspace_bytes */
@@ -65,7 +65,7 @@ typedef enum {
 
 typedef enum { LN_F32 = 0, LN_BF16 = 1 } ln_dtype;
 
-#define LN_MAX_RANK 128
+#define LN_MAX_RANK 256
 #define LN_MAX_PROJ 8   /* projections per lora_nf4_fwd_multi / lora_nf4_bwd_multi call */
 
 /*
@@ -106,7 +106,9 @@ int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows, int6
  *            runs 256 x 256 tiles), where the weight is dequantized once into it
  *            (bf16 [d_out, d_in]: 2 d_in d_out bytes, the same values the fused
  *            kernels produce); when it is 0 the workspace may be NULL.
- * T >= 0, d_in % 64 == 0, d_out % 8 == 0, 1 <= r <= LN_MAX_RANK. s = lora_alpha / r
+ * T >= 0, d_in % 64 == 0, d_out >= 1 (any; a d_out that is not a multiple of 8, and
+ * ranks r % 8 != 0 or r > 64, run the generic 128 x 128 kernels: same results,
+ * lower speed), 1 <= r <= LN_MAX_RANK. s = lora_alpha / r
  * is formed in float32 on the host. T = 0 is an empty batch: nothing is computed
  * and x, y, u_save and the workspace may be NULL. LN_EWORKSPACE if the workspace
  * is needed and NULL or too small; the workspace must not overlap any operand.
@@ -132,7 +134,7 @@ size_t lora_nf4_fwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int3
  * then read once per token tile for all of them; narrow projections such as
  * k/v at d_out = 1024 no longer leave most of the GPU idle).
  *   n_proj               1 .. LN_MAX_PROJ
- *   d_out                HOST array [n_proj]: d_out of each projection (% 8 == 0)
+ *   d_out                HOST array [n_proj]: d_out of each projection (>= 1)
  *   w_codes, w_absmax,
  *   A, B, y              HOST arrays [n_proj] of DEVICE pointers, each laid out as
  *                        for lora_nf4_fwd with that projection's d_out
@@ -194,7 +196,7 @@ int lora_nf4_bwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_a
  * runs over the projections' concatenated d_out (no per-projection dX in HBM)
  * and one pass over x yields every dA; otherwise the projections run one after
  * another and dX accumulates (float32 add of bf16 partial results).
- *   n_proj             1 .. LN_MAX_PROJ;  d_out  HOST array [n_proj] (% 8 == 0)
+ *   n_proj             1 .. LN_MAX_PROJ;  d_out  HOST array [n_proj] (>= 1)
  *   dy, w_codes, w_absmax, A, B, dA, dB
  *                      HOST arrays [n_proj] of DEVICE pointers, laid out as for
  *                      lora_nf4_bwd with that projection's d_out

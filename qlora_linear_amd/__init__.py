@@ -38,7 +38,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "liblora_nf4.so")
 
 LN_OK, LN_F32, LN_BF16 = 0, 0, 1
-LN_MAX_RANK = 128
+LN_MAX_RANK = 256
 LN_MAX_PROJ = 8
 EXPORTED_SYMBOLS = ("nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_fwd_multi",
                     "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_merge",

@@ -41,7 +41,7 @@ int check_linear_shape(int64_t T, int64_t K, int64_t N, int32_t r, float alpha) 
   if (T < 0 || K < 1 || N < 1) return LN_EINVAL;
   if (!std::isfinite(alpha)) return LN_EINVAL;
   if (r < 1 || r > LN_MAX_RANK) return LN_ERANK;
-  if (K % 64 != 0 || N % 8 != 0) return LN_ESHAPE;
+  if (K % 64 != 0) return LN_ESHAPE;
   if (T > kMaxDim || K > kMaxDim || N > kMaxDim) return LN_ESHAPE;
   return LN_OK;
 }
@@ -56,7 +56,7 @@ const char* lora_nf4_status_string(int status) {
   switch (status) {
     case LN_OK: return "ok";
     case LN_EINVAL: return "invalid argument (null pointer, negative T or other size < 1, non-finite alpha or unknown dtype)";
-    case LN_ESHAPE: return "unsupported shape (d_in/cols must be a multiple of 64, d_out a multiple of 8, sizes below 2^31)";
+    case LN_ESHAPE: return "unsupported shape (d_in/cols must be a multiple of 64, sizes below 2^31)";
     case LN_EALIGN: return "data pointer not 16-byte aligned (workspace: 256-byte)";
     case LN_ERANK: return "LoRA rank r outside [1, LN_MAX_RANK]";
     case LN_EWORKSPACE: return "workspace missing or smaller than the entry point's *_workspace_bytes()";

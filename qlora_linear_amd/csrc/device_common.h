@@ -83,6 +83,19 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// Eight consecutive bf16 values from global memory, of which only the first n
+// (>= 1) exist; the rest read as zero. For rows whose length is not a multiple of
+// 8 (no 16-byte alignment, and a full piece would run into the next row).
+__device__ __forceinline__ uint4 load8_masked(const uint16_t* p, int n) {
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t lo = 2 * q < n ? p[2 * q] : 0u, hi = 2 * q + 1 < n ? p[2 * q + 1] : 0u;
+    w[q] = lo | (hi << 16);
+  }
+  return uint4{w[0], w[1], w[2], w[3]};
+}
+
 // ---- buffer resources (raw buffers: byte offsets, out-of-range loads return 0) ----
 // The range check compares voffset + soffset (+ the instruction offset) against
 // the descriptor's byte count, so a run-ahead load that a uniform soffset pushes

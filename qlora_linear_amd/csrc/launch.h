@@ -141,13 +141,19 @@ hipError_t launch_lora_dx_splitk(int T, int K, int N, int r, float s, const uint
                                  const uint16_t* B, uint16_t* dx, uint16_t* g_out, float* part_x,
                                  float* part_g, hipStream_t stream);
 
-// Buffer resources address at most 2^31 - 1 bytes; the 256 x 256 kernels are
-// used only when every operand they cover fits.
+// The tiled, few-token and rank-r-gradient kernels address operands through
+// buffer resources (at most 2^31 - 1 bytes) and move rows of d_out elements in
+// 16-byte pieces: they are used only when every operand they cover fits and
+// d_out % 8 == 0. Other shapes take the generic kernels.
 inline bool fits_buffer(int64_t T, int64_t K, int64_t N) {
   const int64_t lim = (int64_t(1) << 31) - 1;
-  return T * K * 2 < lim && T * N * 2 < lim && N * K / 2 < lim && N * (K / 64) * 4 < lim &&
+  return N % 8 == 0 && T * K * 2 < lim && T * N * 2 < lim && N * K / 2 < lim && N * (K / 64) * 4 < lim &&
          K * 128 * 2 < lim && N * 64 * 2 < lim;
 }
+
+// 16-column rank tiles of the generic kernels' instances: every count up to 8
+// (r <= 128), then 12 (r <= 192) and 16 (r <= 256).
+inline int generic_rank_tiles(int r) { return r <= 128 ? (r + 15) / 16 : (r <= 192 ? 12 : 16); }
 
 // Rank-r gradients dA, dB in one launch plus one reduce (ranks % 8 == 0, <= 64):
 // dA = x^T G over K columns with G [T][ra] at row stride vsa (>= ra: a column

@@ -34,7 +34,8 @@ struct DxCfg {
   static constexpr int TM = WM / 16, TN = WN / 16;
   static constexpr int RP = ((RT * 16 + 31) / 32) * 32;
   static constexpr int UT = (RT + 1) / 2;
-  static constexpr int ES = RP + 8;
+  static constexpr int EC = RP < 64 ? RP : 64;  // rank columns per epilogue pass
+  static constexpr int ES = EC + 8;
   static constexpr int SX = (BM * (ES > kLds ? ES : kLds));
   static constexpr int SW = (BN * (ES > kLds ? ES : kLds));
   static constexpr int KPW = BN / 4;  // weight columns (k) dequantized per wave per step
@@ -74,23 +75,30 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
   }
 
   const int NS = (N + kBK - 1) / kBK;
+  const bool vec = (N & 7) == 0;
   for (int ns = 0; ns < NS; ++ns) {
     const int n0 = ns * kBK;
     __syncthreads();
     // dY tile [BM x 64]
+    // (16-byte loads when d_out % 8 == 0; otherwise rows are not 16-byte aligned and
+    // the last chunk of a row would run into the next, so element by element)
     for (int c = tid; c < BM * 8; c += kThreads) {
       const int row = c >> 3, ch = c & 7;
       uint4 v = {0u, 0u, 0u, 0u};
-      if (m0 + row < T && n0 + ch * 8 < N)
-        v = *reinterpret_cast<const uint4*>(dy + static_cast<size_t>(m0 + row) * N + n0 + ch * 8);
+      if (m0 + row < T && n0 + ch * 8 < N) {
+        const uint16_t* src = dy + static_cast<size_t>(m0 + row) * N + n0 + ch * 8;
+        v = vec ? *reinterpret_cast<const uint4*>(src) : load8_masked(src, N - n0 - ch * 8);
+      }
       *reinterpret_cast<uint4*>(dys + row * kLds + ch * 8) = v;
     }
     // B slice [r x 64] (rows of B are contiguous in n)
     for (int c = tid; c < RT * 16 * 8; c += kThreads) {
       const int j = c >> 3, ch = c & 7;
       uint4 v = {0u, 0u, 0u, 0u};
-      if (j < r && n0 + ch * 8 < N)
-        v = *reinterpret_cast<const uint4*>(B + static_cast<size_t>(j) * N + n0 + ch * 8);
+      if (j < r && n0 + ch * 8 < N) {
+        const uint16_t* src = B + static_cast<size_t>(j) * N + n0 + ch * 8;
+        v = vec ? *reinterpret_cast<const uint4*>(src) : load8_masked(src, N - n0 - ch * 8);
+      }
       *reinterpret_cast<uint4*>(bs + j * kLds + ch * 8) = v;
     }
     // weight tile: lane = row n (64 rows), wave = a run of KPW columns k;
@@ -146,51 +154,66 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
     }
   }
 
-  // ---- epilogue: acc += bf16(G) A^T, G = s dY B^T ----------------------------------
-  __syncthreads();
-  uint16_t* gs = dys;  // [BM][ES]
-  uint16_t* at = ds;   // [BN][ES]: rows k, rank contiguous (A is [K, r] row-major)
+  // ---- epilogue: acc += bf16(G) A^T, G = s dY B^T, EC rank columns per pass --------
+  if (tk == 0) {
 #pragma unroll
-  for (int u = 0; u < C::UT; ++u) {
-    const int jt = 2 * u + wn;
-    if (jt < RT) {
+    for (int u = 0; u < C::UT; ++u) {
+      const int jt = 2 * u + wn;
+      if (jt < RT) {
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = wm * C::WM + i * 16 + lq * 4 + e, col = jt * 16 + l16;
+            if (col < r && m0 + row < T) g_out[static_cast<size_t>(m0 + row) * r + col] = to_bf16(s * gacc[i][u][e]);
+          }
+      }
+    }
+  }
+  if (dx == nullptr) return;
+  uint16_t* gs = dys;  // [BM][ES]: bf16(G) columns c0 .. c0 + EC - 1, zero past the rank
+  uint16_t* at = ds;   // [BN][ES]: rows k, the same rank columns (A is [K, r] row-major)
+#pragma unroll
+  for (int c0 = 0; c0 < C::RP; c0 += C::EC) {
+    __syncthreads();  // the previous pass (or the K-loop) is done with dys and ds
+#pragma unroll
+    for (int u = 0; u < C::UT; ++u) {
+      const int jt = 2 * u + wn;
+      if (jt < RT && jt * 16 >= c0 && jt * 16 < c0 + C::EC) {
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = wm * C::WM + i * 16 + lq * 4 + e;
+            gs[row * C::ES + jt * 16 - c0 + l16] = to_bf16(s * gacc[i][u][e]);
+          }
+      }
+    }
+    const int tail = (RT * 16 > c0 && RT * 16 < c0 + C::EC) ? c0 + C::EC - RT * 16 : 0;
+    for (int e = tid; e < BM * tail; e += kThreads) {
+      const int row = e / tail, col = RT * 16 - c0 + (e - row * tail);
+      gs[row * C::ES + col] = 0;
+    }
+    for (int e = tid; e < BN * C::EC; e += kThreads) {
+      const int c = e / C::EC, j = e - c * C::EC;
+      at[c * C::ES + j] = (c0 + j < r && k0 + c < K) ? A[static_cast<size_t>(k0 + c) * r + c0 + j] : uint16_t(0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < C::EC / 32; ++ks) {
+      const int kc = ks * 32 + lq * 8;
+      uint4 af[C::TM], bfr[C::TN];
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+        af[i] = *reinterpret_cast<const uint4*>(gs + (wm * C::WM + i * 16 + l16) * C::ES + kc);
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        bfr[j] = *reinterpret_cast<const uint4*>(at + (wn * C::WN + j * 16 + l16) * C::ES + kc);
 #pragma unroll
       for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = wm * C::WM + i * 16 + lq * 4 + e, col = jt * 16 + l16;
-          const uint16_t gv = to_bf16(s * gacc[i][u][e]);
-          gs[row * C::ES + col] = gv;
-          if (tk == 0 && col < r && m0 + row < T) g_out[static_cast<size_t>(m0 + row) * r + col] = gv;
-        }
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
     }
-  }
-  constexpr int PADC = C::RP - RT * 16;
-  if (PADC > 0)
-    for (int e = tid; e < BM * PADC; e += kThreads) {
-      const int row = e / PADC, col = RT * 16 + (e - row * PADC);
-      gs[row * C::ES + col] = 0;
-    }
-  for (int e = tid; e < BN * C::RP; e += kThreads) {
-    const int c = e / C::RP, j = e - c * C::RP;
-    at[c * C::ES + j] = (j < r && k0 + c < K) ? A[static_cast<size_t>(k0 + c) * r + j] : uint16_t(0);
-  }
-  __syncthreads();
-  if (dx == nullptr) return;
-#pragma unroll
-  for (int ks = 0; ks < C::RP / 32; ++ks) {
-    const int kc = ks * 32 + lq * 8;
-    uint4 af[C::TM], bfr[C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-      af[i] = *reinterpret_cast<const uint4*>(gs + (wm * C::WM + i * 16 + l16) * C::ES + kc);
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-      bfr[j] = *reinterpret_cast<const uint4*>(at + (wn * C::WN + j * 16 + l16) * C::ES + kc);
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
   }
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
@@ -253,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void lora_u_kernel(int T, int K, int r,
 }
 
 // partial[split][c][j] = sum over the split's token range of M[t][c] * V[t][j].
-// M is [T, C] (C % 8 == 0), V is [T, r]. 128 columns per workgroup; each wave
+// M is [T, C] (any C), V is [T, r]. 128 columns per workgroup; each wave
 // owns 32 columns x all rank tiles. Both operands are staged transposed in LDS
 // so the token (reduction) index is contiguous for the MFMA fragments.
 template <int RT>
@@ -281,8 +304,10 @@ __global__ __launch_bounds__(kThreads) void skinny_tn_kernel(int T, int Ccols, i
     for (int c = tid; c < kBK * (BC / 8); c += kThreads) {
       const int tl = c / (BC / 8), ch = c - tl * (BC / 8);
       uint4 v = {0u, 0u, 0u, 0u};
-      if (t0 + tl < t_end && c0 + ch * 8 < Ccols)
-        v = *reinterpret_cast<const uint4*>(M + static_cast<size_t>(t0 + tl) * Ccols + c0 + ch * 8);
+      if (t0 + tl < t_end && c0 + ch * 8 < Ccols) {
+        const uint16_t* src = M + static_cast<size_t>(t0 + tl) * Ccols + c0 + ch * 8;
+        v = (Ccols & 7) == 0 ? *reinterpret_cast<const uint4*>(src) : load8_masked(src, Ccols - c0 - ch * 8);
+      }
       const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
@@ -425,7 +450,7 @@ hipError_t launch_u(int T, int K, int r, const uint16_t* x, const uint16_t* A, u
 #define LNF4_U(RT_) \
   lora_u_kernel<RT_><<<(T + 63) / 64, kThreads, 0, stream>>>(T, K, r, x, A, u); \
   return hipGetLastError()
-  switch ((r + 15) / 16) {
+  switch (generic_rank_tiles(r)) {
     case 1: LNF4_U(1);
     case 2: LNF4_U(2);
     case 3: LNF4_U(3);
@@ -434,6 +459,8 @@ hipError_t launch_u(int T, int K, int r, const uint16_t* x, const uint16_t* A, u
     case 6: LNF4_U(6);
     case 7: LNF4_U(7);
     case 8: LNF4_U(8);
+    case 12: LNF4_U(12);
+    case 16: LNF4_U(16);
     default: return hipErrorInvalidValue;
   }
 #undef LNF4_U
@@ -460,7 +487,7 @@ int choose_splits(int64_t T, int64_t cols) {
 BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r) {
   BwdPlan p{};
   p.fast = lora_dx_supported(r) && lora_skinny_supported(r) && fits_buffer(T, K, N);
-  const int64_t rs = p.fast ? r : ((r + 15) / 16) * 16;
+  const int64_t rs = p.fast ? r : generic_rank_tiles(r) * 16;
   p.rp = static_cast<int>(((r + 31) / 32) * 32);
   if (p.fast) {
     p.splits_a = p.splits_b = skinny_splits(T, K, N);
@@ -511,7 +538,7 @@ hipError_t launch_lora_bwd(int T, int K, int N, int r, float s, const uint16_t* 
 #define LNF4_BWD(RT_)                                                                              \
   return launch_bwd_rt<RT_>(T, K, N, r, s, x, dy, codes, absmax, A, B, u_saved, dx, dA, dB,        \
                             workspace, plan, stream)
-  switch ((r + 15) / 16) {
+  switch (generic_rank_tiles(r)) {
     case 1: LNF4_BWD(1);
     case 2: LNF4_BWD(2);
     case 3: LNF4_BWD(3);
@@ -520,6 +547,8 @@ hipError_t launch_lora_bwd(int T, int K, int N, int r, float s, const uint16_t* 
     case 6: LNF4_BWD(6);
     case 7: LNF4_BWD(7);
     case 8: LNF4_BWD(8);
+    case 12: LNF4_BWD(12);
+    case 16: LNF4_BWD(16);
     default: return hipErrorInvalidValue;
   }
 #undef LNF4_BWD

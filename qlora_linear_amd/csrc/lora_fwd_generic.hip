@@ -32,7 +32,8 @@ struct FwdCfg {
   static constexpr int TM = WM / 16, TN = WN / 16;      // 16 x 16 MFMA tiles per wave
   static constexpr int RP = ((RT * 16 + 31) / 32) * 32; // rank padded to the MFMA reduction step
   static constexpr int UT = (RT + 1) / 2;               // U column tiles per wave (split over wn)
-  static constexpr int ES = RP + 8;                     // epilogue LDS row stride
+  static constexpr int EC = RP < 64 ? RP : 64;          // rank columns per epilogue pass
+  static constexpr int ES = EC + 8;                     // epilogue LDS row stride
   static constexpr int SX = (BM * (ES > kLds ? ES : kLds));
   static constexpr int SW = (BN * (ES > kLds ? ES : kLds));
 };
@@ -137,51 +138,69 @@ __global__ __launch_bounds__(kThreads) void lora_fwd_kernel(
     }
   }
 
-  // ---- epilogue: acc += bf16(s U) B -------------------------------------------------
-  __syncthreads();
-  uint16_t* us = xs;   // [BM][ES]  bf16(s U), rank padded with zeros
-  uint16_t* bts = ws;  // [BN][ES]  B^T tile, rank padded with zeros
+  // ---- epilogue: acc += bf16(s U) B, EC rank columns per pass ---------------------
+  if (u_save != nullptr && tn == 0) {
 #pragma unroll
-  for (int u = 0; u < C::UT; ++u) {
-    const int jt = 2 * u + wn;
-    if (jt < RT) {
+    for (int u = 0; u < C::UT; ++u) {
+      const int jt = 2 * u + wn;
+      if (jt < RT) {
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = wm * C::WM + i * 16 + lq * 4 + e, col = jt * 16 + l16;
+            if (col < r && m0 + row < T) u_save[static_cast<size_t>(m0 + row) * r + col] = to_bf16(uacc[i][u][e]);
+          }
+      }
+    }
+  }
+  uint16_t* us = xs;   // [BM][ES]  bf16(s U) columns c0 .. c0 + EC - 1, zero past the rank
+  uint16_t* bts = ws;  // [BN][ES]  the same columns of B^T
+#pragma unroll
+  for (int c0 = 0; c0 < C::RP; c0 += C::EC) {
+    __syncthreads();  // the previous pass (or the K-loop) is done with xs and ws
+#pragma unroll
+    for (int u = 0; u < C::UT; ++u) {
+      const int jt = 2 * u + wn;
+      if (jt < RT && jt * 16 >= c0 && jt * 16 < c0 + C::EC) {
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = wm * C::WM + i * 16 + lq * 4 + e;
+            us[row * C::ES + jt * 16 - c0 + l16] = to_bf16(s * uacc[i][u][e]);
+          }
+      }
+    }
+    const int kTail = (RT * 16 > c0 && RT * 16 < c0 + C::EC) ? c0 + C::EC - RT * 16 : 0;
+    if (RT * 16 <= c0) {
+      for (int e = tid; e < BM * C::EC; e += kThreads) us[(e / C::EC) * C::ES + e % C::EC] = 0;
+    } else if (kTail > 0) {
+      for (int e = tid; e < BM * kTail; e += kThreads) {
+        const int row = e / kTail, col = RT * 16 - c0 + (e - row * kTail);
+        us[row * C::ES + col] = 0;
+      }
+    }
+    for (int e = tid; e < C::EC * BN; e += kThreads) {
+      const int j = e / BN, c = e - j * BN;
+      bts[c * C::ES + j] = (c0 + j < r && n0 + c < N) ? B[static_cast<size_t>(c0 + j) * N + n0 + c] : uint16_t(0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < C::EC / 32; ++ks) {
+      const int kc = ks * 32 + lq * 8;
+      uint4 af[C::TM], bfr[C::TN];
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+        af[i] = *reinterpret_cast<const uint4*>(us + (wm * C::WM + i * 16 + l16) * C::ES + kc);
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        bfr[j] = *reinterpret_cast<const uint4*>(bts + (wn * C::WN + j * 16 + l16) * C::ES + kc);
 #pragma unroll
       for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = wm * C::WM + i * 16 + lq * 4 + e, col = jt * 16 + l16;
-          const float uv = uacc[i][u][e];
-          us[row * C::ES + col] = to_bf16(s * uv);
-          if (u_save != nullptr && tn == 0 && col < r && m0 + row < T)
-            u_save[static_cast<size_t>(m0 + row) * r + col] = to_bf16(uv);
-        }
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
     }
-  }
-  constexpr int PADC = C::RP - RT * 16;
-  if (PADC > 0)
-    for (int e = tid; e < BM * PADC; e += kThreads) {
-      const int row = e / PADC, col = RT * 16 + (e - row * PADC);
-      us[row * C::ES + col] = 0;
-    }
-  for (int e = tid; e < C::RP * BN; e += kThreads) {
-    const int j = e / BN, c = e - j * BN;
-    bts[c * C::ES + j] = (j < r && n0 + c < N) ? B[static_cast<size_t>(j) * N + n0 + c] : uint16_t(0);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int ks = 0; ks < C::RP / 32; ++ks) {
-    const int kc = ks * 32 + lq * 8;
-    uint4 af[C::TM], bfr[C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-      af[i] = *reinterpret_cast<const uint4*>(us + (wm * C::WM + i * 16 + l16) * C::ES + kc);
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-      bfr[j] = *reinterpret_cast<const uint4*>(bts + (wn * C::WN + j * 16 + l16) * C::ES + kc);
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
   }
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
@@ -211,7 +230,7 @@ hipError_t launch_fwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
 hipError_t launch_lora_fwd_generic(int T, int K, int N, int r, float s, const uint16_t* x,
                            const uint8_t* codes, const float* absmax, const uint16_t* A,
                            const uint16_t* B, uint16_t* y, uint16_t* u_save, hipStream_t stream) {
-  switch ((r + 15) / 16) {
+  switch (generic_rank_tiles(r)) {
     case 1: return launch_fwd_rt<1>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
     case 2: return launch_fwd_rt<2>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
     case 3: return launch_fwd_rt<3>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
@@ -220,6 +239,8 @@ hipError_t launch_lora_fwd_generic(int T, int K, int N, int r, float s, const ui
     case 6: return launch_fwd_rt<6>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
     case 7: return launch_fwd_rt<7>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
     case 8: return launch_fwd_rt<8>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
+    case 12: return launch_fwd_rt<12>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
+    case 16: return launch_fwd_rt<16>(T, K, N, r, s, x, codes, absmax, A, B, y, u_save, stream);
     default: return hipErrorInvalidValue;
   }
 }

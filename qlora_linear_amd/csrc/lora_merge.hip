@@ -12,8 +12,8 @@
 // of d_in). The op is bound by HBM (0.5625 bytes of packed weight in, 2 or 4
 // bytes out per element):
 //   1. A rows k0 .. k0 + 255 and B columns n0 .. n0 + 63 go to LDS, rank padded
-//      with zeros to a multiple of 32 (the only LDS use, so several workgroups
-//      share a CU);
+//      with zeros to a multiple of 32, at most 128 rank columns per pass (the only
+//      LDS use, so several workgroups share a CU);
 //   2. v_mfma_f32_16x16x32_bf16 forms (A B)^T with A as the row operand (its rows
 //      are contiguous in the reduction j). The MFMA row m of block b reads A row
 //      32 (b >> 1) + 8 (m >> 2) + 4 (b & 1) + (m & 3) of the wave's 64 columns, so
@@ -33,7 +33,9 @@ constexpr int kThreads = 256;
 constexpr int kMN = 64;    // d_out rows per workgroup
 constexpr int kMK = 256;   // d_in columns per workgroup (64 per wave)
 
-template <int RP, bool OUT_BF16>
+// MP: more than one rank pass (r > RP); otherwise the pass loop is compiled out and
+// only one n-block's accumulators are live at a time.
+template <int RP, bool OUT_BF16, bool MP>
 __global__ __launch_bounds__(kThreads) void lora_merge_kernel(int K, int N, int r, float s,
                                                               const uint8_t* __restrict__ codes,
                                                               const float* __restrict__ absmax,
@@ -66,94 +68,75 @@ __global__ __launch_bounds__(kThreads) void lora_merge_kernel(int K, int N, int 
     av[nb] = ok ? absmax[static_cast<size_t>(n) * KB + kw / 64] : 0.f;
   }
 
-  // ---- 1. stage A and B. A rows k0 .. k0 + 255 are one contiguous run of 256 r
-  // elements; B columns n0 .. n0 + 63 are 128-byte runs of its rows. With r and
-  // d_out multiples of 8 both are read as 16-byte chunks (few loads in flight per
-  // thread, all independent); otherwise element by element in batches of 8.
-  const int na = kMK * r;
-  if (r % 8 == 0 && N % 8 == 0) {
-    for (int c0 = tid; c0 < na / 8; c0 += 4 * kThreads) {
-      uint4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = c0 + u * kThreads, e = 8 * c;
-        v[u] = (c < na / 8 && k0 + e / r < K) ? *reinterpret_cast<const uint4*>(A + static_cast<size_t>(k0) * r + e)
-                                              : uint4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = c0 + u * kThreads, e = 8 * c;
-        if (c < na / 8) *reinterpret_cast<uint4*>(at + (e / r) * RS + e % r) = v[u];
-      }
-    }
-    for (int c = tid; c < r * (kMN / 8); c += kThreads) {
-      const int j = c / (kMN / 8), nn = 8 * (c - j * (kMN / 8));
-      const uint4 v = n0 + nn < N ? *reinterpret_cast<const uint4*>(B + static_cast<size_t>(j) * N + n0 + nn)
-                                  : uint4{0u, 0u, 0u, 0u};
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int t = 0; t < 8; ++t) bt[(nn + t) * RS + j] = static_cast<uint16_t>(w[t >> 1] >> (16 * (t & 1)));
-    }
-    for (int e = tid; e < kMN * (RP - r); e += kThreads) {
-      const int nn = e / (RP - r), jj = r + e - nn * (RP - r);
-      bt[nn * RS + jj] = 0;
-    }
-  } else {
-    for (int e0 = tid; e0 < na; e0 += 8 * kThreads) {
-      uint16_t v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * kThreads;
-        v[u] = (e < na && k0 + e / r < K) ? A[static_cast<size_t>(k0) * r + e] : uint16_t(0);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * kThreads;
-        if (e < na) at[(e / r) * RS + e % r] = v[u];
-      }
-    }
-    for (int e0 = tid; e0 < kMN * RP; e0 += 8 * kThreads) {
-      uint16_t v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * kThreads, j = e / kMN, nn = e % kMN;
-        v[u] = (e < kMN * RP && j < r && n0 + nn < N) ? B[static_cast<size_t>(j) * N + n0 + nn] : uint16_t(0);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * kThreads;
-        if (e < kMN * RP) bt[(e % kMN) * RS + e / kMN] = v[u];
-      }
-    }
-  }
-  for (int e = tid; e < kMK * (RP - r); e += kThreads) {
-    const int kk = e / (RP - r), j = r + e - kk * (RP - r);
-    at[kk * RS + j] = 0;
-  }
-  __syncthreads();
-  if (kw >= K) return;
-
-  // ---- 2 + 3. per n-block: (A B)^T for 16 rows x 64 columns, then the elements
+  // ---- 1. stage A and B, RP rank columns per pass (one pass up to r = 128). A rows
+  // k0 .. k0 + 255 and B columns n0 .. n0 + 63 of the pass's rank columns go to LDS
+  // as 16-byte pieces, element by element where a row of A (r % 8 != 0) or of B
+  // (d_out % 8 != 0) is not 16-byte aligned; rank columns past r are zero.
+  // ---- 2. per n-block: (A B)^T for 16 rows x 64 columns, accumulated over the passes.
   // A row of MFMA row l16 in block b: 64 wave + 32 (b >> 1) + 8 (l16 >> 2) + 4 (b & 1) + (l16 & 3)
   const int arow = 64 * wave + 8 * (l16 >> 2) + (l16 & 3);
-  const unsigned char* lutb = reinterpret_cast<const unsigned char*>(lut);
+  f32x4_t acc[4][4];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int n = n0 + 16 * nb + l16;
-    f32x4_t acc[4];
+  for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < 4; ++b) acc[nb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const bool avec = r % 8 == 0, bvec = N % 8 == 0;
+  auto stage = [&](int j0) {
+    for (int c = tid; c < kMK * (RP / 8); c += kThreads) {
+      const int kk = c / (RP / 8), j = j0 + 8 * (c - kk * (RP / 8));
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (j < r && k0 + kk < K) {
+        const uint16_t* src = A + static_cast<size_t>(k0 + kk) * r + j;
+        v = avec ? *reinterpret_cast<const uint4*>(src) : load8_masked(src, r - j);
+      }
+      *reinterpret_cast<uint4*>(at + kk * RS + (j - j0)) = v;
+    }
+    for (int c = tid; c < RP * (kMN / 8); c += kThreads) {
+      const int jj = c / (kMN / 8), nn = 8 * (c - jj * (kMN / 8)), j = j0 + jj;
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (j < r && n0 + nn < N) {
+        const uint16_t* src = B + static_cast<size_t>(j) * N + n0 + nn;
+        v = bvec ? *reinterpret_cast<const uint4*>(src) : load8_masked(src, N - n0 - nn);
+      }
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) bt[(nn + t) * RS + jj] = static_cast<uint16_t>(w[t >> 1] >> (16 * (t & 1)));
+    }
+  };
+  auto product = [&](int nb, f32x4_t* a4) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int jq = 0; jq < RP / 32; ++jq) {
         const uint4 a = *reinterpret_cast<const uint4*>(at + (arow + 32 * (b >> 1) + 4 * (b & 1)) * RS + 32 * jq + 8 * g);
         const uint4 bb = *reinterpret_cast<const uint4*>(bt + (16 * nb + l16) * RS + 32 * jq + 8 * g);
-        acc[b] = mfma16(a, bb, acc[b]);
+        a4[b] = mfma16(a, bb, a4[b]);
       }
-    }
+  };
+  // every pass but the last accumulates all four n-blocks; the last pass forms each
+  // n-block's product right before its elements (one pass for r <= 128)
+  int j0 = 0;
+  for (; MP && j0 + RP < r; j0 += RP) {
+    stage(j0);
+    __syncthreads();
+    if (kw < K)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) product(nb, acc[nb]);
+    __syncthreads();
+  }
+  stage(j0);
+  __syncthreads();
+  if (kw >= K) return;
+
+  // ---- 3. the elements: lane (l16, g) holds column 32 (b >> 1) + 8 g + 4 (b & 1) + e
+  // of row n in acc[nb][b][e]; v[i] is column 8 g + i (i < 8) or 32 + 8 g + i - 8,
+  // i.e. acc[nb][i >> 2][i & 3]
+  const unsigned char* lutb = reinterpret_cast<const unsigned char*>(lut);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int n = n0 + 16 * nb + l16;
+    product(nb, acc[nb]);
     if (n >= N) continue;
-    // lane (l16, g) now holds column 32 (b >> 1) + 8 g + 4 (b & 1) + e of row n in acc[b][e];
-    // v[i] is column 8 g + i (i < 8) or 32 + 8 g + i - 8, i.e. acc[i >> 2][i & 3]
     const float sc = av[nb];
     const uint32_t w2[2] = {cw[nb].x, cw[nb].y};
     float v[16];
@@ -164,10 +147,10 @@ __global__ __launch_bounds__(kThreads) void lora_merge_kernel(int K, int N, int 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i0 = 8 * h + 2 * j, i1 = i0 + 1;
-        v[i0] = *reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(ev, 8 * j, 8)) * sc +
-                s * acc[i0 >> 2][i0 & 3];
-        v[i1] = *reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(od, 8 * j, 8)) * sc +
-                s * acc[i1 >> 2][i1 & 3];
+        v[i0] = __fmul_rn(*reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(ev, 8 * j, 8)), sc) +
+                s * acc[nb][i0 >> 2][i0 & 3];
+        v[i1] = __fmul_rn(*reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(od, 8 * j, 8)), sc) +
+                s * acc[nb][i1 >> 2][i1 & 3];
       }
     }
     const size_t o = static_cast<size_t>(n) * K + kw + 8 * g;
@@ -187,15 +170,15 @@ __global__ __launch_bounds__(kThreads) void lora_merge_kernel(int K, int N, int 
   }
 }
 
-template <int RP>
+template <int RP, bool MP = false>
 hipError_t launch_merge_t(int K, int N, int r, float s, const uint8_t* codes, const float* absmax,
                           const uint16_t* A, const uint16_t* B, bool out_bf16, void* out,
                           hipStream_t stream) {
   const dim3 grid((K + kMK - 1) / kMK, (N + kMN - 1) / kMN);
   if (out_bf16)
-    lora_merge_kernel<RP, true><<<grid, kThreads, 0, stream>>>(K, N, r, s, codes, absmax, A, B, out);
+    lora_merge_kernel<RP, true, MP><<<grid, kThreads, 0, stream>>>(K, N, r, s, codes, absmax, A, B, out);
   else
-    lora_merge_kernel<RP, false><<<grid, kThreads, 0, stream>>>(K, N, r, s, codes, absmax, A, B, out);
+    lora_merge_kernel<RP, false, MP><<<grid, kThreads, 0, stream>>>(K, N, r, s, codes, absmax, A, B, out);
   return hipGetLastError();
 }
 
@@ -208,7 +191,8 @@ hipError_t launch_lora_merge(int K, int N, int r, float s, const uint8_t* codes,
     case 1: return launch_merge_t<32>(K, N, r, s, codes, absmax, A, B, out_bf16, out, stream);
     case 2: return launch_merge_t<64>(K, N, r, s, codes, absmax, A, B, out_bf16, out, stream);
     case 3: return launch_merge_t<96>(K, N, r, s, codes, absmax, A, B, out_bf16, out, stream);
-    default: return launch_merge_t<128>(K, N, r, s, codes, absmax, A, B, out_bf16, out, stream);
+    case 4: return launch_merge_t<128>(K, N, r, s, codes, absmax, A, B, out_bf16, out, stream);
+    default: return launch_merge_t<128, true>(K, N, r, s, codes, absmax, A, B, out_bf16, out, stream);
   }
 }
 

@@ -71,9 +71,15 @@ def test_fwd_validation(lib):
     assert _fwd(lib, T=0, A=None) == LN_EINVAL
     assert _fwd(lib, alpha=float("nan")) == LN_EINVAL
     assert _fwd(lib, r=0) == LN_ERANK
-    assert _fwd(lib, r=129) == LN_ERANK
+    assert _fwd(lib, r=257) == LN_ERANK
     assert _fwd(lib, K=100) == LN_ESHAPE
-    assert _fwd(lib, N=12) == LN_ESHAPE
+    # the shape rules of the linear: 1 <= r <= 256 and any d_out >= 1 (checked with
+    # an empty batch, which validates every size and then enqueues nothing)
+    for r in (1, 129, 200, 256):
+        assert _fwd(lib, T=0, r=r) == LN_OK
+    for n in (1, 7, 12, 13):
+        assert _fwd(lib, T=0, N=n) == LN_OK
+    assert _fwd(lib, T=0, N=0) == LN_EINVAL
     assert _fwd(lib, x=P + 8) == LN_EALIGN
     assert _fwd(lib, y=P) == LN_EALIAS                      # output on top of x
     assert _fwd(lib, u=P + (5 << 30) + 64) == LN_EALIAS     # u_save inside y
@@ -141,7 +147,8 @@ def test_fwd_multi_validation(lib):
     assert _fwd_multi(lib, null="A") == LN_EINVAL
     assert _fwd_multi(lib, x=None) == LN_EINVAL
     assert _fwd_multi(lib, ptrs={"B": (1, None)}) == LN_EINVAL
-    assert _fwd_multi(lib, N=(64, 12, 16)) == LN_ESHAPE
+    assert _fwd_multi(lib, T=0, N=(64, 12, 16)) == LN_OK   # empty batch: validated, nothing enqueued
+    assert _fwd_multi(lib, N=(64, 0, 16)) == LN_EINVAL
     assert _fwd_multi(lib, K=100) == LN_ESHAPE
     assert _fwd_multi(lib, r=0) == LN_ERANK
     assert _fwd_multi(lib, alpha=float("inf")) == LN_EINVAL
@@ -195,6 +202,23 @@ def test_bwd_validation_and_workspace(lib):
     assert call(dB=dA) == LN_EALIAS
 
 
+def test_bwd_accepts_rank_256_and_any_d_out(lib):
+    """1 <= r <= 256 and any d_out >= 1 are valid sizes (the generic kernels take r >
+    64 and d_out % 8 != 0): the workspace query, which returns 0 for invalid sizes,
+    sizes them, with the rank-r partial sums at the rank's 16-column tiles. No call
+    here reaches a launch."""
+    for T, K, N, r in ((8, 64, 64, 256), (300, 128, 1, 16), (70, 192, 7, 24), (5, 64, 13, 200)):
+        assert lib.lora_nf4_bwd_workspace_bytes(T, K, N, r) > 0, (T, K, N, r)
+    assert lib.lora_nf4_bwd_workspace_bytes(8, 64, 64, 257) == 0
+    assert lib.lora_nf4_bwd_workspace_bytes(8, 64, 0, 16) == 0
+    ptrs = [P + (i << 30) for i in range(12)]
+    x, dy, c, a, A, B, u, dx, dA, dB, ws = ptrs[:11]
+    assert lib.lora_nf4_bwd(8, 64, 64, 257, 16.0, x, dy, c, a, A, B, u, dx, dA, dB, ws, ctypes.c_size_t(1 << 30),
+                            None) == LN_ERANK
+    # the partial sums of dA cover 16 rank-tile columns at r = 256: splits x d_in x 256 x 4 bytes
+    assert lib.lora_nf4_bwd_workspace_bytes(64, 64, 64, 256) >= 64 * 256 * 4
+
+
 def test_merge_validation(lib):
     c, a, A, B, o = (P + (i << 30) for i in range(5))
 
@@ -208,7 +232,7 @@ def test_merge_validation(lib):
     assert call(N=0) == LN_EINVAL
     assert call(alpha=float("nan")) == LN_EINVAL
     assert call(r=0) == LN_ERANK
-    assert call(r=200) == LN_ERANK
+    assert call(r=257) == LN_ERANK
     assert call(K=96) == LN_ESHAPE
     assert call(A=A + 2) == LN_EALIGN
     assert call(o=c + 64) == LN_EALIAS
@@ -245,7 +269,11 @@ def test_bwd_multi_validation(lib):
     assert call(dA=arr([base[17], None, base[19]])) == LN_EINVAL
     assert call(r=0) == LN_ERANK
     assert call(K=96) == LN_ESHAPE
-    assert call(d=(ctypes.c_int64 * n)(64, 60, 128)) == LN_ESHAPE
+    assert call(d=(ctypes.c_int64 * n)(64, 0, 128)) == LN_EINVAL
+    assert call(r=257) == LN_ERANK
+    # any d_out >= 1 and r up to 256 are valid (the query returns their workspace)
+    assert lib.lora_nf4_bwd_multi_workspace_bytes(64, 128, n, (ctypes.c_int64 * n)(64, 60, 128), 16) > 0
+    assert lib.lora_nf4_bwd_multi_workspace_bytes(64, 128, n, d_out, 256) > 0
     assert call(dx=base[16] + 8) == LN_EALIGN
     assert call(ws=None) == LN_EWORKSPACE
     assert call(ws_bytes=16) == LN_EWORKSPACE
@@ -295,7 +323,7 @@ def test_rslora_alpha_gives_the_rank_stabilized_scale_exactly(lib):
     import numpy as np
     from oracle import optim
     for alpha in (1.0, 16.0, 32.0, 7.5, 0.3):
-        for r in (1, 2, 3, 5, 8, 12, 16, 24, 32, 48, 64, 100, 128):
+        for r in (1, 2, 3, 5, 8, 12, 16, 24, 32, 48, 64, 100, 128, 200, 256):
             a = lib.lora_nf4_rslora_alpha(alpha, r)
             got = np.float32(a) / np.float32(r)  # the library's own s = lora_alpha / r in float32
             want = np.float32(optim.rslora_scale(float(np.float32(alpha)), r))  # alpha crosses as float32

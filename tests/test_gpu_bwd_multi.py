@@ -10,7 +10,8 @@ tiles, from 1024 tokens on weights dequantized into the workspace; and the
 per-projection path (a d_out not a multiple of 64, up to 128 tokens,
 no dX). One case runs the Qwen-14B-shaped q/k/v at full size
 (8192 tokens, 5120 -> 5120 each, r = 16) and checks sampled rows of dX and
-sampled columns of dA and dB against the oracle.
+sampled columns of dA and dB against the oracle; another runs the Llama-3-70B
+gate and up projections (8192 -> 28672, 4096 tokens) the same way.
 """
 import numpy as np
 import pytest
@@ -153,3 +154,40 @@ def test_bwd_multi_full_size_qwen_qkv(q):
         assert olora.rel_err(got_dB, dB_ref) <= TOL, ("dB", g)
     got = host_f64(dx)[rows]
     assert olora.rel_err(got, dx_ref) <= TOL
+
+
+def test_bwd_multi_full_size_70b_gate_up(q):
+    """Llama-3-70B gate and up (8192 -> 28672 each) at 4096 tokens, r = 16, sharing
+    x as the fused path runs them (the benchmark's --fuse grouping): sampled dX rows
+    (the sum over both projections) and sampled dA / dB columns against the oracle."""
+    from tests.gpu_util import host_f64
+    w = next(x for x in synth.WORKLOADS if x.name == "llama3-70b-layer")
+    names = [p.name for p in w.projections]
+    pis = [names.index("gate_proj"), names.index("up_proj")]
+    ins = [synth.projection_inputs(w, pi) for pi in pis]
+    ins[1]["x"] = ins[0]["x"]
+    x, codes, absmax, A, B, dy = _dev_inputs(q, ins)
+    us = q.lora_nf4_fwd_multi(x, codes, absmax, A, B, w.alpha)[1]
+    dx, dAs, dBs = q.lora_nf4_bwd_multi(x, dy, codes, absmax, A, B, w.alpha, u_saved=us)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    T, K = ins[0]["x"].shape
+    rows = np.sort(rng.choice(T, 6, replace=False))
+    cols = np.sort(rng.choice(K, 6, replace=False))
+    xr = _f64(ins[0]["x"])
+    s = w.alpha / w.r
+    dx_ref = np.zeros((rows.size, K))
+    for g, inp in enumerate(ins):
+        c, a = onf4.quantize(synth.bf16_bits_to_f32(inp["W"]))
+        D = onf4.dequantize_exact(c, a)
+        Ag, Bg, dYg = _f64(inp["A"]), _f64(inp["B"]), _f64(inp["dY"])
+        G = s * (dYg @ Bg.T)
+        dx_ref += dYg[rows] @ D + G[rows] @ Ag.T
+        del D
+        dA_ref = xr[:, cols].T @ G
+        U = xr @ Ag
+        ncols = np.sort(rng.choice(dYg.shape[1], 6, replace=False))
+        dB_ref = s * (U.T @ dYg[:, ncols])
+        assert olora.rel_err(host_f64(dAs[g])[cols], dA_ref) <= TOL, ("dA", g)
+        assert olora.rel_err(host_f64(dBs[g])[:, ncols], dB_ref) <= TOL, ("dB", g)
+    assert olora.rel_err(host_f64(dx)[rows], dx_ref) <= TOL

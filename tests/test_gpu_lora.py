@@ -73,13 +73,17 @@ def test_tiny_workload(q):
 
 
 # (T, d_in, d_out, r): ragged token counts, partial tiles in every dimension,
-# ranks from 1 to the maximum; the last four split the reduction of the tiled
+# ranks from 1 to the maximum (256), d_out from 1; the last four split the reduction of the tiled
 # kernels across workgroups: the forward's over d_in (few tiles, d_in >= 1024),
 # then dX's over d_out (few tiles, d_out >= 2048).
 ODD = [(1, 64, 64, 1), (63, 128, 192, 8), (65, 192, 64, 16), (200, 320, 136, 64),
        (130, 256, 8, 128), (257, 64, 520, 24), (129, 384, 264, 17), (17, 640, 1000, 40),
        (260, 192, 296, 48), (300, 2048, 200, 16), (200, 1536, 136, 64), (300, 256, 2048, 16),
-       (200, 192, 2056, 64)]
+       (200, 192, 2056, 64),
+       # d_out not a multiple of 8 (generic kernels, unaligned rows of dY, y and B) and
+       # ranks above 128 (rank tiles of 12 and 16, epilogues in passes of 64 columns)
+       (40, 128, 13, 16), (300, 192, 7, 24), (5, 64, 1, 8), (129, 320, 1001, 64), (70, 256, 200, 256),
+       (130, 128, 64, 200), (1, 64, 13, 256), (260, 192, 136, 160)]
 
 
 @pytest.mark.parametrize("T,K,N,r", ODD)
@@ -230,16 +234,26 @@ def test_dx_tile_edges_agree(q, r):
     assert olora.rel_err(host_f64(dx)[:, cols], dx_ref) <= TOL
 
 
-@pytest.mark.parametrize("T,K,N,r", [(300, 256, 192, 16), (7, 320, 200, 24), (8200, 256, 192, 16)])
+@pytest.mark.parametrize("T,K,N,r", [(300, 256, 192, 16), (7, 320, 200, 24), (8200, 256, 192, 16),
+                                     (48, 4096, 1024, 16), (4100, 512, 256, 64)])
 def test_recompute_u_and_skip_dx_paths(q, T, K, N, r):
+    """The backward with u_saved = NULL recomputes U = x A itself; its dX, dA and dB
+    are checked against the oracle directly (tiled, few-token, split-K and
+    large-token shapes), and the dX-less call gives the same dA and dB bits."""
     from tests.gpu_util import host_f64
+    alpha = 32.0
     inp = synth.custom_inputs(2, T, K, N, r)
-    y, u, dx, dA, dB = _run_gpu(q, inp, 32.0, u_saved=True)
-    _, _, dx2, dA2, dB2 = _run_gpu(q, inp, 32.0, u_saved=False)
-    _, _, dx3, dA3, dB3 = _run_gpu(q, inp, 32.0, u_saved=True, need_dx=False)
+    y, u, dx, dA, dB = _run_gpu(q, inp, alpha, u_saved=True)
+    _, _, dx2, dA2, dB2 = _run_gpu(q, inp, alpha, u_saved=False)
+    _, _, dx3, dA3, dB3 = _run_gpu(q, inp, alpha, u_saved=True, need_dx=False)
     assert dx3 is None
-    for a, b in ((dA, dA2), (dB, dB2), (dx, dx2)):
-        assert olora.rel_err(host_f64(b), host_f64(a)) <= TOL
+    x, A, B, dY = (_f64(inp[k]) for k in ("x", "A", "B", "dY"))
+    dX_ref, dA_ref, dB_ref = olora.backward(x, dY, _oracle_D(inp), A, B, alpha, r)
+    errs = {"dx": olora.rel_err(host_f64(dx2), dX_ref), "dA": olora.rel_err(host_f64(dA2), dA_ref),
+            "dB": olora.rel_err(host_f64(dB2), dB_ref)}
+    print(f"recompute-U T={T} K={K} N={N} r={r}", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
     assert torch.equal(dA3, dA) and torch.equal(dB3, dB)
 
 
@@ -342,7 +356,10 @@ def _sample_rows(T, n=48, seed=0):
     return rows
 
 
-FULL = [(1, 0), (2, 1), (2, 3), (3, 0), (4, 1), (4, 4)]
+# every distinct projection shape of the five workloads: 8B q (4096 -> 4096, r = 16),
+# 8B k/o at r = 64, Qwen-14B (5120 -> 5120), and the 70B q (8192 -> 8192), k, gate
+# (8192 -> 28672) and down (28672 -> 8192) projections at 4096 tokens
+FULL = [(1, 0), (2, 1), (2, 3), (3, 0), (4, 0), (4, 1), (4, 4), (4, 6)]
 
 
 @pytest.mark.parametrize("wi,pi", FULL)

@@ -30,9 +30,11 @@ def _bf16_ulp(v):
     return np.where(a > 0, 2.0 ** (e - 7), 2.0 ** -133)
 
 
-# (d_in, d_out, r, alpha): partial tiles in both directions, ranks 1 .. 128
+# (d_in, d_out, r, alpha): partial tiles in both directions, ranks 1 .. 256 (above
+# 128 in two rank passes), d_out not a multiple of 8 (rows of B unaligned)
 SHAPES = [(256, 64, 16, 16.0), (320, 72, 8, 16.0), (192, 200, 24, 32.0), (64, 8, 1, 2.0),
-          (512, 100, 128, 16.0), (4096, 4096, 16, 16.0)]
+          (512, 100, 128, 16.0), (4096, 4096, 16, 16.0), (320, 13, 24, 16.0), (128, 1, 7, 16.0),
+          (384, 77, 256, 16.0), (256, 200, 160, 32.0)]
 
 
 @pytest.mark.parametrize("K,N,r,alpha", SHAPES)
