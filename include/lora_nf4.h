@@ -243,6 +243,28 @@ int lora_nf4_merge(int64_t d_in, int64_t d_out, int32_t r, float lora_alpha, con
 size_t lora_nf4_bwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t r);
 
 /*
+ * lora_nf4_bwd_noalloc — lora_nf4_bwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, the same results. Its
+ * workspace is a scratch array the library owns, LN_NOALLOC_SCRATCH_BYTES of device
+ * memory per GPU, reserved when the library's code is loaded on that GPU and held
+ * until the process ends; the call itself allocates nothing. Where lora_nf4_bwd's
+ * workspace fits the scratch it runs exactly that plan; otherwise the plan without
+ * the dequantized weight copy (bf16 d_in x d_out bytes), which gives the same bits;
+ * LN_EWORKSPACE if even that does not fit (the rank-r partial sums and G, U of very
+ * large shapes). Every call on one GPU shares that GPU's scratch: calls that overlap
+ * in time on one GPU (concurrent streams, several host threads) race and must be
+ * serialized by the caller; calls on different GPUs are independent. The scratch
+ * keeps the last call's contents; nothing in it needs to start at zero.
+ */
+#define LN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int lora_nf4_bwd_noalloc(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha,
+                         const uint16_t* x, const uint16_t* dy, const uint8_t* w_codes,
+                         const float* w_absmax, const uint16_t* A, const uint16_t* B,
+                         const uint16_t* u_saved, uint16_t* dx, uint16_t* dA, uint16_t* dB,
+                         void* stream);
+
+/*
  * lora_adamw_step — one AdamW update of a LoRA factor (A or B), the optimizer
  * phase of a training step ("Unsloth performance measured: is it really 2x
  * faster?", section 2.2 time table, optimizer.step row; section 3: 16-bit

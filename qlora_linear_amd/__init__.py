@@ -31,7 +31,7 @@ __all__ = [
     "lora_nf4_fwd", "lora_nf4_fwd_multi", "lora_nf4_bwd", "lora_nf4_bwd_workspace_bytes", "lora_nf4_merge",
     "status_string", "EXPORTED_SYMBOLS", "LN_MAX_RANK", "LN_MAX_PROJ",
     "lora_adamw_step", "rslora_alpha", "nf4_absmax_quantize", "nf4_absmax_dequantize",
-    "lora_nf4_bwd_multi", "lora_nf4_bwd_multi_workspace_bytes",
+    "lora_nf4_bwd_multi", "lora_nf4_bwd_multi_workspace_bytes", "lora_nf4_bwd_noalloc",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -45,7 +45,7 @@ EXPORTED_SYMBOLS = ("nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_
                     "lora_nf4_status_string", "lora_adamw_step", "lora_nf4_rslora_alpha",
                     "nf4_absmax_quantize", "nf4_absmax_dequantize", "lora_nf4_bwd_multi",
                     "lora_nf4_bwd_multi_workspace_bytes", "lora_nf4_fwd_workspace_bytes",
-                    "lora_nf4_fwd_multi_workspace_bytes")
+                    "lora_nf4_fwd_multi_workspace_bytes", "lora_nf4_bwd_noalloc")
 
 _lib = None
 
@@ -63,6 +63,8 @@ _SIGS = {
     "lora_nf4_bwd": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_float,
                                     _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
     "lora_nf4_bwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, ctypes.c_int32]),
+    "lora_nf4_bwd_noalloc": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_float,
+                                            _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "lora_nf4_merge": (ctypes.c_int, [_i64, _i64, ctypes.c_int32, ctypes.c_float, _p, _p, _p, _p,
                                       ctypes.c_int, _p, _p]),
     "lora_nf4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -269,6 +271,28 @@ def lora_nf4_bwd(x, dy, codes, absmax, A, B, lora_alpha: float, u_saved=None, ne
         T, K, N, r, float(lora_alpha), x.data_ptr(), dy.data_ptr(), codes.data_ptr(),
         absmax.data_ptr(), A.data_ptr(), B.data_ptr(), _ptr(u_saved), _ptr(dx), dA.data_ptr(),
         dB.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x)))
+    return dx, dA, dB
+
+
+def lora_nf4_bwd_noalloc(x, dy, codes, absmax, A, B, lora_alpha: float, u_saved=None, need_dx: bool = True):
+    """lora_nf4_bwd without a workspace argument: the library's own device scratch
+    serves as its workspace (calls overlapping on one GPU race)."""
+    bf = torch.bfloat16
+    _dev(x, "x", bf, 2), _dev(dy, "dy", bf, 2), _dev(codes, "codes", torch.uint8, 2)
+    _dev(absmax, "absmax", torch.float32, 2), _dev(A, "A", bf, 2), _dev(B, "B", bf, 2)
+    T, K, N, r = _lora_shapes(x, codes, A, B)
+    if dy.shape != (T, N):
+        raise ValueError("dy must be [T, d_out]")
+    if u_saved is not None:
+        _dev(u_saved, "u_saved", bf, 2)
+    dev = x.device
+    dx = torch.empty((T, K), dtype=bf, device=dev) if need_dx else None
+    dA = torch.empty((K, r), dtype=bf, device=dev)
+    dB = torch.empty((r, N), dtype=bf, device=dev)
+    _check("lora_nf4_bwd_noalloc", library().lora_nf4_bwd_noalloc(
+        T, K, N, r, float(lora_alpha), x.data_ptr(), dy.data_ptr(), codes.data_ptr(),
+        absmax.data_ptr(), A.data_ptr(), B.data_ptr(), _ptr(u_saved), _ptr(dx), dA.data_ptr(),
+        dB.data_ptr(), _stream(x)))
     return dx, dA, dB
 
 

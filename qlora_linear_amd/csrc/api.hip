@@ -4,6 +4,7 @@
 // argument errors are reported without a GPU and nothing is enqueued on error.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "launch.h"
 #include "lora_nf4.h"
@@ -214,11 +215,17 @@ size_t lora_nf4_bwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int3
   return lnf4::plan_bwd(T, d_in, d_out, r).bytes;
 }
 
-int lora_nf4_bwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha,
-                 const uint16_t* x, const uint16_t* dy, const uint8_t* w_codes,
-                 const float* w_absmax, const uint16_t* A, const uint16_t* B,
-                 const uint16_t* u_saved, uint16_t* dx, uint16_t* dA, uint16_t* dB,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of lora_nf4_bwd that precede the workspace: LN_OK with *empty set
+// when T = 0 (after zeroing dA and dB on the stream), LN_OK otherwise, or the error.
+int check_bwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha, const uint16_t* x,
+              const uint16_t* dy, const uint8_t* w_codes, const float* w_absmax, const uint16_t* A,
+              const uint16_t* B, const uint16_t* u_saved, uint16_t* dx, uint16_t* dA, uint16_t* dB,
+              void* stream, bool* empty) {
+  *empty = false;
   if (w_codes == nullptr || w_absmax == nullptr || A == nullptr || B == nullptr || dA == nullptr ||
       dB == nullptr)
     return LN_EINVAL;
@@ -235,26 +242,104 @@ int lora_nf4_bwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_a
     hipError_t e = lnf4::launch_zero_u16(dA, static_cast<int64_t>(d_in) * r, static_cast<hipStream_t>(stream));
     if (e == hipSuccess)
       e = lnf4::launch_zero_u16(dB, static_cast<int64_t>(r) * d_out, static_cast<hipStream_t>(stream));
+    *empty = true;
     return hip_status(e);
   }
   if (!aligned16(x) || !aligned16(dy) || !aligned16(w_codes) || !aligned16(w_absmax) ||
       !aligned16(A) || !aligned16(B) || !aligned16(dA) || !aligned16(dB) ||
       (u_saved != nullptr && !aligned16(u_saved)) || (dx != nullptr && !aligned16(dx)))
     return LN_EALIGN;
-  const lnf4::BwdPlan plan = lnf4::plan_bwd(T, d_in, d_out, r);
-  if (workspace == nullptr || workspace_bytes < plan.bytes) return LN_EWORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LN_EALIGN;
+  return LN_OK;
+}
+
+// Alias checks of the backward's outputs (the workspace among them) against its inputs.
+bool bwd_aliases(int64_t T, int64_t d_in, int64_t d_out, int32_t r, const uint16_t* x, const uint16_t* dy,
+                 const uint8_t* w_codes, const float* w_absmax, const uint16_t* A, const uint16_t* B,
+                 const uint16_t* u_saved, uint16_t* dx, uint16_t* dA, uint16_t* dB, const void* workspace,
+                 size_t ws_bytes) {
   const size_t t = T, k = d_in, n = d_out, rr = r;
-  const Span outs[4] = {{dx, t * k * 2}, {dA, k * rr * 2}, {dB, rr * n * 2}, {workspace, plan.bytes}};
+  const Span outs[4] = {{dx, t * k * 2}, {dA, k * rr * 2}, {dB, rr * n * 2}, {workspace, ws_bytes}};
   const Span ins[7] = {{x, t * k * 2},        {dy, t * n * 2},   {w_codes, n * k / 2},
                        {w_absmax, n * k / 64 * 4}, {A, k * rr * 2}, {B, rr * n * 2},
                        {u_saved, t * rr * 2}};
-  if (any_alias(outs, 4, ins, 7)) return LN_EALIAS;
+  return any_alias(outs, 4, ins, 7);
+}
+
+// The no-allocation backward's scratch: one backward workspace in device memory the
+// library owns. A file-scope device array, so each GPU the library runs on holds
+// its own copy (64 MiB) until the process ends. Host code must not pass the array's
+// name to a kernel (on the host it only stands in for the symbol): its device
+// address is looked up once per device, with that device current, and kept.
+constexpr size_t kScratchBytes = LN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lora_nf4_bwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha,
+                 const uint16_t* x, const uint16_t* dy, const uint8_t* w_codes,
+                 const float* w_absmax, const uint16_t* A, const uint16_t* B,
+                 const uint16_t* u_saved, uint16_t* dx, uint16_t* dA, uint16_t* dB,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  const int st = check_bwd(T, d_in, d_out, r, lora_alpha, x, dy, w_codes, w_absmax, A, B, u_saved, dx, dA, dB,
+                           stream, &empty);
+  if (st != LN_OK || empty) return st;
+  const lnf4::BwdPlan plan = lnf4::plan_bwd(T, d_in, d_out, r);
+  if (workspace == nullptr || workspace_bytes < plan.bytes) return LN_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LN_EALIGN;
+  if (bwd_aliases(T, d_in, d_out, r, x, dy, w_codes, w_absmax, A, B, u_saved, dx, dA, dB, workspace, plan.bytes))
+    return LN_EALIAS;
   const float s = lora_alpha / static_cast<float>(r);
   return hip_status(lnf4::launch_lora_bwd(static_cast<int>(T), static_cast<int>(d_in),
                                           static_cast<int>(d_out), r, s, x, dy, w_codes, w_absmax,
                                           A, B, u_saved, dx, dA, dB, workspace, plan,
                                           static_cast<hipStream_t>(stream)));
+}
+
+int lora_nf4_bwd_noalloc(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha,
+                         const uint16_t* x, const uint16_t* dy, const uint8_t* w_codes,
+                         const float* w_absmax, const uint16_t* A, const uint16_t* B,
+                         const uint16_t* u_saved, uint16_t* dx, uint16_t* dA, uint16_t* dB, void* stream) {
+  bool empty = false;
+  const int st = check_bwd(T, d_in, d_out, r, lora_alpha, x, dy, w_codes, w_absmax, A, B, u_saved, dx, dA, dB,
+                           stream, &empty);
+  if (st != LN_OK || empty) return st;
+  // the same plan as lora_nf4_bwd where its workspace fits the scratch, else the
+  // plan without the dequantized weight (the same results, in-loop dequantization)
+  lnf4::BwdPlan plan = lnf4::plan_bwd(T, d_in, d_out, r);
+  if (plan.bytes > kScratchBytes) plan = lnf4::plan_bwd(T, d_in, d_out, r, false);
+  if (plan.bytes > kScratchBytes) return LN_EWORKSPACE;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return LN_EHIP;
+  if (bwd_aliases(T, d_in, d_out, r, x, dy, w_codes, w_absmax, A, B, u_saved, dx, dA, dB, ws, plan.bytes))
+    return LN_EALIAS;
+  const float s = lora_alpha / static_cast<float>(r);
+  return hip_status(lnf4::launch_lora_bwd(static_cast<int>(T), static_cast<int>(d_in),
+                                          static_cast<int>(d_out), r, s, x, dy, w_codes, w_absmax,
+                                          A, B, u_saved, dx, dA, dB, ws, plan, static_cast<hipStream_t>(stream)));
 }
 
 size_t lora_nf4_bwd_multi_workspace_bytes(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d_out,

@@ -187,7 +187,9 @@ struct BwdPlan {
   size_t off_w;                         // that weight, bf16 [N][K]
   size_t bytes;       // total workspace bytes
 };
-BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r);
+// allow_dq = false: never the dequantized-weight dX (its workspace holds 2 d_in d_out
+// bytes more); the results are the same bits either way.
+BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r, bool allow_dq = true);
 
 hipError_t launch_lora_bwd(int T, int K, int N, int r, float s, const uint16_t* x,
                            const uint16_t* dy, const uint8_t* codes, const float* absmax,

@@ -484,7 +484,7 @@ int choose_splits(int64_t T, int64_t cols) {
 
 }  // namespace
 
-BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r) {
+BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r, bool allow_dq) {
   BwdPlan p{};
   p.fast = lora_dx_supported(r) && lora_skinny_supported(r) && fits_buffer(T, K, N);
   const int64_t rs = p.fast ? r : generic_rank_tiles(r) * 16;
@@ -520,7 +520,7 @@ BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r) {
       off = align256(off + static_cast<size_t>(d.splits) * T * K * 4);
       p.off_pg = off;
       off = align256(off + static_cast<size_t>(d.splits) * T * r * 4);
-    } else if (dx_dq(T, K, N, r)) {
+    } else if (allow_dq && dx_dq(T, K, N, r)) {
       p.dqx = true;
       p.off_w = off;
       off = align256(off + static_cast<size_t>(N) * K * 2);

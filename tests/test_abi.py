@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
                             "lora_nf4_status_string", "lora_adamw_step", "lora_nf4_rslora_alpha",
                             "nf4_absmax_quantize", "nf4_absmax_dequantize", "lora_nf4_bwd_multi",
                             "lora_nf4_bwd_multi_workspace_bytes", "lora_nf4_fwd_workspace_bytes",
-                            "lora_nf4_fwd_multi_workspace_bytes"])
+                            "lora_nf4_fwd_multi_workspace_bytes", "lora_nf4_bwd_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -217,6 +217,26 @@ def test_bwd_accepts_rank_256_and_any_d_out(lib):
                             None) == LN_ERANK
     # the partial sums of dA cover 16 rank-tile columns at r = 256: splits x d_in x 256 x 4 bytes
     assert lib.lora_nf4_bwd_workspace_bytes(64, 64, 64, 256) >= 64 * 256 * 4
+
+
+def test_bwd_noalloc_validation(lib):
+    """The no-allocation backward checks its arguments like lora_nf4_bwd and rejects
+    shapes whose workspace exceeds its scratch, all before any HIP call."""
+    ptrs = [P + (i << 30) for i in range(12)]
+    x, dy, c, a, A, B, u, dx, dA, dB = ptrs[:10]
+
+    def call(T=8, K=64, N=64, r=8, **kw):
+        args = dict(x=x, dy=dy, c=c, a=a, A=A, B=B, u=u, dx=dx, dA=dA, dB=dB)
+        args.update(kw)
+        return lib.lora_nf4_bwd_noalloc(T, K, N, r, 16.0, args["x"], args["dy"], args["c"], args["a"], args["A"],
+                                        args["B"], args["u"], args["dx"], args["dA"], args["dB"], None)
+
+    assert call(dA=None) == LN_EINVAL
+    assert call(r=257) == LN_ERANK
+    assert call(K=96) == LN_ESHAPE
+    assert call(dx=x + 8) == LN_EALIGN
+    # G and U alone of 2^20 tokens at rank 256 are 1 GiB: past the 64 MiB scratch
+    assert call(T=1 << 20, K=8192, N=28672, r=256) == LN_EWORKSPACE
 
 
 def test_merge_validation(lib):
