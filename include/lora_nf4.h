@@ -101,11 +101,15 @@ int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows, int6
  *            separate workspaces). That size is non-zero where the reduction
  *            over d_in is split across workgroups and fp32 partial sums meet in
  *            the workspace (few tokens: T <= 128 at r % 8 == 0, r <= 64; and
- *            token counts whose output tiles leave most of the GPU idle), and
- *            at large token counts (from T = 1024, or 4096 where the output grid
- *            runs 256 x 256 tiles), where the weight is dequantized once into it
- *            (bf16 [d_out, d_in]: 2 d_in d_out bytes, the same values the fused
- *            kernels produce); when it is 0 the workspace may be NULL.
+ *            token counts whose output tiles leave most of the GPU idle); from
+ *            T = 1024 on 128 x 128 tiles, where the weight is dequantized once
+ *            into it (bf16 [d_out, d_in]: 2 d_in d_out bytes, the same values the
+ *            fused kernels produce); and from T = 4096 with d_in % 256 == 0,
+ *            r % 8 == 0, r <= 64 (256 x 256 tiles that dequantize into
+ *            registers), at ranks other than 16, where it holds A^T and
+ *            bf16(s x A) of a pass over x ahead of the tiles (2 r (d_in + T)
+ *            bytes, each part rounded up to 256; at r = 16 the tiles form x A
+ *            themselves). When it is 0 the workspace may be NULL.
  * T >= 0, d_in % 64 == 0, d_out >= 1 (any; a d_out that is not a multiple of 8, and
  * ranks r % 8 != 0 or r > 64, run the generic 128 x 128 kernels: same results,
  * lower speed), 1 <= r <= LN_MAX_RANK. s = lora_alpha / r
@@ -144,7 +148,10 @@ size_t lora_nf4_fwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int3
  *                        projections run one after the other on a path that
  *                        needs one (they reuse it in turn), and for one shared
  *                        launch at large token counts (every projection's
- *                        weight dequantized into it, one after another)
+ *                        weight dequantized into it, one after another; or,
+ *                        on register-dequantizing tiles at ranks other than
+ *                        16, A^T and bf16(s x A) of all projections: one pass
+ *                        over x when n_proj r <= 64, else one per projection)
  * All projections share T, d_in, r and lora_alpha. The host arrays are read
  * during the call only. Every output (each y[g], each u_save[g], the workspace)
  * must be disjoint from every input and from the other outputs (LN_EALIAS).

@@ -126,6 +126,13 @@ __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t rs, void* 
                                            16, static_cast<int>(voff), static_cast<int>(soff), 0, 0);
 }
 
+// 4 bytes per lane from global straight into LDS: lane i writes lds_base + 4 i.
+__device__ __forceinline__ void buf_load4_lds(__amdgpu_buffer_rsrc_t rs, void* lds_base, uint32_t voff,
+                                              uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds_base),
+                                           4, static_cast<int>(voff), static_cast<int>(soff), 0, 0);
+}
+
 // Wait until every vector-memory load this wave issued has landed (vmcnt = 0).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

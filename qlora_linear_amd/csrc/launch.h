@@ -44,6 +44,45 @@ hipError_t launch_lora_fwd_multi(int T, int K, int n_proj, const int* N, int r, 
                                  const uint16_t* const* B, uint16_t* const* y,
                                  uint16_t* const* u_save, void* workspace, hipStream_t stream);
 
+// Projections of one tiled forward launch (a single projection is a one-entry
+// table); tile_end[g] = column tiles of projections 0..g.
+struct ProjTable {
+  int n;
+  int tile_end[kMaxProj];
+  int N[kMaxProj];
+  const uint8_t* codes[kMaxProj];
+  const float* absmax[kMaxProj];
+  const uint16_t* wdq[kMaxProj];  // bf16 [N][K] dequantized weight (DQ kernels only)
+  const uint16_t* usg[kMaxProj];  // bf16(s U) [T][r] from the U pass (RU = 0 kernels only)
+  int us_stride;                  // row stride of usg (register-dequantizing kernel)
+  const uint16_t* A[kMaxProj];
+  const uint16_t* B[kMaxProj];
+  uint16_t* y[kMaxProj];
+  uint16_t* u[kMaxProj];
+};
+
+// U = x A of up to LN_MAX_PROJ projections that share x, in one pass over x:
+// us [T][n r] bf16(s U) side by side (set by launch_upass inside the workspace),
+// u[g] [T][r] bf16(U_g) (nullable). n r <= 64.
+struct UpassTable {
+  int n;
+  const uint16_t* A[kMaxProj];
+  uint16_t* u[kMaxProj];
+  uint16_t* us;
+};
+size_t upass_table_bytes(int64_t T, int64_t K, int n, int r);
+hipError_t launch_upass(int T, int K, int r, float s, const uint16_t* x, UpassTable& tab, void* workspace,
+                        hipStream_t stream);
+
+// Register-dequantizing forward (256 x 256 tiles, eight waves of 256 x 32): the
+// packed NF4 codes of a K-step go straight into MFMA B fragments in registers,
+// x runs through a four-stage LDS pipeline; at rank 16 U = x A is formed in the
+// K loop, otherwise bf16(s U) is read from tab.usg (the U pass).
+bool fwd_rw_supported(int64_t T, int64_t K, int r);
+bool fwd_rw_inloop_u(int r);  // the kernel computes U itself (no U pass, no workspace)
+hipError_t launch_fwd_rw(int T, int K, int r, float s, const uint16_t* x, const ProjTable& tab,
+                         hipStream_t stream);
+
 // Split-K weight-streaming forward for up to 128 tokens (r % 8 == 0, r <= 64):
 // workgroups of 64 weight rows x one of `splits` d_in chunks (plus one per split
 // and 16-wide rank block for U), fp32 partials [splits][T][N] and [splits][T][r]

@@ -64,20 +64,6 @@ struct FwdTile {
   static constexpr int kMinBlocks = BT == 128 ? 2 : 1;
 };
 
-// Projections of one launch; tile_end[g] = column tiles of projections 0..g.
-struct ProjTable {
-  int n;
-  int tile_end[kMaxProj];
-  int N[kMaxProj];
-  const uint8_t* codes[kMaxProj];
-  const float* absmax[kMaxProj];
-  const uint16_t* wdq[kMaxProj];  // bf16 [N][K] dequantized weight (DQ kernels only)
-  const uint16_t* usg[kMaxProj];  // bf16(s U) [T][r] from the U pass (RU = 0 kernels only)
-  const uint16_t* A[kMaxProj];
-  const uint16_t* B[kMaxProj];
-  uint16_t* y[kMaxProj];
-  uint16_t* u[kMaxProj];
-};
 
 // BT: tile edge; RU: U columns accumulated in the K-loop (16 for r <= 16, else r
 // rounded up to 32); RE: rank padded to the 16-wide reduction step of the
@@ -711,6 +697,40 @@ size_t dq_bytes(int64_t T, int64_t K, int64_t N, int r) {
   return b;
 }
 
+// From 4096 tokens on 256 x 256 tiles the register-dequantizing kernel
+// (lora_fwd_rw.hip) replaces dequantize-then-GEMM: the weight stays packed in HBM,
+// each tile dequantizes its 256 x 64 block of a step once, into MFMA fragments.
+// At rank 16 the kernel computes U = x A itself (no workspace). Otherwise U comes
+// from the U pass (lora_upass.hip; A^T and bf16(s U) in the workspace): one pass
+// over x for all projections when their ranks sum to at most 64, else one per
+// projection.
+bool fwd_rw(int64_t T, int64_t K, int bt, int r) { return bt == 256 && fwd_rw_supported(T, K, r); }
+size_t rw_bytes(int64_t T, int64_t K, int n, int r) {
+  if (fwd_rw_inloop_u(r)) return 0;
+  return n * r <= 64 ? upass_table_bytes(T, K, n, r) : n * upass_table_bytes(T, K, 1, r);
+}
+hipError_t launch_rw_with_upass(int T, int K, int r, float s, const uint16_t* x, ProjTable& tab, void* workspace,
+                                hipStream_t stream) {
+  if (fwd_rw_inloop_u(r)) return launch_fwd_rw(T, K, r, s, x, tab, stream);
+  unsigned char* w = static_cast<unsigned char*>(workspace);
+  const int groups = tab.n * r <= 64 ? 1 : tab.n;  // U passes
+  const int per = tab.n / groups;                   // projections per pass
+  for (int p = 0; p < groups; ++p) {
+    UpassTable ut{};
+    ut.n = per;
+    for (int g = 0; g < per; ++g) {
+      ut.A[g] = tab.A[p * per + g];
+      ut.u[g] = tab.u[p * per + g];
+    }
+    const hipError_t e = launch_upass(T, K, r, s, x, ut, w, stream);
+    if (e != hipSuccess) return e;
+    for (int g = 0; g < per; ++g) tab.usg[p * per + g] = ut.us + g * r;
+    w += upass_table_bytes(T, K, per, r);
+  }
+  tab.us_stride = per * r;
+  return launch_fwd_rw(T, K, r, s, x, tab, stream);
+}
+
 size_t tiled_split_bytes(int64_t T, int64_t N, int r, int splits) {
   if (splits <= 1) return 0;
   const size_t a = (static_cast<size_t>(splits) * T * N * 4 + 255) & ~static_cast<size_t>(255);
@@ -734,6 +754,7 @@ hipError_t launch_fwd_table(int T, int K, int r, float s, const uint16_t* x, Pro
   }
   TiledSplit sp{bt, 1, K / BK};
   if (tab.n == 1 && workspace != nullptr) sp = tiled_split(T, K, tab.N[0], r);
+  if (sp.splits == 1 && fwd_rw(T, K, bt, r)) return launch_rw_with_upass(T, K, r, s, x, tab, workspace, stream);
   // the weights of every projection dequantized one after another into the workspace
   const bool dq = workspace != nullptr && sp.splits == 1 && fwd_dq(T, bt);
   const bool ug = dq && fwd_ug(T, r);
@@ -796,6 +817,7 @@ size_t fwd_workspace_bytes(int64_t T, int64_t K, int64_t N, int r) {
     return plan_fwd_splitk(static_cast<int>(T), static_cast<int>(K), static_cast<int>(N), r).bytes;
   if (r % 8 != 0 || r > 64 || !fits_buffer(T, K, N) || lora_fwd_stream_supported(T, r)) return 0;
   const TiledSplit ts = tiled_split(T, K, N, r);
+  if (ts.splits == 1 && fwd_rw(T, K, ts.bt, r)) return rw_bytes(T, K, 1, r);
   if (ts.splits == 1 && fwd_dq(T, ts.bt)) return dq_bytes(T, K, N, r);
   return tiled_split_bytes(T, N, r, ts.splits);
 }
@@ -813,6 +835,7 @@ int table_edge(int64_t T, int n_proj, const int* N, int r) {
 
 size_t fwd_multi_workspace_bytes(int64_t T, int64_t K, int n_proj, const int* N, int r) {
   if (fwd_multi_tiled(T, K, n_proj, N, r)) {
+    if (fwd_rw(T, K, table_edge(T, n_proj, N, r), r)) return rw_bytes(T, K, n_proj, r);
     size_t b = 0;
     for (int g = 0; fwd_dq(T, table_edge(T, n_proj, N, r)) && g < n_proj; ++g) b += dq_bytes(T, K, N[g], r);
     return b;
@@ -871,8 +894,8 @@ hipError_t launch_lora_fwd_multi(int T, int K, int n_proj, const int* N, int r, 
     tab.y[g] = y[g];
     tab.u[g] = u_save == nullptr ? nullptr : u_save[g];
   }
-  return launch_fwd_table(T, K, r, s, x, tab, fwd_dq(T, table_edge(T, n_proj, N, r)) ? workspace : nullptr,
-                          stream);
+  const int bt = table_edge(T, n_proj, N, r);
+  return launch_fwd_table(T, K, r, s, x, tab, fwd_rw(T, K, bt, r) || fwd_dq(T, bt) ? workspace : nullptr, stream);
 }
 
 }  // namespace lnf4

@@ -96,8 +96,13 @@ def test_fwd_workspace(lib):
     assert lib.lora_nf4_fwd_workspace_bytes(8, 4096, 8192, 16) > 0       # few tokens, wide d_out
     assert lib.lora_nf4_fwd_workspace_bytes(8, 4096, 4096, 16) == 0      # few tokens: streaming
     assert lib.lora_nf4_fwd_workspace_bytes(1000, 4096, 4096, 16) == 0   # tiled
-    # from 1024 tokens the weight is dequantized once into the workspace (bf16)
-    assert lib.lora_nf4_fwd_workspace_bytes(8192, 4096, 4096, 16) == 4096 * 4096 * 2
+    # from 4096 tokens on 256 x 256 tiles (d_in % 256 == 0) the weight stays packed:
+    # at rank 16 the kernel computes U itself (no workspace); at other ranks the
+    # workspace holds A^T and bf16(s U) of the U pass
+    assert lib.lora_nf4_fwd_workspace_bytes(8192, 4096, 4096, 16) == 0
+    assert lib.lora_nf4_fwd_workspace_bytes(8192, 4096, 4096, 32) == 32 * 4096 * 2 + 8192 * 32 * 2
+    # from 1024 tokens on 128 x 128 tiles the weight is dequantized once into it (bf16)
+    assert lib.lora_nf4_fwd_workspace_bytes(2048, 4096, 4096, 16) >= 4096 * 4096 * 2
     assert lib.lora_nf4_fwd_workspace_bytes(1024, 320, 200, 16) == (320 * 200 * 2 + 255) // 256 * 256
     assert lib.lora_nf4_fwd_workspace_bytes(64, 64, 64, 12) == 0         # r % 8 != 0: generic kernels
     assert lib.lora_nf4_fwd_workspace_bytes(0, 64, 64, 8) == 0
@@ -108,12 +113,15 @@ def test_fwd_workspace(lib):
     assert _fwd(lib, T=64, ws=P + (5 << 30)) == LN_EALIAS            # workspace on top of y
     assert _fwd(lib, T=64, ws=P + (3 << 30)) == LN_EALIAS            # workspace on top of A
     assert _fwd(lib, T=0, ws=None, ws_bytes=0) == LN_OK
-    # multi: the largest per-projection need, none for the tiled single launch
+    # multi: the largest per-projection need when the projections run one by one
     vp = ctypes.c_void_p
     d_out = (ctypes.c_int64 * 3)(64, 16, 16)
     assert lib.lora_nf4_fwd_multi_workspace_bytes(64, 64, 3, ctypes.cast(d_out, vp), 8) == need
     big = (ctypes.c_int64 * 3)(4096, 1024, 1024)
-    assert lib.lora_nf4_fwd_multi_workspace_bytes(8192, 4096, 3, ctypes.cast(big, vp), 16) == 6144 * 4096 * 2
+    # one launch of 256 x 256 register-dequantizing tiles: at rank 16 U is computed in
+    # the kernel (none); at rank 32 one U pass per projection (A^T and bf16(s U) each)
+    assert lib.lora_nf4_fwd_multi_workspace_bytes(8192, 4096, 3, ctypes.cast(big, vp), 16) == 0
+    assert lib.lora_nf4_fwd_multi_workspace_bytes(8192, 4096, 3, ctypes.cast(big, vp), 32) == 3 * (32 * 4096 * 2 + 8192 * 32 * 2)
     assert lib.lora_nf4_fwd_multi_workspace_bytes(64, 64, 0, ctypes.cast(d_out, vp), 8) == 0
 
 

@@ -176,6 +176,24 @@ def test_forward_u_pass(q, T, K, N, r):
     _check_full(q, inp, 16.0, r, f"u-pass T={T} K={K} N={N} r={r}")
 
 
+# From 4096 tokens, where the grid takes 256 x 256 tiles and d_in % 256 == 0, the
+# forward runs the register-dequantizing kernel (packed codes straight into MFMA
+# fragments, x through a four-stage LDS ring, U from the U pass): ragged T and
+# d_out (partial tiles in both directions), ranks 8 .. 64, one to four groups of
+# four K-steps; the full oracle on every output, and bitwise determinism.
+RW = [(4100, 512, 2056, 16), (4350, 768, 2104, 24), (4096, 1024, 4104, 64), (8192, 256, 1032, 8)]
+
+
+@pytest.mark.parametrize("T,K,N,r", RW)
+def test_forward_register_dequant(q, T, K, N, r):
+    inp = synth.custom_inputs(16, T, K, N, r)
+    assert q.lora_nf4_fwd_workspace_bytes(T, K, N, r) < K * N * 2  # no dequantized weight
+    _check_full(q, inp, 16.0, r, f"rw T={T} K={K} N={N} r={r}")
+    r1 = _run_gpu(q, inp, 16.0)
+    r2 = _run_gpu(q, inp, 16.0)
+    assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
+
+
 # From 4096 tokens on 256 x 256 dX tiles (1024 on 128 x 128 tiles) the dX kernel
 # runs on the weight dequantized once into the workspace. Large token counts,
 # ragged T and d_in, one to eight d_out steps, ranks 8 and 16; the full oracle on
@@ -431,7 +449,18 @@ def test_fwd_multi_full_size_qkv(q):
         c, a = q.nf4_quantize(dev_bf16(inp["W"]))
         codes.append(c), absmax.append(a), A.append(dev_bf16(inp["A"])), B.append(dev_bf16(inp["B"]))
     ys, us = q.lora_nf4_fwd_multi(x, codes, absmax, A, B, w.alpha)
+    # the shared launch runs 256 x 256 register-dequantizing tiles over all three
+    # projections; a separate k or v call (1024 columns) runs 128 x 128 tiles, whose
+    # summation order differs: equal U (the same U pass), y within the tolerance of
+    # each other, and sampled rows against the oracle
+    rows = _sample_rows(w.tokens, n=6, seed=3)
+    rows_t = torch.from_numpy(rows).cuda()
+    from tests.gpu_util import host_f64
     for g in range(3):
         y1, u1 = q.lora_nf4_fwd(x, codes[g], absmax[g], A[g], B[g], w.alpha)
         torch.cuda.synchronize()
-        assert torch.equal(ys[g], y1) and torch.equal(us[g], u1), g
+        assert torch.equal(us[g], u1), g
+        assert olora.rel_err(host_f64(ys[g]), host_f64(y1)) <= TOL, g
+        y_ref, _ = olora.forward(_f64(ins[0]["x"][rows]), _oracle_D(ins[g]), _f64(ins[g]["A"]), _f64(ins[g]["B"]),
+                                 w.alpha, w.r)
+        assert olora.rel_err(host_f64(ys[g][rows_t]), y_ref) <= TOL, g
