@@ -15,6 +15,12 @@ hipError_t launch_nf4_quantize(const void* w, bool w_is_bf16, int64_t rows, int6
 hipError_t launch_nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows,
                                  int64_t cols, bool out_bf16, void* out, hipStream_t stream);
 
+// The packed weight of N rows x K columns transposed: codes_t [K][N/2] (code of
+// (n, k) in byte n / 2 of row k, the even n in the low nibble) and absmax_t
+// [K/64][N]. N % 128 == 0, K % 128 == 0.
+hipError_t launch_nf4_transpose(const uint8_t* codes, const float* absmax, int64_t N, int64_t K,
+                                uint8_t* codes_t, float* absmax_t, hipStream_t stream);
+
 // Zero n 16-bit elements (a fill kernel, so the call can sit in a captured graph).
 hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t stream);
 
@@ -82,6 +88,15 @@ bool fwd_rw_supported(int64_t T, int64_t K, int r);
 bool fwd_rw_inloop_u(int r);  // the kernel computes U itself (no U pass, no workspace)
 hipError_t launch_fwd_rw(int T, int K, int r, float s, const uint16_t* x, const ProjTable& tab,
                          hipStream_t stream);
+// dX on register-dequantized 256 x 256 tiles (rank 16, from 4096 tokens, d_in and
+// d_out multiples of 256): the packed weight is transposed into the workspace
+// (dx_rw_bytes), then one launch forms dX and bf16(s G) into g_out [T][16]. dx
+// null: G only (the same tiles' G, one column tile per token tile).
+bool dx_rw_supported(int64_t T, int64_t K, int64_t N, int r);
+size_t dx_rw_bytes(int64_t K, int64_t N);
+hipError_t launch_dx_rw(int T, int K, int N, float s, const uint16_t* dy, const uint8_t* codes,
+                        const float* absmax, const uint16_t* A, const uint16_t* B, uint16_t* dx,
+                        uint16_t* g_out, void* workspace, hipStream_t stream);
 
 // Split-K weight-streaming forward for up to 128 tokens (r % 8 == 0, r <= 64):
 // workgroups of 64 weight rows x one of `splits` d_in chunks (plus one per split
@@ -223,7 +238,8 @@ struct BwdPlan {
   size_t off_g, off_u, off_pa, off_pb;  // byte offsets into the workspace
   size_t off_px, off_pg;                // weight-streaming dX partials
   bool dqx;                             // tiled dX on the dequantized weight (dx_dq)
-  size_t off_w;                         // that weight, bf16 [N][K]
+  bool rwx;                             // dX on register-dequantized tiles (dx_rw_supported)
+  size_t off_w;                         // dqx: that weight, bf16 [N][K]; rwx: the transposed packed weight
   size_t bytes;       // total workspace bytes
 };
 // allow_dq = false: never the dequantized-weight dX (its workspace holds 2 d_in d_out

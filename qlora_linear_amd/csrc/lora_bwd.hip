@@ -383,6 +383,8 @@ hipError_t launch_bwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
     e = launch_lora_dx_splitk(T, K, N, r, s, dy, codes, absmax, A, B, dx, g,
                               reinterpret_cast<float*>(ws + p.off_px),
                               reinterpret_cast<float*>(ws + p.off_pg), stream);
+  } else if (p.rwx) {
+    e = launch_dx_rw(T, K, N, s, dy, codes, absmax, A, B, dx, g, ws + p.off_w, stream);
   } else if (p.fast) {
     const bool split = p.splits_x > 1;
     uint16_t* w = p.dqx ? reinterpret_cast<uint16_t*>(ws + p.off_w) : nullptr;
@@ -520,6 +522,10 @@ BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r, bool allow_dq) {
       off = align256(off + static_cast<size_t>(d.splits) * T * K * 4);
       p.off_pg = off;
       off = align256(off + static_cast<size_t>(d.splits) * T * r * 4);
+    } else if (dx_rw_supported(T, K, N, r)) {
+      p.rwx = true;
+      p.off_w = off;
+      off = align256(off + dx_rw_bytes(K, N));
     } else if (allow_dq && dx_dq(T, K, N, r)) {
       p.dqx = true;
       p.off_w = off;

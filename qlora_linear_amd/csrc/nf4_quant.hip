@@ -125,12 +125,60 @@ hipError_t launch_nf4_dequantize(const uint8_t* codes, const float* absmax, int6
 }
 
 namespace {
+// codes [N][K/2] -> codes^T [K][N/2] and absmax [N][K/64] -> absmax^T [K/64][N]. A
+// 256-thread workgroup takes 128 weight rows x 128 columns: thread (g, c) reads
+// the code dwords of rows 8 g .. 8 g + 7 at dword column c (8 columns each, 64
+// bytes of a row per 16 threads), transposes the 8 x 8 nibbles in registers and
+// stages them in LDS, from where each thread stores 32 bytes of one codes^T row.
+__global__ __launch_bounds__(256) void nf4_transpose_kernel(const uint32_t* __restrict__ codes,
+                                                            const float* __restrict__ absmax, int N, int K,
+                                                            uint32_t* __restrict__ codes_t,
+                                                            float* __restrict__ absmax_t) {
+  __shared__ uint32_t tile[128 * 17];  // [column][row group of 8], padded
+  const int tid = threadIdx.x, g = tid >> 4, c = tid & 15;
+  const int n0 = blockIdx.y * 128, k0 = blockIdx.x * 128;
+  const int kw = K / 8, nw = N / 8;  // dwords per row of codes, of codes^T
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = codes[static_cast<size_t>(n0 + 8 * g + i) * kw + k0 / 8 + c];
+  // w[i] nibble j = code(n0 + 8 g + i, k0 + 8 c + j)  ->  o[j] nibble i
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t o = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o |= ((w[i] >> (4 * j)) & 15u) << (4 * i);
+    tile[(8 * c + j) * 17 + g] = o;
+  }
+  {  // absmax: 128 rows x 2 blocks
+    const int n = tid & 127, kb = tid >> 7;
+    absmax_t[static_cast<size_t>(k0 / 64 + kb) * N + n0 + n] = absmax[static_cast<size_t>(n0 + n) * (K / 64) + k0 / 64 + kb];
+  }
+  __syncthreads();
+  const int row = tid >> 1, half = tid & 1;  // codes^T row k0 + row, dwords 8 half .. +7 of the block
+  uint32_t v[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) v[q] = tile[row * 17 + 8 * half + q];
+  uint4* dst = reinterpret_cast<uint4*>(codes_t + static_cast<size_t>(k0 + row) * nw + n0 / 8 + 8 * half);
+  dst[0] = uint4{v[0], v[1], v[2], v[3]};
+  dst[1] = uint4{v[4], v[5], v[6], v[7]};
+}
+
 __global__ void zero_u16_kernel(uint16_t* __restrict__ p, int64_t n) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x)
     p[i] = 0;
 }
 }  // namespace
+
+hipError_t launch_nf4_transpose(const uint8_t* codes, const float* absmax, int64_t N, int64_t K,
+                                uint8_t* codes_t, float* absmax_t, hipStream_t stream) {
+  if (N % 128 != 0 || K % 128 != 0) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(K / 128), static_cast<unsigned>(N / 128));
+  nf4_transpose_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<const uint32_t*>(codes), absmax,
+                                                 static_cast<int>(N), static_cast<int>(K),
+                                                 reinterpret_cast<uint32_t*>(codes_t), absmax_t);
+  return hipGetLastError();
+}
 
 hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;

@@ -172,17 +172,27 @@ def test_fwd_multi_validation(lib):
 
 def test_bwd_workspace_holds_the_dequantized_weight_at_large_token_counts(lib):
     """dX runs on a bf16 copy of the weight from 1024 tokens on 128 x 128 tiles and
-    from 4096 on 256 x 256 tiles (q_proj 4096 x 4096 takes 128 tiles at 1024 tokens
-    and 256 at 4095 and 4096): the workspace grows by at least 2 d_in d_out bytes
-    across each threshold."""
+    (ranks other than 16) from 4096 on 256 x 256 tiles (q_proj 4096 x 4096 takes 128
+    tiles at 1024 tokens and 256 at 4095 and 4096): the workspace grows by at least
+    2 d_in d_out bytes across each threshold. At rank 16 the 256 x 256 dX tiles
+    dequantize in registers from the packed weight transposed into the workspace:
+    d_in d_out / 2 bytes of codes plus d_in d_out / 16 of absmax."""
     K = N = 4096
     w = 2 * K * N
+    packed_t = K * N // 2 + (K // 64) * N * 4
     for r in (16, 64):
         assert lib.lora_nf4_bwd_workspace_bytes(1023, K, N, r) < w
         assert lib.lora_nf4_bwd_workspace_bytes(1024, K, N, r) - lib.lora_nf4_bwd_workspace_bytes(1023, K, N, r) >= w
         assert lib.lora_nf4_bwd_workspace_bytes(4095, K, N, r) < w
-        assert lib.lora_nf4_bwd_workspace_bytes(4096, K, N, r) - lib.lora_nf4_bwd_workspace_bytes(4095, K, N, r) >= w
-        assert lib.lora_nf4_bwd_workspace_bytes(8192, K, N, r) >= w
+    r = 64
+    assert lib.lora_nf4_bwd_workspace_bytes(4096, K, N, r) - lib.lora_nf4_bwd_workspace_bytes(4095, K, N, r) >= w
+    assert lib.lora_nf4_bwd_workspace_bytes(8192, K, N, r) >= w
+    r = 16
+    grow = lib.lora_nf4_bwd_workspace_bytes(4096, K, N, r) - lib.lora_nf4_bwd_workspace_bytes(4095, K, N, r)
+    assert packed_t <= grow < w
+    assert lib.lora_nf4_bwd_workspace_bytes(8192, K, N, r) < w
+    # the register path needs whole 256-column tiles on both sides: d_out = 4160 falls back
+    assert lib.lora_nf4_bwd_workspace_bytes(8192, K, 4160, r) >= 2 * K * 4160
 
 
 def test_bwd_validation_and_workspace(lib):

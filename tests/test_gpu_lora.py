@@ -194,8 +194,29 @@ def test_forward_register_dequant(q, T, K, N, r):
     assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
 
 
-# From 4096 tokens on 256 x 256 dX tiles (1024 on 128 x 128 tiles) the dX kernel
-# runs on the weight dequantized once into the workspace. Large token counts,
+# From 4096 tokens at rank 16, d_in and d_out multiples of 256, dX runs on
+# register-dequantized 256 x 256 tiles: the packed weight transposed once into the
+# workspace (codes^T, absmax^T), its codes straight into MFMA fragments, G = s dY
+# B^T in the same loop. Ragged T, one to three column tiles, one to four groups of
+# four d_out steps; the full oracle on every output, bitwise determinism, and the
+# dX-less call (G only) giving the same dA and dB bits.
+RWX = [(4100, 512, 256, 16), (4350, 768, 1024, 16), (8192, 256, 512, 16)]
+
+
+@pytest.mark.parametrize("T,K,N,r", RWX)
+def test_dx_register_dequant(q, T, K, N, r):
+    inp = synth.custom_inputs(17, T, K, N, r, dy_std=0.1)
+    _check_full(q, inp, 16.0, r, f"rwx T={T} K={K} N={N} r={r}")
+    r1 = _run_gpu(q, inp, 16.0)
+    r2 = _run_gpu(q, inp, 16.0)
+    assert all(torch.equal(a, b) for a, b in zip(r1[2:], r2[2:]))
+    _, _, dx3, dA3, dB3 = _run_gpu(q, inp, 16.0, need_dx=False)
+    assert dx3 is None and torch.equal(dA3, r1[3]) and torch.equal(dB3, r1[4])
+
+
+# From 4096 tokens on 256 x 256 dX tiles (1024 on 128 x 128 tiles; at rank 16 only
+# where the register path above does not apply) the dX kernel runs on the weight
+# dequantized once into the workspace. Large token counts,
 # ragged T and d_in, one to eight d_out steps, ranks 8 and 16; the full oracle on
 # every output.
 DQ_BWD = [(8200, 320, 192, 16), (8230, 192, 128, 8), (9000, 128, 64, 16), (8300, 448, 512, 16)]
@@ -253,7 +274,7 @@ def test_dx_tile_edges_agree(q, r):
 
 
 @pytest.mark.parametrize("T,K,N,r", [(300, 256, 192, 16), (7, 320, 200, 24), (8200, 256, 192, 16),
-                                     (48, 4096, 1024, 16), (4100, 512, 256, 64)])
+                                     (48, 4096, 1024, 16), (4100, 512, 256, 64), (4352, 512, 512, 16)])
 def test_recompute_u_and_skip_dx_paths(q, T, K, N, r):
     """The backward with u_saved = NULL recomputes U = x A itself; its dX, dA and dB
     are checked against the oracle directly (tiled, few-token, split-K and
