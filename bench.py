@@ -45,9 +45,15 @@ import synth  # noqa: E402
 METRIC = "fused NF4-LoRA linear fwd+bwd TFLOP/s & tokens/s, % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 bf16 FLOP/clk x 2.4 GHz (published: 2.5 PFLOP/s dense)
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_lora_fwd_kernel_llama3-8b-q_proj.json")
-FWD_SOURCES = ("qlora_linear_amd/csrc/lora_fwd.hip", "qlora_linear_amd/csrc/nf4_quant.hip",
-               "qlora_linear_amd/csrc/device_common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_lora_fwd_rw_kernel_llama3-8b-q_proj.json")
+FWD_SOURCES = ("qlora_linear_amd/csrc/lora_rw.hip", "qlora_linear_amd/csrc/lora_fwd.hip",
+               "qlora_linear_amd/csrc/nf4_quant.hip", "qlora_linear_amd/csrc/device_common.h")
+# tile kernels of the forward and of dX, and the launches that may precede them in
+# the same call (the weight dequantized to bf16 with staging on; the packed weight
+# transposed for the register-dequantizing dX)
+FWD_KERNELS = ("lora_fwd_rw_kernel", "lora_fwd_kernel")
+DX_KERNELS = ("lora_dx_rw_kernel", "lora_dx_kernel")
+PRE_KERNELS = ("nf4_dequantize_kernel", "nf4_transpose_kernel")
 
 
 def parse():
@@ -68,6 +74,14 @@ def parse():
                     help="token count of the weight-bound measurement (0: skip)")
     ap.add_argument("--medium-tokens", type=int, default=512,
                     help="token count of the medium-size measurement (0: skip)")
+    ap.add_argument("--staged", action="store_true",
+                    help="time the headline with weight staging on (lora_nf4_set_weight_staging(1))")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the staging, cold-cache and per-config legs")
+    ap.add_argument("--sustain-s", type=float, default=2.0,
+                    help="seconds of back-to-back headline steps with the clock sampled (0: skip)")
+    ap.add_argument("--leg-steps", type=int, default=10,
+                    help="timed steps of each per-config leg")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run under rocprofv3 --pmc: one plain copy of COPY_BYTES (calibration), "
                          "then --steps fwd+bwd steps; prints nothing else")
@@ -119,26 +133,30 @@ def counter_dispatches(d: str, counter: str) -> list:
 
 
 def forward_kib(disp: list) -> tuple:
-    """Mean counter value (KiB) per forward call and per other kernel. From 1024 tokens a
-    forward call is two launches, the weight's dequantization and the tile kernel
-    (lora_fwd_kernel); the backward's input gradient likewise pairs it with the dX tile
-    kernel (lora_dx_kernel)."""
+    """Mean counter value (KiB) per forward call and per other kernel. A forward call
+    is the tile kernel (lora_fwd_rw_kernel, or lora_fwd_kernel), preceded with weight
+    staging on by the weight's dequantization (counted with it); the backward's input
+    gradient pairs its tile kernel with the launch before it the same way (the
+    dequantization, or the transposition of the packed weight)."""
     import collections
     fwd, other = [], collections.defaultdict(list)
     prev = None
+    short = lambda name, keys: next((k for k in keys if k in name), None)
     for _, name, v in disp:
-        after_dq = prev is not None and "nf4_dequantize_kernel" in prev[0]
-        if "lora_fwd_kernel" in name:
-            fwd.append(prev[1] + v if after_dq else v)
-        elif "lora_dx_kernel" in name and after_dq:
-            other["lora_dx (nf4_dequantize_kernel + lora_dx_kernel)"].append(prev[1] + v)
-        elif "nf4_dequantize" not in name:
-            for key in ("lora_dx_kernel", "skinny_partial_kernel", "skinny_reduce2_kernel", "MulFunctor"):
+        pre = short(prev[0], PRE_KERNELS) if prev is not None else None
+        fk, dk = short(name, FWD_KERNELS), short(name, DX_KERNELS)
+        if fk is not None:
+            fwd.append(prev[1] + v if pre == "nf4_dequantize_kernel" else v)
+        elif dk is not None and pre is not None:
+            other[f"lora_dx ({pre} + {dk})"].append(prev[1] + v)
+        elif short(name, PRE_KERNELS) is None:
+            for key in DX_KERNELS + ("skinny_partial_kernel", "skinny_reduce2_kernel", "MulFunctor"):
                 if key in name:
                     other[key].append(v)
+                    break
         prev = (name, v)
     if not fwd:
-        raise SystemExit("no dispatch of lora_fwd_kernel in the counter data")
+        raise SystemExit("no dispatch of a forward tile kernel in the counter data")
     return sum(fwd) / len(fwd), {k: sum(v) / len(v) for k, v in other.items()}
 
 
@@ -150,7 +168,7 @@ def ingest_counters(fetch_dir: str, write_dir: str):
         raise SystemExit("no dispatch of the calibration copy in the counter data")
     cal_f = (COPY_BYTES / 1024) / fetch_other[copy_key]
     cal_w = (COPY_BYTES / 1024) / write_other[copy_key]
-    rec = {"kernel": "lora_fwd (nf4_dequantize_kernel + lora_fwd_kernel at large token counts)",
+    rec = {"kernel": "lora_fwd_rw_kernel (the forward call at 8192 tokens: one launch)",
            "workload": "llama3-8b-q_proj",
            "commands": ["rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o run --output-format csv -- "
                         "python3 bench.py --counter-pass --steps 2",
@@ -175,11 +193,8 @@ def cpu_baseline(w: synth.Workload, target_s: float):
     token sample sized to take about target_s seconds on this host."""
     from oracle import lora as olora
     from oracle import nf4 as onf4
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    host = host_facts()
+    cores = host["blas_threads"] or host["nproc"]
     p = w.projections[0]
     inp = synth.projection_inputs(w, 0)
     codes, absmax = onf4.quantize(synth.bf16_bits_to_f32(inp["W"]))   # one-time, not timed
@@ -197,19 +212,49 @@ def cpu_baseline(w: synth.Workload, target_s: float):
     dt = time.perf_counter() - t0
     tok = int(min(w.tokens, max(64, tok * target_s / max(dt, 1e-3))))
     tok = max(64, (tok // 64) * 64)
-    # the whole workload may take well under target_s on a fast host: repeat it
-    reps = max(1, min(20, int(target_s / max(dt * tok / min(256, w.tokens), 1e-3))))
-    t0 = time.perf_counter()
-    for _ in range(reps):
+    # three passes over the sample (the median is reported); a pass is sized so the
+    # three take about target_s together
+    tok = int(min(w.tokens, max(64, tok * (target_s / 3) / max(dt, 1e-3))))
+    tok = max(64, (tok // 64) * 64)
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
         step(tok)
-    dt = (time.perf_counter() - t0) / reps
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
     fl = synth.flops(tok, p.d_in, p.d_out, w.r)
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle", "seconds_per_pass": round(dt, 3), "passes": reps,
-            "tokens_per_s": round(tok / dt, 1),
-            "sample": f"{p.name} {p.d_in}->{p.d_out} r={w.r}, {tok} of {w.tokens} tokens"
-                      f"{f' x {reps} passes' if reps > 1 else ''}, "
+            "kind": "oracle", "seconds_per_pass": round(dt, 3), "passes": 3, "statistic": "median",
+            "tokens_per_s": round(tok / dt, 1), "host": host,
+            "sample": f"{p.name} {p.d_in}->{p.d_out} r={w.r}, {tok} of {w.tokens} tokens x 3 passes, "
                       f"fp64 NumPy fwd+bwd incl. dequantization"}
+
+
+def host_facts() -> dict:
+    """The host the CPU baseline runs on: logical CPUs, CPU model, the BLAS library
+    NumPy calls and its thread count."""
+    facts = {"nproc": os.cpu_count(), "cpu_model": None, "blas": None, "blas_threads": None}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    facts["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        facts["sched_affinity"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            facts["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            facts["blas_threads"] = int(blas[0].get("num_threads", 1))
+    except Exception:  # pragma: no cover
+        pass
+    return facts
 
 
 def time_fwd_bwd(lib, q, torch, d, w, tokens, sp, reps):
@@ -456,6 +501,326 @@ def to_dev_bf16(bits):
     return t.to("cuda").view(torch.bfloat16)
 
 
+class Runner:
+    """One workload resident on the GPU: inputs drawn from synth (seeded), NF4
+    weights quantized once (model load), every output and workspace allocated up
+    front. step() enqueues one forward + backward of every projection (or of every
+    fused group, see --fuse) through the C ABI on the current stream."""
+
+    def __init__(self, lib, q, torch, w, fuse):
+        import ctypes
+        self.lib, self.q, self.w = lib, q, w
+        self.sp = torch.cuda.current_stream().cuda_stream
+        projs = []
+        for pi, p in enumerate(w.projections):
+            inp = synth.projection_inputs(w, pi)
+            x, W, A, B, dY = (to_dev_bf16(inp[k]) for k in ("x", "W", "A", "B", "dY"))
+            del inp
+            codes, absmax = q.nf4_quantize(W)
+            del W
+            T, K, N, r = w.tokens, p.d_in, p.d_out, w.r
+            projs.append(dict(p=p, x=x, A=A, B=B, dY=dY, codes=codes, absmax=absmax,
+                              y=torch.empty((T, N), dtype=torch.bfloat16, device="cuda"),
+                              u=torch.empty((T, r), dtype=torch.bfloat16, device="cuda"),
+                              dx=torch.empty((T, K), dtype=torch.bfloat16, device="cuda"),
+                              dA=torch.empty((K, r), dtype=torch.bfloat16, device="cuda"),
+                              dB=torch.empty((r, N), dtype=torch.bfloat16, device="cuda")))
+        # forward units: one projection each, or (fuse) the groups that share x
+        units, seen = [], {}
+        for j, d in enumerate(projs):
+            key = {"q_proj": "qkv", "k_proj": "qkv", "v_proj": "qkv", "gate_proj": "gu",
+                   "up_proj": "gu"}.get(d["p"].name) if fuse else None
+            if key is not None and key in seen:
+                units[seen[key]].append(j)
+                d["x"] = projs[units[seen[key]][0]]["x"]  # the group reads one x
+            else:
+                if key is not None:
+                    seen[key] = len(units)
+                units.append([j])
+        self.projs, self.units = projs, units
+        self.multi = {}
+        for ui, un in enumerate(units):
+            if len(un) > 1:
+                arr = lambda key: (ctypes.c_void_p * len(un))(*[projs[j][key].data_ptr() for j in un])
+                self.multi[ui] = dict(d_out=(ctypes.c_int64 * len(un))(*[projs[j]["p"].d_out for j in un]),
+                                      codes=arr("codes"), absmax=arr("absmax"), A=arr("A"), B=arr("B"),
+                                      y=arr("y"), u=arr("u"), dy=arr("dY"), dA=arr("dA"), dB=arr("dB"))
+        self.size_workspaces(torch)
+
+    def size_workspaces(self, torch):
+        """(Re)allocate the workspaces for the current weight-staging mode."""
+        q, w = self.q, self.w
+        for d in self.projs:
+            T, K, N, r = w.tokens, d["p"].d_in, d["p"].d_out, w.r
+            d["ws"] = torch.empty(max(q.lora_nf4_bwd_workspace_bytes(T, K, N, r), 256), dtype=torch.uint8,
+                                  device="cuda")
+            d["fws"] = torch.empty(max(q.lora_nf4_fwd_workspace_bytes(T, K, N, r), 256), dtype=torch.uint8,
+                                   device="cuda")
+        for ui, m in self.multi.items():
+            un = self.units[ui]
+            d_out = [self.projs[j]["p"].d_out for j in un]
+            K = self.projs[un[0]]["p"].d_in
+            m["ws"] = torch.empty(max(q.lora_nf4_bwd_multi_workspace_bytes(w.tokens, K, d_out, w.r), 256),
+                                  dtype=torch.uint8, device="cuda")
+            m["fws"] = torch.empty(max(q.lora_nf4_fwd_multi_workspace_bytes(w.tokens, K, d_out, w.r), 256),
+                                   dtype=torch.uint8, device="cuda")
+            for j in un:  # the group's per-projection workspaces are not used
+                self.projs[j]["ws"] = self.projs[j]["fws"] = None
+        torch.cuda.empty_cache()
+
+    def fwd_unit(self, ui):
+        import ctypes
+        lib, q, w, sp = self.lib, self.q, self.w, self.sp
+        un = self.units[ui]
+        if len(un) == 1:
+            d = self.projs[un[0]]
+            p = d["p"]
+            st = lib.lora_nf4_fwd(w.tokens, p.d_in, p.d_out, w.r, w.alpha, d["x"].data_ptr(),
+                                  d["codes"].data_ptr(), d["absmax"].data_ptr(), d["A"].data_ptr(),
+                                  d["B"].data_ptr(), d["y"].data_ptr(), d["u"].data_ptr(), d["fws"].data_ptr(),
+                                  d["fws"].numel(), sp)
+            if st != 0:
+                raise q.LoraNF4Error("lora_nf4_fwd", st)
+            return
+        m, d0 = self.multi[ui], self.projs[un[0]]
+        cv = lambda a: ctypes.cast(a, ctypes.c_void_p)
+        st = lib.lora_nf4_fwd_multi(w.tokens, d0["p"].d_in, len(un), cv(m["d_out"]), w.r, w.alpha,
+                                    d0["x"].data_ptr(), cv(m["codes"]), cv(m["absmax"]), cv(m["A"]),
+                                    cv(m["B"]), cv(m["y"]), cv(m["u"]), m["fws"].data_ptr(), m["fws"].numel(), sp)
+        if st != 0:
+            raise q.LoraNF4Error("lora_nf4_fwd_multi", st)
+
+    def bwd_unit(self, ui):
+        import ctypes
+        lib, q, w, sp = self.lib, self.q, self.w, self.sp
+        un = self.units[ui]
+        if len(un) == 1:
+            d = self.projs[un[0]]
+            p = d["p"]
+            st = lib.lora_nf4_bwd(w.tokens, p.d_in, p.d_out, w.r, w.alpha, d["x"].data_ptr(),
+                                  d["dY"].data_ptr(), d["codes"].data_ptr(), d["absmax"].data_ptr(),
+                                  d["A"].data_ptr(), d["B"].data_ptr(), d["u"].data_ptr(),
+                                  d["dx"].data_ptr(), d["dA"].data_ptr(), d["dB"].data_ptr(),
+                                  d["ws"].data_ptr(), d["ws"].numel(), sp)
+            if st != 0:
+                raise q.LoraNF4Error("lora_nf4_bwd", st)
+            return
+        m, d0 = self.multi[ui], self.projs[un[0]]
+        cv = lambda a: ctypes.cast(a, ctypes.c_void_p)
+        st = lib.lora_nf4_bwd_multi(w.tokens, d0["p"].d_in, len(un), cv(m["d_out"]), w.r, w.alpha,
+                                    d0["x"].data_ptr(), cv(m["dy"]), cv(m["codes"]), cv(m["absmax"]),
+                                    cv(m["A"]), cv(m["B"]), cv(m["u"]), d0["dx"].data_ptr(), cv(m["dA"]),
+                                    cv(m["dB"]), m["ws"].data_ptr(), m["ws"].numel(), sp)
+        if st != 0:
+            raise q.LoraNF4Error("lora_nf4_bwd_multi", st)
+
+    def step(self):
+        for ui in range(len(self.units)):
+            self.fwd_unit(ui)
+            self.bwd_unit(ui)
+
+    def flops(self):
+        w = self.w
+        return sum(synth.flops(w.tokens, d["p"].d_in, d["p"].d_out, w.r) for d in self.projs)
+
+    def big_unit(self):
+        """(unit index, its projections' forward FLOPs, label) of the unit holding the largest projection."""
+        projs, w = self.projs, self.w
+        big = max(range(len(projs)), key=lambda j: projs[j]["p"].d_in * projs[j]["p"].d_out)
+        bu = next(ui for ui, un in enumerate(self.units) if big in un)
+        fl = sum(2 * w.tokens * projs[j]["p"].d_in * projs[j]["p"].d_out
+                 + 2 * w.tokens * w.r * (projs[j]["p"].d_in + projs[j]["p"].d_out) for j in self.units[bu])
+        label = " + ".join(f"{projs[j]['p'].name} {projs[j]['p'].d_in}->{projs[j]['p'].d_out}"
+                           for j in self.units[bu])
+        return bu, fl, label
+
+
+def timed_steps(torch, run, steps, warmup, scrub=None):
+    """`warmup` untimed steps, then `steps` timed ones. HIP events on the stream
+    bracket the whole region, every step, and the forward / backward calls of the
+    largest projection's unit. scrub: a callable enqueued before every timed step
+    (outside its events), e.g. a cache flush. Returns total ms and the per-step ms
+    lists of the whole step, of that unit's forward and of its backward."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        run.step()
+    torch.cuda.synchronize()
+    bu, _, _ = run.big_unit()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    t0, t1 = ev(), ev()
+    st = [(ev(), ev(), ev(), ev(), ev()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        if scrub is not None:
+            scrub()
+        s0, f0, f1, b1, s1 = st[i]
+        s0.record(stream)
+        for ui in range(len(run.units)):
+            if ui == bu:
+                f0.record(stream)
+            run.fwd_unit(ui)
+            if ui == bu:
+                f1.record(stream)
+            run.bwd_unit(ui)
+            if ui == bu:
+                b1.record(stream)
+        s1.record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    per_step = [e[0].elapsed_time(e[4]) for e in st]
+    fwd = [e[1].elapsed_time(e[2]) for e in st]
+    bwd = [e[2].elapsed_time(e[3]) for e in st]
+    return t0.elapsed_time(t1), per_step, fwd, bwd
+
+
+def progress(msg):
+    """One line on stderr per finished part (stdout carries only the JSON line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def pct(xs, p):
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), p))
+
+
+class ClockSampler:
+    """Shader clock (MHz) of GPU 0, polled with amd-smi in a background thread while a
+    timed region runs. None where amd-smi gives no reading."""
+
+    def __init__(self, period_s=0.05):
+        import threading
+        self.period, self.samples, self.stop = period_s, [], threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def read():
+        import re
+        import subprocess
+        try:
+            out = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True,
+                                 text=True, timeout=5).stdout
+            starts = [i for i in (out.find("{"), out.find("[")) if i >= 0]
+            data = json.loads(out[min(starts):])
+        except Exception:
+            return None
+        vals = []
+
+        # {"gpu_data": [{"clock": {"gfx_0": {"clk": {"value": 2100, "unit": "MHz"}, ...}, ...}}]}:
+        # the current clock of every graphics partition (not min_clk / max_clk)
+        def walk(o, path):
+            if isinstance(o, dict):
+                for k, v in o.items():
+                    walk(v, path + [str(k).lower()])
+            elif isinstance(o, list):
+                for v in o:
+                    walk(v, path)
+            elif (len(path) >= 3 and path[-3].startswith("gfx") and path[-2] == "clk"
+                  and path[-1] == "value"):
+                try:
+                    vals.append(float(re.sub(r"[^0-9.]", "", str(o))))
+                except ValueError:
+                    pass
+        walk(data, [])
+        vals = [v for v in vals if v > 0]
+        return sum(vals) / len(vals) if vals else None  # mean over the XCDs' graphics clocks
+
+    def _run(self):
+        while not self.stop.is_set():
+            v = self.read()
+            if v is not None:
+                self.samples.append(v)
+            self.stop.wait(self.period)
+
+    def __enter__(self):
+        self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        self.thread.join(timeout=10)
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return None
+        return {"median_mhz": round(pct(self.samples, 50), 1), "min_mhz": round(min(self.samples), 1),
+                "max_mhz": round(max(self.samples), 1), "samples": len(self.samples),
+                "source": "amd-smi metric -g 0 -c (mean of the XCDs' gfx clocks), polled every 50 ms"}
+
+
+def sustained_run(torch, run, seconds):
+    """The headline step repeated back to back for about `seconds` (well past the
+    timed region's few tens of ms), the shader clock polled with amd-smi meanwhile:
+    the clock the GPU holds under this load, and the median step time at it."""
+    if seconds <= 0:
+        return None
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    per = []
+    with ClockSampler() as clock:
+        t_end = time.perf_counter() + seconds
+        while time.perf_counter() < t_end:
+            batch = [(ev(), ev()) for _ in range(50)]
+            for a, b in batch:
+                a.record(stream)
+                run.step()
+                b.record(stream)
+            torch.cuda.synchronize()
+            per.extend(a.elapsed_time(b) for a, b in batch)
+    return {"seconds": seconds, "steps": len(per), "step_ms": step_stats(per), "sclk": clock.summary()}
+
+
+def step_stats(per_step):
+    return {"p10": round(pct(per_step, 10), 4), "p50": round(pct(per_step, 50), 4),
+            "p90": round(pct(per_step, 90), 4)}
+
+
+def config_leg(lib, q, torch, name, steps, warmup):
+    """fwd + bwd of every projection of one workload (fused where the projections
+    share x), per-step HIP events; median step time, TFLOP/s and tokens/s."""
+    w = next(x for x in synth.WORKLOADS if x.name == name)
+    run = Runner(lib, q, torch, w, fuse=True)
+    total, per_step, fwd, bwd = timed_steps(torch, run, steps, warmup)
+    med = pct(per_step, 50)
+    out = {"tokens": w.tokens, "r": w.r, "fwd_ms_p50_largest_unit": round(pct(fwd, 50), 4),
+           "bwd_ms_p50_largest_unit": round(pct(bwd, 50), 4),
+           "projections": [f"{d['p'].name} {d['p'].d_in}->{d['p'].d_out}" for d in run.projs],
+           "fused": [[run.projs[j]["p"].name for j in un] for un in run.units if len(un) > 1],
+           "steps": steps, "step_ms": step_stats(per_step), "ms_per_step_mean": round(total / steps, 4),
+           "tflops_median_step": round(run.flops() / (med * 1e-3) / 1e12, 2),
+           "tokens_per_s_median_step": round(w.tokens / (med * 1e-3), 1),
+           "pct_of_bf16_peak": round(100.0 * run.flops() / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    del run
+    torch.cuda.empty_cache()
+    return out
+
+
+def mfma_probe(lib, torch, sp):
+    """The library's MFMA-only probe (lora_nf4_mfma_probe): back-to-back
+    v_mfma_f32_32x32x16_bf16 on register operands, two waves per SIMD on every CU;
+    HIP events around one launch after a warm-up launch. None if the probe is absent."""
+    if not hasattr(lib, "lora_nf4_mfma_probe"):
+        return None
+    sink = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    iters = 4096
+    flops = lib.lora_nf4_mfma_probe(iters, sink.data_ptr(), sp)  # warm-up; returns the launch's FLOPs
+    if flops <= 0:
+        return None
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        lib.lora_nf4_mfma_probe(iters, sink.data_ptr(), sp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "launch_ms": round(ms, 4),
+            "frac_of_spec": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "what": "v_mfma_f32_32x32x16_bf16 back to back on registers, 8 independent accumulators per "
+                    "wave, 8 waves per CU, no memory traffic"}
+
+
 def main():
     args = parse()
     if args.ingest_counters:
@@ -472,106 +837,11 @@ def main():
     w = next((x for x in synth.WORKLOADS if x.name == args.workload), None)
     if w is None:
         sys.exit(f"unknown workload {args.workload}")
-    q.library()
-    torch.cuda.set_device(0)
-    stream = torch.cuda.current_stream()
-
-    # resident inputs, NF4 weights quantized once (model load), workspaces preallocated
-    projs = []
-    for pi, p in enumerate(w.projections):
-        inp = synth.projection_inputs(w, pi)
-        x, W, A, B, dY = (to_dev_bf16(inp[k]) for k in ("x", "W", "A", "B", "dY"))
-        codes, absmax = q.nf4_quantize(W)
-        del W
-        T, K, N, r = w.tokens, p.d_in, p.d_out, w.r
-        ws = torch.empty(q.lora_nf4_bwd_workspace_bytes(T, K, N, r), dtype=torch.uint8, device="cuda")
-        fws = torch.empty(max(q.lora_nf4_fwd_workspace_bytes(T, K, N, r), 256), dtype=torch.uint8, device="cuda")
-        projs.append(dict(p=p, x=x, A=A, B=B, dY=dY, codes=codes, absmax=absmax, ws=ws, fws=fws,
-                          y=torch.empty((T, N), dtype=torch.bfloat16, device="cuda"),
-                          u=torch.empty((T, r), dtype=torch.bfloat16, device="cuda"),
-                          dx=torch.empty((T, K), dtype=torch.bfloat16, device="cuda"),
-                          dA=torch.empty((K, r), dtype=torch.bfloat16, device="cuda"),
-                          dB=torch.empty((r, N), dtype=torch.bfloat16, device="cuda")))
     lib = q.library()
-    sp = stream.cuda_stream
-
-    # forward units: one projection each, or (--fuse) the groups that share x
-    units, seen = [], {}
-    for j, d in enumerate(projs):
-        key = {"q_proj": "qkv", "k_proj": "qkv", "v_proj": "qkv", "gate_proj": "gu",
-               "up_proj": "gu"}.get(d["p"].name) if args.fuse else None
-        if key is not None and key in seen:
-            units[seen[key]].append(j)
-            d["x"] = projs[units[seen[key]][0]]["x"]  # the group reads one x
-        else:
-            if key is not None:
-                seen[key] = len(units)
-            units.append([j])
-    import ctypes
-    multi_args = {}
-    for ui, un in enumerate(units):
-        if len(un) > 1:
-            arr = lambda key: (ctypes.c_void_p * len(un))(*[projs[j][key].data_ptr() for j in un])
-            d_out = [projs[j]["p"].d_out for j in un]
-            nb = q.lora_nf4_bwd_multi_workspace_bytes(w.tokens, projs[un[0]]["p"].d_in, d_out, w.r)
-            nf = q.lora_nf4_fwd_multi_workspace_bytes(w.tokens, projs[un[0]]["p"].d_in, d_out, w.r)
-            multi_args[ui] = dict(d_out=(ctypes.c_int64 * len(un))(*d_out),
-                                  codes=arr("codes"), absmax=arr("absmax"), A=arr("A"), B=arr("B"),
-                                  y=arr("y"), u=arr("u"), dy=arr("dY"), dA=arr("dA"), dB=arr("dB"),
-                                  ws=torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda"),
-                                  fws=torch.empty(max(nf, 256), dtype=torch.uint8, device="cuda"))
-            for j in un:  # the group's per-projection backward workspaces are not used
-                projs[j]["ws"] = torch.empty(0, dtype=torch.uint8, device="cuda")
-    torch.cuda.empty_cache()
-
-    def fwd(d):
-        p = d["p"]
-        st = lib.lora_nf4_fwd(w.tokens, p.d_in, p.d_out, w.r, w.alpha, d["x"].data_ptr(),
-                              d["codes"].data_ptr(), d["absmax"].data_ptr(), d["A"].data_ptr(),
-                              d["B"].data_ptr(), d["y"].data_ptr(), d["u"].data_ptr(), d["fws"].data_ptr(),
-                              d["fws"].numel(), sp)
-        if st != 0:
-            raise q.LoraNF4Error("lora_nf4_fwd", st)
-
-    def bwd(d):
-        p = d["p"]
-        st = lib.lora_nf4_bwd(w.tokens, p.d_in, p.d_out, w.r, w.alpha, d["x"].data_ptr(),
-                              d["dY"].data_ptr(), d["codes"].data_ptr(), d["absmax"].data_ptr(),
-                              d["A"].data_ptr(), d["B"].data_ptr(), d["u"].data_ptr(),
-                              d["dx"].data_ptr(), d["dA"].data_ptr(), d["dB"].data_ptr(),
-                              d["ws"].data_ptr(), d["ws"].numel(), sp)
-        if st != 0:
-            raise q.LoraNF4Error("lora_nf4_bwd", st)
-
-    def fwd_unit(ui):
-        un = units[ui]
-        if len(un) == 1:
-            return fwd(projs[un[0]])
-        m, d0 = multi_args[ui], projs[un[0]]
-        cv = lambda a: ctypes.cast(a, ctypes.c_void_p)
-        st = lib.lora_nf4_fwd_multi(w.tokens, d0["p"].d_in, len(un), cv(m["d_out"]), w.r, w.alpha,
-                                    d0["x"].data_ptr(), cv(m["codes"]), cv(m["absmax"]), cv(m["A"]),
-                                    cv(m["B"]), cv(m["y"]), cv(m["u"]), m["fws"].data_ptr(), m["fws"].numel(), sp)
-        if st != 0:
-            raise q.LoraNF4Error("lora_nf4_fwd_multi", st)
-
-    def bwd_unit(ui):
-        un = units[ui]
-        if len(un) == 1:
-            return bwd(projs[un[0]])
-        m, d0 = multi_args[ui], projs[un[0]]
-        cv = lambda a: ctypes.cast(a, ctypes.c_void_p)
-        st = lib.lora_nf4_bwd_multi(w.tokens, d0["p"].d_in, len(un), cv(m["d_out"]), w.r, w.alpha,
-                                    d0["x"].data_ptr(), cv(m["dy"]), cv(m["codes"]), cv(m["absmax"]),
-                                    cv(m["A"]), cv(m["B"]), cv(m["u"]), d0["dx"].data_ptr(), cv(m["dA"]),
-                                    cv(m["dB"]), m["ws"].data_ptr(), m["ws"].numel(), sp)
-        if st != 0:
-            raise q.LoraNF4Error("lora_nf4_bwd_multi", st)
-
-    def step_all():
-        for ui, un in enumerate(units):
-            fwd_unit(ui)
-            bwd_unit(ui)
+    torch.cuda.set_device(0)
+    q.set_weight_staging(bool(args.staged))
+    run = Runner(lib, q, torch, w, args.fuse)
+    sp = run.sp
 
     if args.counter_pass:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -579,56 +849,27 @@ def main():
         torch.mul(src, 1.0, out=dst)  # plain copy of known size: calibrates the counters
         torch.cuda.synchronize()
         for _ in range(args.steps):
-            step_all()
+            run.step()
         torch.cuda.synchronize()
         return
 
-    for _ in range(args.warmup):
-        step_all()
-    torch.cuda.synchronize()
-
-    # events around every forward launch (one kernel each; one per unit) and the
-    # backward calls of the unit's projections
-    nev = args.steps * len(units)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nev)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record(stream)
-    i = 0
-    for _ in range(args.steps):
-        for ui, un in enumerate(units):
-            ev[i][0].record(stream)
-            fwd_unit(ui)
-            ev[i][1].record(stream)
-            bwd_unit(ui)
-            ev[i][2].record(stream)
-            i += 1
-    t_end.record(stream)
-    torch.cuda.synchronize()
+    total_ms, per_step, fwd_ms, bwd_ms = timed_steps(torch, run, args.steps, args.warmup)
     wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-
-    flops_step = sum(synth.flops(w.tokens, d["p"].d_in, d["p"].d_out, w.r) for d in projs)
+    progress(f"{w.name}: {args.steps} steps, {ms_step:.4f} ms/step")
+    flops_step = run.flops()
     tflops = flops_step / (ms_step * 1e-3) / 1e12
     tokens_s = w.tokens / (ms_step * 1e-3)
-
-    # forward launch of the unit holding the largest projection: average duration
-    big = max(range(len(projs)), key=lambda j: projs[j]["p"].d_in * projs[j]["p"].d_out)
-    bu = next(ui for ui, un in enumerate(units) if big in un)
-    fwd_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(nev) if k % len(units) == bu]
-    bwd_ms = [ev[k][1].elapsed_time(ev[k][2]) for k in range(nev) if k % len(units) == bu]
-    pb = projs[big]["p"]
+    bu, fwd_flops, unit_label = run.big_unit()
+    pb = run.projs[run.units[bu][0]]["p"]
     T, K, N, r = w.tokens, pb.d_in, pb.d_out, w.r
-    fwd_flops = sum(2 * T * projs[j]["p"].d_in * projs[j]["p"].d_out
-                    + 2 * T * r * (projs[j]["p"].d_in + projs[j]["p"].d_out) for j in units[bu])
-    unit_label = " + ".join(f"{projs[j]['p'].name} {projs[j]['p'].d_in}->{projs[j]['p'].d_out}"
-                            for j in units[bu])
     fwd_avg = float(np.mean(fwd_ms))
     achieved = fwd_flops / (fwd_avg * 1e-3) / 1e12
     traffic = measured_traffic()
+    staged = q.lora_nf4_fwd_workspace_bytes(T, K, N, r) >= K * N * 2
+    kernel = ("lora_fwd (nf4_dequantize_kernel + lora_fwd_kernel on the staged bf16 weight)" if staged else
+              "lora_fwd_rw_kernel (NF4 dequantized into MFMA fragments in the K loop)")
 
     out = {
         "metric": METRIC,
@@ -645,32 +886,74 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.tokens, "batch": w.batch, "seq": w.seq,
                    "r": w.r, "alpha": w.alpha,
-                   "projections": [f"{d['p'].name} {d['p'].d_in}->{d['p'].d_out}" for d in projs],
+                   "projections": [f"{d['p'].name} {d['p'].d_in}->{d['p'].d_out}" for d in run.projs],
                    "weights": "NF4 blocksize 64, fp32 absmax", "parallelism": "single GPU",
-                   "fused_forward": [[projs[j]["p"].name for j in un] for un in units if len(un) > 1],
-                   "fused_backward": [[projs[j]["p"].name for j in un] for un in units if len(un) > 1]},
+                   "weight_staging": bool(args.staged),
+                   "fused_forward": [[run.projs[j]["p"].name for j in un] for un in run.units if len(un) > 1],
+                   "fused_backward": [[run.projs[j]["p"].name for j in un] for un in run.units if len(un) > 1]},
         "tokens_per_s": round(tokens_s, 1),
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "step_ms": step_stats(per_step),
         "fwd_ms": round(fwd_avg, 4),
+        "fwd_ms_p50": round(pct(fwd_ms, 50), 4),
         "bwd_ms": round(float(np.mean(bwd_ms)), 4),
+        "bwd_ms_p50": round(pct(bwd_ms, 50), 4),
         "host_wall_s": round(wall, 4),
-        "roofline": {"kernel": ("lora_fwd (nf4_dequantize_kernel + lora_fwd_kernel)"
-                                if q.lora_nf4_fwd_workspace_bytes(T, K, N, r) >= K * N * 2
-                                else "lora_fwd_kernel"), "projection": unit_label,
+        "sustained": sustained_run(torch, run, args.sustain_s),
+        "roofline": {"kernel": kernel, "projection": unit_label,
                      "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
+    out["mfma_probe"] = mfma_probe(lib, torch, sp)
+    if out["mfma_probe"] is not None:
+        out["roofline"]["frac_of_measured_mfma_peak"] = round(achieved / out["mfma_probe"]["tflops"], 4)
+    if not args.no_legs:
+        # the same step with the weight dequantized to bf16 into the workspace first
+        prev = q.set_weight_staging(not args.staged)
+        run.size_workspaces(torch)
+        total2, per2, fwd2, bwd2 = timed_steps(torch, run, args.steps, args.warmup)
+        q.set_weight_staging(prev)
+        run.size_workspaces(torch)
+        med2 = pct(per2, 50)
+        progress(f"weight staging {'off' if args.staged else 'on'}: median step {med2:.4f} ms")
+        out["weight_staging_" + ("off" if args.staged else "on")] = {
+            "step_ms": step_stats(per2), "fwd_ms_p50": round(pct(fwd2, 50), 4),
+            "bwd_ms_p50": round(pct(bwd2, 50), 4),
+            "tflops_median_step": round(flops_step / (med2 * 1e-3) / 1e12, 2),
+            "note": "lora_nf4_set_weight_staging(1): the forward and dX read a bf16 copy of the weight "
+                    "dequantized into their workspace (2 B/weight) instead of dequantizing in the K loop"}
+        # cold caches: a 512 MiB write (twice the 256 MB memory-side cache) before every step
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        _, per3, fwd3, bwd3 = timed_steps(torch, run, max(10, args.steps // 5), 2, scrub=lambda: flush.fill_(1))
+        del flush
+        progress(f"cold cache: median step {pct(per3, 50):.4f} ms")
+        out["cold_cache"] = {"step_ms": step_stats(per3), "fwd_ms_p50": round(pct(fwd3, 50), 4),
+                             "bwd_ms_p50": round(pct(bwd3, 50), 4),
+                             "steps": len(per3),
+                             "scrub": "512 MiB device fill before every step (outside its events)"}
+    progress("mfma probe: " + (f"{out['mfma_probe']['tflops']} TFLOP/s" if out["mfma_probe"] else "absent"))
     if args.small_tokens > 0:
-        out["small_tokens"] = small_token_run(lib, q, torch, projs[big], w, args.small_tokens, sp)
+        out["small_tokens"] = small_token_run(lib, q, torch, run.projs[run.units[bu][0]], w, args.small_tokens, sp)
     if args.medium_tokens > 0:
-        out["medium_tokens"] = medium_token_run(lib, q, torch, projs[big], w, args.medium_tokens, sp)
-    out["merge"] = merge_run(lib, q, torch, projs[big], w, sp)
-    out["train_step"] = train_step_run(lib, q, torch, projs[big], w, sp)
+        out["medium_tokens"] = medium_token_run(lib, q, torch, run.projs[run.units[bu][0]], w, args.medium_tokens, sp)
+    out["merge"] = merge_run(lib, q, torch, run.projs[run.units[bu][0]], w, sp)
+    out["train_step"] = train_step_run(lib, q, torch, run.projs[run.units[bu][0]], w, sp)
+    progress("small / medium tokens, merge, training step done")
+    del run
+    torch.cuda.empty_cache()
     if not args.no_multi:
         out["multi_projection"] = multi_projection_run(lib, q, torch, sp)
+        progress("multi-projection leg done")
+    if not args.no_legs:
+        out["configs"] = {}
+        for name in ("llama3-8b-attn-r64", "qwen14b-attn", "llama3-70b-layer"):
+            if name != w.name:
+                out["configs"][name] = config_leg(lib, q, torch, name, args.leg_steps, 3)
+                progress(f"{name}: median step {out['configs'][name]['step_ms']['p50']} ms")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        progress("cpu baseline done")
     print(json.dumps(out), flush=True)
 
 

@@ -102,14 +102,15 @@ int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t rows, int6
  *            over d_in is split across workgroups and fp32 partial sums meet in
  *            the workspace (few tokens: T <= 128 at r % 8 == 0, r <= 64; and
  *            token counts whose output tiles leave most of the GPU idle); from
- *            T = 1024 on 128 x 128 tiles, where the weight is dequantized once
- *            into it (bf16 [d_out, d_in]: 2 d_in d_out bytes, the same values the
- *            fused kernels produce); and from T = 4096 with d_in % 256 == 0,
- *            r % 8 == 0, r <= 64 (256 x 256 tiles that dequantize into
- *            registers), at ranks other than 16, where it holds A^T and
- *            bf16(s x A) of a pass over x ahead of the tiles (2 r (d_in + T)
- *            bytes, each part rounded up to 256; at r = 16 the tiles form x A
- *            themselves). When it is 0 the workspace may be NULL.
+ *            T = 4096 with d_in % 256 == 0, r % 8 == 0, r <= 64 (256 x 256 tiles
+ *            that dequantize into registers), at ranks other than 16, where it
+ *            holds A^T and bf16(s x A) of a pass over x ahead of the tiles
+ *            (2 r (d_in + T) bytes, each part rounded up to 256; at r = 16 the
+ *            tiles form x A themselves); and, with weight staging on
+ *            (lora_nf4_set_weight_staging), from T = 1024 (T = 4096 on
+ *            256 x 256 tiles), where the weight is dequantized once into it
+ *            (bf16 [d_out, d_in]: 2 d_in d_out bytes, the same values the fused
+ *            kernels produce). When it is 0 the workspace may be NULL.
  * T >= 0, d_in % 64 == 0, d_out >= 1 (any; a d_out that is not a multiple of 8, and
  * ranks r % 8 != 0 or r > 64, run the generic 128 x 128 kernels: same results,
  * lower speed), 1 <= r <= LN_MAX_RANK. s = lora_alpha / r
@@ -147,11 +148,12 @@ size_t lora_nf4_fwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int3
  *                        lora_nf4_fwd_multi_workspace_bytes: non-zero when the
  *                        projections run one after the other on a path that
  *                        needs one (they reuse it in turn), and for one shared
- *                        launch at large token counts (every projection's
- *                        weight dequantized into it, one after another; or,
- *                        on register-dequantizing tiles at ranks other than
- *                        16, A^T and bf16(s x A) of all projections: one pass
- *                        over x when n_proj r <= 64, else one per projection)
+ *                        launch at large token counts (on register-
+ *                        dequantizing tiles at ranks other than 16, A^T and
+ *                        bf16(s x A) of all projections: one pass over x when
+ *                        n_proj r <= 64, else one per projection; with weight
+ *                        staging on, every projection's weight dequantized
+ *                        into it, one after another)
  * All projections share T, d_in, r and lora_alpha. The host arrays are read
  * during the call only. Every output (each y[g], each u_save[g], the workspace)
  * must be disjoint from every input and from the other outputs (LN_EALIAS).
@@ -179,9 +181,14 @@ size_t lora_nf4_fwd_multi_workspace_bytes(int64_t T, int64_t d_in, int32_t n_pro
  *   workspace  device scratch of at least lora_nf4_bwd_workspace_bytes(T, d_in,
  *            d_out, r) bytes, 256-byte aligned, owned by the caller; its contents
  *            on entry do not matter and on return are unspecified. Two calls that
- *            may run concurrently need separate workspaces. At large token counts
- *            (from T = 1024, or 4096 where dX runs 256 x 256 tiles) it also holds
- *            the bf16 dequantized weight, 2 d_in d_out bytes.
+ *            may run concurrently need separate workspaces. From T = 4096 at
+ *            r = 16 with d_in and d_out multiples of 256 (dX on 256 x 256 tiles
+ *            that dequantize into registers) it also holds the packed weight
+ *            transposed, d_in d_out / 2 + d_in d_out / 16 bytes (codes and
+ *            absmax, each part rounded up to 256). With weight staging on
+ *            (lora_nf4_set_weight_staging) it instead holds, at large token
+ *            counts (from T = 1024, or 4096 where dX runs 256 x 256 tiles), the
+ *            bf16 dequantized weight, 2 d_in d_out bytes.
  * Shape rules as for lora_nf4_fwd. With T = 0 (empty batch) dA and dB are set to
  * zero (empty sums), x, dy, u_saved, dx and the workspace may be NULL, and
  * lora_nf4_bwd_workspace_bytes is 0.
@@ -290,6 +297,47 @@ int lora_nf4_bwd_noalloc(int64_t T, int64_t d_in, int64_t d_out, int32_t r, floa
 int lora_adamw_step(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* grad, uint16_t* m,
                     uint16_t* v, int32_t step, float lr, float beta1, float beta2, float eps,
                     float weight_decay, void* stream);
+
+/*
+ * lora_nf4_mfma_probe — measurement aid, no part of the linear: one launch of
+ * v_mfma_f32_32x32x16_bf16 issued back to back on register operands (eight
+ * independent accumulators per wave, two waves per SIMD, one 512-thread
+ * workgroup on each of 256 CUs, no memory traffic), `iters` rounds of eight per
+ * wave. Timing it (e.g. with HIP events on `stream`) gives the bf16 matrix-core
+ * throughput the GPU sustains, the practical ceiling of the tile kernels next to
+ * the published 2.5 PFLOP/s dense bf16 peak.
+ *   iters  1 .. 2^20
+ *   sink   device float32 [256], 16-byte aligned: one value per workgroup (output;
+ *          keeps the work observable, value meaningless)
+ * Returns the launch's floating-point operation count (2 x 32 x 32 x 16 per MFMA)
+ * on success, a negative LN_* status otherwise (LN_EINVAL for bad arguments or a
+ * launch error, LN_EALIGN).
+ */
+int64_t lora_nf4_mfma_probe(int32_t iters, float* sink, void* stream);
+
+/*
+ * lora_nf4_set_weight_staging — how the tile kernels at large token counts read
+ * the NF4 weight, for every later call in the process.
+ *   mode 0 (the default): every path dequantizes the packed weight inside its
+ *          GEMM main loop, into LDS or straight into MFMA fragments (the fused
+ *          design of "Unsloth acceleration principles: CUDA kernel fusion and
+ *          memory optimization", kernel-fusion section); no bf16 copy of the
+ *          weight exists at any time.
+ *   mode 1: from 1024 tokens (4096 where the grid runs 256 x 256 tiles) the
+ *          forward and dX first dequantize the weight to bf16 into their
+ *          workspace (2 d_in d_out bytes per projection, see the
+ *          *_workspace_bytes queries) and the tile kernels read that copy. The
+ *          results are identical in value to mode 0's within the tolerance of
+ *          the linear (the same dequantized bf16 weights; products summed in a
+ *          different order). Measured on MI355X at 8192 tokens, 4096 -> 4096,
+ *          r = 16: forward 257 us (mode 1) vs 287 us (mode 0), dX 250 vs 278 us.
+ *   mode -1: query only.
+ * Returns the mode in effect before the call (0 or 1), LN_EINVAL for any other
+ * mode. Process-wide and read when a call is enqueued and when workspace sizes
+ * are queried: set it before querying sizes and keep it while calls sized that
+ * way are issued. Host function, no GPU work.
+ */
+int lora_nf4_set_weight_staging(int32_t mode);
 
 /*
  * lora_nf4_rslora_alpha — the lora_alpha to pass to the entry points above so

@@ -32,6 +32,7 @@ __all__ = [
     "status_string", "EXPORTED_SYMBOLS", "LN_MAX_RANK", "LN_MAX_PROJ",
     "lora_adamw_step", "rslora_alpha", "nf4_absmax_quantize", "nf4_absmax_dequantize",
     "lora_nf4_bwd_multi", "lora_nf4_bwd_multi_workspace_bytes", "lora_nf4_bwd_noalloc",
+    "set_weight_staging", "weight_staging",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -45,7 +46,8 @@ EXPORTED_SYMBOLS = ("nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_
                     "lora_nf4_status_string", "lora_adamw_step", "lora_nf4_rslora_alpha",
                     "nf4_absmax_quantize", "nf4_absmax_dequantize", "lora_nf4_bwd_multi",
                     "lora_nf4_bwd_multi_workspace_bytes", "lora_nf4_fwd_workspace_bytes",
-                    "lora_nf4_fwd_multi_workspace_bytes", "lora_nf4_bwd_noalloc")
+                    "lora_nf4_fwd_multi_workspace_bytes", "lora_nf4_bwd_noalloc",
+                    "lora_nf4_set_weight_staging", "lora_nf4_mfma_probe")
 
 _lib = None
 
@@ -71,6 +73,8 @@ _SIGS = {
     "lora_adamw_step": (ctypes.c_int, [_i64, _p, _p, _p, _p, _p, ctypes.c_int32, ctypes.c_float,
                                        ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, _p]),
     "lora_nf4_rslora_alpha": (ctypes.c_float, [ctypes.c_float, ctypes.c_int32]),
+    "lora_nf4_set_weight_staging": (ctypes.c_int, [ctypes.c_int32]),
+    "lora_nf4_mfma_probe": (ctypes.c_int64, [ctypes.c_int32, _p, _p]),
     "lora_nf4_bwd_multi": (ctypes.c_int, [_i64, _i64, ctypes.c_int32, _p, ctypes.c_int32, ctypes.c_float,
                                           _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
     "lora_nf4_bwd_multi_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, ctypes.c_int32, _p, ctypes.c_int32]),
@@ -381,6 +385,31 @@ def rslora_alpha(lora_alpha: float, r: int) -> float:
     if a != a:
         raise ValueError(f"no rank-stabilized alpha for lora_alpha={lora_alpha}, r={r}")
     return a
+
+
+def set_weight_staging(enabled: bool) -> bool:
+    """lora_nf4_set_weight_staging: True makes the large-token forward and dX read a
+    bf16 copy of the weight dequantized into their workspace; False (the default)
+    keeps the dequantization inside every kernel's main loop. Returns the previous
+    setting."""
+    return bool(library().lora_nf4_set_weight_staging(1 if enabled else 0))
+
+
+class weight_staging:
+    """Context manager: `with weight_staging(True): ...` runs the block with weight
+    staging set as given and restores the previous setting on exit."""
+
+    def __init__(self, enabled: bool):
+        self.enabled = bool(enabled)
+        self.prev = None
+
+    def __enter__(self):
+        self.prev = set_weight_staging(self.enabled)
+        return self
+
+    def __exit__(self, *exc):
+        set_weight_staging(self.prev)
+        return False
 
 
 def nf4_absmax_quantize(absmax):

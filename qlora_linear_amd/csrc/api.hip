@@ -2,12 +2,20 @@
 //
 // Every entry point validates its arguments on the host before touching HIP, so
 // argument errors are reported without a GPU and nothing is enqueued on error.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
 
 #include "launch.h"
 #include "lora_nf4.h"
+
+namespace lnf4 {
+namespace {
+std::atomic<bool> g_weight_staging{false};
+}  // namespace
+bool weight_staging() { return g_weight_staging.load(std::memory_order_relaxed); }
+}  // namespace lnf4
 
 namespace {
 
@@ -433,6 +441,19 @@ int lora_adamw_step(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* grad,
   if (any_alias(outs, 4, ins, 1)) return LN_EALIAS;
   return hip_status(lnf4::launch_adamw(n, p, p_bf16, grad, m, v, step, lr, beta1, beta2, eps,
                                        weight_decay, static_cast<hipStream_t>(stream)));
+}
+
+int64_t lora_nf4_mfma_probe(int32_t iters, float* sink, void* stream) {
+  if (iters < 1 || iters > (1 << 20) || sink == nullptr) return LN_EINVAL;
+  if (!aligned16(sink)) return LN_EALIGN;
+  const int64_t f = lnf4::launch_mfma_probe(iters, sink, static_cast<hipStream_t>(stream));
+  return f < 0 ? static_cast<int64_t>(LN_EINVAL) : f;
+}
+
+int lora_nf4_set_weight_staging(int32_t mode) {
+  if (mode < -1 || mode > 1) return LN_EINVAL;
+  if (mode < 0) return lnf4::weight_staging() ? 1 : 0;
+  return lnf4::g_weight_staging.exchange(mode == 1) ? 1 : 0;
 }
 
 float lora_nf4_rslora_alpha(float lora_alpha, int32_t r) {

@@ -21,6 +21,10 @@ hipError_t launch_nf4_dequantize(const uint8_t* codes, const float* absmax, int6
 hipError_t launch_nf4_transpose(const uint8_t* codes, const float* absmax, int64_t N, int64_t K,
                                 uint8_t* codes_t, float* absmax_t, hipStream_t stream);
 
+// MFMA-only throughput probe over every CU: returns the launch's FLOPs (-1 on a
+// launch error); sink receives one float per workgroup (256).
+int64_t launch_mfma_probe(int iters, float* sink, hipStream_t stream);
+
 // Zero n 16-bit elements (a fill kernel, so the call can sit in a captured graph).
 hipError_t launch_zero_u16(uint16_t* p, int64_t n, hipStream_t stream);
 
@@ -85,6 +89,10 @@ hipError_t launch_upass(int T, int K, int r, float s, const uint16_t* x, UpassTa
 // x runs through a four-stage LDS pipeline; at rank 16 U = x A is formed in the
 // K loop, otherwise bf16(s U) is read from tab.usg (the U pass).
 bool fwd_rw_supported(int64_t T, int64_t K, int r);
+// Weight staging (lora_nf4_set_weight_staging): false (default) = every tile path
+// dequantizes in its main loop; true = from 1024 / 4096 tokens the weight is
+// dequantized to bf16 once into the workspace and the tile kernels read that.
+bool weight_staging();
 bool fwd_rw_inloop_u(int r);  // the kernel computes U itself (no U pass, no workspace)
 hipError_t launch_fwd_rw(int T, int K, int r, float s, const uint16_t* x, const ProjTable& tab,
                          hipStream_t stream);

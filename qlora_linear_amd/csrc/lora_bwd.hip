@@ -522,7 +522,7 @@ BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r, bool allow_dq) {
       off = align256(off + static_cast<size_t>(d.splits) * T * K * 4);
       p.off_pg = off;
       off = align256(off + static_cast<size_t>(d.splits) * T * r * 4);
-    } else if (dx_rw_supported(T, K, N, r)) {
+    } else if (!weight_staging() && dx_rw_supported(T, K, N, r)) {
       p.rwx = true;
       p.off_w = off;
       off = align256(off + dx_rw_bytes(K, N));

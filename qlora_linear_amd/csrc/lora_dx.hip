@@ -672,9 +672,10 @@ DxTiledSplit dx_tiled_split(int64_t T, int64_t K, int64_t N, int r) {
 // The tiled dX on a weight dequantized beforehand: from 1024 tokens on 128 x 128
 // tiles and 4096 on 256 x 256 tiles (the forward's rule: there each weight tile
 // is read by at least eight token tiles), with the bf16 weight within one buffer
-// range.
+// range. Taken only with weight staging on (lora_nf4_set_weight_staging).
 bool dx_dq(int64_t T, int64_t K, int64_t N, int r) {
-  return T >= (dx_tile_edge(T, K, r) == 256 ? 4096 : 1024) && N * K * 2 < (int64_t(1) << 31) - 1;
+  return weight_staging() && T >= (dx_tile_edge(T, K, r) == 256 ? 4096 : 1024) &&
+         N * K * 2 < (int64_t(1) << 31) - 1;
 }
 
 hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* dy,

@@ -682,7 +682,8 @@ TiledSplit tiled_split(int64_t T, int64_t K, int64_t N, int r) {
 // 15 % faster in-loop (586 -> 496 us), and 256-row grids at 2048 tokens are within
 // +-5 % either way. Same values: the dequantization rounds exactly as the in-loop
 // one.
-bool fwd_dq(int64_t T, int bt) { return T >= (bt == 256 ? 4096 : 1024); }
+// Taken only with weight staging on (lora_nf4_set_weight_staging).
+bool fwd_dq(int64_t T, int bt) { return weight_staging() && T >= (bt == 256 ? 4096 : 1024); }
 // Rank > 16 on that path from 4096 tokens also takes the U pass (A^T [r][K] and
 // bf16(s U) [T][r] follow each projection's weight in the workspace). Measured on
 // MI355X, forward at 8192 tokens, in-loop U -> U pass: 4096 -> 4096 r = 32
@@ -704,7 +705,7 @@ size_t dq_bytes(int64_t T, int64_t K, int64_t N, int r) {
 // from the U pass (lora_upass.hip; A^T and bf16(s U) in the workspace): one pass
 // over x for all projections when their ranks sum to at most 64, else one per
 // projection.
-bool fwd_rw(int64_t T, int64_t K, int bt, int r) { return bt == 256 && fwd_rw_supported(T, K, r); }
+bool fwd_rw(int64_t T, int64_t K, int bt, int r) { return !weight_staging() && bt == 256 && fwd_rw_supported(T, K, r); }
 size_t rw_bytes(int64_t T, int64_t K, int n, int r) {
   if (fwd_rw_inloop_u(r)) return 0;
   return n * r <= 64 ? upass_table_bytes(T, K, n, r) : n * upass_table_bytes(T, K, 1, r);

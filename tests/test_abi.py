@@ -1,5 +1,6 @@
 """C-ABI checks that need no GPU: the library loads, exports every entry point the
 header declares, and rejects bad arguments on the host before any HIP call."""
+import contextlib
 import ctypes
 import os
 import re
@@ -21,6 +22,17 @@ def lib():
     return q.library()
 
 
+@contextlib.contextmanager
+def staging(lib, on):
+    """Weight staging (lora_nf4_set_weight_staging) set for the block, then restored."""
+    prev = lib.lora_nf4_set_weight_staging(1 if on else 0)
+    assert prev in (0, 1)
+    try:
+        yield
+    finally:
+        lib.lora_nf4_set_weight_staging(prev)
+
+
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -34,7 +46,8 @@ def test_header_declares_the_boundary():
                             "lora_nf4_status_string", "lora_adamw_step", "lora_nf4_rslora_alpha",
                             "nf4_absmax_quantize", "nf4_absmax_dequantize", "lora_nf4_bwd_multi",
                             "lora_nf4_bwd_multi_workspace_bytes", "lora_nf4_fwd_workspace_bytes",
-                            "lora_nf4_fwd_multi_workspace_bytes", "lora_nf4_bwd_noalloc"])
+                            "lora_nf4_fwd_multi_workspace_bytes", "lora_nf4_bwd_noalloc",
+                            "lora_nf4_set_weight_staging", "lora_nf4_mfma_probe"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -101,9 +114,15 @@ def test_fwd_workspace(lib):
     # workspace holds A^T and bf16(s U) of the U pass
     assert lib.lora_nf4_fwd_workspace_bytes(8192, 4096, 4096, 16) == 0
     assert lib.lora_nf4_fwd_workspace_bytes(8192, 4096, 4096, 32) == 32 * 4096 * 2 + 8192 * 32 * 2
-    # from 1024 tokens on 128 x 128 tiles the weight is dequantized once into it (bf16)
-    assert lib.lora_nf4_fwd_workspace_bytes(2048, 4096, 4096, 16) >= 4096 * 4096 * 2
-    assert lib.lora_nf4_fwd_workspace_bytes(1024, 320, 200, 16) == (320 * 200 * 2 + 255) // 256 * 256
+    # by default no path stages a bf16 copy of the weight
+    assert lib.lora_nf4_fwd_workspace_bytes(2048, 4096, 4096, 16) == 0
+    assert lib.lora_nf4_fwd_workspace_bytes(1024, 320, 200, 16) == 0
+    with staging(lib, True):
+        # staged: from 1024 tokens on 128 x 128 tiles the weight is dequantized once
+        # into it (bf16), and from 4096 on 256 x 256 tiles
+        assert lib.lora_nf4_fwd_workspace_bytes(2048, 4096, 4096, 16) >= 4096 * 4096 * 2
+        assert lib.lora_nf4_fwd_workspace_bytes(1024, 320, 200, 16) == (320 * 200 * 2 + 255) // 256 * 256
+        assert lib.lora_nf4_fwd_workspace_bytes(8192, 4096, 4096, 16) >= 4096 * 4096 * 2
     assert lib.lora_nf4_fwd_workspace_bytes(64, 64, 64, 12) == 0         # r % 8 != 0: generic kernels
     assert lib.lora_nf4_fwd_workspace_bytes(0, 64, 64, 8) == 0
     assert lib.lora_nf4_fwd_workspace_bytes(64, 65, 64, 8) == 0          # invalid sizes
@@ -171,28 +190,40 @@ def test_fwd_multi_validation(lib):
 
 
 def test_bwd_workspace_holds_the_dequantized_weight_at_large_token_counts(lib):
-    """dX runs on a bf16 copy of the weight from 1024 tokens on 128 x 128 tiles and
-    (ranks other than 16) from 4096 on 256 x 256 tiles (q_proj 4096 x 4096 takes 128
-    tiles at 1024 tokens and 256 at 4095 and 4096): the workspace grows by at least
-    2 d_in d_out bytes across each threshold. At rank 16 the 256 x 256 dX tiles
-    dequantize in registers from the packed weight transposed into the workspace:
-    d_in d_out / 2 bytes of codes plus d_in d_out / 16 of absmax."""
+    """With weight staging on, dX runs on a bf16 copy of the weight from 1024 tokens
+    on 128 x 128 tiles and from 4096 on 256 x 256 tiles (q_proj 4096 x 4096 takes
+    128 tiles at 1024 tokens and 256 at 4095 and 4096): the workspace grows by at
+    least 2 d_in d_out bytes across each threshold. By default there is no such
+    copy; at rank 16 the 256 x 256 dX tiles dequantize in registers from the packed
+    weight transposed into the workspace: d_in d_out / 2 bytes of codes plus
+    d_in d_out / 16 of absmax."""
     K = N = 4096
     w = 2 * K * N
     packed_t = K * N // 2 + (K // 64) * N * 4
+    with staging(lib, True):
+        for r in (16, 64):
+            assert lib.lora_nf4_bwd_workspace_bytes(1023, K, N, r) < w
+            assert lib.lora_nf4_bwd_workspace_bytes(1024, K, N, r) - lib.lora_nf4_bwd_workspace_bytes(1023, K, N, r) >= w
+            assert lib.lora_nf4_bwd_workspace_bytes(4095, K, N, r) < w
+            assert lib.lora_nf4_bwd_workspace_bytes(4096, K, N, r) - lib.lora_nf4_bwd_workspace_bytes(4095, K, N, r) >= w
+            assert lib.lora_nf4_bwd_workspace_bytes(8192, K, N, r) >= w
     for r in (16, 64):
-        assert lib.lora_nf4_bwd_workspace_bytes(1023, K, N, r) < w
-        assert lib.lora_nf4_bwd_workspace_bytes(1024, K, N, r) - lib.lora_nf4_bwd_workspace_bytes(1023, K, N, r) >= w
-        assert lib.lora_nf4_bwd_workspace_bytes(4095, K, N, r) < w
-    r = 64
-    assert lib.lora_nf4_bwd_workspace_bytes(4096, K, N, r) - lib.lora_nf4_bwd_workspace_bytes(4095, K, N, r) >= w
-    assert lib.lora_nf4_bwd_workspace_bytes(8192, K, N, r) >= w
+        for T in (1024, 2048, 4096, 8192):
+            assert lib.lora_nf4_bwd_workspace_bytes(T, K, N, r) < w
+        assert lib.lora_nf4_bwd_workspace_bytes(8192, K, 4160, r) < 2 * K * 4160
     r = 16
     grow = lib.lora_nf4_bwd_workspace_bytes(4096, K, N, r) - lib.lora_nf4_bwd_workspace_bytes(4095, K, N, r)
     assert packed_t <= grow < w
-    assert lib.lora_nf4_bwd_workspace_bytes(8192, K, N, r) < w
-    # the register path needs whole 256-column tiles on both sides: d_out = 4160 falls back
-    assert lib.lora_nf4_bwd_workspace_bytes(8192, K, 4160, r) >= 2 * K * 4160
+
+
+def test_weight_staging_mode(lib):
+    assert lib.lora_nf4_set_weight_staging(-1) == 0  # the default: in-loop dequantization
+    assert lib.lora_nf4_set_weight_staging(2) == LN_EINVAL
+    assert lib.lora_nf4_set_weight_staging(-2) == LN_EINVAL
+    assert lib.lora_nf4_set_weight_staging(1) == 0
+    assert lib.lora_nf4_set_weight_staging(-1) == 1
+    assert lib.lora_nf4_set_weight_staging(0) == 1
+    assert lib.lora_nf4_set_weight_staging(-1) == 0
 
 
 def test_bwd_validation_and_workspace(lib):
@@ -379,3 +410,11 @@ def test_binding_rejects_cpu_tensors():
     import qlora_linear_amd as q
     with pytest.raises(ValueError):
         q.nf4_quantize(torch.zeros(4, 64))
+
+
+def test_mfma_probe_validation(lib):
+    # rejected before any launch
+    assert lib.lora_nf4_mfma_probe(0, P, None) == LN_EINVAL
+    assert lib.lora_nf4_mfma_probe(1 << 21, P, None) == LN_EINVAL
+    assert lib.lora_nf4_mfma_probe(16, None, None) == LN_EINVAL
+    assert lib.lora_nf4_mfma_probe(16, P + 4, None) == LN_EALIGN

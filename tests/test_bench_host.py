@@ -36,3 +36,21 @@ def test_forward_traffic_single_launch_below_1024_tokens():
             (4, "void lnf4::lora_fwd_kernel<128, 16, 16, false>(int)", 72.0)]
     fwd, other = bench.forward_kib(rows)
     assert fwd == 71.0 and other["lora_dx_kernel"] == 60.0
+
+
+def test_register_path_pairs_the_transposition_with_dx():
+    """Default mode: the forward is one register-dequantizing launch; dX is the packed
+    weight's transposition followed by the register-dequantizing dX kernel."""
+    rows = [(1, "MulFunctor", 8.0)]
+    did = 2
+    for _ in range(3):
+        for name, v in (("void lnf4::lora_fwd_rw_kernel<16, true>(int)", 90.0),
+                        ("lnf4::nf4_transpose_kernel(unsigned int const*)", 12.0),
+                        ("lnf4::lora_dx_rw_kernel(int)", 95.0),
+                        ("void lnf4::skinny_partial_kernel<32>(int)", 30.0)):
+            rows.append((did, name, v))
+            did += 1
+    fwd, other = bench.forward_kib(rows)
+    assert fwd == 90.0
+    assert other["lora_dx (nf4_transpose_kernel + lora_dx_rw_kernel)"] == 107.0
+    assert "lora_dx_rw_kernel" not in other and other["skinny_partial_kernel"] == 30.0

@@ -92,17 +92,22 @@ def test_bwd_multi_matches_oracle(q, T, K, Ns, r, with_u, with_dx):
 
 
 def test_bwd_multi_dx_dequantized_matches_in_loop(q):
-    """From 1024 tokens (128 x 128 tiles) the fused dX reads weights dequantized
-    into the workspace; rows 0 .. 1022 match the in-loop path at 1023 tokens bit
-    for bit (rows are independent, the summation order is the same)."""
+    """With weight staging on, from 1024 tokens (128 x 128 tiles) the fused dX reads
+    weights dequantized into the workspace; rows 0 .. 1022 match the in-loop path at
+    1023 tokens bit for bit (rows are independent, the summation order is the same),
+    and the default (in-loop at every token count) gives those bits too."""
     T, K, Ns, r = 1100, 320, (128, 64, 64), 16
     ins = [synth.custom_inputs(40 + g, T, K, N, r, dy_std=0.1) for g, N in enumerate(Ns)]
     x, codes, absmax, A, B, dy = _dev_inputs(q, ins)
-    dx, _, _ = q.lora_nf4_bwd_multi(x, dy, codes, absmax, A, B, 16.0)
-    dx1, _, _ = q.lora_nf4_bwd_multi(x[:1023].contiguous(), [d[:1023].contiguous() for d in dy], codes, absmax,
-                                     A, B, 16.0)
-    torch.cuda.synchronize()
+    with q.weight_staging(True):
+        dx, _, _ = q.lora_nf4_bwd_multi(x, dy, codes, absmax, A, B, 16.0)
+        dx1, _, _ = q.lora_nf4_bwd_multi(x[:1023].contiguous(), [d[:1023].contiguous() for d in dy], codes,
+                                         absmax, A, B, 16.0)
+        torch.cuda.synchronize()
     assert torch.equal(dx[:1023], dx1)
+    dx0, _, _ = q.lora_nf4_bwd_multi(x, dy, codes, absmax, A, B, 16.0)
+    torch.cuda.synchronize()
+    assert torch.equal(dx0, dx)
 
 
 def test_bwd_multi_empty_batch(q):

@@ -136,9 +136,10 @@ def test_forward_tile_edges_agree(q, r):
     assert olora.rel_err(host_f64(u), u_ref) <= TOL
 
 
-# From 1024 tokens the forward dequantizes the weight once into its workspace and
-# runs the tiles on bf16; the values are those of the in-loop dequantization.
-# Ragged T, d_in and d_out (odd step counts), every rank block.
+# With weight staging on, from 1024 tokens the forward dequantizes the weight once
+# into its workspace and runs the tiles on bf16; the values are those of the
+# in-loop dequantization. Ragged T, d_in and d_out (odd step counts), every rank
+# block.
 DQ = [(1100, 320, 200, 16), (1030, 448, 520, 64), (2080, 192, 264, 24), (1040, 256, 136, 40)]
 
 
@@ -151,18 +152,23 @@ def test_forward_dequantized_matches_in_loop(q, T, K, N, r):
     inp = synth.custom_inputs(12, T, K, N, r)
     x, W, A, B = (dev_bf16(inp[k]) for k in ("x", "W", "A", "B"))
     codes, absmax = q.nf4_quantize(W)
-    assert q.lora_nf4_fwd_workspace_bytes(T, K, N, r) >= K * N * 2
-    assert q.lora_nf4_fwd_workspace_bytes(1023, K, N, r) == 0
-    y, u = q.lora_nf4_fwd(x, codes, absmax, A, B, 16.0)
-    y1, u1 = q.lora_nf4_fwd(x[:1023].contiguous(), codes, absmax, A, B, 16.0)
+    with q.weight_staging(True):
+        assert q.lora_nf4_fwd_workspace_bytes(T, K, N, r) >= K * N * 2
+        assert q.lora_nf4_fwd_workspace_bytes(1023, K, N, r) == 0
+        y, u = q.lora_nf4_fwd(x, codes, absmax, A, B, 16.0)
+        y1, u1 = q.lora_nf4_fwd(x[:1023].contiguous(), codes, absmax, A, B, 16.0)
+        torch.cuda.synchronize()
+    y0, u0 = q.lora_nf4_fwd(x, codes, absmax, A, B, 16.0)  # default: in-loop at every T
     torch.cuda.synchronize()
+    assert torch.equal(y0[:1023], y1) and torch.equal(u0[:1023], u1)
     assert torch.equal(y[:1023], y1) and torch.equal(u[:1023], u1)
     y_ref, u_ref = olora.forward(_f64(inp["x"]), _oracle_D(inp), _f64(inp["A"]), _f64(inp["B"]), 16.0, r)
     assert olora.rel_err(host_f64(y), y_ref) <= TOL
     assert olora.rel_err(host_f64(u), u_ref) <= TOL
 
 
-# From 4096 tokens at rank > 16 the dequantize-then-GEMM forward takes U = x A
+# With weight staging on, from 4096 tokens at rank > 16 the dequantize-then-GEMM
+# forward takes U = x A
 # from a separate pass (d_in split over four waves, fixed-order sum; the tile
 # kernel reads bf16(s U) in its epilogue): ranks 24 (half the 32-wide block), 40
 # and 64, ragged T, d_in and d_out; the full oracle on every output.
@@ -172,8 +178,9 @@ UPASS = [(4100, 320, 200, 64), (4130, 192, 136, 24), (4096, 448, 72, 40)]
 @pytest.mark.parametrize("T,K,N,r", UPASS)
 def test_forward_u_pass(q, T, K, N, r):
     inp = synth.custom_inputs(15, T, K, N, r)
-    assert q.lora_nf4_fwd_workspace_bytes(T, K, N, r) >= K * N * 2 + T * r * 2
-    _check_full(q, inp, 16.0, r, f"u-pass T={T} K={K} N={N} r={r}")
+    with q.weight_staging(True):
+        assert q.lora_nf4_fwd_workspace_bytes(T, K, N, r) >= K * N * 2 + T * r * 2
+        _check_full(q, inp, 16.0, r, f"u-pass T={T} K={K} N={N} r={r}")
 
 
 # From 4096 tokens, where the grid takes 256 x 256 tiles and d_in % 256 == 0, the
@@ -214,18 +221,21 @@ def test_dx_register_dequant(q, T, K, N, r):
     assert dx3 is None and torch.equal(dA3, r1[3]) and torch.equal(dB3, r1[4])
 
 
-# From 4096 tokens on 256 x 256 dX tiles (1024 on 128 x 128 tiles; at rank 16 only
-# where the register path above does not apply) the dX kernel runs on the weight
-# dequantized once into the workspace. Large token counts,
+# With weight staging on, from 4096 tokens on 256 x 256 dX tiles (1024 on 128 x 128
+# tiles) the dX kernel runs on the weight dequantized once into the workspace; by
+# default the same shapes run the in-loop kernels (or, at rank 16 on whole tiles,
+# the register path above). Large token counts,
 # ragged T and d_in, one to eight d_out steps, ranks 8 and 16; the full oracle on
 # every output.
 DQ_BWD = [(8200, 320, 192, 16), (8230, 192, 128, 8), (9000, 128, 64, 16), (8300, 448, 512, 16)]
 
 
 @pytest.mark.parametrize("T,K,N,r", DQ_BWD)
-def test_backward_dequantized(q, T, K, N, r):
+@pytest.mark.parametrize("staged", [True, False])
+def test_backward_dequantized(q, T, K, N, r, staged):
     inp = synth.custom_inputs(13, T, K, N, r)
-    _check_full(q, inp, 16.0, r, f"dq-bwd T={T} K={K} N={N} r={r}")
+    with q.weight_staging(staged):
+        _check_full(q, inp, 16.0, r, f"{'dq' if staged else 'in-loop'}-bwd T={T} K={K} N={N} r={r}")
 
 
 # The same path against the in-loop dequantization: rows of dX are independent,
@@ -241,11 +251,12 @@ def test_dx_dequantized_matches_in_loop(q, T, K, N, r, T_in):
     inp = synth.custom_inputs(14, T, K, N, r, dy_std=0.1)
     x, W, A, B, dY = (dev_bf16(inp[k]) for k in ("x", "W", "A", "B", "dY"))
     codes, absmax = q.nf4_quantize(W)
-    dx, _, _ = q.lora_nf4_bwd(x, dY, codes, absmax, A, B, 16.0)
-    dx1, _, _ = q.lora_nf4_bwd(x[:T_in].contiguous(), dY[:T_in].contiguous(), codes, absmax, A, B, 16.0)
-    torch.cuda.synchronize()
-    assert torch.equal(dx[:T_in], dx1)
-    _check_full(q, inp, 16.0, r, f"dqx T={T} K={K} N={N} r={r}")
+    with q.weight_staging(True):
+        dx, _, _ = q.lora_nf4_bwd(x, dY, codes, absmax, A, B, 16.0)
+        dx1, _, _ = q.lora_nf4_bwd(x[:T_in].contiguous(), dY[:T_in].contiguous(), codes, absmax, A, B, 16.0)
+        torch.cuda.synchronize()
+        assert torch.equal(dx[:T_in], dx1)
+        _check_full(q, inp, 16.0, r, f"dqx T={T} K={K} N={N} r={r}")
 
 
 @pytest.mark.parametrize("r", [16, 64])
