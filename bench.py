@@ -364,19 +364,24 @@ def train_step_run(lib, q, torch, d, w, sp, reps=50):
     """The training-step companions on one projection, HIP events around `reps`
     back-to-back C-ABI calls each:
       adamw      lora_adamw_step over A and B (float32 master, bf16 copy, bf16
-                 gradient and moments); bytes = 4 + 2 + 2 + 2*2 + 2*2 read/written
-                 per element = 16 (master in and out, copy out, gradient in, m, v in
-                 and out);
+                 gradient, float32 moments); bytes per element: master in and out 8,
+                 copy out 2, gradient in 2, each moment in and out 8 = 28;
+      adamw8     lora_adamw8_step (8-bit blockwise moments): 8 + 2 + 2 + 2 x 2 = 16
+                 per element (+ 16 per 256 for the scales);
       absmax_dq  nf4_absmax_quantize of the projection's block scales; bytes = 4 in
-                 + 1 out per scale (+ 8 per 256)."""
+                 + 1 out per scale (+ 8 per 256).
+    And the optimizer fused into the backward: lora_nf4_bwd_adamw against
+    lora_nf4_bwd + two lora_adamw_step calls on the same state, at the
+    workload's token count."""
     p = d["p"]
     K, N, r = p.d_in, p.d_out, w.r
     n = K * r + r * N
     master = torch.zeros(n, dtype=torch.float32, device="cuda")
     copy = torch.empty(n, dtype=torch.bfloat16, device="cuda")
     grad = torch.full((n,), 1e-3, dtype=torch.bfloat16, device="cuda")
-    m = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
-    v = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    m = torch.zeros(n, dtype=torch.float32, device="cuda")
+    v = torch.zeros(n, dtype=torch.float32, device="cuda")
+    st8 = q.adamw8_state(n)
     na = d["absmax"].numel()
     dq_q = torch.empty(na, dtype=torch.uint8, device="cuda")
     dq_s = torch.empty((na + 255) // 256, dtype=torch.float32, device="cuda")
@@ -388,6 +393,13 @@ def train_step_run(lib, q, torch, d, w, sp, reps=50):
         if st != 0:
             raise q.LoraNF4Error("lora_adamw_step", st)
 
+    def adamw8(step):
+        st = lib.lora_adamw8_step(n, master.data_ptr(), copy.data_ptr(), grad.data_ptr(), st8[0].data_ptr(),
+                                  st8[1].data_ptr(), st8[2].data_ptr(), st8[3].data_ptr(), step, 1e-4, 0.9,
+                                  0.999, 1e-8, 0.01, sp)
+        if st != 0:
+            raise q.LoraNF4Error("lora_adamw8_step", st)
+
     def dq(step):
         st = lib.nf4_absmax_quantize(d["absmax"].data_ptr(), na, dq_q.data_ptr(), dq_s.data_ptr(),
                                      dq_o.data_ptr(), sp)
@@ -396,23 +408,73 @@ def train_step_run(lib, q, torch, d, w, sp, reps=50):
 
     out = {}
     stream = torch.cuda.current_stream()
-    for name, fn, nbytes in (("adamw", adamw, 16 * n), ("absmax_dq", dq, 5 * na + 8 * dq_s.numel())):
+
+    def time_calls(fn, count):
         for i in range(3):
             fn(i + 1)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(reps):
+        for i in range(count):
             fn(i + 4)
         e1.record(stream)
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1000.0 / reps
-        out[name] = {"elements": n if name == "adamw" else na, "us": round(us, 2), "bytes": nbytes,
+        return e0.elapsed_time(e1) * 1000.0 / count
+
+    for name, fn, nbytes, elems in (("adamw", adamw, 28 * n, n), ("adamw8", adamw8, 16 * n + n // 16, n),
+                                    ("absmax_dq", dq, 5 * na + 8 * dq_s.numel(), na)):
+        us = time_calls(fn, reps)
+        out[name] = {"elements": elems, "us": round(us, 2), "bytes": nbytes,
                      "bound": "hbm", "achieved": round(nbytes / us / 1e3, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
+    # fused optimizer: backward + AdamW of A and B in one call, against backward + two steps
+    T = w.tokens
+    A2, B2 = d["A"].clone(), d["B"].clone()
+    sa = [torch.zeros(K * r, dtype=torch.float32, device="cuda") for _ in range(3)]
+    sb = [torch.zeros(r * N, dtype=torch.float32, device="cuda") for _ in range(3)]
+    sa[0].copy_(A2.float().view(-1)), sb[0].copy_(B2.float().view(-1))
+    dx = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty((K, r), dtype=torch.bfloat16, device="cuda")
+    dB = torch.empty((r, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(q.lora_nf4_bwd_workspace_bytes(T, K, N, r), 256), dtype=torch.uint8, device="cuda")
+
+    def fused(step):
+        st = lib.lora_nf4_bwd_adamw(T, K, N, r, w.alpha, d["x"].data_ptr(), d["dY"].data_ptr(),
+                                    d["codes"].data_ptr(), d["absmax"].data_ptr(), A2.data_ptr(), B2.data_ptr(),
+                                    d["u"].data_ptr(), dx.data_ptr(), *(t.data_ptr() for t in sa),
+                                    *(t.data_ptr() for t in sb), step, 1e-4, 0.9, 0.999, 1e-8, 0.01,
+                                    ws.data_ptr(), ws.numel(), sp)
+        if st != 0:
+            raise q.LoraNF4Error("lora_nf4_bwd_adamw", st)
+
+    def unfused(step):
+        st = lib.lora_nf4_bwd(T, K, N, r, w.alpha, d["x"].data_ptr(), d["dY"].data_ptr(), d["codes"].data_ptr(),
+                              d["absmax"].data_ptr(), A2.data_ptr(), B2.data_ptr(), d["u"].data_ptr(),
+                              dx.data_ptr(), dA.data_ptr(), dB.data_ptr(), ws.data_ptr(), ws.numel(), sp)
+        st = st or lib.lora_adamw_step(K * r, sa[0].data_ptr(), A2.data_ptr(), dA.data_ptr(), sa[1].data_ptr(),
+                                       sa[2].data_ptr(), step, 1e-4, 0.9, 0.999, 1e-8, 0.01, sp)
+        st = st or lib.lora_adamw_step(r * N, sb[0].data_ptr(), B2.data_ptr(), dB.data_ptr(), sb[1].data_ptr(),
+                                       sb[2].data_ptr(), step, 1e-4, 0.9, 0.999, 1e-8, 0.01, sp)
+        if st != 0:
+            raise q.LoraNF4Error("lora_nf4_bwd + lora_adamw_step", st)
+
+    if lora_bwd_adamw_available(q, r, N):
+        # interleaved rounds (the clock drifts over a run), median of each
+        tf, tu = [], []
+        for _ in range(5):
+            tf.append(time_calls(fused, 10))
+            tu.append(time_calls(unfused, 10))
+        t_f, t_u = float(np.median(tf)), float(np.median(tu))
+        out["bwd_with_optimizer"] = {"tokens": T, "fused_us": round(t_f, 2), "separate_us": round(t_u, 2),
+                                     "what": "lora_nf4_bwd_adamw (AdamW of A and B in the rank-r reduction) "
+                                             "against lora_nf4_bwd + two lora_adamw_step launches"}
     out["projection"] = f"{p.name} {K}->{N}"
-    del master, copy, grad, m, v, dq_q, dq_s, dq_o
+    del master, copy, grad, m, v, st8, dq_q, dq_s, dq_o, A2, B2, sa, sb, dx, dA, dB, ws
     return out
+
+
+def lora_bwd_adamw_available(q, r, N):
+    return r % 8 == 0 and r <= 64 and N % 8 == 0
 
 
 def multi_projection_run(lib, q, torch, sp, reps=10):
@@ -743,8 +805,10 @@ class ClockSampler:
     def summary(self):
         if not self.samples:
             return None
-        return {"median_mhz": round(pct(self.samples, 50), 1), "min_mhz": round(min(self.samples), 1),
-                "max_mhz": round(max(self.samples), 1), "samples": len(self.samples),
+        top = max(self.samples)
+        busy = [v for v in self.samples if v >= 0.5 * top]  # idle readings at the window's edges dropped
+        return {"median_mhz": round(pct(busy, 50), 1), "min_mhz": round(min(busy), 1),
+                "max_mhz": round(top, 1), "samples": len(busy), "dropped_idle": len(self.samples) - len(busy),
                 "source": "amd-smi metric -g 0 -c (mean of the XCDs' gfx clocks), polled every 50 ms"}
 
 

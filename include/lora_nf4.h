@@ -281,22 +281,68 @@ int lora_nf4_bwd_noalloc(int64_t T, int64_t d_in, int64_t d_out, int32_t r, floa
 /*
  * lora_adamw_step — one AdamW update of a LoRA factor (A or B), the optimizer
  * phase of a training step ("Unsloth performance measured: is it really 2x
- * faster?", section 2.2 time table, optimizer.step row; section 3: 16-bit
- * gradient states). Decoupled weight decay; for every element i < n, in float32:
- *     g = grad[i];  m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g^2
- *     p = p (1 - lr weight_decay) - (lr / (1 - beta1^step)) m / (sqrt(v) / sqrt(1 - beta2^step) + eps)
- * then m and v are stored as bf16 (nearest-even), p stays float32 and p_bf16 =
- * bf16(p) is the copy lora_nf4_fwd / lora_nf4_bwd read.
+ * faster?", section 2.2 time table, optimizer.step row). Decoupled weight decay;
+ * for every element i < n, as this fixed sequence of float32 operations, each
+ * rounded to nearest-even:
+ *     g = grad[i];  m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) (g g)
+ *     p = p (1 - lr wd) - (lr / (1 - b1^step)) (m / (sqrt(v) (1 / sqrt(1 - b2^step)) + eps))
+ * where each parenthesised constant is formed in float64 from the float32
+ * arguments and rounded once. p stays float32 and p_bf16 = bf16(p) is the copy
+ * lora_nf4_fwd / lora_nf4_bwd read.
  *   p       float32 [n] master copy (in/out)      p_bf16  bf16 [n] (out)
  *   grad    bf16 [n] (e.g. dA or dB of lora_nf4_bwd)
- *   m, v    bf16 [n] first and second moments (in/out; zero before step 1)
+ *   m, v    float32 [n] first and second moments (in/out; zero before step 1)
  *   step    1-based step number (bias correction)
  * n >= 0 (0: nothing to do); eps > 0; 0 <= beta1, beta2 < 1; finite lr and
  * weight_decay. All arrays disjoint (LN_EALIAS), 16-byte aligned (LN_EALIGN).
  */
-int lora_adamw_step(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* grad, uint16_t* m,
-                    uint16_t* v, int32_t step, float lr, float beta1, float beta2, float eps,
-                    float weight_decay, void* stream);
+int lora_adamw_step(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* grad, float* m, float* v,
+                    int32_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
+                    void* stream);
+
+/*
+ * lora_adamw8_step — lora_adamw_step with 8-bit moments (the 8-bit AdamW of
+ * "Reading the Unsloth changelog", section 1 memory list: optimizer state at a
+ * quarter of float32). Each moment is stored blockwise, 256 consecutive elements
+ * per block: one E4M3 code per element (OCP FP8 E4M3FN: nearest code, ties to
+ * even, saturating at 448) and one float32 scale per block. A step decodes
+ * m = f32(e4m3(code) * scale) (likewise v), runs lora_adamw_step's float32
+ * update, and re-encodes: scale = f32(max |x| over the block / 448), code =
+ * e4m3(f32(x / scale)), code 0 where the scale is 0.
+ *   m_codes, v_codes    uint8 [n] (in/out; zero before step 1)
+ *   m_scales, v_scales  float32 [ceil(n / 256)] (in/out; zero before step 1)
+ *   the other arguments and rules as for lora_adamw_step.
+ */
+int lora_adamw8_step(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* grad, uint8_t* m_codes,
+                     float* m_scales, uint8_t* v_codes, float* v_scales, int32_t step, float lr, float beta1,
+                     float beta2, float eps, float weight_decay, void* stream);
+
+/*
+ * lora_nf4_bwd_adamw — lora_nf4_bwd followed by lora_adamw_step of A and B, with
+ * the update applied by the backward's final reduction of dA and dB: the
+ * gradients are the float32 sums themselves (never rounded to bf16, never stored)
+ * and A and B are rewritten in place as bf16 of their updated masters. The
+ * optimizer phase then costs no launch of its own (the low-bit AdamW kernel of
+ * "Unsloth performance measured: is it really 2x faster?", section 2.2 time
+ * table). Use lora_nf4_bwd + lora_adamw_step where gradients accumulate over
+ * several micro-batches before a step.
+ *   A, B               bf16, read by the backward, then overwritten (in/out)
+ *   a_master, a_m, a_v float32 [d_in, r]: A's master copy and moments (in/out)
+ *   b_master, b_m, b_v float32 [r, d_out]: B's (in/out)
+ *   step, lr, beta1, beta2, eps, weight_decay   as for lora_adamw_step
+ *   the other arguments as for lora_nf4_bwd (dA, dB are not produced); the
+ *   workspace is sized by lora_nf4_bwd_workspace_bytes.
+ * T >= 1; r % 8 == 0 and r <= 64, d_out % 8 == 0 (the shapes whose rank-r
+ * gradients take the one-launch reduction; LN_ERANK / LN_ESHAPE otherwise).
+ * Every output (dx, A, B, the six state arrays, the workspace) disjoint from
+ * every input and from the others (LN_EALIAS).
+ */
+int lora_nf4_bwd_adamw(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha,
+                       const uint16_t* x, const uint16_t* dy, const uint8_t* w_codes, const float* w_absmax,
+                       uint16_t* A, uint16_t* B, const uint16_t* u_saved, uint16_t* dx, float* a_master,
+                       float* a_m, float* a_v, float* b_master, float* b_m, float* b_v, int32_t step, float lr,
+                       float beta1, float beta2, float eps, float weight_decay, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /*
  * lora_nf4_mfma_probe — measurement aid, no part of the linear: one launch of

@@ -32,7 +32,7 @@ __all__ = [
     "status_string", "EXPORTED_SYMBOLS", "LN_MAX_RANK", "LN_MAX_PROJ",
     "lora_adamw_step", "rslora_alpha", "nf4_absmax_quantize", "nf4_absmax_dequantize",
     "lora_nf4_bwd_multi", "lora_nf4_bwd_multi_workspace_bytes", "lora_nf4_bwd_noalloc",
-    "set_weight_staging", "weight_staging",
+    "set_weight_staging", "weight_staging", "lora_adamw8_step", "adamw8_state", "lora_nf4_bwd_adamw",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -47,7 +47,8 @@ EXPORTED_SYMBOLS = ("nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_
                     "nf4_absmax_quantize", "nf4_absmax_dequantize", "lora_nf4_bwd_multi",
                     "lora_nf4_bwd_multi_workspace_bytes", "lora_nf4_fwd_workspace_bytes",
                     "lora_nf4_fwd_multi_workspace_bytes", "lora_nf4_bwd_noalloc",
-                    "lora_nf4_set_weight_staging", "lora_nf4_mfma_probe")
+                    "lora_nf4_set_weight_staging", "lora_nf4_mfma_probe", "lora_adamw8_step",
+                    "lora_nf4_bwd_adamw")
 
 _lib = None
 
@@ -72,6 +73,12 @@ _SIGS = {
     "lora_nf4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "lora_adamw_step": (ctypes.c_int, [_i64, _p, _p, _p, _p, _p, ctypes.c_int32, ctypes.c_float,
                                        ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, _p]),
+    "lora_adamw8_step": (ctypes.c_int, [_i64, _p, _p, _p, _p, _p, _p, _p, ctypes.c_int32, ctypes.c_float,
+                                        ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, _p]),
+    "lora_nf4_bwd_adamw": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_float, _p, _p, _p, _p,
+                                          _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_int32,
+                                          ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                          ctypes.c_float, _p, ctypes.c_size_t, _p]),
     "lora_nf4_rslora_alpha": (ctypes.c_float, [ctypes.c_float, ctypes.c_int32]),
     "lora_nf4_set_weight_staging": (ctypes.c_int, [ctypes.c_int32]),
     "lora_nf4_mfma_probe": (ctypes.c_int64, [ctypes.c_int32, _p, _p]),
@@ -366,10 +373,10 @@ def lora_nf4_merge(codes, absmax, A, B, lora_alpha: float, dtype=torch.bfloat16)
 
 def lora_adamw_step(p_master, p_bf16, grad, m, v, step: int, lr: float, betas=(0.9, 0.999),
                     eps: float = 1e-8, weight_decay: float = 0.0):
-    """One AdamW step in place: p_master (float32), p_bf16 = bf16(p_master), moments m, v (bf16)."""
-    bf = torch.bfloat16
-    _dev(p_master, "p_master", torch.float32), _dev(p_bf16, "p_bf16", bf), _dev(grad, "grad", bf)
-    _dev(m, "m", bf), _dev(v, "v", bf)
+    """One AdamW step in place: p_master (float32), p_bf16 = bf16(p_master), moments m, v (float32)."""
+    bf, f32 = torch.bfloat16, torch.float32
+    _dev(p_master, "p_master", f32), _dev(p_bf16, "p_bf16", bf), _dev(grad, "grad", bf)
+    _dev(m, "m", f32), _dev(v, "v", f32)
     n = p_master.numel()
     for t, name in ((p_bf16, "p_bf16"), (grad, "grad"), (m, "m"), (v, "v")):
         if t.numel() != n:
@@ -377,6 +384,65 @@ def lora_adamw_step(p_master, p_bf16, grad, m, v, step: int, lr: float, betas=(0
     _check("lora_adamw_step", library().lora_adamw_step(
         n, p_master.data_ptr(), p_bf16.data_ptr(), grad.data_ptr(), m.data_ptr(), v.data_ptr(), int(step),
         float(lr), float(betas[0]), float(betas[1]), float(eps), float(weight_decay), _stream(p_master)))
+
+
+def adamw8_state(n: int, device="cuda"):
+    """Zero 8-bit AdamW state for n elements: (m codes, m scales, v codes, v scales)."""
+    nb = (n + 255) // 256
+    return (torch.zeros(n, dtype=torch.uint8, device=device), torch.zeros(nb, dtype=torch.float32, device=device),
+            torch.zeros(n, dtype=torch.uint8, device=device), torch.zeros(nb, dtype=torch.float32, device=device))
+
+
+def lora_adamw8_step(p_master, p_bf16, grad, state, step: int, lr: float, betas=(0.9, 0.999),
+                     eps: float = 1e-8, weight_decay: float = 0.0):
+    """One AdamW step with 8-bit blockwise moments, in place; state from adamw8_state."""
+    bf, f32, u8 = torch.bfloat16, torch.float32, torch.uint8
+    mq, ms, vq, vs = state
+    _dev(p_master, "p_master", f32), _dev(p_bf16, "p_bf16", bf), _dev(grad, "grad", bf)
+    _dev(mq, "m codes", u8), _dev(ms, "m scales", f32), _dev(vq, "v codes", u8), _dev(vs, "v scales", f32)
+    n = p_master.numel()
+    nb = (n + 255) // 256
+    for t, name, want in ((p_bf16, "p_bf16", n), (grad, "grad", n), (mq, "m codes", n), (vq, "v codes", n),
+                          (ms, "m scales", nb), (vs, "v scales", nb)):
+        if t.numel() != want:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {want}")
+    _check("lora_adamw8_step", library().lora_adamw8_step(
+        n, p_master.data_ptr(), p_bf16.data_ptr(), grad.data_ptr(), mq.data_ptr(), ms.data_ptr(), vq.data_ptr(),
+        vs.data_ptr(), int(step), float(lr), float(betas[0]), float(betas[1]), float(eps), float(weight_decay),
+        _stream(p_master)))
+
+
+def lora_nf4_bwd_adamw(x, dy, codes, absmax, A, B, lora_alpha: float, state, step: int, lr: float,
+                       betas=(0.9, 0.999), eps: float = 1e-8, weight_decay: float = 0.0, u_saved=None,
+                       need_dx: bool = True, workspace: torch.Tensor | None = None):
+    """The backward with the AdamW step of A and B applied in its rank-r reduction:
+    A and B (bf16) are updated in place, state = (A master, A m, A v, B master, B m, B v)
+    float32 tensors shaped like A and B. Returns dx (or None)."""
+    bf, f32 = torch.bfloat16, torch.float32
+    _dev(x, "x", bf, 2), _dev(dy, "dy", bf, 2), _dev(codes, "codes", torch.uint8, 2)
+    _dev(absmax, "absmax", f32, 2), _dev(A, "A", bf, 2), _dev(B, "B", bf, 2)
+    T, K, N, r = _lora_shapes(x, codes, A, B)
+    if dy.shape != (T, N):
+        raise ValueError("dy must be [T, d_out]")
+    if u_saved is not None:
+        _dev(u_saved, "u_saved", bf, 2)
+    names = ("A master", "A m", "A v", "B master", "B m", "B v")
+    for t, name, shape in zip(state, names, (A.shape,) * 3 + (B.shape,) * 3):
+        _dev(t, name, f32)
+        if t.shape != shape:
+            raise ValueError(f"{name} must have shape {tuple(shape)}")
+    dev = x.device
+    dx = torch.empty((T, K), dtype=bf, device=dev) if need_dx else None
+    nbytes = lora_nf4_bwd_workspace_bytes(T, K, N, r)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8)
+    _check("lora_nf4_bwd_adamw", library().lora_nf4_bwd_adamw(
+        T, K, N, r, float(lora_alpha), x.data_ptr(), dy.data_ptr(), codes.data_ptr(), absmax.data_ptr(),
+        A.data_ptr(), B.data_ptr(), _ptr(u_saved), _ptr(dx), *(t.data_ptr() for t in state), int(step),
+        float(lr), float(betas[0]), float(betas[1]), float(eps), float(weight_decay), workspace.data_ptr(),
+        workspace.numel(), _stream(x)))
+    return dx
 
 
 def rslora_alpha(lora_alpha: float, r: int) -> float:

@@ -422,13 +422,21 @@ int lora_nf4_bwd_multi(int64_t T, int64_t d_in, int32_t n_proj, const int64_t* d
                                                 workspace, plan, static_cast<hipStream_t>(stream)));
 }
 
-int lora_adamw_step(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* grad, uint16_t* m,
-                    uint16_t* v, int32_t step, float lr, float beta1, float beta2, float eps,
-                    float weight_decay, void* stream) {
-  if (n < 0 || step < 1) return LN_EINVAL;
-  if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(eps) || !(eps > 0.0f) ||
-      !(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
-    return LN_EINVAL;
+}  // extern "C"
+
+namespace {
+bool adamw_hparams_ok(int32_t step, float lr, float beta1, float beta2, float eps, float weight_decay) {
+  return step >= 1 && std::isfinite(lr) && std::isfinite(weight_decay) && std::isfinite(eps) && eps > 0.0f &&
+         beta1 >= 0.0f && beta1 < 1.0f && beta2 >= 0.0f && beta2 < 1.0f;
+}
+}  // namespace
+
+extern "C" {
+
+int lora_adamw_step(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* grad, float* m, float* v,
+                    int32_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
+                    void* stream) {
+  if (n < 0 || !adamw_hparams_ok(step, lr, beta1, beta2, eps, weight_decay)) return LN_EINVAL;
   if (n == 0) return LN_OK;
   if (p == nullptr || p_bf16 == nullptr || grad == nullptr || m == nullptr || v == nullptr)
     return LN_EINVAL;
@@ -436,11 +444,75 @@ int lora_adamw_step(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* grad,
   if (!aligned16(p) || !aligned16(p_bf16) || !aligned16(grad) || !aligned16(m) || !aligned16(v))
     return LN_EALIGN;
   const size_t nn = static_cast<size_t>(n);
-  const Span outs[4] = {{p, nn * 4}, {p_bf16, nn * 2}, {m, nn * 2}, {v, nn * 2}};
+  const Span outs[4] = {{p, nn * 4}, {p_bf16, nn * 2}, {m, nn * 4}, {v, nn * 4}};
   const Span ins[1] = {{grad, nn * 2}};
   if (any_alias(outs, 4, ins, 1)) return LN_EALIAS;
-  return hip_status(lnf4::launch_adamw(n, p, p_bf16, grad, m, v, step, lr, beta1, beta2, eps,
-                                       weight_decay, static_cast<hipStream_t>(stream)));
+  return hip_status(lnf4::launch_adamw(n, p, p_bf16, grad, m, v,
+                                       lnf4::adamw_args(step, lr, beta1, beta2, eps, weight_decay),
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int lora_adamw8_step(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* grad, uint8_t* m_codes,
+                     float* m_scales, uint8_t* v_codes, float* v_scales, int32_t step, float lr, float beta1,
+                     float beta2, float eps, float weight_decay, void* stream) {
+  if (n < 0 || !adamw_hparams_ok(step, lr, beta1, beta2, eps, weight_decay)) return LN_EINVAL;
+  if (n == 0) return LN_OK;
+  if (p == nullptr || p_bf16 == nullptr || grad == nullptr || m_codes == nullptr || m_scales == nullptr ||
+      v_codes == nullptr || v_scales == nullptr)
+    return LN_EINVAL;
+  if (n > (int64_t(1) << 40)) return LN_ESHAPE;
+  if (!aligned16(p) || !aligned16(p_bf16) || !aligned16(grad) || !aligned16(m_codes) || !aligned16(m_scales) ||
+      !aligned16(v_codes) || !aligned16(v_scales))
+    return LN_EALIGN;
+  const size_t nn = static_cast<size_t>(n), nb = (nn + 255) / 256;
+  const Span outs[6] = {{p, nn * 4}, {p_bf16, nn * 2}, {m_codes, nn}, {m_scales, nb * 4}, {v_codes, nn},
+                        {v_scales, nb * 4}};
+  const Span ins[1] = {{grad, nn * 2}};
+  if (any_alias(outs, 6, ins, 1)) return LN_EALIAS;
+  return hip_status(lnf4::launch_adamw8(n, p, p_bf16, grad, m_codes, m_scales, v_codes, v_scales,
+                                        lnf4::adamw_args(step, lr, beta1, beta2, eps, weight_decay),
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int lora_nf4_bwd_adamw(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha,
+                       const uint16_t* x, const uint16_t* dy, const uint8_t* w_codes, const float* w_absmax,
+                       uint16_t* A, uint16_t* B, const uint16_t* u_saved, uint16_t* dx, float* a_master,
+                       float* a_m, float* a_v, float* b_master, float* b_m, float* b_v, int32_t step, float lr,
+                       float beta1, float beta2, float eps, float weight_decay, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (x == nullptr || dy == nullptr || w_codes == nullptr || w_absmax == nullptr || A == nullptr ||
+      B == nullptr || a_master == nullptr || a_m == nullptr || a_v == nullptr || b_master == nullptr ||
+      b_m == nullptr || b_v == nullptr)
+    return LN_EINVAL;
+  if (T < 1 || !adamw_hparams_ok(step, lr, beta1, beta2, eps, weight_decay)) return LN_EINVAL;
+  int st = check_linear_shape(T, d_in, d_out, r, lora_alpha);
+  if (st != LN_OK) return st;
+  const lnf4::BwdPlan plan = lnf4::plan_bwd(T, d_in, d_out, r);
+  if (!lnf4::bwd_adamw_supported(plan)) return r % 8 != 0 || r > 64 ? LN_ERANK : LN_ESHAPE;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(w_codes) || !aligned16(w_absmax) || !aligned16(A) ||
+      !aligned16(B) || (u_saved != nullptr && !aligned16(u_saved)) || (dx != nullptr && !aligned16(dx)) ||
+      !aligned16(a_master) || !aligned16(a_m) || !aligned16(a_v) || !aligned16(b_master) || !aligned16(b_m) ||
+      !aligned16(b_v))
+    return LN_EALIGN;
+  if (workspace == nullptr || workspace_bytes < plan.bytes) return LN_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LN_EALIGN;
+  const size_t t = T, k = d_in, n = d_out, rr = r;
+  // A and B are read by the backward and rewritten by the update: each counts as an output
+  const Span outs[10] = {{dx, t * k * 2},       {A, k * rr * 2},       {B, rr * n * 2},
+                         {a_master, k * rr * 4}, {a_m, k * rr * 4},     {a_v, k * rr * 4},
+                         {b_master, rr * n * 4}, {b_m, rr * n * 4},     {b_v, rr * n * 4},
+                         {workspace, plan.bytes}};
+  const Span ins[5] = {{x, t * k * 2}, {dy, t * n * 2}, {w_codes, n * k / 2}, {w_absmax, n * k / 64 * 4},
+                       {u_saved, t * rr * 2}};
+  if (any_alias(outs, 10, ins, 5)) return LN_EALIAS;
+  lnf4::SkinnyAdamW adam;
+  adam.a = lnf4::AdamState{a_master, A, a_m, a_v};
+  adam.b = lnf4::AdamState{b_master, B, b_m, b_v};
+  adam.h = lnf4::adamw_args(step, lr, beta1, beta2, eps, weight_decay);
+  const float s = lora_alpha / static_cast<float>(r);
+  return hip_status(lnf4::launch_lora_bwd(static_cast<int>(T), static_cast<int>(d_in), static_cast<int>(d_out),
+                                          r, s, x, dy, w_codes, w_absmax, A, B, u_saved, dx, nullptr, nullptr,
+                                          workspace, plan, static_cast<hipStream_t>(stream), &adam));
 }
 
 int64_t lora_nf4_mfma_probe(int32_t iters, float* sink, void* stream) {

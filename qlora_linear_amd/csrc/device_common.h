@@ -145,6 +145,23 @@ __device__ __forceinline__ void wait_vmem_upto() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// ---- AdamW of one element, as a fixed sequence of float32 operations, each rounded
+// to nearest-even (no fused multiply-add), so every path that updates a LoRA
+// factor gives the same bits:
+//   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) (g g)
+//   p = p (1 - lr wd) - (lr / (1 - b1^t)) (m / (sqrt(v) (1 / sqrt(1 - b2^t)) + eps))
+// AdamWArgs (launch.h) carries the constants, rounded once from float64.
+// (Contraction is switched off in the body; `/` and __builtin_sqrtf are correctly
+// rounded in HIP device code, whereas __fsqrt_rn is the native approximation.)
+template <class Args>
+__device__ __forceinline__ void adamw_elem(const Args& h, float g, float& p, float& m, float& v) {
+#pragma clang fp contract(off)
+  m = h.beta1 * m + h.one_m_beta1 * g;
+  v = h.beta2 * v + h.one_m_beta2 * (g * g);
+  const float d = __builtin_sqrtf(v) * h.inv_sqrt_bc2 + h.eps;
+  p = p * h.decay - h.step_size * (m / d);
+}
+
 // Workgroup ids are dispatched round-robin over the 8 XCDs of MI355X (each with
 // its own L2). Map them so that each XCD receives one contiguous range of
 // logical tile ids; neighbouring logical tiles (which share input rows) then

@@ -217,6 +217,40 @@ inline bool fits_buffer(int64_t T, int64_t K, int64_t N) {
 // (r <= 128), then 12 (r <= 192) and 16 (r <= 256).
 inline int generic_rank_tiles(int r) { return r <= 128 ? (r + 15) / 16 : (r <= 192 ? 12 : 16); }
 
+// One AdamW step's float32 constants, formed in float64 and rounded once (see
+// adamw_elem in device_common.h).
+struct AdamWArgs {
+  float beta1, one_m_beta1, beta2, one_m_beta2, eps;
+  float decay;          // 1 - lr * weight_decay
+  float step_size;      // lr / (1 - beta1^t)
+  float inv_sqrt_bc2;   // 1 / sqrt(1 - beta2^t)
+};
+AdamWArgs adamw_args(int step, float lr, float beta1, float beta2, float eps, float weight_decay);
+// AdamW of a LoRA factor with float32 moments m, v [n].
+hipError_t launch_adamw(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* g, float* m, float* v,
+                        const AdamWArgs& h, hipStream_t stream);
+// AdamW with 8-bit blockwise moments: E4M3 codes [n] and float32 scales [ceil(n / 256)].
+hipError_t launch_adamw8(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* g, uint8_t* m_codes,
+                         float* m_scales, uint8_t* v_codes, float* v_scales, const AdamWArgs& h,
+                         hipStream_t stream);
+// The AdamW state of one LoRA factor updated in place by the fused backward: float32
+// master copy, the bf16 factor the kernels read, float32 moments.
+struct AdamState {
+  float* p;
+  uint16_t* w;
+  float* m;
+  float* v;
+};
+
+// Double quantization of n float32 block scales: E4M3 codes, one float32 scale
+// and offset per 256 scales; and its inverse.
+// The float32-moment AdamW step of A and B, applied by the rank-r reduction in
+// place of storing dA and dB (one projection).
+struct SkinnyAdamW {
+  AdamState a, b;
+  AdamWArgs h;
+};
+
 // Rank-r gradients dA, dB in one launch plus one reduce (ranks % 8 == 0, <= 64):
 // dA = x^T G over K columns with G [T][ra] at row stride vsa (>= ra: a column
 // slice of a wider array), dB = s U^T dY over N columns with U [T][rb]; K = 0 or
@@ -232,7 +266,7 @@ int skinny_splits(int64_t T, int64_t K, int64_t N);
 hipError_t launch_lora_skinny(int T, int K, int N, int ra, int rb, int vsa, float s, const uint16_t* x,
                               const uint16_t* g, const uint16_t* dy, const uint16_t* u,
                               float* part_a, float* part_b, int splits, const DaOut& da,
-                              uint16_t* dB, hipStream_t stream);
+                              uint16_t* dB, hipStream_t stream, const SkinnyAdamW* adam = nullptr);
 
 // Backward plan: how the workspace is carved. Shared by the launcher and the
 // workspace-size query so the two always agree.
@@ -258,7 +292,9 @@ hipError_t launch_lora_bwd(int T, int K, int N, int r, float s, const uint16_t* 
                            const uint16_t* dy, const uint8_t* codes, const float* absmax,
                            const uint16_t* A, const uint16_t* B, const uint16_t* u_saved,
                            uint16_t* dx, uint16_t* dA, uint16_t* dB, void* workspace,
-                           const BwdPlan& plan, hipStream_t stream);
+                           const BwdPlan& plan, hipStream_t stream, const SkinnyAdamW* adam = nullptr);
+// Whether the backward can apply AdamW in its rank-r reduction (plan.fast).
+inline bool bwd_adamw_supported(const BwdPlan& plan) { return plan.fast; }
 
 // Backward of several projections that share x (dX summed over them). Fused: one
 // dX launch over all projections (G side by side in [T][n r]); for n r <= 64 one
@@ -286,12 +322,6 @@ hipError_t launch_lora_bwd_multi(int T, int K, int n, const int* N, int r, float
 
 // AdamW step of one parameter array (float32 master p, bf16 copy, bf16 gradient
 // and moments), elementwise over n elements.
-hipError_t launch_adamw(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* g, uint16_t* m,
-                        uint16_t* v, int step, float lr, float beta1, float beta2, float eps,
-                        float weight_decay, hipStream_t stream);
-
-// Double quantization of n float32 block scales: E4M3 codes, one float32 scale
-// and offset per 256 scales; and its inverse.
 hipError_t launch_absmax_dq(int64_t n, const float* absmax, uint8_t* q, float* scale, float* offset,
                             hipStream_t stream);
 hipError_t launch_absmax_undq(int64_t n, const uint8_t* q, const float* scale, const float* offset,

@@ -372,7 +372,8 @@ hipError_t launch_bwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
                          const uint16_t* dy, const uint8_t* codes, const float* absmax,
                          const uint16_t* A, const uint16_t* B, const uint16_t* u_saved,
                          uint16_t* dx, uint16_t* dA, uint16_t* dB, void* workspace,
-                         const BwdPlan& p, hipStream_t stream) {
+                         const BwdPlan& p, hipStream_t stream, const SkinnyAdamW* adam) {
+  if (adam != nullptr && !p.fast) return hipErrorInvalidValue;
   char* ws = static_cast<char*>(workspace);
   uint16_t* g = reinterpret_cast<uint16_t*>(ws + p.off_g);
   uint16_t* u = reinterpret_cast<uint16_t*>(ws + p.off_u);
@@ -410,7 +411,7 @@ hipError_t launch_bwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
     DaOut da{};
     da.p[0] = dA;
     da.gw = r;
-    return launch_lora_skinny(T, K, N, r, r, r, s, x, g, dy, uu, pa, pb, p.splits_a, da, dB, stream);
+    return launch_lora_skinny(T, K, N, r, r, r, s, x, g, dy, uu, pa, pb, p.splits_a, da, dB, stream, adam);
   }
   const int tca = (T + p.splits_a - 1) / p.splits_a;
   const int tcb = (T + p.splits_b - 1) / p.splits_b;
@@ -540,10 +541,10 @@ hipError_t launch_lora_bwd(int T, int K, int N, int r, float s, const uint16_t* 
                            const uint16_t* dy, const uint8_t* codes, const float* absmax,
                            const uint16_t* A, const uint16_t* B, const uint16_t* u_saved,
                            uint16_t* dx, uint16_t* dA, uint16_t* dB, void* workspace,
-                           const BwdPlan& plan, hipStream_t stream) {
+                           const BwdPlan& plan, hipStream_t stream, const SkinnyAdamW* adam) {
 #define LNF4_BWD(RT_)                                                                              \
   return launch_bwd_rt<RT_>(T, K, N, r, s, x, dy, codes, absmax, A, B, u_saved, dx, dA, dB,        \
-                            workspace, plan, stream)
+                            workspace, plan, stream, adam)
   switch (generic_rank_tiles(r)) {
     case 1: LNF4_BWD(1);
     case 2: LNF4_BWD(2);

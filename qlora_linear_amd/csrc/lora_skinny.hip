@@ -213,6 +213,41 @@ __global__ __launch_bounds__(256) void skinny_reduce2_kernel(const float* __rest
   }
 }
 
+// The same reduction for one projection (ra = rb = r), with the AdamW step of A and
+// B applied to the float32 sums instead of storing dA and dB: the gradient never
+// goes to HBM. A's state is indexed like A [K][r], B's like B [r][N].
+__global__ __launch_bounds__(256) void skinny_reduce2_adamw_kernel(const float* __restrict__ part_a,
+                                                                   const float* __restrict__ part_b,
+                                                                   int splits, int K, int N, int r, float s,
+                                                                   const AdamState sa, const AdamState sb,
+                                                                   const AdamWArgs h) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t na = static_cast<int64_t>(K) * r;
+  AdamState st;
+  size_t e;
+  float g;
+  if (idx < na) {
+    const int j = static_cast<int>(idx / K), c = static_cast<int>(idx - static_cast<int64_t>(j) * K);
+    g = sum_splits(part_a + static_cast<size_t>(j) * K + c, splits, static_cast<size_t>(r) * K);
+    st = sa;
+    e = static_cast<size_t>(c) * r + j;
+  } else if (idx < na + static_cast<int64_t>(N) * r) {
+    const int64_t i2 = idx - na;
+    const int j = static_cast<int>(i2 / N), c = static_cast<int>(i2 - static_cast<int64_t>(j) * N);
+    g = __fmul_rn(s, sum_splits(part_b + static_cast<size_t>(j) * N + c, splits, static_cast<size_t>(r) * N));
+    st = sb;
+    e = static_cast<size_t>(j) * N + c;
+  } else {
+    return;
+  }
+  float p = st.p[e], m = st.m[e], v = st.v[e];
+  adamw_elem(h, g, p, m, v);
+  st.p[e] = p;
+  st.m[e] = m;
+  st.v[e] = v;
+  st.w[e] = to_bf16(p);
+}
+
 }  // namespace
 
 bool lora_skinny_supported(int r) { return r % 8 == 0 && r <= 64; }
@@ -233,7 +268,7 @@ int skinny_splits(int64_t T, int64_t K, int64_t N) {
 hipError_t launch_lora_skinny(int T, int K, int N, int ra, int rb, int vsa, float s, const uint16_t* x,
                               const uint16_t* g, const uint16_t* dy, const uint16_t* u,
                               float* part_a, float* part_b, int splits, const DaOut& da,
-                              uint16_t* dB, hipStream_t stream) {
+                              uint16_t* dB, hipStream_t stream, const SkinnyAdamW* adam) {
   int per = (T + splits - 1) / splits;
   per = ((per + TT - 1) / TT) * TT;
   const int cb_a = (K + BC - 1) / BC, cb_b = (N + BC - 1) / BC;
@@ -247,6 +282,12 @@ hipError_t launch_lora_skinny(int T, int K, int N, int ra, int rb, int vsa, floa
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t total = static_cast<int64_t>(K) * ra + static_cast<int64_t>(N) * rb;
+  if (adam != nullptr) {
+    if (ra != rb) return hipErrorInvalidValue;
+    skinny_reduce2_adamw_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(
+        part_a, part_b, splits, K, N, ra, s, adam->a, adam->b, adam->h);
+    return hipGetLastError();
+  }
   skinny_reduce2_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(
       part_a, part_b, splits, K, N, ra, rb, s, da, dB);
   return hipGetLastError();

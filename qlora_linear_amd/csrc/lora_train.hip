@@ -1,11 +1,15 @@
 // Training-step companions of the fused NF4-LoRA linear (gfx950):
 //
-//  * adamw_kernel — the optimizer update of a LoRA factor. The pages time the
-//    optimizer step as its own phase and run it as a GPU kernel with 16-bit
+//  * adamw_kernel / adamw8_kernel — the optimizer update of a LoRA factor. The
+//    pages time the optimizer step as its own phase, a GPU kernel with low-bit
 //    state ("Unsloth performance measured: is it really 2x faster?", section 2.2
-//    time table and section 3). Decoupled weight decay (AdamW); float32 master
-//    weights, bf16 copy for the GEMM kernels, bf16 moments. One pass reads and
-//    writes every array once: bound by HBM.
+//    time table; "Reading the Unsloth changelog", section 1: 8-bit AdamW at a
+//    quarter of the state memory). Decoupled weight decay (AdamW); float32
+//    master weights, bf16 copy for the GEMM kernels; moments in float32, or
+//    8-bit: per 256-element block one float32 scale and one E4M3 code per
+//    element. One pass reads and writes every array once: bound by HBM. (The
+//    backward can also apply the float32-moment update itself, in its rank-r
+//    reduction: lora_skinny.hip.)
 //
 //  * absmax double quantization — the float32 block scales of the NF4 weight
 //    stored once more as 8-bit E4M3 codes with one float32 scale and offset per
@@ -27,68 +31,38 @@ namespace {
 
 // ---- AdamW ---------------------------------------------------------------------------
 
-struct AdamWArgs {
-  float beta1, one_m_beta1, beta2, one_m_beta2, eps;
-  float decay;          // 1 - lr * weight_decay
-  float step_size;      // lr / (1 - beta1^t)
-  float inv_sqrt_bc2;   // 1 / sqrt(1 - beta2^t)
-};
-
-__device__ __forceinline__ void adamw_elem(const AdamWArgs& h, float g, float& p, float& m, float& v) {
-  m = h.beta1 * m + h.one_m_beta1 * g;
-  v = h.beta2 * v + h.one_m_beta2 * (g * g);
-  const float denom = __fsqrt_rn(v) * h.inv_sqrt_bc2 + h.eps;
-  p = p * h.decay - h.step_size * __fdiv_rn(m, denom);
-}
-
 constexpr int kAdamThreads = 256;
 
-// Thread i owns elements 8 i .. 8 i + 7: 16-byte loads of the bf16 arrays and two
-// float4 of the master copy. The last thread of a ragged length runs elementwise.
+// float32 moments. Thread i owns elements 4 i .. 4 i + 3: float4 loads of the
+// master copy and both moments, 8-byte loads of the bf16 gradient. The last
+// thread of a ragged length runs elementwise.
 __global__ __launch_bounds__(kAdamThreads) void adamw_kernel(int64_t n, float* __restrict__ p,
                                                              uint16_t* __restrict__ p_bf16,
                                                              const uint16_t* __restrict__ g,
-                                                             uint16_t* __restrict__ m,
-                                                             uint16_t* __restrict__ v,
+                                                             float* __restrict__ m, float* __restrict__ v,
                                                              const AdamWArgs h) {
-  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * kAdamThreads + threadIdx.x) * 8;
+  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * kAdamThreads + threadIdx.x) * 4;
   if (i0 >= n) return;
-  if (i0 + 8 <= n) {
-    const uint4 gq = *reinterpret_cast<const uint4*>(g + i0);
-    const uint4 mq = *reinterpret_cast<const uint4*>(m + i0);
-    const uint4 vq = *reinterpret_cast<const uint4*>(v + i0);
-    float4 pa = *reinterpret_cast<const float4*>(p + i0);
-    float4 pb = *reinterpret_cast<const float4*>(p + i0 + 4);
-    const uint32_t gw[4] = {gq.x, gq.y, gq.z, gq.w}, mw[4] = {mq.x, mq.y, mq.z, mq.w},
-                   vw[4] = {vq.x, vq.y, vq.z, vq.w};
-    float pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-    uint32_t mo[4], vo[4], po[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float mm[2], vv[2];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const float gg = __uint_as_float((h2 ? gw[q] & 0xFFFF0000u : gw[q] << 16));
-        mm[h2] = __uint_as_float((h2 ? mw[q] & 0xFFFF0000u : mw[q] << 16));
-        vv[h2] = __uint_as_float((h2 ? vw[q] & 0xFFFF0000u : vw[q] << 16));
-        adamw_elem(h, gg, pv[2 * q + h2], mm[h2], vv[h2]);
-      }
-      mo[q] = pack_bf16x2(mm[0], mm[1]);
-      vo[q] = pack_bf16x2(vv[0], vv[1]);
-      po[q] = pack_bf16x2(pv[2 * q], pv[2 * q + 1]);
-    }
-    *reinterpret_cast<uint4*>(m + i0) = uint4{mo[0], mo[1], mo[2], mo[3]};
-    *reinterpret_cast<uint4*>(v + i0) = uint4{vo[0], vo[1], vo[2], vo[3]};
-    *reinterpret_cast<uint4*>(p_bf16 + i0) = uint4{po[0], po[1], po[2], po[3]};
-    *reinterpret_cast<float4*>(p + i0) = float4{pv[0], pv[1], pv[2], pv[3]};
-    *reinterpret_cast<float4*>(p + i0 + 4) = float4{pv[4], pv[5], pv[6], pv[7]};
+  if (i0 + 4 <= n) {
+    const uint2 gq = *reinterpret_cast<const uint2*>(g + i0);
+    float4 pq = *reinterpret_cast<const float4*>(p + i0);
+    float4 mq = *reinterpret_cast<const float4*>(m + i0);
+    float4 vq = *reinterpret_cast<const float4*>(v + i0);
+    adamw_elem(h, __uint_as_float(gq.x << 16), pq.x, mq.x, vq.x);
+    adamw_elem(h, __uint_as_float(gq.x & 0xFFFF0000u), pq.y, mq.y, vq.y);
+    adamw_elem(h, __uint_as_float(gq.y << 16), pq.z, mq.z, vq.z);
+    adamw_elem(h, __uint_as_float(gq.y & 0xFFFF0000u), pq.w, mq.w, vq.w);
+    *reinterpret_cast<float4*>(p + i0) = pq;
+    *reinterpret_cast<float4*>(m + i0) = mq;
+    *reinterpret_cast<float4*>(v + i0) = vq;
+    *reinterpret_cast<uint2*>(p_bf16 + i0) = uint2{pack_bf16x2(pq.x, pq.y), pack_bf16x2(pq.z, pq.w)};
   } else {
     for (int64_t i = i0; i < n; ++i) {
-      float pp = p[i], mm = bf16_to_f32(m[i]), vv = bf16_to_f32(v[i]);
+      float pp = p[i], mm = m[i], vv = v[i];
       adamw_elem(h, bf16_to_f32(g[i]), pp, mm, vv);
       p[i] = pp;
-      m[i] = to_bf16(mm);
-      v[i] = to_bf16(vv);
+      m[i] = mm;
+      v[i] = vv;
       p_bf16[i] = to_bf16(pp);
     }
   }
@@ -122,6 +96,54 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   else if (e == 0) v = static_cast<float>(mant) * 0.001953125f;  // 2^-9
   else v = __uint_as_float(((e + 120u) << 23) | (mant << 20));
   return (c & 0x80u) ? -v : v;
+}
+
+// ---- AdamW with 8-bit blockwise moments ---------------------------------------------
+// One 256-thread workgroup per block of 256 state elements: decode both moments
+// (f32(e4m3(code) * scale)), the float32 step, then the block's new maxima (exact,
+// two-level max over the waves) give the new scales f32(max / 448) and codes
+// e4m3(f32(x / scale)) (code 0 when the scale is 0).
+__global__ __launch_bounds__(kDqBlock) void adamw8_kernel(int64_t n, float* __restrict__ p,
+                                                          uint16_t* __restrict__ p_bf16,
+                                                          const uint16_t* __restrict__ g,
+                                                          uint8_t* __restrict__ mq, float* __restrict__ ms,
+                                                          uint8_t* __restrict__ vq, float* __restrict__ vs,
+                                                          const AdamWArgs h) {
+  __shared__ float red[2][kDqBlock / 64];
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kDqBlock + threadIdx.x;
+  const bool ok = i < n;
+  float pp = 0.f, m = 0.f, v = 0.f;
+  if (ok) {
+    m = __fmul_rn(e4m3_value(mq[i]), ms[blockIdx.x]);
+    v = __fmul_rn(e4m3_value(vq[i]), vs[blockIdx.x]);
+    pp = p[i];
+    adamw_elem(h, bf16_to_f32(g[i]), pp, m, v);
+  }
+  float am = fabsf(m), av = v;  // zero past a ragged end
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    am = fmaxf(am, __shfl_xor(am, o));
+    av = fmaxf(av, __shfl_xor(av, o));
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][wave] = am;
+    red[1][wave] = av;
+  }
+  __syncthreads();  // every thread has read its block's old scales
+  am = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  av = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+  const float nms = __fdiv_rn(am, 448.0f), nvs = __fdiv_rn(av, 448.0f);
+  if (ok) {
+    mq[i] = static_cast<uint8_t>(nms > 0.0f ? e4m3_encode(__fdiv_rn(m, nms)) : 0u);
+    vq[i] = static_cast<uint8_t>(nvs > 0.0f ? e4m3_encode(__fdiv_rn(v, nvs)) : 0u);
+    p[i] = pp;
+    p_bf16[i] = to_bf16(pp);
+  }
+  if (threadIdx.x == 0) {
+    ms[blockIdx.x] = nms;
+    vs[blockIdx.x] = nvs;
+  }
 }
 
 // One 256-thread workgroup per block of 256 scales.
@@ -172,23 +194,35 @@ __global__ __launch_bounds__(256) void absmax_undq_kernel(int64_t n, const uint8
 
 }  // namespace
 
-hipError_t launch_adamw(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* g, uint16_t* m,
-                        uint16_t* v, int step, float lr, float beta1, float beta2, float eps,
-                        float weight_decay, hipStream_t stream) {
+AdamWArgs adamw_args(int step, float lr, float beta1, float beta2, float eps, float weight_decay) {
   AdamWArgs h;
   h.beta1 = beta1;
   h.one_m_beta1 = static_cast<float>(1.0 - static_cast<double>(beta1));
   h.beta2 = beta2;
   h.one_m_beta2 = static_cast<float>(1.0 - static_cast<double>(beta2));
   h.eps = eps;
-  h.decay = static_cast<float>(1.0 - static_cast<double>(lr) * weight_decay);
-  const double bc1 = 1.0 - std::pow(static_cast<double>(beta1), step);
-  const double bc2 = 1.0 - std::pow(static_cast<double>(beta2), step);
-  h.step_size = static_cast<float>(lr / bc1);
+  h.decay = static_cast<float>(1.0 - static_cast<double>(lr) * static_cast<double>(weight_decay));
+  const double bc1 = 1.0 - std::pow(static_cast<double>(beta1), static_cast<double>(step));
+  const double bc2 = 1.0 - std::pow(static_cast<double>(beta2), static_cast<double>(step));
+  h.step_size = static_cast<float>(static_cast<double>(lr) / bc1);
   h.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(bc2));
-  const int64_t threads = (n + 7) / 8;
+  return h;
+}
+
+hipError_t launch_adamw(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* g, float* m, float* v,
+                        const AdamWArgs& h, hipStream_t stream) {
+  const int64_t threads = (n + 3) / 4;
   const int64_t blocks = (threads + kAdamThreads - 1) / kAdamThreads;
   adamw_kernel<<<static_cast<unsigned>(blocks), kAdamThreads, 0, stream>>>(n, p, p_bf16, g, m, v, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_adamw8(int64_t n, float* p, uint16_t* p_bf16, const uint16_t* g, uint8_t* m_codes,
+                         float* m_scales, uint8_t* v_codes, float* v_scales, const AdamWArgs& h,
+                         hipStream_t stream) {
+  const int64_t blocks = (n + kDqBlock - 1) / kDqBlock;
+  adamw8_kernel<<<static_cast<unsigned>(blocks), kDqBlock, 0, stream>>>(n, p, p_bf16, g, m_codes, m_scales,
+                                                                       v_codes, v_scales, h);
   return hipGetLastError();
 }
 

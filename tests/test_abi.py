@@ -47,7 +47,8 @@ def test_header_declares_the_boundary():
                             "nf4_absmax_quantize", "nf4_absmax_dequantize", "lora_nf4_bwd_multi",
                             "lora_nf4_bwd_multi_workspace_bytes", "lora_nf4_fwd_workspace_bytes",
                             "lora_nf4_fwd_multi_workspace_bytes", "lora_nf4_bwd_noalloc",
-                            "lora_nf4_set_weight_staging", "lora_nf4_mfma_probe"])
+                            "lora_nf4_set_weight_staging", "lora_nf4_mfma_probe", "lora_adamw8_step",
+                            "lora_nf4_bwd_adamw"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -374,6 +375,50 @@ def test_adamw_validation(lib):
     assert call(v=v + 8) == LN_EALIGN
     assert call(m=g + 64) == LN_EALIAS  # a moment overlapping the gradient
     assert call(pb=p + 128) == LN_EALIAS
+
+
+def test_adamw8_validation(lib):
+    p, pb, g, mq, ms, vq, vs = (P + (i << 30) for i in range(7))
+
+    def call(n=300, step=1, **kw):
+        a = dict(p=p, pb=pb, g=g, mq=mq, ms=ms, vq=vq, vs=vs)
+        a.update(kw)
+        return lib.lora_adamw8_step(n, a["p"], a["pb"], a["g"], a["mq"], a["ms"], a["vq"], a["vs"], step,
+                                    1e-3, 0.9, 0.999, 1e-8, 0.0, None)
+
+    assert call(n=0, p=None) == LN_OK
+    assert call(step=0) == LN_EINVAL
+    assert call(ms=None) == LN_EINVAL
+    assert call(vs=vs + 4) == LN_EALIGN
+    assert call(ms=mq + 256) == LN_EALIAS   # the scales inside the 300 codes
+    assert call(vq=g + 512) == LN_EALIAS    # codes on top of the gradient
+
+
+def test_bwd_adamw_validation(lib):
+    T, K, N, r = 8, 64, 64, 8
+    ptrs = [P + (i << 30) for i in range(16)]
+    x, dy, c, a, A, B, dx, am, amm, av, bm, bmm, bv, ws = ptrs[:14]
+    need = lib.lora_nf4_bwd_workspace_bytes(T, K, N, r)
+
+    def call(T=T, K=K, N=N, r=r, step=1, u=None, ws_bytes=need, **kw):
+        d = dict(x=x, dy=dy, c=c, a=a, A=A, B=B, dx=dx, am=am, amm=amm, av=av, bm=bm, bmm=bmm, bv=bv, ws=ws)
+        d.update(kw)
+        return lib.lora_nf4_bwd_adamw(T, K, N, r, 16.0, d["x"], d["dy"], d["c"], d["a"], d["A"], d["B"], u,
+                                      d["dx"], d["am"], d["amm"], d["av"], d["bm"], d["bmm"], d["bv"], step,
+                                      1e-3, 0.9, 0.999, 1e-8, 0.0, d["ws"], ctypes.c_size_t(ws_bytes), None)
+
+    assert call(T=0) == LN_EINVAL          # nothing to learn from
+    assert call(step=0) == LN_EINVAL
+    assert call(bv=None) == LN_EINVAL
+    assert call(r=12) == LN_ERANK           # the fused reduction needs r % 8 == 0, r <= 64
+    assert call(r=72) == LN_ERANK
+    assert call(N=60) == LN_ESHAPE          # ... and d_out % 8 == 0
+    assert call(ws=None) == LN_EWORKSPACE
+    assert call(ws_bytes=need - 1) == LN_EWORKSPACE
+    assert call(amm=am + 8) == LN_EALIGN
+    assert call(amm=am + 16) == LN_EALIAS   # A's moments overlapping its master copy
+    assert call(A=x) == LN_EALIAS           # the factor on top of x
+    assert call(bm=B) == LN_EALIAS
 
 
 def test_absmax_dq_validation(lib):
