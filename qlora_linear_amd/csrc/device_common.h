@@ -97,9 +97,17 @@ __device__ __forceinline__ uint4 load8_masked(const uint16_t* p, int n) {
 }
 
 // ---- buffer resources (raw buffers: byte offsets, out-of-range loads return 0) ----
-// The range check compares voffset + soffset (+ the instruction offset) against
-// the descriptor's byte count, so a run-ahead load that a uniform soffset pushes
-// past the end reads zeros, never the memory that follows (checked on gfx950).
+// A load whose lane offset (voffset) lies at or past the descriptor's byte count
+// returns zeros. The kernels put every row and column index in the lane offset and
+// keep the scalar offset (if any) for a K-step that is clamped to the last step,
+// or advance the descriptor's base to the step and pass 0; either way no load
+// depends on whether the scalar offset enters the range check, and none reaches
+// past its operand.
+// kOutOfRange: a lane offset past every descriptor's byte count (the library keeps
+// each operand a descriptor covers below 0x7FFFFF00 bytes, so it also stays out of
+// range, without wrapping, with any scalar offset below that), for loads that must
+// read zeros.
+constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;
 // Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format).
 constexpr int kBufferFlags = 0x00020000;
 

@@ -208,7 +208,7 @@ hipError_t launch_lora_dx_splitk(int T, int K, int N, int r, float s, const uint
 // 16-byte pieces: they are used only when every operand they cover fits and
 // d_out % 8 == 0. Other shapes take the generic kernels.
 inline bool fits_buffer(int64_t T, int64_t K, int64_t N) {
-  const int64_t lim = (int64_t(1) << 31) - 1;
+  const int64_t lim = 0x7FFFFF00;  // below kOutOfRange (device_common.h)
   return N % 8 == 0 && T * K * 2 < lim && T * N * 2 < lim && N * K / 2 < lim && N * (K / 64) * 4 < lim &&
          K * 128 * 2 < lim && N * 64 * 2 < lim;
 }

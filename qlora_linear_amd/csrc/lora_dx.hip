@@ -102,12 +102,17 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
   if (tid < 16) lut[tid] = nf4_level(tid);
 
   // ---- buffer resources: out-of-range loads return zeros ------------------------
+  // Every load takes a descriptor whose base is advanced to its step by scalar
+  // arithmetic (scalar offset 0), and whose byte count ends with its operand's
+  // range for this tile: the lane offset holds only the position within the step,
+  // so rows past T or d_out lie past the range and read zeros, and no load reaches
+  // past its operand. Step indices are clamped to the projection's last step, so
+  // the run-ahead loads past the end re-read that step (unused).
   // Several projections: each load stream (dY one step ahead; codes, absmax and
-  // B two steps ahead) keeps its projection's descriptors and offsets in
-  // registers and moves to the next projection when its step crosses a boundary
-  // (steps advance by one, every projection has at least one), so the loop reads
-  // the table only at those crossings. Steps past the end stay in the last
-  // projection beyond its range: their loads read zeros or unused bytes.
+  // B two steps ahead) keeps its projection's bases and offsets in registers and
+  // moves to the next projection when its step crosses a boundary (steps advance
+  // by one, every projection has at least one), so the loop reads the table only
+  // at those crossings. Steps past the end stay in the last projection.
   const int rows_t = min(T - m0, BM);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
@@ -122,7 +127,8 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
     }
   };
   set_yvoff(N0);
-  auto rs_y = make_rsrc(tab.dy[0] + static_cast<size_t>(m0) * N0, static_cast<uint32_t>(rows_t) * N0 * 2);
+  const uint16_t* y_ptr = tab.dy[0] + static_cast<size_t>(m0) * N0;
+  uint32_t y_bytes = static_cast<uint32_t>(rows_t) * N0 * 2;
   // DQ weight tile: wave w fills 1 KB pieces 4 w .. 4 w + 3 of the [64][BT] stage;
   // lane l of piece c lands at element 512 c + 8 l (row n, 16-byte piece p') and
   // loads piece p' ^ 4 (n & 3) of that weight row. Rows past d_out lie outside the
@@ -133,33 +139,41 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
     const int e = (wave * 4 + q) * 512 + lane * 8, n = e / BT, pp = (e % BT) / 8;
     wvoff[q] = static_cast<uint32_t>(n) * K * 2 + ((pp ^ (4 * (n & 3))) * 16);
   }
-  auto w_rsrc = [&](int g) {
-    return make_rsrc(DQ ? tab.wdq[g] + k0 : tab.dy[g],
-                     DQ ? static_cast<uint32_t>((static_cast<size_t>(tab.N[g]) * K - k0) * 2) : 0u);
-  };
-  auto rs_w = w_rsrc(0);
-  int y_g = 0, y_beg = 0, y_end = tab.step_end[0];
+  const uint16_t* w_ptr = DQ ? tab.wdq[0] + k0 : nullptr;
+  uint32_t w_bytes = DQ ? static_cast<uint32_t>((static_cast<size_t>(N0) * K - k0) * 2) : 0u;
+  int y_g = 0, y_beg = 0, y_end = tab.step_end[0], y_N = N0;
+  int y_ls = 0;  // the clamped step (within its projection) of the last load_y_lds
   auto load_y_lds = [&](int st, uint16_t* stage) {
     if constexpr (MULTI) {
       if (st >= y_end && y_g + 1 < tab.n) {
         ++y_g;
         y_beg = y_end;
         y_end = tab.step_end[y_g];
-        const int Ng = tab.N[y_g];
-        rs_y = make_rsrc(tab.dy[y_g] + static_cast<size_t>(m0) * Ng, static_cast<uint32_t>(rows_t) * Ng * 2);
-        set_yvoff(Ng);
-        if constexpr (DQ) rs_w = w_rsrc(y_g);
+        y_N = tab.N[y_g];
+        y_ptr = tab.dy[y_g] + static_cast<size_t>(m0) * y_N;
+        y_bytes = static_cast<uint32_t>(rows_t) * y_N * 2;
+        set_yvoff(y_N);
+        if constexpr (DQ) {
+          w_ptr = tab.wdq[y_g] + k0;
+          w_bytes = static_cast<uint32_t>((static_cast<size_t>(y_N) * K - k0) * 2);
+        }
       }
     }
+    y_ls = min(st, y_end - 1) - y_beg;
+    const auto rs_y = make_rsrc(y_ptr + y_ls * BK, y_bytes - y_ls * BK * 2);
+    // On the step with d_out's last columns, chunks past d_out read the next row's
+    // dY (the tile's last row reads zeros there): they meet weight rows past d_out,
+    // which read zeros, so they add nothing (a non-finite value there could only
+    // reach a dX that already holds the non-finite products of its own row).
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      buf_load16_lds(rs_y, stage + (wave_u * 4 + q) * 512, yvoff[q], (st - y_beg) * BK * 2);
+    for (int q = 0; q < 4; ++q) buf_load16_lds(rs_y, stage + (wave_u * 4 + q) * 512, yvoff[q], 0);
   };
   // the weight tile of the step load_y_lds was last called with
-  auto load_w_lds = [&](int st, uint16_t* stage) {
+  auto load_w_lds = [&](uint16_t* stage) {
+    const auto rs_w = make_rsrc(w_ptr + static_cast<size_t>(y_ls) * BK * K,
+                                w_bytes - static_cast<uint32_t>(y_ls) * BK * K * 2);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      buf_load16_lds(rs_w, stage + (wave_u * 4 + q) * 512, wvoff[q], (st - y_beg) * BK * K * 2);
+    for (int q = 0; q < 4; ++q) buf_load16_lds(rs_w, stage + (wave_u * 4 + q) * 512, wvoff[q], 0);
   };
   // weight codes: one of the 64 rows of the step, 32 columns (one half of an NF4
   // block) at one of the BT / 32 runs of the tile. Thread bits, 256 x 256 tiles:
@@ -173,17 +187,18 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
   const uint32_t cvoff = static_cast<uint32_t>(nl) * K2 + run * 16;
   const uint32_t svoff = (static_cast<uint32_t>(nl) * KB + (run >> 1)) * 4;
   // B slice: row j = tid >> 3 (+ kThreads / 8 per further load, < RU), 8 columns
-  // at chunk tid & 7; columns past d_out are zeroed here (the buffer range would
-  // only stop them at the end of B)
+  // at chunk tid & 7; columns past d_out are zeroed here (rows past r read zeros)
   constexpr int kBPer = (RU * 8 + kThreads - 1) / kThreads;
   const int bj = tid >> 3, bch = tid & 7;
   uint4 creg[2], breg[2][kBPer];
   float sreg[2];
-  // 2 + kBPer loads per thread and step (rows j >= r fall outside rs_b and read
-  // zeros), so every wave can wait on the same vmcnt.
-  auto rs_c = make_rsrc(tab.codes[0] + k0 / 2, static_cast<uint32_t>(static_cast<size_t>(N0) * K2 - k0 / 2));
-  auto rs_s = make_rsrc(tab.absmax[0] + k0 / 64, static_cast<uint32_t>((static_cast<size_t>(N0) * KB - k0 / 64) * 4));
-  auto rs_b = make_rsrc(tab.B[0], static_cast<uint32_t>(r) * N0 * 2);
+  // 2 + kBPer loads per thread and step, so every wave can wait on the same vmcnt.
+  const uint8_t* c_ptr = tab.codes[0] + k0 / 2;
+  uint32_t c_bytes = static_cast<uint32_t>(static_cast<size_t>(N0) * K2 - k0 / 2);
+  const float* s_ptr = tab.absmax[0] + k0 / 64;
+  uint32_t s_bytes = static_cast<uint32_t>((static_cast<size_t>(N0) * KB - k0 / 64) * 4);
+  const uint16_t* b_ptr = tab.B[0];
+  uint32_t b_bytes = static_cast<uint32_t>(r) * N0 * 2;
   uint32_t bvoff = static_cast<uint32_t>(bj) * N0 * 2 + bch * 16;
   int w_g = 0, w_beg = 0, w_end = tab.step_end[0], w_N = N0;
   auto load_regs = [&](int st, int slot) {
@@ -194,23 +209,26 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
         w_end = tab.step_end[w_g];
         w_N = tab.N[w_g];
         if constexpr (!DQ) {
-          rs_c = make_rsrc(tab.codes[w_g] + k0 / 2,
-                           static_cast<uint32_t>(static_cast<size_t>(w_N) * K2 - k0 / 2));
-          rs_s = make_rsrc(tab.absmax[w_g] + k0 / 64,
-                           static_cast<uint32_t>((static_cast<size_t>(w_N) * KB - k0 / 64) * 4));
+          c_ptr = tab.codes[w_g] + k0 / 2;
+          c_bytes = static_cast<uint32_t>(static_cast<size_t>(w_N) * K2 - k0 / 2);
+          s_ptr = tab.absmax[w_g] + k0 / 64;
+          s_bytes = static_cast<uint32_t>((static_cast<size_t>(w_N) * KB - k0 / 64) * 4);
         }
-        rs_b = make_rsrc(tab.B[w_g], static_cast<uint32_t>(r) * w_N * 2);
+        b_ptr = tab.B[w_g];
+        b_bytes = static_cast<uint32_t>(r) * w_N * 2;
         bvoff = static_cast<uint32_t>(bj) * w_N * 2 + bch * 16;
       }
     }
-    const int ls = st - w_beg;
+    const int ls = min(st, w_end - 1) - w_beg;
     if constexpr (!DQ) {
-      creg[slot] = buf_load16(rs_c, cvoff, ls * 64 * K2);
-      sreg[slot] = __uint_as_float(buf_load4(rs_s, svoff, ls * 64 * KB * 4));
+      const uint32_t cstep = static_cast<uint32_t>(ls) * 64 * K2, sstep = static_cast<uint32_t>(ls) * 64 * KB;
+      creg[slot] = buf_load16(make_rsrc(c_ptr + cstep, c_bytes - cstep), cvoff, 0);
+      sreg[slot] = __uint_as_float(buf_load4(make_rsrc(s_ptr + sstep, s_bytes - sstep * 4), svoff, 0));
     }
+    const auto rs_b = make_rsrc(b_ptr + ls * BK, b_bytes - ls * BK * 2);
 #pragma unroll
     for (int i = 0; i < kBPer; ++i) {
-      const uint4 v = buf_load16(rs_b, bvoff + i * (kThreads / 8) * w_N * 2, ls * BK * 2);
+      const uint4 v = buf_load16(rs_b, bvoff + i * (kThreads / 8) * w_N * 2, 0);
       breg[slot][i] = (ls * BK + bch * 8 < w_N) ? v : uint4{0u, 0u, 0u, 0u};
     }
   };
@@ -290,7 +308,7 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
 
   // prologue: step 0 into stage 0, step 1 into registers
   load_y_lds(sbeg, ys0);
-  if constexpr (DQ) load_w_lds(sbeg, ds0);
+  if constexpr (DQ) load_w_lds(ds0);
   load_regs(sbeg, 0);
   wait_vmem();
   __syncthreads();  // lut and dY of step 0 visible
@@ -322,7 +340,7 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
     uint16_t* dn = cur ? ds0 : ds1;
     uint16_t* bn = cur ? bs0 : bs1;
     load_y_lds(st + 1, yn);
-    if constexpr (DQ) load_w_lds(st + 1, dn);
+    if constexpr (DQ) load_w_lds(dn);
     load_regs(st + 2, cur);
     // DQ: keep the next stage's loads at the top of the step
     if constexpr (DQ) __builtin_amdgcn_sched_barrier(0);

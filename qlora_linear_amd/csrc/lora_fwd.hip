@@ -155,13 +155,19 @@ __global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) voi
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
     xvoff[q] = static_cast<uint32_t>(row) * K * 2 + chunk * 16;
   }
+  // Every step index passed to a load is clamped to this workgroup's last step:
+  // the run-ahead loads of the last steps (one and two past the end) then read
+  // that step again (unused) and never address past the operands.
+  const int klast = nsteps - 1;
   auto load_x_lds = [&](int kt, uint16_t* stage) {
+    kt = min(kt, klast);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       buf_load16_lds(rs_x, stage + (wave_u * 4 + q) * 512, xvoff[q], kt * BK * 2);
   };
   // DQ: weight rows have x's row stride (K), so x's lane offsets serve them
   auto load_w_lds = [&](int kt, uint16_t* stage) {
+    kt = min(kt, klast);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       buf_load16_lds(rs_w, stage + (wave_u * 4 + q) * 512, xvoff[q], kt * BK * 2);
@@ -178,13 +184,18 @@ __global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) voi
   uint4 creg[2], areg[2][kAPer > 0 ? kAPer : 1];
   float sreg[2];
   auto load_codes = [&](int kt, int slot) {
+    kt = min(kt, klast);
     creg[slot] = buf_load16(rs_c, cvoff, kt * 32);
     sreg[slot] = __uint_as_float(buf_load4(rs_s, svoff, kt * 4));
   };
+  // (chunks past the slice's 8 r read zeros: at the last step they would lie past A)
   auto load_a = [&](int kt, int slot) {
+    kt = min(kt, klast);
 #pragma unroll
-    for (int i = 0; i < kAPer; ++i)
-      areg[slot][i] = buf_load16(rs_a, (tid + kThreads * i) * 16, kt * BK * r * 2);
+    for (int i = 0; i < kAPer; ++i) {
+      const int ch = tid + kThreads * i;
+      areg[slot][i] = buf_load16(rs_a, ch < 8 * r ? ch * 16 : kOutOfRange, kt * BK * r * 2);
+    }
   };
 
   // Loop-invariant LDS element offsets. Every fragment row this lane reads has
@@ -302,14 +313,14 @@ __global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) voi
     }
     store_a(as0, areg[0]);
   }
-  if constexpr (!DQ) load_codes(1, 1);  // past the last step these loads return unused data (or zeros)
+  if constexpr (!DQ) load_codes(1, 1);  // clamped: a one-step tile loads step 0 again (unused)
   load_a(1, 1);
   __syncthreads();
 
   // One K-step. `cur` is a compile-time stage index (the loop is unrolled by two)
   // so every LDS address below is a loop-invariant register plus an immediate.
   // The step is branch-free: on the last step the next-stage work lands in the
-  // unused stage (loads past the end read zeros or unused bytes), which keeps
+  // unused stage (the clamped loads re-read the last step, unused), which keeps
   // the whole step one basic block for the scheduler. Fragments of k-slice
   // ks + 1 and the level lookups of code dword ks + 1 are issued one slice ahead
   // of their use.

@@ -121,16 +121,16 @@ __device__ __forceinline__ void rw_tile(const RwTile& t) {
 
   // token operand: wave w fills rows 32 w .. 32 w + 31 with four 1 KB direct-to-LDS
   // loads of 8 rows; lane i lands on physical chunk i & 7 of its row and loads the
-  // logical chunk that the (row >> 1) & 7 XOR swizzle maps there. Rows 16 apart
-  // share the swizzle, so two lane offsets serve all the loads (the rest is scalar).
+  // logical chunk that the (row >> 1) & 7 XOR swizzle maps there. The row is in the
+  // lane offset and only the step in the scalar offset, so rows past T lie past
+  // the descriptor's range through the lane offset alone.
   constexpr int kXR = kBT / kWaves, kXL = kXR / 8;  // rows and loads per wave
-  uint32_t xvoff[2];
+  uint32_t xvoff[kXL];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < kXL; ++q) {
     const int row = kXR * wave + 8 * q + (lane >> 3);
     xvoff[q] = static_cast<uint32_t>(row) * L * 2 + (((lane & 7) ^ ((row >> 1) & 7)) << 4);
   }
-  const uint32_t xrow16 = static_cast<uint32_t>(16) * L * 2;  // bytes of 16 rows
   // rank slice (LU), 256 bytes per wave, 4 per lane. Forward: the step's 64 rows
   // of A are 2 KB contiguous; wave w takes bytes 256 w ... dX: wave w takes rows
   // j = 2 w, 2 w + 1 of B's 64 step columns, stored [16][64] with 16-byte chunks
@@ -149,7 +149,7 @@ __device__ __forceinline__ void rw_tile(const RwTile& t) {
     const uint32_t k = static_cast<uint32_t>(min(kt, last));
 #pragma unroll
     for (int q = 0; q < kXL; ++q)
-      buf_load16_lds(rs_x, stage + (kXR * wave_u + 8 * q) * 64, xvoff[q & 1], k * 128 + (q >> 1) * xrow16);
+      buf_load16_lds(rs_x, stage + (kXR * wave_u + 8 * q) * 64, xvoff[q], k * 128);
     if constexpr (LU) buf_load4_lds(rs_l, stage + kTileElems + 128 * wave_u, lvoff, DX ? k * 128 : k * 2048);
     // the next step's absmax (its dequantization runs during this stage's step)
     if constexpr (DX) buf_load4_lds(rs_s, stage + kAOff + 128 * wave_u, avoff, static_cast<uint32_t>(min(kt + 1, last)) * 256);

@@ -59,12 +59,10 @@ __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(
   const int t_end = min(T, t_begin + t_per_split);
   const int steps = (t_end - t_begin + TT - 1) / TT;
 
-  // Rows past t_end belong to the next split: the ranges stop at t_end so they
-  // read as zeros.
-  const auto rs_m = make_rsrc(M + static_cast<size_t>(t_begin) * C,
-                              static_cast<uint32_t>(t_end - t_begin) * C * 2);
-  const auto rs_v = make_rsrc(V + static_cast<size_t>(t_begin) * vstr,
-                              static_cast<uint32_t>(t_end - t_begin - 1) * vstr * 2 + r * 2);
+  // Rows past t_end belong to the next split: each step's descriptors start at the
+  // step's first row (scalar arithmetic, scalar offset 0) and stop at t_end, so the
+  // lane offsets hold only rows within the step and rows past t_end read zeros.
+  const int nrows = t_end - t_begin;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   // M stage: each wave fills 16 rows with eight 1 KB loads (2 rows each); lane i
@@ -89,17 +87,19 @@ __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(
 #pragma unroll
   for (int p = 0; p < kVPW; ++p) {
     const int piece = wave * kVPW + p, e = piece * 512 + lane * 8;
-    vvoff[p] = piece < v_pieces ? static_cast<uint32_t>((e / r) * vstr + e % r) * 2 : 0x7FFFFFF0u;
+    vvoff[p] = piece < v_pieces ? static_cast<uint32_t>((e / r) * vstr + e % r) * 2 : kOutOfRange;
   }
   auto issue = [&](int st) {
-    const int stage = st % kStages;
+    const int stage = st % kStages, left = nrows - st * TT;  // >= 1 rows from the step on
+    const size_t row0 = static_cast<size_t>(t_begin) + st * TT;
+    const auto rs_m = make_rsrc(M + row0 * C, static_cast<uint32_t>(left) * C * 2);
+    const auto rs_v = make_rsrc(V + row0 * vstr, static_cast<uint32_t>(left - 1) * vstr * 2 + r * 2);
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      buf_load16_lds(rs_m, &ms[stage][(wave_u * 8 + q) * 512], mvoff[q], st * TT * C * 2);
+    for (int q = 0; q < 8; ++q) buf_load16_lds(rs_m, &ms[stage][(wave_u * 8 + q) * 512], mvoff[q], 0);
 #pragma unroll
     for (int p = 0; p < kVPW; ++p) {
       const int piece = wave_u * kVPW + p;
-      buf_load16_lds(rs_v, &vs[stage][piece * 512], vvoff[p], st * TT * vstr * 2);
+      buf_load16_lds(rs_v, &vs[stage][piece * 512], vvoff[p], 0);
     }
   };
 
