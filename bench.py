@@ -14,9 +14,11 @@ Prints ONE JSON line. `value` is algorithmic TFLOP/s of the whole step:
 padding, no redundant in-tile work counted). `roofline` describes the forward
 kernel (one launch per lora_nf4_fwd call, timed with HIP events on the stream it
 runs on); `cpu_baseline` times the CPU fp64 oracle on a bounded token sample of
-the same projection; `small_tokens` times forward and backward of the largest
-projection at a few tokens (the weight-streaming kernels), where the bound is
-reading the packed weight from HBM; `medium_tokens` does the same at a few hundred
+the same projection; `small_tokens` times forward and backward of the Llama-3-70B
+gate projection (8192 -> 28672, 132 MB of packed weight) at 1 and 16 tokens (the
+weight-streaming kernels, bound by reading the packed weight), back to back and
+cold (after a 1 GiB read), and `small_tokens_headline_projection` the headline
+projection at a few tokens; `medium_tokens` does the same at a few hundred
 tokens (tiled kernels on a grid of 128 x 128 tiles); `merge` times lora_nf4_merge of that
 projection (the 16-bit export, also HBM-bound); `train_step` times the AdamW step of A and B and the
 absmax double quantization; `multi_projection` times Llama-3-8B q/k/v (r = 64, one x) as one
@@ -85,6 +87,11 @@ def parse():
     ap.add_argument("--counter-pass", action="store_true",
                     help="run under rocprofv3 --pmc: one plain copy of COPY_BYTES (calibration), "
                          "then --steps fwd+bwd steps; prints nothing else")
+    ap.add_argument("--small-token-pass", action="store_true",
+                    help="run under rocprofv3 --pmc: the calibration copy, then two fwd+bwd of the "
+                         "Llama-3-70B gate projection at 1 and at 16 tokens; prints nothing else")
+    ap.add_argument("--ingest-small-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="per-kernel HBM bytes of two --small-token-pass counter runs, as markdown")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output dirs (FETCH_SIZE, WRITE_SIZE runs of "
                          "--counter-pass) into the traffic record used by the roofline")
@@ -188,6 +195,54 @@ def ingest_counters(fetch_dir: str, write_dir: str):
     print(json.dumps(rec))
 
 
+SMALL_TOKENS = (1, 16)  # token counts of the weight-bound measurement (70B gate projection)
+
+
+def gate_projection(q, torch):
+    """The Llama-3-70B gate projection's draws (x and dY at 16 tokens), NF4 weight
+    quantized on the device."""
+    w = next(x for x in synth.WORKLOADS if x.name == "llama3-70b-layer")
+    pi = next(i for i, p in enumerate(w.projections) if p.name == "gate_proj")
+    inp = synth.projection_inputs(w, pi, tokens=max(SMALL_TOKENS))
+    d = {"p": w.projections[pi]}
+    for k in ("x", "A", "B", "dY"):
+        d[k] = to_dev_bf16(inp[k])
+    d["codes"], d["absmax"] = q.nf4_quantize(to_dev_bf16(inp["W"]))
+    return w, d
+
+
+def ingest_small_counters(fetch_dir: str, write_dir: str):
+    """Mean FETCH_SIZE / WRITE_SIZE per dispatch of each kernel of the small-token
+    pass (first half of the dispatches after the calibration copy: 1 token, second
+    half: 16 tokens), scaled by the calibration copy, as a markdown table."""
+    import collections
+    out = []
+    cal = {}
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        disp = counter_dispatches(d, counter)
+        i = next(j for j, (_, n, _) in enumerate(disp) if "MulFunctor" in n)
+        cal[counter] = (COPY_BYTES / 1024) / disp[i][2]
+        rest = [x for x in disp[i + 1:] if "lnf4" in x[1]]
+        half = len(rest) // 2
+        for ti, chunk in enumerate((rest[:half], rest[half:])):
+            acc = collections.defaultdict(list)
+            for _, name, v in chunk:
+                key = name.replace("(anonymous namespace)::", "").replace("void ", "").replace("lnf4::", "")
+                key = key.split("(")[0]
+                acc[key].append(v * cal[counter] * 1024)
+            for k, v in acc.items():
+                per.setdefault((SMALL_TOKENS[ti], k), {})[counter] = sum(v) / len(v)
+    out.append("| tokens | kernel | read MB / dispatch | written MB / dispatch |")
+    out.append("|---|---|---|---|")
+    for (t, k), v in sorted(per.items()):
+        out.append(f"| {t} | `{k}` | {v.get('FETCH_SIZE', 0) / 1e6:.2f} | {v.get('WRITE_SIZE', 0) / 1e6:.2f} |")
+    out.append("")
+    out.append(f"calibration: FETCH_SIZE x {cal['FETCH_SIZE']:.3f}, WRITE_SIZE x {cal['WRITE_SIZE']:.3f} "
+               f"(a {COPY_BYTES >> 20} MiB copy)")
+    print("\n".join(out))
+
+
 def cpu_baseline(w: synth.Workload, target_s: float):
     """The oracle as it stands, fwd + bwd of the workload's first projection on a
     token sample sized to take about target_s seconds on this host."""
@@ -257,7 +312,7 @@ def host_facts() -> dict:
     return facts
 
 
-def time_fwd_bwd(lib, q, torch, d, w, tokens, sp, reps):
+def time_fwd_bwd(lib, q, torch, d, w, tokens, sp, reps, warm=5):
     """Forward and backward of one projection on the first `tokens` rows of the
     resident x and dY, back to back through the C ABI with preallocated buffers;
     HIP events on the stream bracket `reps` calls of each. Returns (T, K, N, r,
@@ -290,7 +345,7 @@ def time_fwd_bwd(lib, q, torch, d, w, tokens, sp, reps):
     stream = torch.cuda.current_stream()
     res = {}
     for name, fn in (("fwd", fwd), ("bwd", bwd)):
-        for _ in range(5):
+        for _ in range(warm):
             fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -314,6 +369,69 @@ def small_token_run(lib, q, torch, d, w, tokens, sp, reps=50):
             "fwd_weight_GBps": round(wbytes / res["fwd"] / 1e3, 1),
             "fwd_frac": round(wbytes / res["fwd"] / 1e3 / PEAK_HBM_GBS, 4),
             "bwd_weight_GBps": round(wbytes / res["bwd"] / 1e3, 1)}
+
+
+def small_token_cold(lib, q, torch, d, w, tokens, sp, reps=15):
+    """The same calls one at a time after a 1 GiB read (four times the memory-side
+    cache, read rather than written so that no dirty lines are written back during
+    the call), HIP events around each call; medians."""
+    T = min(tokens, w.tokens)
+    p = d["p"]
+    K, N, r = p.d_in, p.d_out, w.r
+    x, dy = d["x"][:T], d["dY"][:T]
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    u = torch.empty((T, r), dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty((K, r), dtype=torch.bfloat16, device="cuda")
+    dB = torch.empty((r, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(q.lora_nf4_bwd_workspace_bytes(T, K, N, r), 256), dtype=torch.uint8, device="cuda")
+    fws = torch.empty(max(q.lora_nf4_fwd_workspace_bytes(T, K, N, r), 256), dtype=torch.uint8, device="cuda")
+    scrub = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        return lib.lora_nf4_fwd(T, K, N, r, w.alpha, x.data_ptr(), d["codes"].data_ptr(), d["absmax"].data_ptr(),
+                                d["A"].data_ptr(), d["B"].data_ptr(), y.data_ptr(), u.data_ptr(),
+                                fws.data_ptr(), fws.numel(), sp)
+
+    def bwd():
+        return lib.lora_nf4_bwd(T, K, N, r, w.alpha, x.data_ptr(), dy.data_ptr(), d["codes"].data_ptr(),
+                                d["absmax"].data_ptr(), d["A"].data_ptr(), d["B"].data_ptr(), u.data_ptr(),
+                                dx.data_ptr(), dA.data_ptr(), dB.data_ptr(), ws.data_ptr(), ws.numel(), sp)
+    res = {}
+    for name, fn in (("fwd", fwd), ("bwd", bwd)):
+        ts = []
+        for _ in range(reps):
+            scrub.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st = fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if st != 0:
+                raise q.LoraNF4Error("lora_nf4_" + name, st)
+            ts.append(e0.elapsed_time(e1) * 1000.0)
+        res[name] = pct(ts, 50)
+    del scrub
+    return res["fwd"], res["bwd"]
+
+
+def weight_bound_legs(lib, q, torch, d, w, sp, tokens=(1, 16)):
+    """The Llama-3-70B gate projection (8192 -> 28672, 132 MB of packed weight) at a
+    few tokens: forward and backward back to back (warm: the weight may stay in the
+    256 MB memory-side cache) and one call at a time after a cache scrub (cold),
+    as weight GB/s against the 8 TB/s HBM peak."""
+    out = []
+    for T in tokens:
+        leg = small_token_run(lib, q, torch, d, w, T, sp)
+        f_c, b_c = small_token_cold(lib, q, torch, d, w, T, sp)
+        wb = leg["weight_bytes"]
+        leg.update({"cold_fwd_us": round(f_c, 2), "cold_bwd_us": round(b_c, 2),
+                    "cold_fwd_weight_GBps": round(wb / f_c / 1e3, 1),
+                    "cold_fwd_frac": round(wb / f_c / 1e3 / PEAK_HBM_GBS, 4),
+                    "cold_bwd_weight_GBps": round(wb / b_c / 1e3, 1)})
+        out.append(leg)
+    return out
 
 
 def medium_token_run(lib, q, torch, d, w, tokens, sp, reps=50):
@@ -855,12 +973,14 @@ def step_stats(per_step):
             "p90": round(pct(per_step, 90), 4)}
 
 
-def config_leg(lib, q, torch, name, steps, warmup):
+def config_leg(lib, q, torch, name, steps, warmup, extra=None):
     """fwd + bwd of every projection of one workload (fused where the projections
-    share x), per-step HIP events; median step time, TFLOP/s and tokens/s."""
+    share x), per-step HIP events; median step time, TFLOP/s and tokens/s. `extra`
+    (run) -> dict runs further measurements on the resident workload."""
     w = next(x for x in synth.WORKLOADS if x.name == name)
     run = Runner(lib, q, torch, w, fuse=True)
     total, per_step, fwd, bwd = timed_steps(torch, run, steps, warmup)
+    more = extra(run) if extra is not None else {}
     med = pct(per_step, 50)
     out = {"tokens": w.tokens, "r": w.r, "fwd_ms_p50_largest_unit": round(pct(fwd, 50), 4),
            "bwd_ms_p50_largest_unit": round(pct(bwd, 50), 4),
@@ -870,6 +990,7 @@ def config_leg(lib, q, torch, name, steps, warmup):
            "tflops_median_step": round(run.flops() / (med * 1e-3) / 1e12, 2),
            "tokens_per_s_median_step": round(w.tokens / (med * 1e-3), 1),
            "pct_of_bf16_peak": round(100.0 * run.flops() / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    out.update(more)
     del run
     torch.cuda.empty_cache()
     return out
@@ -906,6 +1027,9 @@ def main():
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters)
         return
+    if args.ingest_small_counters:
+        ingest_small_counters(*args.ingest_small_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus N with N > 1 is not supported "
               "(the path shards over tokens with one all-reduce of dA/dB, which is not built here).",
@@ -920,6 +1044,17 @@ def main():
     lib = q.library()
     torch.cuda.set_device(0)
     q.set_weight_staging(bool(args.staged))
+    if args.small_token_pass:
+        gw, gd = gate_projection(q, torch)
+        sp = torch.cuda.current_stream().cuda_stream
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)  # plain copy of known size: calibrates the counters
+        torch.cuda.synchronize()
+        for T in SMALL_TOKENS:
+            time_fwd_bwd(lib, q, torch, gd, gw, T, sp, 2, warm=0)
+        torch.cuda.synchronize()
+        return
     run = Runner(lib, q, torch, w, args.fuse)
     sp = run.sp
 
@@ -1020,7 +1155,8 @@ def main():
                              "scrub": "512 MiB device fill before every step (outside its events)"}
     progress("mfma probe: " + (f"{out['mfma_probe']['tflops']} TFLOP/s" if out["mfma_probe"] else "absent"))
     if args.small_tokens > 0:
-        out["small_tokens"] = small_token_run(lib, q, torch, run.projs[run.units[bu][0]], w, args.small_tokens, sp)
+        out["small_tokens_headline_projection"] = small_token_run(lib, q, torch, run.projs[run.units[bu][0]], w,
+                                                                  args.small_tokens, sp)
     if args.medium_tokens > 0:
         out["medium_tokens"] = medium_token_run(lib, q, torch, run.projs[run.units[bu][0]], w, args.medium_tokens, sp)
     out["merge"] = merge_run(lib, q, torch, run.projs[run.units[bu][0]], w, sp)
@@ -1035,8 +1171,16 @@ def main():
         out["configs"] = {}
         for name in ("llama3-8b-attn-r64", "qwen14b-attn", "llama3-70b-layer"):
             if name != w.name:
-                out["configs"][name] = config_leg(lib, q, torch, name, args.leg_steps, 3)
+                extra = None
+                if name == "llama3-70b-layer" and args.small_tokens > 0:
+                    def extra(run):
+                        gate = next(dd for dd in run.projs if dd["p"].name == "gate_proj")
+                        return {"small_tokens_gate": weight_bound_legs(lib, q, torch, gate, run.w, sp)}
+                out["configs"][name] = config_leg(lib, q, torch, name, args.leg_steps, 3, extra)
                 progress(f"{name}: median step {out['configs'][name]['step_ms']['p50']} ms")
+                if "small_tokens_gate" in out["configs"][name]:
+                    out["small_tokens"] = out["configs"][name].pop("small_tokens_gate")
+                    progress("small tokens (70B gate) done")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
         progress("cpu baseline done")

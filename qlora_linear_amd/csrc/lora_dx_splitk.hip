@@ -74,8 +74,12 @@ __global__ __launch_bounds__(kKThreads) void lora_dx_splitk_kernel(
   const bool grole = static_cast<int>(blockIdx.x) >= nmain;  // workgroup-uniform
   const int rj = (r + 15) / 16;
   const int gb = blockIdx.x - nmain;
-  const int sp = grole ? gb / rj : blockIdx.x / kcb;
-  const int kb = grole ? 0 : blockIdx.x % kcb;
+  // main workgroups: each XCD takes one contiguous range of (slice, column block)
+  // ids, so the column blocks that share 128-byte lines of codes (two) and of
+  // absmax (sixteen) run on one L2 at about the same time
+  const int mid = grole ? 0 : xcd_remap(blockIdx.x, nmain);
+  const int sp = grole ? gb / rj : mid / kcb;
+  const int kb = grole ? 0 : mid % kcb;
   const int jb = grole ? gb % rj : 0;
   const int k0 = kb * kCols;
   const int nbeg = sp * rows_per_split;

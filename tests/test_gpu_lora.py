@@ -97,12 +97,14 @@ def test_odd_shapes(q, T, K, N, r):
 # and the split-K weight-streaming dX (T <= 128). Cases cover a single half-filled
 # reduction step (d_in = 64), a half-filled last step (d_in % 128 == 64), d_out
 # not a multiple of the 16- or 64-row block, one, two, four and eight 16-token
-# blocks, one and many d_in splits, and every rank block count.
+# blocks, one and many d_in splits, every rank block count, and wide d_out (up to
+# 32776) at few tokens.
 FEW = [(1, 64, 16, 8), (1, 4096, 64, 16), (5, 192, 40, 16), (9, 64, 8, 56), (16, 256, 48, 24),
        (17, 320, 136, 64), (32, 448, 1000, 32), (32, 128, 8, 8), (16, 4096, 4096, 16),
        (32, 4096, 1024, 64), (48, 192, 72, 24), (64, 4096, 4096, 16), (100, 320, 200, 64),
        (128, 448, 1000, 32), (127, 2048, 136, 8), (1, 320, 4104, 16), (8, 192, 5000, 64),
-       (32, 2048, 4160, 40)]
+       (32, 2048, 4160, 40), (3, 1024, 28672, 16), (16, 1024, 32776, 8), (20, 1024, 20488, 32),
+       (12, 1024, 16392, 64), (7, 3072, 12296, 48), (1, 2048, 9000, 24), (25, 3072, 520, 16)]
 
 
 @pytest.mark.parametrize("T,K,N,r", FEW)
@@ -410,6 +412,28 @@ def _sample_rows(T, n=48, seed=0):
 # 8B k/o at r = 64, Qwen-14B (5120 -> 5120), and the 70B q (8192 -> 8192), k, gate
 # (8192 -> 28672) and down (28672 -> 8192) projections at 4096 tokens
 FULL = [(1, 0), (2, 1), (2, 3), (3, 0), (4, 0), (4, 1), (4, 4), (4, 6)]
+
+
+@pytest.mark.parametrize("T", [1, 16, 32])
+def test_full_size_few_tokens_70b_gate(q, T):
+    """Llama-3-70B gate (8192 -> 28672, r = 16) at 1, 16 and 32 tokens (the
+    workload's draws at that token count): the few-token forward and dX in the
+    launch configuration the benchmark's small-token leg times, every output
+    against the oracle."""
+    from tests.gpu_util import host_f64
+    w = synth.WORKLOADS[4]
+    inp = synth.projection_inputs(w, 4, tokens=T)
+    y, u, dx, dA, dB = _run_gpu(q, inp, w.alpha)
+    x, A, B, dY = (_f64(inp[k]) for k in ("x", "A", "B", "dY"))
+    D = _oracle_D(inp)
+    y_ref, U_ref = olora.forward(x, D, A, B, w.alpha, w.r)
+    dX_ref, dA_ref, dB_ref = olora.backward(x, dY, D, A, B, w.alpha, w.r)
+    errs = {"y": olora.rel_err(host_f64(y), y_ref), "u": olora.rel_err(host_f64(u), U_ref),
+            "dx": olora.rel_err(host_f64(dx), dX_ref), "dA": olora.rel_err(host_f64(dA), dA_ref),
+            "dB": olora.rel_err(host_f64(dB), dB_ref)}
+    print("70b gate", T, {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= TOL, (T, k, v)
 
 
 @pytest.mark.parametrize("wi,pi", FULL)
