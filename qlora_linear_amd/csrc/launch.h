@@ -79,10 +79,16 @@ struct UpassTable {
   const uint16_t* A[kMaxProj];
   uint16_t* u[kMaxProj];
   uint16_t* us;
+  int us_stride;  // row stride of us (elements); 0: n r
 };
 size_t upass_table_bytes(int64_t T, int64_t K, int n, int r);
 hipError_t launch_upass(int T, int K, int r, float s, const uint16_t* x, UpassTable& tab, void* workspace,
                         hipStream_t stream);
+// G = bf16(s dY B^T) of one projection (r <= 64, d_out % 256 == 0) into columns
+// 0 .. r - 1 of g [T][g_stride]: the U pass with dY for x and B (r rows along
+// d_out) for A^T.
+hipError_t launch_gpass(int T, int N, int r, float s, const uint16_t* dy, const uint16_t* B, uint16_t* g,
+                        int g_stride, hipStream_t stream);
 
 // Register-dequantizing forward (256 x 256 tiles, eight waves of 256 x 32): the
 // packed NF4 codes of a K-step go straight into MFMA B fragments in registers,
@@ -178,8 +184,10 @@ struct DxTable {
 // Several projections take this kernel when every d_out is a multiple of 64 and
 // n r <= 64 (r % 8 == 0).
 bool lora_dx_multi_supported(int n_proj, const int* N, int r);
+// g_ready: G (bf16, [T][n r]) is already in g_out (launch_gpass); the tiles then
+// read it in their epilogue instead of forming it in the K loop.
 hipError_t launch_lora_dx_table(int T, int K, int r, float s, const DxTable& tab, uint16_t* dx,
-                                uint16_t* g_out, hipStream_t stream);
+                                uint16_t* g_out, hipStream_t stream, bool g_ready = false);
 
 // Split-K weight-streaming dX for up to 128 tokens (r % 8 == 0, r <= 64):
 // workgroups of 128 d_in columns x one of `splits` d_out slices (plus one per slice

@@ -561,6 +561,17 @@ hipError_t launch_lora_bwd(int T, int K, int N, int r, float s, const uint16_t* 
 #undef LNF4_BWD
 }
 
+// The fused dX takes G from a G pass (launch_gpass) at rank > 16 from 4096 tokens,
+// when every d_out is a multiple of 256 and weights are not staged (measured on
+// MI355X, Llama-3-8B q/k/v at r = 64: the in-loop G is 25 % more MFMA work in
+// every one of the 16 column tiles of the tiled dX).
+bool dx_gpass(int64_t T, int n, const int* N, int r) {
+  if (n < 2 || r <= 16 || T < 4096 || weight_staging()) return false;
+  for (int g = 0; g < n; ++g)
+    if (N[g] % 256 != 0) return false;
+  return true;
+}
+
 BwdMultiPlan plan_bwd_multi(int64_t T, int64_t K, int n, const int* N, int r) {
   BwdMultiPlan p{};
   p.n = n;
@@ -653,7 +664,15 @@ hipError_t launch_lora_bwd_multi(int T, int K, int n, const int* N, int r, float
     }
   }
   uint16_t* G = reinterpret_cast<uint16_t*>(ws + p.off_g);
-  if ((e = launch_lora_dx_table(T, K, r, s, tab, dx, G, stream)) != hipSuccess) return e;
+  // rank > 16 from 4096 tokens (every d_out a multiple of 256): G = s dY_g B_g^T of
+  // each projection in a pass of its own over dY_g (the U pass's kernel), so the
+  // dX tiles skip the rank-wide MFMAs that every column tile would repeat
+  const bool gpass = dx_gpass(T, n, N, r);
+  if (gpass)
+    for (int g = 0; g < n; ++g)
+      if ((e = launch_gpass(T, N[g], r, s, dy[g], B[g], G + g * r, n * r, stream)) != hipSuccess) return e;
+  if ((dx != nullptr || !gpass) && (e = launch_lora_dx_table(T, K, r, s, tab, dx, G, stream, gpass)) != hipSuccess)
+    return e;
   const uint16_t* uu[kMaxProj];
   for (int g = 0; g < n; ++g) {
     uu[g] = u_saved == nullptr ? nullptr : u_saved[g];

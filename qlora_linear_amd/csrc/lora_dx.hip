@@ -63,6 +63,8 @@ struct DxTile {
   static constexpr int kMinBlocks = BT == 128 ? 2 : 1;
 };
 
+// RU = 0 (several projections): G is already in g_out (the G pass); the K loop
+// forms dY deq(W) alone and the epilogue reads G back.
 // Split mode (part_x != nullptr, one projection): workgroup b runs tile b % tiles
 // over d_out steps [steps_per (b / tiles), ...) and writes fp32 partial dX to
 // part_x [split][T][K] and, from the first column tile, fp32 partial dY B^T to
@@ -80,8 +82,8 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
   __shared__ __align__(16) uint16_t ys1[kTileElems];
   __shared__ __align__(16) uint16_t ds0[kDElems];
   __shared__ __align__(16) uint16_t ds1[kDElems];
-  __shared__ __align__(16) uint16_t bs0[RU * kBStride];
-  __shared__ __align__(16) uint16_t bs1[RU * kBStride];
+  __shared__ __align__(16) uint16_t bs0[(RU > 0 ? RU : 1) * kBStride];
+  __shared__ __align__(16) uint16_t bs1[(RU > 0 ? RU : 1) * kBStride];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Tl::kWN, wn = wave % Tl::kWN;  // 2 x kWN waves, BT / 2 x 64 each
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
   // at chunk tid & 7; columns past d_out are zeroed here (rows past r read zeros)
   constexpr int kBPer = (RU * 8 + kThreads - 1) / kThreads;
   const int bj = tid >> 3, bch = tid & 7;
-  uint4 creg[2], breg[2][kBPer];
+  uint4 creg[2], breg[2][kBPer > 0 ? kBPer : 1];
   float sreg[2];
   // 2 + kBPer loads per thread and step, so every wave can wait on the same vmcnt.
   const uint8_t* c_ptr = tab.codes[0] + k0 / 2;
@@ -525,7 +527,7 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
       *reinterpret_cast<uint4*>(at + ep(c, jc - c0)) = v;
     }
   };
-  if constexpr (MULTI) {
+  if constexpr (MULTI || RU == 0) {  // G from g_out (stored at projection ends, or precomputed)
     if (dx == nullptr) return;
     __threadfence_block();  // this tile's G stores, before other waves read them back
     // n r may exceed RE: the rank columns are added RE at a time
@@ -603,8 +605,12 @@ hipError_t launch_dx_t(int T, int K, int r, float s, const DxTable& tab, uint16_
 
 template <int BT>
 hipError_t launch_dx_rank(int T, int K, int r, float s, const DxTable& tab, uint16_t* dx, uint16_t* g_out,
-                          const DxSplitArgs& a, hipStream_t stream) {
+                          const DxSplitArgs& a, hipStream_t stream, bool g_ready = false) {
   const int R = tab.n * r;
+  // several projections with G already in g_out: no G in the K loop (RU = 0)
+  if (g_ready && tab.n > 1 && a.part_x == nullptr)
+    return launch_dx_t<BT, 0, 64, true>(T, K, r, s, tab, dx, g_out, a, stream);
+  if (g_ready) return hipErrorInvalidValue;
   if (tab.n == 1) {
     switch ((r + 15) / 16) {
       case 1: return launch_dx_t<BT, 16, 16, false>(T, K, r, s, tab, dx, g_out, a, stream);
@@ -658,10 +664,10 @@ bool lora_dx_multi_supported(int n_proj, const int* N, int r) {
 }
 
 hipError_t launch_lora_dx_table(int T, int K, int r, float s, const DxTable& tab, uint16_t* dx,
-                                uint16_t* g_out, hipStream_t stream) {
+                                uint16_t* g_out, hipStream_t stream, bool g_ready) {
   const DxSplitArgs a{1, tab.step_end[tab.n - 1], nullptr, nullptr};
-  if (dx_tile_edge(T, K, r) == 256) return launch_dx_rank<256>(T, K, r, s, tab, dx, g_out, a, stream);
-  return launch_dx_rank<128>(T, K, r, s, tab, dx, g_out, a, stream);
+  if (dx_tile_edge(T, K, r) == 256) return launch_dx_rank<256>(T, K, r, s, tab, dx, g_out, a, stream, g_ready);
+  return launch_dx_rank<128>(T, K, r, s, tab, dx, g_out, a, stream, g_ready);
 }
 
 // d_out splits of the tiled dX of one projection: the rule of the tiled forward's

@@ -714,18 +714,18 @@ size_t dq_bytes(int64_t T, int64_t K, int64_t N, int r) {
 // each tile dequantizes its 256 x 64 block of a step once, into MFMA fragments.
 // At rank 16 the kernel computes U = x A itself (no workspace). Otherwise U comes
 // from the U pass (lora_upass.hip; A^T and bf16(s U) in the workspace): one pass
-// over x for all projections when their ranks sum to at most 64, else one per
+// over x for all projections when their ranks sum to at most 256, else one per
 // projection.
 bool fwd_rw(int64_t T, int64_t K, int bt, int r) { return !weight_staging() && bt == 256 && fwd_rw_supported(T, K, r); }
 size_t rw_bytes(int64_t T, int64_t K, int n, int r) {
   if (fwd_rw_inloop_u(r)) return 0;
-  return n * r <= 64 ? upass_table_bytes(T, K, n, r) : n * upass_table_bytes(T, K, 1, r);
+  return n * r <= 256 ? upass_table_bytes(T, K, n, r) : n * upass_table_bytes(T, K, 1, r);
 }
 hipError_t launch_rw_with_upass(int T, int K, int r, float s, const uint16_t* x, ProjTable& tab, void* workspace,
                                 hipStream_t stream) {
   if (fwd_rw_inloop_u(r)) return launch_fwd_rw(T, K, r, s, x, tab, stream);
   unsigned char* w = static_cast<unsigned char*>(workspace);
-  const int groups = tab.n * r <= 64 ? 1 : tab.n;  // U passes
+  const int groups = tab.n * r <= 256 ? 1 : tab.n;  // U passes
   const int per = tab.n / groups;                   // projections per pass
   for (int p = 0; p < groups; ++p) {
     UpassTable ut{};

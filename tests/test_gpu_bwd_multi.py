@@ -6,7 +6,7 @@ Cases cover the fused path (every d_out a multiple of 64, T > 128: one dX
 launch over the concatenated d_out; for n r <= 64 one pass over x for every dA,
 wider sums in several epilogue passes and one dA pass per projection) with 2, 3
 and 4 projections and ranks 8 .. 64, ragged token counts and partial d_in
-tiles, from 1024 tokens on weights dequantized into the workspace; and the
+tiles, G from a pass of its own (rank > 16, from 4096 tokens), from 1024 tokens on weights dequantized into the workspace; and the
 per-projection path (a d_out not a multiple of 64, up to 128 tokens,
 no dX). One case runs the Qwen-14B-shaped q/k/v at full size
 (8192 tokens, 5120 -> 5120 each, r = 16) and checks sampled rows of dX and
@@ -58,6 +58,10 @@ CASES = [
     (150, 192, (64, 128), 40, True, True),          # fused, n r = 80 > 64: two epilogue passes, dA per projection
     (100, 256, (128, 64, 64), 16, True, True),      # up to 128 tokens: per projection (split-K dX)
     (260, 256, (128, 64, 64), 64, True, True),      # fused, rank 64 q/k/v-like: n r = 192
+    # from 4096 tokens at rank > 16 (d_out % 256 == 0): G from a G pass, dX tiles without it
+    (4100, 256, (256, 512, 256), 64, True, True),
+    (4096, 320, (256, 256), 24, False, True),       # U recomputed, ragged d_in tile
+    (4100, 256, (256, 256, 256), 48, True, False),  # no dX: the G pass alone feeds dA
     (200, 128, (64, 64, 64), 32, False, True),      # fused, n r = 96, U recomputed
     (300, 256, (256, 64, 64), 16, True, False),     # fused, dX not requested
     (1100, 320, (128, 64, 64), 16, True, True),     # fused, dX on the dequantized weights (128 tiles)

@@ -222,21 +222,22 @@ def check_skinny(chk, T, C, r, vstr, splits):
                 chk("skinny V", ((T - 1) * vstr + r) * 2, row0 * vstr * 2, ((left - 1) * vstr + r) * 2, vvoff, 0, 16)
 
 
-# ---- U pass (lora_upass.hip): 32 token rows, stages of 256 columns -------------------
-def check_upass(chk, T, K, R, AR):
+# ---- U pass (lora_upass.hip): 32 token rows, stages of SC columns ------------------
+def check_upass(chk, T, K, R, AR, SC):
     tid, lane, wave = lanes(256)
-    nst = K // 256
-    xvo = np.concatenate([(2 * (4 * wave + q) + (lane >> 5)) * K * 2
-                          + (((lane & 31) ^ ((2 * (4 * wave + q) + (lane >> 5)) & 15)) << 4) for q in range(4)])
-    kaw = AR // 4
-    avo = np.concatenate([(kaw * wave + 2 * q + (lane >> 5)) * K * 2
-                          + (((lane & 31) ^ ((kaw * wave + 2 * q + (lane >> 5)) & 15)) << 4)
-                          for q in range(AR // 8)])
+    nst = K // SC
+    rpl, cpr = 1024 // (2 * SC), SC // 8
+    kxl, kal, kaw = 32 // rpl // 4, AR // rpl // 4, AR // 4
+
+    def voff(row):
+        return row * K * 2 + (((lane % cpr) ^ (row & 15)) << 4)
+    xvo = np.concatenate([voff(rpl * (kxl * wave + q) + lane // cpr) for q in range(kxl)])
+    avo = np.concatenate([voff(kaw * wave + rpl * q + lane // cpr) for q in range(kal)])
     for tm in boundary(-(-T // 32)):
         m0 = tm * 32
         rows = min(T - m0, 32)
         for i in range(nst + 3):
-            soff = min(i, nst - 1) * 512
+            soff = min(i, nst - 1) * SC * 2
             chk("upass x", T * K * 2, m0 * K * 2, rows * K * 2, xvo, soff, 16)
             chk("upass A^T", R * K * 2, 0, R * K * 2, avo, soff, 16)
 
@@ -289,10 +290,13 @@ def test_skinny_loads(T, C, r, vstr, splits):
     assert chk.loads > 0
 
 
-@pytest.mark.parametrize("T,K,R,AR", [(1000, 4096, 48, 64), (33, 256, 16, 16), (8192, 512, 64, 64), (70, 768, 24, 32)])
-def test_upass_loads(T, K, R, AR):
+@pytest.mark.parametrize("T,K,R,AR,SC", [(1000, 4096, 48, 64, 256), (33, 256, 16, 16, 256), (8192, 512, 64, 64, 256),
+                                          (70, 768, 24, 32, 256), (1000, 4096, 192, 192, 128),
+                                          (33, 256, 96, 128, 128), (4100, 1024, 256, 256, 128),
+                                          (70, 768, 144, 192, 128)])
+def test_upass_loads(T, K, R, AR, SC):
     chk = Checker()
-    check_upass(chk, T, K, R, AR)
+    check_upass(chk, T, K, R, AR, SC)
     assert chk.loads > 0
 
 
