@@ -160,7 +160,7 @@ DxTiledSplit dx_tiled_split(int64_t T, int64_t K, int64_t N, int r);
 hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* dy,
                           const uint8_t* codes, const float* absmax, const uint16_t* A,
                           const uint16_t* B, const uint16_t* wdq, uint16_t* dx, uint16_t* g_out, float* part_x,
-                          float* part_g, hipStream_t stream);
+                          float* part_g, hipStream_t stream, bool g_ready = false);
 // Whether the tiled dX takes a weight dequantized beforehand (large token counts).
 bool dx_dq(int64_t T, int64_t K, int64_t N, int r);
 
@@ -270,6 +270,8 @@ struct DaOut {
   int gw;
 };
 bool lora_skinny_supported(int r);
+// the rank-r gradient kernel for a side-by-side G of several projections (dA only)
+bool lora_skinny_wide_supported(int r);
 int skinny_splits(int64_t T, int64_t K, int64_t N);
 hipError_t launch_lora_skinny(int T, int K, int N, int ra, int rb, int vsa, float s, const uint16_t* x,
                               const uint16_t* g, const uint16_t* dy, const uint16_t* u,
@@ -290,6 +292,7 @@ struct BwdPlan {
   bool dqx;                             // tiled dX on the dequantized weight (dx_dq)
   bool rwx;                             // dX on register-dequantized tiles (dx_rw_supported)
   size_t off_w;                         // dqx: that weight, bf16 [N][K]; rwx: the transposed packed weight
+  bool gpass;                           // G from a G pass (launch_gpass), the tiles at RU = 0
   size_t bytes;       // total workspace bytes
 };
 // allow_dq = false: never the dequantized-weight dX (its workspace holds 2 d_in d_out

@@ -390,9 +390,17 @@ hipError_t launch_bwd_rt(int T, int K, int N, int r, float s, const uint16_t* x,
     const bool split = p.splits_x > 1;
     uint16_t* w = p.dqx ? reinterpret_cast<uint16_t*>(ws + p.off_w) : nullptr;
     if (p.dqx && (e = launch_nf4_dequantize(codes, absmax, N, K, true, w, stream)) != hipSuccess) return e;
-    e = launch_lora_dx(T, K, N, r, s, dy, codes, absmax, A, B, w, dx, g,
-                       split ? reinterpret_cast<float*>(ws + p.off_px) : nullptr,
-                       split ? reinterpret_cast<float*>(ws + p.off_pg) : nullptr, stream);
+    if (p.gpass) {
+      // G = s dY B^T in a pass of its own; the dX tiles (if any) read it back
+      if ((e = launch_gpass(T, N, r, s, dy, B, g, r, stream)) != hipSuccess) return e;
+      e = dx == nullptr ? hipSuccess
+                        : launch_lora_dx(T, K, N, r, s, dy, codes, absmax, A, B, w, dx, g, nullptr, nullptr,
+                                         stream, true);
+    } else {
+      e = launch_lora_dx(T, K, N, r, s, dy, codes, absmax, A, B, w, dx, g,
+                         split ? reinterpret_cast<float*>(ws + p.off_px) : nullptr,
+                         split ? reinterpret_cast<float*>(ws + p.off_pg) : nullptr, stream);
+    }
   } else {
     constexpr int BM = 128, BN = 128;
     const int tiles = ((T + BM - 1) / BM) * ((K + BN - 1) / BN);
@@ -532,6 +540,8 @@ BwdPlan plan_bwd(int64_t T, int64_t K, int64_t N, int r, bool allow_dq) {
       p.off_w = off;
       off = align256(off + static_cast<size_t>(N) * K * 2);
     }
+    // rank > 16 from 4096 tokens, unsplit, packed weight: G from a G pass
+    p.gpass = p.splits_x <= 1 && !p.rwx && !p.dqx && r > 16 && T >= 4096 && N % 256 == 0;
   }
   p.bytes = off;
   return p;
@@ -588,15 +598,17 @@ BwdMultiPlan plan_bwd_multi(int64_t T, int64_t K, int n, const int* N, int r) {
     p.off_u = off;
     off = align256(off + static_cast<size_t>(n) * T * r * 2);
     // n r <= 64: one pass over x for every dA (rank n r) with the first dB, then
-    // one pass per further dB; wider: one pass per projection for its dA and dB
-    // (G read as a column slice of the side-by-side array)
+    // one pass per further dB; n r <= 192: one pass over x for every dA alone, then
+    // one pass per dB; wider: one pass per projection for its dA and dB (G read as a
+    // column slice of the side-by-side array)
     const bool one_pass = lora_skinny_supported(p.R);
-    p.splits_a = skinny_splits(T, K, N[0]);
-    size_t pa = static_cast<size_t>(p.splits_a) * K * (one_pass ? p.R : r) * 4;
-    size_t pb = static_cast<size_t>(p.splits_a) * N[0] * r * 4;
-    for (int g = 1; g < n; ++g) {
-      p.splits_b[g] = skinny_splits(T, one_pass ? 0 : K, N[g]);
-      if (!one_pass) pa = std::max(pa, static_cast<size_t>(p.splits_b[g]) * K * r * 4);
+    const bool wide = !one_pass && lora_skinny_wide_supported(p.R);
+    p.splits_a = skinny_splits(T, K, wide ? 0 : N[0]);
+    size_t pa = static_cast<size_t>(p.splits_a) * K * (one_pass || wide ? p.R : r) * 4;
+    size_t pb = wide ? 0 : static_cast<size_t>(p.splits_a) * N[0] * r * 4;
+    for (int g = wide ? 0 : 1; g < n; ++g) {
+      p.splits_b[g] = skinny_splits(T, one_pass || wide ? 0 : K, N[g]);
+      if (!one_pass && !wide) pa = std::max(pa, static_cast<size_t>(p.splits_b[g]) * K * r * 4);
       pb = std::max(pb, static_cast<size_t>(p.splits_b[g]) * N[g] * r * 4);
     }
     p.off_pa = off;
@@ -692,6 +704,16 @@ hipError_t launch_lora_bwd_multi(int T, int K, int n, const int* N, int r, float
     e = launch_lora_skinny(T, K, N[0], p.R, r, p.R, s, x, G, dy[0], uu[0], pa, pb, p.splits_a, da, dB[0],
                            stream);
     for (int g = 1; g < n && e == hipSuccess; ++g)
+      e = launch_lora_skinny(T, 0, N[g], p.R, r, p.R, s, x, G, dy[g], uu[g], pa, pb, p.splits_b[g], da, dB[g],
+                             stream);
+    return e;
+  }
+  if (lora_skinny_wide_supported(p.R)) {
+    for (int g = 0; g < n; ++g) da.p[g] = dA[g];
+    // n r up to 192: dA of every projection from one pass over x on its own (the wide
+    // rank kernel), then one dB pass per projection
+    e = launch_lora_skinny(T, K, 0, p.R, r, p.R, s, x, G, dy[0], uu[0], pa, pb, p.splits_a, da, nullptr, stream);
+    for (int g = 0; g < n && e == hipSuccess; ++g)
       e = launch_lora_skinny(T, 0, N[g], p.R, r, p.R, s, x, G, dy[g], uu[g], pa, pb, p.splits_b[g], da, dB[g],
                              stream);
     return e;

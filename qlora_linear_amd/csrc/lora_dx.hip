@@ -63,8 +63,8 @@ struct DxTile {
   static constexpr int kMinBlocks = BT == 128 ? 2 : 1;
 };
 
-// RU = 0 (several projections): G is already in g_out (the G pass); the K loop
-// forms dY deq(W) alone and the epilogue reads G back.
+// RU = 0: G is already in g_out (the G pass); the K loop forms dY deq(W) alone and
+// the epilogue reads G back.
 // Split mode (part_x != nullptr, one projection): workgroup b runs tile b % tiles
 // over d_out steps [steps_per (b / tiles), ...) and writes fp32 partial dX to
 // part_x [split][T][K] and, from the first column tile, fp32 partial dY B^T to
@@ -607,10 +607,14 @@ template <int BT>
 hipError_t launch_dx_rank(int T, int K, int r, float s, const DxTable& tab, uint16_t* dx, uint16_t* g_out,
                           const DxSplitArgs& a, hipStream_t stream, bool g_ready = false) {
   const int R = tab.n * r;
-  // several projections with G already in g_out: no G in the K loop (RU = 0)
-  if (g_ready && tab.n > 1 && a.part_x == nullptr)
-    return launch_dx_t<BT, 0, 64, true>(T, K, r, s, tab, dx, g_out, a, stream);
-  if (g_ready) return hipErrorInvalidValue;
+  // G already in g_out: no G in the K loop (RU = 0)
+  if (g_ready) {
+    if (a.part_x != nullptr || r <= 16) return hipErrorInvalidValue;
+    if (tab.n > 1) return launch_dx_t<BT, 0, 64, true>(T, K, r, s, tab, dx, g_out, a, stream);
+    if (r <= 32) return launch_dx_t<BT, 0, 32, false>(T, K, r, s, tab, dx, g_out, a, stream);
+    if (r <= 48) return launch_dx_t<BT, 0, 48, false>(T, K, r, s, tab, dx, g_out, a, stream);
+    return launch_dx_t<BT, 0, 64, false>(T, K, r, s, tab, dx, g_out, a, stream);
+  }
   if (tab.n == 1) {
     switch ((r + 15) / 16) {
       case 1: return launch_dx_t<BT, 16, 16, false>(T, K, r, s, tab, dx, g_out, a, stream);
@@ -705,7 +709,7 @@ bool dx_dq(int64_t T, int64_t K, int64_t N, int r) {
 hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* dy,
                           const uint8_t* codes, const float* absmax, const uint16_t* A,
                           const uint16_t* B, const uint16_t* wdq, uint16_t* dx, uint16_t* g_out, float* part_x,
-                          float* part_g, hipStream_t stream) {
+                          float* part_g, hipStream_t stream, bool g_ready) {
   DxTable tab{};
   tab.n = 1;
   tab.step_end[0] = (N + BK - 1) / BK;
@@ -717,7 +721,8 @@ hipError_t launch_lora_dx(int T, int K, int N, int r, float s, const uint16_t* d
   tab.B[0] = B;
   tab.wdq[0] = wdq;
   const DxTiledSplit sp = part_x != nullptr ? dx_tiled_split(T, K, N, r) : DxTiledSplit{1, tab.step_end[0]};
-  if (sp.splits <= 1) return launch_lora_dx_table(T, K, r, s, tab, dx, g_out, stream);
+  if (sp.splits <= 1) return launch_lora_dx_table(T, K, r, s, tab, dx, g_out, stream, g_ready);
+  if (g_ready) return hipErrorInvalidValue;
   const DxSplitArgs a{sp.splits, sp.steps_per, part_x, part_g};
   const hipError_t e = dx_tile_edge(T, K, r) == 256 ? launch_dx_rank<256>(T, K, r, s, tab, dx, g_out, a, stream)
                                                     : launch_dx_rank<128>(T, K, r, s, tab, dx, g_out, a, stream);

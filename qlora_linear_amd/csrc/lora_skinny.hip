@@ -14,6 +14,8 @@
 // token-contiguous fragments the MFMA wants without transposed stores.
 // A second kernel sums the partials in split order (deterministic), applies the
 // scale and stores bf16 in each gradient's layout.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -39,8 +41,9 @@ __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(
     float* __restrict__ part_a, float* __restrict__ part_b) {
   // V stages hold [64][r] bf16 contiguous (64 r * 2 bytes); fragment reads of the
   // padding ranks j >= r may run up to 64 bytes past a stage. Four stages fit the
-  // 160 KB LDS for r <= 32, three for r <= 64.
-  constexpr int kStages = RU <= 32 ? 4 : 3;
+  // 160 KB LDS for r <= 32, three for r <= 128, two above (the side-by-side G of
+  // several projections, up to 192 ranks).
+  constexpr int kStages = RU <= 32 ? 4 : (RU <= 128 ? 3 : 2);
   __shared__ __align__(16) uint16_t ms[kStages][kMElems];
   __shared__ __align__(16) uint16_t vs[kStages][TT * RU + 64];
 
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(
     }
   };
 
-  static_assert(kStages == 3 || kStages == 4, "wait counts below assume 3 or 4 stages");
+  static_assert(kStages >= 2 && kStages <= 4, "wait counts below assume 2 to 4 stages");
   // fragment addresses (transposing reads; 16-lane group g16, lane m16)
   const int g16 = lane >> 4, m16 = lane & 15;
   // A operand = V^T: rows j (M dim), reduction t. Lane m16 points at token row
@@ -251,6 +254,7 @@ __global__ __launch_bounds__(256) void skinny_reduce2_adamw_kernel(const float* 
 }  // namespace
 
 bool lora_skinny_supported(int r) { return r % 8 == 0 && r <= 64; }
+bool lora_skinny_wide_supported(int r) { return r % 8 == 0 && r <= 192; }
 
 // Token splits: about one workgroup per CU in total, each split a whole number
 // of 64-token steps.
@@ -273,12 +277,21 @@ hipError_t launch_lora_skinny(int T, int K, int N, int ra, int rb, int vsa, floa
   per = ((per + TT - 1) / TT) * TT;
   const int cb_a = (K + BC - 1) / BC, cb_b = (N + BC - 1) / BC;
   const dim3 grid(cb_a + cb_b, splits);
-  if ((K > 0 ? ra : 0) <= 32 && (N > 0 ? rb : 0) <= 32)
+  const int rmax = std::max(K > 0 ? ra : 0, N > 0 ? rb : 0);
+  if (rmax <= 32)
     skinny_partial_kernel<32><<<grid, kThreads, 0, stream>>>(T, K, N, ra, rb, vsa, cb_a, per, x, g, dy, u,
                                                              part_a, part_b);
-  else
+  else if (rmax <= 64)
     skinny_partial_kernel<64><<<grid, kThreads, 0, stream>>>(T, K, N, ra, rb, vsa, cb_a, per, x, g, dy, u,
                                                              part_a, part_b);
+  else if (rmax <= 128)
+    skinny_partial_kernel<128><<<grid, kThreads, 0, stream>>>(T, K, N, ra, rb, vsa, cb_a, per, x, g, dy, u,
+                                                              part_a, part_b);
+  else if (rmax <= 192)
+    skinny_partial_kernel<192><<<grid, kThreads, 0, stream>>>(T, K, N, ra, rb, vsa, cb_a, per, x, g, dy, u,
+                                                              part_a, part_b);
+  else
+    return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t total = static_cast<int64_t>(K) * ra + static_cast<int64_t>(N) * rb;

@@ -223,6 +223,23 @@ def test_dx_register_dequant(q, T, K, N, r):
     assert dx3 is None and torch.equal(dA3, r1[3]) and torch.equal(dB3, r1[4])
 
 
+# From 4096 tokens at rank > 16 with d_out a multiple of 256 (and dX not split over
+# d_out), G = s dY B^T comes from a pass of its own over dY and the dX tiles run
+# without G in their K loop, reading it back in the epilogue: ranks 24, 40 and 64,
+# ragged T and d_in; the full oracle on every output, and the dX-less call (the G
+# pass alone) giving the same dA and dB bits.
+GPASS = [(4100, 320, 512, 24), (4096, 768, 256, 64), (8200, 256, 1024, 40)]
+
+
+@pytest.mark.parametrize("T,K,N,r", GPASS)
+def test_dx_with_g_pass(q, T, K, N, r):
+    inp = synth.custom_inputs(18, T, K, N, r, dy_std=0.1)
+    _check_full(q, inp, 16.0, r, f"gpass T={T} K={K} N={N} r={r}")
+    r1 = _run_gpu(q, inp, 16.0)
+    _, _, dx3, dA3, dB3 = _run_gpu(q, inp, 16.0, need_dx=False)
+    assert dx3 is None and torch.equal(dA3, r1[3]) and torch.equal(dB3, r1[4])
+
+
 # With weight staging on, from 4096 tokens on 256 x 256 dX tiles (1024 on 128 x 128
 # tiles) the dX kernel runs on the weight dequantized once into the workspace; by
 # default the same shapes run the in-loop kernels (or, at rank 16 on whole tiles,

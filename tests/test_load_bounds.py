@@ -190,7 +190,7 @@ def check_dx_tiled(chk, T, K, Ns, r, BT, dq, steps_per=None):
 # ---- small-token weight-gradient kernel (lora_skinny.hip) ----------------------------
 def check_skinny(chk, T, C, r, vstr, splits):
     TT, BC = 64, 256
-    RU = 32 if r <= 32 else 64
+    RU = next(ru for ru in (32, 64, 128, 192) if r <= ru)
     tid, lane, wave = lanes(256)
     per = -(-T // splits)
     per = -(-per // TT) * TT
@@ -283,7 +283,8 @@ def test_dx_tiled_loads(BT, T, K, Ns, r):
 
 
 @pytest.mark.parametrize("T,C,r,vstr,splits", [(1, 4096, 16, 16, 1), (100, 4104, 16, 48, 2),
-                                               (1000, 520, 64, 64, 7), (64, 256, 8, 24, 1), (4000, 4096, 32, 96, 16)])
+                                               (1000, 520, 64, 64, 7), (64, 256, 8, 24, 1), (4000, 4096, 32, 96, 16),
+                                               (8200, 4096, 192, 192, 13), (300, 768, 96, 96, 3)])
 def test_skinny_loads(T, C, r, vstr, splits):
     chk = Checker()
     check_skinny(chk, T, C, r, vstr, splits)
