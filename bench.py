@@ -595,11 +595,12 @@ def lora_bwd_adamw_available(q, r, N):
     return r % 8 == 0 and r <= 64 and N % 8 == 0
 
 
-def multi_projection_run(lib, q, torch, sp, reps=10):
+def multi_projection_run(lib, q, torch, sp, reps=10, rounds=5):
     """Llama-3-8B q/k/v (4096 -> 4096, 1024, 1024) at 8192 tokens, r = 64, sharing one
     x: one fwd + bwd of the three projections as lora_nf4_fwd_multi + lora_nf4_bwd_multi
     (dX summed over them) against three lora_nf4_fwd + three lora_nf4_bwd calls (three
-    separate dX, not summed). HIP events around `reps` back-to-back steps each."""
+    separate dX, not summed). HIP events around blocks of `reps` back-to-back steps,
+    `rounds` blocks per side, alternating."""
     w = next(x for x in synth.WORKLOADS if x.name == "llama3-8b-attn-r64")
     T, r = w.tokens, w.r
     ins = [synth.projection_inputs(w, g, tensors=("W", "A", "B", "dY") if g else ("x", "W", "A", "B", "dY"))
@@ -657,19 +658,28 @@ def multi_projection_run(lib, q, torch, sp, reps=10):
     out = {"workload": "llama3-8b-attn-r64 q_proj + k_proj + v_proj (one x)", "tokens": T, "r": r}
     stream = torch.cuda.current_stream()
     flops = sum(synth.flops(T, K, N, r) for N in Ns)
-    for name, fn in (("fused", fused), ("separate", separate)):
+    for fn in (fused, separate):
         for _ in range(2):
             fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+    torch.cuda.synchronize()
+    # alternating blocks of `reps` back-to-back steps, so that a change of clock
+    # during the leg reaches both sides; medians over the blocks
+    per = {"fused": [], "separate": []}
+    for _ in range(rounds):
+        for name, fn in (("fused", fused), ("separate", separate)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per[name].append(e0.elapsed_time(e1) / reps)
+    for name, v in per.items():
+        ms = pct(v, 50)
         out[f"{name}_ms"] = round(ms, 4)
         out[f"{name}_tflops"] = round(flops / (ms * 1e-3) / 1e12, 2)
+    out["fused_faster_by"] = round(1.0 - out["fused_ms"] / out["separate_ms"], 4)
+    out["blocks"] = f"{rounds} alternating blocks of {reps} steps each side, medians"
     out["note"] = "separate leaves three dX arrays unsummed; fused returns their sum"
     del x, codes, absmax, A, B, dy, ys, us, dx, dxs, dAs, dBs, wsm, wss
     return out

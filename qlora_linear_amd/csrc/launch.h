@@ -273,6 +273,26 @@ bool lora_skinny_supported(int r);
 // the rank-r gradient kernel for a side-by-side G of several projections (dA only)
 bool lora_skinny_wide_supported(int r);
 int skinny_splits(int64_t T, int64_t K, int64_t N);
+// token splits for `blocks` 256-column blocks in one launch
+int skinny_splits_blocks(int64_t T, int64_t blocks);
+
+// One job of a rank-r gradient launch: M^T V reduced over the T tokens, M [T][C]
+// (x or dY), V [T][vstr] of which the first r columns are used (G or U; r % 8 == 0,
+// r <= 192), fp32 partials [splits][r][C] at part. is_a (first job only): dA,
+// stored through the DaOut split, unscaled; otherwise out [r][C] = bf16(s sum) (dB).
+constexpr int kMaxSkinnyJobs = kMaxProj + 1;
+struct SkinnyJob {
+  const uint16_t* M;
+  const uint16_t* V;
+  float* part;
+  uint16_t* out;
+  int C, r, vstr;
+  bool is_a;
+};
+// Up to kMaxSkinnyJobs jobs in one partial-sum launch (every job's column blocks x
+// the same token splits) and one reduce: several projections' dB in one pass.
+hipError_t launch_skinny_jobs(int T, int n, const SkinnyJob* jobs, int splits, float s, const DaOut& da,
+                              hipStream_t stream, const SkinnyAdamW* adam = nullptr);
 hipError_t launch_lora_skinny(int T, int K, int N, int ra, int rb, int vsa, float s, const uint16_t* x,
                               const uint16_t* g, const uint16_t* dy, const uint16_t* u,
                               float* part_a, float* part_b, int splits, const DaOut& da,
@@ -315,8 +335,9 @@ inline bool bwd_adamw_supported(const BwdPlan& plan) { return plan.fast; }
 struct BwdMultiPlan {
   bool fused;
   int n, R;                   // projections, n r
-  int splits_a;               // fused: token splits of the first rank-r pass
-  int splits_b[kMaxProj];     // fused: token splits of the passes of projections 1 ..
+  int splits_a;               // fused: token splits of the launch with every dA
+  int splits_b[kMaxProj];     // fused: [0] of the launch with every dB (n r <= 192), else
+                              // [g] of projection g's own launch (g >= 1)
   size_t off_g, off_u, off_pa, off_pb;  // fused
   bool dq;                              // fused: dX on the dequantized weights (dx_dq)
   size_t off_w[kMaxProj];               // those weights, bf16 [N_g][K]

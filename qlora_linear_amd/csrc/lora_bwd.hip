@@ -597,19 +597,36 @@ BwdMultiPlan plan_bwd_multi(int64_t T, int64_t K, int n, const int* N, int r) {
     off = align256(off + static_cast<size_t>(T) * p.R * 2);
     p.off_u = off;
     off = align256(off + static_cast<size_t>(n) * T * r * 2);
-    // n r <= 64: one pass over x for every dA (rank n r) with the first dB, then
-    // one pass per further dB; n r <= 192: one pass over x for every dA alone, then
-    // one pass per dB; wider: one pass per projection for its dA and dB (G read as a
-    // column slice of the side-by-side array)
+    // n r <= 64: one launch for every dA (one pass over x, rank n r) and every dB;
+    // n r <= 192: one launch for every dA (the wide-rank kernel), one for every dB;
+    // wider: one launch per projection for its dA and dB (G read as a column slice
+    // of the side-by-side array). dB partials of the projections lie side by side.
     const bool one_pass = lora_skinny_supported(p.R);
     const bool wide = !one_pass && lora_skinny_wide_supported(p.R);
-    p.splits_a = skinny_splits(T, K, wide ? 0 : N[0]);
-    size_t pa = static_cast<size_t>(p.splits_a) * K * (one_pass || wide ? p.R : r) * 4;
-    size_t pb = wide ? 0 : static_cast<size_t>(p.splits_a) * N[0] * r * 4;
-    for (int g = wide ? 0 : 1; g < n; ++g) {
-      p.splits_b[g] = skinny_splits(T, one_pass || wide ? 0 : K, N[g]);
-      if (!one_pass && !wide) pa = std::max(pa, static_cast<size_t>(p.splits_b[g]) * K * r * 4);
-      pb = std::max(pb, static_cast<size_t>(p.splits_b[g]) * N[g] * r * 4);
+    const auto blocks = [](int64_t c) { return (c + 255) / 256; };
+    int64_t nb = 0, nsum = 0;
+    for (int g = 0; g < n; ++g) {
+      nb += blocks(N[g]);
+      nsum += N[g];
+    }
+    size_t pa = 0, pb = 0;
+    if (one_pass) {
+      p.splits_a = p.splits_b[0] = skinny_splits_blocks(T, blocks(K) + nb);
+      pa = static_cast<size_t>(p.splits_a) * K * p.R * 4;
+      pb = static_cast<size_t>(p.splits_a) * nsum * r * 4;
+    } else if (wide) {
+      p.splits_a = skinny_splits(T, K, 0);
+      p.splits_b[0] = skinny_splits_blocks(T, nb);
+      pa = static_cast<size_t>(p.splits_a) * K * p.R * 4;
+      pb = static_cast<size_t>(p.splits_b[0]) * nsum * r * 4;
+    } else {
+      for (int g = 0; g < n; ++g) {
+        const int sp = skinny_splits(T, K, N[g]);
+        if (g == 0) p.splits_a = sp;
+        else p.splits_b[g] = sp;
+        pa = std::max(pa, static_cast<size_t>(sp) * K * r * 4);
+        pb = std::max(pb, static_cast<size_t>(sp) * N[g] * r * 4);
+      }
     }
     p.off_pa = off;
     off = align256(off + pa);
@@ -698,25 +715,26 @@ hipError_t launch_lora_bwd_multi(int T, int K, int n, const int* N, int r, float
   float* pb = reinterpret_cast<float*>(ws + p.off_pb);
   DaOut da{};
   da.gw = r;
-  if (lora_skinny_supported(p.R)) {
+  const bool one_pass = lora_skinny_supported(p.R);
+  if (one_pass || lora_skinny_wide_supported(p.R)) {
     for (int g = 0; g < n; ++g) da.p[g] = dA[g];
-    // dA of every projection from one pass over x (G side by side), with dB of the first
-    e = launch_lora_skinny(T, K, N[0], p.R, r, p.R, s, x, G, dy[0], uu[0], pa, pb, p.splits_a, da, dB[0],
-                           stream);
-    for (int g = 1; g < n && e == hipSuccess; ++g)
-      e = launch_lora_skinny(T, 0, N[g], p.R, r, p.R, s, x, G, dy[g], uu[g], pa, pb, p.splits_b[g], da, dB[g],
-                             stream);
-    return e;
-  }
-  if (lora_skinny_wide_supported(p.R)) {
-    for (int g = 0; g < n; ++g) da.p[g] = dA[g];
-    // n r up to 192: dA of every projection from one pass over x on its own (the wide
-    // rank kernel), then one dB pass per projection
-    e = launch_lora_skinny(T, K, 0, p.R, r, p.R, s, x, G, dy[0], uu[0], pa, pb, p.splits_a, da, nullptr, stream);
-    for (int g = 0; g < n && e == hipSuccess; ++g)
-      e = launch_lora_skinny(T, 0, N[g], p.R, r, p.R, s, x, G, dy[g], uu[g], pa, pb, p.splits_b[g], da, dB[g],
-                             stream);
-    return e;
+    // dA of every projection from one pass over x (G side by side); n r <= 64: in the
+    // same launch as every dB, else (the wide-rank kernel) alone, then every dB in one
+    // launch (each projection's partials at its own offset)
+    SkinnyJob jobs[kMaxSkinnyJobs];
+    int nj = 0;
+    jobs[nj++] = SkinnyJob{x, G, pa, nullptr, K, p.R, p.R, true};
+    if (!one_pass) {
+      if ((e = launch_skinny_jobs(T, 1, jobs, p.splits_a, s, da, stream)) != hipSuccess) return e;
+      nj = 0;
+    }
+    float* pbg = pb;
+    const int sb = one_pass ? p.splits_a : p.splits_b[0];
+    for (int g = 0; g < n; ++g) {
+      jobs[nj++] = SkinnyJob{dy[g], uu[g], pbg, dB[g], N[g], r, r, false};
+      pbg += static_cast<size_t>(sb) * r * N[g];
+    }
+    return launch_skinny_jobs(T, nj, jobs, sb, s, da, stream);
   }
   for (int g = 0; g < n && e == hipSuccess; ++g) {  // one pass per projection, G column slice g
     da.p[0] = dA[g];

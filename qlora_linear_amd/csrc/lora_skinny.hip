@@ -34,11 +34,19 @@ __device__ __forceinline__ int m_off(int t, int c) {
   return t * BC + ((((c >> 4) ^ (2 * (t & 3)))) << 4) + (c & 15);
 }
 
+// Jobs of one launch: job i reduces M_i^T V_i over the tokens, workgroups
+// cb_end[i - 1] .. cb_end[i] - 1 (x the token splits) taking its 256-column blocks.
+struct SkinnyTab {
+  int n;
+  int cb_end[kMaxSkinnyJobs];
+  const uint16_t* M[kMaxSkinnyJobs];  // [T][C] (x or dY)
+  const uint16_t* V[kMaxSkinnyJobs];  // [T][vstr], r columns used (G or U)
+  float* part[kMaxSkinnyJobs];        // [splits][r][C] fp32
+  int C[kMaxSkinnyJobs], r[kMaxSkinnyJobs], vstr[kMaxSkinnyJobs];
+};
+
 template <int RU>
-__global__ __launch_bounds__(kThreads) void skinny_partial_kernel(
-    int T, int K, int N, int ra, int rb, int vsa, int cb_a, int t_per_split, const uint16_t* __restrict__ x,
-    const uint16_t* __restrict__ g, const uint16_t* __restrict__ dy, const uint16_t* __restrict__ u,
-    float* __restrict__ part_a, float* __restrict__ part_b) {
+__global__ __launch_bounds__(kThreads) void skinny_partial_kernel(int T, int t_per_split, const SkinnyTab tab) {
   // V stages hold [64][r] bf16 contiguous (64 r * 2 bytes); fragment reads of the
   // padding ranks j >= r may run up to 64 bytes past a stage. Four stages fit the
   // 160 KB LDS for r <= 32, three for r <= 128, two above (the side-by-side G of
@@ -48,14 +56,24 @@ __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(
   __shared__ __align__(16) uint16_t vs[kStages][TT * RU + 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool job_a = static_cast<int>(blockIdx.x) < cb_a;
-  const int cb = job_a ? blockIdx.x : blockIdx.x - cb_a;
-  const int r = job_a ? ra : rb;      // rank of this job's V (the columns used)
-  const int vstr = job_a ? vsa : rb;  // V row stride (elements): G may be a column slice
-  const int C = job_a ? K : N;
-  const uint16_t* M = job_a ? x : dy;
-  const uint16_t* V = job_a ? g : u;
-  float* part = job_a ? part_a : part_b;
+  // this workgroup's job (uniform; constant table indices, so the fields stay in
+  // scalar registers)
+  const int bid = blockIdx.x;
+  const uint16_t* M = tab.M[0];
+  const uint16_t* V = tab.V[0];
+  float* part = tab.part[0];
+  int C = tab.C[0], r = tab.r[0], vstr = tab.vstr[0], cb = bid;
+#pragma unroll
+  for (int i = 1; i < kMaxSkinnyJobs; ++i)
+    if (i < tab.n && bid >= tab.cb_end[i - 1]) {
+      M = tab.M[i];
+      V = tab.V[i];
+      part = tab.part[i];
+      C = tab.C[i];
+      r = tab.r[i];  // rank of this job's V (the columns used)
+      vstr = tab.vstr[i];  // V row stride (elements): G may be a column slice
+      cb = bid - tab.cb_end[i - 1];
+    }
   const int c0 = cb * BC;
   const int split = blockIdx.y;
   const int t_begin = split * t_per_split;
@@ -194,25 +212,44 @@ __device__ __forceinline__ float sum_splits(const float* __restrict__ p, int spl
   return sum;
 }
 
-// dA[c][j] = sum_split part_a[split][j][c], columns j split into projections of
-// da.gw ranks (dA_g[c][j - g gw]);  dB[j][c] = s sum_split part_b[split][j][c]
-__global__ __launch_bounds__(256) void skinny_reduce2_kernel(const float* __restrict__ part_a,
-                                                             const float* __restrict__ part_b,
-                                                             int splits, int K, int N, int ra, int rb,
-                                                             float s, const DaOut da,
-                                                             uint16_t* __restrict__ dB) {
+// Sums of the jobs' partials in split order, elements el_end[i - 1] .. el_end[i] - 1
+// for job i ([r][C] of it). Job 0 may be dA (first_a): column j of its sum goes to
+// projection j / da.gw, dA_g[c][j - g gw], unscaled; every other job stores
+// out[j][c] = bf16(s sum) (dB).
+struct SkinnyRed {
+  int n, first_a;
+  int64_t el_end[kMaxSkinnyJobs];
+  const float* part[kMaxSkinnyJobs];
+  int C[kMaxSkinnyJobs], r[kMaxSkinnyJobs];
+  uint16_t* out[kMaxSkinnyJobs];
+};
+
+__global__ __launch_bounds__(256) void skinny_reduce2_kernel(const SkinnyRed red, int64_t total, int splits,
+                                                             float s, const DaOut da) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t na = static_cast<int64_t>(K) * ra;
-  if (idx < na) {
-    const int j = static_cast<int>(idx / K), c = static_cast<int>(idx - static_cast<int64_t>(j) * K);
-    const float sum = sum_splits(part_a + static_cast<size_t>(j) * K + c, splits, static_cast<size_t>(ra) * K);
+  if (idx >= total) return;
+  const float* part = red.part[0];
+  int C = red.C[0], r = red.r[0];
+  uint16_t* out = red.out[0];
+  int64_t li = idx;
+  bool is_a = red.first_a != 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSkinnyJobs; ++i)
+    if (i < red.n && idx >= red.el_end[i - 1]) {
+      part = red.part[i];
+      C = red.C[i];
+      r = red.r[i];
+      out = red.out[i];
+      li = idx - red.el_end[i - 1];
+      is_a = false;
+    }
+  const int j = static_cast<int>(li / C), c = static_cast<int>(li - static_cast<int64_t>(j) * C);
+  const float sum = sum_splits(part + static_cast<size_t>(j) * C + c, splits, static_cast<size_t>(r) * C);
+  if (is_a) {
     const int g = j / da.gw, jj = j - g * da.gw;
     da.p[g][static_cast<size_t>(c) * da.gw + jj] = to_bf16(sum);
-  } else if (idx < na + static_cast<int64_t>(N) * rb) {
-    const int64_t i2 = idx - na;
-    const int j = static_cast<int>(i2 / N), c = static_cast<int>(i2 - static_cast<int64_t>(j) * N);
-    const float sum = sum_splits(part_b + static_cast<size_t>(j) * N + c, splits, static_cast<size_t>(rb) * N);
-    dB[static_cast<size_t>(j) * N + c] = to_bf16(s * sum);
+  } else {
+    out[static_cast<size_t>(j) * C + c] = to_bf16(s * sum);
   }
 }
 
@@ -256,54 +293,93 @@ __global__ __launch_bounds__(256) void skinny_reduce2_adamw_kernel(const float* 
 bool lora_skinny_supported(int r) { return r % 8 == 0 && r <= 64; }
 bool lora_skinny_wide_supported(int r) { return r % 8 == 0 && r <= 192; }
 
-// Token splits: about one workgroup per CU in total, each split a whole number
-// of 64-token steps.
+// Token splits, each a whole number of 64-token steps. The partial-sum kernel holds
+// one workgroup per CU (its LDS stages), so a grid of blocks x splits workgroups
+// takes ceil(blocks splits / 256) rounds, each of `per` tokens plus about three
+// steps' worth of fixed cost (pipeline fill, partial-sum stores): the split count
+// minimizes that (ties: fewer splits, fewer partials to reduce). A grid just past
+// 256 workgroups would otherwise run a second round for a few of them.
 int skinny_splits(int64_t T, int64_t K, int64_t N) {
-  const int64_t blocks = (K + BC - 1) / BC + (N + BC - 1) / BC;
-  int64_t want = (256 + blocks - 1) / blocks;
-  const int64_t max_splits = (T + TT - 1) / TT;
-  if (want > max_splits) want = max_splits;
-  if (want < 1) want = 1;
-  int64_t per = (T + want - 1) / want;
+  return skinny_splits_blocks(T, (K + BC - 1) / BC + (N + BC - 1) / BC);
+}
+
+int skinny_splits_blocks(int64_t T, int64_t blocks) {
+  if (blocks < 1) blocks = 1;
+  const int64_t max_splits = std::min<int64_t>(std::max<int64_t>((T + TT - 1) / TT, 1), 256);
+  int64_t best = 1, best_cost = -1;
+  for (int64_t want = 1; want <= max_splits; ++want) {
+    const int64_t per = ((std::max<int64_t>((T + want - 1) / want, 1) + TT - 1) / TT) * TT;
+    const int64_t sp = std::max<int64_t>((T + per - 1) / per, 1);
+    const int64_t cost = ((blocks * sp + 255) / 256) * (per + 3 * TT);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = sp;
+    }
+  }
+  return static_cast<int>(best);
+}
+
+hipError_t launch_skinny_jobs(int T, int n, const SkinnyJob* jobs, int splits, float s, const DaOut& da,
+                              hipStream_t stream, const SkinnyAdamW* adam) {
+  if (n < 1 || n > kMaxSkinnyJobs || splits < 1) return hipErrorInvalidValue;
+  int per = (T + splits - 1) / splits;
   per = ((per + TT - 1) / TT) * TT;
-  return static_cast<int>((T + per - 1) / per);
+  SkinnyTab tab{};
+  SkinnyRed red{};
+  tab.n = red.n = n;
+  red.first_a = jobs[0].is_a ? 1 : 0;
+  int cbs = 0, rmax = 0;
+  int64_t els = 0;
+  for (int i = 0; i < n; ++i) {
+    const SkinnyJob& j = jobs[i];
+    if (j.C < 1 || j.r < 1 || j.r % 8 != 0 || j.vstr < j.r || (i > 0 && j.is_a)) return hipErrorInvalidValue;
+    cbs += (j.C + BC - 1) / BC;
+    els += static_cast<int64_t>(j.r) * j.C;
+    tab.cb_end[i] = cbs;
+    tab.M[i] = j.M;
+    tab.V[i] = j.V;
+    tab.part[i] = j.part;
+    tab.C[i] = red.C[i] = j.C;
+    tab.r[i] = red.r[i] = j.r;
+    tab.vstr[i] = j.vstr;
+    red.el_end[i] = els;
+    red.part[i] = j.part;
+    red.out[i] = j.out;
+    rmax = std::max(rmax, j.r);
+  }
+  const dim3 grid(cbs, splits);
+  if (rmax <= 32)
+    skinny_partial_kernel<32><<<grid, kThreads, 0, stream>>>(T, per, tab);
+  else if (rmax <= 64)
+    skinny_partial_kernel<64><<<grid, kThreads, 0, stream>>>(T, per, tab);
+  else if (rmax <= 128)
+    skinny_partial_kernel<128><<<grid, kThreads, 0, stream>>>(T, per, tab);
+  else if (rmax <= 192)
+    skinny_partial_kernel<192><<<grid, kThreads, 0, stream>>>(T, per, tab);
+  else
+    return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (adam != nullptr) {  // one projection: dA (job 0) and dB (job 1) of one rank
+    if (n != 2 || !jobs[0].is_a || jobs[0].r != jobs[1].r) return hipErrorInvalidValue;
+    skinny_reduce2_adamw_kernel<<<static_cast<unsigned>((els + 255) / 256), 256, 0, stream>>>(
+        jobs[0].part, jobs[1].part, splits, jobs[0].C, jobs[1].C, jobs[0].r, s, adam->a, adam->b, adam->h);
+    return hipGetLastError();
+  }
+  skinny_reduce2_kernel<<<static_cast<unsigned>((els + 255) / 256), 256, 0, stream>>>(red, els, splits, s, da);
+  return hipGetLastError();
 }
 
 hipError_t launch_lora_skinny(int T, int K, int N, int ra, int rb, int vsa, float s, const uint16_t* x,
                               const uint16_t* g, const uint16_t* dy, const uint16_t* u,
                               float* part_a, float* part_b, int splits, const DaOut& da,
                               uint16_t* dB, hipStream_t stream, const SkinnyAdamW* adam) {
-  int per = (T + splits - 1) / splits;
-  per = ((per + TT - 1) / TT) * TT;
-  const int cb_a = (K + BC - 1) / BC, cb_b = (N + BC - 1) / BC;
-  const dim3 grid(cb_a + cb_b, splits);
-  const int rmax = std::max(K > 0 ? ra : 0, N > 0 ? rb : 0);
-  if (rmax <= 32)
-    skinny_partial_kernel<32><<<grid, kThreads, 0, stream>>>(T, K, N, ra, rb, vsa, cb_a, per, x, g, dy, u,
-                                                             part_a, part_b);
-  else if (rmax <= 64)
-    skinny_partial_kernel<64><<<grid, kThreads, 0, stream>>>(T, K, N, ra, rb, vsa, cb_a, per, x, g, dy, u,
-                                                             part_a, part_b);
-  else if (rmax <= 128)
-    skinny_partial_kernel<128><<<grid, kThreads, 0, stream>>>(T, K, N, ra, rb, vsa, cb_a, per, x, g, dy, u,
-                                                              part_a, part_b);
-  else if (rmax <= 192)
-    skinny_partial_kernel<192><<<grid, kThreads, 0, stream>>>(T, K, N, ra, rb, vsa, cb_a, per, x, g, dy, u,
-                                                              part_a, part_b);
-  else
-    return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t total = static_cast<int64_t>(K) * ra + static_cast<int64_t>(N) * rb;
-  if (adam != nullptr) {
-    if (ra != rb) return hipErrorInvalidValue;
-    skinny_reduce2_adamw_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(
-        part_a, part_b, splits, K, N, ra, s, adam->a, adam->b, adam->h);
-    return hipGetLastError();
-  }
-  skinny_reduce2_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(
-      part_a, part_b, splits, K, N, ra, rb, s, da, dB);
-  return hipGetLastError();
+  SkinnyJob jobs[2];
+  int n = 0;
+  if (K > 0) jobs[n++] = SkinnyJob{x, g, part_a, nullptr, K, ra, vsa, true};
+  if (N > 0) jobs[n++] = SkinnyJob{dy, u, part_b, dB, N, rb, rb, false};
+  if (n == 0) return hipSuccess;
+  return launch_skinny_jobs(T, n, jobs, splits, s, da, stream, adam);
 }
 
 }  // namespace lnf4
