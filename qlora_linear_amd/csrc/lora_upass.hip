@@ -68,8 +68,15 @@ __global__ __launch_bounds__(kThreads) void lora_upass_kernel(int T, int K, int 
   constexpr int kAW = AR / 4;
 #pragma unroll
   for (int q = 0; q < kAL; ++q) avo[q] = voff(kAW * wave + kRPL * q + lane / kCPR);
+  // workgroup m starts at 256-column block m % (K / 256) and wraps around: the
+  // workgroups in flight then read different columns of x and A^T (all starting at
+  // column 0, their 8 KB-strided rows met in the same memory channels: 30 % slower
+  // at 8192 x 4096, r = 64). The per-wave column order still depends only on K.
+  const int rot = (static_cast<int>(blockIdx.x) % (K / 256)) * (256 / SC);
   auto load_stage = [&](int i, int slot) {
-    const uint32_t soff = static_cast<uint32_t>(min(i, nst - 1)) * SC * 2;  // clamped: past the end, reload the last
+    int g = min(i, nst - 1) + rot;  // clamped: past the end, reload the last
+    if (g >= nst) g -= nst;
+    const uint32_t soff = static_cast<uint32_t>(g) * SC * 2;
     uint16_t* dst = ring + slot * kStage;
 #pragma unroll
     for (int q = 0; q < kXL; ++q) buf_load16_lds(rs_x, dst + kRPL * (kXL * wave_u + q) * SC, xvo[q], soff);

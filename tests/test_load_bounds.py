@@ -223,11 +223,12 @@ def check_skinny(chk, T, C, r, vstr, splits):
 
 
 # ---- U pass (lora_upass.hip): 32 token rows, stages of SC columns ------------------
-def check_upass(chk, T, K, R, AR, SC):
+def check_upass(chk, T, K, R, AR, NS, SC):
     tid, lane, wave = lanes(256)
     nst = K // SC
     rpl, cpr = 1024 // (2 * SC), SC // 8
     kxl, kal, kaw = 32 // rpl // 4, AR // rpl // 4, AR // 4
+    assert kxl >= 1 and kal >= 1
 
     def voff(row):
         return row * K * 2 + (((lane % cpr) ^ (row & 15)) << 4)
@@ -236,8 +237,9 @@ def check_upass(chk, T, K, R, AR, SC):
     for tm in boundary(-(-T // 32)):
         m0 = tm * 32
         rows = min(T - m0, 32)
-        for i in range(nst + 3):
-            soff = min(i, nst - 1) * SC * 2
+        rot = (tm % (K // 256)) * (256 // SC)  # workgroup tm starts at 256-column block tm % (K / 256)
+        for i in range(nst + NS - 1):  # the ring's run-ahead issues up to step nst + NS - 2
+            soff = ((min(i, nst - 1) + rot) % nst) * SC * 2
             chk("upass x", T * K * 2, m0 * K * 2, rows * K * 2, xvo, soff, 16)
             chk("upass A^T", R * K * 2, 0, R * K * 2, avo, soff, 16)
 
@@ -291,13 +293,13 @@ def test_skinny_loads(T, C, r, vstr, splits):
     assert chk.loads > 0
 
 
-@pytest.mark.parametrize("T,K,R,AR,SC", [(1000, 4096, 48, 64, 256), (33, 256, 16, 16, 256), (8192, 512, 64, 64, 256),
-                                          (70, 768, 24, 32, 256), (1000, 4096, 192, 192, 128),
-                                          (33, 256, 96, 128, 128), (4100, 1024, 256, 256, 128),
-                                          (70, 768, 144, 192, 128)])
-def test_upass_loads(T, K, R, AR, SC):
+@pytest.mark.parametrize("T,K,R,AR,NS,SC", [(1000, 4096, 48, 64, 3, 256), (33, 256, 16, 16, 4, 256),
+                                             (8192, 512, 64, 64, 3, 256), (70, 768, 24, 32, 4, 256),
+                                             (1000, 4096, 192, 192, 2, 128), (33, 256, 96, 128, 2, 128),
+                                             (4100, 1024, 256, 256, 2, 128), (70, 768, 144, 192, 2, 128)])
+def test_upass_loads(T, K, R, AR, NS, SC):
     chk = Checker()
-    check_upass(chk, T, K, R, AR, SC)
+    check_upass(chk, T, K, R, AR, NS, SC)
     assert chk.loads > 0
 
 
