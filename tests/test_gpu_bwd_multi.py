@@ -3,9 +3,10 @@ oracle: dX summed over the projections, dA and dB of each, within the linear's
 tolerance (max|err| / max|ref| <= 1e-2).
 
 Cases cover the fused path (every d_out a multiple of 64, T > 128: one dX
-launch over the concatenated d_out; for n r <= 64 one pass over x for every dA,
-wider sums in several epilogue passes and one dA pass per projection) with 2, 3
-and 4 projections and ranks 8 .. 64, ragged token counts and partial d_in
+launch over the concatenated d_out; for n r <= 64 one rank-r launch for every
+dA and dB, up to 192 one for every dA and one for every dB, wider sums one per
+projection; n r > 64 in several epilogue passes) with 2, 3,
+4 and 8 projections and ranks 8 .. 64, ragged token counts and partial d_in
 tiles, G from a pass of its own (rank > 16, from 4096 tokens), from 1024 tokens on weights dequantized into the workspace; and the
 per-projection path (a d_out not a multiple of 64, up to 128 tokens,
 no dX). One case runs the Qwen-14B-shaped q/k/v at full size
@@ -66,6 +67,8 @@ CASES = [
     (300, 256, (256, 64, 64), 16, True, False),     # fused, dX not requested
     (1100, 320, (128, 64, 64), 16, True, True),     # fused, dX on the dequantized weights (128 tiles)
     (4100, 256, (128, 64, 64), 64, False, True),    # the same at rank 64, U recomputed
+    (300, 256, (64,) * 8, 8, True, True),           # eight projections, n r = 64: nine rank-r jobs in one launch
+    (260, 128, (64,) * 8, 16, True, True),          # eight projections, n r = 128: every dA, then every dB
 ]
 
 
