@@ -67,7 +67,9 @@ __global__ __launch_bounds__(kKThreads) void lora_fwd_splitk_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const uint16_t* __restrict__ A,
     float* __restrict__ part, float* __restrict__ upart) {
   using C = SplitCfg<TB>;
-  __shared__ __align__(1024) float lut[16];  // first in LDS: level addresses need no base
+  // level pairs of every code byte, (q[b & 15], q[b >> 4]) at 8 b: first in LDS, so
+  // a table address needs no base
+  __shared__ __align__(1024) float lut[512];
   __shared__ __align__(16) unsigned char smem[C::kBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -86,7 +88,10 @@ __global__ __launch_bounds__(kKThreads) void lora_fwd_splitk_kernel(
   const int st_begin = sp * steps_per;
   const int n_my = min(nsteps - st_begin, steps_per);  // >= 1 (the plan leaves no split empty)
 
-  if (tid < 16) lut[tid] = nf4_level(tid);
+  for (int e = tid; e < 256; e += kKThreads) {
+    lut[2 * e] = nf4_level(e & 15);
+    lut[2 * e + 1] = nf4_level(e >> 4);
+  }
 
   const int rows_w = min(N - n0, kRowsPerWg);
   const auto rs_c = make_rsrc(codes + static_cast<size_t>(n0) * K2, static_cast<uint32_t>(rows_w) * K2);
@@ -149,14 +154,15 @@ __global__ __launch_bounds__(kKThreads) void lora_fwd_splitk_kernel(
 
   const unsigned char* lutb = reinterpret_cast<const unsigned char*>(lut);
   auto dequant8 = [&](uint32_t w, float a) {
-    uint32_t ev = (w << 2) & 0x3C3C3C3Cu, od = (w >> 2) & 0x3C3C3C3Cu;
-    // keep the two planes: otherwise each address is rebuilt as shift + mask
-    asm volatile("" : "+v"(ev), "+v"(od));
+    // each code byte (the lower element in its low nibble) addresses its pair of
+    // levels: one 64-bit LDS read per two elements
     float v[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[2 * j] = *reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(ev, 8 * j, 8));
-      v[2 * j + 1] = *reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(od, 8 * j, 8));
+      const uint32_t ad = (j == 0 ? (w << 3) : (w >> (8 * j - 3))) & 0x7F8u;
+      const float2 p = *reinterpret_cast<const float2*>(lutb + ad);
+      v[2 * j] = p.x;
+      v[2 * j + 1] = p.y;
     }
     uint4 o;
     o.x = pack_bf16x2(v[0] * a, v[1] * a);

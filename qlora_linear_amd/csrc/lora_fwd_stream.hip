@@ -62,7 +62,9 @@ __global__ __launch_bounds__((StreamCfg<TB, RJ>::kSThreads)) void lora_fwd_strea
     uint16_t* __restrict__ u_save) {
   using C = StreamCfg<TB, RJ>;
   constexpr int kSWaves = C::kSWaves, kSThreads = C::kSThreads;
-  __shared__ __align__(1024) float lut[16];  // first in LDS: level addresses need no base
+  // level pairs of every code byte, (q[b & 15], q[b >> 4]) at 8 b: first in LDS, so
+  // a table address needs no base
+  __shared__ __align__(1024) float lut[512];
   __shared__ __align__(16) unsigned char smem[C::kBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -73,7 +75,10 @@ __global__ __launch_bounds__((StreamCfg<TB, RJ>::kSThreads)) void lora_fwd_strea
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int nw = nch > wave_u ? (nch - wave_u + kSWaves - 1) / kSWaves : 0;  // chunks of this wave
 
-  if (tid < 16) lut[tid] = nf4_level(tid);
+  for (int e = tid; e < 256; e += kSThreads) {
+    lut[2 * e] = nf4_level(e & 15);
+    lut[2 * e + 1] = nf4_level(e >> 4);
+  }
 
   // Buffer resources: rows past N (codes, absmax), token rows past T (x) and rows
   // past d_in (A) read as zeros.
@@ -139,14 +144,15 @@ __global__ __launch_bounds__((StreamCfg<TB, RJ>::kSThreads)) void lora_fwd_strea
 
   const unsigned char* lutb = reinterpret_cast<const unsigned char*>(lut);
   auto dequant = [&](uint32_t w, float a) {
-    uint32_t ev = (w << 2) & 0x3C3C3C3Cu, od = (w >> 2) & 0x3C3C3C3Cu;
-    // keep the two planes: otherwise each address is rebuilt as shift + mask
-    asm volatile("" : "+v"(ev), "+v"(od));
+    // each code byte (the lower element in its low nibble) addresses its pair of
+    // levels: one 64-bit LDS read per two elements
     float v[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[2 * j] = *reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(ev, 8 * j, 8));
-      v[2 * j + 1] = *reinterpret_cast<const float*>(lutb + __builtin_amdgcn_ubfe(od, 8 * j, 8));
+      const uint32_t ad = (j == 0 ? (w << 3) : (w >> (8 * j - 3))) & 0x7F8u;
+      const float2 p = *reinterpret_cast<const float2*>(lutb + ad);
+      v[2 * j] = p.x;
+      v[2 * j + 1] = p.y;
     }
     uint4 o;
     o.x = pack_bf16x2(v[0] * a, v[1] * a);
