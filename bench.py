@@ -20,7 +20,8 @@ weight-streaming kernels, bound by reading the packed weight), back to back and
 cold (after a 1 GiB read), and `small_tokens_headline_projection` the headline
 projection at a few tokens; `medium_tokens` does the same at a few hundred
 tokens (tiled kernels on a grid of 128 x 128 tiles); `merge` times lora_nf4_merge of that
-projection (the 16-bit export, also HBM-bound); `train_step` times the AdamW step of A and B and the
+projection (the 16-bit export, also HBM-bound); `rank_r_gradients` times the backward's
+rank-r step alone (lora_nf4_grad_ab, bound by reading x and dY); `train_step` times the AdamW step of A and B and the
 absmax double quantization; `multi_projection` times Llama-3-8B q/k/v (r = 64, one x) as one
 lora_nf4_fwd_multi + lora_nf4_bwd_multi against separate calls. With --fuse, projections that read the same
 activations in a transformer layer (q/k/v, gate/up) share one x, run their
@@ -474,6 +475,45 @@ def merge_run(lib, q, torch, d, w, sp, reps=20):
     nbytes = N * K // 2 + N * (K // 64) * 4 + N * K * 2
     del out
     return {"projection": f"{p.name} {K}->{N}", "r": r, "us": round(us, 2), "bytes": nbytes,
+            "bound": "hbm", "achieved": round(nbytes / us / 1e3, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
+
+
+def rank_r_run(lib, q, torch, d, w, sp, reps=50):
+    """The backward's rank-r step alone (lora_nf4_grad_ab: dA = x^T G, dB = s U^T dY)
+    on the whole projection, HIP events around `reps` back-to-back C-ABI calls; G and
+    U (bf16 [T, r]) made once with float32 torch products. Bytes = x and dY in (the
+    bound: 2 T (d_in + d_out)) + G and U in + dA and dB out."""
+    p = d["p"]
+    K, N, r, T = p.d_in, p.d_out, w.r, w.tokens
+    s = w.alpha / r
+    x, dy = d["x"], d["dY"]
+    g = (dy.float() @ d["B"].float().t() * s).bfloat16().contiguous()
+    u = (x.float() @ d["A"].float()).bfloat16().contiguous()
+    dA = torch.empty((K, r), dtype=torch.bfloat16, device="cuda")
+    dB = torch.empty((r, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(q.lora_nf4_grad_ab_workspace_bytes(T, K, N, r), 256), dtype=torch.uint8, device="cuda")
+
+    def call():
+        st = lib.lora_nf4_grad_ab(T, K, N, r, w.alpha, x.data_ptr(), g.data_ptr(), dy.data_ptr(), u.data_ptr(),
+                                  dA.data_ptr(), dB.data_ptr(), ws.data_ptr(), ws.numel(), sp)
+        if st != 0:
+            raise q.LoraNF4Error("lora_nf4_grad_ab", st)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
+    nbytes = 2 * T * (K + N) + 2 * 2 * T * r + 2 * r * (K + N)
+    del g, u, dA, dB, ws
+    return {"projection": f"{p.name} {K}->{N}", "tokens": T, "r": r, "us": round(us, 2), "bytes": nbytes,
             "bound": "hbm", "achieved": round(nbytes / us / 1e3, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
 
@@ -1170,6 +1210,7 @@ def main():
     if args.medium_tokens > 0:
         out["medium_tokens"] = medium_token_run(lib, q, torch, run.projs[run.units[bu][0]], w, args.medium_tokens, sp)
     out["merge"] = merge_run(lib, q, torch, run.projs[run.units[bu][0]], w, sp)
+    out["rank_r_gradients"] = rank_r_run(lib, q, torch, run.projs[run.units[bu][0]], w, sp)
     out["train_step"] = train_step_run(lib, q, torch, run.projs[run.units[bu][0]], w, sp)
     progress("small / medium tokens, merge, training step done")
     del run

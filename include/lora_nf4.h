@@ -201,6 +201,28 @@ int lora_nf4_bwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_a
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * lora_nf4_grad_ab — the gradients of the LoRA factors alone, from the
+ * intermediates the backward forms ("Unlocking AI potential: Unsloth's algorithms
+ * and implementation", core algorithms: the hand-written backward's dA and dB):
+ *     dA = x^T G      bf16 [d_in, r]
+ *     dB = s U^T dY   bf16 [r, d_out],  s = lora_alpha / r
+ * with G = bf16(s dY B^T) and U = bf16(x A) as the caller holds them (the
+ * backward's own rank-r step, for callers that keep G and U, and to time that
+ * step alone). Float32 sums over the T tokens in split-T partials, reduced in a
+ * fixed order (the results do not depend on the run).
+ *   x   bf16 [T, d_in]     g  bf16 [T, r]     dy  bf16 [T, d_out]     u  bf16 [T, r]
+ *   workspace  at least lora_nf4_grad_ab_workspace_bytes(T, d_in, d_out, r) bytes,
+ *            256-byte aligned, caller-owned, contents on entry irrelevant.
+ * Shape rules as for lora_nf4_fwd. T = 0: dA and dB are set to zero, the inputs and
+ * the workspace may be NULL. dA, dB and the workspace must not overlap the inputs
+ * or each other (LN_EALIAS).
+ */
+size_t lora_nf4_grad_ab_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t r);
+int lora_nf4_grad_ab(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha,
+                     const uint16_t* x, const uint16_t* g, const uint16_t* dy, const uint16_t* u,
+                     uint16_t* dA, uint16_t* dB, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * lora_nf4_bwd_multi — the backward of n_proj projections that read the same x
  * (q/k/v or gate/up, as for lora_nf4_fwd_multi): their input gradients add up,
  *     dX = sum_g ( dY[g] D_g + s (dY[g] B[g]^T) A[g]^T )

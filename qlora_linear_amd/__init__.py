@@ -33,6 +33,7 @@ __all__ = [
     "lora_adamw_step", "rslora_alpha", "nf4_absmax_quantize", "nf4_absmax_dequantize",
     "lora_nf4_bwd_multi", "lora_nf4_bwd_multi_workspace_bytes", "lora_nf4_bwd_noalloc",
     "set_weight_staging", "weight_staging", "lora_adamw8_step", "adamw8_state", "lora_nf4_bwd_adamw",
+    "lora_nf4_grad_ab", "lora_nf4_grad_ab_workspace_bytes",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -48,7 +49,7 @@ EXPORTED_SYMBOLS = ("nf4_quantize", "nf4_dequantize", "lora_nf4_fwd", "lora_nf4_
                     "lora_nf4_bwd_multi_workspace_bytes", "lora_nf4_fwd_workspace_bytes",
                     "lora_nf4_fwd_multi_workspace_bytes", "lora_nf4_bwd_noalloc",
                     "lora_nf4_set_weight_staging", "lora_nf4_mfma_probe", "lora_adamw8_step",
-                    "lora_nf4_bwd_adamw")
+                    "lora_nf4_bwd_adamw", "lora_nf4_grad_ab", "lora_nf4_grad_ab_workspace_bytes")
 
 _lib = None
 
@@ -66,6 +67,9 @@ _SIGS = {
     "lora_nf4_bwd": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_float,
                                     _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
     "lora_nf4_bwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, ctypes.c_int32]),
+    "lora_nf4_grad_ab_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, ctypes.c_int32]),
+    "lora_nf4_grad_ab": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_float,
+                                        _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
     "lora_nf4_bwd_noalloc": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_float,
                                             _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "lora_nf4_merge": (ctypes.c_int, [_i64, _i64, ctypes.c_int32, ctypes.c_float, _p, _p, _p, _p,
@@ -283,6 +287,32 @@ def lora_nf4_bwd(x, dy, codes, absmax, A, B, lora_alpha: float, u_saved=None, ne
         absmax.data_ptr(), A.data_ptr(), B.data_ptr(), _ptr(u_saved), _ptr(dx), dA.data_ptr(),
         dB.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x)))
     return dx, dA, dB
+
+
+def lora_nf4_grad_ab_workspace_bytes(T: int, K: int, N: int, r: int) -> int:
+    return int(library().lora_nf4_grad_ab_workspace_bytes(T, K, N, r))
+
+
+def lora_nf4_grad_ab(x, g, dy, u, lora_alpha: float, workspace: torch.Tensor | None = None):
+    """(dA, dB) = (x^T g, s u^T dy) from the backward's intermediates g = bf16(s dy B^T)
+    and u = bf16(x A), each [T, r]."""
+    bf = torch.bfloat16
+    _dev(x, "x", bf, 2), _dev(g, "g", bf, 2), _dev(dy, "dy", bf, 2), _dev(u, "u", bf, 2)
+    T, K = x.shape
+    N, r = dy.shape[1], g.shape[1]
+    if dy.shape[0] != T or g.shape[0] != T or u.shape != (T, r):
+        raise ValueError("x [T, d_in], g [T, r], dy [T, d_out] and u [T, r] must agree")
+    dev = x.device
+    dA = torch.empty((K, r), dtype=bf, device=dev)
+    dB = torch.empty((r, N), dtype=bf, device=dev)
+    nbytes = lora_nf4_grad_ab_workspace_bytes(T, K, N, r)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8)
+    _check("lora_nf4_grad_ab", library().lora_nf4_grad_ab(
+        T, K, N, r, float(lora_alpha), x.data_ptr(), g.data_ptr(), dy.data_ptr(), u.data_ptr(), dA.data_ptr(),
+        dB.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x)))
+    return dA, dB
 
 
 def lora_nf4_bwd_noalloc(x, dy, codes, absmax, A, B, lora_alpha: float, u_saved=None, need_dx: bool = True):

@@ -326,6 +326,40 @@ int lora_nf4_bwd(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_a
                                           static_cast<hipStream_t>(stream)));
 }
 
+size_t lora_nf4_grad_ab_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t r) {
+  if (T == 0 || check_linear_shape(T, d_in, d_out, r, 1.0f) != LN_OK) return 0;
+  return lnf4::plan_grad_ab(T, d_in, d_out, r).bytes;
+}
+
+int lora_nf4_grad_ab(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha, const uint16_t* x,
+                     const uint16_t* g, const uint16_t* dy, const uint16_t* u, uint16_t* dA, uint16_t* dB,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (dA == nullptr || dB == nullptr) return LN_EINVAL;
+  if (T != 0 && (x == nullptr || g == nullptr || dy == nullptr || u == nullptr)) return LN_EINVAL;
+  const int st = check_linear_shape(T, d_in, d_out, r, lora_alpha);
+  if (st != LN_OK) return st;
+  if (!aligned16(dA) || !aligned16(dB)) return LN_EALIGN;
+  const size_t t = T, k = d_in, n = d_out, rr = r;
+  if (T == 0) {  // empty sums
+    const Span outs[2] = {{dA, k * rr * 2}, {dB, rr * n * 2}};
+    if (any_alias(outs, 2, nullptr, 0)) return LN_EALIAS;
+    hipError_t e = lnf4::launch_zero_u16(dA, static_cast<int64_t>(k * rr), static_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = lnf4::launch_zero_u16(dB, static_cast<int64_t>(rr * n), static_cast<hipStream_t>(stream));
+    return hip_status(e);
+  }
+  if (!aligned16(x) || !aligned16(g) || !aligned16(dy) || !aligned16(u)) return LN_EALIGN;
+  const lnf4::GradPlan plan = lnf4::plan_grad_ab(T, d_in, d_out, r);
+  if (workspace == nullptr || workspace_bytes < plan.bytes) return LN_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LN_EALIGN;
+  const Span outs[3] = {{dA, k * rr * 2}, {dB, rr * n * 2}, {workspace, plan.bytes}};
+  const Span ins[4] = {{x, t * k * 2}, {g, t * rr * 2}, {dy, t * n * 2}, {u, t * rr * 2}};
+  if (any_alias(outs, 3, ins, 4)) return LN_EALIAS;
+  const float s = lora_alpha / static_cast<float>(r);
+  return hip_status(lnf4::launch_grad_ab(static_cast<int>(T), static_cast<int>(d_in), static_cast<int>(d_out), r,
+                                         s, x, g, dy, u, dA, dB, workspace, plan,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int lora_nf4_bwd_noalloc(int64_t T, int64_t d_in, int64_t d_out, int32_t r, float lora_alpha,
                          const uint16_t* x, const uint16_t* dy, const uint8_t* w_codes,
                          const float* w_absmax, const uint16_t* A, const uint16_t* B,

@@ -298,6 +298,18 @@ hipError_t launch_lora_skinny(int T, int K, int N, int ra, int rb, int vsa, floa
                               float* part_a, float* part_b, int splits, const DaOut& da,
                               uint16_t* dB, hipStream_t stream, const SkinnyAdamW* adam = nullptr);
 
+// The rank-r gradients alone (dA = x^T G, dB = s U^T dY from bf16 G [T][r] and U
+// [T][r]): partials [splits_a][K][rs] at offset 0 and [splits_b][N][rs] at off_pb.
+struct GradPlan {
+  bool fast;  // the one-launch rank-r kernel (r % 8 == 0, r <= 64)
+  int rs, splits_a, splits_b;
+  size_t off_pb, bytes;
+};
+GradPlan plan_grad_ab(int64_t T, int64_t K, int64_t N, int r);
+hipError_t launch_grad_ab(int T, int K, int N, int r, float s, const uint16_t* x, const uint16_t* g,
+                          const uint16_t* dy, const uint16_t* u, uint16_t* dA, uint16_t* dB, void* workspace,
+                          const GradPlan& p, hipStream_t stream);
+
 // Backward plan: how the workspace is carved. Shared by the launcher and the
 // workspace-size query so the two always agree.
 struct BwdPlan {

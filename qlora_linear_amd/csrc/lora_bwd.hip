@@ -571,6 +571,73 @@ hipError_t launch_lora_bwd(int T, int K, int N, int r, float s, const uint16_t* 
 #undef LNF4_BWD
 }
 
+// The rank-r gradients alone, from G and U the caller holds: the backward's own
+// rank-r step (one launch and one reduce for r % 8 == 0, r <= 64; the generic
+// split-T kernels otherwise), its partials at the start of the workspace.
+GradPlan plan_grad_ab(int64_t T, int64_t K, int64_t N, int r) {
+  GradPlan p{};
+  p.fast = lora_skinny_supported(r) && fits_buffer(T, K, N);
+  p.rs = p.fast ? r : generic_rank_tiles(r) * 16;
+  if (p.fast) {
+    p.splits_a = p.splits_b = skinny_splits(T, K, N);
+  } else {
+    p.splits_a = choose_splits(T, K);
+    p.splits_b = choose_splits(T, N);
+  }
+  p.off_pb = align256(static_cast<size_t>(p.splits_a) * K * p.rs * 4);
+  p.bytes = p.off_pb + align256(static_cast<size_t>(p.splits_b) * N * p.rs * 4);
+  return p;
+}
+
+namespace {
+template <int RT>
+hipError_t launch_grad_ab_rt(int T, int K, int N, int r, float s, const uint16_t* x, const uint16_t* g,
+                             const uint16_t* dy, const uint16_t* u, uint16_t* dA, uint16_t* dB, float* pa,
+                             float* pb, const GradPlan& p, hipStream_t stream) {
+  const int tca = (T + p.splits_a - 1) / p.splits_a;
+  const int tcb = (T + p.splits_b - 1) / p.splits_b;
+  skinny_tn_kernel<RT><<<dim3((K + 127) / 128, p.splits_a), kThreads, 0, stream>>>(T, K, r, tca, x, g, pa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  skinny_tn_kernel<RT><<<dim3((N + 127) / 128, p.splits_b), kThreads, 0, stream>>>(T, N, r, tcb, dy, u, pb);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  skinny_reduce_kernel<<<(K * r + kThreads - 1) / kThreads, kThreads, 0, stream>>>(pa, p.splits_a, K, r, RT * 16,
+                                                                                    1.0f, 0, dA);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  skinny_reduce_kernel<<<(N * r + kThreads - 1) / kThreads, kThreads, 0, stream>>>(pb, p.splits_b, N, r, RT * 16,
+                                                                                    s, 1, dB);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_grad_ab(int T, int K, int N, int r, float s, const uint16_t* x, const uint16_t* g,
+                          const uint16_t* dy, const uint16_t* u, uint16_t* dA, uint16_t* dB, void* workspace,
+                          const GradPlan& p, hipStream_t stream) {
+  float* pa = static_cast<float*>(workspace);
+  float* pb = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_pb);
+  if (p.fast) {
+    DaOut da{};
+    da.p[0] = dA;
+    da.gw = r;
+    return launch_lora_skinny(T, K, N, r, r, r, s, x, g, dy, u, pa, pb, p.splits_a, da, dB, stream);
+  }
+#define LNF4_GRAD(RT_) return launch_grad_ab_rt<RT_>(T, K, N, r, s, x, g, dy, u, dA, dB, pa, pb, p, stream)
+  switch (generic_rank_tiles(r)) {
+    case 1: LNF4_GRAD(1);
+    case 2: LNF4_GRAD(2);
+    case 3: LNF4_GRAD(3);
+    case 4: LNF4_GRAD(4);
+    case 5: LNF4_GRAD(5);
+    case 6: LNF4_GRAD(6);
+    case 7: LNF4_GRAD(7);
+    case 8: LNF4_GRAD(8);
+    case 12: LNF4_GRAD(12);
+    case 16: LNF4_GRAD(16);
+    default: return hipErrorInvalidValue;
+  }
+#undef LNF4_GRAD
+}
+
 // The fused dX takes G from a G pass (launch_gpass) at rank > 16 from 4096 tokens,
 // when every d_out is a multiple of 256 and weights are not staged (measured on
 // MI355X, Llama-3-8B q/k/v at r = 64: the in-loop G is 25 % more MFMA work in

@@ -48,7 +48,7 @@ def test_header_declares_the_boundary():
                             "lora_nf4_bwd_multi_workspace_bytes", "lora_nf4_fwd_workspace_bytes",
                             "lora_nf4_fwd_multi_workspace_bytes", "lora_nf4_bwd_noalloc",
                             "lora_nf4_set_weight_staging", "lora_nf4_mfma_probe", "lora_adamw8_step",
-                            "lora_nf4_bwd_adamw"])
+                            "lora_nf4_bwd_adamw", "lora_nf4_grad_ab", "lora_nf4_grad_ab_workspace_bytes"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -250,6 +250,38 @@ def test_bwd_validation_and_workspace(lib):
     assert call(ws_ptr=ws + 16) == LN_EALIGN                # workspace must be 256-byte aligned
     assert call(dx=x) == LN_EALIAS
     assert call(dB=dA) == LN_EALIAS
+
+
+def test_grad_ab_validation_and_workspace(lib):
+    """The rank-r gradients alone: the workspace query (0 for invalid sizes or T = 0)
+    and every argument check ahead of any HIP call."""
+    T, K, N, r = 300, 128, 72, 16
+    need = lib.lora_nf4_grad_ab_workspace_bytes(T, K, N, r)
+    assert need >= 2 * 256  # dA and dB partial sums
+    assert lib.lora_nf4_grad_ab_workspace_bytes(0, K, N, r) == 0
+    assert lib.lora_nf4_grad_ab_workspace_bytes(T, 65, N, r) == 0
+    assert lib.lora_nf4_grad_ab_workspace_bytes(T, K, N, 257) == 0
+    assert lib.lora_nf4_grad_ab_workspace_bytes(T, K, N, 12) > 0   # generic rank tiles
+    ptrs = [P + (i << 30) for i in range(8)]
+    x, g, dy, u, dA, dB, ws = ptrs[:7]
+
+    def call(ws_ptr=ws, ws_bytes=need, rank=r, t=T, **kw):
+        a = dict(x=x, g=g, dy=dy, u=u, dA=dA, dB=dB)
+        a.update(kw)
+        return lib.lora_nf4_grad_ab(t, K, N, rank, 16.0, a["x"], a["g"], a["dy"], a["u"], a["dA"], a["dB"],
+                                    ws_ptr, ctypes.c_size_t(ws_bytes), None)
+
+    assert call(dA=None) == LN_EINVAL
+    assert call(g=None) == LN_EINVAL
+    assert call(rank=0) == LN_ERANK
+    assert call(ws_ptr=None) == LN_EWORKSPACE
+    assert call(ws_bytes=need - 1) == LN_EWORKSPACE
+    assert call(ws_ptr=ws + 16) == LN_EALIGN
+    assert call(u=u + 2) == LN_EALIGN
+    assert call(dA=x) == LN_EALIAS
+    assert call(dB=dA) == LN_EALIAS
+    assert call(ws_ptr=g) == LN_EALIAS
+    assert call(t=0, dA=dA, dB=dA) == LN_EALIAS  # the empty batch still checks its outputs
 
 
 def test_bwd_accepts_rank_256_and_any_d_out(lib):
