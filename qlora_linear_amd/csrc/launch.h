@@ -73,7 +73,7 @@ struct ProjTable {
 
 // U = x A of up to LN_MAX_PROJ projections that share x, in one pass over x:
 // us [T][n r] bf16(s U) side by side (set by launch_upass inside the workspace),
-// u[g] [T][r] bf16(U_g) (nullable). n r <= 64.
+// u[g] [T][r] bf16(U_g) (nullable). n r <= 256.
 struct UpassTable {
   int n;
   const uint16_t* A[kMaxProj];
@@ -182,7 +182,7 @@ struct DxTable {
   const uint16_t* wdq[kMaxProj];
 };
 // Several projections take this kernel when every d_out is a multiple of 64 and
-// n r <= 64 (r % 8 == 0).
+// r % 8 == 0, r <= 64 (rank sums above 64 take several epilogue passes).
 bool lora_dx_multi_supported(int n_proj, const int* N, int r);
 // g_ready: G (bf16, [T][n r]) is already in g_out (launch_gpass); the tiles then
 // read it in their epilogue instead of forming it in the K loop.
@@ -341,9 +341,10 @@ inline bool bwd_adamw_supported(const BwdPlan& plan) { return plan.fast; }
 
 // Backward of several projections that share x (dX summed over them). Fused: one
 // dX launch over all projections (G side by side in [T][n r]); for n r <= 64 one
-// pass over x for every dA with the first projection's dB and one pass per further
-// dB, else one pass per projection for its dA and dB. Otherwise (ragged d_out, up
-// to 128 tokens) one backward per projection, dX accumulated from a scratch copy.
+// rank-r launch for every dA (one pass over x) and every dB, for n r <= 192 one for
+// every dA and one for every dB, else one per projection for its dA and dB.
+// Otherwise (ragged d_out, up to 128 tokens) one backward per projection, dX
+// accumulated from a scratch copy.
 struct BwdMultiPlan {
   bool fused;
   int n, R;                   // projections, n r
