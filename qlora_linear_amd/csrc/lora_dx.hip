@@ -98,7 +98,6 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
   const int NS_all = tab.step_end[tab.n - 1];  // reduction steps over all d_out
   const int sbeg = sp * steps_per;              // this workgroup's first step (0 unless split)
   const int NS = min(NS_all, sbeg + steps_per);  // one past its last step
-  constexpr bool multi = MULTI;
   const int R = tab.n * r;  // g_out row length
 
   if (tid < 16) lut[tid] = nf4_level(tid);
