@@ -32,9 +32,18 @@ FLAGS = [
 ]
 
 
+# Per-file additions. The register-dequantizing tiles are scheduled for the most
+# instruction-level parallelism (the AMDGPU backend's max-ilp strategy, an option
+# of that backend only, so the host pass ignores it): measured on MI355X at q_proj,
+# 8192 tokens, forward 283 -> 277 us, dX 0.6 % faster, the same bits.
+FILE_FLAGS = {
+    "lora_rw.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{p.stdout}\n{p.stderr}")
