@@ -49,8 +49,10 @@ METRIC = "fused NF4-LoRA linear fwd+bwd TFLOP/s & tokens/s, % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 bf16 FLOP/clk x 2.4 GHz (published: 2.5 PFLOP/s dense)
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_lora_fwd_rw_kernel_llama3-8b-q_proj.json")
+# (build.py holds the compile flags, among them the tile file's scheduling strategy)
 FWD_SOURCES = ("qlora_linear_amd/csrc/lora_rw.hip", "qlora_linear_amd/csrc/lora_fwd.hip",
-               "qlora_linear_amd/csrc/nf4_quant.hip", "qlora_linear_amd/csrc/device_common.h")
+               "qlora_linear_amd/csrc/nf4_quant.hip", "qlora_linear_amd/csrc/device_common.h",
+               "qlora_linear_amd/build.py")
 # tile kernels of the forward and of dX, and the launches that may precede them in
 # the same call (the weight dequantized to bf16 with staging on; the packed weight
 # transposed for the register-dequantizing dX)
