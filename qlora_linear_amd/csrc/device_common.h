@@ -24,6 +24,20 @@ __host__ __device__ constexpr uint32_t kNf4LevelBits[16] = {
 
 __device__ __forceinline__ float nf4_level(int c) { return __uint_as_float(kNf4LevelBits[c]); }
 
+// The same level for a per-lane code, formed in registers by a select over the 16
+// constants: the kernels fill their LDS level tables with it at the start, where a
+// read of the table from memory (and the wait for it) would come ahead of their
+// first operand loads.
+__device__ __forceinline__ float nf4_level_reg(int c) {
+  uint32_t b = kNf4LevelBits[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) {
+    b = c == i ? kNf4LevelBits[i] : b;
+    asm volatile("" : "+v"(b));  // keeps the selects (no table in memory)
+  }
+  return __uint_as_float(b);
+}
+
 // Two float32 -> packed nearest-even bf16 (v_cvt_pk_bf16_f32); `lo` lands in the
 // low half, i.e. at the lower address.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

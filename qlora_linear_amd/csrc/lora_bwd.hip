@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void lora_dx_kernel(
   const int m0 = tm * BM, k0 = tk * BN;
   const int K2 = K / 2, KB = K / kBK;
 
-  if (tid < 16) lut[tid] = nf4_level(tid);
+  if (tid < 16) lut[tid] = nf4_level_reg(tid);
 
   f32x4_t acc[C::TM][C::TN];
   f32x4_t gacc[C::TM][C::UT];

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(DxTile<BT>::kThreads, DxTile<BT>::kMinBlocks) void 
   const int NS = min(NS_all, sbeg + steps_per);  // one past its last step
   const int R = tab.n * r;  // g_out row length
 
-  if (tid < 16) lut[tid] = nf4_level(tid);
+  if (tid < 16) lut[tid] = nf4_level_reg(tid);
 
   // ---- buffer resources: out-of-range loads return zeros ------------------------
   // Every load takes a descriptor whose base is advanced to its step by scalar

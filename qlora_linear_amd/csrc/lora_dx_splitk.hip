@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kKThreads) void lora_dx_splitk_kernel(
   const int steps = (min(N, nbeg + rows_per_split) - nbeg + kNS - 1) / kNS;  // >= 1
   const int K2 = K / 2, KB = K / 64;
 
-  if (tid < 16) lut[tid] = nf4_level(tid);
+  if (tid < 16) lut[tid] = nf4_level_reg(tid);
 
   // Buffer resources over whole operands: rows past d_out (codes, absmax, B rows
   // read along d_out), token rows past T (dY) and rank rows past r (B) read as

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(FwdTile<BT>::kThreads, FwdTile<BT>::kMinBlocks) voi
   const int kbeg = sp * steps_per;                 // first K-step of this workgroup
   const int nsteps = min(KB - kbeg, steps_per);    // >= 1
 
-  if (tid < 16) lut[tid] = nf4_level(tid);
+  if (tid < 16) lut[tid] = nf4_level_reg(tid);
   // A^T slice rows r .. RU-1 stay zero in both stages
   for (int e = r * kAStride + tid; e < RU * kAStride; e += kThreads) {
     as0[e] = 0;

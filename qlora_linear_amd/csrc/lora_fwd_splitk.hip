@@ -89,8 +89,8 @@ __global__ __launch_bounds__(kKThreads) void lora_fwd_splitk_kernel(
   const int n_my = min(nsteps - st_begin, steps_per);  // >= 1 (the plan leaves no split empty)
 
   for (int e = tid; e < 256; e += kKThreads) {
-    lut[2 * e] = nf4_level(e & 15);
-    lut[2 * e + 1] = nf4_level(e >> 4);
+    lut[2 * e] = nf4_level_reg(e & 15);
+    lut[2 * e + 1] = nf4_level_reg(e >> 4);
   }
 
   const int rows_w = min(N - n0, kRowsPerWg);

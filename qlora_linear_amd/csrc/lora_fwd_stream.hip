@@ -76,8 +76,8 @@ __global__ __launch_bounds__((StreamCfg<TB, RJ>::kSThreads)) void lora_fwd_strea
   const int nw = nch > wave_u ? (nch - wave_u + kSWaves - 1) / kSWaves : 0;  // chunks of this wave
 
   for (int e = tid; e < 256; e += kSThreads) {
-    lut[2 * e] = nf4_level(e & 15);
-    lut[2 * e + 1] = nf4_level(e >> 4);
+    lut[2 * e] = nf4_level_reg(e & 15);
+    lut[2 * e + 1] = nf4_level_reg(e >> 4);
   }
 
   // Buffer resources: rows past N (codes, absmax), token rows past T (x) and rows

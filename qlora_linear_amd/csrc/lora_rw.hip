@@ -105,8 +105,8 @@ __device__ __forceinline__ void rw_tile(const RwTile& t) {
   const int L2 = L / 2, LB = L / 64, last = LB - 1;
 
   for (int e = tid; e < 256; e += kThreads) {
-    lut[2 * e] = nf4_level(e & 15);
-    lut[2 * e + 1] = nf4_level(e >> 4);
+    lut[2 * e] = nf4_level_reg(e & 15);
+    lut[2 * e + 1] = nf4_level_reg(e >> 4);
   }
 
   // ---- buffer resources: this tile's rows only; rows past T (tokens) or ncols

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void nf4_dequantize_kernel(const uint32_t* __r
                                                              const float* __restrict__ absmax,
                                                              int64_t ndw, void* __restrict__ out) {
   __shared__ float lut[16];
-  if (threadIdx.x < 16) lut[threadIdx.x] = nf4_level(threadIdx.x);
+  if (threadIdx.x < 16) lut[threadIdx.x] = nf4_level_reg(threadIdx.x);
   __syncthreads();
   for (int64_t base = static_cast<int64_t>(blockIdx.x) * 256 * kDqWords; base < ndw;
        base += static_cast<int64_t>(gridDim.x) * 256 * kDqWords) {
