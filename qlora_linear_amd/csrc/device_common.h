@@ -97,6 +97,18 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// ds_read_b64_tr_b4 (4-bit transposing LDS read). Within each group of 16 lanes,
+// lane m supplies the address of 16 consecutive 4-bit values (8 bytes, the first
+// value in the low nibble); lane j receives value (j & 15) of the chunks supplied
+// by the group's lanes 0 .. 15, the one from lane i in nibble i: a 16 x 16 nibble
+// transpose (the layout was read off an in-bounds probe on gfx950).
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 lds_read_tr4(const void* p) {
+  const i32x2_t v = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+      (__attribute__((address_space(3))) i32x2_t*)(const_cast<void*>(p)));
+  return __builtin_bit_cast(uint2, v);
+}
+
 // Eight consecutive bf16 values from global memory, of which only the first n
 // (>= 1) exist; the rest read as zero. For rows whose length is not a multiple of
 // 8 (no 16-byte alignment, and a full piece would run into the next row).

@@ -197,6 +197,7 @@ struct DxSplitPlan {
   int kcb;              // 128-column blocks of d_in
   int splits;           // d_out slices (each non-empty)
   int rows_per_split;   // multiple of 64
+  bool tr;              // the transposing-code kernel (up to 32 tokens, long slices)
   size_t part_x_bytes, part_g_bytes;
 };
 bool lora_dx_splitk_supported(int64_t T, int r);

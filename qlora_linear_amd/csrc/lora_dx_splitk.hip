@@ -5,14 +5,19 @@
 // streaming, with the reduction over d_out split across workgroups (gfx950).
 //
 //   * lora_dx_splitk_kernel: workgroup (128 d_in columns, one d_out slice), four
-//     waves of 32 columns. Per 64-row step the 64 x 128 NF4 tile is dequantized
-//     (half an NF4 block per thread, one step ahead of its use) into one of two
-//     LDS tiles in natural row-major order and read back transposed
-//     (ds_read_b64_tr_b16) as v_mfma_f32_16x16x32_bf16 B fragments: the reduction
-//     runs along the weight's rows. The waves share each step's dY chunk, staged
-//     in LDS by direct-to-LDS loads (XOR-swizzled, double-buffered); one barrier
-//     per step; codes run three steps ahead. fp32 partial sums go to a workspace
-//     [slice][T][d_in].
+//     waves of 32 columns. Each 64-row step's packed codes (64 rows x 64 bytes),
+//     the absmax of every wave's rows and the step's dY chunk go to LDS by
+//     direct-to-LDS loads, in a ring of stages three steps ahead; one barrier per
+//     step. The reduction runs along the weight's rows, so each lane takes its
+//     column's codes with a 4-bit transposing read (ds_read_b64_tr_b4: within a
+//     16-lane group, lane j receives column j of the 16 rows the group's lanes
+//     address, row e in nibble e) and dequantizes them in registers (a 256-entry
+//     table of level pairs, one per code byte, times each row's own absmax) into
+//     v_mfma_f32_16x16x32_bf16 B fragments; no dequantized tile passes through
+//     LDS. fp32 partial sums go to a workspace [slice][T][d_in]. Taken up to 32
+//     tokens when each slice is at least eight steps long; otherwise
+//     lora_dx_splitk_tile_kernel dequantizes each step's 64 x 128 tile into LDS
+//     and reads it back transposed (ds_read_b64_tr_b16).
 //     G: the grid has one more workgroup per (slice, 16-wide rank block), which
 //     stages the same dY chunks and loads rows of B straight from global memory
 //     (contiguous along d_out, as the MFMA operand needs); its wave w takes the
@@ -31,29 +36,34 @@ namespace {
 constexpr int kKThreads = 256;          // 4 waves x 32 d_in columns
 constexpr int kCols = 128;              // d_in columns per workgroup
 constexpr int kNS = 64;                 // d_out rows per step
-constexpr int kDStride = kCols + 32;    // dequantized tile row pitch, bf16 (320 bytes)
 constexpr uint32_t kOut = 0x7FFFFFF0u;  // a per-lane offset past every buffer range: reads zeros
 constexpr int kMaxSplits = 16;
 // Workgroups of lora_dx_splitk_kernel<TB> resident per CU (LDS and registers on
 // gfx950): the slice count fills one resident round.
-constexpr int kResident[3] = {3, 2, 2};  // TB = 2, 4, 8
-
-// Row n of the dequantized tile starts at n kDStride + dshift(n): the pitch is 64
-// bytes past a multiple of 256, so the four rows of one transposing read fall on
-// distinct banks, and rows four apart shift by 16 bytes per group of four, which
-// spreads the 16-byte dequantization stores of a 16-lane group over all banks
-// (and the two 16-lane groups of a transposing read over disjoint banks).
-__device__ __forceinline__ int dshift(int n) { return 8 * ((n >> 2) & 3); }
+constexpr int kResidentTr = 4;                 // lora_dx_splitk_kernel<2>
+constexpr int kResidentTile[3] = {3, 2, 2};  // lora_dx_splitk_tile_kernel<TB>, TB = 2, 4, 8
+constexpr int kTrMinSteps = 8;  // slice length from which the transposing-code kernel is taken
 
 // TB: 16-token blocks (T <= 16 TB, TB >= 2 so every wave issues the same number
-// of dY copies per step).
+// of dY copies per step). A stage: dY [16 TB][64] bf16, then (main workgroups)
+// the codes [64 rows][64 bytes] of the step, whose 16-byte chunks are XOR-swizzled
+// by (row >> 2) & 3 (a transposing read of 16 rows at one chunk then touches
+// distinct banks), then the absmax of the step's rows for each wave's block
+// [4 waves][64] floats.
 template <int TB>
 struct DxSplitCfg {
-  static constexpr int kTile = kNS * kDStride * 2;  // bytes of one dequantized tile
-  static constexpr int kYBytes = 16 * TB * kNS * 2;  // one dY stage [16 TB][64] bf16
-  static constexpr int kCopies = 2 * TB;             // 1 KB direct-to-LDS copies per stage
+  static constexpr int kYBytes = 16 * TB * kNS * 2;
+  static constexpr int kCBytes = kNS * 64;
+  static constexpr int kABytes = 4 * kNS * 4;
+  static constexpr int kStage = kYBytes + kCBytes + kABytes;
+  static constexpr int kNB = TB <= 4 ? 4 : 2;         // ring of stages
+  static constexpr int kCopies = 2 * TB;             // 1 KB dY copies per stage
   static constexpr int kPerWave = kCopies / 4;
-  static constexpr int kBytes = 2 * kTile + 2 * kYBytes;
+  static constexpr int kBytes = kNB * kStage;
+  // loads per wave and step in main workgroups: dY copies, codes, absmax; at the
+  // top of step i, stage i has landed once the later stages' loads are all that
+  // is outstanding
+  static constexpr int kMainWait = (kNB - 2) * (kPerWave + 2);
 };
 
 // Workgroups 0 .. kcb * splits - 1: (column block, slice); the next
@@ -64,6 +74,266 @@ __global__ __launch_bounds__(kKThreads) void lora_dx_splitk_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const uint16_t* __restrict__ B,
     float* __restrict__ part_x, float* __restrict__ part_g) {
   using C = DxSplitCfg<TB>;
+  // level pairs of every code byte, (q[b & 15], q[b >> 4]) at 8 b: first in LDS, so
+  // a table address needs no base
+  __shared__ __align__(1024) float lut[512];
+  __shared__ __align__(16) unsigned char smem[C::kBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int nmain = kcb * splits;
+  const bool grole = static_cast<int>(blockIdx.x) >= nmain;  // workgroup-uniform
+  const int rj = (r + 15) / 16;
+  const int gb = blockIdx.x - nmain;
+  // main workgroups: each XCD takes one contiguous range of (slice, column block)
+  // ids, so the column blocks that share 128-byte lines of codes (two) and of
+  // absmax (sixteen) run on one L2 at about the same time
+  const int mid = grole ? 0 : xcd_remap(blockIdx.x, nmain);
+  const int sp = grole ? gb / rj : mid / kcb;
+  const int kb = grole ? 0 : mid % kcb;
+  const int jb = grole ? gb % rj : 0;
+  const int k0 = kb * kCols;
+  const int nbeg = sp * rows_per_split;
+  const int steps = (min(N, nbeg + rows_per_split) - nbeg + kNS - 1) / kNS;  // >= 1
+  const int K2 = K / 2, KB = K / 64;
+
+  for (int e = tid; e < 256; e += kKThreads) {
+    lut[2 * e] = nf4_level_reg(e & 15);
+    lut[2 * e + 1] = nf4_level_reg(e >> 4);
+  }
+
+  // Buffer resources over whole operands: rows past d_out (codes, absmax, B rows
+  // read along d_out), token rows past T (dY) and rank rows past r (B) read as
+  // zeros. Columns past d_out inside a dY or B row are masked explicitly.
+  const auto rs_c = make_rsrc(codes, static_cast<uint32_t>(static_cast<size_t>(N) * K2));
+  const auto rs_s = make_rsrc(absmax, static_cast<uint32_t>(static_cast<size_t>(N) * KB * 4));
+  const auto rs_y = make_rsrc(dy, static_cast<uint32_t>(T) * N * 2);
+  const auto rs_b = make_rsrc(B, static_cast<uint32_t>(r) * N * 2);
+
+  // codes stage: wave w copies rows 16 w .. 16 w + 15 (1 KB); lane L lands on row
+  // 16 w + (L >> 2), physical chunk L & 3, and loads the logical chunk stored there.
+  // Columns past d_in (a last block of 128 with d_in % 128 == 64) read unrelated
+  // in-range bytes; those columns are never stored.
+  const int crow = 16 * wave + (lane >> 2);
+  const uint32_t cvoff = static_cast<uint32_t>(nbeg + crow) * K2 + k0 / 2 + 16 * ((lane & 3) ^ ((crow >> 2) & 3));
+  // absmax stage: wave w copies the step's 64 rows of its block (k0 + 32 w) / 64
+  const uint32_t avoff = (static_cast<uint32_t>(nbeg + lane) * KB + (k0 + 32 * wave) / 64) * 4;
+  const bool wval = k0 + 32 * wave < K;  // the wave's columns lie inside d_in
+  // transposing code read for the wave's 16-column block c: lane (l16, g) addresses
+  // row 16 g + l16, byte 16 w + 8 c of the row (logical chunk w, half c) and receives
+  // column 32 w + 16 c + l16 of rows 16 g .. 16 g + 15 (nibble e = row 16 g + e)
+  const int trow = 16 * g + l16;
+  const int c_off = trow * 64 + 16 * (wave ^ ((trow >> 2) & 3));  // + 8 c
+  // dY stage: [16 TB rows][8 pieces of 8 elements], piece p of row t stored at
+  // physical piece p ^ ((t >> 1) & 7). Copy i fills rows 8 i .. 8 i + 7 (1 KB);
+  // wave w issues copies w, w + 4, ...; lane L lands on row 8 i + (L >> 3),
+  // physical piece L & 7, and loads the logical piece stored there.
+  uint32_t yvoff[C::kPerWave];
+  int ypiece[C::kPerWave];
+#pragma unroll
+  for (int c = 0; c < C::kPerWave; ++c) {
+    const int t = 8 * (wave + 4 * c) + (lane >> 3);
+    ypiece[c] = (lane & 7) ^ ((t >> 1) & 7);
+    yvoff[c] = static_cast<uint32_t>(t) * N * 2 + 16 * ypiece[c];
+  }
+  // dY A fragment for k-slice q and token block tb: row 16 tb + l16. G workgroups:
+  // logical piece 4 q + g (d_out rows 32 q + 8 g .. +7 of the step, matching their
+  // B rows); main workgroups: piece 2 g + q (rows 16 g + 8 q .. +7, matching the
+  // transposed codes)
+  auto y_off = [&](int tb, int q) {
+    const int t = 16 * tb + l16;
+    return t * kNS + (((4 * q + g) ^ ((t >> 1) & 7)) << 3);
+  };
+  auto y_off_main = [&](int tb, int q) {
+    const int t = 16 * tb + l16;
+    return t * kNS + (((2 * g + q) ^ ((t >> 1) & 7)) << 3);
+  };
+
+  auto stage_of = [&](int i) { return smem + (i % C::kNB) * C::kStage; };
+  // one stage: the dY chunk; main workgroups also the codes and the absmax
+  auto load_stage = [&](int i) {
+    unsigned char* st = stage_of(i);
+    const int n = nbeg + i * kNS;
+#pragma unroll
+    for (int c = 0; c < C::kPerWave; ++c) {
+      const uint32_t off = n + 8 * ypiece[c] < N ? yvoff[c] + static_cast<uint32_t>(n) * 2 : kOut;
+      buf_load16_lds(rs_y, st + (wave_u + 4 * c) * 1024, off, 0);
+    }
+    if (grole) return;
+    const uint32_t row = static_cast<uint32_t>(i) * kNS;
+    buf_load16_lds(rs_c, st + C::kYBytes + wave_u * 1024, cvoff + row * K2, 0);
+    buf_load4_lds(rs_s, st + C::kYBytes + C::kCBytes + wave_u * 256, avoff + row * KB * 4, 0);
+  };
+  // G workgroups: rows 16 jb + l16 of B, d_out columns of k-slice q: 32 q + 8 g .. +7
+  uint4 breg[2][2];
+  auto load_b = [&](int i, int slot) {
+    if (!grole) return;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int n = nbeg + i * kNS + 32 * q + 8 * g;
+      const uint32_t off = n < N ? static_cast<uint32_t>(16 * jb + l16) * N * 2 + n * 2 : kOut;
+      breg[slot][q] = buf_load16(rs_b, off, 0);
+    }
+  };
+
+  // B fragment from 8 transposed codes (one dword: rows 16 g + 8 q + 2 j and + 1 in
+  // the low and high nibble of byte j) and those rows' absmax: each code byte reads
+  // its pair of levels, and every element is multiplied by its own row's absmax
+  const unsigned char* lutb = reinterpret_cast<const unsigned char*>(lut);
+  auto dequant8 = [&](uint32_t w, const float* a) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t ad = (j == 0 ? (w << 3) : (w >> (8 * j - 3))) & 0x7F8u;
+      const float2 p = *reinterpret_cast<const float2*>(lutb + ad);
+      v[2 * j] = p.x;
+      v[2 * j + 1] = p.y;
+    }
+    return uint4{pack_bf16x2(__fmul_rn(v[0], a[0]), __fmul_rn(v[1], a[1])),
+                 pack_bf16x2(__fmul_rn(v[2], a[2]), __fmul_rn(v[3], a[3])),
+                 pack_bf16x2(__fmul_rn(v[4], a[4]), __fmul_rn(v[5], a[5])),
+                 pack_bf16x2(__fmul_rn(v[6], a[6]), __fmul_rn(v[7], a[7]))};
+  };
+
+  f32x4_t acc[TB][2];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) acc[tb][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // G workgroups: token blocks wave and wave + 4 (a runtime block index would put
+  // acc in scratch memory, so these accumulators are indexed by k only)
+  f32x4_t gacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+
+  // prologue, in issue order: stages 0 .. kNB - 2, B rows of step 0 (G)
+#pragma unroll
+  for (int j = 0; j < C::kNB - 1; ++j) load_stage(j);
+  load_b(0, 0);
+
+  // Step i: at its top stage i has landed once at most the loads of the later
+  // stages are outstanding (main); G workgroups (B rows issued one step ahead)
+  // wait for all. The barrier makes stage i visible (and, at step 0, the level
+  // table) and ends every wave's reads of step i - 1, whose buffer the stage of
+  // step i + kNB - 1 then overwrites. Unrolled by four: compile-time slots.
+  auto step = [&](int i, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;  // i % 4
+    constexpr int b = slot & 1;
+    const unsigned char* st = stage_of(i);
+    const uint16_t* ycur = reinterpret_cast<const uint16_t*>(st);
+    if (grole) wait_vmem();
+    else wait_vmem_upto<C::kMainWait>();
+    __syncthreads();
+    load_stage(i + C::kNB - 1);
+    if (grole) {
+      load_b(i + 1, b ^ 1);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int tb = wave_u + 4 * k;
+        if (tb < TB) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            gacc[k] = mfma16(*reinterpret_cast<const uint4*>(ycur + y_off(tb, q)), breg[b][q], gacc[k]);
+        }
+      }
+      return;
+    }
+    (void)b;
+    // this lane's 16 rows' absmax (a wave past d_in takes zeros: its codes are
+    // unrelated bytes) and its two columns' transposed codes
+    const float* ap = reinterpret_cast<const float*>(st + C::kYBytes + C::kCBytes + wave_u * 256) + 16 * g;
+    float a[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = *reinterpret_cast<const float4*>(ap + 4 * j);
+      a[4 * j] = wval ? v.x : 0.f;
+      a[4 * j + 1] = wval ? v.y : 0.f;
+      a[4 * j + 2] = wval ? v.z : 0.f;
+      a[4 * j + 3] = wval ? v.w : 0.f;
+    }
+    const unsigned char* cst = st + C::kYBytes + c_off;
+    uint2 cc[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) cc[c] = lds_read_tr4(cst + 8 * c);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      uint4 yf[TB];
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) yf[tb] = *reinterpret_cast<const uint4*>(ycur + y_off_main(tb, q));
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint4 wfr = dequant8(q ? cc[c].y : cc[c].x, a + 8 * q);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) acc[tb][c] = mfma16(yf[tb], wfr, acc[tb][c]);
+      }
+    }
+  };
+  for (int i = 0; i < steps; i += 4) {
+    step(i, std::integral_constant<int, 0>{});
+    if (i + 1 < steps) step(i + 1, std::integral_constant<int, 1>{});
+    if (i + 2 < steps) step(i + 2, std::integral_constant<int, 2>{});
+    if (i + 3 < steps) step(i + 3, std::integral_constant<int, 3>{});
+  }
+  wait_vmem();  // run-ahead loads (direct-to-LDS ones included) land before the workgroup ends
+
+  // C layout: lane (l16, g) holds column l16, rows 4 g + e of each 16 x 16 block
+  if (!grole) {
+    float* dst = part_x + static_cast<size_t>(sp) * T * K;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * tb + 4 * g + e;
+        if (t >= T) continue;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int k = k0 + 32 * wave + 16 * c + l16;
+          if (k < K) dst[static_cast<size_t>(t) * K + k] = acc[tb][c][e];
+        }
+      }
+    return;
+  }
+  float* gdst = part_g + static_cast<size_t>(sp) * T * r;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int tb = wave + 4 * k;
+    if (tb >= TB) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * tb + 4 * g + e, j = 16 * jb + l16;
+      if (t < T && j < r) gdst[static_cast<size_t>(t) * r + j] = gacc[k][e];
+    }
+  }
+}
+
+// The same product with the weight dequantized into LDS (one step ahead, half an
+// NF4 block per thread, natural row-major layout) and read back transposed
+// (ds_read_b64_tr_b16); taken where the transposing-code kernel measured slower
+// (more than 32 tokens, or slices of fewer than eight steps).
+constexpr int kDStride = kCols + 32;    // dequantized tile row pitch, bf16 (320 bytes)
+// Row n of the dequantized tile starts at n kDStride + dshift(n): the pitch is 64
+// bytes past a multiple of 256, so the four rows of one transposing read fall on
+// distinct banks, and rows four apart shift by 16 bytes per group of four, which
+// spreads the 16-byte dequantization stores of a 16-lane group over all banks
+// (and the two 16-lane groups of a transposing read over disjoint banks).
+__device__ __forceinline__ int dshift(int n) { return 8 * ((n >> 2) & 3); }
+
+template <int TB>
+struct DxTileCfg {
+  static constexpr int kTile = kNS * kDStride * 2;  // bytes of one dequantized tile
+  static constexpr int kYBytes = 16 * TB * kNS * 2;  // one dY stage [16 TB][64] bf16
+  static constexpr int kCopies = 2 * TB;             // 1 KB direct-to-LDS copies per stage
+  static constexpr int kPerWave = kCopies / 4;
+  static constexpr int kBytes = 2 * kTile + 2 * kYBytes;
+};
+
+// Workgroups 0 .. kcb * splits - 1: (column block, slice); the next
+// splits * ceil(r / 16): (slice, rank block) of G.
+template <int TB>
+__global__ __launch_bounds__(kKThreads) void lora_dx_splitk_tile_kernel(
+    int T, int K, int N, int r, int rows_per_split, int kcb, int splits, const uint16_t* __restrict__ dy,
+    const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const uint16_t* __restrict__ B,
+    float* __restrict__ part_x, float* __restrict__ part_g) {
+  using C = DxTileCfg<TB>;
   __shared__ __align__(1024) float lut[16];  // first in LDS: level addresses need no base
   __shared__ __align__(16) unsigned char smem[C::kBytes];
 
@@ -374,8 +644,13 @@ hipError_t launch_dx_splitk_t(int T, int K, int N, int r, const DxSplitPlan& p, 
                               const uint8_t* codes, const float* absmax, const uint16_t* B, float* part_x,
                               float* part_g, hipStream_t stream) {
   const int blocks = (p.kcb + (r + 15) / 16) * p.splits;
-  lora_dx_splitk_kernel<TB><<<blocks, kKThreads, 0, stream>>>(T, K, N, r, p.rows_per_split, p.kcb, p.splits,
-                                                             dy, codes, absmax, B, part_x, part_g);
+  if (TB == 2 && p.tr)
+    lora_dx_splitk_kernel<2><<<blocks, kKThreads, 0, stream>>>(T, K, N, r, p.rows_per_split, p.kcb, p.splits,
+                                                              dy, codes, absmax, B, part_x, part_g);
+  else
+    lora_dx_splitk_tile_kernel<TB><<<blocks, kKThreads, 0, stream>>>(T, K, N, r, p.rows_per_split, p.kcb,
+                                                                    p.splits, dy, codes, absmax, B, part_x,
+                                                                    part_g);
   return hipGetLastError();
 }
 
@@ -391,10 +666,22 @@ DxSplitPlan plan_dx_splitk(int64_t T, int64_t K, int64_t N, int r) {
   const int nsteps = static_cast<int>((N + kNS - 1) / kNS);
   const int tbi = T <= 32 ? 0 : (T <= 64 ? 1 : 2);
   const int per_split = p.kcb + (r + 15) / 16;
-  int S = 256 * kResident[tbi] / per_split;
-  S = S < 1 ? 1 : (S > kMaxSplits ? kMaxSplits : S);
-  S = S > nsteps ? nsteps : S;
-  const int steps_per = (nsteps + S - 1) / S;
+  // Slices: every slice adds per_split workgroups; as many as one resident round
+  // holds, at most kMaxSplits. Up to 32 tokens the transposing-code kernel runs
+  // when its slices are at least kTrMinSteps steps long.
+  auto slice = [&](int resident, int& steps_per) {
+    int S = 256 * resident / per_split;
+    S = S < 1 ? 1 : (S > kMaxSplits ? kMaxSplits : S);
+    S = S > nsteps ? nsteps : S;
+    steps_per = (nsteps + S - 1) / S;
+  };
+  int steps_per = 0;
+  p.tr = false;
+  if (tbi == 0) {
+    slice(kResidentTr, steps_per);
+    p.tr = steps_per >= kTrMinSteps;
+  }
+  if (!p.tr) slice(kResidentTile[tbi], steps_per);
   p.rows_per_split = steps_per * kNS;
   p.splits = (nsteps + steps_per - 1) / steps_per;  // every slice non-empty
   p.part_x_bytes = align256(static_cast<size_t>(p.splits) * T * K * 4);
