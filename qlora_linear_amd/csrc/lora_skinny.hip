@@ -36,6 +36,9 @@ __device__ __forceinline__ int m_off(int t, int c) {
 
 // Jobs of one launch: job i reduces M_i^T V_i over the tokens, workgroups
 // cb_end[i - 1] .. cb_end[i] - 1 (x the token splits) taking its 256-column blocks.
+// With one token split and no optimizer step (`direct`), each workgroup stores its
+// sums as the reduce would (job 0 may be dA: into da, unscaled; every other job
+// bf16(s sum) into out) and no reduce is launched.
 struct SkinnyTab {
   int n;
   int cb_end[kMaxSkinnyJobs];
@@ -43,6 +46,10 @@ struct SkinnyTab {
   const uint16_t* V[kMaxSkinnyJobs];  // [T][vstr], r columns used (G or U)
   float* part[kMaxSkinnyJobs];        // [splits][r][C] fp32
   int C[kMaxSkinnyJobs], r[kMaxSkinnyJobs], vstr[kMaxSkinnyJobs];
+  int direct, first_a;
+  float s;
+  uint16_t* out[kMaxSkinnyJobs];
+  DaOut da;
 };
 
 template <int RU>
@@ -62,6 +69,8 @@ __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(int T, int t_p
   const uint16_t* M = tab.M[0];
   const uint16_t* V = tab.V[0];
   float* part = tab.part[0];
+  uint16_t* out = tab.out[0];
+  bool is_a = tab.first_a != 0;
   int C = tab.C[0], r = tab.r[0], vstr = tab.vstr[0], cb = bid;
 #pragma unroll
   for (int i = 1; i < kMaxSkinnyJobs; ++i)
@@ -69,6 +78,8 @@ __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(int T, int t_p
       M = tab.M[i];
       V = tab.V[i];
       part = tab.part[i];
+      out = tab.out[i];
+      is_a = false;
       C = tab.C[i];
       r = tab.r[i];  // rank of this job's V (the columns used)
       vstr = tab.vstr[i];  // V row stride (elements): G may be a column slice
@@ -182,6 +193,57 @@ __global__ __launch_bounds__(kThreads) void skinny_partial_kernel(int T, int t_p
   }
 
   // partial[split][j][c]: lane column c = l & 31 of each 32-column tile
+  if constexpr (RU <= 128) {
+    if (tab.direct) {  // uniform: the one split's sums, rounded as the reduce rounds (0 + sum)
+      // The workgroup's block goes through the (now idle) M stages so that it leaves
+      // in 16-byte stores: dA as [256 columns][RU + 8], each column's ranks
+      // contiguous like dA's rows; dB as [RU][256 + 8], like dB's rows.
+      constexpr int kAS = RU + 8, kBS = BC + 8;
+      static_assert(BC * kAS <= kStages * kMElems && RU * kBS <= kStages * kMElems, "staging fits");
+      uint16_t* ot = &ms[0][0];
+      __syncthreads();  // every wave is done with the last stage
+#pragma unroll
+      for (int a = 0; a < RU / 32; ++a)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int cl = wave * 64 + j * 32 + (lane & 31);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int jr = a * 32 + mfma32_row(e, lane);
+            const float sum = 0.f + acc[a][j][e];
+            if (is_a) ot[cl * kAS + jr] = to_bf16(sum);
+            else ot[jr * kBS + cl] = to_bf16(tab.s * sum);
+          }
+        }
+      __syncthreads();
+      if (is_a) {  // 8 ranks of one column per store; r and the projection width are multiples of 8
+        const int gw = tab.da.gw, q8 = r / 8;
+        for (int q = tid; q < BC * q8; q += kThreads) {
+          const int cl = q / q8, jr = 8 * (q - cl * q8), c = c0 + cl;
+          if (c >= C) continue;
+          const int g = jr / gw, jj = jr - g * gw;
+          uint16_t* dst = tab.da.p[g] + static_cast<size_t>(c) * gw + jj;
+          if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(ot + cl * kAS + jr);
+          } else {
+            for (int e = 0; e < 8; ++e) dst[e] = ot[cl * kAS + jr + e];
+          }
+        }
+      } else {  // 8 columns of one rank row per store where whole and aligned, else one by one
+        for (int q = tid; q < r * (BC / 8); q += kThreads) {
+          const int jr = q / (BC / 8), cl = 8 * (q - jr * (BC / 8)), c = c0 + cl;
+          if (c >= C) continue;
+          uint16_t* dst = out + static_cast<size_t>(jr) * C + c;
+          if (c + 8 <= C && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(ot + jr * kBS + cl);
+          } else {
+            for (int e = 0; e < 8 && c + e < C; ++e) dst[e] = ot[jr * kBS + cl + e];
+          }
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int a = 0; a < RU / 32; ++a)
 #pragma unroll
@@ -348,6 +410,13 @@ hipError_t launch_skinny_jobs(int T, int n, const SkinnyJob* jobs, int splits, f
     rmax = std::max(rmax, j.r);
   }
   const dim3 grid(cbs, splits);
+  // one token split, no optimizer step, ranks up to 128 (the staging of the
+  // workgroup's block fits the M stages): no partials and no reduce launch
+  tab.direct = splits == 1 && adam == nullptr && rmax <= 128;
+  tab.first_a = red.first_a;
+  tab.s = s;
+  tab.da = da;
+  for (int i = 0; i < n; ++i) tab.out[i] = jobs[i].out;
   if (rmax <= 32)
     skinny_partial_kernel<32><<<grid, kThreads, 0, stream>>>(T, per, tab);
   else if (rmax <= 64)
@@ -359,7 +428,7 @@ hipError_t launch_skinny_jobs(int T, int n, const SkinnyJob* jobs, int splits, f
   else
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || tab.direct) return e;
   if (adam != nullptr) {  // one projection: dA (job 0) and dB (job 1) of one rank
     if (n != 2 || !jobs[0].is_a || jobs[0].r != jobs[1].r) return hipErrorInvalidValue;
     skinny_reduce2_adamw_kernel<<<static_cast<unsigned>((els + 255) / 256), 256, 0, stream>>>(
