@@ -98,13 +98,16 @@ def test_odd_shapes(q, T, K, N, r):
 # reduction step (d_in = 64), a half-filled last step (d_in % 128 == 64), d_out
 # not a multiple of the 16- or 64-row block, one, two, four and eight 16-token
 # blocks, one and many d_in splits, every rank block count, and wide d_out (up to
-# 32776) at few tokens.
+# 32776) at few tokens. The wide-d_out cases up to 32 tokens run the dX that reads
+# each column's codes with the 4-bit transposing LDS read (slices of eight or more
+# steps), the last two with a last 128-column block half past d_in.
 FEW = [(1, 64, 16, 8), (1, 4096, 64, 16), (5, 192, 40, 16), (9, 64, 8, 56), (16, 256, 48, 24),
        (17, 320, 136, 64), (32, 448, 1000, 32), (32, 128, 8, 8), (16, 4096, 4096, 16),
        (32, 4096, 1024, 64), (48, 192, 72, 24), (64, 4096, 4096, 16), (100, 320, 200, 64),
        (128, 448, 1000, 32), (127, 2048, 136, 8), (1, 320, 4104, 16), (8, 192, 5000, 64),
        (32, 2048, 4160, 40), (3, 1024, 28672, 16), (16, 1024, 32776, 8), (20, 1024, 20488, 32),
-       (12, 1024, 16392, 64), (7, 3072, 12296, 48), (1, 2048, 9000, 24), (25, 3072, 520, 16)]
+       (12, 1024, 16392, 64), (7, 3072, 12296, 48), (1, 2048, 9000, 24), (25, 3072, 520, 16),
+       (5, 320, 16392, 16), (9, 192, 12352, 64)]
 
 
 @pytest.mark.parametrize("T,K,N,r", FEW)
