@@ -63,13 +63,13 @@ struct DxSplitCfg {
   // loads per wave and step in main workgroups: dY copies, codes, absmax; at the
   // top of step i, stage i has landed once the later stages' loads are all that
   // is outstanding
-  static constexpr int kMainWait = (kNB - 2) * (kPerWave + 2);
+  static constexpr int kMainWait = (kNB - 3) * (kPerWave + 2);  // stages i and i + 1 landed
 };
 
 // Workgroups 0 .. kcb * splits - 1: (column block, slice); the next
 // splits * ceil(r / 16): (slice, rank block) of G.
 template <int TB>
-__global__ __launch_bounds__(kKThreads) void lora_dx_splitk_kernel(
+__global__ __launch_bounds__(kKThreads, 4) void lora_dx_splitk_kernel(
     int T, int K, int N, int r, int rows_per_split, int kcb, int splits, const uint16_t* __restrict__ dy,
     const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const uint16_t* __restrict__ B,
     float* __restrict__ part_x, float* __restrict__ part_g) {
@@ -205,6 +205,29 @@ __global__ __launch_bounds__(kKThreads) void lora_dx_splitk_kernel(
   // acc in scratch memory, so these accumulators are indexed by k only)
   f32x4_t gacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 
+  // B fragments of one stage: this lane's 16 rows' absmax (a wave past d_in takes
+  // zeros: its codes are unrelated bytes) and its two columns' transposed codes
+  uint4 wf[2][2];
+  auto dequant_stage = [&](const unsigned char* st, uint4 (*w)[2]) {
+    const float* ap = reinterpret_cast<const float*>(st + C::kYBytes + C::kCBytes + wave_u * 256) + 16 * g;
+    float a[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = *reinterpret_cast<const float4*>(ap + 4 * j);
+      a[4 * j] = wval ? v.x : 0.f;
+      a[4 * j + 1] = wval ? v.y : 0.f;
+      a[4 * j + 2] = wval ? v.z : 0.f;
+      a[4 * j + 3] = wval ? v.w : 0.f;
+    }
+    const unsigned char* cst = st + C::kYBytes + c_off;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint2 cc = lds_read_tr4(cst + 8 * c);
+      w[c][0] = dequant8(cc.x, a);
+      w[c][1] = dequant8(cc.y, a + 8);
+    }
+  };
+
   // prologue, in issue order: stages 0 .. kNB - 2, B rows of step 0 (G)
 #pragma unroll
   for (int j = 0; j < C::kNB - 1; ++j) load_stage(j);
@@ -238,34 +261,26 @@ __global__ __launch_bounds__(kKThreads) void lora_dx_splitk_kernel(
       return;
     }
     (void)b;
-    // this lane's 16 rows' absmax (a wave past d_in takes zeros: its codes are
-    // unrelated bytes) and its two columns' transposed codes
-    const float* ap = reinterpret_cast<const float*>(st + C::kYBytes + C::kCBytes + wave_u * 256) + 16 * g;
-    float a[16];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 v = *reinterpret_cast<const float4*>(ap + 4 * j);
-      a[4 * j] = wval ? v.x : 0.f;
-      a[4 * j + 1] = wval ? v.y : 0.f;
-      a[4 * j + 2] = wval ? v.z : 0.f;
-      a[4 * j + 3] = wval ? v.w : 0.f;
-    }
-    const unsigned char* cst = st + C::kYBytes + c_off;
-    uint2 cc[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) cc[c] = lds_read_tr4(cst + 8 * c);
+    // the B fragments of step i were formed during step i - 1 (step 0: here); those
+    // of step i + 1 are formed now, beside step i's MFMAs
+    if (i == 0) dequant_stage(st, wf);
+    uint4 wn[2][2];
+    if (i + 1 < steps) dequant_stage(stage_of(i + 1), wn);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       uint4 yf[TB];
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) yf[tb] = *reinterpret_cast<const uint4*>(ycur + y_off_main(tb, q));
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint4 wfr = dequant8(q ? cc[c].y : cc[c].x, a + 8 * q);
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) acc[tb][c] = mfma16(yf[tb], wfr, acc[tb][c]);
-      }
+        for (int tb = 0; tb < TB; ++tb) acc[tb][c] = mfma16(yf[tb], wf[c][q], acc[tb][c]);
     }
+    if (i + 1 < steps)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) wf[c][q] = wn[c][q];
   };
   for (int i = 0; i < steps; i += 4) {
     step(i, std::integral_constant<int, 0>{});
